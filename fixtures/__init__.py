@@ -1,0 +1,279 @@
+"""Seeded synthetic inputs for the canvas denoiser, shared by the CPU oracle
+and by the callers of the GPU library (tests and bench).
+
+This module holds no arithmetic of the method itself: it only produces the
+random-init weights, prompt ids and kernel-level test tensors that both sides
+consume, as the same bytes.  The recipe (hash, Box-Muller, bf16 / e4m3
+storage) is in ``gen.c``; every value is a pure function of
+(seed, tensor id, flat index).
+
+Weights follow the "random-init N(0, 0.02)" recipe of the synthetic
+configurations; logical layouts are ``[in, out]`` row-major:
+E [V, d], Wq [d, Hq*D], Wk/Wv [d, Hkv*D], Wo [Hq*D, d], Wr [d, E],
+Wg/Wu [E, d, F], Wd [E, F, d].  RMSNorm gains are 1 and are not stored.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfixtures.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gen.c into libfixtures.so (plain C, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
+             os.path.join(_HERE, "gen.c"), "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        u64, u32, i64, vp = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p
+        lib.fx_normal_f32.argtypes = [u64, u32, u64, u64, ctypes.c_float, vp]
+        lib.fx_normal_bf16.argtypes = [u64, u32, u64, u64, ctypes.c_float, vp]
+        lib.fx_uniform_ids.argtypes = [u64, u32, u64, u64, u32, vp]
+        lib.fx_quant_e4m3_cols.argtypes = [vp, i64, i64, vp, vp]
+        lib.fx_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.fx_e4m3_encode.restype = ctypes.c_uint8
+        lib.fx_bf16_encode.argtypes = [ctypes.c_float]
+        lib.fx_bf16_encode.restype = ctypes.c_uint16
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+# --------------------------------------------------------------------------- raw streams
+def normal(seed: int, tid: int, shape, sigma: float, dtype: str = "f32", start: int = 0,
+           out: np.ndarray | None = None) -> np.ndarray:
+    """sigma * N(0,1) for flat indices [start, start + prod(shape)).
+
+    dtype "f32" returns float32; "bf16" returns the bf16 bit patterns as uint16.
+    """
+    n = int(np.prod(shape))
+    lib = _load()
+    if dtype == "f32":
+        a = out if out is not None else np.empty(shape, np.float32)
+        lib.fx_normal_f32(seed, tid, start, n, sigma, _ptr(a))
+    elif dtype == "bf16":
+        a = out if out is not None else np.empty(shape, np.uint16)
+        lib.fx_normal_bf16(seed, tid, start, n, sigma, _ptr(a))
+    else:
+        raise ValueError(dtype)
+    return a
+
+
+def uniform_ids(seed: int, tid: int, n: int, vocab: int, start: int = 0) -> np.ndarray:
+    a = np.empty(n, np.int32)
+    _load().fx_uniform_ids(seed, tid, start, n, vocab, _ptr(a))
+    return a
+
+
+def quant_e4m3_cols(w: np.ndarray):
+    """Per-output-column e4m3 quantisation of a [rows, cols] float32 matrix.
+
+    Returns (codes uint8 [rows, cols], scales float32 [cols]).
+    """
+    w = np.ascontiguousarray(w, np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty(cols, np.float32)
+    _load().fx_quant_e4m3_cols(_ptr(w), rows, cols, _ptr(q), _ptr(s))
+    return q, s
+
+
+def e4m3_encode_scalar(x: float) -> int:
+    return int(_load().fx_e4m3_encode(float(x)))
+
+
+def bf16_encode_scalar(x: float) -> int:
+    return int(_load().fx_bf16_encode(float(x)))
+
+
+def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 exactly (a storage view)."""
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """All 256 OCP e4m3 code values as float64 (NaN for the two NaN codes)."""
+    t = np.empty(256, np.float64)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 7
+        if e == 0xF and m == 7:
+            t[c] = np.nan
+        elif e == 0:
+            t[c] = s * m * 2.0 ** -9
+        else:
+            t[c] = s * (1 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+# --------------------------------------------------------------------------- tensor ids
+TID_EMBED = 1
+TID_PROMPT = 2
+TID_ATTN_Q, TID_ATTN_K, TID_ATTN_V = 3, 4, 5
+TID_MOE_X = 6
+KINDS = ("wq", "wk", "wv", "wo", "wr", "wg", "wu", "wd")
+
+
+def layer_tid(kind: str, layer: int) -> int:
+    return 64 + 16 * layer + KINDS.index(kind)
+
+
+# --------------------------------------------------------------------------- workloads
+@dataclass(frozen=True)
+class Workload:
+    """Sizes and storage types of one synthetic denoiser configuration."""
+    name: str
+    n_layers: int
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    n_experts: int
+    top_k: int
+    d_ff: int
+    vocab: int
+    prompt_len: int
+    canvas: int = 256
+    T: int = 12
+    n_canvases: int = 1
+    act: str = "bf16"          # "f32" | "bf16"
+    experts: str = "bf16"      # "f32" | "bf16" | "fp8"
+    rope_base: float = 10000.0
+    rms_eps: float = 1e-6
+    temperature: float = 1.0
+    sigma: float = 0.02
+    seed: int = 0
+
+    @property
+    def max_ctx(self) -> int:
+        return self.prompt_len + self.n_canvases * self.canvas
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+TINY_FP32 = Workload("tiny_fp32_2L_d256_V1024", n_layers=2, d_model=256, n_q_heads=4,
+                     n_kv_heads=2, head_dim=64, n_experts=8, top_k=2, d_ff=512, vocab=1024,
+                     prompt_len=64, act="f32", experts="f32")
+MOE26B = Workload("moe26b_30L_d2816_E128k8_V262144_P8192", n_layers=30, d_model=2816,
+                  n_q_heads=16, n_kv_heads=8, head_dim=128, n_experts=128, top_k=8, d_ff=704,
+                  vocab=262144, prompt_len=8192)
+MOE26B_FP8_LONG = MOE26B.with_(name="moe26b_fp8experts_P131072_K4", experts="fp8",
+                               prompt_len=131072, n_canvases=4)
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str = "attn_gqa16x8_D128_S4096p256_bf16"
+    n_q_heads: int = 16
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    prompt_len: int = 4096
+    canvas: int = 256
+    seed: int = 0
+
+    @property
+    def seq(self) -> int:
+        return self.prompt_len + self.canvas
+
+
+@dataclass(frozen=True)
+class MoeWorkload:
+    name: str = "moe_layer_T256_d2816_E128k8_F704_bf16"
+    tokens: int = 256
+    d_model: int = 2816
+    n_experts: int = 128
+    top_k: int = 8
+    d_ff: int = 704
+    sigma: float = 0.02
+    seed: int = 0
+
+
+ATTN = AttnWorkload()
+MOE_LAYER = MoeWorkload()
+
+
+# --------------------------------------------------------------------------- model tensors
+def tensor_shape(w: Workload, kind: str) -> tuple:
+    d, hq, hkv, D, E, F, V = (w.d_model, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                              w.n_experts, w.d_ff, w.vocab)
+    return {"embed": (V, d), "wq": (d, hq * D), "wk": (d, hkv * D), "wv": (d, hkv * D),
+            "wo": (hq * D, d), "wr": (d, E), "wg": (E, d, F), "wu": (E, d, F),
+            "wd": (E, F, d)}[kind]
+
+
+def is_expert(kind: str) -> bool:
+    return kind in ("wg", "wu", "wd")
+
+
+def storage_dtype(w: Workload, kind: str) -> str:
+    if is_expert(kind):
+        return w.experts
+    return w.act
+
+
+def model_tensor(w: Workload, kind: str, layer: int = 0, expert: int | None = None):
+    """One logical weight tensor in the workload's storage type.
+
+    f32  -> float32 array
+    bf16 -> uint16 array of bf16 bit patterns
+    fp8  -> (uint8 codes, float32 per-output-column scales); experts only,
+            one expert at a time (``expert`` required)
+    """
+    shape = tensor_shape(w, kind)
+    tid = TID_EMBED if kind == "embed" else layer_tid(kind, layer)
+    dt = storage_dtype(w, kind)
+    start = 0
+    if is_expert(kind) and expert is not None:
+        shape = shape[1:]
+        start = expert * int(np.prod(shape))
+    if dt == "fp8":
+        if expert is None:
+            raise ValueError("fp8 experts are produced one expert at a time")
+        vals = normal(w.seed, tid, shape, w.sigma, "f32", start=start)
+        return quant_e4m3_cols(vals)
+    return normal(w.seed, tid, shape, w.sigma, dt, start=start)
+
+
+def prompt_ids(w: Workload) -> np.ndarray:
+    return uniform_ids(w.seed, TID_PROMPT, w.prompt_len, w.vocab)
+
+
+def attn_inputs(a: AttnWorkload = ATTN):
+    """Q [Hq, C, D], K and V [Hkv, S, D] as bf16 bit patterns, each N(0, 1)."""
+    q = normal(a.seed, TID_ATTN_Q, (a.n_q_heads, a.canvas, a.head_dim), 1.0, "bf16")
+    k = normal(a.seed, TID_ATTN_K, (a.n_kv_heads, a.seq, a.head_dim), 1.0, "bf16")
+    v = normal(a.seed, TID_ATTN_V, (a.n_kv_heads, a.seq, a.head_dim), 1.0, "bf16")
+    return q, k, v
+
+
+def moe_inputs(m: MoeWorkload = MOE_LAYER):
+    """Hidden states X [T, d] ~ N(0,1) and the layer-0 router / expert weights (bf16 bits)."""
+    x = normal(m.seed, TID_MOE_X, (m.tokens, m.d_model), 1.0, "bf16")
+    wr = normal(m.seed, layer_tid("wr", 0), (m.d_model, m.n_experts), m.sigma, "bf16")
+    wg = normal(m.seed, layer_tid("wg", 0), (m.n_experts, m.d_model, m.d_ff), m.sigma, "bf16")
+    wu = normal(m.seed, layer_tid("wu", 0), (m.n_experts, m.d_model, m.d_ff), m.sigma, "bf16")
+    wd = normal(m.seed, layer_tid("wd", 0), (m.n_experts, m.d_ff, m.d_model), m.sigma, "bf16")
+    return x, wr, wg, wu, wd

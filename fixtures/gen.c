@@ -1,0 +1,106 @@
+/*
+ * Seeded synthetic-input generator.  Shared by the CPU oracle and by the
+ * GPU library's callers (tests, bench); it holds none of the denoiser's
+ * arithmetic, only the recipe for the random-init weights and inputs.
+ *
+ * Every value is a pure function of (seed, tensor id, flat index), so any
+ * slice of any tensor can be produced on its own, in any order, by any
+ * number of threads.
+ *
+ *   hash   : SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014)
+ *            applied to  seed + (tid * 2^40 + index + 1) * golden-gamma.
+ *   normal : Box-Muller on two 24-bit uniforms taken from one 64-bit hash,
+ *            single precision (glibc logf / sinf / cosf), element 2j takes
+ *            the cosine branch of pair j, element 2j+1 the sine branch.
+ *   ids    : multiply-high of the upper 32 hash bits by the vocabulary size.
+ *   bf16   : round-to-nearest-even of the float value.
+ *   e4m3   : OCP FP8 E4M3 (bias 7, max 448, no infinities), per output
+ *            column scale = amax / 448, round-to-nearest-even, saturating.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+static inline uint64_t fx_hash(uint64_t seed, uint32_t tid, uint64_t index) {
+    uint64_t z = seed + (((uint64_t)tid << 40) + index + 1ull) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+static inline float fx_normal_at(uint64_t seed, uint32_t tid, uint64_t idx) {
+    uint64_t h = fx_hash(seed, tid, idx >> 1);
+    /* (2m+1) * 2^-24 with m < 2^23: exact in float, strictly inside (0,1) */
+    float u1 = (float)(((h >> 41) << 1) | 1ull) * 0x1p-24f;
+    float u2 = (float)((h >> 8) & 0xFFFFFFull) * 0x1p-24f;
+    float r = sqrtf(-2.0f * logf(u1));
+    float th = 6.28318530717958647692f * u2;
+    return (idx & 1) ? r * sinf(th) : r * cosf(th);
+}
+
+static inline uint16_t fx_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+void fx_normal_f32(uint64_t seed, uint32_t tid, uint64_t start, uint64_t n, float sigma,
+                   float* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < (int64_t)n; ++i)
+        out[i] = sigma * fx_normal_at(seed, tid, start + (uint64_t)i);
+}
+
+void fx_normal_bf16(uint64_t seed, uint32_t tid, uint64_t start, uint64_t n, float sigma,
+                    uint16_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < (int64_t)n; ++i)
+        out[i] = fx_f32_to_bf16(sigma * fx_normal_at(seed, tid, start + (uint64_t)i));
+}
+
+void fx_uniform_ids(uint64_t seed, uint32_t tid, uint64_t start, uint64_t n, uint32_t vocab,
+                    int32_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < (int64_t)n; ++i) {
+        uint64_t h = fx_hash(seed, tid, start + (uint64_t)i);
+        out[i] = (int32_t)(((h >> 32) * (uint64_t)vocab) >> 32);
+    }
+}
+
+/* float -> OCP e4m3 code, round-to-nearest-even, saturating to +-448. */
+static inline uint8_t fx_f32_to_e4m3(float x) {
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    float a = fabsf(x);
+    if (isnan(x)) return 0x7f;
+    if (a >= 0x1p-6f) {
+        int e;
+        frexpf(a, &e);           /* a = f * 2^e, f in [0.5, 1) */
+        e -= 1;                  /* a = 1.m * 2^e */
+        float q = nearbyintf(ldexpf(a, 3 - e));   /* in [8, 16] */
+        if (q >= 16.0f) { q = 8.0f; e += 1; }
+        if (e > 8 || (e == 8 && q > 14.0f)) return (uint8_t)(sign | 0x7e); /* 448 */
+        return (uint8_t)(sign | ((e + 7) << 3) | ((int)q - 8));
+    }
+    float q = nearbyintf(ldexpf(a, 9));           /* subnormal steps of 2^-9 */
+    return (uint8_t)(sign | (int)q);              /* q == 8 is the smallest normal */
+}
+
+/* Per output column quantisation of a row-major [rows, cols] float matrix. */
+void fx_quant_e4m3_cols(const float* w, int64_t rows, int64_t cols, uint8_t* q,
+                        float* scales) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; ++c) {
+        float amax = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) amax = fmaxf(amax, fabsf(w[r * cols + c]));
+        scales[c] = amax > 0.0f ? amax / 448.0f : 1.0f;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = fx_f32_to_e4m3(w[r * cols + c] / scales[c]);
+}
+
+/* Exposed for the generator's own unit tests. */
+uint8_t fx_e4m3_encode(float x) { return fx_f32_to_e4m3(x); }
+uint16_t fx_bf16_encode(float x) { return fx_f32_to_bf16(x); }
