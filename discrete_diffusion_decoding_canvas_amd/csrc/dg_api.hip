@@ -1,0 +1,805 @@
+// C ABI of the canvas-denoising library: handle, weight re-layout, KV cache,
+// and the orchestration of prefill / denoise pass / block / commit.
+//
+// Stages follow the generation pipeline of the DiffusionGemma technical-report
+// summary (Method): the causal encoder fills the KV cache from the prompt
+// (prefill), the decoder refines the canvas with bidirectional attention over
+// [KV cache || canvas] (denoise pass), and the finished canvas is encoded
+// causally and appended to the cache (commit).  Positions follow the P + K*C
+// layout (same page, Dataset, "Example and sequence structure").
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/dg.h"
+#include "kernels.h"
+
+using namespace dg;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                       \
+    do {                                                                                    \
+        hipError_t e_ = (expr);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail(DG_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));           \
+    } while (0)
+
+#define DG_TRY(expr)                                                                        \
+    do {                                                                                    \
+        int r_ = (expr);                                                                    \
+        if (r_ != DG_OK) return r_;                                                         \
+    } while (0)
+
+constexpr int kPrefillChunk = 4096;   // tokens per causal-encoder chunk
+
+size_t dsize(int dt) { return dt == kF32 ? 4 : dt == kBF16 ? 2 : 1; }
+
+}  // namespace
+
+struct dg_handle {
+    dg_model_cfg cfg;
+    int L, d, Hq, Hkv, D, E, k, F, V, C;
+    int act, edt;
+    int64_t max_ctx, kv_rows;
+    int max_tokens;
+    int qkv_n;
+
+    std::vector<void*> allocs;
+
+    void* embed = nullptr;
+    std::vector<void*> wqkv, wo, wr, w1, wu, w2;
+    std::vector<float*> s1, s2;
+    std::vector<uint8_t> loaded;   // per (layer, kind) dense flags and per expert flags
+    bool ready = false;
+
+    void* kcache = nullptr;   // [L][Hkv][kv_rows][D]
+    void* vcache = nullptr;   // f32: same as K; bf16: [L][Hkv][D][kv_rows] transposed-permuted
+    float* cos_t = nullptr;
+    float* sin_t = nullptr;
+
+    float* x = nullptr;
+    void* a = nullptr;
+    uint8_t* a8 = nullptr;
+    float* qkv = nullptr;
+    void* q = nullptr;
+    void* attn_o = nullptr;
+    float* part = nullptr;
+    int64_t part_floats = 0;
+    float* rlog = nullptr;
+    int32_t* idx = nullptr;
+    float* gates = nullptr;
+    int32_t* counts = nullptr;
+    int32_t* base = nullptr;
+    int32_t* offsets = nullptr;
+    int32_t* perm_token = nullptr;
+    int32_t* inv = nullptr;
+    void* H = nullptr;
+    float* Y = nullptr;
+
+    HeadPartials hp{};
+    float* st_m = nullptr;
+    int32_t* st_a = nullptr;
+    float* st_lse = nullptr;
+    float* st_conf = nullptr;
+    int32_t* st_draw = nullptr;
+    int32_t* bad = nullptr;
+    float* logits_cap = nullptr;
+    int32_t* cap_idx = nullptr;
+    float* cap_gates = nullptr;
+    float* cap_hidden = nullptr;
+    int32_t* blk_canvas = nullptr;
+    uint8_t* blk_mask = nullptr;
+
+    void* stage = nullptr;
+    size_t stage_bytes = 0;
+
+    int64_t n_ctx = 0;
+    int k_blk = 0;
+    bool prefilled = false;
+
+    int alloc(void** p, size_t bytes) {
+        if (bytes == 0) bytes = 256;
+        if (hipMalloc(p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            *p = nullptr;
+            return fail(DG_ENOMEM, "hipMalloc of %zu bytes failed", bytes);
+        }
+        allocs.push_back(*p);
+        if (hipMemset(*p, 0, bytes) != hipSuccess) return fail(DG_EHIP, "hipMemset failed");
+        return DG_OK;
+    }
+    template <typename T>
+    int allocT(T** p, size_t count) {
+        void* v = nullptr;
+        int r = alloc(&v, count * sizeof(T));
+        *p = (T*)v;
+        return r;
+    }
+
+    size_t kv_layer_elems() const { return (size_t)Hkv * kv_rows * D; }
+    void* klayer(int l) const { return (char*)kcache + (size_t)l * kv_layer_elems() * dsize(act); }
+    void* vlayer(int l) const { return (char*)vcache + (size_t)l * kv_layer_elems() * dsize(act); }
+
+    // loaded flags: [L][5 dense] then [L][3][E]
+    uint8_t& dense_flag(int l, int kind) { return loaded[1 + l * 5 + kind]; }
+    uint8_t& expert_flag(int l, int which, int e) {
+        return loaded[1 + L * 5 + ((size_t)l * 3 + which) * E + e];
+    }
+};
+
+// =========================================================================== helpers
+static int validate_cfg(const dg_model_cfg* c) {
+    if (!c) return fail(DG_EINVAL, "cfg is NULL");
+    if (c->n_layers <= 0 || c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+        c->head_dim <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0 ||
+        c->vocab <= 0 || c->canvas <= 0 || c->max_ctx <= 0)
+        return fail(DG_EINVAL, "all sizes must be positive");
+    if (c->n_q_heads % c->n_kv_heads) return fail(DG_EINVAL, "n_q_heads %% n_kv_heads != 0");
+    if (c->top_k > c->n_experts || c->top_k > 16) return fail(DG_EINVAL, "top_k must be <= E and <= 16");
+    if (c->n_experts > 256) return fail(DG_EINVAL, "n_experts must be <= 256");
+    if (c->canvas > kMaxCanvas) return fail(DG_EINVAL, "canvas must be <= %d", kMaxCanvas);
+    if (c->head_dim & 1) return fail(DG_EINVAL, "head_dim must be even");
+    if (c->max_ctx < c->canvas) return fail(DG_EINVAL, "max_ctx must hold at least one canvas");
+    if (!(c->temperature > 0.f)) return fail(DG_EINVAL, "temperature must be > 0");
+    if (!(c->rope_base > 0.0)) return fail(DG_EINVAL, "rope_base must be > 0");
+    if (c->act_dtype == DG_F32) {
+        if (c->expert_dtype != DG_F32) return fail(DG_EINVAL, "f32 activations need f32 experts");
+        if (c->head_dim != 64 && c->head_dim != 128) return fail(DG_EINVAL, "f32 head_dim must be 64 or 128");
+    } else if (c->act_dtype == DG_BF16) {
+        if (c->expert_dtype != DG_BF16 && c->expert_dtype != DG_FP8_E4M3)
+            return fail(DG_EINVAL, "bf16 activations need bf16 or e4m3 experts");
+        if (c->head_dim != 128) return fail(DG_EINVAL, "bf16 path needs head_dim 128");
+        if (c->d_model % 64 || c->d_ff % 64) return fail(DG_EINVAL, "bf16 path needs d_model and d_ff multiples of 64");
+        if (c->vocab % 128) return fail(DG_EINVAL, "bf16 path needs vocab multiple of 128");
+        if ((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim % 64 || c->n_experts % 64)
+            return fail(DG_EINVAL, "bf16 path needs (Hq+2Hkv)*D and E multiples of 64");
+    } else {
+        return fail(DG_EINVAL, "act_dtype must be DG_F32 or DG_BF16");
+    }
+    return DG_OK;
+}
+
+static int ensure_ready(dg_handle* h) {
+    if (h->ready) return DG_OK;
+    for (size_t i = 0; i < h->loaded.size(); ++i)
+        if (!h->loaded[i]) return fail(DG_ESTATE, "weights not fully loaded (slot %zu missing)", i);
+    h->ready = true;
+    return DG_OK;
+}
+
+static ExpertWeights expert_weights(dg_handle* h, int l) {
+    ExpertWeights w;
+    w.w1 = h->w1[l];
+    w.wu = h->wu.empty() ? nullptr : h->wu[l];
+    w.w2 = h->w2[l];
+    w.s1 = h->s1.empty() ? nullptr : h->s1[l];
+    w.s2 = h->s2.empty() ? nullptr : h->s2[l];
+    return w;
+}
+
+#define K_TRY(expr) HIP_TRY(expr)
+
+// MoE block of one layer on h->a (and h->a8) for n tokens: router -> permute ->
+// expert GEMMs.  Leaves Y, gates, inv ready for the combine.
+static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* xin8,
+                   hipStream_t s) {
+    K_TRY(launch_gemm(h->act, kEpiStoreF32, xin, h->d, n, h->wr[l], h->d, h->E, h->rlog, h->E, s));
+    K_TRY(launch_router_permute(h->rlog, n, h->E, h->k, h->idx, h->gates, h->counts, h->base,
+                                h->offsets, h->perm_token, h->inv, s));
+    ExpertWeights w = expert_weights(h, l);
+    const int rows = n * h->k;
+    const void* X1 = (h->edt == kFP8) ? (const void*)xin8 : xin;
+    K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows, h->H, s));
+    K_TRY(launch_moe_gemm2(h->edt, w, h->H, h->offsets, h->E, h->d, h->F, rows, h->Y, s));
+    return DG_OK;
+}
+
+// One transformer layer for n tokens at positions pos0..pos0+n-1 (x, a hold the
+// residual and its norm).  Keys: cache rows [0, pos0 + n).  kv_only: stop after
+// writing K/V (the last encoder layer).
+static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool kv_only,
+                     hipStream_t s) {
+    K_TRY(launch_gemm(h->act, kEpiStoreF32, h->a, h->d, n, h->wqkv[l], h->d, h->qkv_n, h->qkv,
+                      h->qkv_n, s));
+    K_TRY(launch_rope_scatter(h->act, h->qkv, n, h->Hq, h->Hkv, h->D, pos0, h->cos_t, h->sin_t,
+                              h->q, h->klayer(l), h->vlayer(l), h->kv_rows, s));
+    if (kv_only) return DG_OK;
+    AttnArgs aa;
+    aa.q = h->q;
+    aa.k = h->klayer(l);
+    aa.v = h->vlayer(l);
+    aa.o = h->attn_o;
+    aa.Hq = h->Hq;
+    aa.Hkv = h->Hkv;
+    aa.M = n;
+    aa.S = (int)(pos0 + n);
+    aa.D = h->D;
+    aa.kv_rows = h->kv_rows;
+    aa.v_rows = h->kv_rows;
+    aa.scale = 1.0f / sqrtf((float)h->D);
+    aa.causal = causal ? 1 : 0;
+    aa.q_pos0 = pos0;
+    aa.part_o = h->part;
+    aa.part_ml = nullptr;
+    aa.part_capacity = h->part_floats;
+    K_TRY(launch_attention(h->act, aa, s));
+    K_TRY(launch_gemm(h->act, kEpiAddF32, h->attn_o, h->Hq * h->D, n, h->wo[l], h->Hq * h->D,
+                      h->d, h->x, h->d, s));
+    K_TRY(launch_rmsnorm(h->act, h->x, n, h->d, h->cfg.rms_eps, h->a,
+                         h->edt == kFP8 ? h->a8 : nullptr, s));
+    DG_TRY(run_moe(h, l, n, h->a, h->a8, s));
+    // residual add, then the next norm (next layer's input, or the final norm)
+    K_TRY(launch_moe_combine(h->act, 0, h->Y, n, h->d, h->k, h->gates, h->inv, h->x,
+                             h->cfg.rms_eps, h->a, h->edt == kFP8 ? h->a8 : nullptr, nullptr, s));
+    return DG_OK;
+}
+
+// Causal encoder over n tokens at positions pos0.. (prefill chunk or commit).
+static int encode(dg_handle* h, const int32_t* tokens, int n, int64_t pos0, hipStream_t s) {
+    K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, tokens, h->embed, n, h->d,
+                               h->cfg.rms_eps, h->x, h->a, s));
+    for (int l = 0; l < h->L; ++l)
+        DG_TRY(run_layer(h, l, n, pos0, true, l == h->L - 1, s));
+    return DG_OK;
+}
+
+// =========================================================================== C ABI
+extern "C" {
+
+const char* dg_last_error(void) { return g_err.c_str(); }
+
+int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
+    g_err.clear();
+    if (!out) return fail(DG_EINVAL, "out is NULL");
+    *out = nullptr;
+    DG_TRY(validate_cfg(cfg));
+    dg_handle* h = new dg_handle();
+    h->cfg = *cfg;
+    h->L = cfg->n_layers;
+    h->d = cfg->d_model;
+    h->Hq = cfg->n_q_heads;
+    h->Hkv = cfg->n_kv_heads;
+    h->D = cfg->head_dim;
+    h->E = cfg->n_experts;
+    h->k = cfg->top_k;
+    h->F = cfg->d_ff;
+    h->V = cfg->vocab;
+    h->C = cfg->canvas;
+    h->act = cfg->act_dtype == DG_F32 ? kF32 : kBF16;
+    h->edt = cfg->expert_dtype == DG_F32 ? kF32 : cfg->expert_dtype == DG_BF16 ? kBF16 : kFP8;
+    h->max_ctx = cfg->max_ctx;
+    h->kv_rows = (cfg->max_ctx + 31) & ~(int64_t)31;
+    h->max_tokens = std::max(h->C, kPrefillChunk);
+    h->qkv_n = (h->Hq + 2 * h->Hkv) * h->D;
+    h->loaded.assign(1 + (size_t)h->L * 5 + (size_t)h->L * 3 * h->E, 0);
+
+    auto cleanup = [&](int r) {
+        dg_destroy(h);
+        return r;
+    };
+    const size_t as = dsize(h->act), es = dsize(h->edt);
+    const size_t L = h->L, d = h->d, E = h->E, F = h->F, V = h->V, k = h->k;
+    const size_t T = h->max_tokens;
+    int r;
+#define A_TRY(call) do { if ((r = (call)) != DG_OK) return cleanup(r); } while (0)
+    A_TRY(h->alloc(&h->embed, V * d * as));
+    h->wqkv.resize(L);
+    h->wo.resize(L);
+    h->wr.resize(L);
+    h->w1.resize(L);
+    h->w2.resize(L);
+    if (h->edt == kF32) h->wu.resize(L);
+    if (h->edt == kFP8) {
+        h->s1.resize(L);
+        h->s2.resize(L);
+    }
+    for (size_t l = 0; l < L; ++l) {
+        A_TRY(h->alloc(&h->wqkv[l], d * h->qkv_n * as));
+        A_TRY(h->alloc(&h->wo[l], (size_t)h->Hq * h->D * d * as));
+        A_TRY(h->alloc(&h->wr[l], d * E * as));
+        A_TRY(h->alloc(&h->w1[l], E * d * F * es * (h->edt == kF32 ? 1 : 2)));
+        if (h->edt == kF32) A_TRY(h->alloc(&h->wu[l], E * d * F * es));
+        A_TRY(h->alloc(&h->w2[l], E * F * d * es));
+        if (h->edt == kFP8) {
+            A_TRY(h->allocT(&h->s1[l], E * 2 * F));
+            A_TRY(h->allocT(&h->s2[l], E * d));
+        }
+    }
+    const size_t kv = L * (size_t)h->Hkv * h->kv_rows * h->D * as;
+    A_TRY(h->alloc(&h->kcache, kv));
+    A_TRY(h->alloc(&h->vcache, kv));
+    // RoPE tables in double precision, stored as float: angle = pos * base^(-2j/D)
+    {
+        const int half = h->D / 2;
+        std::vector<float> c((size_t)h->kv_rows * half), sn((size_t)h->kv_rows * half);
+        std::vector<double> theta(half);
+        for (int j = 0; j < half; ++j) theta[j] = pow(cfg->rope_base, -2.0 * j / h->D);
+        for (int64_t p = 0; p < h->kv_rows; ++p)
+            for (int j = 0; j < half; ++j) {
+                const double ang = (double)p * theta[j];
+                c[(size_t)p * half + j] = (float)cos(ang);
+                sn[(size_t)p * half + j] = (float)sin(ang);
+            }
+        A_TRY(h->allocT(&h->cos_t, c.size()));
+        A_TRY(h->allocT(&h->sin_t, sn.size()));
+        if (hipMemcpy(h->cos_t, c.data(), c.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(h->sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+            return cleanup(fail(DG_EHIP, "RoPE table upload failed"));
+    }
+    A_TRY(h->allocT(&h->x, T * d));
+    A_TRY(h->alloc(&h->a, T * d * as));
+    if (h->edt == kFP8) A_TRY(h->allocT(&h->a8, T * d));
+    A_TRY(h->allocT(&h->qkv, T * h->qkv_n));
+    A_TRY(h->alloc(&h->q, T * h->Hq * h->D * as));
+    A_TRY(h->alloc(&h->attn_o, T * h->Hq * h->D * as));
+    // split-KV partials: the split count keeps (splits x query workgroups) near 512,
+    // so (D + 2) floats for at most 1024 x 128 query rows bound every call
+    h->part_floats = h->act == kF32 ? 64 : (int64_t)1024 * 128 * (h->D + 2);
+    A_TRY(h->allocT(&h->part, (size_t)h->part_floats));
+    A_TRY(h->allocT(&h->rlog, T * E));
+    A_TRY(h->allocT(&h->idx, T * k));
+    A_TRY(h->allocT(&h->gates, T * k));
+    const size_t n_chunks = (T * k + kPermChunk - 1) / kPermChunk;
+    A_TRY(h->allocT(&h->counts, n_chunks * E));
+    A_TRY(h->allocT(&h->base, n_chunks * E));
+    A_TRY(h->allocT(&h->offsets, E + 1));
+    A_TRY(h->allocT(&h->perm_token, T * k));
+    A_TRY(h->allocT(&h->inv, T * k));
+    A_TRY(h->alloc(&h->H, T * k * F * (h->edt == kF32 ? 4 : h->edt == kBF16 ? 2 : 1)));
+    A_TRY(h->allocT(&h->Y, T * k * d));
+    const int ns = lm_head_slices(h->act, h->V);
+    h->hp.n_slices = ns;
+    A_TRY(h->allocT(&h->hp.m, (size_t)h->C * ns));
+    A_TRY(h->allocT(&h->hp.a, (size_t)h->C * ns));
+    A_TRY(h->allocT(&h->hp.s, (size_t)h->C * ns));
+    A_TRY(h->allocT(&h->hp.g, (size_t)h->C * ns));
+    A_TRY(h->allocT(&h->hp.gi, (size_t)h->C * ns));
+    A_TRY(h->allocT(&h->st_m, h->C));
+    A_TRY(h->allocT(&h->st_a, h->C));
+    A_TRY(h->allocT(&h->st_lse, h->C));
+    A_TRY(h->allocT(&h->st_conf, h->C));
+    A_TRY(h->allocT(&h->st_draw, h->C));
+    A_TRY(h->allocT(&h->bad, 1));
+    A_TRY(h->allocT(&h->blk_canvas, h->C));
+    A_TRY(h->allocT(&h->blk_mask, h->C));
+    if (cfg->capture_mask & DG_CAP_LOGITS) A_TRY(h->allocT(&h->logits_cap, (size_t)h->C * V));
+    if (cfg->capture_mask & DG_CAP_ROUTING) {
+        A_TRY(h->allocT(&h->cap_idx, L * h->C * k));
+        A_TRY(h->allocT(&h->cap_gates, L * h->C * k));
+    }
+    if (cfg->capture_mask & DG_CAP_HIDDEN) A_TRY(h->allocT(&h->cap_hidden, L * h->C * d));
+#undef A_TRY
+    *out = h;
+    return DG_OK;
+}
+
+void dg_destroy(dg_handle* h) {
+    if (!h) return;
+    (void)hipDeviceSynchronize();
+    for (void* p : h->allocs) (void)hipFree(p);
+    if (h->stage) (void)hipFree(h->stage);
+    delete h;
+}
+
+static int stage_upload(dg_handle* h, const void* src, size_t bytes, void** dev) {
+    if (bytes > h->stage_bytes) {
+        if (h->stage) (void)hipFree(h->stage);
+        h->stage = nullptr;
+        h->stage_bytes = 0;
+        if (hipMalloc(&h->stage, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(DG_ENOMEM, "staging allocation of %zu bytes failed", bytes);
+        }
+        h->stage_bytes = bytes;
+    }
+    HIP_TRY(hipMemcpy(h->stage, src, bytes, hipMemcpyHostToDevice));
+    *dev = h->stage;
+    return DG_OK;
+}
+
+int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
+                   const void* host_src, size_t bytes, const float* host_scales) {
+    g_err.clear();
+    if (!h || !host_src) return fail(DG_EINVAL, "NULL handle or source");
+    if (kind < DG_T_EMBED || kind > DG_T_WD) return fail(DG_EINVAL, "bad tensor kind %d", kind);
+    const bool is_exp = kind >= DG_T_WG;
+    if (kind != DG_T_EMBED && (layer < 0 || layer >= h->L)) return fail(DG_EINVAL, "bad layer %d", layer);
+    if (is_exp && (expert < -1 || expert >= h->E)) return fail(DG_EINVAL, "bad expert %d", expert);
+    const int dt = is_exp ? h->edt : h->act;
+    const size_t es = dsize(dt);
+    const int nexp = (is_exp && expert < 0) ? h->E : 1;
+    const int e0 = (is_exp && expert >= 0) ? expert : 0;
+    int K = 0, N = 0;
+    switch (kind) {
+        case DG_T_EMBED: K = h->d; N = h->V; break;
+        case DG_T_WQ: K = h->d; N = h->Hq * h->D; break;
+        case DG_T_WK: case DG_T_WV: K = h->d; N = h->Hkv * h->D; break;
+        case DG_T_WO: K = h->Hq * h->D; N = h->d; break;
+        case DG_T_WR: K = h->d; N = h->E; break;
+        case DG_T_WG: case DG_T_WU: K = h->d; N = h->F; break;
+        case DG_T_WD: K = h->F; N = h->d; break;
+    }
+    const size_t per = (size_t)K * N * es;
+    if (bytes != per * nexp)
+        return fail(DG_EINVAL, "tensor kind %d: expected %zu bytes, got %zu", kind, per * nexp, bytes);
+    if (dt == kFP8 && !host_scales) return fail(DG_EINVAL, "e4m3 tensors need column scales");
+    void* src = nullptr;
+    DG_TRY(stage_upload(h, host_src, bytes, &src));
+    hipStream_t s = 0;
+    if (kind == DG_T_EMBED) {
+        if (dt == kF32) HIP_TRY(hipMemcpy(h->embed, src, bytes, hipMemcpyDeviceToDevice));
+        else HIP_TRY(launch_pack_b16(src, false, K, N, 1, 0, h->embed, s));
+        h->loaded[0] = 1;
+    } else if (!is_exp) {
+        void* dst = nullptr;
+        int col0 = 0, ldn = N;
+        if (kind == DG_T_WQ || kind == DG_T_WK || kind == DG_T_WV) {
+            dst = h->wqkv[layer];
+            ldn = h->qkv_n;
+            col0 = kind == DG_T_WQ ? 0 : kind == DG_T_WK ? h->Hq * h->D : (h->Hq + h->Hkv) * h->D;
+        } else if (kind == DG_T_WO) dst = h->wo[layer];
+        else dst = h->wr[layer];
+        if (dt == kF32)
+            HIP_TRY(hipMemcpy2D((float*)dst + col0, (size_t)ldn * 4, src, (size_t)N * 4,
+                                (size_t)N * 4, K, hipMemcpyDeviceToDevice));
+        else
+            HIP_TRY(launch_pack_b16(src, true, K, N, 1, col0 / 16, dst, s));
+        h->dense_flag(layer, kind - DG_T_WQ) = 1;
+    } else {
+        const int which = kind - DG_T_WG;   // 0 gate, 1 up, 2 down
+        std::vector<float> dummy;
+        float* sdev = nullptr;
+        if (dt == kFP8) {
+            // scales are small: upload them through a temporary allocation
+            const size_t sb = (size_t)N * nexp * 4;
+            if (hipMalloc(&sdev, sb) != hipSuccess) return fail(DG_ENOMEM, "scale staging failed");
+            if (hipMemcpy(sdev, host_scales, sb, hipMemcpyHostToDevice) != hipSuccess) {
+                (void)hipFree(sdev);
+                return fail(DG_EHIP, "scale upload failed");
+            }
+        }
+        int rc = DG_OK;
+        for (int i = 0; i < nexp && rc == DG_OK; ++i) {
+            const int e = e0 + i;
+            const char* se = (const char*)src + per * i;
+            hipError_t he = hipSuccess;
+            if (dt == kF32) {
+                void* dst = which == 0 ? h->w1[layer] : which == 1 ? h->wu[layer] : h->w2[layer];
+                he = hipMemcpy((char*)dst + per * e, se, per, hipMemcpyDeviceToDevice);
+            } else if (dt == kBF16) {
+                if (which < 2) {
+                    char* dst = (char*)h->w1[layer] + (size_t)e * 2 * per;
+                    he = launch_pack_b16(se, true, K, N, 2, which, dst, s);
+                } else {
+                    he = launch_pack_b16(se, true, K, N, 1, 0, (char*)h->w2[layer] + per * e, s);
+                }
+            } else {
+                if (which < 2) {
+                    char* dst = (char*)h->w1[layer] + (size_t)e * 2 * per;
+                    he = launch_pack_b8(se, K, N, 2, which, dst, s);
+                    if (he == hipSuccess)
+                        he = launch_scatter_scales(sdev + (size_t)N * i, N, 2, which,
+                                                   h->s1[layer] + (size_t)e * 2 * N, s);
+                } else {
+                    he = launch_pack_b8(se, K, N, 1, 0, (char*)h->w2[layer] + per * e, s);
+                    if (he == hipSuccess)
+                        he = hipMemcpy(h->s2[layer] + (size_t)e * N, sdev + (size_t)N * i,
+                                       (size_t)N * 4, hipMemcpyDeviceToDevice);
+                }
+            }
+            if (he != hipSuccess) rc = fail(DG_EHIP, "expert load failed: %s", hipGetErrorString(he));
+            else h->expert_flag(layer, which, e) = 1;
+        }
+        if (hipDeviceSynchronize() != hipSuccess && rc == DG_OK) rc = fail(DG_EHIP, "load sync failed");
+        if (sdev) (void)hipFree(sdev);
+        return rc;
+    }
+    HIP_TRY(hipDeviceSynchronize());
+    return DG_OK;
+}
+
+int dg_reset_context(dg_handle* h) {
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    h->n_ctx = 0;
+    h->k_blk = 0;
+    h->prefilled = false;
+    return DG_OK;
+}
+
+int dg_get_state(dg_handle* h, int64_t* n_ctx, int32_t* k_blk) {
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    if (n_ctx) *n_ctx = h->n_ctx;
+    if (k_blk) *k_blk = h->k_blk;
+    return DG_OK;
+}
+
+int dg_prefill_prompt_kv(dg_handle* h, const int32_t* d_prompt_ids, int32_t P, void* stream) {
+    g_err.clear();
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    if (P < 0) return fail(DG_EINVAL, "P must be >= 0");
+    if (P > 0 && !d_prompt_ids) return fail(DG_EINVAL, "NULL prompt ids");
+    if ((int64_t)P + h->C > h->max_ctx)
+        return fail(DG_ECAPACITY, "prompt %d plus one canvas %d exceeds max_ctx %lld", P, h->C,
+                    (long long)h->max_ctx);
+    DG_TRY(ensure_ready(h));
+    hipStream_t s = (hipStream_t)stream;
+    for (int c0 = 0; c0 < P; c0 += kPrefillChunk) {
+        const int n = std::min(kPrefillChunk, P - c0);
+        DG_TRY(encode(h, d_prompt_ids + c0, n, c0, s));
+    }
+    h->n_ctx = P;
+    h->k_blk = 0;
+    h->prefilled = true;
+    return DG_OK;
+}
+
+int dg_commit_canvas(dg_handle* h, const int32_t* d_canvas, void* stream) {
+    g_err.clear();
+    if (!h || !d_canvas) return fail(DG_EINVAL, "NULL handle or canvas");
+    if (!h->prefilled) return fail(DG_ESTATE, "commit before prefill");
+    if (h->n_ctx + h->C > h->max_ctx)
+        return fail(DG_ECAPACITY, "commit would exceed max_ctx %lld", (long long)h->max_ctx);
+    DG_TRY(ensure_ready(h));
+    DG_TRY(encode(h, d_canvas, h->C, h->n_ctx, (hipStream_t)stream));
+    h->n_ctx += h->C;
+    h->k_blk += 1;
+    return DG_OK;
+}
+
+int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t step,
+                    int32_t T, uint64_t seed, void* stream) {
+    g_err.clear();
+    if (!h || !d_canvas || !d_locked_mask) return fail(DG_EINVAL, "NULL handle, canvas or mask");
+    if (T <= 0 || step < 0 || step >= T) return fail(DG_EINVAL, "need 0 <= step < T (step %d, T %d)", step, T);
+    if (!h->prefilled) return fail(DG_ESTATE, "denoise step before prefill");
+    if (h->n_ctx + h->C > h->max_ctx)
+        return fail(DG_ECAPACITY, "canvas at %lld exceeds max_ctx %lld", (long long)h->n_ctx,
+                    (long long)h->max_ctx);
+    DG_TRY(ensure_ready(h));
+    hipStream_t s = (hipStream_t)stream;
+    const int C = h->C;
+    K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, C, h->d,
+                               h->cfg.rms_eps, h->x, h->a, s));
+    for (int l = 0; l < h->L; ++l) {
+        DG_TRY(run_layer(h, l, C, h->n_ctx, false, false, s));
+        if (h->cap_idx) {
+            HIP_TRY(hipMemcpyAsync(h->cap_idx + (size_t)l * C * h->k, h->idx,
+                                   (size_t)C * h->k * 4, hipMemcpyDeviceToDevice, s));
+            HIP_TRY(hipMemcpyAsync(h->cap_gates + (size_t)l * C * h->k, h->gates,
+                                   (size_t)C * h->k * 4, hipMemcpyDeviceToDevice, s));
+        }
+        if (h->cap_hidden)
+            HIP_TRY(hipMemcpyAsync(h->cap_hidden + (size_t)l * C * h->d, h->x,
+                                   (size_t)C * h->d * 4, hipMemcpyDeviceToDevice, s));
+    }
+    K_TRY(launch_lm_head(h->act, h->a, C, h->d, h->embed, h->V, 1.0f / h->cfg.temperature,
+                         d_locked_mask, seed, step, h->k_blk, h->hp, h->logits_cap, s));
+    K_TRY(launch_head_stats(h->hp, C, d_locked_mask, h->st_m, h->st_a, h->st_lse, h->st_conf,
+                            h->st_draw, h->bad, s));
+    K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, C, step, T, s));
+    return DG_OK;
+}
+
+static int check_bad(dg_handle* h, hipStream_t s) {
+    int32_t bad = 0;
+    HIP_TRY(hipMemcpyAsync(&bad, h->bad, 4, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    if (bad) {
+        HIP_TRY(launch_fill_u32(h->bad, 0u, 1, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        return fail(DG_ENONFINITE, "non-finite logits statistics");
+    }
+    return DG_OK;
+}
+
+int dg_check_finite(dg_handle* h, void* stream) {
+    g_err.clear();
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    return check_bad(h, (hipStream_t)stream);
+}
+
+int dg_init_canvas(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, uint64_t seed,
+                   void* stream) {
+    g_err.clear();
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    if (!d_canvas && !d_locked_mask) return DG_OK;
+    hipStream_t s = (hipStream_t)stream;
+    K_TRY(launch_canvas_init(d_canvas, d_locked_mask, h->C, h->V, seed, h->k_blk, s));
+    return DG_OK;
+}
+
+int dg_generate_block(dg_handle* h, int32_t* d_out_tokens, int32_t T, uint64_t seed,
+                      int32_t commit, void* stream) {
+    g_err.clear();
+    if (!h || !d_out_tokens) return fail(DG_EINVAL, "NULL handle or output");
+    if (T <= 0) return fail(DG_EINVAL, "T must be > 0");
+    if (!h->prefilled) return fail(DG_ESTATE, "generate before prefill");
+    if (h->n_ctx + h->C > h->max_ctx)
+        return fail(DG_ECAPACITY, "canvas at %lld exceeds max_ctx %lld", (long long)h->n_ctx,
+                    (long long)h->max_ctx);
+    DG_TRY(ensure_ready(h));
+    hipStream_t s = (hipStream_t)stream;
+    K_TRY(launch_canvas_init(h->blk_canvas, h->blk_mask, h->C, h->V, seed, h->k_blk, s));
+    for (int st = 0; st < T; ++st)
+        DG_TRY(dg_denoise_step(h, h->blk_canvas, h->blk_mask, st, T, seed, stream));
+    HIP_TRY(hipMemcpyAsync(d_out_tokens, h->blk_canvas, (size_t)h->C * 4,
+                           hipMemcpyDeviceToDevice, s));
+    if (commit) DG_TRY(dg_commit_canvas(h, h->blk_canvas, stream));
+    return check_bad(h, s);
+}
+
+int dg_get_capture(dg_handle* h, uint32_t what, int32_t layer, void* d_dst, size_t bytes,
+                   void* stream) {
+    g_err.clear();
+    if (!h || !d_dst) return fail(DG_EINVAL, "NULL handle or destination");
+    hipStream_t s = (hipStream_t)stream;
+    const size_t C = h->C;
+    if (what == DG_CAP_STATS) {
+        if (bytes != C * 4 * 5) return fail(DG_EINVAL, "stats capture is %zu bytes", C * 20);
+        char* d = (char*)d_dst;
+        HIP_TRY(hipMemcpyAsync(d, h->st_m, C * 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(d + C * 4, h->st_a, C * 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(d + C * 8, h->st_lse, C * 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(d + C * 12, h->st_conf, C * 4, hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync(d + C * 16, h->st_draw, C * 4, hipMemcpyDeviceToDevice, s));
+        return DG_OK;
+    }
+    if (what == DG_CAP_LOGITS) {
+        if (!h->logits_cap) return fail(DG_ESTATE, "logits capture not enabled");
+        if (bytes != C * h->V * 4) return fail(DG_EINVAL, "logits capture is %zu bytes", C * h->V * 4);
+        HIP_TRY(hipMemcpyAsync(d_dst, h->logits_cap, bytes, hipMemcpyDeviceToDevice, s));
+        return DG_OK;
+    }
+    if (layer < 0 || layer >= h->L) return fail(DG_EINVAL, "bad layer %d", layer);
+    if (what == DG_CAP_ROUTING) {
+        if (!h->cap_idx) return fail(DG_ESTATE, "routing capture not enabled");
+        const size_t n = C * h->k * 4;
+        if (bytes != 2 * n) return fail(DG_EINVAL, "routing capture is %zu bytes", 2 * n);
+        HIP_TRY(hipMemcpyAsync(d_dst, h->cap_idx + (size_t)layer * C * h->k, n,
+                               hipMemcpyDeviceToDevice, s));
+        HIP_TRY(hipMemcpyAsync((char*)d_dst + n, h->cap_gates + (size_t)layer * C * h->k, n,
+                               hipMemcpyDeviceToDevice, s));
+        return DG_OK;
+    }
+    if (what == DG_CAP_HIDDEN) {
+        if (!h->cap_hidden) return fail(DG_ESTATE, "hidden capture not enabled");
+        const size_t n = C * h->d * 4;
+        if (bytes != n) return fail(DG_EINVAL, "hidden capture is %zu bytes", n);
+        HIP_TRY(hipMemcpyAsync(d_dst, h->cap_hidden + (size_t)layer * C * h->d, n,
+                               hipMemcpyDeviceToDevice, s));
+        return DG_OK;
+    }
+    return fail(DG_EINVAL, "unknown capture %u", what);
+}
+
+int dg_get_kv(dg_handle* h, int32_t layer, int32_t which, int64_t row0, int64_t n, void* d_dst,
+              void* stream) {
+    g_err.clear();
+    if (!h || !d_dst) return fail(DG_EINVAL, "NULL handle or destination");
+    if (layer < 0 || layer >= h->L || (which != 0 && which != 1)) return fail(DG_EINVAL, "bad layer or which");
+    if (row0 < 0 || n < 0 || row0 + n > h->kv_rows) return fail(DG_EINVAL, "rows out of range");
+    const bool vp = which == 1 && h->act == kBF16;
+    HIP_TRY(launch_read_kv(h->act, vp, which ? h->vlayer(layer) : h->klayer(layer), h->Hkv, h->D,
+                           h->kv_rows, row0, n, d_dst, (hipStream_t)stream));
+    return DG_OK;
+}
+
+// ---------------------------------------------------------------- kernel-level entry points
+namespace {
+struct AttnWorkspace {
+    void* vt = nullptr;
+    size_t vt_bytes = 0;
+    float* part = nullptr;
+    size_t part_floats = 0;
+};
+std::map<int, AttnWorkspace> g_attn_ws;   // per device; calls on one device must not overlap
+}  // namespace
+
+int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, int32_t Hq,
+                 int32_t Hkv, int32_t M, int32_t S, int32_t D, float scale, int32_t causal,
+                 int32_t q_pos0, int32_t dtype, void* stream) {
+    g_err.clear();
+    if (!d_q || !d_k || !d_v || !d_o) return fail(DG_EINVAL, "NULL tensor");
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || M <= 0 || S <= 0 || D <= 0 || q_pos0 < 0)
+        return fail(DG_EINVAL, "bad attention sizes");
+    if (dtype != DG_F32 && dtype != DG_BF16) return fail(DG_EINVAL, "dtype must be DG_F32 or DG_BF16");
+    if (dtype == DG_F32 && D != 64 && D != 128) return fail(DG_EINVAL, "f32 needs D 64 or 128");
+    if (dtype == DG_BF16 && D != 128) return fail(DG_EINVAL, "bf16 needs D 128");
+    if (causal && (int64_t)q_pos0 + M > S) return fail(DG_EINVAL, "causal queries beyond the keys");
+    hipStream_t s = (hipStream_t)stream;
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    AttnWorkspace& ws = g_attn_ws[dev];
+    AttnArgs aa;
+    aa.q = d_q;
+    aa.k = d_k;
+    aa.v = d_v;
+    aa.o = d_o;
+    aa.Hq = Hq;
+    aa.Hkv = Hkv;
+    aa.M = M;
+    aa.S = S;
+    aa.D = D;
+    aa.kv_rows = S;
+    aa.v_rows = S;
+    aa.scale = scale;
+    aa.causal = causal;
+    aa.q_pos0 = q_pos0;
+    aa.part_ml = nullptr;
+    const int dt = dtype == DG_F32 ? kF32 : kBF16;
+    const size_t pf = (size_t)attention_part_floats(dt, Hq, M, S, D);
+    if (dt == kBF16) {
+        const int64_t rows = ((int64_t)S + 31) & ~(int64_t)31;
+        const size_t vb = (size_t)Hkv * D * rows * 2;
+        if (vb > ws.vt_bytes || pf > ws.part_floats) {
+            HIP_TRY(hipStreamSynchronize(s));
+            if (vb > ws.vt_bytes) {
+                if (ws.vt) (void)hipFree(ws.vt);
+                ws.vt = nullptr;
+                ws.vt_bytes = 0;
+                if (hipMalloc(&ws.vt, vb) != hipSuccess) return fail(DG_ENOMEM, "attention workspace");
+                ws.vt_bytes = vb;
+            }
+            if (pf > ws.part_floats) {
+                if (ws.part) (void)hipFree(ws.part);
+                ws.part = nullptr;
+                ws.part_floats = 0;
+                if (hipMalloc(&ws.part, pf * 4) != hipSuccess) return fail(DG_ENOMEM, "attention workspace");
+                ws.part_floats = pf;
+            }
+        }
+        HIP_TRY(launch_pack_vt(d_v, Hkv, S, D, ws.vt, rows, s));
+        aa.v = ws.vt;
+        aa.v_rows = rows;
+    }
+    aa.part_o = ws.part;
+    aa.part_capacity = (int64_t)ws.part_floats;
+    HIP_TRY(launch_attention(dt, aa, s));
+    return DG_OK;
+}
+
+int dg_moe_layer(dg_handle* h, int32_t layer, const void* d_x, int32_t n_tokens, void* d_y,
+                 int32_t* d_idx, float* d_gates, void* stream) {
+    g_err.clear();
+    if (!h || !d_x || !d_y) return fail(DG_EINVAL, "NULL handle or tensor");
+    if (layer < 0 || layer >= h->L) return fail(DG_EINVAL, "bad layer %d", layer);
+    if (n_tokens <= 0 || n_tokens > h->max_tokens)
+        return fail(DG_EINVAL, "n_tokens must be in [1, %d]", h->max_tokens);
+    for (int kind = 0; kind < 3; ++kind)
+        for (int e = 0; e < h->E; ++e)
+            if (!h->expert_flag(layer, kind, e)) return fail(DG_ESTATE, "experts of layer %d not loaded", layer);
+    if (!h->dense_flag(layer, DG_T_WR - DG_T_WQ)) return fail(DG_ESTATE, "router of layer %d not loaded", layer);
+    hipStream_t s = (hipStream_t)stream;
+    const uint8_t* x8 = nullptr;
+    if (h->edt == kFP8) {
+        K_TRY(launch_cast_e4m3(d_x, (int64_t)n_tokens * h->d, h->a8, s));
+        x8 = h->a8;
+    }
+    DG_TRY(run_moe(h, layer, n_tokens, d_x, x8, s));
+    K_TRY(launch_moe_combine(h->act, 1, h->Y, n_tokens, h->d, h->k, h->gates, h->inv, nullptr,
+                             0.f, nullptr, nullptr, d_y, s));
+    if (d_idx) HIP_TRY(hipMemcpyAsync(d_idx, h->idx, (size_t)n_tokens * h->k * 4, hipMemcpyDeviceToDevice, s));
+    if (d_gates) HIP_TRY(hipMemcpyAsync(d_gates, h->gates, (size_t)n_tokens * h->k * 4, hipMemcpyDeviceToDevice, s));
+    return DG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Kernel launchers of the gfx950 canvas-denoising library (internal interface).
+#pragma once
+
+#include "common.h"
+
+namespace dg {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+constexpr int kFP8 = 2;
+
+constexpr int kPermChunk = 1024;   // entries per permutation workgroup
+constexpr int kMaxCanvas = 1024;   // sampler capacity (one workgroup)
+
+// Transposed, key-permuted V cache: Vt[h][dim][slot], rows padded to a multiple
+// of 32.  Within each 32-key block, key 16*hi + 4*g + j sits at slot 8*g + 4*hi + j,
+// so one 16-byte load gives a lane exactly the 8 keys its MFMA operand needs.
+DG_DEV size_t vt_index(int64_t h, int64_t dim, int64_t pos, int64_t D, int64_t rows) {
+    const int64_t r = pos & 31;
+    const int64_t slot = (pos & ~(int64_t)31) + 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3);
+    return (size_t)((h * D + dim) * rows + slot);
+}
+
+// Per (row, vocabulary slice) partial statistics of the LM head, [C][n_slices] each.
+struct HeadPartials {
+    float* m;       // max tempered logit
+    int32_t* a;     // lowest id attaining it
+    float* s;       // sum exp(z - m)
+    float* g;       // best Gumbel-perturbed score (-inf for locked rows)
+    int32_t* gi;    // its id
+    int n_slices;
+};
+
+// ---------------------------------------------------------------- misc
+hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, const void* E,
+                                int C, int d, float eps, float* x, void* a, hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
+                          uint8_t* a8, hipStream_t s);
+hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int Hkv, int D,
+                               int64_t pos0, const float* cos_t, const float* sin_t, void* q,
+                               void* kc, void* vc, int64_t kv_rows, hipStream_t s);
+hipError_t launch_pack_vt(const void* v, int Hkv, int S, int D, void* vt, int64_t rows,
+                          hipStream_t s);
+hipError_t launch_read_kv(int dtype, bool vpacked, const void* cache, int Hkv, int D,
+                          int64_t rows, int64_t row0, int64_t n, void* dst, hipStream_t s);
+hipError_t launch_router_permute(const float* logits, int M, int E, int k, int32_t* idx,
+                                 float* gates, int32_t* counts, int32_t* base, int32_t* offsets,
+                                 int32_t* perm_token, int32_t* inv, hipStream_t s);
+hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
+                              const float* gates, const int32_t* inv, float* x, float eps,
+                              void* a, uint8_t* a8, void* out, hipStream_t s);
+hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint64_t seed,
+                              int k_blk, hipStream_t s);
+hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, float* st_m,
+                             int32_t* st_a, float* st_lse, float* st_conf, int32_t* st_draw,
+                             int32_t* bad, hipStream_t s);
+hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t* draw,
+                          int32_t* canvas, uint8_t* mask, int C, int step, int T, hipStream_t s);
+hipError_t launch_pack_b16(const void* src, bool src_kn, int K, int N, int gstride, int goff,
+                           void* dst, hipStream_t s);
+hipError_t launch_pack_b8(const void* src, int K, int N, int gstride, int goff, void* dst,
+                          hipStream_t s);
+hipError_t launch_scatter_scales(const float* src, int N, int gstride, int goff, float* dst,
+                                 hipStream_t s);
+hipError_t launch_fill_u32(void* p, uint32_t v, int64_t n, hipStream_t s);
+hipError_t launch_cast_e4m3(const void* x_bf16, int64_t n, uint8_t* out, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMMs
+// Epilogue modes of the dense GEMM.
+constexpr int kEpiStoreF32 = 0;   // C[m, n] = acc
+constexpr int kEpiAddF32 = 1;     // C[m, n] += acc (residual add, single writer)
+
+// C = A[M, K] B[K, N].  bf16: A row-major (lda), B packed (see packed_b_index).
+// f32: A row-major, B row-major [K, N].
+hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const void* B, int K,
+                       int N, float* C, int ldc, hipStream_t s);
+
+// Expert GEMMs over the permuted entries (offsets[e]..offsets[e+1] belong to expert e).
+// GEMM 1: H[entry, :F] = silu(x Wg_e) * (x Wu_e), x = X[perm_token[entry]].
+//   bf16: X bf16 [*, d], W1 packed with interleaved gate/up groups, H bf16.
+//   fp8 : X e4m3 [*, d], W1 packed e4m3 + column scales (2F), H e4m3.
+//   f32 : X f32, Wg/Wu row-major [E][d][F], H f32.
+// GEMM 2: Y[entry, :d] = H[entry] Wd_e (float).
+struct ExpertWeights {
+    const void* w1;        // bf16/fp8 packed gate|up, or f32 Wg
+    const void* wu;        // f32 Wu (f32 path only)
+    const void* w2;        // down projection (packed or row-major)
+    const float* s1;       // fp8 column scales of w1 [E][2F] (interleaved)
+    const float* s2;       // fp8 column scales of w2 [E][d]
+};
+hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
+                            const int32_t* perm_token, const int32_t* offsets, int E, int d,
+                            int F, int max_rows, void* H, hipStream_t s);
+hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
+                            const int32_t* offsets, int E, int d, int F, int max_rows, float* Y,
+                            hipStream_t s);
+
+// LM head: per (row, slice) partial max / argmax / sum-exp / Gumbel best of
+// z = (h E^T) / tau over the vocabulary.  Gumbel noise for rows with mask == 0.
+hipError_t launch_lm_head(int dtype, const void* h, int C, int d, const void* E, int V,
+                          float inv_tau, const uint8_t* mask, uint64_t seed, int step, int k_blk,
+                          const HeadPartials& p, float* logits_out, hipStream_t s);
+int lm_head_slices(int dtype, int V);
+
+// ---------------------------------------------------------------- attention
+// q [Hq][M][D]; K [Hkv][rows][D]; V natural [Hkv][rows][D] (f32) or
+// transposed-permuted (bf16, vt_index); O [M][Hq*D].  Keys 0..S-1.
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int Hq, Hkv, M, S, D;
+    int64_t kv_rows;       // row capacity per head of K (and of f32 V)
+    int64_t v_rows;        // row capacity per head of the bf16 transposed V (multiple of 32)
+    float scale;
+    int causal;
+    int64_t q_pos0;
+    float* part_o;         // split partials workspace
+    float* part_ml;
+    int64_t part_capacity; // floats available in part_o
+};
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
+int64_t attention_part_floats(int dtype, int Hq, int M, int S, int D);
+
+}  // namespace dg

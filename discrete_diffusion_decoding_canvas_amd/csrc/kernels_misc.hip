@@ -1,0 +1,621 @@
+// Element-wise, routing, permutation, statistics and sampler kernels (gfx950).
+//
+// Method steps (DiffusionGemma technical-report summary, Method; alphasignal
+// "How text diffusion actually works"):
+//   canvas embedding + RMSNorm, RoPE and K/V cache write, top-k router,
+//   per-expert token permutation, weighted expert combine + residual,
+//   per-position LM-head statistics, and the lock / redraw sampler.
+#include "kernels.h"
+
+namespace dg {
+
+// Packed MFMA B-operand index of logical element (n, k) of a K x N matrix:
+// [N/16][K/32][64 lanes][8], lane = n%16 + 16*((k%32)/8), element k%8.
+DG_DEV size_t packed_b_index(int64_t n, int64_t k, int64_t K) {
+    return ((size_t)((n >> 4) * (K >> 5) + (k >> 5)) << 9) +
+           ((size_t)((n & 15) + (((k & 31) >> 3) << 4)) << 3) + (size_t)(k & 7);
+}
+
+// ------------------------------------------------------------------ block reductions
+template <int NT>
+DG_DEV float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t += red[i];
+    return t;
+}
+
+// ------------------------------------------------------------------ embed + RMSNorm
+// x[i, :] = E[canvas[i], :] (float residual), a[i, :] = rmsnorm(x[i, :]).
+template <typename T, bool PACKED>
+__global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict__ tokens,
+                                                       const T* __restrict__ E, int d,
+                                                       float eps, float* __restrict__ x,
+                                                       T* __restrict__ a) {
+    __shared__ float red[4];
+    const int i = blockIdx.x;
+    const int64_t v = tokens[i];
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < d; c += 256) {
+        float e = PACKED ? to_f32<T>(E[packed_b_index(v, c, d)]) : to_f32<T>(E[v * d + c]);
+        x[(int64_t)i * d + c] = e;
+        ss += e * e;
+    }
+    float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
+    for (int c = threadIdx.x; c < d; c += 256)
+        a[(int64_t)i * d + c] = from_f32<T>(x[(int64_t)i * d + c] * r);
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// a = rmsnorm(x) (unit gains); a8 (optional) = e4m3(a) for fp8 expert inputs.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int d, float eps,
+                                                 T* __restrict__ a, uint8_t* __restrict__ a8) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * d;
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < d; c += 256) ss += xr[c] * xr[c];
+    float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
+    for (int c = threadIdx.x; c < d; c += 256) {
+        T av = from_f32<T>(xr[c] * r);
+        a[row * d + c] = av;
+        if (a8) a8[row * d + c] = (uint8_t)f32_to_e4m3(to_f32<T>(av));
+    }
+}
+
+// ------------------------------------------------------------------ RoPE + scatter
+// qkv float [M, (Hq + 2 Hkv) D] -> Q [Hq][M][D] rotated, K cache rows pos0+m rotated,
+// V cache rows pos0+m.  Rotate-half pairs (j, j + D/2), angle table [pos][D/2].
+// bf16 V is stored transposed and key-permuted for the attention MFMA (vt_index).
+template <typename T, bool VPACKED>
+__global__ void k_rope_scatter(const float* __restrict__ qkv, int M, int Hq, int Hkv, int D,
+                               int64_t pos0, const float* __restrict__ cos_t,
+                               const float* __restrict__ sin_t, T* __restrict__ q,
+                               T* __restrict__ kc, T* __restrict__ vc, int64_t kv_rows) {
+    const int m = blockIdx.x;
+    const int head = blockIdx.y;           // 0..Hq-1 queries, Hq..Hq+Hkv-1 keys, then values
+    const int half = D >> 1;
+    const int64_t pos = pos0 + m;
+    const float* src = qkv + (int64_t)m * (Hq + 2 * Hkv) * D + (int64_t)head * D;
+    for (int j = threadIdx.x; j < half; j += blockDim.x) {
+        float x1 = src[j], x2 = src[j + half];
+        if (head < Hq + Hkv) {
+            float c = cos_t[pos * half + j], s = sin_t[pos * half + j];
+            float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
+            if (head < Hq) {
+                T* dst = q + ((int64_t)head * M + m) * D;
+                dst[j] = from_f32<T>(y1);
+                dst[j + half] = from_f32<T>(y2);
+            } else {
+                T* dst = kc + ((int64_t)(head - Hq) * kv_rows + pos) * D;
+                dst[j] = from_f32<T>(y1);
+                dst[j + half] = from_f32<T>(y2);
+            }
+        } else {
+            const int h = head - Hq - Hkv;
+            if (VPACKED) {
+                vc[vt_index(h, j, pos, D, kv_rows)] = from_f32<T>(x1);
+                vc[vt_index(h, j + half, pos, D, kv_rows)] = from_f32<T>(x2);
+            } else {
+                T* dst = vc + ((int64_t)h * kv_rows + pos) * D;
+                dst[j] = from_f32<T>(x1);
+                dst[j + half] = from_f32<T>(x2);
+            }
+        }
+    }
+}
+
+// Natural [Hkv][S][D] V -> transposed key-permuted layout (for the attention entry point).
+__global__ void k_pack_vt(const bf16_t* __restrict__ v, int Hkv, int S, int D,
+                          bf16_t* __restrict__ vt, int64_t rows) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)Hkv * rows * D;
+    if (idx >= total) return;
+    const int t = (int)(idx % D);
+    const int64_t p = (idx / D) % rows;
+    const int h = (int)(idx / ((int64_t)D * rows));
+    vt[vt_index(h, t, p, D, rows)] = p < S ? v[((int64_t)h * S + p) * D + t] : (bf16_t)0;
+}
+
+// K/V read-back in natural [Hkv][n][D] layout (debug / tests).
+template <typename T, bool VPACKED>
+__global__ void k_read_kv(const T* __restrict__ cache, int Hkv, int D, int64_t rows,
+                          int64_t row0, int64_t n, T* __restrict__ dst) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)Hkv * n * D) return;
+    const int t = (int)(idx % D);
+    const int64_t p = (idx / D) % n;
+    const int h = (int)(idx / ((int64_t)D * n));
+    dst[idx] = VPACKED ? cache[vt_index(h, t, row0 + p, D, rows)]
+                       : cache[((int64_t)h * rows + row0 + p) * D + t];
+}
+
+// ------------------------------------------------------------------ router top-k
+// One wave per token: rank logits (descending, ties to the lower expert id),
+// gates = softmax over the k chosen logits (= p_e / sum of chosen p).
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int M,
+                                                     int E, int k, int32_t* __restrict__ idx,
+                                                     float* __restrict__ gates) {
+    const int wave = (blockIdx.x * 4) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wave >= M) return;
+    const float* r = logits + (int64_t)wave * E;
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        int e = lane + 64 * q;
+        v[q] = e < E ? r[e] : -INFINITY;
+    }
+    float sel_v[16];
+    int sel_e[16];
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int e = lane + 64 * q;
+            if (e < E && (v[q] > bv || (v[q] == bv && e < be))) { bv = v[q]; be = e; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            float ov = __shfl_xor(bv, o, 64);
+            int oe = __shfl_xor(be, o, 64);
+            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        }
+        sel_v[j] = bv;
+        sel_e[j] = be;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane + 64 * q == be) v[q] = -INFINITY;
+    }
+    if (lane == 0) {
+        float mx = sel_v[0], s = 0.f;
+        for (int j = 0; j < k; ++j) s += expf(sel_v[j] - mx);
+        for (int j = 0; j < k; ++j) {
+            idx[(int64_t)wave * k + j] = sel_e[j];
+            gates[(int64_t)wave * k + j] = expf(sel_v[j] - mx) / s;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ permutation
+// Entries are (token, slot) pairs, flat id = token * k + slot, grouped by expert,
+// stable in flat id.  Chunks of kPermChunk entries per workgroup.
+__global__ __launch_bounds__(256) void k_moe_count(const int32_t* __restrict__ idx, int n,
+                                                   int E, int32_t* __restrict__ counts) {
+    extern __shared__ int32_t cnt[];
+    for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+    __syncthreads();
+    const int base = blockIdx.x * kPermChunk;
+    for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+        int f = base + i;
+        if (f < n) atomicAdd(&cnt[idx[f]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// One workgroup: base[c][e] = offset[e] + sum_{c' < c} counts[c'][e];
+// offsets[e] = exclusive scan of per-expert totals, offsets[E] = n.
+__global__ __launch_bounds__(1024) void k_moe_scan(const int32_t* __restrict__ counts,
+                                                   int n_chunks, int E,
+                                                   int32_t* __restrict__ base,
+                                                   int32_t* __restrict__ offsets) {
+    extern __shared__ int32_t tot[];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int c = 0; c < n_chunks; ++c) {
+            base[(int64_t)c * E + e] = run;
+            run += counts[(int64_t)c * E + e];
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            int t = tot[e];
+            tot[e] = run;
+            offsets[e] = run;
+            run += t;
+        }
+        offsets[E] = run;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        for (int c = 0; c < n_chunks; ++c) base[(int64_t)c * E + e] += tot[e];
+}
+
+__global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__ idx, int n,
+                                                     int E, int k,
+                                                     const int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ perm_token,
+                                                     int32_t* __restrict__ inv) {
+    __shared__ int32_t ex[kPermChunk];
+    const int c0 = blockIdx.x * kPermChunk;
+    for (int i = threadIdx.x; i < kPermChunk; i += 256)
+        ex[i] = (c0 + i < n) ? idx[c0 + i] : -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+        const int e = ex[i];
+        if (e < 0) continue;
+        int rank = 0;
+        for (int j = 0; j < i; ++j) rank += (ex[j] == e);
+        const int pos = base[(int64_t)blockIdx.x * E + e] + rank;
+        perm_token[pos] = (c0 + i) / k;
+        inv[c0 + i] = pos;
+    }
+}
+
+// ------------------------------------------------------------------ combine (+ RMSNorm)
+// y = sum_j gates[t, j] * Y[inv[t*k + j], :] in slot order.
+// MODE 0: x += y, then a = rmsnorm(x) (and a8 = e4m3(a) if given) when a != null.
+// MODE 1: out = y (stored as T), no residual (the stand-alone MoE layer).
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y, int d, int k,
+                                                     const float* __restrict__ gates,
+                                                     const int32_t* __restrict__ inv,
+                                                     float* __restrict__ x, float eps,
+                                                     T* __restrict__ a, uint8_t* __restrict__ a8,
+                                                     T* __restrict__ out) {
+    __shared__ float red[4];
+    __shared__ float g_s[16];
+    __shared__ int32_t r_s[16];
+    const int64_t t = blockIdx.x;
+    if (threadIdx.x < k) {
+        g_s[threadIdx.x] = gates[t * k + threadIdx.x];
+        r_s[threadIdx.x] = inv[t * k + threadIdx.x];
+    }
+    __syncthreads();
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < d; c += 256) {
+        float y = 0.f;
+        for (int j = 0; j < k; ++j) y += g_s[j] * Y[(int64_t)r_s[j] * d + c];
+        if (MODE == 0) {
+            float nx = x[t * d + c] + y;
+            x[t * d + c] = nx;
+            ss += nx * nx;
+        } else {
+            out[t * d + c] = from_f32<T>(y);
+        }
+    }
+    if (MODE == 0 && a != nullptr) {
+        float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
+        for (int c = threadIdx.x; c < d; c += 256) {
+            T av = from_f32<T>(x[t * d + c] * r);
+            a[t * d + c] = av;
+            if (a8) a8[t * d + c] = (uint8_t)f32_to_e4m3(to_f32<T>(av));
+        }
+    }
+}
+
+// ------------------------------------------------------------------ canvas init
+__global__ void k_canvas_init(int32_t* __restrict__ canvas, uint8_t* __restrict__ mask, int C,
+                              int V, uint64_t seed, int k_blk) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= C) return;
+    u32x4 c = {(uint32_t)(i >> 2), (uint32_t)k_blk, 0u, kInitTag};
+    u32x4 r = philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    uint32_t w = (i & 3) == 0 ? r.x : (i & 3) == 1 ? r.y : (i & 3) == 2 ? r.z : r.w;
+    if (canvas) canvas[i] = (int32_t)(((uint64_t)w * (uint64_t)V) >> 32);
+    if (mask) mask[i] = 0;
+}
+
+// ------------------------------------------------------------------ LM-head statistics
+// Reduce the per-slice partials of one row in a fixed tree: max with the
+// lowest id on ties, sum of exp(z - max), Gumbel best with the lowest id on ties.
+struct HeadPart { float m; int32_t a; float s; float g; int32_t gi; };
+
+DG_DEV void head_merge(HeadPart& x, const HeadPart& y) {
+    if (y.m > x.m || (y.m == x.m && y.a < x.a)) {
+        float sx = (x.m == -INFINITY) ? 0.f : x.s * exp2f((x.m - y.m) * 1.4426950408889634f);
+        x.s = y.s + sx;
+        x.m = y.m;
+        x.a = y.a;
+    } else {
+        float sy = (y.m == -INFINITY) ? 0.f : y.s * exp2f((y.m - x.m) * 1.4426950408889634f);
+        x.s += sy;
+    }
+    if (y.g > x.g || (y.g == x.g && y.gi < x.gi)) { x.g = y.g; x.gi = y.gi; }
+}
+
+__global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm,
+                                                    const int32_t* __restrict__ pa,
+                                                    const float* __restrict__ ps,
+                                                    const float* __restrict__ pg,
+                                                    const int32_t* __restrict__ pgi,
+                                                    int n_slices, const uint8_t* __restrict__ mask,
+                                                    float* __restrict__ st_m,
+                                                    int32_t* __restrict__ st_a,
+                                                    float* __restrict__ st_lse,
+                                                    float* __restrict__ st_conf,
+                                                    int32_t* __restrict__ st_draw,
+                                                    int32_t* __restrict__ bad) {
+    __shared__ HeadPart sh[256];
+    const int row = blockIdx.x;
+    HeadPart acc = {-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff};
+    for (int i = threadIdx.x; i < n_slices; i += 256) {
+        const int64_t o = (int64_t)row * n_slices + i;
+        HeadPart p = {pm[o], pa[o], ps[o], pg[o], pgi[o]};
+        head_merge(acc, p);
+    }
+    sh[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (threadIdx.x < w) {
+            HeadPart a = sh[threadIdx.x];
+            head_merge(a, sh[threadIdx.x + w]);
+            sh[threadIdx.x] = a;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        HeadPart r = sh[0];
+        const float ls = logf(r.s);
+        st_m[row] = r.m;
+        st_a[row] = r.a;
+        st_lse[row] = r.m + ls;
+        st_conf[row] = -ls;
+        st_draw[row] = mask[row] ? -1 : r.gi;
+        if (!isfinite(r.m) || !isfinite(ls) || (!mask[row] && r.gi < 0)) atomicOr(bad, 1);
+    }
+}
+
+// ------------------------------------------------------------------ sampler
+// One workgroup.  Among unlocked positions, the n_s with the highest
+// confidence (ties to the lower position) are locked to their argmax; the
+// other unlocked positions take their Gumbel draw.  Locked ones are untouched.
+__global__ __launch_bounds__(1024) void k_sampler(const float* __restrict__ conf,
+                                                  const int32_t* __restrict__ amax,
+                                                  const int32_t* __restrict__ draw,
+                                                  int32_t* __restrict__ canvas,
+                                                  uint8_t* __restrict__ mask, int C, int step,
+                                                  int T) {
+    __shared__ float cf[kMaxCanvas];
+    __shared__ uint8_t un[kMaxCanvas];
+    __shared__ int n_unl;
+    if (threadIdx.x == 0) n_unl = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int i = threadIdx.x; i < C; i += blockDim.x) {
+        cf[i] = conf[i];
+        un[i] = mask[i] == 0;
+        mine += un[i];
+    }
+    atomicAdd(&n_unl, mine);
+    __syncthreads();
+    const int nu = n_unl;
+    const int quota = (C + T - 1) / T;
+    const int n_s = (step == T - 1) ? nu : (quota < nu ? quota : nu);
+    for (int i = threadIdx.x; i < C; i += blockDim.x) {
+        if (!un[i]) continue;
+        const float ci = cf[i];
+        int rank = 0;
+        for (int j = 0; j < C; ++j)
+            rank += un[j] && (cf[j] > ci || (cf[j] == ci && j < i));
+        if (rank < n_s) {
+            canvas[i] = amax[i];
+            mask[i] = 1;
+        } else {
+            canvas[i] = draw[i];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ weight packing
+// src [K][N] (SRC_KN) or [N][K] (!SRC_KN), 16-bit elements -> packed B operand.
+// The destination column group of source group g is g * gstride + goff (the
+// gate / up interleave of the first expert GEMM uses gstride 2).
+template <bool SRC_KN>
+__global__ void k_pack_b16(const uint16_t* __restrict__ src, int K, int N, int gstride, int goff,
+                           uint16_t* __restrict__ dst) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)K * N) return;
+    int64_t n, kk;
+    if (SRC_KN) { kk = idx / N; n = idx % N; } else { n = idx / K; kk = idx % K; }
+    const int64_t dn = ((n >> 4) * gstride + goff) * 16 + (n & 15);
+    dst[packed_b_index(dn, kk, K)] = src[idx];
+}
+
+// e4m3 codes [K][N] -> packed [N/16][K/64][64 lanes][16 bytes]; byte b < 8 holds
+// k = 64*kb + 8*(lane/16) + b, byte b >= 8 holds k = 64*kb + 32 + 8*(lane/16) + b - 8.
+__global__ void k_pack_b8(const uint8_t* __restrict__ src, int K, int N, int gstride, int goff,
+                          uint8_t* __restrict__ dst) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)K * N) return;
+    const int64_t kk = idx / N, n = idx % N;
+    const int64_t dn = ((n >> 4) * gstride + goff) * 16 + (n & 15);
+    const int64_t kb = kk >> 6, r = kk & 63;
+    const int half = (int)(r >> 5), g = (int)((r & 31) >> 3), b = (int)(r & 7);
+    const int lane = (int)(dn & 15) + 16 * g;
+    dst[((((dn >> 4) * (K >> 6) + kb) * 64 + lane) << 4) + half * 8 + b] = src[idx];
+}
+
+// Column scales of the interleaved gate/up weights follow the same group map.
+__global__ void k_scatter_scales(const float* __restrict__ src, int N, int gstride, int goff,
+                                 float* __restrict__ dst) {
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    dst[((n >> 4) * gstride + goff) * 16 + (n & 15)] = src[n];
+}
+
+__global__ void k_cast_e4m3(const bf16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = (uint8_t)f32_to_e4m3(bf16_to_f32(x[i]));
+}
+
+__global__ void k_fill_u32(uint32_t* p, uint32_t v, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// ================================================================== launchers
+#define LAUNCH_CHECK() return hipGetLastError()
+
+hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, const void* E,
+                                int C, int d, float eps, float* x, void* a, hipStream_t s) {
+    if (dtype == kF32)
+        k_embed_rmsnorm<float, false><<<C, 256, 0, s>>>(tokens, (const float*)E, d, eps, x,
+                                                        (float*)a);
+    else if (packed)
+        k_embed_rmsnorm<bf16_t, true><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, d, eps, x,
+                                                        (bf16_t*)a);
+    else
+        k_embed_rmsnorm<bf16_t, false><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, d, eps, x,
+                                                         (bf16_t*)a);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
+                          uint8_t* a8, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (dtype == kF32)
+        k_rmsnorm<float><<<M, 256, 0, s>>>(x, d, eps, (float*)a, a8);
+    else
+        k_rmsnorm<bf16_t><<<M, 256, 0, s>>>(x, d, eps, (bf16_t*)a, a8);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int Hkv, int D,
+                               int64_t pos0, const float* cos_t, const float* sin_t, void* q,
+                               void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    dim3 grid(M, Hq + 2 * Hkv);
+    int threads = D / 2 < 64 ? 64 : D / 2;
+    if (dtype == kF32)
+        k_rope_scatter<float, false><<<grid, threads, 0, s>>>(
+            qkv, M, Hq, Hkv, D, pos0, cos_t, sin_t, (float*)q, (float*)kc, (float*)vc, kv_rows);
+    else
+        k_rope_scatter<bf16_t, true><<<grid, threads, 0, s>>>(
+            qkv, M, Hq, Hkv, D, pos0, cos_t, sin_t, (bf16_t*)q, (bf16_t*)kc, (bf16_t*)vc,
+            kv_rows);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_pack_vt(const void* v, int Hkv, int S, int D, void* vt, int64_t rows,
+                          hipStream_t s) {
+    int64_t total = (int64_t)Hkv * rows * D;
+    k_pack_vt<<<(unsigned)((total + 255) / 256), 256, 0, s>>>((const bf16_t*)v, Hkv, S, D,
+                                                              (bf16_t*)vt, rows);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_read_kv(int dtype, bool vpacked, const void* cache, int Hkv, int D,
+                          int64_t rows, int64_t row0, int64_t n, void* dst, hipStream_t s) {
+    int64_t total = (int64_t)Hkv * n * D;
+    if (total <= 0) return hipSuccess;
+    unsigned blocks = (unsigned)((total + 255) / 256);
+    if (dtype == kF32)
+        k_read_kv<float, false><<<blocks, 256, 0, s>>>((const float*)cache, Hkv, D, rows, row0,
+                                                       n, (float*)dst);
+    else if (vpacked)
+        k_read_kv<bf16_t, true><<<blocks, 256, 0, s>>>((const bf16_t*)cache, Hkv, D, rows, row0,
+                                                       n, (bf16_t*)dst);
+    else
+        k_read_kv<bf16_t, false><<<blocks, 256, 0, s>>>((const bf16_t*)cache, Hkv, D, rows,
+                                                        row0, n, (bf16_t*)dst);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_router_permute(const float* logits, int M, int E, int k, int32_t* idx,
+                                 float* gates, int32_t* counts, int32_t* base, int32_t* offsets,
+                                 int32_t* perm_token, int32_t* inv, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, M, E, k, idx, gates);
+    const int n = M * k;
+    const int n_chunks = (n + kPermChunk - 1) / kPermChunk;
+    k_moe_count<<<n_chunks, 256, E * sizeof(int32_t), s>>>(idx, n, E, counts);
+    k_moe_scan<<<1, 1024, E * sizeof(int32_t), s>>>(counts, n_chunks, E, base, offsets);
+    k_moe_scatter<<<n_chunks, 256, 0, s>>>(idx, n, E, k, base, perm_token, inv);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
+                              const float* gates, const int32_t* inv, float* x, float eps,
+                              void* a, uint8_t* a8, void* out, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (dtype == kF32) {
+        if (mode == 0)
+            k_moe_combine<float, 0><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, (float*)a, a8,
+                                                      nullptr);
+        else
+            k_moe_combine<float, 1><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, nullptr,
+                                                      nullptr, (float*)out);
+    } else {
+        if (mode == 0)
+            k_moe_combine<bf16_t, 0><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, (bf16_t*)a,
+                                                       a8, nullptr);
+        else
+            k_moe_combine<bf16_t, 1><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, nullptr,
+                                                       nullptr, (bf16_t*)out);
+    }
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint64_t seed,
+                              int k_blk, hipStream_t s) {
+    k_canvas_init<<<(C + 255) / 256, 256, 0, s>>>(canvas, mask, C, V, seed, k_blk);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, float* st_m,
+                             int32_t* st_a, float* st_lse, float* st_conf, int32_t* st_draw,
+                             int32_t* bad, hipStream_t s) {
+    k_head_stats<<<C, 256, 0, s>>>(p.m, p.a, p.s, p.g, p.gi, p.n_slices, mask, st_m, st_a,
+                                   st_lse, st_conf, st_draw, bad);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t* draw,
+                          int32_t* canvas, uint8_t* mask, int C, int step, int T,
+                          hipStream_t s) {
+    k_sampler<<<1, 1024, 0, s>>>(conf, amax, draw, canvas, mask, C, step, T);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_pack_b16(const void* src, bool src_kn, int K, int N, int gstride, int goff,
+                           void* dst, hipStream_t s) {
+    int64_t total = (int64_t)K * N;
+    unsigned blocks = (unsigned)((total + 255) / 256);
+    if (src_kn)
+        k_pack_b16<true><<<blocks, 256, 0, s>>>((const uint16_t*)src, K, N, gstride, goff,
+                                                (uint16_t*)dst);
+    else
+        k_pack_b16<false><<<blocks, 256, 0, s>>>((const uint16_t*)src, K, N, gstride, goff,
+                                                 (uint16_t*)dst);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_pack_b8(const void* src, int K, int N, int gstride, int goff, void* dst,
+                          hipStream_t s) {
+    int64_t total = (int64_t)K * N;
+    k_pack_b8<<<(unsigned)((total + 255) / 256), 256, 0, s>>>((const uint8_t*)src, K, N,
+                                                              gstride, goff, (uint8_t*)dst);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_scatter_scales(const float* src, int N, int gstride, int goff, float* dst,
+                                 hipStream_t s) {
+    k_scatter_scales<<<(N + 255) / 256, 256, 0, s>>>(src, N, gstride, goff, dst);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_fill_u32(void* p, uint32_t v, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    k_fill_u32<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((uint32_t*)p, v, n);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_cast_e4m3(const void* x, int64_t n, uint8_t* out, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    k_cast_e4m3<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const bf16_t*)x, n, out);
+    LAUNCH_CHECK();
+}
+
+}  // namespace dg

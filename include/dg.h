@@ -1,0 +1,233 @@
+/*
+ * dg.h — C ABI of the MI355X (gfx950) canvas-denoising library (libdg.so).
+ *
+ * The library runs the parallel canvas-denoising step of block discrete
+ * diffusion as described for DiffusionGemma:
+ *   - "DiffusionGemma" technical-report summary (hyper.ai paper page),
+ *     section Method: the three-stage generation pipeline (causal encoder
+ *     fills the KV cache from the prompt; the decoder refines a noisy canvas
+ *     with bidirectional attention across the canvas and attention to the KV
+ *     cache; the finished canvas goes back through the encoder and is
+ *     appended to the cache), the decoder logits equation L_t in R^{C x V},
+ *     and the update equations (tempered softmax, Step map);
+ *   - same page, section Dataset, "Example and sequence structure": the
+ *     P + K*C layout of prompt tokens and canvases;
+ *   - "Google's DiffusionGemma Generates 256 Tokens at Once" (alphasignal),
+ *     "How text diffusion actually works": canvas initialised with random
+ *     tokens, passes that lock high-confidence tokens and refine the rest,
+ *     convergence after T passes.
+ *
+ * Conventions
+ *   - Every function returns DG_OK (0) or a negative status; the message of
+ *     the last failure on the calling thread is in dg_last_error().
+ *   - Argument errors are detected before any work is enqueued and leave the
+ *     handle unchanged.
+ *   - Work is enqueued asynchronously on the caller's HIP stream (a
+ *     hipStream_t passed as void*, NULL = the default stream).  No call
+ *     synchronises the host except dg_load_tensor (which copies from host
+ *     memory) and the entry points documented as synchronous.
+ *   - Pointers prefixed d_ are device pointers owned by the caller; they must
+ *     stay valid until the enqueued work completes.  Host pointers are read
+ *     before the call returns.
+ *   - The handle owns weights, the KV cache and all workspace (device memory
+ *     allocated in dg_create).  A handle is not thread-safe: use it from one
+ *     host thread and one stream at a time.
+ *   - Token ids are int32 in [0, vocab); lock masks are uint8 in {0, 1}.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define DG_OK 0
+#define DG_EINVAL (-1)      /* bad argument: null pointer, out-of-range value, size mismatch */
+#define DG_ENOMEM (-2)      /* device allocation failed */
+#define DG_EHIP (-3)        /* a HIP runtime call failed (message has the HIP error) */
+#define DG_ECAPACITY (-4)   /* the KV cache cannot hold n_ctx + canvas rows */
+#define DG_ESTATE (-5)      /* call out of order: no prompt prefilled, weights missing */
+#define DG_ENONFINITE (-6)  /* non-finite logits statistics were produced */
+
+/* ---------------------------------------------------------------- dtypes */
+#define DG_F32 0
+#define DG_BF16 1
+#define DG_FP8_E4M3 2       /* OCP FP8 E4M3 (bias 7, max 448); expert weights only */
+
+/* ---------------------------------------------------------------- tensors
+ * Logical layouts are [in, out] row-major (y = x W):
+ *   DG_T_EMBED [V, d]        token embedding, also the tied LM head (logits = h E^T)
+ *   DG_T_WQ    [d, Hq*D]     query projection
+ *   DG_T_WK    [d, Hkv*D]    key projection
+ *   DG_T_WV    [d, Hkv*D]    value projection
+ *   DG_T_WO    [Hq*D, d]     attention output projection
+ *   DG_T_WR    [d, E]        router
+ *   DG_T_WG    [d, F]        expert gate projection (one expert)
+ *   DG_T_WU    [d, F]        expert up projection   (one expert)
+ *   DG_T_WD    [F, d]        expert down projection (one expert)
+ * Element type: act_dtype for the non-expert tensors, expert_dtype for
+ * DG_T_WG / DG_T_WU / DG_T_WD.  bf16 is passed as its 16-bit pattern,
+ * e4m3 as its 8-bit code plus one float scale per output column. */
+#define DG_T_EMBED 0
+#define DG_T_WQ 1
+#define DG_T_WK 2
+#define DG_T_WV 3
+#define DG_T_WO 4
+#define DG_T_WR 5
+#define DG_T_WG 6
+#define DG_T_WU 7
+#define DG_T_WD 8
+
+/* ---------------------------------------------------------------- captures
+ * Debug captures of the last dg_denoise_step, enabled per handle by
+ * capture_mask.  Layouts:
+ *   DG_CAP_LOGITS   float [C, V] tempered logits of the last pass
+ *   DG_CAP_STATS    per position, 5 arrays of C elements in this order:
+ *                   float m (max tempered logit), int32 argmax,
+ *                   float lse, float conf (= m - lse), int32 redraw token
+ *                   (-1 where the position was locked on entry)
+ *   DG_CAP_ROUTING  per layer: int32 idx [C, k] then float gates [C, k]
+ *   DG_CAP_HIDDEN   per layer: float residual stream [C, d] after the layer
+ */
+#define DG_CAP_LOGITS 1u
+#define DG_CAP_STATS 2u
+#define DG_CAP_ROUTING 4u
+#define DG_CAP_HIDDEN 8u
+
+typedef struct dg_model_cfg {
+    int32_t n_layers;      /* L */
+    int32_t d_model;       /* d, multiple of 32 for bf16/fp8 */
+    int32_t n_q_heads;     /* Hq, multiple of n_kv_heads */
+    int32_t n_kv_heads;    /* Hkv */
+    int32_t head_dim;      /* D: 64 or 128 (bf16 path: 128) */
+    int32_t n_experts;     /* E */
+    int32_t top_k;         /* k <= E, k <= 16 */
+    int32_t d_ff;          /* F, expert hidden width, multiple of 32 for bf16/fp8 */
+    int32_t vocab;         /* V, multiple of 16 */
+    int32_t canvas;        /* C, canvas length (<= 1024) */
+    int64_t max_ctx;       /* KV rows per layer: >= P + K*C */
+    double rope_base;      /* RoPE base (rotate-half pairs, absolute positions) */
+    float rms_eps;         /* RMSNorm epsilon (unit gains) */
+    float temperature;     /* tau > 0: p0 = softmax(logits / tau) */
+    int32_t act_dtype;     /* DG_F32 or DG_BF16: activations, KV cache, dense weights */
+    int32_t expert_dtype;  /* DG_F32, DG_BF16 or DG_FP8_E4M3 (needs act_dtype DG_BF16) */
+    uint32_t capture_mask; /* DG_CAP_* bits */
+} dg_model_cfg;
+
+typedef struct dg_handle dg_handle;
+
+/* Create a handle: validates cfg, allocates weights, KV cache
+ * ([L][Hkv][max_ctx][D] for K and for V), RoPE tables and workspace on the
+ * current HIP device.  *out receives the handle.  Synchronous. */
+int dg_create(const dg_model_cfg* cfg, dg_handle** out);
+
+/* Free everything the handle owns.  Waits for the device.  NULL is a no-op. */
+void dg_destroy(dg_handle* h);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* dg_last_error(void);
+
+/* Copy one logical tensor from host memory into the handle, re-laid out for
+ * the kernels.  kind = DG_T_*; layer in [0, L) (ignored for DG_T_EMBED);
+ * expert in [0, E) for expert tensors, else ignored.  bytes must equal the
+ * tensor size in its storage type.  host_scales: e4m3 experts only, float
+ * per output column (F for WG/WU, d for WD); NULL otherwise.  Synchronous. */
+int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
+                   const void* host_src, size_t bytes, const float* host_scales);
+
+/* Stage 1 (technical report, Method, generation pipeline): run the causal
+ * encoder over P prompt ids (d_prompt_ids, device int32 [P]) and fill K/V
+ * rows 0..P-1 of every layer.  Resets the context: afterwards n_ctx = P and
+ * the canvas index k_blk = 0.  P >= 0 (P = 0 gives an empty context). */
+int dg_prefill_prompt_kv(dg_handle* h, const int32_t* d_prompt_ids, int32_t P, void* stream);
+
+/* Stage 2, one denoise pass over the canvas at positions n_ctx..n_ctx+C-1:
+ * logits = Decoder(canvas, KV cache) with bidirectional attention over
+ * [KV cache || canvas]; p0 = softmax(logits / tau); among unlocked positions
+ * the n_s with the highest confidence log max p0 (ties to the lower
+ * position) are locked to their argmax token (ties to the lower id), where
+ * n_s = min(ceil(C/T), #unlocked) and n_s = #unlocked at step T-1; every
+ * other unlocked position is redrawn from p0 by Gumbel-max with Philox4x32-10
+ * uniforms (key = seed; counter (v, i>>2, step | k_blk<<16, 0x47554D42),
+ * word i&3, u = (2*(word>>9)+1) * 2^-24).  Locked positions are not written.
+ * d_canvas: device int32 [C], updated in place; d_locked_mask: device uint8
+ * [C], updated in place.  0 <= step < T.  Needs a prefilled context
+ * (DG_ESTATE otherwise) and room for C rows (DG_ECAPACITY). */
+int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t step,
+                    int32_t T, uint64_t seed, void* stream);
+
+/* Canvas initialisation alone (alphasignal, "How text diffusion actually
+ * works", step 1; technical report, Method, forward process at kappa = 0):
+ * d_canvas[i] = uniform token from Philox (counter (i>>2, k_blk, 0,
+ * 0x494E4954), word i&3, token = word*V >> 32), d_locked_mask[i] = 0, for
+ * the handle's current canvas index k_blk.  Either pointer may be NULL. */
+int dg_init_canvas(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, uint64_t seed,
+                   void* stream);
+
+/* One 256-token block (technical report, Method, block-autoregressive
+ * generation): initialise the canvas uniformly over [0, V) with Philox
+ * (counter (i>>2, k_blk, 0, 0x494E4954), word i&3, token = word*V >> 32),
+ * run T denoise passes, write the canvas to d_out_tokens (device int32 [C]);
+ * if commit != 0, run stage 3 (the causal encoder over the final canvas,
+ * appending its K/V; n_ctx += C, k_blk += 1).  Synchronous only if the
+ * handle checks the non-finite flag (always: it reads one int at the end). */
+int dg_generate_block(dg_handle* h, int32_t* d_out_tokens, int32_t T, uint64_t seed,
+                      int32_t commit, void* stream);
+
+/* Stage 3 alone: append the causal-encoder K/V of a finished canvas
+ * (device int32 [C]) at rows n_ctx..n_ctx+C-1; n_ctx += C, k_blk += 1. */
+int dg_commit_canvas(dg_handle* h, const int32_t* d_canvas, void* stream);
+
+/* Read and clear the handle's non-finite flag (set by any pass whose logits
+ * statistics were not finite).  Synchronises the stream.  DG_ENONFINITE if set. */
+int dg_check_finite(dg_handle* h, void* stream);
+
+/* Forget the context (n_ctx = 0, k_blk = 0).  Weights stay loaded. */
+int dg_reset_context(dg_handle* h);
+
+/* Current committed context length and canvas index. */
+int dg_get_state(dg_handle* h, int64_t* n_ctx, int32_t* k_blk);
+
+/* Copy a capture of the last denoise pass (see DG_CAP_*) into device memory
+ * d_dst of exactly `bytes` bytes.  layer selects the layer for per-layer
+ * captures.  DG_ESTATE if the capture was not enabled. */
+int dg_get_capture(dg_handle* h, uint32_t what, int32_t layer, void* d_dst, size_t bytes,
+                   void* stream);
+
+/* Copy one layer's K or V cache rows [row0, row0+n) into device memory as
+ * [Hkv, n, D] in act_dtype (which = 0 for K, 1 for V). */
+int dg_get_kv(dg_handle* h, int32_t layer, int32_t which, int64_t row0, int64_t n, void* d_dst,
+              void* stream);
+
+/* ---------------------------------------------------------------- kernel-level entry points */
+
+/* Attention for one batch of queries (the decoder's attention step):
+ *   O[m, h*D + t] = sum_j softmax_j(scale * q_h,m . k_g,j [+ mask]) v_g,j,t
+ * with GQA group g = h / (Hq / Hkv).  d_q: [Hq, M, D]; d_k, d_v: [Hkv, S, D];
+ * d_o: [M, Hq*D]; all dtype (DG_F32 or DG_BF16, bf16 requires D = 128).
+ * causal != 0 masks key j for query m when j > q_pos0 + m (keys are at
+ * positions 0..S-1); causal = 0 is the canvas' bidirectional attention.
+ * Uses a library-owned device workspace (allocated on first use). */
+int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, int32_t Hq,
+                 int32_t Hkv, int32_t M, int32_t S, int32_t D, float scale, int32_t causal,
+                 int32_t q_pos0, int32_t dtype, void* stream);
+
+/* One MoE FFN layer on hidden states (the decoder's MoE step, applied to its
+ * input directly: no norm, no residual): router logits r = x Wr; top-k of
+ * softmax(r) (ties to the lower expert id) with gates renormalised over the
+ * k chosen; y = sum_j gate_j * (silu(x Wg_e) * (x Wu_e)) Wd_e, e = idx_j.
+ * Uses layer `layer` of the handle's weights.  d_x: [n_tokens, d] act_dtype;
+ * d_y: [n_tokens, d] act_dtype.  Optional d_idx (int32 [n_tokens, k]) and
+ * d_gates (float [n_tokens, k]) receive the routing; pass NULL to skip.
+ * n_tokens <= handle capacity max(C, max_ctx). */
+int dg_moe_layer(dg_handle* h, int32_t layer, const void* d_x, int32_t n_tokens, void* d_y,
+                 int32_t* d_idx, float* d_gates, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

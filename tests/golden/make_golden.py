@@ -1,0 +1,114 @@
+"""Write the oracle's expected values for the full-width parity tests.
+
+Calls only the CPU oracle (``oracle/``) on inputs from the seeded generator
+(``fixtures/``); nothing here touches the GPU library.  Outputs are small
+.npz files next to this script: per-position statistics and decisions with
+their margins, routing with margins, sampled logits and sampled K/V rows.
+
+    python tests/golden/make_golden.py moe26b_2layer
+    python tests/golden/make_golden.py moe26b_fp8_long_1layer
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import fixtures as fx  # noqa: E402
+from oracle.model import OracleModel  # noqa: E402
+from oracle.philox import init_canvas  # noqa: E402
+from oracle.weights import FixtureWeights  # noqa: E402
+
+N_LOGIT_SAMPLES = 16384
+N_KV_SAMPLES = 64
+
+
+def _step_record(prefix, res, logits_rng, V):
+    z = res.logits
+    C = z.shape[0]
+    rows = logits_rng.integers(0, C, N_LOGIT_SAMPLES)
+    cols = logits_rng.integers(0, V, N_LOGIT_SAMPLES)
+    # also every row's argmax and a near-max column, where relative error matters most
+    rows = np.concatenate([rows, np.arange(C)])
+    cols = np.concatenate([cols, res.stats.argmax])
+    out = {
+        f"{prefix}_m": res.stats.m, f"{prefix}_argmax": res.stats.argmax,
+        f"{prefix}_lse": res.stats.lse, f"{prefix}_conf": res.stats.conf,
+        f"{prefix}_top2_gap": res.stats.top2_gap, f"{prefix}_redraw": res.redraw,
+        f"{prefix}_redraw_gap": res.redraw_gap, f"{prefix}_canvas_out": res.canvas,
+        f"{prefix}_mask_out": res.mask, f"{prefix}_cut": np.array([res.sampler.cut_low, res.sampler.cut_high]),
+        f"{prefix}_logit_rows": rows.astype(np.int32), f"{prefix}_logit_cols": cols.astype(np.int32),
+        f"{prefix}_logit_vals": z[rows, cols],
+    }
+    for l, (idx, g, mg) in enumerate(zip(res.route_idx, res.route_gates, res.route_margin)):
+        out[f"{prefix}_route_idx_{l}"] = idx
+        out[f"{prefix}_route_gates_{l}"] = g
+        out[f"{prefix}_route_margin_{l}"] = mg
+    return out
+
+
+def _kv_samples(m, rng, n_ctx):
+    pos = np.sort(rng.choice(n_ctx, size=min(N_KV_SAMPLES, n_ctx), replace=False))
+    out = {"kv_pos": pos.astype(np.int64)}
+    for l in range(m.L):
+        out[f"k_{l}"] = m.K[l][:, pos, :]
+        out[f"v_{l}"] = m.V[l][:, pos, :]
+    return out
+
+
+def moe26b_2layer():
+    """The 26B-class MoE denoiser truncated to layers 0-1, at full widths, P = 8192:
+    prefill, canvas init, pass 0, and pass 1 teacher-forced from the oracle's state."""
+    w = fx.MOE26B.with_(name="moe26b_2layer", n_layers=2)
+    t0 = time.time()
+    m = OracleModel(w, FixtureWeights(w))
+    m.prefill(fx.prompt_ids(w))
+    print(f"prefill {time.time() - t0:.1f}s", flush=True)
+    rng = np.random.default_rng(20260)
+    out = {"seed": np.array(w.seed), "T": np.array(w.T)}
+    out.update(_kv_samples(m, rng, m.n_ctx))
+    canvas = init_canvas(w.seed, 0, w.canvas, w.vocab)
+    mask = np.zeros(w.canvas, np.uint8)
+    out["canvas_in_0"], out["mask_in_0"] = canvas, mask
+    for s in range(2):
+        res = m.denoise_step(canvas, mask, s, w.T, w.seed, keep_logits=True)
+        out.update(_step_record(f"s{s}", res, rng, w.vocab))
+        print(f"pass {s} {time.time() - t0:.1f}s", flush=True)
+        canvas, mask = res.canvas, res.mask
+        if s == 0:
+            out["canvas_in_1"], out["mask_in_1"] = canvas, mask
+    np.savez_compressed(os.path.join(HERE, "moe26b_2layer.npz"), **out)
+
+
+def moe26b_fp8_long_1layer():
+    """The long-context fp8-expert variant truncated to layer 0, P = 131072: canvas 0
+    pass 0, then canvas 1 pass 0 after committing the oracle's canvas-0 pass-0 output."""
+    w = fx.MOE26B_FP8_LONG.with_(name="moe26b_fp8_long_1layer", n_layers=1)
+    t0 = time.time()
+    m = OracleModel(w, FixtureWeights(w))
+    m.prefill(fx.prompt_ids(w))
+    print(f"prefill {time.time() - t0:.1f}s", flush=True)
+    rng = np.random.default_rng(20261)
+    out = {"seed": np.array(w.seed), "T": np.array(w.T)}
+    out.update(_kv_samples(m, rng, m.n_ctx))
+    for blk in range(2):
+        canvas = init_canvas(w.seed, blk, w.canvas, w.vocab)
+        mask = np.zeros(w.canvas, np.uint8)
+        out[f"b{blk}_canvas_in"] = canvas
+        res = m.denoise_step(canvas, mask, 0, w.T, w.seed, keep_logits=True)
+        out.update(_step_record(f"b{blk}", res, rng, w.vocab))
+        print(f"canvas {blk} {time.time() - t0:.1f}s", flush=True)
+        if blk == 0:
+            m.commit(res.canvas)
+            out["commit_tokens"] = res.canvas
+    np.savez_compressed(os.path.join(HERE, "moe26b_fp8_long_1layer.npz"), **out)
+
+
+if __name__ == "__main__":
+    for name in sys.argv[1:]:
+        globals()[name]()

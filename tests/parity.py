@@ -1,0 +1,62 @@
+"""Comparison helpers for GPU-vs-oracle parity (test infrastructure).
+
+Tolerances:
+  * continuous values: |gpu - oracle| <= atol + rtol * |oracle| element-wise;
+    bf16 paths atol 2e-2, rtol 1e-2; fp32 path 1e-4 / 1e-4; fp8 experts
+    2e-2 / 5e-2;
+  * discrete decisions (routing, argmax, lock set, redraw) must agree exactly
+    wherever the oracle's own margin for that decision exceeds DELTA = 1e-2 in
+    natural-log probability units (= logit units at temperature 1); inside the
+    band a disagreement is counted, not failed.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+DELTA = 1e-2
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4), "fp8": (2e-2, 5e-2)}
+
+
+def assert_close(name, gpu, ref, atol, rtol, max_bad_frac=0.0):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    err = np.abs(gpu - ref)
+    bad = ~(err <= atol + rtol * np.abs(ref))
+    frac = bad.mean() if bad.size else 0.0
+    if frac > max_bad_frac:
+        i = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        raise AssertionError(f"{name}: {bad.sum()} / {bad.size} outside tolerance; worst at {i}: "
+                             f"gpu {gpu[i]!r} oracle {ref[i]!r} (max abs err {err.max():.3g})")
+    return float(err.max()) if err.size else 0.0
+
+
+def gated_mismatches(gpu, ref, margin, delta=DELTA):
+    """Mismatches among decisions whose oracle margin exceeds delta, and the counts."""
+    gpu = np.asarray(gpu)
+    ref = np.asarray(ref)
+    margin = np.asarray(margin, np.float64)
+    gated = margin > delta
+    if gpu.ndim > margin.ndim:
+        diff = np.any(gpu != ref, axis=tuple(range(margin.ndim, gpu.ndim)))
+    else:
+        diff = gpu != ref
+    return int(np.sum(diff & gated)), int(gated.sum()), int(np.sum(diff & ~gated))
+
+
+def lock_set_check(gpu_mask_out, ref_mask_out, mask_in, conf_ref, cut_low, cut_high,
+                   delta=DELTA):
+    """New locks must agree for unlocked positions whose confidence is more than
+    delta away from the cut; the number of new locks must agree exactly."""
+    mask_in = np.asarray(mask_in).astype(bool)
+    g_new = np.asarray(gpu_mask_out).astype(bool) & ~mask_in
+    r_new = np.asarray(ref_mask_out).astype(bool) & ~mask_in
+    assert g_new.sum() == r_new.sum(), (g_new.sum(), r_new.sum())
+    if np.isinf(cut_low) or np.isinf(cut_high):
+        assert np.array_equal(g_new, r_new)
+        return 0
+    cut = 0.5 * (cut_low + cut_high)
+    far = np.abs(np.asarray(conf_ref) - cut) > delta
+    bad = (g_new != r_new) & far & ~mask_in
+    assert not bad.any(), f"lock decisions differ away from the cut at {np.flatnonzero(bad)}"
+    return int(np.sum((g_new != r_new) & ~far))
