@@ -1,0 +1,280 @@
+"""Throughput of the canvas denoising step on one MI355X.
+
+Workload: the 26B-class synthetic MoE denoiser in bf16 (30 layers, d=2816,
+16/8 heads of dim 128, 128 experts top-8 with FFN width 704, vocabulary
+262144), random-init N(0, 0.02) weights from the seeded generator, a prompt of
+8192 uniform-random ids prefilled once, one 256-token canvas.
+
+A step is one denoise pass over the canvas (embedding, 30 x [RMSNorm, QKV +
+RoPE + cache write, attention over the 8448 keys, output projection, RMSNorm,
+router, permutation, expert GEMMs, combine], final norm, LM head with the
+streaming vocabulary statistics, lock / redraw sampler), cycling through the
+12-pass block schedule; the canvas initialisation is part of the first pass
+of every block.  value = canvas tokens per second of denoise passes (256 per
+pass).  Also reported: output tokens per second of whole 256-token blocks
+(12 passes, with and without the commit), per-kernel-class times from HIP
+events recorded on the stream inside the timed region, the roofline of the
+dominant kernel (the expert gate/up GEMM), and the CPU oracle timed on a
+bounded sample of the same pass.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def moe1_algorithmic_bytes(w, n_active_experts):
+    """Expert gate/up weights of every expert hit, the normed activations once, H written."""
+    weights = n_active_experts * w.d_model * 2 * w.d_ff * 2
+    act = w.canvas * w.d_model * 2
+    hid = w.canvas * w.top_k * w.d_ff * 2
+    return weights + act + hid
+
+
+def pass_flops(w, S):
+    d, D, Hq, Hkv, E, k, F, V, C = (w.d_model, w.head_dim, w.n_q_heads, w.n_kv_heads,
+                                    w.n_experts, w.top_k, w.d_ff, w.vocab, w.canvas)
+    per_layer = 2 * C * d * (Hq + 2 * Hkv) * D + 4 * C * S * D * Hq + 2 * C * Hq * D * d \
+        + 2 * C * d * E + 2 * C * k * 3 * d * F
+    return w.n_layers * per_layer + 2 * C * d * V
+
+
+def cpu_baseline(w, seconds_budget=30.0):
+    """Time the CPU oracle on a bounded sample of one denoise pass: decoder layer 0 of the
+    canvas over the 8192-token prompt context, plus the LM head and sampler; the pass time is
+    estimated as n_layers x (layer time) + (head time)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import fixtures as fx
+    from oracle.model import OracleModel, lm_head_stats, gumbel_draw, sampler_update
+    from oracle.numerics import rmsnorm, round_bf16
+    from oracle.philox import init_canvas, gumbel_uniforms
+    from oracle.weights import FixtureWeights
+
+    w1 = w.with_(n_layers=1)
+    W = FixtureWeights(w1)
+    m = OracleModel(w1, W)
+    m.prefill(fx.prompt_ids(w1))              # layer-0 K/V of the prompt (untimed set-up)
+    for e in range(w.n_experts):              # generate weights outside the timed region
+        for kind in ("wg", "wu", "wd"):
+            W.expert(kind, 0, e)
+    E = W.embed()
+    canvas = init_canvas(w.seed, 0, w.canvas, w.vocab)
+    h = E[canvas]
+    pos = np.arange(m.n_ctx, m.n_ctx + w.canvas)
+    t0 = time.perf_counter()
+    hl, _, _, _ = m._layer(0, h, pos, m.K[0], m.V[0], causal=False, ctx_pos=np.arange(m.n_ctx))
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    hn = round_bf16(rmsnorm(hl, w.rms_eps))
+    z = (hn @ E.T) / w.temperature
+    st = lm_head_stats(z)
+    red = np.empty(w.canvas, np.int32)
+    for c0 in range(0, w.canvas, 16):
+        rows = np.arange(c0, c0 + 16)
+        red[rows], _ = gumbel_draw(z[rows], gumbel_uniforms(w.seed, 0, 0, rows, w.vocab))
+    sampler_update(canvas, np.zeros(w.canvas, np.uint8), st.conf, st.argmax, red, 0, w.T)
+    t_head = time.perf_counter() - t0
+    t_pass = w.n_layers * t_layer + t_head
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(w.canvas / t_pass, 3), "unit": "canvas tok/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"decoder layer 0 of one pass ({t_layer:.2f} s, 256 canvas queries over "
+                       f"{m.n_ctx + w.canvas} keys + MoE) and the LM head + sampler "
+                       f"({t_head:.2f} s); pass = {w.n_layers} x layer + head = {t_pass:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=24)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=None, help=argparse.SUPPRESS)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the denoise pass is "
+              "measured on a single MI355X; multi-GPU sharding is not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import discrete_diffusion_decoding_canvas_amd as dg
+    import fixtures as fx
+    from fixtures.dg_glue import build_handle
+
+    w = fx.MOE26B
+    if args.layers:
+        w = w.with_(n_layers=args.layers)
+    torch.cuda.set_device(0)
+    log(f"building {w.name} (weights from the seeded generator)")
+    t0 = time.time()
+    h = build_handle(dg, w, max_ctx=w.prompt_len + 2 * w.canvas)
+    log(f"weights loaded in {time.time() - t0:.1f} s; prefilling {w.prompt_len} tokens")
+    ids = torch.from_numpy(fx.prompt_ids(w)).cuda()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dg.dg_prefill_prompt_kv(h, ids, w.prompt_len)
+    torch.cuda.synchronize()
+    prefill_ms = (time.perf_counter() - t0) * 1e3
+    log(f"prefill {prefill_ms:.1f} ms")
+
+    C, T, seed = w.canvas, w.T, w.seed
+    canvas = torch.empty(C, dtype=torch.int32, device="cuda")
+    mask = torch.empty(C, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        s = i % T
+        if s == 0:
+            dg.dg_init_canvas(h, canvas, mask, seed + i // T)
+        dg.dg_denoise_step(h, canvas, mask, s, T, seed + i // T)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} passes done; timing {args.steps} passes")
+
+    dg.dg_profile_begin(h, args.steps * (w.n_layers * 7 + 4))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+    prof_ms, prof_n = dg.dg_profile_end(h)
+    dg.dg_check_finite(h)
+    ms_per_pass = ms_total / args.steps
+    canvas_tok_s = C * args.steps / (ms_total / 1e3)
+    log(f"{ms_per_pass:.3f} ms per pass ({canvas_tok_s:.0f} canvas tok/s; wall {wall:.2f} s)")
+
+    # routing of one more (untimed) pass: experts actually hit per layer set the
+    # algorithmic weight bytes of the expert GEMMs
+    dg.dg_set_capture(h, dg.DG_CAP_ROUTING)
+    dg.dg_init_canvas(h, canvas, mask, seed)
+    dg.dg_denoise_step(h, canvas, mask, 0, T, seed)
+    active, max_load = [], []
+    rbuf = torch.empty(2 * C * w.top_k, dtype=torch.int32, device="cuda")
+    for l in range(w.n_layers):
+        dg.dg_get_capture(h, dg.DG_CAP_ROUTING, l, rbuf)
+        torch.cuda.synchronize()
+        ids = rbuf[:C * w.top_k].cpu().numpy()
+        cnt = np.bincount(ids, minlength=w.n_experts)
+        active.append(int((cnt > 0).sum()))
+        max_load.append(int(cnt.max()))
+    dg.dg_set_capture(h, 0)
+    mean_active = float(np.mean(active))
+    log(f"experts hit per layer: mean {mean_active:.1f}, min {min(active)}, max {max(active)}; "
+        f"largest per-expert load {max(max_load)} tokens")
+
+    # whole blocks: 12 passes (+ the commit of the final canvas)
+    out = torch.empty(C, dtype=torch.int32, device="cuda")
+    dg.dg_generate_block(h, out, T, seed, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_blocks = 2
+    for b in range(n_blocks):
+        dg.dg_generate_block(h, out, T, seed + b, False)
+    torch.cuda.synchronize()
+    block_ms = (time.perf_counter() - t0) * 1e3 / n_blocks
+    t0 = time.perf_counter()
+    dg.dg_commit_canvas(h, out)
+    torch.cuda.synchronize()
+    commit_ms = (time.perf_counter() - t0) * 1e3
+    log(f"block {block_ms:.2f} ms, commit {commit_ms:.2f} ms")
+
+    # roofline of the dominant kernel (expert gate/up GEMM + SwiGLU)
+    names = ["moe_gemm1", "moe_gemm2", "attention", "lm_head", "dense_gemm"]
+    per_class_us = {n: (prof_ms[i] / prof_n[i] * 1e3 if prof_n[i] else None)
+                    for i, n in enumerate(names)}
+    per_pass_us = {n: prof_ms[i] / args.steps * 1e3 for i, n in enumerate(names)}
+    moe1_us = per_class_us["moe_gemm1"]
+    moe1_bytes = int(moe1_algorithmic_bytes(w, mean_active))
+    moe1_gbs = moe1_bytes / (moe1_us * 1e-6) / 1e9
+    moe2_bytes = int(mean_active * w.d_ff * w.d_model * 2 + C * w.top_k * (w.d_ff * 2 + w.d_model * 4))
+    moe2_gbs = moe2_bytes / (per_class_us["moe_gemm2"] * 1e-6) / 1e9
+    S = w.prompt_len + C
+    attn_flops = 4 * C * S * w.head_dim * w.n_q_heads
+    attn_tflops = attn_flops / (per_class_us["attention"] * 1e-6) / 1e12
+    head_flops = 2 * C * w.d_model * w.vocab
+    head_tflops = head_flops / (per_class_us["lm_head"] * 1e-6) / 1e12
+    head_gbs = w.vocab * w.d_model * 2 / (per_class_us["lm_head"] * 1e-6) / 1e9
+    moe_flops = 2 * C * w.top_k * 3 * w.d_model * w.d_ff
+    moe_tflops = moe_flops / ((per_class_us["moe_gemm1"] + per_class_us["moe_gemm2"]) * 1e-6) / 1e12
+    flops = pass_flops(w, S)
+
+    result = {
+        "metric": "canvas tok/s per denoise pass",
+        "value": round(canvas_tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_pass, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init N(0,0.02) weights, uniform-random prompt ids)",
+        "config": {"workload": w.name, "layers": w.n_layers, "d_model": w.d_model,
+                   "experts": w.n_experts, "top_k": w.top_k, "d_ff": w.d_ff,
+                   "vocab": w.vocab, "prompt": w.prompt_len, "canvas": C,
+                   "passes_per_block": T},
+        "output_tok_s_per_block": round(C / (block_ms / 1e3), 1),
+        "output_tok_s_per_block_with_commit": round(C / ((block_ms + commit_ms) / 1e3), 1),
+        "block_ms": round(block_ms, 3),
+        "commit_ms": round(commit_ms, 3),
+        "prefill_ms": round(prefill_ms, 2),
+        "pass_tflops": round(flops / (ms_per_pass * 1e-3) / 1e12, 2),
+        "mfma_util_pct": {
+            "moe_grouped_gemm": round(100 * moe_tflops / BF16_PEAK_TFLOPS, 2),
+            "attention": round(100 * attn_tflops / BF16_PEAK_TFLOPS, 2),
+            "lm_head": round(100 * head_tflops / BF16_PEAK_TFLOPS, 2),
+        },
+        "hbm_util_pct": {
+            "moe_gemm1": round(100 * moe1_gbs / HBM_PEAK_GBS, 2),
+            "moe_gemm2": round(100 * moe2_gbs / HBM_PEAK_GBS, 2),
+            "lm_head": round(100 * head_gbs / HBM_PEAK_GBS, 2),
+        },
+        "kernel_us_per_launch": {k: (round(v, 2) if v else None) for k, v in per_class_us.items()},
+        "experts_hit_per_layer": {"mean": round(mean_active, 2), "min": min(active),
+                                  "max": max(active), "largest_expert_load": max(max_load)},
+        "kernel_us_per_pass": {k: round(v, 1) for k, v in per_pass_us.items()},
+        "roofline": {"bound": "hbm", "kernel": "moe_gemm1 (expert gate/up GEMM + SwiGLU)",
+                     "achieved": round(moe1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(moe1_gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": moe1_bytes,
+                     "avg_launch_us": round(moe1_us, 2), "traffic": None},
+    }
+    dg.dg_destroy(h)
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

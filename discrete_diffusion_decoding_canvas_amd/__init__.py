@@ -17,14 +17,17 @@ LIB_PATH = os.path.join(HERE, "libdg.so")
 DG_OK, DG_EINVAL, DG_ENOMEM, DG_EHIP, DG_ECAPACITY, DG_ESTATE, DG_ENONFINITE = 0, -1, -2, -3, -4, -5, -6
 DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
 DG_T_EMBED, DG_T_WQ, DG_T_WK, DG_T_WV, DG_T_WO, DG_T_WR, DG_T_WG, DG_T_WU, DG_T_WD = range(9)
-DG_CAP_LOGITS, DG_CAP_STATS, DG_CAP_ROUTING, DG_CAP_HIDDEN = 1, 2, 4, 8
+DG_CAP_LOGITS, DG_CAP_STATS, DG_CAP_ROUTING, DG_CAP_HIDDEN, DG_CAP_ATTN, DG_CAP_ROUTER_LOGITS = 1, 2, 4, 8, 16, 32
 
 EXPORTED = (
     "dg_create", "dg_destroy", "dg_last_error", "dg_load_tensor", "dg_prefill_prompt_kv",
     "dg_denoise_step", "dg_generate_block", "dg_commit_canvas", "dg_check_finite",
     "dg_reset_context", "dg_get_state", "dg_get_capture", "dg_get_kv", "dg_attention",
-    "dg_moe_layer", "dg_init_canvas",
+    "dg_moe_layer", "dg_init_canvas", "dg_profile_begin", "dg_profile_end", "dg_set_kv",
+    "dg_set_capture",
 )
+DG_PROF_MOE_GEMM1, DG_PROF_MOE_GEMM2, DG_PROF_ATTENTION, DG_PROF_LM_HEAD, DG_PROF_DENSE = range(5)
+DG_PROF_N = 5
 
 
 class DGError(RuntimeError):
@@ -67,10 +70,14 @@ def _load_library():
         "dg_get_state": ([vp, ctypes.POINTER(i64), ctypes.POINTER(i32)], i32),
         "dg_get_capture": ([vp, u32, i32, vp, sz, vp], i32),
         "dg_get_kv": ([vp, i32, i32, i64, i64, vp, vp], i32),
+        "dg_set_kv": ([vp, i32, i32, i64, i64, vp, vp], i32),
+        "dg_set_capture": ([vp, u32], i32),
         "dg_attention": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float, i32, i32,
                           i32, vp], i32),
         "dg_moe_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
         "dg_init_canvas": ([vp, vp, vp, u64, vp], i32),
+        "dg_profile_begin": ([vp, i32], i32),
+        "dg_profile_end": ([vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -169,6 +176,10 @@ def dg_get_state(h):
     return n.value, k.value
 
 
+def dg_set_capture(h, capture_mask: int) -> None:
+    _check(_lib.dg_set_capture(h, capture_mask))
+
+
 def dg_get_capture(h, what: int, layer: int, d_dst, stream=None) -> None:
     nbytes = d_dst.numel() * d_dst.element_size()
     _check(_lib.dg_get_capture(h, what, layer, _ptr(d_dst), nbytes, _stream(stream)))
@@ -176,6 +187,10 @@ def dg_get_capture(h, what: int, layer: int, d_dst, stream=None) -> None:
 
 def dg_get_kv(h, layer: int, which: int, row0: int, n: int, d_dst, stream=None) -> None:
     _check(_lib.dg_get_kv(h, layer, which, row0, n, _ptr(d_dst), _stream(stream)))
+
+
+def dg_set_kv(h, layer: int, which: int, row0: int, n: int, d_src, stream=None) -> None:
+    _check(_lib.dg_set_kv(h, layer, which, row0, n, _ptr(d_src), _stream(stream)))
 
 
 def dg_attention(d_q, d_k, d_v, d_o, Hq: int, Hkv: int, M: int, S: int, D: int, scale: float,
@@ -188,6 +203,18 @@ def dg_moe_layer(h, layer: int, d_x, n_tokens: int, d_y, d_idx=None, d_gates=Non
                  stream=None) -> None:
     _check(_lib.dg_moe_layer(h, layer, _ptr(d_x), n_tokens, _ptr(d_y), _ptr(d_idx),
                              _ptr(d_gates), _stream(stream)))
+
+
+def dg_profile_begin(h, max_launches: int) -> None:
+    _check(_lib.dg_profile_begin(h, max_launches))
+
+
+def dg_profile_end(h):
+    """Returns (summed ms, launch counts), one entry per DG_PROF_* class."""
+    ms = (ctypes.c_double * DG_PROF_N)()
+    n = (ctypes.c_int32 * DG_PROF_N)()
+    _check(_lib.dg_profile_end(h, ms, n))
+    return list(ms), list(n)
 
 
 # ------------------------------------------------------------------ convenience

@@ -50,6 +50,7 @@ int fail(int code, const char* fmt, ...) {
     } while (0)
 
 constexpr int kPrefillChunk = 4096;   // tokens per causal-encoder chunk
+constexpr int kRouterSplit = 8;       // K split of the router GEMM
 
 size_t dsize(int dt) { return dt == kF32 ? 4 : dt == kBF16 ? 2 : 1; }
 
@@ -106,6 +107,10 @@ struct dg_handle {
     int32_t* cap_idx = nullptr;
     float* cap_gates = nullptr;
     float* cap_hidden = nullptr;
+    void* cap_attn = nullptr;
+    float* cap_rlog = nullptr;
+    uint32_t cap_mask = 0;    // captures recorded by the next passes (buffers allocated)
+    bool cap(uint32_t bit) const { return (cap_mask & bit) != 0; }
     int32_t* blk_canvas = nullptr;
     uint8_t* blk_mask = nullptr;
 
@@ -115,6 +120,12 @@ struct dg_handle {
     int64_t n_ctx = 0;
     int k_blk = 0;
     bool prefilled = false;
+
+    // per-kernel-class event timing
+    bool prof = false;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> ev_cls;
+    int ev_used = 0;
 
     int alloc(void** p, size_t bytes) {
         if (bytes == 0) bytes = 256;
@@ -158,6 +169,7 @@ static int validate_cfg(const dg_model_cfg* c) {
     if (c->n_experts > 256) return fail(DG_EINVAL, "n_experts must be <= 256");
     if (c->canvas > kMaxCanvas) return fail(DG_EINVAL, "canvas must be <= %d", kMaxCanvas);
     if (c->head_dim & 1) return fail(DG_EINVAL, "head_dim must be even");
+    if (c->d_model > 256 * kCombineCols) return fail(DG_EINVAL, "d_model must be <= %d", 256 * kCombineCols);
     if (c->max_ctx < c->canvas) return fail(DG_EINVAL, "max_ctx must hold at least one canvas");
     if (!(c->temperature > 0.f)) return fail(DG_EINVAL, "temperature must be > 0");
     if (!(c->rope_base > 0.0)) return fail(DG_EINVAL, "rope_base must be > 0");
@@ -196,20 +208,66 @@ static ExpertWeights expert_weights(dg_handle* h, int l) {
     return w;
 }
 
+// Allocate the capture buffers a mask needs (once) and make it the active mask.
+static int alloc_captures(dg_handle* h, uint32_t mask) {
+    const size_t L = h->L, C = h->C, k = h->k;
+    if ((mask & DG_CAP_LOGITS) && !h->logits_cap) DG_TRY(h->allocT(&h->logits_cap, C * h->V));
+    if ((mask & DG_CAP_ROUTING) && !h->cap_idx) {
+        DG_TRY(h->allocT(&h->cap_idx, L * C * k));
+        DG_TRY(h->allocT(&h->cap_gates, L * C * k));
+    }
+    if ((mask & DG_CAP_HIDDEN) && !h->cap_hidden) DG_TRY(h->allocT(&h->cap_hidden, L * C * h->d));
+    if ((mask & DG_CAP_ATTN) && !h->cap_attn)
+        DG_TRY(h->alloc(&h->cap_attn, L * C * h->Hq * h->D * dsize(h->act)));
+    if ((mask & DG_CAP_ROUTER_LOGITS) && !h->cap_rlog) DG_TRY(h->allocT(&h->cap_rlog, L * C * h->E));
+    h->cap_mask = mask;
+    return DG_OK;
+}
+
 #define K_TRY(expr) HIP_TRY(expr)
+
+// Event pair around one launch of a timed kernel class (no-op unless profiling).
+struct ProfScope {
+    dg_handle* h;
+    hipStream_t s;
+    int slot = -1;
+    ProfScope(dg_handle* hh, int cls, hipStream_t ss) : h(hh), s(ss) {
+        if (h->prof && h->ev_used + 2 <= (int)h->ev.size()) {
+            slot = h->ev_used;
+            h->ev_used += 2;
+            h->ev_cls[slot] = cls;
+            (void)hipEventRecord(h->ev[slot], s);
+        }
+    }
+    ~ProfScope() {
+        if (slot >= 0) (void)hipEventRecord(h->ev[slot + 1], s);
+    }
+};
 
 // MoE block of one layer on h->a (and h->a8) for n tokens: router -> permute ->
 // expert GEMMs.  Leaves Y, gates, inv ready for the combine.
 static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* xin8,
                    hipStream_t s) {
-    K_TRY(launch_gemm(h->act, kEpiStoreF32, xin, h->d, n, h->wr[l], h->d, h->E, h->rlog, h->E, s));
-    K_TRY(launch_router_permute(h->rlog, n, h->E, h->k, h->idx, h->gates, h->counts, h->base,
-                                h->offsets, h->perm_token, h->inv, s));
+    // the router GEMM is narrow (N = E): split K over workgroups; top-k adds the partials
+    const int ksplit = (h->act == kBF16 && !h->cap(DG_CAP_ROUTER_LOGITS)) ? kRouterSplit : 1;
+    {
+        ProfScope p(h, DG_PROF_DENSE, s);
+        K_TRY(launch_gemm(h->act, kEpiStoreF32, xin, h->d, n, h->wr[l], h->d, h->E, h->rlog, h->E,
+                          s, ksplit));
+    }
+    K_TRY(launch_router_permute(h->rlog, ksplit, n, h->E, h->k, h->idx, h->gates, h->counts,
+                                h->base, h->offsets, h->perm_token, h->inv, s));
     ExpertWeights w = expert_weights(h, l);
     const int rows = n * h->k;
     const void* X1 = (h->edt == kFP8) ? (const void*)xin8 : xin;
-    K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows, h->H, s));
-    K_TRY(launch_moe_gemm2(h->edt, w, h->H, h->offsets, h->E, h->d, h->F, rows, h->Y, s));
+    {
+        ProfScope p(h, DG_PROF_MOE_GEMM1, s);
+        K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows, h->H, s));
+    }
+    {
+        ProfScope p(h, DG_PROF_MOE_GEMM2, s);
+        K_TRY(launch_moe_gemm2(h->edt, w, h->H, h->offsets, h->E, h->d, h->F, rows, h->Y, s));
+    }
     return DG_OK;
 }
 
@@ -217,9 +275,12 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
 // residual and its norm).  Keys: cache rows [0, pos0 + n).  kv_only: stop after
 // writing K/V (the last encoder layer).
 static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool kv_only,
-                     hipStream_t s) {
-    K_TRY(launch_gemm(h->act, kEpiStoreF32, h->a, h->d, n, h->wqkv[l], h->d, h->qkv_n, h->qkv,
-                      h->qkv_n, s));
+                     hipStream_t s, bool capture = false) {
+    {
+        ProfScope p(h, DG_PROF_DENSE, s);
+        K_TRY(launch_gemm(h->act, kEpiStoreF32, h->a, h->d, n, h->wqkv[l], h->d, h->qkv_n, h->qkv,
+                          h->qkv_n, s));
+    }
     K_TRY(launch_rope_scatter(h->act, h->qkv, n, h->Hq, h->Hkv, h->D, pos0, h->cos_t, h->sin_t,
                               h->q, h->klayer(l), h->vlayer(l), h->kv_rows, s));
     if (kv_only) return DG_OK;
@@ -241,12 +302,26 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
     aa.part_o = h->part;
     aa.part_ml = nullptr;
     aa.part_capacity = h->part_floats;
-    K_TRY(launch_attention(h->act, aa, s));
-    K_TRY(launch_gemm(h->act, kEpiAddF32, h->attn_o, h->Hq * h->D, n, h->wo[l], h->Hq * h->D,
-                      h->d, h->x, h->d, s));
+    {
+        ProfScope p(h, DG_PROF_ATTENTION, s);
+        K_TRY(launch_attention(h->act, aa, s));
+    }
+    if (capture && h->cap(DG_CAP_ATTN)) {
+        const size_t b = (size_t)n * h->Hq * h->D * dsize(h->act);
+        HIP_TRY(hipMemcpyAsync((char*)h->cap_attn + (size_t)l * b, h->attn_o, b,
+                               hipMemcpyDeviceToDevice, s));
+    }
+    {
+        ProfScope p(h, DG_PROF_DENSE, s);
+        K_TRY(launch_gemm(h->act, kEpiAddF32, h->attn_o, h->Hq * h->D, n, h->wo[l], h->Hq * h->D,
+                          h->d, h->x, h->d, s));
+    }
     K_TRY(launch_rmsnorm(h->act, h->x, n, h->d, h->cfg.rms_eps, h->a,
                          h->edt == kFP8 ? h->a8 : nullptr, s));
     DG_TRY(run_moe(h, l, n, h->a, h->a8, s));
+    if (capture && h->cap(DG_CAP_ROUTER_LOGITS))
+        HIP_TRY(hipMemcpyAsync(h->cap_rlog + (size_t)l * n * h->E, h->rlog, (size_t)n * h->E * 4,
+                               hipMemcpyDeviceToDevice, s));
     // residual add, then the next norm (next layer's input, or the final norm)
     K_TRY(launch_moe_combine(h->act, 0, h->Y, n, h->d, h->k, h->gates, h->inv, h->x,
                              h->cfg.rms_eps, h->a, h->edt == kFP8 ? h->a8 : nullptr, nullptr, s));
@@ -355,7 +430,7 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     // so (D + 2) floats for at most 1024 x 128 query rows bound every call
     h->part_floats = h->act == kF32 ? 64 : (int64_t)1024 * 128 * (h->D + 2);
     A_TRY(h->allocT(&h->part, (size_t)h->part_floats));
-    A_TRY(h->allocT(&h->rlog, T * E));
+    A_TRY(h->allocT(&h->rlog, T * E * kRouterSplit));
     A_TRY(h->allocT(&h->idx, T * k));
     A_TRY(h->allocT(&h->gates, T * k));
     const size_t n_chunks = (T * k + kPermChunk - 1) / kPermChunk;
@@ -381,12 +456,7 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->bad, 1));
     A_TRY(h->allocT(&h->blk_canvas, h->C));
     A_TRY(h->allocT(&h->blk_mask, h->C));
-    if (cfg->capture_mask & DG_CAP_LOGITS) A_TRY(h->allocT(&h->logits_cap, (size_t)h->C * V));
-    if (cfg->capture_mask & DG_CAP_ROUTING) {
-        A_TRY(h->allocT(&h->cap_idx, L * h->C * k));
-        A_TRY(h->allocT(&h->cap_gates, L * h->C * k));
-    }
-    if (cfg->capture_mask & DG_CAP_HIDDEN) A_TRY(h->allocT(&h->cap_hidden, L * h->C * d));
+    A_TRY(alloc_captures(h, cfg->capture_mask));
 #undef A_TRY
     *out = h;
     return DG_OK;
@@ -395,6 +465,7 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
 void dg_destroy(dg_handle* h) {
     if (!h) return;
     (void)hipDeviceSynchronize();
+    for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
     for (void* p : h->allocs) (void)hipFree(p);
     if (h->stage) (void)hipFree(h->stage);
     delete h;
@@ -517,6 +588,50 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
     return DG_OK;
 }
 
+int dg_set_capture(dg_handle* h, uint32_t capture_mask) {
+    g_err.clear();
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    if (capture_mask & ~(uint32_t)63) return fail(DG_EINVAL, "unknown capture bits");
+    HIP_TRY(hipDeviceSynchronize());
+    return alloc_captures(h, capture_mask);
+}
+
+int dg_profile_begin(dg_handle* h, int32_t max_launches) {
+    g_err.clear();
+    if (!h || max_launches <= 0) return fail(DG_EINVAL, "bad profile arguments");
+    while ((int)h->ev.size() < 2 * max_launches) {
+        hipEvent_t e;
+        HIP_TRY(hipEventCreate(&e));
+        h->ev.push_back(e);
+    }
+    h->ev_cls.assign(h->ev.size(), -1);
+    h->ev_used = 0;
+    h->prof = true;
+    return DG_OK;
+}
+
+int dg_profile_end(dg_handle* h, double* total_ms, int32_t* counts) {
+    g_err.clear();
+    if (!h || !total_ms || !counts) return fail(DG_EINVAL, "NULL argument");
+    h->prof = false;
+    HIP_TRY(hipDeviceSynchronize());
+    for (int c = 0; c < DG_PROF_N; ++c) {
+        total_ms[c] = 0.0;
+        counts[c] = 0;
+    }
+    for (int i = 0; i + 1 < h->ev_used; i += 2) {
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, h->ev[i], h->ev[i + 1]));
+        const int c = h->ev_cls[i];
+        if (c >= 0 && c < DG_PROF_N) {
+            total_ms[c] += ms;
+            counts[c] += 1;
+        }
+    }
+    h->ev_used = 0;
+    return DG_OK;
+}
+
 int dg_reset_context(dg_handle* h) {
     if (!h) return fail(DG_EINVAL, "NULL handle");
     h->n_ctx = 0;
@@ -580,19 +695,23 @@ int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int
     K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, C, h->d,
                                h->cfg.rms_eps, h->x, h->a, s));
     for (int l = 0; l < h->L; ++l) {
-        DG_TRY(run_layer(h, l, C, h->n_ctx, false, false, s));
-        if (h->cap_idx) {
+        DG_TRY(run_layer(h, l, C, h->n_ctx, false, false, s, true));
+        if (h->cap(DG_CAP_ROUTING)) {
             HIP_TRY(hipMemcpyAsync(h->cap_idx + (size_t)l * C * h->k, h->idx,
                                    (size_t)C * h->k * 4, hipMemcpyDeviceToDevice, s));
             HIP_TRY(hipMemcpyAsync(h->cap_gates + (size_t)l * C * h->k, h->gates,
                                    (size_t)C * h->k * 4, hipMemcpyDeviceToDevice, s));
         }
-        if (h->cap_hidden)
+        if (h->cap(DG_CAP_HIDDEN))
             HIP_TRY(hipMemcpyAsync(h->cap_hidden + (size_t)l * C * h->d, h->x,
                                    (size_t)C * h->d * 4, hipMemcpyDeviceToDevice, s));
     }
-    K_TRY(launch_lm_head(h->act, h->a, C, h->d, h->embed, h->V, 1.0f / h->cfg.temperature,
-                         d_locked_mask, seed, step, h->k_blk, h->hp, h->logits_cap, s));
+    {
+        ProfScope p(h, DG_PROF_LM_HEAD, s);
+        K_TRY(launch_lm_head(h->act, h->a, C, h->d, h->embed, h->V, 1.0f / h->cfg.temperature,
+                             d_locked_mask, seed, step, h->k_blk, h->hp,
+                             h->cap(DG_CAP_LOGITS) ? h->logits_cap : nullptr, s));
+    }
     K_TRY(launch_head_stats(h->hp, C, d_locked_mask, h->st_m, h->st_a, h->st_lse, h->st_conf,
                             h->st_draw, h->bad, s));
     K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, C, step, T, s));
@@ -680,6 +799,22 @@ int dg_get_capture(dg_handle* h, uint32_t what, int32_t layer, void* d_dst, size
                                hipMemcpyDeviceToDevice, s));
         return DG_OK;
     }
+    if (what == DG_CAP_ATTN) {
+        if (!h->cap_attn) return fail(DG_ESTATE, "attention capture not enabled");
+        const size_t n = C * h->Hq * h->D * dsize(h->act);
+        if (bytes != n) return fail(DG_EINVAL, "attention capture is %zu bytes", n);
+        HIP_TRY(hipMemcpyAsync(d_dst, (char*)h->cap_attn + (size_t)layer * n, n,
+                               hipMemcpyDeviceToDevice, s));
+        return DG_OK;
+    }
+    if (what == DG_CAP_ROUTER_LOGITS) {
+        if (!h->cap_rlog) return fail(DG_ESTATE, "router logits capture not enabled");
+        const size_t n = C * h->E * 4;
+        if (bytes != n) return fail(DG_EINVAL, "router logits capture is %zu bytes", n);
+        HIP_TRY(hipMemcpyAsync(d_dst, h->cap_rlog + (size_t)layer * C * h->E, n,
+                               hipMemcpyDeviceToDevice, s));
+        return DG_OK;
+    }
     if (what == DG_CAP_HIDDEN) {
         if (!h->cap_hidden) return fail(DG_ESTATE, "hidden capture not enabled");
         const size_t n = C * h->d * 4;
@@ -700,6 +835,18 @@ int dg_get_kv(dg_handle* h, int32_t layer, int32_t which, int64_t row0, int64_t 
     const bool vp = which == 1 && h->act == kBF16;
     HIP_TRY(launch_read_kv(h->act, vp, which ? h->vlayer(layer) : h->klayer(layer), h->Hkv, h->D,
                            h->kv_rows, row0, n, d_dst, (hipStream_t)stream));
+    return DG_OK;
+}
+
+int dg_set_kv(dg_handle* h, int32_t layer, int32_t which, int64_t row0, int64_t n,
+              const void* d_src, void* stream) {
+    g_err.clear();
+    if (!h || !d_src) return fail(DG_EINVAL, "NULL handle or source");
+    if (layer < 0 || layer >= h->L || (which != 0 && which != 1)) return fail(DG_EINVAL, "bad layer or which");
+    if (row0 < 0 || n < 0 || row0 + n > h->max_ctx) return fail(DG_EINVAL, "rows out of range");
+    const bool vp = which == 1 && h->act == kBF16;
+    HIP_TRY(launch_write_kv(h->act, vp, which ? h->vlayer(layer) : h->klayer(layer), h->Hkv, h->D,
+                            h->kv_rows, row0, n, d_src, (hipStream_t)stream));
     return DG_OK;
 }
 

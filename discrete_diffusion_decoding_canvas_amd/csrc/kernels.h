@@ -11,6 +11,8 @@ constexpr int kFP8 = 2;
 
 constexpr int kPermChunk = 1024;   // entries per permutation workgroup
 constexpr int kMaxCanvas = 1024;   // sampler capacity (one workgroup)
+constexpr int kMaxTopK = 16;       // experts per token
+constexpr int kCombineCols = 16;   // combine: columns per thread, d <= 256 * 16
 
 // Transposed, key-permuted V cache: Vt[h][dim][slot], rows padded to a multiple
 // of 32.  Within each 32-key block, key 16*hi + 4*g + j sits at slot 8*g + 4*hi + j,
@@ -43,7 +45,10 @@ hipError_t launch_pack_vt(const void* v, int Hkv, int S, int D, void* vt, int64_
                           hipStream_t s);
 hipError_t launch_read_kv(int dtype, bool vpacked, const void* cache, int Hkv, int D,
                           int64_t rows, int64_t row0, int64_t n, void* dst, hipStream_t s);
-hipError_t launch_router_permute(const float* logits, int M, int E, int k, int32_t* idx,
+hipError_t launch_write_kv(int dtype, bool vpacked, void* cache, int Hkv, int D, int64_t rows,
+                           int64_t row0, int64_t n, const void* src, hipStream_t s);
+// logits: nsplit partial sums [nsplit][M][E], added in order.
+hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, int k, int32_t* idx,
                                  float* gates, int32_t* counts, int32_t* base, int32_t* offsets,
                                  int32_t* perm_token, int32_t* inv, hipStream_t s);
 hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
@@ -71,9 +76,10 @@ constexpr int kEpiStoreF32 = 0;   // C[m, n] = acc
 constexpr int kEpiAddF32 = 1;     // C[m, n] += acc (residual add, single writer)
 
 // C = A[M, K] B[K, N].  bf16: A row-major (lda), B packed (see packed_b_index).
-// f32: A row-major, B row-major [K, N].
+// f32: A row-major, B row-major [K, N].  bf16 with ksplit > 1 (store epilogue
+// only): partial sums over ksplit K ranges at C + z * M * ldc, z < ksplit.
 hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const void* B, int K,
-                       int N, float* C, int ldc, hipStream_t s);
+                       int N, float* C, int ldc, hipStream_t s, int ksplit = 1);
 
 // Expert GEMMs over the permuted entries (offsets[e]..offsets[e+1] belong to expert e).
 // GEMM 1: H[entry, :F] = silu(x Wg_e) * (x Wu_e), x = X[perm_token[entry]].

@@ -120,13 +120,17 @@ __global__ __launch_bounds__(256) void k_attn_bf16(
             const float m_new = fmaxf(m_run[qb], mx);
             const float base = (m_new == -INFINITY) ? 0.f : m_new;
             const float alpha = exp2f(m_run[qb] - base);
+            // P = hi + lo in two bf16 parts (~16 significant bits): the softmax
+            // weights stay fp32-accurate through the bf16 MFMA.
             float psum = 0.f;
-            AFrag pf;
+            AFrag pf, pl;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float p = exp2f(sc[i] - base);
                 psum += p;
-                pf.h[i] = f32_to_bf16(p);
+                const bf16_t hi = f32_to_bf16(p);
+                pf.h[i] = hi;
+                pl.h[i] = f32_to_bf16(p - bf16_to_f32(hi));
             }
             l_run[qb] = l_run[qb] * alpha + psum;
             m_run[qb] = m_new;
@@ -134,6 +138,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(
             for (int dt = 0; dt < 8; ++dt) {
                 o[qb][dt] *= alpha;
                 o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt].b, pf.b, o[qb][dt],
+                                                                    0, 0, 0);
+                o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt].b, pl.b, o[qb][dt],
                                                                     0, 0, 0);
             }
         }

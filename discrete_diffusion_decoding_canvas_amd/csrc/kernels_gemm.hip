@@ -10,22 +10,35 @@
 //   * weights are pre-packed at load time into the exact MFMA B-operand lane
 //     order, so every weight load is one coalesced 16-byte load per lane
 //     (1 KiB per wave, contiguous) straight into registers;
-//   * the four waves of a workgroup split the reduction (K) dimension, so a
-//     workgroup covers a narrow 64-column slab with full memory-level
-//     parallelism, and the partial tiles are summed once through LDS;
+//   * the waves of a workgroup split the reduction (K) dimension, so a
+//     workgroup covers a narrow 64-column slab with many bytes in flight, and
+//     the partial tiles are summed once through LDS in a fixed order;
+//   * each wave keeps kPrefetch k-steps of operands in flight in registers
+//     (a rolling buffer), which hides HBM latency without LDS staging;
 //   * tokens sit on the 16-row MFMA side (v_mfma_f32_16x16x32_bf16, or
 //     v_mfma_f32_16x16x32_fp8_fp8 for e4m3 experts), 32-row chunks per pass;
 //   * the SwiGLU of the first expert GEMM runs in the epilogue (gate and up
-//     columns are interleaved per 16-column group at pack time).
+//     columns are interleaved per 16-column group at pack time);
+//   * narrow GEMMs (the router, N = E) split K across workgroups as well and
+//     leave the partial sums to their consumer, which adds them in order.
 #include "kernels.h"
 
 namespace dg {
+
+#ifndef DG_GEMM_WAVES
+#define DG_GEMM_WAVES 8
+#endif
+#ifndef DG_GEMM_PREFETCH
+#define DG_GEMM_PREFETCH 3
+#endif
 
 constexpr int kTileM = 32;   // rows per chunk (2 MFMA row tiles)
 constexpr int kTileN = 64;   // weight columns per workgroup (4 MFMA column groups)
 constexpr int kMT = 2;
 constexpr int kNT = 4;
-constexpr int kWaves = 4;
+constexpr int kWaves = DG_GEMM_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPrefetch = DG_GEMM_PREFETCH;
 
 union Frag16 {
     uint4 u;
@@ -36,77 +49,76 @@ union Frag16 {
 DG_DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 DG_DEV long ld8(const void* p) { return *reinterpret_cast<const long*>(p); }
 
-// ------------------------------------------------------------------ main loops
-// bf16: A rows given per lane (row pointers for the two row tiles), B packed
-// [group][KB][64][8] starting at the workgroup's first column group.
-DG_DEV void mainloop_bf16(const bf16_t* a0, const bf16_t* a1, const bf16_t* bgrp, int KB,
-                          int kb_begin, int kb_end, f32x4_t (&acc)[kMT][kNT]) {
-    const int lane = threadIdx.x & 63;
+struct Stage {
+    Frag16 a[kMT];
+    Frag16 b[kNT];
+};
+
+// ------------------------------------------------------------------ main loop
+// A rows given per lane (row pointers for the two row tiles), B packed
+// [group][KB][64 lanes][16 bytes] starting at the workgroup's first column group.
+// bf16: one k-step = 32 elements; fp8: one k-step = 64 codes (two MFMAs).
+template <bool FP8>
+DG_DEV void load_stage(Stage& st, const uint8_t* a0, const uint8_t* a1, const uint8_t* bgrp,
+                       size_t gstride, int kb, int lane) {
     const int koff = 8 * (lane >> 4);
-    const size_t gstride = (size_t)KB * 512;
-    if (kb_begin >= kb_end) return;
-    Frag16 ca[kMT], cb[kNT], na[kMT], nb[kNT];
-    auto load = [&](int kb, Frag16 (&fa)[kMT], Frag16 (&fb)[kNT]) {
-        fa[0].u = ld16(a0 + kb * 32 + koff);
-        fa[1].u = ld16(a1 + kb * 32 + koff);
+    if (FP8) {
+        st.a[0].l.lo = ld8(a0 + kb * 64 + koff);
+        st.a[0].l.hi = ld8(a0 + kb * 64 + 32 + koff);
+        st.a[1].l.lo = ld8(a1 + kb * 64 + koff);
+        st.a[1].l.hi = ld8(a1 + kb * 64 + 32 + koff);
+    } else {
+        st.a[0].u = ld16(a0 + (kb * 32 + koff) * 2);
+        st.a[1].u = ld16(a1 + (kb * 32 + koff) * 2);
+    }
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-            fb[nt].u = ld16(bgrp + nt * gstride + ((size_t)kb * 64 + lane) * 8);
-    };
-    load(kb_begin, ca, cb);
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-        if (kb + 1 < kb_end) load(kb + 1, na, nb);
+    for (int nt = 0; nt < kNT; ++nt)
+        st.b[nt].u = ld16(bgrp + nt * gstride + ((size_t)kb * 64 + lane) * 16);
+}
+
+template <bool FP8>
+DG_DEV void mma_stage(const Stage& st, f32x4_t (&acc)[kMT][kNT]) {
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[mt].b, cb[nt].b,
+        for (int nt = 0; nt < kNT; ++nt) {
+            if (FP8) {
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                    st.a[mt].l.lo, st.b[nt].l.lo, acc[mt][nt], 0, 0, 0);
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                    st.a[mt].l.hi, st.b[nt].l.hi, acc[mt][nt], 0, 0, 0);
+            } else {
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.a[mt].b, st.b[nt].b,
                                                                       acc[mt][nt], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < kMT; ++i) ca[i] = na[i];
-#pragma unroll
-        for (int i = 0; i < kNT; ++i) cb[i] = nb[i];
-    }
-}
-
-// fp8: K step 64 per packed block (two MFMA k-steps per 16-byte lane load).
-// A rows are e4m3 row-major; a lane reads bytes [8g, 8g+8) and [32+8g, 32+8g+8).
-DG_DEV void mainloop_fp8(const uint8_t* a0, const uint8_t* a1, const uint8_t* bgrp, int KB64,
-                         int kb_begin, int kb_end, f32x4_t (&acc)[kMT][kNT]) {
-    const int lane = threadIdx.x & 63;
-    const int koff = 8 * (lane >> 4);
-    const size_t gstride = (size_t)KB64 * 1024;
-    if (kb_begin >= kb_end) return;
-    Frag16 ca[kMT], cb[kNT], na[kMT], nb[kNT];
-    auto load = [&](int kb, Frag16 (&fa)[kMT], Frag16 (&fb)[kNT]) {
-        fa[0].l.lo = ld8(a0 + kb * 64 + koff);
-        fa[0].l.hi = ld8(a0 + kb * 64 + 32 + koff);
-        fa[1].l.lo = ld8(a1 + kb * 64 + koff);
-        fa[1].l.hi = ld8(a1 + kb * 64 + 32 + koff);
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-            fb[nt].u = ld16(bgrp + nt * gstride + ((size_t)kb * 64 + lane) * 16);
-    };
-    load(kb_begin, ca, cb);
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-        if (kb + 1 < kb_end) load(kb + 1, na, nb);
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-                    ca[mt].l.lo, cb[nt].l.lo, acc[mt][nt], 0, 0, 0);
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-                    ca[mt].l.hi, cb[nt].l.hi, acc[mt][nt], 0, 0, 0);
             }
+        }
+}
+
+template <bool FP8>
+DG_DEV void mainloop(const uint8_t* a0, const uint8_t* a1, const uint8_t* bgrp, int KB,
+                     int kb_begin, int kb_end, f32x4_t (&acc)[kMT][kNT]) {
+    const int lane = threadIdx.x & 63;
+    const size_t gstride = (size_t)KB * 1024;   // bytes per packed column group
+    Stage buf[kPrefetch];
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) ca[i] = na[i];
+    for (int s = 0; s < kPrefetch - 1; ++s)
+        if (kb_begin + s < kb_end) load_stage<FP8>(buf[s], a0, a1, bgrp, gstride, kb_begin + s, lane);
+    for (int kb = kb_begin; kb < kb_end; kb += kPrefetch) {
 #pragma unroll
-        for (int i = 0; i < kNT; ++i) cb[i] = nb[i];
+        for (int u = 0; u < kPrefetch; ++u) {
+            const int k = kb + u;
+            if (k < kb_end) {
+                const int kn = k + kPrefetch - 1;
+                if (kn < kb_end)
+                    load_stage<FP8>(buf[(u + kPrefetch - 1) % kPrefetch], a0, a1, bgrp, gstride,
+                                    kn, lane);
+                mma_stage<FP8>(buf[u], acc);
+            }
+        }
     }
 }
 
-// Sum the four waves' partial tiles into red[0][r][c] (r < 32, c < 64).
+// Sum the waves' partial tiles, in wave order, into red[0][r][c] (r < 32, c < 64).
 DG_DEV void reduce_waves(f32x4_t (&acc)[kMT][kNT], float (*red)[kTileM][kTileN]) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -117,51 +129,62 @@ DG_DEV void reduce_waves(f32x4_t (&acc)[kMT][kNT], float (*red)[kTileM][kTileN])
             for (int j = 0; j < 4; ++j)
                 red[w][16 * mt + 4 * (lane >> 4) + j][16 * nt + (lane & 15)] = acc[mt][nt][j];
     __syncthreads();
-    for (int e = threadIdx.x; e < kTileM * kTileN; e += 256) {
+    for (int e = threadIdx.x; e < kTileM * kTileN; e += kThreads) {
         const int r = e >> 6, c = e & 63;
-        red[0][r][c] = red[0][r][c] + red[1][r][c] + red[2][r][c] + red[3][r][c];
+        float v = red[0][r][c];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) v += red[i][r][c];
+        red[0][r][c] = v;
     }
     __syncthreads();
 }
 
-DG_DEV void split_k(int KB, int& b, int& e) {
-    const int w = threadIdx.x >> 6;
-    const int per = KB / kWaves, rem = KB % kWaves;
-    b = w * per + (w < rem ? w : rem);
-    e = b + per + (w < rem ? 1 : 0);
+DG_DEV void split_range(int KB, int parts, int idx, int& b, int& e) {
+    const int per = KB / parts, rem = KB % parts;
+    b = idx * per + (idx < rem ? idx : rem);
+    e = b + per + (idx < rem ? 1 : 0);
+}
+
+DG_DEV void zero_acc(f32x4_t (&acc)[kMT][kNT]) {
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
 // ------------------------------------------------------------------ dense bf16 GEMM
+// grid (N / 64, ceil(M / 32), ksplit).  With ksplit > 1 workgroup z sums its
+// share of K and stores the partial tile at C + z * M * ldc (store epilogue).
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ A, int lda, int M,
-                                                   const bf16_t* __restrict__ Bp, int K, int N,
-                                                   float* __restrict__ C, int ldc) {
+__global__ __launch_bounds__(kThreads) void k_gemm_bf16(const bf16_t* __restrict__ A, int lda,
+                                                        int M, const bf16_t* __restrict__ Bp,
+                                                        int K, int N, float* __restrict__ C,
+                                                        int ldc) {
     __shared__ float red[kWaves][kTileM][kTileN];
     const int lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * kTileN;
     const int m0 = blockIdx.y * kTileM;
     const int KB = K >> 5;
-    const int g0 = n0 >> 4;
     f32x4_t acc[kMT][kNT];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    zero_acc(acc);
     int r0 = m0 + (lane & 15), r1 = m0 + 16 + (lane & 15);
     r0 = r0 < M ? r0 : M - 1;
     r1 = r1 < M ? r1 : M - 1;
-    int kb0, kb1;
-    split_k(KB, kb0, kb1);
-    mainloop_bf16(A + (size_t)r0 * lda, A + (size_t)r1 * lda, Bp + (size_t)g0 * KB * 512, KB,
-                  kb0, kb1, acc);
+    int zb, ze, kb0, kb1;
+    split_range(KB, gridDim.z, blockIdx.z, zb, ze);
+    split_range(ze - zb, kWaves, threadIdx.x >> 6, kb0, kb1);
+    mainloop<false>((const uint8_t*)(A + (size_t)r0 * lda), (const uint8_t*)(A + (size_t)r1 * lda),
+                    (const uint8_t*)(Bp + (size_t)(n0 >> 4) * KB * 512), KB, zb + kb0, zb + kb1,
+                    acc);
     reduce_waves(acc, red);
-    for (int e = threadIdx.x; e < kTileM * kTileN; e += 256) {
+    float* Cz = C + (size_t)blockIdx.z * M * ldc;
+    for (int e = threadIdx.x; e < kTileM * kTileN; e += kThreads) {
         const int r = e >> 6, c = e & 63;
         const int m = m0 + r, n = n0 + c;
         if (m >= M) continue;
         const float v = red[0][r][c];
-        if (EPI == kEpiStoreF32) C[(size_t)m * ldc + n] = v;
-        else C[(size_t)m * ldc + n] += v;
+        if (EPI == kEpiStoreF32) Cz[(size_t)m * ldc + n] = v;
+        else Cz[(size_t)m * ldc + n] += v;
     }
 }
 
@@ -216,12 +239,12 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 // grid (2F / 64 column slabs, E).  Each workgroup loops over its expert's
 // 32-row chunks; weight slab columns are [g_j | u_j | g_j+1 | u_j+1] (16 each).
 template <bool FP8>
-__global__ __launch_bounds__(256) void k_moe1_mfma(const void* __restrict__ X, int d, int F,
-                                                   const int32_t* __restrict__ perm_token,
-                                                   const int32_t* __restrict__ offsets,
-                                                   const void* __restrict__ W1,
-                                                   const float* __restrict__ s1,
-                                                   void* __restrict__ H) {
+__global__ __launch_bounds__(kThreads) void k_moe1_mfma(const void* __restrict__ X, int d, int F,
+                                                        const int32_t* __restrict__ perm_token,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const void* __restrict__ W1,
+                                                        const float* __restrict__ s1,
+                                                        void* __restrict__ H) {
     __shared__ float red[kWaves][kTileM][kTileN];
     const int e = blockIdx.y;
     const int off = offsets[e];
@@ -232,29 +255,23 @@ __global__ __launch_bounds__(256) void k_moe1_mfma(const void* __restrict__ X, i
     const int N1 = 2 * F;
     const int KB = FP8 ? (d >> 6) : (d >> 5);
     int kb0, kb1;
-    split_k(KB, kb0, kb1);
-    const size_t gsize = FP8 ? (size_t)KB * 1024 : (size_t)KB * 512 * 2;   // bytes per group
-    const uint8_t* wexp = (const uint8_t*)W1 + (size_t)e * (N1 >> 4) * gsize;
-    const uint8_t* bgrp = wexp + (size_t)(n0 >> 4) * gsize;
+    split_range(KB, kWaves, threadIdx.x >> 6, kb0, kb1);
+    const size_t gsize = (size_t)KB * 1024;      // bytes per packed column group
+    const uint8_t* bgrp = (const uint8_t*)W1 + (size_t)e * (N1 >> 4) * gsize +
+                          (size_t)(n0 >> 4) * gsize;
+    const size_t xrow = FP8 ? (size_t)d : (size_t)d * 2;
     for (int mc = 0; mc < n_e; mc += kTileM) {
         f32x4_t acc[kMT][kNT];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        zero_acc(acc);
         int e0 = mc + (lane & 15), e1 = mc + 16 + (lane & 15);
         e0 = off + (e0 < n_e ? e0 : n_e - 1);
         e1 = off + (e1 < n_e ? e1 : n_e - 1);
         const int64_t t0 = perm_token[e0], t1 = perm_token[e1];
-        if (FP8)
-            mainloop_fp8((const uint8_t*)X + t0 * d, (const uint8_t*)X + t1 * d, bgrp, KB, kb0,
-                         kb1, acc);
-        else
-            mainloop_bf16((const bf16_t*)X + t0 * d, (const bf16_t*)X + t1 * d,
-                          (const bf16_t*)bgrp, KB, kb0, kb1, acc);
+        mainloop<FP8>((const uint8_t*)X + t0 * xrow, (const uint8_t*)X + t1 * xrow, bgrp, KB, kb0,
+                      kb1, acc);
         reduce_waves(acc, red);
         const int h0 = n0 >> 1;
-        for (int q = threadIdx.x; q < kTileM * (kTileN / 2); q += 256) {
+        for (int q = threadIdx.x; q < kTileM * (kTileN / 2); q += kThreads) {
             const int r = q >> 5, hc = q & 31;
             if (mc + r >= n_e) continue;
             const int cg = ((hc >> 4) << 5) + (hc & 15);
@@ -275,11 +292,11 @@ __global__ __launch_bounds__(256) void k_moe1_mfma(const void* __restrict__ X, i
 // ------------------------------------------------------------------ expert GEMM 2 (MFMA)
 // grid (d / 64 column slabs, E): Y[entry, n] = H[entry, :] Wd_e[:, n].
 template <bool FP8>
-__global__ __launch_bounds__(256) void k_moe2_mfma(const void* __restrict__ H, int d, int F,
-                                                   const int32_t* __restrict__ offsets,
-                                                   const void* __restrict__ W2,
-                                                   const float* __restrict__ s2,
-                                                   float* __restrict__ Y) {
+__global__ __launch_bounds__(kThreads) void k_moe2_mfma(const void* __restrict__ H, int d, int F,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const void* __restrict__ W2,
+                                                        const float* __restrict__ s2,
+                                                        float* __restrict__ Y) {
     __shared__ float red[kWaves][kTileM][kTileN];
     const int e = blockIdx.y;
     const int off = offsets[e];
@@ -289,27 +306,21 @@ __global__ __launch_bounds__(256) void k_moe2_mfma(const void* __restrict__ H, i
     const int n0 = blockIdx.x * kTileN;
     const int KB = FP8 ? (F >> 6) : (F >> 5);
     int kb0, kb1;
-    split_k(KB, kb0, kb1);
-    const size_t gsize = FP8 ? (size_t)KB * 1024 : (size_t)KB * 512 * 2;
+    split_range(KB, kWaves, threadIdx.x >> 6, kb0, kb1);
+    const size_t gsize = (size_t)KB * 1024;
     const uint8_t* bgrp = (const uint8_t*)W2 + (size_t)e * (d >> 4) * gsize +
                           (size_t)(n0 >> 4) * gsize;
-    const size_t esz = FP8 ? 1 : 2;
+    const size_t hrow = FP8 ? (size_t)F : (size_t)F * 2;
     for (int mc = 0; mc < n_e; mc += kTileM) {
         f32x4_t acc[kMT][kNT];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        zero_acc(acc);
         int e0 = mc + (lane & 15), e1 = mc + 16 + (lane & 15);
         e0 = off + (e0 < n_e ? e0 : n_e - 1);
         e1 = off + (e1 < n_e ? e1 : n_e - 1);
-        const uint8_t* a0 = (const uint8_t*)H + (size_t)e0 * F * esz;
-        const uint8_t* a1 = (const uint8_t*)H + (size_t)e1 * F * esz;
-        if (FP8) mainloop_fp8(a0, a1, bgrp, KB, kb0, kb1, acc);
-        else mainloop_bf16((const bf16_t*)a0, (const bf16_t*)a1, (const bf16_t*)bgrp, KB, kb0,
-                           kb1, acc);
+        mainloop<FP8>((const uint8_t*)H + (size_t)e0 * hrow, (const uint8_t*)H + (size_t)e1 * hrow,
+                      bgrp, KB, kb0, kb1, acc);
         reduce_waves(acc, red);
-        for (int q = threadIdx.x; q < kTileM * kTileN; q += 256) {
+        for (int q = threadIdx.x; q < kTileM * kTileN; q += kThreads) {
             const int r = q >> 6, c = q & 63;
             if (mc + r >= n_e) continue;
             float v = red[0][r][c];
@@ -367,9 +378,10 @@ __global__ void k_moe2_f32(const float* __restrict__ H, int d, int F,
 
 // ================================================================== launchers
 hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const void* B, int K,
-                       int N, float* C, int ldc, hipStream_t s) {
+                       int N, float* C, int ldc, hipStream_t s, int ksplit) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if (dtype == kF32) {
+        if (ksplit != 1) return hipErrorInvalidValue;
         dim3 grid((N + 63) / 64, (M + 63) / 64);
         if (epi == kEpiStoreF32)
             k_gemm_f32<kEpiStoreF32><<<grid, 256, 0, s>>>((const float*)A, lda, M,
@@ -378,14 +390,15 @@ hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const 
             k_gemm_f32<kEpiAddF32><<<grid, 256, 0, s>>>((const float*)A, lda, M,
                                                         (const float*)B, K, N, C, ldc);
     } else {
-        if ((K & 31) || (N % kTileN)) return hipErrorInvalidValue;
-        dim3 grid((N + kTileN - 1) / kTileN, (M + kTileM - 1) / kTileM);
+        if ((K & 31) || (N % kTileN) || ksplit < 1 || (ksplit > 1 && epi != kEpiStoreF32))
+            return hipErrorInvalidValue;
+        dim3 grid(N / kTileN, (M + kTileM - 1) / kTileM, ksplit);
         if (epi == kEpiStoreF32)
-            k_gemm_bf16<kEpiStoreF32><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, M,
-                                                           (const bf16_t*)B, K, N, C, ldc);
+            k_gemm_bf16<kEpiStoreF32><<<grid, kThreads, 0, s>>>((const bf16_t*)A, lda, M,
+                                                                (const bf16_t*)B, K, N, C, ldc);
         else
-            k_gemm_bf16<kEpiAddF32><<<grid, 256, 0, s>>>((const bf16_t*)A, lda, M,
-                                                         (const bf16_t*)B, K, N, C, ldc);
+            k_gemm_bf16<kEpiAddF32><<<grid, kThreads, 0, s>>>((const bf16_t*)A, lda, M,
+                                                              (const bf16_t*)B, K, N, C, ldc);
     }
     return hipGetLastError();
 }
@@ -402,9 +415,9 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
     } else {
         dim3 grid((2 * F) / kTileN, E);
         if (dtype == kFP8)
-            k_moe1_mfma<true><<<grid, 256, 0, s>>>(X, d, F, perm_token, offsets, w.w1, w.s1, H);
+            k_moe1_mfma<true><<<grid, kThreads, 0, s>>>(X, d, F, perm_token, offsets, w.w1, w.s1, H);
         else
-            k_moe1_mfma<false><<<grid, 256, 0, s>>>(X, d, F, perm_token, offsets, w.w1, w.s1, H);
+            k_moe1_mfma<false><<<grid, kThreads, 0, s>>>(X, d, F, perm_token, offsets, w.w1, w.s1, H);
     }
     return hipGetLastError();
 }
@@ -420,9 +433,9 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
     } else {
         dim3 grid(d / kTileN, E);
         if (dtype == kFP8)
-            k_moe2_mfma<true><<<grid, 256, 0, s>>>(H, d, F, offsets, w.w2, w.s2, Y);
+            k_moe2_mfma<true><<<grid, kThreads, 0, s>>>(H, d, F, offsets, w.w2, w.s2, Y);
         else
-            k_moe2_mfma<false><<<grid, 256, 0, s>>>(H, d, F, offsets, w.w2, w.s2, Y);
+            k_moe2_mfma<false><<<grid, kThreads, 0, s>>>(H, d, F, offsets, w.w2, w.s2, Y);
     }
     return hipGetLastError();
 }

@@ -136,121 +136,16 @@ __global__ void k_read_kv(const T* __restrict__ cache, int Hkv, int D, int64_t r
                        : cache[((int64_t)h * rows + row0 + p) * D + t];
 }
 
-// ------------------------------------------------------------------ router top-k
-// One wave per token: rank logits (descending, ties to the lower expert id),
-// gates = softmax over the k chosen logits (= p_e / sum of chosen p).
-__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int M,
-                                                     int E, int k, int32_t* __restrict__ idx,
-                                                     float* __restrict__ gates) {
-    const int wave = (blockIdx.x * 4) + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (wave >= M) return;
-    const float* r = logits + (int64_t)wave * E;
-    float v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        int e = lane + 64 * q;
-        v[q] = e < E ? r[e] : -INFINITY;
-    }
-    float sel_v[16];
-    int sel_e[16];
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            int e = lane + 64 * q;
-            if (e < E && (v[q] > bv || (v[q] == bv && e < be))) { bv = v[q]; be = e; }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            float ov = __shfl_xor(bv, o, 64);
-            int oe = __shfl_xor(be, o, 64);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-        }
-        sel_v[j] = bv;
-        sel_e[j] = be;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (lane + 64 * q == be) v[q] = -INFINITY;
-    }
-    if (lane == 0) {
-        float mx = sel_v[0], s = 0.f;
-        for (int j = 0; j < k; ++j) s += expf(sel_v[j] - mx);
-        for (int j = 0; j < k; ++j) {
-            idx[(int64_t)wave * k + j] = sel_e[j];
-            gates[(int64_t)wave * k + j] = expf(sel_v[j] - mx) / s;
-        }
-    }
-}
-
-// ------------------------------------------------------------------ permutation
-// Entries are (token, slot) pairs, flat id = token * k + slot, grouped by expert,
-// stable in flat id.  Chunks of kPermChunk entries per workgroup.
-__global__ __launch_bounds__(256) void k_moe_count(const int32_t* __restrict__ idx, int n,
-                                                   int E, int32_t* __restrict__ counts) {
-    extern __shared__ int32_t cnt[];
-    for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
-    __syncthreads();
-    const int base = blockIdx.x * kPermChunk;
-    for (int i = threadIdx.x; i < kPermChunk; i += 256) {
-        int f = base + i;
-        if (f < n) atomicAdd(&cnt[idx[f]], 1);
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
-}
-
-// One workgroup: base[c][e] = offset[e] + sum_{c' < c} counts[c'][e];
-// offsets[e] = exclusive scan of per-expert totals, offsets[E] = n.
-__global__ __launch_bounds__(1024) void k_moe_scan(const int32_t* __restrict__ counts,
-                                                   int n_chunks, int E,
-                                                   int32_t* __restrict__ base,
-                                                   int32_t* __restrict__ offsets) {
-    extern __shared__ int32_t tot[];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int run = 0;
-        for (int c = 0; c < n_chunks; ++c) {
-            base[(int64_t)c * E + e] = run;
-            run += counts[(int64_t)c * E + e];
-        }
-        tot[e] = run;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            int t = tot[e];
-            tot[e] = run;
-            offsets[e] = run;
-            run += t;
-        }
-        offsets[E] = run;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        for (int c = 0; c < n_chunks; ++c) base[(int64_t)c * E + e] += tot[e];
-}
-
-__global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__ idx, int n,
-                                                     int E, int k,
-                                                     const int32_t* __restrict__ base,
-                                                     int32_t* __restrict__ perm_token,
-                                                     int32_t* __restrict__ inv) {
-    __shared__ int32_t ex[kPermChunk];
-    const int c0 = blockIdx.x * kPermChunk;
-    for (int i = threadIdx.x; i < kPermChunk; i += 256)
-        ex[i] = (c0 + i < n) ? idx[c0 + i] : -1;
-    __syncthreads();
-    for (int i = threadIdx.x; i < kPermChunk; i += 256) {
-        const int e = ex[i];
-        if (e < 0) continue;
-        int rank = 0;
-        for (int j = 0; j < i; ++j) rank += (ex[j] == e);
-        const int pos = base[(int64_t)blockIdx.x * E + e] + rank;
-        perm_token[pos] = (c0 + i) / k;
-        inv[c0 + i] = pos;
-    }
+template <typename T, bool VPACKED>
+__global__ void k_write_kv(T* __restrict__ cache, int Hkv, int D, int64_t rows, int64_t row0,
+                           int64_t n, const T* __restrict__ src) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)Hkv * n * D) return;
+    const int t = (int)(idx % D);
+    const int64_t p = (idx / D) % n;
+    const int h = (int)(idx / ((int64_t)D * n));
+    if (VPACKED) cache[vt_index(h, t, row0 + p, D, rows)] = src[idx];
+    else cache[((int64_t)h * rows + row0 + p) * D + t] = src[idx];
 }
 
 // ------------------------------------------------------------------ combine (+ RMSNorm)
@@ -265,32 +160,46 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y
                                                      T* __restrict__ a, uint8_t* __restrict__ a8,
                                                      T* __restrict__ out) {
     __shared__ float red[4];
-    __shared__ float g_s[16];
-    __shared__ int32_t r_s[16];
     const int64_t t = blockIdx.x;
-    if (threadIdx.x < k) {
-        g_s[threadIdx.x] = gates[t * k + threadIdx.x];
-        r_s[threadIdx.x] = inv[t * k + threadIdx.x];
+    float g[kMaxTopK];
+    const float* yr[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        g[j] = j < k ? gates[t * k + j] : 0.f;
+        yr[j] = Y + (int64_t)(j < k ? inv[t * k + j] : inv[t * k]) * d;
     }
-    __syncthreads();
+    float xs[kCombineCols];
     float ss = 0.f;
-    for (int c = threadIdx.x; c < d; c += 256) {
-        float y = 0.f;
-        for (int j = 0; j < k; ++j) y += g_s[j] * Y[(int64_t)r_s[j] * d + c];
-        if (MODE == 0) {
-            float nx = x[t * d + c] + y;
-            x[t * d + c] = nx;
-            ss += nx * nx;
-        } else {
-            out[t * d + c] = from_f32<T>(y);
+#pragma unroll
+    for (int i = 0; i < kCombineCols; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < d) {
+            float v[kMaxTopK];
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) v[j] = j < k ? yr[j][c] : 0.f;
+            float y = 0.f;
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) y += g[j] * v[j];   // slot order
+            if (MODE == 0) {
+                const float nx = x[t * d + c] + y;
+                x[t * d + c] = nx;
+                xs[i] = nx;
+                ss += nx * nx;
+            } else {
+                out[t * d + c] = from_f32<T>(y);
+            }
         }
     }
     if (MODE == 0 && a != nullptr) {
-        float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-        for (int c = threadIdx.x; c < d; c += 256) {
-            T av = from_f32<T>(x[t * d + c] * r);
-            a[t * d + c] = av;
-            if (a8) a8[t * d + c] = (uint8_t)f32_to_e4m3(to_f32<T>(av));
+        const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
+#pragma unroll
+        for (int i = 0; i < kCombineCols; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            if (c < d) {
+                const T av = from_f32<T>(xs[i] * r);
+                a[t * d + c] = av;
+                if (a8) a8[t * d + c] = (uint8_t)f32_to_e4m3(to_f32<T>(av));
+            }
         }
     }
 }
@@ -523,16 +432,20 @@ hipError_t launch_read_kv(int dtype, bool vpacked, const void* cache, int Hkv, i
     LAUNCH_CHECK();
 }
 
-hipError_t launch_router_permute(const float* logits, int M, int E, int k, int32_t* idx,
-                                 float* gates, int32_t* counts, int32_t* base, int32_t* offsets,
-                                 int32_t* perm_token, int32_t* inv, hipStream_t s) {
-    if (M <= 0) return hipSuccess;
-    k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, M, E, k, idx, gates);
-    const int n = M * k;
-    const int n_chunks = (n + kPermChunk - 1) / kPermChunk;
-    k_moe_count<<<n_chunks, 256, E * sizeof(int32_t), s>>>(idx, n, E, counts);
-    k_moe_scan<<<1, 1024, E * sizeof(int32_t), s>>>(counts, n_chunks, E, base, offsets);
-    k_moe_scatter<<<n_chunks, 256, 0, s>>>(idx, n, E, k, base, perm_token, inv);
+hipError_t launch_write_kv(int dtype, bool vpacked, void* cache, int Hkv, int D, int64_t rows,
+                           int64_t row0, int64_t n, const void* src, hipStream_t s) {
+    int64_t total = (int64_t)Hkv * n * D;
+    if (total <= 0) return hipSuccess;
+    unsigned blocks = (unsigned)((total + 255) / 256);
+    if (dtype == kF32)
+        k_write_kv<float, false><<<blocks, 256, 0, s>>>((float*)cache, Hkv, D, rows, row0, n,
+                                                        (const float*)src);
+    else if (vpacked)
+        k_write_kv<bf16_t, true><<<blocks, 256, 0, s>>>((bf16_t*)cache, Hkv, D, rows, row0, n,
+                                                        (const bf16_t*)src);
+    else
+        k_write_kv<bf16_t, false><<<blocks, 256, 0, s>>>((bf16_t*)cache, Hkv, D, rows, row0, n,
+                                                         (const bf16_t*)src);
     LAUNCH_CHECK();
 }
 

@@ -1,0 +1,178 @@
+// MoE routing and token permutation (gfx950).
+//
+// The decoder's mixture-of-experts FFN (DiffusionGemma technical-report
+// summary, Experiment: a small number of active experts among many): router
+// softmax over the experts, top-k with gates renormalised over the k chosen,
+// then the (token, slot) entries grouped by expert for the grouped GEMMs.
+//
+// Top-k: one wave per token.  The logits go to LDS and every lane ranks its
+// own logits against all of them (rank = number of larger logits plus equal
+// ones with a lower expert id), so the k winners land at their rank in one
+// pass with no serial reduction chain.  Router logits may arrive as several
+// split-K partial sums; they are added here in a fixed order.
+//
+// Permutation: per-expert counts with LDS integer atomics, one exclusive scan,
+// then each entry takes the next free row of its expert.  The order of rows
+// inside an expert is not fixed, but every expert-GEMM output row depends only
+// on its own input row, so the results are bit-identical across runs.
+#include "kernels.h"
+
+namespace dg {
+
+constexpr int kMaxExperts = 256;
+
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int nsplit,
+                                                     int M, int E, int k,
+                                                     int32_t* __restrict__ idx,
+                                                     float* __restrict__ gates) {
+    __shared__ float lg[4][kMaxExperts];
+    __shared__ float sv[4][16];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + w;
+    if (t >= M) return;   // no block-level synchronisation below: only wave-level LDS use
+    for (int e = lane; e < E; e += 64) {
+        float v = 0.f;
+        for (int sp = 0; sp < nsplit; ++sp) v += logits[((int64_t)sp * M + t) * E + e];
+        lg[w][e] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int e = lane; e < E; e += 64) {
+        const float v = lg[w][e];
+        int rank = 0;
+        for (int j = 0; j < E; ++j) {
+            const float u = lg[w][j];
+            rank += (u > v) || (u == v && j < e);
+        }
+        if (rank < k) {
+            idx[(int64_t)t * k + rank] = e;
+            sv[w][rank] = v;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane < k) {
+        const float mx = sv[w][0];
+        float s = 0.f;
+        for (int j = 0; j < k; ++j) s += expf(sv[w][j] - mx);
+        gates[(int64_t)t * k + lane] = expf(sv[w][lane] - mx) / s;
+    }
+}
+
+// One workgroup for up to kPermSmall entries: counts, scan, row assignment.
+constexpr int kPermSmall = 8192;
+
+__global__ __launch_bounds__(1024) void k_moe_permute_small(const int32_t* __restrict__ idx, int n,
+                                                            int E, int k,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ perm_token,
+                                                            int32_t* __restrict__ inv) {
+    __shared__ int32_t cnt[kMaxExperts];
+    __shared__ int32_t off[kMaxExperts + 1];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    for (int f = threadIdx.x; f < n; f += blockDim.x) atomicAdd(&cnt[idx[f]], 1);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = run;
+            run += cnt[e];
+        }
+        off[E] = run;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    for (int f = threadIdx.x; f < n; f += blockDim.x) {
+        const int e = idx[f];
+        const int pos = off[e] + atomicAdd(&cnt[e], 1);
+        perm_token[pos] = f / k;
+        inv[f] = pos;
+    }
+}
+
+// Larger batches (prefill chunks): per-chunk counts, one scan, per-chunk assignment.
+__global__ __launch_bounds__(256) void k_moe_count(const int32_t* __restrict__ idx, int n,
+                                                   int E, int32_t* __restrict__ counts) {
+    __shared__ int32_t cnt[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+    __syncthreads();
+    const int base = blockIdx.x * kPermChunk;
+    for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+        const int f = base + i;
+        if (f < n) atomicAdd(&cnt[idx[f]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ counts,
+                                                  int n_chunks, int E,
+                                                  int32_t* __restrict__ base,
+                                                  int32_t* __restrict__ offsets) {
+    __shared__ int32_t tot[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int c = 0; c < n_chunks; ++c) {
+            base[(int64_t)c * E + e] = run;
+            run += counts[(int64_t)c * E + e];
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            const int t = tot[e];
+            tot[e] = run;
+            offsets[e] = run;
+            run += t;
+        }
+        offsets[E] = run;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        for (int c = 0; c < n_chunks; ++c) base[(int64_t)c * E + e] += tot[e];
+}
+
+__global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__ idx, int n,
+                                                     int E, int k,
+                                                     const int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ perm_token,
+                                                     int32_t* __restrict__ inv) {
+    __shared__ int32_t fill[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += 256) fill[e] = 0;
+    __syncthreads();
+    const int c0 = blockIdx.x * kPermChunk;
+    for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+        const int f = c0 + i;
+        if (f >= n) continue;
+        const int e = idx[f];
+        const int pos = base[(int64_t)blockIdx.x * E + e] + atomicAdd(&fill[e], 1);
+        perm_token[pos] = f / k;
+        inv[f] = pos;
+    }
+}
+
+hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, int k,
+                                 int32_t* idx, float* gates, int32_t* counts, int32_t* base,
+                                 int32_t* offsets, int32_t* perm_token, int32_t* inv,
+                                 hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (E > kMaxExperts || k > 16) return hipErrorInvalidValue;
+    k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
+    const int n = M * k;
+    if (n <= kPermSmall) {
+        k_moe_permute_small<<<1, 1024, 0, s>>>(idx, n, E, k, offsets, perm_token, inv);
+    } else {
+        const int n_chunks = (n + kPermChunk - 1) / kPermChunk;
+        k_moe_count<<<n_chunks, 256, 0, s>>>(idx, n, E, counts);
+        k_moe_scan<<<1, 256, 0, s>>>(counts, n_chunks, E, base, offsets);
+        k_moe_scatter<<<n_chunks, 256, 0, s>>>(idx, n, E, k, base, perm_token, inv);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dg

@@ -177,6 +177,11 @@ class Workload:
 TINY_FP32 = Workload("tiny_fp32_2L_d256_V1024", n_layers=2, d_model=256, n_q_heads=4,
                      n_kv_heads=2, head_dim=64, n_experts=8, top_k=2, d_ff=512, vocab=1024,
                      prompt_len=64, act="f32", experts="f32")
+# Small bf16 model through the same MFMA kernels as the large ones; the prompt spans two
+# prefill chunks with a ragged tail.
+SMALL_BF16 = Workload("small_bf16_2L_d256_E64k4_V1024_P4296", n_layers=2, d_model=256,
+                      n_q_heads=4, n_kv_heads=2, head_dim=128, n_experts=64, top_k=4, d_ff=128,
+                      vocab=1024, prompt_len=4296)
 MOE26B = Workload("moe26b_30L_d2816_E128k8_V262144_P8192", n_layers=30, d_model=2816,
                   n_q_heads=16, n_kv_heads=8, head_dim=128, n_experts=128, top_k=8, d_ff=704,
                   vocab=262144, prompt_len=8192)

@@ -46,18 +46,43 @@ static inline uint16_t fx_f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+/* Both Box-Muller branches of one pair share the hash, log and square root. */
+static inline void fx_normal_pair(uint64_t seed, uint32_t tid, uint64_t pair, float* c, float* s) {
+    uint64_t h = fx_hash(seed, tid, pair);
+    float u1 = (float)(((h >> 41) << 1) | 1ull) * 0x1p-24f;
+    float u2 = (float)((h >> 8) & 0xFFFFFFull) * 0x1p-24f;
+    float r = sqrtf(-2.0f * logf(u1));
+    float th = 6.28318530717958647692f * u2;
+    *c = r * cosf(th);
+    *s = r * sinf(th);
+}
+
+#define FX_NORMAL_BODY(STORE)                                                      \
+    int64_t i0 = 0;                                                                \
+    if ((start & 1) && n > 0) { STORE(0, sigma * fx_normal_at(seed, tid, start)); i0 = 1; } \
+    int64_t npairs = ((int64_t)n - i0) / 2;                                        \
+    _Pragma("omp parallel for schedule(static)")                                   \
+    for (int64_t q = 0; q < npairs; ++q) {                                         \
+        float c, sn;                                                               \
+        fx_normal_pair(seed, tid, (start + (uint64_t)i0) / 2 + (uint64_t)q, &c, &sn); \
+        STORE(i0 + 2 * q, sigma * c);                                              \
+        STORE(i0 + 2 * q + 1, sigma * sn);                                         \
+    }                                                                              \
+    if (i0 + 2 * npairs < (int64_t)n)                                              \
+        STORE((int64_t)n - 1, sigma * fx_normal_at(seed, tid, start + n - 1));
+
 void fx_normal_f32(uint64_t seed, uint32_t tid, uint64_t start, uint64_t n, float sigma,
                    float* out) {
-    #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < (int64_t)n; ++i)
-        out[i] = sigma * fx_normal_at(seed, tid, start + (uint64_t)i);
+#define ST_F32(i, v) (out[(i)] = (v))
+    FX_NORMAL_BODY(ST_F32)
+#undef ST_F32
 }
 
 void fx_normal_bf16(uint64_t seed, uint32_t tid, uint64_t start, uint64_t n, float sigma,
                     uint16_t* out) {
-    #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < (int64_t)n; ++i)
-        out[i] = fx_f32_to_bf16(sigma * fx_normal_at(seed, tid, start + (uint64_t)i));
+#define ST_BF16(i, v) (out[(i)] = fx_f32_to_bf16(v))
+    FX_NORMAL_BODY(ST_BF16)
+#undef ST_BF16
 }
 
 void fx_uniform_ids(uint64_t seed, uint32_t tid, uint64_t start, uint64_t n, uint32_t vocab,

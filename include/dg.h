@@ -92,11 +92,15 @@ extern "C" {
  *                   (-1 where the position was locked on entry)
  *   DG_CAP_ROUTING  per layer: int32 idx [C, k] then float gates [C, k]
  *   DG_CAP_HIDDEN   per layer: float residual stream [C, d] after the layer
+ *   DG_CAP_ATTN     per layer: attention output [C, Hq*D] in act_dtype
+ *   DG_CAP_ROUTER_LOGITS per layer: float router logits [C, E]
  */
 #define DG_CAP_LOGITS 1u
 #define DG_CAP_STATS 2u
 #define DG_CAP_ROUTING 4u
 #define DG_CAP_HIDDEN 8u
+#define DG_CAP_ATTN 16u
+#define DG_CAP_ROUTER_LOGITS 32u
 
 typedef struct dg_model_cfg {
     int32_t n_layers;      /* L */
@@ -192,6 +196,11 @@ int dg_reset_context(dg_handle* h);
 /* Current committed context length and canvas index. */
 int dg_get_state(dg_handle* h, int64_t* n_ctx, int32_t* k_blk);
 
+/* Change which captures the following passes record (DG_CAP_* bits; 0 turns
+ * them off).  Allocates the buffers a capture needs on first use; waits for
+ * the device. */
+int dg_set_capture(dg_handle* h, uint32_t capture_mask);
+
 /* Copy a capture of the last denoise pass (see DG_CAP_*) into device memory
  * d_dst of exactly `bytes` bytes.  layer selects the layer for per-layer
  * captures.  DG_ESTATE if the capture was not enabled. */
@@ -202,6 +211,29 @@ int dg_get_capture(dg_handle* h, uint32_t what, int32_t layer, void* d_dst, size
  * [Hkv, n, D] in act_dtype (which = 0 for K, 1 for V). */
 int dg_get_kv(dg_handle* h, int32_t layer, int32_t which, int64_t row0, int64_t n, void* d_dst,
               void* stream);
+
+/* Overwrite one layer's K or V cache rows [row0, row0+n) from device memory
+ * laid out [Hkv, n, D] in act_dtype (which = 0 for K, 1 for V; K rows hold
+ * the rotated keys).  Restores a saved cache or injects one computed
+ * elsewhere; n_ctx is not changed.  row0 + n <= max_ctx. */
+int dg_set_kv(dg_handle* h, int32_t layer, int32_t which, int64_t row0, int64_t n,
+              const void* d_src, void* stream);
+
+/* ---------------------------------------------------------------- kernel timing
+ * HIP events recorded on the caller's stream around the launches of each
+ * kernel class, for live per-kernel timing (the events themselves add no
+ * host synchronisation).  dg_profile_begin enables recording for at most
+ * max_launches launches; dg_profile_end synchronises the device, writes the
+ * summed milliseconds and the launch count per class (arrays of DG_PROF_N)
+ * and disables recording. */
+#define DG_PROF_MOE_GEMM1 0   /* expert gate/up GEMM + SwiGLU */
+#define DG_PROF_MOE_GEMM2 1   /* expert down GEMM */
+#define DG_PROF_ATTENTION 2   /* attention incl. split combine */
+#define DG_PROF_LM_HEAD 3     /* LM head with the streaming epilogue */
+#define DG_PROF_DENSE 4       /* QKV, output and router projections */
+#define DG_PROF_N 5
+int dg_profile_begin(dg_handle* h, int32_t max_launches);
+int dg_profile_end(dg_handle* h, double* total_ms, int32_t* counts);
 
 /* ---------------------------------------------------------------- kernel-level entry points */
 

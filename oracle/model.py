@@ -237,6 +237,7 @@ class OracleModel:
         self.V = [None] * self.L
         self.n_ctx = 0
         self.k_blk = 0
+        self.enc_route_margin = [np.zeros(0) for _ in range(self.L)]   # per layer, per row
         self.capture_hidden = capture_hidden
         self.bf16 = w.act == "bf16"
         self.fp8 = w.experts == "fp8"
@@ -305,8 +306,11 @@ class OracleModel:
             last = l == self.L - 1
             kc = self.K[l] if start > 0 else None
             vc = self.V[l] if start > 0 else None
-            h, k, v, _ = self._layer(l, h, positions, kc, vc, causal=True, ctx_pos=ctx_pos,
-                                     need_output=not last)
+            h, k, v, rt = self._layer(l, h, positions, kc, vc, causal=True, ctx_pos=ctx_pos,
+                                      need_output=not last)
+            if rt is not None:
+                self.enc_route_margin[l] = np.concatenate([self.enc_route_margin[l][:start],
+                                                           rt[2]])
             self.K[l] = k if kc is None else np.concatenate([kc, k], axis=1)
             self.V[l] = v if vc is None else np.concatenate([vc, v], axis=1)
         self.n_ctx = start + len(ids)
@@ -314,6 +318,7 @@ class OracleModel:
     def prefill(self, ids):
         self.K = [None] * self.L
         self.V = [None] * self.L
+        self.enc_route_margin = [np.zeros(0) for _ in range(self.L)]
         self.k_blk = 0
         self._encode(ids, 0)
 

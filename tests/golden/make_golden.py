@@ -72,6 +72,9 @@ def moe26b_2layer():
     rng = np.random.default_rng(20260)
     out = {"seed": np.array(w.seed), "T": np.array(w.T)}
     out.update(_kv_samples(m, rng, m.n_ctx))
+    # layer-0 routing margins of the prompt tokens: a layer-1 K/V row can only be trusted
+    # to match when its token's layer-0 routing is not a near tie
+    out["kv_margin0"] = m.enc_route_margin[0][out["kv_pos"]]
     canvas = init_canvas(w.seed, 0, w.canvas, w.vocab)
     mask = np.zeros(w.canvas, np.uint8)
     out["canvas_in_0"], out["mask_in_0"] = canvas, mask

@@ -5,15 +5,21 @@ Tolerances:
     bf16 paths atol 2e-2, rtol 1e-2; fp32 path 1e-4 / 1e-4; fp8 experts
     2e-2 / 5e-2;
   * discrete decisions (routing, argmax, lock set, redraw) must agree exactly
-    wherever the oracle's own margin for that decision exceeds DELTA = 1e-2 in
+    wherever the oracle's own margin for that decision exceeds the gate, in
     natural-log probability units (= logit units at temperature 1); inside the
-    band a disagreement is counted, not failed.
+    band a disagreement is counted, not failed.  The gate is 1e-2 for the fp32
+    configuration.  For bf16 storage it is 3e-2: a relative difference of ~1e-5
+    anywhere upstream of a bf16 store (fp32 vs fp64 accumulation) flips about
+    one in eight roundings of the unit-scale normed activations that feed the
+    router and the LM head, which moves each logit by up to ~6e-3 (measured on
+    the 26B-class model), so a difference of two logits can move by ~1.2e-2.
 """
 from __future__ import annotations
 
 import numpy as np
 
-DELTA = 1e-2
+DELTA = 1e-2                     # fp32 configuration
+GATE = {"f32": 1e-2, "bf16": 3e-2, "fp8": 3e-2}
 TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4), "fp8": (2e-2, 5e-2)}
 
 
@@ -32,7 +38,9 @@ def assert_close(name, gpu, ref, atol, rtol, max_bad_frac=0.0):
 
 
 def gated_mismatches(gpu, ref, margin, delta=DELTA):
-    """Mismatches among decisions whose oracle margin exceeds delta, and the counts."""
+    """Mismatches among decisions whose oracle margin exceeds delta, and the counts.
+
+    Returns (gated mismatches, gated decisions, in-band mismatches)."""
     gpu = np.asarray(gpu)
     ref = np.asarray(ref)
     margin = np.asarray(margin, np.float64)
@@ -42,6 +50,23 @@ def gated_mismatches(gpu, ref, margin, delta=DELTA):
     else:
         diff = gpu != ref
     return int(np.sum(diff & gated)), int(gated.sum()), int(np.sum(diff & ~gated))
+
+
+def routing_sets(idx):
+    """Routing compared as the set of chosen experts per token: the order of the
+    chosen experts (descending gate) is not a decision of the method, the MoE
+    output is the gate-weighted sum over the set."""
+    return np.sort(np.asarray(idx), axis=-1)
+
+
+def worst_mismatch_margin(gpu, ref, margin):
+    """Largest oracle margin among disagreeing decisions (0 when none disagree)."""
+    gpu = np.asarray(gpu)
+    ref = np.asarray(ref)
+    margin = np.asarray(margin, np.float64)
+    diff = np.any(gpu != ref, axis=tuple(range(margin.ndim, gpu.ndim))) if gpu.ndim > margin.ndim \
+        else gpu != ref
+    return float(margin[diff].max()) if diff.any() else 0.0
 
 
 def lock_set_check(gpu_mask_out, ref_mask_out, mask_in, conf_ref, cut_low, cut_high,

@@ -8,7 +8,7 @@ import torch
 import fixtures as fx
 from oracle import model as om
 from oracle.numerics import round_bf16, e4m3_round
-from parity import DELTA, TOL, assert_close, gated_mismatches
+from parity import DELTA, TOL, assert_close, gated_mismatches, routing_sets
 from gpu_util import bf16_dev, bf16_host_f64, bits_f64, log, need_gpu
 
 pytestmark = pytest.mark.gpu
@@ -131,10 +131,14 @@ def _run_moe(dg, x_bits, wr, wg, wu, wd, k, expert_dtype="bf16"):
     else:
         yref = om.moe_ffn(xf, ridx, rg, wfn, expert_round=e4m3_round, hidden_round=e4m3_round)
     gi = idx.cpu().numpy()
-    bad, n_gated, in_band = gated_mismatches(gi, ridx, margin)
+    bad, n_gated, in_band = gated_mismatches(routing_sets(gi), routing_sets(ridx), margin)
     assert bad == 0, f"{bad} gated routing mismatches of {n_gated}"
-    same = np.all(gi == ridx, axis=1)
-    assert_close("gates", gates.cpu().numpy()[same], rg[same], 1e-5, 1e-4)
+    same = np.all(routing_sets(gi) == routing_sets(ridx), axis=1)
+    # gates per expert: order both sides by expert id
+    og, orf = np.argsort(gi, axis=1), np.argsort(ridx, axis=1)
+    g_gpu = np.take_along_axis(gates.cpu().numpy(), og, axis=1)
+    g_ref = np.take_along_axis(rg, orf, axis=1)
+    assert_close("gates", g_gpu[same], g_ref[same], 1e-5, 1e-4)
     tol = TOL["bf16"] if expert_dtype == "bf16" else TOL["fp8"]
     err = assert_close("moe y", bf16_host_f64(y)[same], round_bf16(yref)[same], *tol)
     return err, in_band, np.bincount(ridx.ravel(), minlength=E)

@@ -9,7 +9,7 @@ from fixtures.dg_glue import build_handle
 from oracle.model import OracleModel
 from oracle.philox import init_canvas
 from oracle.weights import FixtureWeights
-from parity import DELTA, TOL, assert_close, gated_mismatches, lock_set_check
+from parity import DELTA, TOL, assert_close, gated_mismatches, lock_set_check, routing_sets
 from gpu_util import (i32_dev, kv_read, log, logits_capture, need_gpu, routing_capture,
                       stats_capture, u8_dev)
 
@@ -63,7 +63,8 @@ def _check_pass(dg, h, oracle, canvas, mask, s, seed):
     assert bad == 0, f"pass {s}: {bad} argmax mismatches"
     for l in range(W.n_layers):
         gi, gg = routing_capture(dg, h, l, W.canvas, W.top_k)
-        bad, n, _ = gated_mismatches(gi, res.route_idx[l], res.route_margin[l])
+        bad, n, _ = gated_mismatches(routing_sets(gi), routing_sets(res.route_idx[l]),
+                                     res.route_margin[l])
         assert bad == 0, f"pass {s} layer {l}: {bad} routing mismatches"
     unl = mask == 0
     gap = np.where(unl, res.redraw_gap, -np.inf)
