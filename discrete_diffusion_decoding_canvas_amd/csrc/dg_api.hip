@@ -95,6 +95,8 @@ struct dg_handle {
     int32_t* inv = nullptr;
     void* H = nullptr;
     float* Y = nullptr;
+    int2* work_items = nullptr;
+    int32_t* work_count = nullptr;
 
     HeadPartials hp{};
     float* st_m = nullptr;
@@ -166,7 +168,8 @@ static int validate_cfg(const dg_model_cfg* c) {
         return fail(DG_EINVAL, "all sizes must be positive");
     if (c->n_q_heads % c->n_kv_heads) return fail(DG_EINVAL, "n_q_heads %% n_kv_heads != 0");
     if (c->top_k > c->n_experts || c->top_k > 16) return fail(DG_EINVAL, "top_k must be <= E and <= 16");
-    if (c->n_experts > 256) return fail(DG_EINVAL, "n_experts must be <= 256");
+    if (c->n_experts > 256 || c->n_experts % 4)
+        return fail(DG_EINVAL, "n_experts must be a multiple of 4, at most 256");
     if (c->canvas > kMaxCanvas) return fail(DG_EINVAL, "canvas must be <= %d", kMaxCanvas);
     if (c->head_dim & 1) return fail(DG_EINVAL, "head_dim must be even");
     if (c->d_model > 256 * kCombineCols) return fail(DG_EINVAL, "d_model must be <= %d", 256 * kCombineCols);
@@ -205,6 +208,15 @@ static ExpertWeights expert_weights(dg_handle* h, int l) {
     w.w2 = h->w2[l];
     w.s1 = h->s1.empty() ? nullptr : h->s1[l];
     w.s2 = h->s2.empty() ? nullptr : h->s2[l];
+    return w;
+}
+
+// Expert-GEMM work list for a batch of n tokens (grid bound from n * k entries).
+static MoeWork moe_work(dg_handle* h, int n) {
+    MoeWork w;
+    w.items = h->work_items;
+    w.count = h->work_count;
+    w.max_items = (n * h->k + kMoeRows - 1) / kMoeRows + h->E;
     return w;
 }
 
@@ -256,17 +268,19 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
                           s, ksplit));
     }
     K_TRY(launch_router_permute(h->rlog, ksplit, n, h->E, h->k, h->idx, h->gates, h->counts,
-                                h->base, h->offsets, h->perm_token, h->inv, s));
+                                h->base, h->offsets, h->perm_token, h->inv, moe_work(h, n), s));
     ExpertWeights w = expert_weights(h, l);
     const int rows = n * h->k;
     const void* X1 = (h->edt == kFP8) ? (const void*)xin8 : xin;
     {
         ProfScope p(h, DG_PROF_MOE_GEMM1, s);
-        K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows, h->H, s));
+        K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows,
+                               moe_work(h, n), h->H, s));
     }
     {
         ProfScope p(h, DG_PROF_MOE_GEMM2, s);
-        K_TRY(launch_moe_gemm2(h->edt, w, h->H, h->offsets, h->E, h->d, h->F, rows, h->Y, s));
+        K_TRY(launch_moe_gemm2(h->edt, w, h->H, h->offsets, h->E, h->d, h->F, rows,
+                               moe_work(h, n), h->Y, s));
     }
     return DG_OK;
 }
@@ -439,6 +453,8 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->offsets, E + 1));
     A_TRY(h->allocT(&h->perm_token, T * k));
     A_TRY(h->allocT(&h->inv, T * k));
+    A_TRY(h->allocT(&h->work_items, (T * k + kMoeRows - 1) / kMoeRows + E));
+    A_TRY(h->allocT(&h->work_count, 1));
     A_TRY(h->alloc(&h->H, T * k * F * (h->edt == kF32 ? 4 : h->edt == kBF16 ? 2 : 1)));
     A_TRY(h->allocT(&h->Y, T * k * d));
     const int ns = lm_head_slices(h->act, h->V);
@@ -893,7 +909,7 @@ int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, i
     aa.q_pos0 = q_pos0;
     aa.part_ml = nullptr;
     const int dt = dtype == DG_F32 ? kF32 : kBF16;
-    const size_t pf = (size_t)attention_part_floats(dt, Hq, M, S, D);
+    const size_t pf = (size_t)attention_part_floats(dt, Hq, Hkv, M, S, D);
     if (dt == kBF16) {
         const int64_t rows = ((int64_t)S + 31) & ~(int64_t)31;
         const size_t vb = (size_t)Hkv * D * rows * 2;

@@ -13,6 +13,16 @@ constexpr int kPermChunk = 1024;   // entries per permutation workgroup
 constexpr int kMaxCanvas = 1024;   // sampler capacity (one workgroup)
 constexpr int kMaxTopK = 16;       // experts per token
 constexpr int kCombineCols = 16;   // combine: columns per thread, d <= 256 * 16
+constexpr int kMoeRows = 32;       // rows of one expert-GEMM work item
+constexpr int kMaxRouterSplit = 8; // K split of the router GEMM (partials summed in top-k)
+
+// Expert-GEMM work list built by the permutation: item i covers rows
+// [row0, row0 + kMoeRows) of expert e (clipped to the expert's count).
+struct MoeWork {
+    int2* items;      // {e, row0}
+    int32_t* count;   // number of valid items
+    int max_items;    // grid bound: ceil(entries / kMoeRows) + E
+};
 
 // Transposed, key-permuted V cache: Vt[h][dim][slot], rows padded to a multiple
 // of 32.  Within each 32-key block, key 16*hi + 4*g + j sits at slot 8*g + 4*hi + j,
@@ -50,7 +60,8 @@ hipError_t launch_write_kv(int dtype, bool vpacked, void* cache, int Hkv, int D,
 // logits: nsplit partial sums [nsplit][M][E], added in order.
 hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, int k, int32_t* idx,
                                  float* gates, int32_t* counts, int32_t* base, int32_t* offsets,
-                                 int32_t* perm_token, int32_t* inv, hipStream_t s);
+                                 int32_t* perm_token, int32_t* inv, const MoeWork& work,
+                                 hipStream_t s);
 hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
                               const float* gates, const int32_t* inv, float* x, float eps,
                               void* a, uint8_t* a8, void* out, hipStream_t s);
@@ -96,10 +107,10 @@ struct ExpertWeights {
 };
 hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             const int32_t* perm_token, const int32_t* offsets, int E, int d,
-                            int F, int max_rows, void* H, hipStream_t s);
+                            int F, int max_rows, const MoeWork& work, void* H, hipStream_t s);
 hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
-                            const int32_t* offsets, int E, int d, int F, int max_rows, float* Y,
-                            hipStream_t s);
+                            const int32_t* offsets, int E, int d, int F, int max_rows,
+                            const MoeWork& work, float* Y, hipStream_t s);
 
 // LM head: per (row, slice) partial max / argmax / sum-exp / Gumbel best of
 // z = (h E^T) / tau over the vocabulary.  Gumbel noise for rows with mask == 0.
@@ -127,6 +138,6 @@ struct AttnArgs {
     int64_t part_capacity; // floats available in part_o
 };
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
-int64_t attention_part_floats(int dtype, int Hq, int M, int S, int D);
+int64_t attention_part_floats(int dtype, int Hq, int Hkv, int M, int S, int D);
 
 }  // namespace dg

@@ -26,10 +26,10 @@
 namespace dg {
 
 #ifndef DG_GEMM_WAVES
-#define DG_GEMM_WAVES 8
+#define DG_GEMM_WAVES 4      // measured best on the 26B-class pass (vs 8 waves, 2-6 stages)
 #endif
 #ifndef DG_GEMM_PREFETCH
-#define DG_GEMM_PREFETCH 3
+#define DG_GEMM_PREFETCH 6
 #endif
 
 constexpr int kTileM = 32;   // rows per chunk (2 MFMA row tiles)
@@ -236,20 +236,24 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 }
 
 // ------------------------------------------------------------------ expert GEMM 1 (MFMA)
-// grid (2F / 64 column slabs, E).  Each workgroup loops over its expert's
-// 32-row chunks; weight slab columns are [g_j | u_j | g_j+1 | u_j+1] (16 each).
+// grid (2F / 64 column slabs, work items): one workgroup per (slab, expert
+// 32-row chunk), so heavily loaded experts spread over many workgroups.
+// Weight slab columns are [g_j | u_j | g_j+1 | u_j+1] (16 each).
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void k_moe1_mfma(const void* __restrict__ X, int d, int F,
                                                         const int32_t* __restrict__ perm_token,
                                                         const int32_t* __restrict__ offsets,
+                                                        const int2* __restrict__ work,
+                                                        const int32_t* __restrict__ work_count,
                                                         const void* __restrict__ W1,
                                                         const float* __restrict__ s1,
                                                         void* __restrict__ H) {
     __shared__ float red[kWaves][kTileM][kTileN];
-    const int e = blockIdx.y;
+    if ((int)blockIdx.y >= *work_count) return;
+    const int2 item = work[blockIdx.y];
+    const int e = item.x;
     const int off = offsets[e];
-    const int n_e = offsets[e + 1] - off;
-    if (n_e <= 0) return;
+    const int n_e = min(offsets[e + 1] - off, item.y + kMoeRows);
     const int lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * kTileN;          // weight column (interleaved)
     const int N1 = 2 * F;
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void k_moe1_mfma(const void* __restrict__
     const uint8_t* bgrp = (const uint8_t*)W1 + (size_t)e * (N1 >> 4) * gsize +
                           (size_t)(n0 >> 4) * gsize;
     const size_t xrow = FP8 ? (size_t)d : (size_t)d * 2;
-    for (int mc = 0; mc < n_e; mc += kTileM) {
+    for (int mc = item.y; mc < n_e; mc += kTileM) {   // one chunk: n_e clipped above
         f32x4_t acc[kMT][kNT];
         zero_acc(acc);
         int e0 = mc + (lane & 15), e1 = mc + 16 + (lane & 15);
@@ -290,18 +294,21 @@ __global__ __launch_bounds__(kThreads) void k_moe1_mfma(const void* __restrict__
 }
 
 // ------------------------------------------------------------------ expert GEMM 2 (MFMA)
-// grid (d / 64 column slabs, E): Y[entry, n] = H[entry, :] Wd_e[:, n].
+// grid (d / 64 column slabs, work items): Y[entry, n] = H[entry, :] Wd_e[:, n].
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void k_moe2_mfma(const void* __restrict__ H, int d, int F,
                                                         const int32_t* __restrict__ offsets,
+                                                        const int2* __restrict__ work,
+                                                        const int32_t* __restrict__ work_count,
                                                         const void* __restrict__ W2,
                                                         const float* __restrict__ s2,
                                                         float* __restrict__ Y) {
     __shared__ float red[kWaves][kTileM][kTileN];
-    const int e = blockIdx.y;
+    if ((int)blockIdx.y >= *work_count) return;
+    const int2 item = work[blockIdx.y];
+    const int e = item.x;
     const int off = offsets[e];
-    const int n_e = offsets[e + 1] - off;
-    if (n_e <= 0) return;
+    const int n_e = min(offsets[e + 1] - off, item.y + kMoeRows);
     const int lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * kTileN;
     const int KB = FP8 ? (F >> 6) : (F >> 5);
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void k_moe2_mfma(const void* __restrict__
     const uint8_t* bgrp = (const uint8_t*)W2 + (size_t)e * (d >> 4) * gsize +
                           (size_t)(n0 >> 4) * gsize;
     const size_t hrow = FP8 ? (size_t)F : (size_t)F * 2;
-    for (int mc = 0; mc < n_e; mc += kTileM) {
+    for (int mc = item.y; mc < n_e; mc += kTileM) {   // one chunk: n_e clipped above
         f32x4_t acc[kMT][kNT];
         zero_acc(acc);
         int e0 = mc + (lane & 15), e1 = mc + 16 + (lane & 15);
@@ -405,7 +412,7 @@ hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const 
 
 hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             const int32_t* perm_token, const int32_t* offsets, int E, int d,
-                            int F, int max_rows, void* H, hipStream_t s) {
+                            int F, int max_rows, const MoeWork& work, void* H, hipStream_t s) {
     if (max_rows <= 0) return hipSuccess;
     if (dtype == kF32) {
         int64_t total = (int64_t)max_rows * F;
@@ -413,29 +420,33 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
             (const float*)X, d, F, perm_token, offsets, E, max_rows, (const float*)w.w1,
             (const float*)w.wu, (float*)H);
     } else {
-        dim3 grid((2 * F) / kTileN, E);
+        dim3 grid((2 * F) / kTileN, work.max_items);
         if (dtype == kFP8)
-            k_moe1_mfma<true><<<grid, kThreads, 0, s>>>(X, d, F, perm_token, offsets, w.w1, w.s1, H);
+            k_moe1_mfma<true><<<grid, kThreads, 0, s>>>(X, d, F, perm_token, offsets, work.items,
+                                                        work.count, w.w1, w.s1, H);
         else
-            k_moe1_mfma<false><<<grid, kThreads, 0, s>>>(X, d, F, perm_token, offsets, w.w1, w.s1, H);
+            k_moe1_mfma<false><<<grid, kThreads, 0, s>>>(X, d, F, perm_token, offsets, work.items,
+                                                         work.count, w.w1, w.s1, H);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
-                            const int32_t* offsets, int E, int d, int F, int max_rows, float* Y,
-                            hipStream_t s) {
+                            const int32_t* offsets, int E, int d, int F, int max_rows,
+                            const MoeWork& work, float* Y, hipStream_t s) {
     if (max_rows <= 0) return hipSuccess;
     if (dtype == kF32) {
         int64_t total = (int64_t)max_rows * d;
         k_moe2_f32<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
             (const float*)H, d, F, offsets, E, max_rows, (const float*)w.w2, Y);
     } else {
-        dim3 grid(d / kTileN, E);
+        dim3 grid(d / kTileN, work.max_items);
         if (dtype == kFP8)
-            k_moe2_mfma<true><<<grid, kThreads, 0, s>>>(H, d, F, offsets, w.w2, w.s2, Y);
+            k_moe2_mfma<true><<<grid, kThreads, 0, s>>>(H, d, F, offsets, work.items, work.count,
+                                                        w.w2, w.s2, Y);
         else
-            k_moe2_mfma<false><<<grid, kThreads, 0, s>>>(H, d, F, offsets, w.w2, w.s2, Y);
+            k_moe2_mfma<false><<<grid, kThreads, 0, s>>>(H, d, F, offsets, work.items, work.count,
+                                                         w.w2, w.s2, Y);
     }
     return hipGetLastError();
 }

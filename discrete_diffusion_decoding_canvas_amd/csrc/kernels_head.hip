@@ -11,8 +11,9 @@
 
 namespace dg {
 
-constexpr int kHeadRows = 256;    // rows per workgroup (4 waves x 64)
-constexpr int kHeadCols = 128;    // vocabulary ids per workgroup (8 MFMA column groups)
+constexpr int kHeadRows = 256;    // rows per workgroup (4 row waves x 64)
+constexpr int kHeadTile = 256;    // vocabulary ids per workgroup (2 column waves)
+constexpr int kHeadCols = 128;    // vocabulary ids per wave = one partial slice
 
 union HFrag {
     uint4 u;
@@ -40,111 +41,155 @@ DG_DEV void run_merge(Run& x, float ym, int32_t ya, float ys, float yg, int32_t 
 
 DG_DEV float gumbel_of(uint32_t w) { return -logf(-logf(philox_open_uniform(w))); }
 
-__global__ __launch_bounds__(256) void k_lm_head_bf16(
+struct EpiArgs {
+    int C, V, v0, rbase, g, l16;
+    float inv_tau;
+    const uint8_t* mask;
+    uint32_t key0, key1, c2;
+    HeadPartials p;
+    float* logits_out;
+};
+
+// Epilogue of one 16-row fragment group MT of a wave's 64 x 128 tile: each lane
+// folds its 8 columns for its 4 rows, then the 16 lanes sharing the rows merge.
+// MT is a template argument so that every accumulator index is static.
+template <int MT>
+DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
+    const int r4 = e.rbase + 16 * MT + 4 * e.g;      // rows r4 .. r4+3 in this lane
+    bool unl[4];
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        unl[j] = (r4 + j < e.C) && e.mask[r4 + j] == 0;
+        any |= unl[j];
+    }
+    Run run[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) run[j] = Run{-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const int v = e.v0 + 16 * nt + e.l16;
+        u32x4 rw = {0u, 0u, 0u, 0u};
+        if (any) rw = philox4x32_10(u32x4{(uint32_t)v, (uint32_t)(r4 >> 2), e.c2, kGumbelTag},
+                                    e.key0, e.key1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t word = j == 0 ? rw.x : j == 1 ? rw.y : j == 2 ? rw.z : rw.w;
+            const float z = acc[nt][j] * e.inv_tau;
+            if (e.logits_out != nullptr && r4 + j < e.C) e.logits_out[(size_t)(r4 + j) * e.V + v] = z;
+            if (z > run[j].m) {
+                run[j].s = (run[j].m == -INFINITY ? 0.f : run[j].s * __expf(run[j].m - z)) + 1.f;
+                run[j].m = z;
+                run[j].a = v;
+            } else {
+                run[j].s += __expf(z - run[j].m);
+            }
+            if (unl[j]) {
+                const float gs = z + gumbel_of(word);
+                if (gs > run[j].g) { run[j].g = gs; run[j].gi = v; }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const float ym = __shfl_xor(run[j].m, o, 64);
+            const int32_t ya = __shfl_xor(run[j].a, o, 64);
+            const float ys = __shfl_xor(run[j].s, o, 64);
+            const float yg = __shfl_xor(run[j].g, o, 64);
+            const int32_t ygi = __shfl_xor(run[j].gi, o, 64);
+            run_merge(run[j], ym, ya, ys, yg, ygi);
+        }
+        if (e.l16 == 0 && r4 + j < e.C) {
+            const size_t o = (size_t)(r4 + j) * e.p.n_slices + e.v0 / kHeadCols;
+            e.p.m[o] = run[j].m;
+            e.p.a[o] = run[j].a;
+            e.p.s[o] = run[j].s;
+            e.p.g[o] = run[j].g;
+            e.p.gi[o] = run[j].gi;
+        }
+    }
+}
+
+// bf16 head: workgroup of 8 waves owns 256 rows x 256 vocabulary ids; per
+// k-step of 32 the rows' and the ids' slices are copied cooperatively into
+// double-buffered LDS in MFMA fragment order (the embedding is packed that way
+// at load time, so its copy is contiguous), and each wave (64 rows x 128 ids)
+// reads its fragments from LDS.
+__global__ __launch_bounds__(512) void k_lm_head_bf16(
     const bf16_t* __restrict__ Hn, int C, int d, const bf16_t* __restrict__ Ep, int V,
     float inv_tau, const uint8_t* __restrict__ mask, uint32_t key0, uint32_t key1, uint32_t c2,
     HeadPartials p, float* __restrict__ logits_out) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ __attribute__((aligned(16))) uint4 a_lds[2][16][64];   // 16 row groups x 1 KiB
+    __shared__ __attribute__((aligned(16))) uint4 b_lds[2][16][64];   // 16 id groups x 1 KiB
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, g = lane >> 4;
-    const int v0 = blockIdx.x * kHeadCols;
-    const int rbase = blockIdx.y * kHeadRows + 64 * w;
-    if (rbase >= C) return;   // no block-level synchronisation in this kernel
+    const int wr = w & 3, wc = w >> 2;
+    const int row_base = blockIdx.y * kHeadRows;
+    const int v0 = blockIdx.x * kHeadTile + kHeadCols * wc;   // this wave's first id
+    const int rbase = row_base + 64 * wr;
     const int KB = d >> 5;
     f32x4_t acc[4][8];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const bf16_t* arow[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        int r = rbase + 16 * mt + l16;
-        r = r < C ? r : C - 1;
-        arow[mt] = Hn + (size_t)r * d + 8 * g;
-    }
-    const size_t gstride = (size_t)KB * 512;
-    const bf16_t* bgrp = Ep + (size_t)(v0 >> 4) * gstride + (size_t)lane * 8;
-    HFrag ca[4], cb[8], na[4], nb[8];
-    auto load = [&](int kb, HFrag (&fa)[4], HFrag (&fb)[8]) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) fa[mt].u = *reinterpret_cast<const uint4*>(arow[mt] + kb * 32);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-            fb[nt].u = *reinterpret_cast<const uint4*>(bgrp + nt * gstride + (size_t)kb * 512);
-    };
-    load(0, ca, cb);
+
+    // cooperative copy of one k-step: pieces tid and tid + 512 of A (256 rows) and of
+    // B (256 ids); a piece is one fragment lane (16 bytes) of one 16-row / 16-id group
+    const int pg0 = tid >> 6, pg1 = pg0 + 8;
+    const int chunk = lane >> 4;
+    int ar0 = row_base + 16 * pg0 + l16, ar1 = row_base + 16 * pg1 + l16;
+    ar0 = ar0 < C ? ar0 : C - 1;
+    ar1 = ar1 < C ? ar1 : C - 1;
+    const uint4* a0 = reinterpret_cast<const uint4*>(Hn + (size_t)ar0 * d + 8 * chunk);
+    const uint4* a1 = reinterpret_cast<const uint4*>(Hn + (size_t)ar1 * d + 8 * chunk);
+    const size_t gstride = (size_t)KB * 64;   // uint4 per 16-id group
+    const uint4* b0 = reinterpret_cast<const uint4*>(Ep) +
+                      (size_t)(blockIdx.x * (kHeadTile / 16) + pg0) * gstride + lane;
+    const uint4* b1 = b0 + 8 * gstride;
+    uint4 ra0 = a0[0], ra1 = a1[0], rb0 = b0[0], rb1 = b1[0];
+    a_lds[0][pg0][lane] = ra0;
+    a_lds[0][pg1][lane] = ra1;
+    b_lds[0][pg0][lane] = rb0;
+    b_lds[0][pg1][lane] = rb1;
+    __syncthreads();
     for (int kb = 0; kb < KB; ++kb) {
-        if (kb + 1 < KB) load(kb + 1, na, nb);
+        const int buf = kb & 1;
+        const bool more = kb + 1 < KB;
+        if (more) {
+            ra0 = a0[4 * (kb + 1)];      // 32 bf16 = 4 uint4 per k-step along a row
+            ra1 = a1[4 * (kb + 1)];
+            rb0 = b0[64 * (kb + 1)];
+            rb1 = b1[64 * (kb + 1)];
+        }
+        HFrag fa[4], fb[8];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) fa[mt].u = a_lds[buf][4 * wr + mt][lane];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) fb[nt].u = b_lds[buf][8 * wc + nt][lane];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[mt].b, cb[nt].b,
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt].b, fb[nt].b,
                                                                       acc[mt][nt], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ca[i] = na[i];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cb[i] = nb[i];
+        if (more) {
+            a_lds[buf ^ 1][pg0][lane] = ra0;
+            a_lds[buf ^ 1][pg1][lane] = ra1;
+            b_lds[buf ^ 1][pg0][lane] = rb0;
+            b_lds[buf ^ 1][pg1][lane] = rb1;
+        }
+        __syncthreads();
     }
-    // ---------------- epilogue: per row, fold the lane's 8 columns, then the 16 lanes
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int r4 = rbase + 16 * mt + 4 * g;      // rows r4 .. r4+3 in this lane
-        bool unl[4];
-        bool any = false;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            unl[j] = (r4 + j < C) && mask[r4 + j] == 0;
-            any |= unl[j];
-        }
-        Run run[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) run[j] = Run{-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff};
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const int v = v0 + 16 * nt + l16;
-            u32x4 rw = {0u, 0u, 0u, 0u};
-            if (any) rw = philox4x32_10(u32x4{(uint32_t)v, (uint32_t)(r4 >> 2), c2, kGumbelTag},
-                                        key0, key1);
-            const uint32_t words[4] = {rw.x, rw.y, rw.z, rw.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float z = acc[mt][nt][j] * inv_tau;
-                if (logits_out != nullptr && r4 + j < C) logits_out[(size_t)(r4 + j) * V + v] = z;
-                if (z > run[j].m) {
-                    run[j].s = (run[j].m == -INFINITY ? 0.f : run[j].s * __expf(run[j].m - z)) + 1.f;
-                    run[j].m = z;
-                    run[j].a = v;
-                } else {
-                    run[j].s += __expf(z - run[j].m);
-                }
-                if (unl[j]) {
-                    const float gs = z + gumbel_of(words[j]);
-                    if (gs > run[j].g) { run[j].g = gs; run[j].gi = v; }
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-                const float ym = __shfl_xor(run[j].m, o, 64);
-                const int32_t ya = __shfl_xor(run[j].a, o, 64);
-                const float ys = __shfl_xor(run[j].s, o, 64);
-                const float yg = __shfl_xor(run[j].g, o, 64);
-                const int32_t ygi = __shfl_xor(run[j].gi, o, 64);
-                run_merge(run[j], ym, ya, ys, yg, ygi);
-            }
-            if (l16 == 0 && r4 + j < C) {
-                const size_t o = (size_t)(r4 + j) * p.n_slices + blockIdx.x;
-                p.m[o] = run[j].m;
-                p.a[o] = run[j].a;
-                p.s[o] = run[j].s;
-                p.g[o] = run[j].g;
-                p.gi[o] = run[j].gi;
-            }
-        }
-    }
+    if (rbase >= C) return;
+    const EpiArgs ea{C, V, v0, rbase, g, l16, inv_tau, mask, key0, key1, c2, p, logits_out};
+    head_epilogue<0>(acc[0], ea);
+    head_epilogue<1>(acc[1], ea);
+    head_epilogue<2>(acc[2], ea);
+    head_epilogue<3>(acc[3], ea);
 }
 
 // f32 head (VALU): one thread per (row, vocabulary id), workgroup = 256 ids of one row.
@@ -209,9 +254,9 @@ hipError_t launch_lm_head(int dtype, const void* h, int C, int d, const void* E,
         k_lm_head_f32<<<grid, 256, 0, s>>>((const float*)h, C, d, (const float*)E, V, inv_tau,
                                            mask, key0, key1, c2, p, logits_out);
     } else {
-        if ((V % kHeadCols) || (d & 31)) return hipErrorInvalidValue;
-        dim3 grid(V / kHeadCols, (C + kHeadRows - 1) / kHeadRows);
-        k_lm_head_bf16<<<grid, 256, 0, s>>>((const bf16_t*)h, C, d, (const bf16_t*)E, V,
+        if ((V % kHeadTile) || (d & 31)) return hipErrorInvalidValue;
+        dim3 grid(V / kHeadTile, (C + kHeadRows - 1) / kHeadRows);
+        k_lm_head_bf16<<<grid, 512, 0, s>>>((const bf16_t*)h, C, d, (const bf16_t*)E, V,
                                             inv_tau, mask, key0, key1, c2, p, logits_out);
     }
     return hipGetLastError();

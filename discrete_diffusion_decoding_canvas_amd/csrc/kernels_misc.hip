@@ -40,15 +40,25 @@ __global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict
     __shared__ float red[4];
     const int i = blockIdx.x;
     const int64_t v = tokens[i];
+    float xs[kCombineCols];
     float ss = 0.f;
-    for (int c = threadIdx.x; c < d; c += 256) {
-        float e = PACKED ? to_f32<T>(E[packed_b_index(v, c, d)]) : to_f32<T>(E[v * d + c]);
-        x[(int64_t)i * d + c] = e;
+#pragma unroll
+    for (int j = 0; j < kCombineCols; ++j) {
+        const int c = threadIdx.x + 256 * j;
+        float e = 0.f;
+        if (c < d) e = PACKED ? to_f32<T>(E[packed_b_index(v, c, d)]) : to_f32<T>(E[v * d + c]);
+        xs[j] = e;
         ss += e * e;
     }
-    float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-    for (int c = threadIdx.x; c < d; c += 256)
-        a[(int64_t)i * d + c] = from_f32<T>(x[(int64_t)i * d + c] * r);
+    const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
+#pragma unroll
+    for (int j = 0; j < kCombineCols; ++j) {
+        const int c = threadIdx.x + 256 * j;
+        if (c < d) {
+            x[(int64_t)i * d + c] = xs[j];
+            a[(int64_t)i * d + c] = from_f32<T>(xs[j] * r);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ RMSNorm
@@ -59,13 +69,23 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
     const float* xr = x + row * d;
+    float xs[kCombineCols];   // d <= 256 * kCombineCols: the row stays in registers
     float ss = 0.f;
-    for (int c = threadIdx.x; c < d; c += 256) ss += xr[c] * xr[c];
-    float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-    for (int c = threadIdx.x; c < d; c += 256) {
-        T av = from_f32<T>(xr[c] * r);
-        a[row * d + c] = av;
-        if (a8) a8[row * d + c] = (uint8_t)f32_to_e4m3(to_f32<T>(av));
+#pragma unroll
+    for (int i = 0; i < kCombineCols; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        xs[i] = c < d ? xr[c] : 0.f;
+        ss += xs[i] * xs[i];
+    }
+    const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < kCombineCols; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < d) {
+            const T av = from_f32<T>(xs[i] * r);
+            a[row * d + c] = av;
+            if (a8) a8[row * d + c] = (uint8_t)f32_to_e4m3(to_f32<T>(av));
+        }
     }
 }
 

@@ -25,14 +25,19 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
                                                      int M, int E, int k,
                                                      int32_t* __restrict__ idx,
                                                      float* __restrict__ gates) {
-    __shared__ float lg[4][kMaxExperts];
+    __shared__ __attribute__((aligned(16))) float lg[4][kMaxExperts];
     __shared__ float sv[4][16];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + w;
     if (t >= M) return;   // no block-level synchronisation below: only wave-level LDS use
     for (int e = lane; e < E; e += 64) {
+        float part[kMaxRouterSplit];
+#pragma unroll
+        for (int sp = 0; sp < kMaxRouterSplit; ++sp)   // all loads in flight together
+            part[sp] = sp < nsplit ? logits[((int64_t)sp * M + t) * E + e] : 0.f;
         float v = 0.f;
-        for (int sp = 0; sp < nsplit; ++sp) v += logits[((int64_t)sp * M + t) * E + e];
+#pragma unroll
+        for (int sp = 0; sp < kMaxRouterSplit; ++sp) v += part[sp];   // fixed order
         lg[w][e] = v;
     }
     __builtin_amdgcn_wave_barrier();
@@ -40,9 +45,14 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
     for (int e = lane; e < E; e += 64) {
         const float v = lg[w][e];
         int rank = 0;
-        for (int j = 0; j < E; ++j) {
-            const float u = lg[w][j];
-            rank += (u > v) || (u == v && j < e);
+        const float4* row = reinterpret_cast<const float4*>(lg[w]);
+        for (int j4 = 0; j4 < (E >> 2); ++j4) {   // E is a multiple of 4 (checked by the launcher)
+            const float4 u = row[j4];
+            const int j = 4 * j4;
+            rank += (u.x > v) || (u.x == v && j < e);
+            rank += (u.y > v) || (u.y == v && j + 1 < e);
+            rank += (u.z > v) || (u.z == v && j + 2 < e);
+            rank += (u.w > v) || (u.w == v && j + 3 < e);
         }
         if (rank < k) {
             idx[(int64_t)t * k + rank] = e;
@@ -62,13 +72,34 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
 // One workgroup for up to kPermSmall entries: counts, scan, row assignment.
 constexpr int kPermSmall = 8192;
 
+// Work items of the expert GEMMs: (expert, first row) for every kMoeRows-row
+// chunk of every expert that received entries, experts in order.  woff[e] is
+// the first item of expert e (exclusive scan of the chunk counts).
+DG_DEV void emit_work(const int32_t* cnt, int E, int32_t* woff, int2* items, int32_t* count) {
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            woff[e] = run;
+            run += (cnt[e] + kMoeRows - 1) / kMoeRows;
+        }
+        woff[E] = run;
+        *count = run;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        for (int i = woff[e]; i < woff[e + 1]; ++i) items[i] = make_int2(e, (i - woff[e]) * kMoeRows);
+}
+
 __global__ __launch_bounds__(1024) void k_moe_permute_small(const int32_t* __restrict__ idx, int n,
                                                             int E, int k,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm_token,
-                                                            int32_t* __restrict__ inv) {
+                                                            int32_t* __restrict__ inv,
+                                                            int2* __restrict__ work,
+                                                            int32_t* __restrict__ work_count) {
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
+    __shared__ int32_t woff[kMaxExperts + 1];
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
     for (int f = threadIdx.x; f < n; f += blockDim.x) atomicAdd(&cnt[idx[f]], 1);
@@ -81,6 +112,8 @@ __global__ __launch_bounds__(1024) void k_moe_permute_small(const int32_t* __res
         }
         off[E] = run;
     }
+    __syncthreads();
+    emit_work(cnt, E, woff, work, work_count);
     __syncthreads();
     for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
@@ -111,8 +144,11 @@ __global__ __launch_bounds__(256) void k_moe_count(const int32_t* __restrict__ i
 __global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ counts,
                                                   int n_chunks, int E,
                                                   int32_t* __restrict__ base,
-                                                  int32_t* __restrict__ offsets) {
+                                                  int32_t* __restrict__ offsets,
+                                                  int2* __restrict__ work,
+                                                  int32_t* __restrict__ work_count) {
     __shared__ int32_t tot[kMaxExperts];
+    __shared__ int32_t woff[kMaxExperts + 1];
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int run = 0;
         for (int c = 0; c < n_chunks; ++c) {
@@ -121,6 +157,8 @@ __global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ co
         }
         tot[e] = run;
     }
+    __syncthreads();
+    emit_work(tot, E, woff, work, work_count);
     __syncthreads();
     if (threadIdx.x == 0) {
         int run = 0;
@@ -159,17 +197,19 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__
 hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, int k,
                                  int32_t* idx, float* gates, int32_t* counts, int32_t* base,
                                  int32_t* offsets, int32_t* perm_token, int32_t* inv,
-                                 hipStream_t s) {
+                                 const MoeWork& work, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    if (E > kMaxExperts || k > 16) return hipErrorInvalidValue;
-    k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
+    if (E > kMaxExperts || (E & 3) || k > 16 || nsplit > kMaxRouterSplit) return hipErrorInvalidValue;
     const int n = M * k;
+    if (work.max_items < (n + kMoeRows - 1) / kMoeRows + E) return hipErrorInvalidValue;
+    k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
     if (n <= kPermSmall) {
-        k_moe_permute_small<<<1, 1024, 0, s>>>(idx, n, E, k, offsets, perm_token, inv);
+        k_moe_permute_small<<<1, 1024, 0, s>>>(idx, n, E, k, offsets, perm_token, inv,
+                                                work.items, work.count);
     } else {
         const int n_chunks = (n + kPermChunk - 1) / kPermChunk;
         k_moe_count<<<n_chunks, 256, 0, s>>>(idx, n, E, counts);
-        k_moe_scan<<<1, 256, 0, s>>>(counts, n_chunks, E, base, offsets);
+        k_moe_scan<<<1, 256, 0, s>>>(counts, n_chunks, E, base, offsets, work.items, work.count);
         k_moe_scatter<<<n_chunks, 256, 0, s>>>(idx, n, E, k, base, perm_token, inv);
     }
     return hipGetLastError();

@@ -327,25 +327,32 @@ class OracleModel:
         self.k_blk += 1
 
     # ------------------------------------------------------------ stage 2
-    def decoder_logits(self, canvas, capture: StepResult | None = None):
-        w = self.w
-        C = len(canvas)
-        E = self.W.embed()
-        h = E[np.asarray(canvas)]
+    def decoder_layer(self, l: int, h):
+        """One decoder layer over the canvas rows h [C, d] (positions n_ctx..n_ctx+C-1,
+        bidirectional over the context cache and the canvas).  Returns (h, routing)."""
+        C = h.shape[0]
         positions = np.arange(self.n_ctx, self.n_ctx + C)
         ctx_pos = np.arange(self.n_ctx)
+        kc = self.K[l] if self.n_ctx > 0 else None
+        vc = self.V[l] if self.n_ctx > 0 else None
+        h, _, _, rt = self._layer(l, h, positions, kc, vc, causal=False, ctx_pos=ctx_pos)
+        return h, rt
+
+    def head_logits(self, h):
+        """Final RMSNorm and the tied LM head: logits [C, V] (before the temperature)."""
+        hn = self._act(rmsnorm(h, self.w.rms_eps))
+        return hn @ self.W.embed().T
+
+    def decoder_logits(self, canvas, capture: StepResult | None = None):
+        h = self.W.embed()[np.asarray(canvas)]
         routes = []
         hidden = []
         for l in range(self.L):
-            kc = self.K[l] if self.n_ctx > 0 else None
-            vc = self.V[l] if self.n_ctx > 0 else None
-            h, _, _, rt = self._layer(l, h, positions, kc, vc, causal=False, ctx_pos=ctx_pos)
+            h, rt = self.decoder_layer(l, h)
             routes.append(rt)
             if self.capture_hidden:
                 hidden.append(h.copy())
-        hn = self._act(rmsnorm(h, w.rms_eps))
-        logits = hn @ E.T
-        return logits, routes, hidden
+        return self.head_logits(h), routes, hidden
 
     def denoise_step(self, canvas, mask, s: int, T: int, seed: int, keep_logits=False):
         w = self.w
