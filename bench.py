@@ -44,6 +44,32 @@ def moe1_algorithmic_bytes(w, n_active_experts):
     return weights + act + hid
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "denoise_pass_moe26b_hbm_traffic.txt")
+
+
+def measured_traffic(label):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, copy-calibrated), or None if the kernel's source file has
+    changed since the counters were taken (its hash differs from the recorded one)."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) != 5 or parts[0] != "traffic" or parts[1] != label:
+            continue
+        kv = dict(p.split("=", 1) for p in parts[2:])
+        src = os.path.join(ROOT, "discrete_diffusion_decoding_canvas_amd", "csrc", kv["source"])
+        try:
+            digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        except OSError:
+            return None
+        return int(kv["bytes_per_launch"]) if digest == kv["sha256"] else None
+    return None
+
+
 def pass_flops(w, S):
     d, D, Hq, Hkv, E, k, F, V, C = (w.d_model, w.head_dim, w.n_q_heads, w.n_kv_heads,
                                     w.n_experts, w.top_k, w.d_ff, w.vocab, w.canvas)
@@ -75,9 +101,8 @@ def cpu_baseline(w, seconds_budget=30.0):
     E = W.embed()
     canvas = init_canvas(w.seed, 0, w.canvas, w.vocab)
     h = E[canvas]
-    pos = np.arange(m.n_ctx, m.n_ctx + w.canvas)
     t0 = time.perf_counter()
-    hl, _, _, _ = m._layer(0, h, pos, m.K[0], m.V[0], causal=False, ctx_pos=np.arange(m.n_ctx))
+    hl, _ = m.decoder_layer(0, h)
     t_layer = time.perf_counter() - t0
     t0 = time.perf_counter()
     hn = round_bf16(rmsnorm(hl, w.rms_eps))
@@ -98,14 +123,81 @@ def cpu_baseline(w, seconds_budget=30.0):
                        f"({t_head:.2f} s); pass = {w.n_layers} x layer + head = {t_pass:.1f} s")}
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of COPY_BYTES, five times: the counters of a
+    --pmc run over this command give the bytes each counter reports per byte moved."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}), flush=True)
+
+
+def _grid_key(row):
+    return f"{row.get('Grid_Size_X', row.get('Grid_Size', '?'))}x{row.get('Grid_Size_Y', '')}" \
+           f"x{row.get('Grid_Size_Z', '')}"
+
+
+def summarize_trace(path):
+    """Per (kernel, grid) launch count and mean / min / max duration of a rocprofv3
+    --kernel-trace CSV: the denoise pass and the prefill launch the same kernels on
+    different grids, so they are listed apart."""
+    import csv
+    groups = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            key = (row["Kernel_Name"].split("(")[0][:60], _grid_key(row))
+            groups.setdefault(key, []).append(dur)
+    total = sum(sum(v) for v in groups.values())
+    print(f"{'kernel':60s} {'grid':>18s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} "
+          f"{'max_us':>9s} {'pct':>6s}")
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{name:60s} {grid:>18s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} "
+              f"{max(v):9.2f} {100 * sum(v) / total:6.2f}")
+
+
+def summarize_pmc(path):
+    """Per (kernel, grid, counter) dispatch count and mean value of a rocprofv3 --pmc CSV."""
+    import csv
+    groups = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            key = (row["Kernel_Name"].split("(")[0][:60], _grid_key(row), row["Counter_Name"])
+            groups.setdefault(key, {}).setdefault(row.get("Dispatch_Id", len(groups)), 0.0)
+            groups[key][row.get("Dispatch_Id")] += float(row["Counter_Value"])
+    print(f"{'kernel':60s} {'grid':>18s} {'counter':>12s} {'dispatches':>10s} {'mean':>14s}")
+    for (name, grid, ctr), d in sorted(groups.items()):
+        vals = list(d.values())
+        print(f"{name:60s} {grid:>18s} {ctr:>12s} {len(vals):10d} {sum(vals) / len(vals):14.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-blocks", action="store_true",
+                    help="skip the whole-block timing (short runs under a profiler)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print per-kernel, per-grid durations of a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
+                    help="print per-kernel, per-grid counter means of a rocprofv3 --pmc run")
     ap.add_argument("--layers", type=int, default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the denoise pass is "
               "measured on a single MI355X; multi-GPU sharding is not part of this build.",
@@ -123,6 +215,9 @@ def main():
     if args.layers:
         w = w.with_(n_layers=args.layers)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     log(f"building {w.name} (weights from the seeded generator)")
     t0 = time.time()
     h = build_handle(dg, w, max_ctx=w.prompt_len + 2 * w.canvas)
@@ -188,20 +283,22 @@ def main():
         f"largest per-expert load {max(max_load)} tokens")
 
     # whole blocks: 12 passes (+ the commit of the final canvas)
-    out = torch.empty(C, dtype=torch.int32, device="cuda")
-    dg.dg_generate_block(h, out, T, seed, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    n_blocks = 2
-    for b in range(n_blocks):
-        dg.dg_generate_block(h, out, T, seed + b, False)
-    torch.cuda.synchronize()
-    block_ms = (time.perf_counter() - t0) * 1e3 / n_blocks
-    t0 = time.perf_counter()
-    dg.dg_commit_canvas(h, out)
-    torch.cuda.synchronize()
-    commit_ms = (time.perf_counter() - t0) * 1e3
-    log(f"block {block_ms:.2f} ms, commit {commit_ms:.2f} ms")
+    block_ms = commit_ms = None
+    if not args.no_blocks:
+        out = torch.empty(C, dtype=torch.int32, device="cuda")
+        dg.dg_generate_block(h, out, T, seed, False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n_blocks = 2
+        for b in range(n_blocks):
+            dg.dg_generate_block(h, out, T, seed + b, False)
+        torch.cuda.synchronize()
+        block_ms = (time.perf_counter() - t0) * 1e3 / n_blocks
+        t0 = time.perf_counter()
+        dg.dg_commit_canvas(h, out)
+        torch.cuda.synchronize()
+        commit_ms = (time.perf_counter() - t0) * 1e3
+        log(f"block {block_ms:.2f} ms, commit {commit_ms:.2f} ms")
 
     # roofline of the dominant kernel (expert gate/up GEMM + SwiGLU)
     names = ["moe_gemm1", "moe_gemm2", "attention", "lm_head", "dense_gemm"]
@@ -240,10 +337,11 @@ def main():
                    "experts": w.n_experts, "top_k": w.top_k, "d_ff": w.d_ff,
                    "vocab": w.vocab, "prompt": w.prompt_len, "canvas": C,
                    "passes_per_block": T},
-        "output_tok_s_per_block": round(C / (block_ms / 1e3), 1),
-        "output_tok_s_per_block_with_commit": round(C / ((block_ms + commit_ms) / 1e3), 1),
-        "block_ms": round(block_ms, 3),
-        "commit_ms": round(commit_ms, 3),
+        "output_tok_s_per_block": round(C / (block_ms / 1e3), 1) if block_ms else None,
+        "output_tok_s_per_block_with_commit":
+            round(C / ((block_ms + commit_ms) / 1e3), 1) if block_ms else None,
+        "block_ms": round(block_ms, 3) if block_ms else None,
+        "commit_ms": round(commit_ms, 3) if block_ms else None,
         "prefill_ms": round(prefill_ms, 2),
         "pass_tflops": round(flops / (ms_per_pass * 1e-3) / 1e12, 2),
         "mfma_util_pct": {
@@ -264,7 +362,8 @@ def main():
                      "achieved": round(moe1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(moe1_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": moe1_bytes,
-                     "avg_launch_us": round(moe1_us, 2), "traffic": None},
+                     "avg_launch_us": round(moe1_us, 2),
+                     "traffic": measured_traffic("moe_gemm1")},
     }
     dg.dg_destroy(h)
     torch.cuda.synchronize()
