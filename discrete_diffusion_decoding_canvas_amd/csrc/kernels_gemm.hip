@@ -9,18 +9,21 @@
 // so the design goal is HBM streaming, not MFMA occupancy:
 //   * weights are pre-packed at load time into the exact MFMA B-operand lane
 //     order, so every weight load is one coalesced 16-byte load per lane
-//     (1 KiB per wave, contiguous) straight into registers;
-//   * the waves of a workgroup split the reduction (K) dimension, so a
-//     workgroup covers a narrow 64-column slab with many bytes in flight, and
-//     the partial tiles are summed once through LDS in a fixed order;
-//   * each wave keeps kPrefetch k-steps of operands in flight in registers
-//     (a rolling buffer), which hides HBM latency without LDS staging;
+//     (1 KiB per wave, contiguous);
+//   * dense projections: the waves of a workgroup split the reduction (K)
+//     dimension over a 32-row x 64-column tile, each wave keeps kPrefetch
+//     k-steps of operands in flight in registers (a rolling buffer), and the
+//     partial tiles are summed once through LDS in a fixed order; narrow GEMMs
+//     (the router, N = E) split K across workgroups as well and leave the
+//     partial sums to their consumer, which adds them in order;
+//   * expert GEMMs: a workgroup owns all rows of an expert (up to a whole
+//     canvas) for a 64-column slab, the weight fragments go through LDS once
+//     and feed every wave, so an expert's weights leave HBM once per pass
+//     however many tokens it received;
 //   * tokens sit on the 16-row MFMA side (v_mfma_f32_16x16x32_bf16, or
-//     v_mfma_f32_16x16x32_fp8_fp8 for e4m3 experts), 32-row chunks per pass;
+//     v_mfma_f32_16x16x32_fp8_fp8 for e4m3 experts);
 //   * the SwiGLU of the first expert GEMM runs in the epilogue (gate and up
-//     columns are interleaved per 16-column group at pack time);
-//   * narrow GEMMs (the router, N = E) split K across workgroups as well and
-//     leave the partial sums to their consumer, which adds them in order.
+//     columns are interleaved per 16-column group at pack time).
 #include "kernels.h"
 
 namespace dg {
@@ -235,106 +238,228 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
         }
 }
 
-// ------------------------------------------------------------------ expert GEMM 1 (MFMA)
-// grid (2F / 64 column slabs, work items): one workgroup per (slab, expert
-// 32-row chunk), so heavily loaded experts spread over many workgroups.
-// Weight slab columns are [g_j | u_j | g_j+1 | u_j+1] (16 each).
+// ------------------------------------------------------------------ expert GEMMs (MFMA)
+// One workgroup per (64-column weight slab, work item); a work item is up to
+// kMoeRows = 128 rows of one expert, so an expert's weights leave HBM once per
+// 128 of its rows (once per pass for all but the most loaded experts).
+//
+// The workgroup is split by role:
+//   * one producer wave streams the weight slab stage by stage (two packed
+//     k-steps of the four 16-column groups, 8 KiB per stage) from HBM straight
+//     into an LDS ring of kRing stages with global_load_lds (no registers), and
+//     keeps kRing - 2 stages in flight: before each barrier it waits only for the
+//     stage the consumers read next (a counted vmcnt wait);
+//   * kWideConsumers waves own 32 rows each (two MFMA row tiles), read their
+//     activation rows (gathered token rows for GEMM 1, the expert's H rows for
+//     GEMM 2) straight into registers kWideLead stages ahead, and run the MFMAs
+//     against the weight fragments in LDS.  Waves past the expert's rows only
+//     keep the barrier count.
+// Small workgroups (5 waves, 48 KiB of LDS) let three share a CU, so a CU keeps
+// ~96 KiB of weights in flight.  The producer's barrier is the bare s_barrier (a
+// workgroup fence there would wait for every load in flight); the consumers'
+// is __syncthreads.
+//   GEMM 1: H[entry, :F] = silu(x Wg_e) * (x Wu_e).  The slab's columns are
+//           [g_j | u_j | g_j+1 | u_j+1] (16 each), so a lane holds the gate and
+//           up values of the same (row, column) and the SwiGLU runs in registers.
+//   GEMM 2: Y[entry, :d] = H[entry] Wd_e (fp32).
+// fp8: e4m3 operands on both sides, per output column scales applied after the
+// accumulation.
+constexpr int kWideConsumers = 4;
+constexpr int kWideThreads = 64 * (kWideConsumers + 1);
+constexpr int kRing = 6;                     // LDS stages (8 KiB each)
+constexpr int kWideLead = 3;                 // activation stages loaded ahead per consumer wave
+static_assert(kMoeRows == 32 * kWideConsumers, "a work item is one row tile per consumer wave");
+static_assert(2 * kNT * (kRing - 2) < 64, "vmcnt holds at most 63 loads");
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n, other counters free.
+constexpr int vmcnt_le(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+
 template <bool FP8>
-__global__ __launch_bounds__(kThreads) void k_moe1_mfma(const void* __restrict__ X, int d, int F,
-                                                        const int32_t* __restrict__ perm_token,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int2* __restrict__ work,
-                                                        const int32_t* __restrict__ work_count,
-                                                        const void* __restrict__ W1,
-                                                        const float* __restrict__ s1,
-                                                        void* __restrict__ H) {
-    __shared__ float red[kWaves][kTileM][kTileN];
-    if ((int)blockIdx.y >= *work_count) return;
-    const int2 item = work[blockIdx.y];
-    const int e = item.x;
-    const int off = offsets[e];
-    const int n_e = min(offsets[e + 1] - off, item.y + kMoeRows);
-    const int lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * kTileN;          // weight column (interleaved)
-    const int N1 = 2 * F;
-    const int KB = FP8 ? (d >> 6) : (d >> 5);
-    int kb0, kb1;
-    split_range(KB, kWaves, threadIdx.x >> 6, kb0, kb1);
-    const size_t gsize = (size_t)KB * 1024;      // bytes per packed column group
-    const uint8_t* bgrp = (const uint8_t*)W1 + (size_t)e * (N1 >> 4) * gsize +
-                          (size_t)(n0 >> 4) * gsize;
-    const size_t xrow = FP8 ? (size_t)d : (size_t)d * 2;
-    for (int mc = item.y; mc < n_e; mc += kTileM) {   // one chunk: n_e clipped above
-        f32x4_t acc[kMT][kNT];
-        zero_acc(acc);
-        int e0 = mc + (lane & 15), e1 = mc + 16 + (lane & 15);
-        e0 = off + (e0 < n_e ? e0 : n_e - 1);
-        e1 = off + (e1 < n_e ? e1 : n_e - 1);
-        const int64_t t0 = perm_token[e0], t1 = perm_token[e1];
-        mainloop<FP8>((const uint8_t*)X + t0 * xrow, (const uint8_t*)X + t1 * xrow, bgrp, KB, kb0,
-                      kb1, acc);
-        reduce_waves(acc, red);
-        const int h0 = n0 >> 1;
-        for (int q = threadIdx.x; q < kTileM * (kTileN / 2); q += kThreads) {
-            const int r = q >> 5, hc = q & 31;
-            if (mc + r >= n_e) continue;
-            const int cg = ((hc >> 4) << 5) + (hc & 15);
-            float g = red[0][r][cg], u = red[0][r][cg + 16];
+DG_DEV void wide_load_a(Frag16 (&a)[2][2], const uint8_t* const (&arow)[2], int st, int KB,
+                        int lane) {
+    const int koff = 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int kb = min(2 * st + ks, KB - 1);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
             if (FP8) {
-                g *= s1[(size_t)e * N1 + n0 + cg];
-                u *= s1[(size_t)e * N1 + n0 + cg + 16];
+                a[ks][mt].l.lo = ld8(arow[mt] + kb * 64 + koff);
+                a[ks][mt].l.hi = ld8(arow[mt] + kb * 64 + 32 + koff);
+            } else {
+                a[ks][mt].u = ld16(arow[mt] + (kb * 32 + koff) * 2);
             }
-            const float hv = g / (1.0f + expf(-g)) * u;
-            const size_t o = (size_t)(off + mc + r) * F + h0 + hc;
-            if (FP8) ((uint8_t*)H)[o] = (uint8_t)f32_to_e4m3(hv);
-            else ((bf16_t*)H)[o] = f32_to_bf16(hv);
         }
-        __syncthreads();
     }
 }
 
-// ------------------------------------------------------------------ expert GEMM 2 (MFMA)
-// grid (d / 64 column slabs, work items): Y[entry, n] = H[entry, :] Wd_e[:, n].
+// Both k-steps of a stage for both row tiles, straight-line.  When K has an odd
+// number of packed k-steps the last stage's second k-step is multiplied by a
+// zeroed activation fragment (keep1 = false).
 template <bool FP8>
-__global__ __launch_bounds__(kThreads) void k_moe2_mfma(const void* __restrict__ H, int d, int F,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int2* __restrict__ work,
-                                                        const int32_t* __restrict__ work_count,
-                                                        const void* __restrict__ W2,
-                                                        const float* __restrict__ s2,
-                                                        float* __restrict__ Y) {
-    __shared__ float red[kWaves][kTileM][kTileN];
+DG_DEV void wide_mma(f32x4_t (&acc)[kMT][kNT], const Frag16 (&a)[2][2],
+                     const uint4 (*bs)[kNT][64], bool keep1, int lane) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        Frag16 fb[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) fb[nt].u = bs[ks][nt][lane];
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+            Frag16 am = a[ks][mt];
+            if (ks == 1) {
+                const uint32_t m = keep1 ? 0xffffffffu : 0u;
+                am.u = uint4{am.u.x & m, am.u.y & m, am.u.z & m, am.u.w & m};
+            }
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                if (FP8) {
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                        am.l.lo, fb[nt].l.lo, acc[mt][nt], 0, 0, 0);
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                        am.l.hi, fb[nt].l.hi, acc[mt][nt], 0, 0, 0);
+                } else {
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        am.b, fb[nt].b, acc[mt][nt], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+DG_DEV void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool FP8, int GEMM>
+__global__ __launch_bounds__(kWideThreads) void k_moe_wide(
+    const void* __restrict__ A, int K, int N, int F, const int32_t* __restrict__ perm_token,
+    const int32_t* __restrict__ offsets, const int2* __restrict__ work,
+    const int32_t* __restrict__ work_count, const void* __restrict__ W,
+    const float* __restrict__ scales, void* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint4 bsm[kRing][2][kNT][64];   // [stage][k-step][group][lane]
     if ((int)blockIdx.y >= *work_count) return;
     const int2 item = work[blockIdx.y];
     const int e = item.x;
     const int off = offsets[e];
-    const int n_e = min(offsets[e + 1] - off, item.y + kMoeRows);
-    const int lane = threadIdx.x & 63;
+    const int n_e = min(offsets[e + 1] - off, item.y + kMoeRows);   // rows end (expert-relative)
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * kTileN;
-    const int KB = FP8 ? (F >> 6) : (F >> 5);
-    int kb0, kb1;
-    split_range(KB, kWaves, threadIdx.x >> 6, kb0, kb1);
-    const size_t gsize = (size_t)KB * 1024;
-    const uint8_t* bgrp = (const uint8_t*)W2 + (size_t)e * (d >> 4) * gsize +
-                          (size_t)(n0 >> 4) * gsize;
-    const size_t hrow = FP8 ? (size_t)F : (size_t)F * 2;
-    for (int mc = item.y; mc < n_e; mc += kTileM) {   // one chunk: n_e clipped above
-        f32x4_t acc[kMT][kNT];
-        zero_acc(acc);
-        int e0 = mc + (lane & 15), e1 = mc + 16 + (lane & 15);
-        e0 = off + (e0 < n_e ? e0 : n_e - 1);
-        e1 = off + (e1 < n_e ? e1 : n_e - 1);
-        mainloop<FP8>((const uint8_t*)H + (size_t)e0 * hrow, (const uint8_t*)H + (size_t)e1 * hrow,
-                      bgrp, KB, kb0, kb1, acc);
-        reduce_waves(acc, red);
-        for (int q = threadIdx.x; q < kTileM * kTileN; q += kThreads) {
-            const int r = q >> 6, c = q & 63;
-            if (mc + r >= n_e) continue;
-            float v = red[0][r][c];
-            if (FP8) v *= s2[(size_t)e * d + n0 + c];
-            Y[(size_t)(off + mc + r) * d + n0 + c] = v;
+    const int KB = FP8 ? (K >> 6) : (K >> 5);     // packed k-steps
+    const int NS = (KB + 1) >> 1;                 // stages of two k-steps
+
+    if (w >= kWideConsumers) {
+        // ---------------- producer: the slab's four column groups of every stage, HBM -> LDS
+        const size_t gsize = (size_t)KB * 1024;
+        const uint8_t* src = (const uint8_t*)W + (size_t)e * (N >> 4) * gsize +
+                             (size_t)(n0 >> 4) * gsize + (size_t)lane * 16;
+        auto issue = [&](int st) {            // stage st (clamped source) into ring slot st % kRing
+            const int sc = min(st, NS - 1);
+            const int kb0 = min(2 * sc, KB - 1), kb1 = min(2 * sc + 1, KB - 1);
+            uint4* dst = &bsm[st % kRing][0][0][0];
+#pragma unroll
+            for (int g = 0; g < kNT; ++g) {
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(src + g * gsize + (size_t)kb0 * 1024),
+                    (__attribute__((address_space(3))) void*)(dst + g * 64), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(src + g * gsize + (size_t)kb1 * 1024),
+                    (__attribute__((address_space(3))) void*)(dst + (kNT + g) * 64), 16, 0, 0);
+            }
+        };
+        constexpr int kPerStage = 2 * kNT;    // loads per stage
+        for (int st = 0; st < kRing - 1; ++st) issue(st);
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(kPerStage * (kRing - 2)));   // stage 0 landed
+        bare_barrier();
+        for (int st = 0; st < NS; ++st) {
+            issue(st + kRing - 1);                                       // into the slot of stage st - 1
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(kPerStage * (kRing - 2)));   // stage st + 1 landed
+            bare_barrier();
         }
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+        return;
+    }
+
+    // ---------------- consumer: rows r = item.y + 32 w + 16 mt + lane % 16 (expert-relative)
+    const int wr0 = item.y + 32 * w;
+    const bool act0 = wr0 < n_e, act1 = wr0 + 16 < n_e;   // (row tile 1 runs regardless)
+    if (!act0) {
         __syncthreads();
+        for (int st = 0; st < NS; ++st) __syncthreads();
+        return;
+    }
+    const uint8_t* arow[2];
+    {
+        const size_t row_bytes = FP8 ? (size_t)K : (size_t)K * 2;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            int r = wr0 + 16 * mt + (lane & 15);
+            r = r < n_e ? r : n_e - 1;
+            const int64_t src_row = GEMM == 1 ? (int64_t)perm_token[off + r] : (int64_t)(off + r);
+            arow[mt] = (const uint8_t*)A + src_row * row_bytes;
+        }
+    }
+    constexpr int kSlots = kWideLead + 1;
+    f32x4_t acc[kMT][kNT];
+    zero_acc(acc);
+    Frag16 ra[kSlots][2][2];                      // [slot][k-step][row tile]
+#pragma unroll
+    for (int j = 0; j < kWideLead; ++j) wide_load_a<FP8>(ra[j], arow, min(j, NS - 1), KB, lane);
+    __syncthreads();
+    // unrolled over several slot cycles: the compiler drains the loads in flight at
+    // the loop head, so the head is kept rare
+    constexpr int kUnroll = 3 * kSlots;
+    for (int s0 = 0; s0 < NS; s0 += kUnroll) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int st = s0 + u;
+            if (st >= NS) break;
+            wide_load_a<FP8>(ra[(u + kWideLead) % kSlots], arow, min(st + kWideLead, NS - 1), KB,
+                             lane);
+            __builtin_amdgcn_sched_barrier(0);      // issue the prefetch before the MFMAs
+            wide_mma<FP8>(acc, ra[u % kSlots], bsm[st % kRing], 2 * st + 1 < KB, lane);
+            __syncthreads();
+        }
+    }
+
+    // ---------------- epilogue: lane holds column lane % 16 of each group, rows 4 (lane / 16) + i
+    const int l16 = lane & 15, g4 = 4 * (lane >> 4);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+        if (mt == 1 && !act1) break;
+        if (GEMM == 1) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int cg = n0 + 32 * p + l16, cu = cg + 16;   // interleaved weight columns
+                const float sg = FP8 ? scales[(size_t)e * N + cg] : 1.f;
+                const float su = FP8 ? scales[(size_t)e * N + cu] : 1.f;
+                const int hcol = (n0 >> 1) + 16 * p + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wr0 + 16 * mt + g4 + i;
+                    if (r >= n_e) continue;
+                    const float g = acc[mt][2 * p][i] * sg, uu = acc[mt][2 * p + 1][i] * su;
+                    const float hv = g / (1.0f + expf(-g)) * uu;
+                    const size_t o = (size_t)(off + r) * F + hcol;
+                    if (FP8) ((uint8_t*)out)[o] = (uint8_t)f32_to_e4m3(hv);
+                    else ((bf16_t*)out)[o] = f32_to_bf16(hv);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const int c = n0 + 16 * nt + l16;
+                const float sc = FP8 ? scales[(size_t)e * N + c] : 1.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wr0 + 16 * mt + g4 + i;
+                    if (r >= n_e) continue;
+                    ((float*)out)[(size_t)(off + r) * N + c] = acc[mt][nt][i] * sc;
+                }
+            }
+        }
     }
 }
 
@@ -420,13 +545,14 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
             (const float*)X, d, F, perm_token, offsets, E, max_rows, (const float*)w.w1,
             (const float*)w.wu, (float*)H);
     } else {
+        if ((2 * F) % kTileN || d % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
         dim3 grid((2 * F) / kTileN, work.max_items);
         if (dtype == kFP8)
-            k_moe1_mfma<true><<<grid, kThreads, 0, s>>>(X, d, F, perm_token, offsets, work.items,
-                                                        work.count, w.w1, w.s1, H);
+            k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>(X, d, 2 * F, F, perm_token, offsets,
+                                                              work.items, work.count, w.w1, w.s1, H);
         else
-            k_moe1_mfma<false><<<grid, kThreads, 0, s>>>(X, d, F, perm_token, offsets, work.items,
-                                                         work.count, w.w1, w.s1, H);
+            k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>(X, d, 2 * F, F, perm_token, offsets,
+                                                               work.items, work.count, w.w1, w.s1, H);
     }
     return hipGetLastError();
 }
@@ -440,13 +566,14 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
         k_moe2_f32<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
             (const float*)H, d, F, offsets, E, max_rows, (const float*)w.w2, Y);
     } else {
+        if (d % kTileN || F % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
         dim3 grid(d / kTileN, work.max_items);
         if (dtype == kFP8)
-            k_moe2_mfma<true><<<grid, kThreads, 0, s>>>(H, d, F, offsets, work.items, work.count,
-                                                        w.w2, w.s2, Y);
+            k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>(H, F, d, F, nullptr, offsets,
+                                                              work.items, work.count, w.w2, w.s2, Y);
         else
-            k_moe2_mfma<false><<<grid, kThreads, 0, s>>>(H, d, F, offsets, work.items, work.count,
-                                                         w.w2, w.s2, Y);
+            k_moe_wide<false, 2><<<grid, kWideThreads, 0, s>>>(H, F, d, F, nullptr, offsets,
+                                                               work.items, work.count, w.w2, w.s2, Y);
     }
     return hipGetLastError();
 }
