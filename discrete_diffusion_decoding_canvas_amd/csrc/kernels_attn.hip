@@ -19,16 +19,18 @@
 //   O^T = V^T P^T (A = V^T from the transposed, key-permuted V cache, B = P
 //   taken straight from the score registers), with P split into hi + lo bf16
 //   parts so the softmax weights keep ~16 significant bits.
-// Softmax runs in fp32 in the log2 domain (exp2), scale applied to fp32 scores.
+// Softmax runs in fp32 in the log2 domain: the running max is kept on raw
+// scores and each exponent scale*log2(e)*(s - m) is one fma ahead of exp2.
 #include "kernels.h"
 
 namespace dg {
 
 constexpr int kAttnD = 128;
-constexpr int kAttnWaves = 8;
+constexpr int kAttnWaves = 8;                // consumer waves (32 query rows each)
 constexpr int kAttnRows = 32 * kAttnWaves;   // query rows per workgroup
-constexpr int kKPitch = 136;                 // LDS row pitch of a K row (bf16): 272 B
-constexpr int kVPitch = 40;                  // LDS row pitch of a V^T row (bf16): 80 B
+constexpr int kAttnThreads = 64 * (kAttnWaves + 2);   // + a K and a V^T producer wave
+constexpr int kAttnRing = 6;                 // 32-key blocks in the LDS ring (16 KiB each)
+static_assert(kAttnRing >= 3, "two blocks ahead of the one being consumed");
 
 union AFrag {
     uint4 u;
@@ -36,21 +38,70 @@ union AFrag {
     uint16_t h[8];
 };
 
+// One 32-key block of the LDS ring, in MFMA fragment order: K fragments
+// [key half][32-dim step][lane] (A operand of S^T = K Q^T) and V^T fragments
+// [16-dim group][lane] (A operand of O^T = V^T P^T); every fragment set is 1 KiB,
+// written by one global_load_lds instruction and read back conflict-free.
+struct AttnSlot {
+    uint4 k[2][4][64];
+    uint4 v[8][64];
+};
+
+DG_DEV void attn_bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n, other counters free.
+constexpr int attn_vmcnt_le(int n) {
+    return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+DG_DEV void dma16(const bf16_t* src, uint4* dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// 2^x with the hardware exponential; results below the smallest normal flush to
+// zero (a softmax weight under 2^-126 of the row maximum is dropped).
+DG_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// S^T block of 32 keys x 32 query rows (two query blocks): four independent
+// accumulation chains over the four 32-dimension steps.
+DG_DEV void attn_scores(f32x4_t (&st)[2][2], const AttnSlot& sl, const AFrag (&qf)[2][4],
+                        int lane) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) st[qb][kh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        AFrag kf[2];
+        kf[0].u = sl.k[0][s][lane];
+        kf[1].u = sl.k[1][s][lane];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+                st[qb][kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kh].b, qf[qb][s].b,
+                                                                     st[qb][kh], 0, 0, 0);
+    }
+}
+
 template <bool CAUSAL>
-__global__ __launch_bounds__(512) void k_attn_bf16(
+__global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt,
     int Hq, int Hkv, int M, int S, int64_t k_rows, int64_t v_rows, float scale_log2,
     int64_t q_pos0, int keys_per_split, int n_splits, bf16_t* __restrict__ O,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
-    __shared__ __attribute__((aligned(16))) bf16_t ks[2][32][kKPitch];
-    __shared__ __attribute__((aligned(16))) bf16_t vs[2][kAttnD][kVPitch];
+    __shared__ AttnSlot ring[kAttnRing];
     const int G = Hq / Hkv;
     const int GM = G * M;
     const int kvh = blockIdx.y;
     const int split = blockIdx.z;
     const int row_base = blockIdx.x * kAttnRows;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, g = lane >> 4;
 
     int kbeg = split * keys_per_split;
@@ -63,7 +114,44 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
     }
     const int n_blocks = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
 
-    // this wave's 32 rows: two query blocks of 16, packed over the group's heads
+    if (w >= kAttnWaves) {
+        // ---------------- producers: wave kAttnWaves copies K, the next one V^T, HBM -> LDS
+        const bool is_v = w == kAttnWaves + 1;
+        const bf16_t* Kh = K + (int64_t)kvh * k_rows * kAttnD;
+        const bf16_t* Vh = Vt + (int64_t)kvh * kAttnD * v_rows;
+        const int last = n_blocks > 0 ? n_blocks - 1 : 0;
+        auto issue = [&](int b) {           // block b (clamped) into ring slot b % kAttnRing
+            const int key0 = kbeg + 32 * min(b, last);
+            AttnSlot* slot = &ring[b % kAttnRing];
+            if (!is_v) {
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const int key = min(key0 + 16 * kh + l16, S - 1);
+                    const bf16_t* src = Kh + (int64_t)key * kAttnD + 8 * g;
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) dma16(src + 32 * st, &slot->k[kh][st][0]);
+                }
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+                    dma16(Vh + (int64_t)(16 * dt + l16) * v_rows + key0 + 8 * g, &slot->v[dt][0]);
+            }
+        };
+        // The consumers read K of block b + 1 and V of block b in iteration b, so before
+        // the barrier that opens iteration b the blocks up to b + 1 must have landed.
+        for (int b = 0; b < kAttnRing - 1; ++b) issue(b);
+        __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(8 * (kAttnRing - 3)));   // blocks 0, 1 landed
+        attn_bare_barrier();
+        for (int b = 0; b < n_blocks; ++b) {
+            issue(b + kAttnRing - 1);                                   // into the slot of block b - 1
+            __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(8 * (kAttnRing - 3)));   // block b + 2 landed
+            attn_bare_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(0));
+        return;
+    }
+
+    // ---------------- consumers: this wave's 32 rows, two query blocks of 16, packed over the heads
     const int wrow = row_base + 32 * w;
     const bool wave_active = wrow < GM;
     AFrag qf[2][4];
@@ -86,84 +174,54 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[qb][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // cooperative loads: thread -> one 16-byte piece of the K block and of the V^T block
-    const bf16_t* Kh = K + (int64_t)kvh * k_rows * kAttnD;
-    const bf16_t* Vh = Vt + (int64_t)kvh * kAttnD * v_rows;
-    const int lk_key = tid >> 4, lk_col = (tid & 15) * 8;
-    const int lv_dim = tid >> 2, lv_col = (tid & 3) * 8;
-    auto gload = [&](int key0, uint4& kr, uint4& vr) {
-        int key = key0 + lk_key;
-        key = key < S ? key : S - 1;
-        kr = *reinterpret_cast<const uint4*>(Kh + (int64_t)key * kAttnD + lk_col);
-        vr = *reinterpret_cast<const uint4*>(Vh + (int64_t)lv_dim * v_rows + key0 + lv_col);
-    };
-    auto lstore = [&](int buf, const uint4& kr, const uint4& vr) {
-        *reinterpret_cast<uint4*>(&ks[buf][lk_key][lk_col]) = kr;
-        *reinterpret_cast<uint4*>(&vs[buf][lv_dim][lv_col]) = vr;
-    };
-    uint4 kreg, vreg;
-    if (n_blocks > 0) {
-        gload(kbeg, kreg, vreg);
-        lstore(0, kreg, vreg);
-    }
     __syncthreads();
 
+    // Software pipeline per wave: iteration b issues the score MFMAs of block b + 1
+    // (matrix cores) ahead of the softmax of block b (VALU) and then the PV MFMAs of
+    // block b, so the two units overlap.
+    int qlim[2];                        // causal: last key position each query row sees
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) qlim[qb] = (int)(q_pos0 + qm[qb]);
+    f32x4_t st[2][2];
+    if (wave_active && n_blocks > 0) attn_scores(st, ring[0], qf, lane);
     for (int b = 0; b < n_blocks; ++b) {
         const int key0 = kbeg + 32 * b;
-        const int buf = b & 1;
-        if (b + 1 < n_blocks) gload(key0 + 32, kreg, vreg);   // next block in flight
         if (wave_active) {
-            AFrag kf[2][4], vf[8];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    kf[kh][s].u = *reinterpret_cast<const uint4*>(&ks[buf][16 * kh + l16][32 * s + 8 * g]);
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                vf[dt].u = *reinterpret_cast<const uint4*>(&vs[buf][16 * dt + l16][8 * g]);
-            // scores of both query blocks: four independent accumulation chains
-            f32x4_t st[2][2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) st[qb][kh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int kh = 0; kh < 2; ++kh)
-                        st[qb][kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            kf[kh][s].b, qf[qb][s].b, st[qb][kh], 0, 0, 0);
+            f32x4_t sn[2][2];
+            if (b + 1 < n_blocks) attn_scores(sn, ring[(b + 1) % kAttnRing], qf, lane);
             AFrag pf[2], pl[2];
             float alpha[2];
+            // keys past the end (and, causal, past each row's position) are masked; a
+            // block wholly inside the range skips the per-element test
+            const bool full = !CAUSAL && key0 + 32 <= kend;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const int64_t qpos = q_pos0 + qm[qb];
                 float sc[8];
                 float mx = -INFINITY;
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int key = key0 + 16 * kh + 4 * g + j;
-                        bool ok = key < kend;
-                        if (CAUSAL) ok = ok && key <= qpos;
-                        const float v = ok ? st[qb][kh][j] * scale_log2 : -INFINITY;
+                        float v = st[qb][kh][j];
+                        if (!full) {
+                            const int key = key0 + 16 * kh + 4 * g + j;
+                            bool ok = key < kend;
+                            if (CAUSAL) ok = ok && key <= qlim[qb];
+                            v = ok ? v : -INFINITY;
+                        }
                         sc[4 * kh + j] = v;
                         mx = fmaxf(mx, v);
                     }
                 mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                // running max kept on raw scores; exponents scale_log2 * (s - m) in one fma
                 const float m_new = fmaxf(m_run[qb], mx);
-                const float base = (m_new == -INFINITY) ? 0.f : m_new;
-                alpha[qb] = exp2f(m_run[qb] - base);
+                const float nb = (m_new == -INFINITY) ? 0.f : -m_new * scale_log2;
+                alpha[qb] = fast_exp2(fmaf(m_run[qb], scale_log2, nb));
                 float psum = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float p = exp2f(sc[i] - base);
+                    const float p = fast_exp2(fmaf(sc[i], scale_log2, nb));
                     psum += p;
                     const __bf16 hi = (__bf16)p;                 // round to nearest even
                     pf[qb].b[i] = hi;
@@ -172,27 +230,32 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
                 l_run[qb] = l_run[qb] * alpha[qb] + psum;
                 m_run[qb] = m_new;
             }
-            // O^T = alpha O^T + V^T P^T: sixteen independent accumulators, hi parts then
-            // lo parts (the accumulation into C rounds to nearest even, so the chain over
-            // the key blocks costs no more than fp32 summation)
+            // O^T = alpha O^T + V^T P^T, hi parts then lo parts.  The rescale is skipped
+            // when no lane's running max moved (alpha == 1 exactly).
+            if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) o[qb][dt] *= alpha[qb];
+            }
+            const AttnSlot& sl = ring[b % kAttnRing];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                AFrag vf;
+                vf.u = sl.v[dt][lane];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.b, pf[qb].b, o[qb][dt],
+                                                                        0, 0, 0);
+                    o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.b, pl[qb].b, o[qb][dt],
+                                                                        0, 0, 0);
+                }
+            }
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[qb][dt] *= alpha[qb];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-                    o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt].b, pf[qb].b,
-                                                                        o[qb][dt], 0, 0, 0);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-                    o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt].b, pl[qb].b,
-                                                                        o[qb][dt], 0, 0, 0);
+                for (int kh = 0; kh < 2; ++kh) st[qb][kh] = sn[qb][kh];
         }
-        if (b + 1 < n_blocks) lstore(buf ^ 1, kreg, vreg);
         __syncthreads();
     }
     if (!wave_active) return;
@@ -223,7 +286,7 @@ __global__ __launch_bounds__(512) void k_attn_bf16(
             for (int dt = 0; dt < 8; ++dt)
                 *reinterpret_cast<f32x4_t*>(dst + 16 * dt + 4 * g) = o[qb][dt];
             if (g == 0) {
-                part_ml[pr * 2 + 0] = m_run[qb];
+                part_ml[pr * 2 + 0] = m_run[qb] * scale_log2;   // log2 units, as the weights
                 part_ml[pr * 2 + 1] = l;
             }
         }
@@ -356,12 +419,12 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
     const float sl2 = a.scale * 1.4426950408889634f;
     float* pml = a.part_o + (int64_t)n * a.Hq * a.M * a.D;
     if (a.causal)
-        k_attn_bf16<true><<<grid, 512, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
+        k_attn_bf16<true><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                (const bf16_t*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                a.kv_rows, a.v_rows, sl2, a.q_pos0, kps, n,
                                                (bf16_t*)a.o, a.part_o, pml);
     else
-        k_attn_bf16<false><<<grid, 512, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
+        k_attn_bf16<false><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                 (const bf16_t*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                 a.kv_rows, a.v_rows, sl2, a.q_pos0, kps, n,
                                                 (bf16_t*)a.o, a.part_o, pml);

@@ -146,9 +146,14 @@ def test_pass(forced, s):
     bad, n, _ = gated_mismatches(st["redraw"][unl], g[f"{p}_redraw"][unl], g[f"{p}_redraw_gap"][unl])
     assert bad == 0, f"{bad} of {n} gated redraws differ"
     mo, co = md.cpu().numpy(), cd.cpu().numpy()
+    # the lock set is ranked over all positions: rows whose inputs legitimately differ
+    # (in-band routing upstream) enter the reference ranking with the GPU's confidence
+    from oracle.model import sampler_update
     conf_ref = np.where(ok, g[f"{p}_conf"], st["conf"])
-    cut = g[f"{p}_cut"]
-    lock_set_check(mo, g[f"{p}_mask_out"], mask, conf_ref, cut[0], cut[1])
+    ref = sampler_update(canvas, mask, conf_ref, st["argmax"], st["redraw"], s, int(g["T"]))
+    if ok.all():
+        assert np.array_equal(ref.mask, g[f"{p}_mask_out"])
+    lock_set_check(mo, ref.mask, mask, conf_ref, ref.cut_low, ref.cut_high)
     assert np.array_equal(co[mask == 1], canvas[mask == 1])
 
 
