@@ -274,13 +274,14 @@ static_assert(2 * kNT * (kRing - 2) < 64, "vmcnt holds at most 63 loads");
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n, other counters free.
 constexpr int vmcnt_le(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// Activation fragments of stage st of the k-step range [kb_lo, kb_hi) (clamped).
 template <bool FP8>
-DG_DEV void wide_load_a(Frag16 (&a)[2][2], const uint8_t* const (&arow)[2], int st, int KB,
-                        int lane) {
+DG_DEV void wide_load_a(Frag16 (&a)[2][2], const uint8_t* const (&arow)[2], int st, int kb_lo,
+                        int kb_hi, int lane) {
     const int koff = 8 * (lane >> 4);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        const int kb = min(2 * st + ks, KB - 1);
+        const int kb = min(kb_lo + 2 * st + ks, kb_hi - 1);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             if (FP8) {
@@ -333,13 +334,81 @@ DG_DEV void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
+using WideRing = uint4[kRing][2][kNT][64];       // [stage][k-step][group][lane]
+
+// Producer wave: the four 16-column groups of a 64-column weight slab, k-steps
+// [kb_lo, kb_hi) two per stage, HBM -> LDS ring.  slab points at group 0 of the
+// slab plus lane * 16 bytes; gsize is the byte stride between groups.
+DG_DEV void wide_produce(const uint8_t* slab, size_t gsize, int kb_lo, int kb_hi, WideRing& bsm) {
+    const int NS = (kb_hi - kb_lo + 1) >> 1;
+    auto issue = [&](int st) {            // stage st (clamped source) into ring slot st % kRing
+        const int sc = min(st, NS - 1);
+        const int kb0 = min(kb_lo + 2 * sc, kb_hi - 1), kb1 = min(kb_lo + 2 * sc + 1, kb_hi - 1);
+        uint4* dst = &bsm[st % kRing][0][0][0];
+#pragma unroll
+        for (int g = 0; g < kNT; ++g) {
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(slab + g * gsize + (size_t)kb0 * 1024),
+                (__attribute__((address_space(3))) void*)(dst + g * 64), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(slab + g * gsize + (size_t)kb1 * 1024),
+                (__attribute__((address_space(3))) void*)(dst + (kNT + g) * 64), 16, 0, 0);
+        }
+    };
+    constexpr int kPerStage = 2 * kNT;    // loads per stage
+    for (int st = 0; st < kRing - 1; ++st) issue(st);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(kPerStage * (kRing - 2)));   // stage 0 landed
+    bare_barrier();
+    for (int st = 0; st < NS; ++st) {
+        issue(st + kRing - 1);                                       // into the slot of stage st - 1
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(kPerStage * (kRing - 2)));   // stage st + 1 landed
+        bare_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+}
+
+// A consumer wave without rows keeps the workgroup's barrier count.
+DG_DEV void wide_idle(int kb_lo, int kb_hi) {
+    const int NS = (kb_hi - kb_lo + 1) >> 1;
+    __syncthreads();
+    for (int st = 0; st < NS; ++st) __syncthreads();
+}
+
+// Consumer wave: acc[2 row tiles][4 column groups] over k-steps [kb_lo, kb_hi).
+template <bool FP8>
+DG_DEV void wide_consume(f32x4_t (&acc)[kMT][kNT], const uint8_t* const (&arow)[2], int kb_lo,
+                         int kb_hi, WideRing& bsm, int lane) {
+    const int NS = (kb_hi - kb_lo + 1) >> 1;
+    constexpr int kSlots = kWideLead + 1;
+    zero_acc(acc);
+    Frag16 ra[kSlots][2][2];                      // [slot][k-step][row tile]
+#pragma unroll
+    for (int j = 0; j < kWideLead; ++j) wide_load_a<FP8>(ra[j], arow, min(j, NS - 1), kb_lo, kb_hi, lane);
+    __syncthreads();
+    // unrolled over several slot cycles: the compiler drains the loads in flight at
+    // the loop head, so the head is kept rare
+    constexpr int kUnroll = 3 * kSlots;
+    for (int s0 = 0; s0 < NS; s0 += kUnroll) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int st = s0 + u;
+            if (st >= NS) break;
+            wide_load_a<FP8>(ra[(u + kWideLead) % kSlots], arow, min(st + kWideLead, NS - 1), kb_lo,
+                             kb_hi, lane);
+            __builtin_amdgcn_sched_barrier(0);      // issue the prefetch before the MFMAs
+            wide_mma<FP8>(acc, ra[u % kSlots], bsm[st % kRing], kb_lo + 2 * st + 1 < kb_hi, lane);
+            __syncthreads();
+        }
+    }
+}
+
 template <bool FP8, int GEMM>
 __global__ __launch_bounds__(kWideThreads) void k_moe_wide(
     const void* __restrict__ A, int K, int N, int F, const int32_t* __restrict__ perm_token,
     const int32_t* __restrict__ offsets, const int2* __restrict__ work,
     const int32_t* __restrict__ work_count, const void* __restrict__ W,
     const float* __restrict__ scales, void* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint4 bsm[kRing][2][kNT][64];   // [stage][k-step][group][lane]
+    __shared__ __attribute__((aligned(16))) WideRing bsm;
     if ((int)blockIdx.y >= *work_count) return;
     const int2 item = work[blockIdx.y];
     const int e = item.x;
@@ -348,46 +417,19 @@ __global__ __launch_bounds__(kWideThreads) void k_moe_wide(
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * kTileN;
     const int KB = FP8 ? (K >> 6) : (K >> 5);     // packed k-steps
-    const int NS = (KB + 1) >> 1;                 // stages of two k-steps
 
     if (w >= kWideConsumers) {
-        // ---------------- producer: the slab's four column groups of every stage, HBM -> LDS
         const size_t gsize = (size_t)KB * 1024;
-        const uint8_t* src = (const uint8_t*)W + (size_t)e * (N >> 4) * gsize +
-                             (size_t)(n0 >> 4) * gsize + (size_t)lane * 16;
-        auto issue = [&](int st) {            // stage st (clamped source) into ring slot st % kRing
-            const int sc = min(st, NS - 1);
-            const int kb0 = min(2 * sc, KB - 1), kb1 = min(2 * sc + 1, KB - 1);
-            uint4* dst = &bsm[st % kRing][0][0][0];
-#pragma unroll
-            for (int g = 0; g < kNT; ++g) {
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void*)(src + g * gsize + (size_t)kb0 * 1024),
-                    (__attribute__((address_space(3))) void*)(dst + g * 64), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void*)(src + g * gsize + (size_t)kb1 * 1024),
-                    (__attribute__((address_space(3))) void*)(dst + (kNT + g) * 64), 16, 0, 0);
-            }
-        };
-        constexpr int kPerStage = 2 * kNT;    // loads per stage
-        for (int st = 0; st < kRing - 1; ++st) issue(st);
-        __builtin_amdgcn_s_waitcnt(vmcnt_le(kPerStage * (kRing - 2)));   // stage 0 landed
-        bare_barrier();
-        for (int st = 0; st < NS; ++st) {
-            issue(st + kRing - 1);                                       // into the slot of stage st - 1
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(kPerStage * (kRing - 2)));   // stage st + 1 landed
-            bare_barrier();
-        }
-        __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+        wide_produce((const uint8_t*)W + (size_t)e * (N >> 4) * gsize + (size_t)(n0 >> 4) * gsize +
+                         (size_t)lane * 16,
+                     gsize, 0, KB, bsm);
         return;
     }
-
     // ---------------- consumer: rows r = item.y + 32 w + 16 mt + lane % 16 (expert-relative)
     const int wr0 = item.y + 32 * w;
     const bool act0 = wr0 < n_e, act1 = wr0 + 16 < n_e;   // (row tile 1 runs regardless)
     if (!act0) {
-        __syncthreads();
-        for (int st = 0; st < NS; ++st) __syncthreads();
+        wide_idle(0, KB);
         return;
     }
     const uint8_t* arow[2];
@@ -401,28 +443,8 @@ __global__ __launch_bounds__(kWideThreads) void k_moe_wide(
             arow[mt] = (const uint8_t*)A + src_row * row_bytes;
         }
     }
-    constexpr int kSlots = kWideLead + 1;
     f32x4_t acc[kMT][kNT];
-    zero_acc(acc);
-    Frag16 ra[kSlots][2][2];                      // [slot][k-step][row tile]
-#pragma unroll
-    for (int j = 0; j < kWideLead; ++j) wide_load_a<FP8>(ra[j], arow, min(j, NS - 1), KB, lane);
-    __syncthreads();
-    // unrolled over several slot cycles: the compiler drains the loads in flight at
-    // the loop head, so the head is kept rare
-    constexpr int kUnroll = 3 * kSlots;
-    for (int s0 = 0; s0 < NS; s0 += kUnroll) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int st = s0 + u;
-            if (st >= NS) break;
-            wide_load_a<FP8>(ra[(u + kWideLead) % kSlots], arow, min(st + kWideLead, NS - 1), KB,
-                             lane);
-            __builtin_amdgcn_sched_barrier(0);      // issue the prefetch before the MFMAs
-            wide_mma<FP8>(acc, ra[u % kSlots], bsm[st % kRing], 2 * st + 1 < KB, lane);
-            __syncthreads();
-        }
-    }
+    wide_consume<FP8>(acc, arow, 0, KB, bsm, lane);
 
     // ---------------- epilogue: lane holds column lane % 16 of each group, rows 4 (lane / 16) + i
     const int l16 = lane & 15, g4 = 4 * (lane >> 4);
