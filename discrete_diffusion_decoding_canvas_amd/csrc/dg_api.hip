@@ -93,6 +93,7 @@ struct dg_handle {
     int32_t* offsets = nullptr;
     int32_t* perm_token = nullptr;
     int32_t* inv = nullptr;
+    void* Xf = nullptr;      // expert GEMM 1 activations in fragment order (bf16/fp8)
     void* H = nullptr;
     float* Y = nullptr;
     int2* work_items = nullptr;
@@ -211,6 +212,10 @@ static ExpertWeights expert_weights(dg_handle* h, int l) {
     return w;
 }
 
+// Row padding of the permuted entries: one MFMA row tile for the bf16/fp8 expert
+// GEMMs (their activation fragments are 16 rows of one expert), none for f32.
+static int moe_pad(const dg_handle* h) { return h->edt == kF32 ? 1 : kMoePad; }
+
 // Expert-GEMM work list for a batch of n tokens (grid bound from n * k entries).
 static MoeWork moe_work(dg_handle* h, int n) {
     MoeWork w;
@@ -268,14 +273,15 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
                           s, ksplit));
     }
     K_TRY(launch_router_permute(h->rlog, ksplit, n, h->E, h->k, h->idx, h->gates, h->counts,
-                                h->base, h->offsets, h->perm_token, h->inv, moe_work(h, n), s));
+                                h->base, h->offsets, h->perm_token, h->inv, moe_work(h, n),
+                                moe_pad(h), s));
     ExpertWeights w = expert_weights(h, l);
-    const int rows = n * h->k;
+    const int rows = (int)moe_rows_cap(n, h->k, h->E, moe_pad(h));
     const void* X1 = (h->edt == kFP8) ? (const void*)xin8 : xin;
     {
         ProfScope p(h, DG_PROF_MOE_GEMM1, s);
         K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows,
-                               moe_work(h, n), h->H, s));
+                               moe_work(h, n), h->Xf, h->H, s));
     }
     {
         ProfScope p(h, DG_PROF_MOE_GEMM2, s);
@@ -450,13 +456,16 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     const size_t n_chunks = (T * k + kPermChunk - 1) / kPermChunk;
     A_TRY(h->allocT(&h->counts, n_chunks * E));
     A_TRY(h->allocT(&h->base, n_chunks * E));
+    const size_t rows = (size_t)moe_rows_cap(T, h->k, h->E, moe_pad(h));
+    const size_t esz = h->edt == kF32 ? 4 : h->edt == kBF16 ? 2 : 1;
     A_TRY(h->allocT(&h->offsets, E + 1));
-    A_TRY(h->allocT(&h->perm_token, T * k));
+    A_TRY(h->allocT(&h->perm_token, rows));
     A_TRY(h->allocT(&h->inv, T * k));
     A_TRY(h->allocT(&h->work_items, (T * k + kMoeRows - 1) / kMoeRows + E));
     A_TRY(h->allocT(&h->work_count, 1));
-    A_TRY(h->alloc(&h->H, T * k * F * (h->edt == kF32 ? 4 : h->edt == kBF16 ? 2 : 1)));
-    A_TRY(h->allocT(&h->Y, T * k * d));
+    if (h->edt != kF32) A_TRY(h->alloc(&h->Xf, rows * d * esz));
+    A_TRY(h->alloc(&h->H, rows * F * esz));
+    A_TRY(h->allocT(&h->Y, rows * d));
     const int ns = lm_head_slices(h->act, h->V);
     h->hp.n_slices = ns;
     A_TRY(h->allocT(&h->hp.m, (size_t)h->C * ns));

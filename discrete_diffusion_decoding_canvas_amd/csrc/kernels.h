@@ -15,6 +15,10 @@ constexpr int kMaxTopK = 16;       // experts per token
 constexpr int kCombineCols = 16;   // combine: columns per thread, d <= 256 * 16
 constexpr int kMoeRows = 128;      // rows of one expert-GEMM work item
 constexpr int kMaxRouterSplit = 8; // K split of the router GEMM (partials summed in top-k)
+constexpr int kMoePad = 16;        // expert row padding of the MFMA expert GEMMs (one row tile)
+
+// Permuted-row capacity for n tokens, k experts each, E experts, rows padded to pad.
+inline int64_t moe_rows_cap(int64_t n, int k, int E, int pad) { return n * k + (int64_t)E * (pad - 1); }
 
 // Expert-GEMM work list built by the permutation: item i covers rows
 // [row0, row0 + kMoeRows) of expert e (clipped to the expert's count).
@@ -57,10 +61,12 @@ hipError_t launch_read_kv(int dtype, bool vpacked, const void* cache, int Hkv, i
                           int64_t rows, int64_t row0, int64_t n, void* dst, hipStream_t s);
 hipError_t launch_write_kv(int dtype, bool vpacked, void* cache, int Hkv, int D, int64_t rows,
                            int64_t row0, int64_t n, const void* src, hipStream_t s);
-// logits: nsplit partial sums [nsplit][M][E], added in order.
+// logits: nsplit partial sums [nsplit][M][E], added in order.  Each expert's
+// rows start at a multiple of pad (kMoePad for the MFMA expert GEMMs, 1 for
+// f32); padding rows have perm_token = -1.  perm_token holds moe_rows_cap rows.
 hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, int k, int32_t* idx,
                                  float* gates, int32_t* counts, int32_t* base, int32_t* offsets,
-                                 int32_t* perm_token, int32_t* inv, const MoeWork& work,
+                                 int32_t* perm_token, int32_t* inv, const MoeWork& work, int pad,
                                  hipStream_t s);
 hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
                               const float* gates, const int32_t* inv, float* x, float eps,
@@ -97,6 +103,9 @@ hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const 
 //   bf16: X bf16 [*, d], W1 packed with interleaved gate/up groups, H bf16.
 //   fp8 : X e4m3 [*, d], W1 packed e4m3 + column scales (2F), H e4m3.
 //   f32 : X f32, Wg/Wu row-major [E][d][F], H f32.
+//   bf16/fp8 first gather x into Xf, MFMA A-operand fragment order
+//   ([row / 16][k-step][lane][16 bytes], padding rows zero), and write H in the
+//   same order for GEMM 2; rows padded to kMoePad, max_rows = moe_rows_cap.
 // GEMM 2: Y[entry, :d] = H[entry] Wd_e (float).
 struct ExpertWeights {
     const void* w1;        // bf16/fp8 packed gate|up, or f32 Wg
@@ -107,7 +116,8 @@ struct ExpertWeights {
 };
 hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             const int32_t* perm_token, const int32_t* offsets, int E, int d,
-                            int F, int max_rows, const MoeWork& work, void* H, hipStream_t s);
+                            int F, int max_rows, const MoeWork& work, void* Xf, void* H,
+                            hipStream_t s);
 hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
                             const int32_t* offsets, int E, int d, int F, int max_rows,
                             const MoeWork& work, float* Y, hipStream_t s);

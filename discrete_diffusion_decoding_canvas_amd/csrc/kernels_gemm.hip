@@ -243,68 +243,100 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 // kMoeRows = 128 rows of one expert, so an expert's weights leave HBM once per
 // 128 of its rows (once per pass for all but the most loaded experts).
 //
-// The workgroup is split by role:
-//   * one producer wave streams the weight slab stage by stage (two packed
-//     k-steps of the four 16-column groups, 8 KiB per stage) from HBM straight
-//     into an LDS ring of kRing stages with global_load_lds (no registers), and
-//     keeps kRing - 2 stages in flight: before each barrier it waits only for the
-//     stage the consumers read next (a counted vmcnt wait);
-//   * kWideConsumers waves own 32 rows each (two MFMA row tiles), read their
-//     activation rows (gathered token rows for GEMM 1, the expert's H rows for
-//     GEMM 2) straight into registers kWideLead stages ahead, and run the MFMAs
-//     against the weight fragments in LDS.  Waves past the expert's rows only
-//     keep the barrier count.
-// Small workgroups (5 waves, 48 KiB of LDS) let three share a CU, so a CU keeps
-// ~96 KiB of weights in flight.  The producer's barrier is the bare s_barrier (a
-// workgroup fence there would wait for every load in flight); the consumers'
-// is __syncthreads.
+// Four waves, each with two roles:
+//   * weight streaming: wave w owns column group w of the slab and copies its
+//     two packed k-steps of every stage (2 KiB) from HBM straight into an LDS
+//     ring of kRing stages with global_load_lds (no registers), kRing - 1
+//     stages ahead.  Before the barrier that ends stage st each wave waits,
+//     with a counted vmcnt, only for its own copy of stage st + 1; after the
+//     barrier all four groups of that stage are in LDS;
+//   * MFMA: wave w owns rows 32 w .. 32 w + 31 of the item (two MFMA row
+//     tiles), reads its activation rows (gathered token rows for GEMM 1, the
+//     expert's H rows for GEMM 2) straight into registers kWideLead stages
+//     ahead, and multiplies them with the four groups' fragments in LDS.
+//     Waves past the expert's rows only stream weights.
+// Four-wave workgroups of <= 128 VGPRs and a 40 KiB ring fit four to a CU (a
+// fifth, producer-only wave would limit a CU to two).  The barrier is the bare
+// s_barrier: a workgroup fence would wait for every load in flight.
 //   GEMM 1: H[entry, :F] = silu(x Wg_e) * (x Wu_e).  The slab's columns are
 //           [g_j | u_j | g_j+1 | u_j+1] (16 each), so a lane holds the gate and
 //           up values of the same (row, column) and the SwiGLU runs in registers.
 //   GEMM 2: Y[entry, :d] = H[entry] Wd_e (fp32).
 // fp8: e4m3 operands on both sides, per output column scales applied after the
 // accumulation.
-constexpr int kWideConsumers = 4;
-constexpr int kWideThreads = 64 * (kWideConsumers + 1);
-constexpr int kRing = 6;                     // LDS stages (8 KiB each)
-constexpr int kWideLead = 3;                 // activation stages loaded ahead per consumer wave
-static_assert(kMoeRows == 32 * kWideConsumers, "a work item is one row tile per consumer wave");
-static_assert(2 * kNT * (kRing - 2) < 64, "vmcnt holds at most 63 loads");
+#ifndef DG_WIDE_RING
+#define DG_WIDE_RING 5
+#endif
+constexpr int kWideWaves = 4;
+constexpr int kWideThreads = 64 * kWideWaves;
+constexpr int kRing = DG_WIDE_RING;          // LDS stages (8 KiB each)
+constexpr int kWideLead = 2;                 // activation stages loaded ahead per wave
+constexpr int kWideSlots = kWideLead + 1;
+static_assert(kMoeRows == 32 * kWideWaves, "a work item is one row tile pair per wave");
+static_assert(kNT == kWideWaves, "one column group per wave");
+static_assert(kRing >= 3 && kRing * 8 * 1024 * 4 <= 160 * 1024, "ring size");
+static_assert(kRing <= kWideLead + 3, "the steady-state wait must also hold for the first stages");
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n, other counters free.
 constexpr int vmcnt_le(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// Vector-memory operations a wave issues per stage: the activation loads (one
+// 16-byte fragment load per (k-step, row tile)) and its two weight copies.  The
+// counted waits below rely on these numbers.
+constexpr int kWideAOps = 4;
+constexpr int kWideWaitActive = (kRing - 2) * (kWideAOps + 2);
+constexpr int kWideWaitIdle = (kRing - 2) * 2;
+static_assert(kWideWaitActive < 64, "vmcnt holds at most 63 operations");
+
 // Activation fragments of stage st of the k-step range [kb_lo, kb_hi) (clamped).
-template <bool FP8>
-DG_DEV void wide_load_a(Frag16 (&a)[2][2], const uint8_t* const (&arow)[2], int st, int kb_lo,
-                        int kb_hi, int lane) {
-    const int koff = 8 * (lane >> 4);
+// afrag[mt] points at the row tile's fragment of k-step 0 plus lane * 16 bytes;
+// k-steps are 1 KiB apart, so each load is one contiguous 1 KiB per wave.
+DG_DEV void wide_load_a(Frag16 (&a)[2][2], const uint8_t* const (&afrag)[2], int st, int kb_lo,
+                        int kb_hi) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int kb = min(kb_lo + 2 * st + ks, kb_hi - 1);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            if (FP8) {
-                a[ks][mt].l.lo = ld8(arow[mt] + kb * 64 + koff);
-                a[ks][mt].l.hi = ld8(arow[mt] + kb * 64 + 32 + koff);
-            } else {
-                a[ks][mt].u = ld16(arow[mt] + (kb * 32 + koff) * 2);
-            }
-        }
+        for (int mt = 0; mt < 2; ++mt) a[ks][mt].u = ld16(afrag[mt] + (size_t)kb * 1024);
     }
 }
 
 // Both k-steps of a stage for both row tiles, straight-line.  When K has an odd
 // number of packed k-steps the last stage's second k-step is multiplied by a
 // zeroed activation fragment (keep1 = false).
+//
+// The weight fragments are read from LDS in inline asm: the waves also issue
+// LDS copies (global_load_lds), and the compiler cannot tell the ring slots
+// apart, so for a plain LDS read it would first wait for every copy in flight.
+// The barrier that ends the previous stage orders these reads after the copies
+// they need.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+DG_DEV void lds_read_groups(u32x4_t (&f)[kNT], uint32_t addr) {
+    static_assert(kNT == 4, "four 1 KiB column groups");
+    asm volatile(
+        "ds_read_b128 %0, %4\n"
+        "ds_read_b128 %1, %4 offset:1024\n"
+        "ds_read_b128 %2, %4 offset:2048\n"
+        "ds_read_b128 %3, %4 offset:3072\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+        : "v"(addr)
+        : "memory");
+}
+
 template <bool FP8>
 DG_DEV void wide_mma(f32x4_t (&acc)[kMT][kNT], const Frag16 (&a)[2][2],
                      const uint4 (*bs)[kNT][64], bool keep1, int lane) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         Frag16 fb[kNT];
+        {
+            u32x4_t f[kNT];
+            lds_read_groups(f, (uint32_t)(uintptr_t)&bs[ks][0][lane]);
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) fb[nt].u = bs[ks][nt][lane];
+            for (int nt = 0; nt < kNT; ++nt) fb[nt].u = uint4{f[nt].x, f[nt].y, f[nt].z, f[nt].w};
+        }
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
             Frag16 am = a[ks][mt];
@@ -336,115 +368,139 @@ DG_DEV void bare_barrier() {
 
 using WideRing = uint4[kRing][2][kNT][64];       // [stage][k-step][group][lane]
 
-// Producer wave: the four 16-column groups of a 64-column weight slab, k-steps
-// [kb_lo, kb_hi) two per stage, HBM -> LDS ring.  slab points at group 0 of the
-// slab plus lane * 16 bytes; gsize is the byte stride between groups.
-DG_DEV void wide_produce(const uint8_t* slab, size_t gsize, int kb_lo, int kb_hi, WideRing& bsm) {
+// This wave's weight copy of stage st (clamped to the last stage) into ring slot
+// `slot`: k-steps 2 st and 2 st + 1 of column group g.  The copy is a buffer
+// load to LDS: the group's packed weights are the buffer (rsrc), the lane's
+// 16 bytes its constant VGPR offset (voff = lane * 16) and the k-step its scalar
+// offset, so no VGPR is rewritten per copy (a rewritten address register would
+// make the compiler wait for the copy before reusing it).
+DG_DEV void wide_copy_b(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int st, int slot, int NS,
+                        int kb_lo, int kb_hi, WideRing& bsm, int g) {
+    const int sc = min(st, NS - 1);
+    const int kb0 = min(kb_lo + 2 * sc, kb_hi - 1), kb1 = min(kb_lo + 2 * sc + 1, kb_hi - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)&bsm[slot][0][g][0], 16, voff, kb0 * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)&bsm[slot][1][g][0], 16, voff, kb1 * 1024, 0, 0);
+}
+
+// Buffer resource of one packed 16-column group (nbytes bytes at p): raw, no
+// stride; loads past nbytes return zero.
+DG_DEV __amdgpu_buffer_rsrc_t group_rsrc(const void* p, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
+}
+
+// A wave without rows streams its weight group and keeps the barrier count.
+DG_DEV void wide_stream_only(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int kb_lo, int kb_hi,
+                             WideRing& bsm, int g) {
     const int NS = (kb_hi - kb_lo + 1) >> 1;
-    auto issue = [&](int st) {            // stage st (clamped source) into ring slot st % kRing
-        const int sc = min(st, NS - 1);
-        const int kb0 = min(kb_lo + 2 * sc, kb_hi - 1), kb1 = min(kb_lo + 2 * sc + 1, kb_hi - 1);
-        uint4* dst = &bsm[st % kRing][0][0][0];
 #pragma unroll
-        for (int g = 0; g < kNT; ++g) {
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(slab + g * gsize + (size_t)kb0 * 1024),
-                (__attribute__((address_space(3))) void*)(dst + g * 64), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(slab + g * gsize + (size_t)kb1 * 1024),
-                (__attribute__((address_space(3))) void*)(dst + (kNT + g) * 64), 16, 0, 0);
-        }
-    };
-    constexpr int kPerStage = 2 * kNT;    // loads per stage
-    for (int st = 0; st < kRing - 1; ++st) issue(st);
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(kPerStage * (kRing - 2)));   // stage 0 landed
+    for (int st = 0; st < kRing - 1; ++st) wide_copy_b(rsrc, voff, st, st, NS, kb_lo, kb_hi, bsm, g);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitIdle));             // own copy of stage 0
     bare_barrier();
-    for (int st = 0; st < NS; ++st) {
-        issue(st + kRing - 1);                                       // into the slot of stage st - 1
-        __builtin_amdgcn_s_waitcnt(vmcnt_le(kPerStage * (kRing - 2)));   // stage st + 1 landed
-        bare_barrier();
+    for (int s0 = 0; s0 < NS; s0 += kRing) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            const int st = s0 + u;
+            if (st >= NS) break;
+            wide_copy_b(rsrc, voff, st + kRing - 1, (u + kRing - 1) % kRing, NS, kb_lo, kb_hi, bsm, g);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitIdle));     // own copy of st + 1
+            bare_barrier();
+        }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
-// A consumer wave without rows keeps the workgroup's barrier count.
-DG_DEV void wide_idle(int kb_lo, int kb_hi) {
-    const int NS = (kb_hi - kb_lo + 1) >> 1;
-    __syncthreads();
-    for (int st = 0; st < NS; ++st) __syncthreads();
-}
-
-// Consumer wave: acc[2 row tiles][4 column groups] over k-steps [kb_lo, kb_hi).
+// acc[2 row tiles][4 column groups] over k-steps [kb_lo, kb_hi), streaming weight
+// group g.  Per stage st, in issue order: the activation loads of stage
+// st + kWideLead, the weight copy of stage st + kRing - 1, the MFMAs of stage st,
+// the wait for this wave's copy of stage st + 1 (every operation issued after it:
+// kRing - 2 stages' worth), the barrier.  The slot indices are compile-time: the
+// loop is unrolled over kRing * kWideSlots stages.
 template <bool FP8>
-DG_DEV void wide_consume(f32x4_t (&acc)[kMT][kNT], const uint8_t* const (&arow)[2], int kb_lo,
-                         int kb_hi, WideRing& bsm, int lane) {
+DG_DEV void wide_mainloop(f32x4_t (&acc)[kMT][kNT], const uint8_t* const (&afrag)[2],
+                          __amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int kb_lo, int kb_hi,
+                          WideRing& bsm, int g, int lane) {
     const int NS = (kb_hi - kb_lo + 1) >> 1;
-    constexpr int kSlots = kWideLead + 1;
     zero_acc(acc);
-    Frag16 ra[kSlots][2][2];                      // [slot][k-step][row tile]
 #pragma unroll
-    for (int j = 0; j < kWideLead; ++j) wide_load_a<FP8>(ra[j], arow, min(j, NS - 1), kb_lo, kb_hi, lane);
-    __syncthreads();
-    // unrolled over several slot cycles: the compiler drains the loads in flight at
-    // the loop head, so the head is kept rare
-    constexpr int kUnroll = 3 * kSlots;
+    for (int st = 0; st < kRing - 1; ++st) wide_copy_b(rsrc, voff, st, st, NS, kb_lo, kb_hi, bsm, g);
+    __builtin_amdgcn_sched_barrier(0);          // the copies stay ahead of the activation loads
+    Frag16 ra[kWideSlots][2][2];                  // [slot][k-step][row tile]
+#pragma unroll
+    for (int j = 0; j < kWideLead; ++j) wide_load_a(ra[j], afrag, min(j, NS - 1), kb_lo, kb_hi);
+    __builtin_amdgcn_sched_barrier(0);
+    // issued after the copy of stage 0: the other kRing - 2 copies and kWideLead
+    // stages of activations
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * (kRing - 2) + kWideLead * kWideAOps));
+    bare_barrier();
+    constexpr int kUnroll = kRing * kWideSlots;
     for (int s0 = 0; s0 < NS; s0 += kUnroll) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int st = s0 + u;
             if (st >= NS) break;
-            wide_load_a<FP8>(ra[(u + kWideLead) % kSlots], arow, min(st + kWideLead, NS - 1), kb_lo,
-                             kb_hi, lane);
-            __builtin_amdgcn_sched_barrier(0);      // issue the prefetch before the MFMAs
-            wide_mma<FP8>(acc, ra[u % kSlots], bsm[st % kRing], kb_lo + 2 * st + 1 < kb_hi, lane);
-            __syncthreads();
+            wide_load_a(ra[(u + kWideLead) % kWideSlots], afrag, min(st + kWideLead, NS - 1), kb_lo,
+                        kb_hi);
+            wide_copy_b(rsrc, voff, st + kRing - 1, (u + kRing - 1) % kRing, NS, kb_lo, kb_hi, bsm, g);
+            __builtin_amdgcn_sched_barrier(0);      // issue the loads before the MFMAs
+            wide_mma<FP8>(acc, ra[u % kWideSlots], bsm[u % kRing], kb_lo + 2 * st + 1 < kb_hi, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitActive));   // own copy of st + 1
+            bare_barrier();
         }
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+}
+
+// Byte offset of element (row, col) of a [rows][K] matrix in MFMA A-fragment
+// order: [row / 16][k-step][lane = 16 g + row % 16][16 bytes].  bf16: k-step of
+// 32 columns, lane group g = (col % 32) / 8, element col % 8.  e4m3: k-step of
+// 64 columns, the lane's 16 bytes hold columns 8 g..8 g+7 (low half) and
+// 32 + 8 g..32 + 8 g + 7 (high half) of the k-step.
+template <bool FP8>
+DG_DEV size_t frag_offset(int64_t row, int col, int K) {
+    const int KB = FP8 ? (K >> 6) : (K >> 5);
+    const int kb = FP8 ? (col >> 6) : (col >> 5);
+    const int g = (col & 31) >> 3;
+    const int byte = FP8 ? (8 * ((col >> 5) & 1) + (col & 7)) : 2 * (col & 7);
+    return ((size_t)((row >> 4) * KB + kb) * 64 + 16 * g + (row & 15)) * 16 + byte;
 }
 
 template <bool FP8, int GEMM>
-__global__ __launch_bounds__(kWideThreads) void k_moe_wide(
-    const void* __restrict__ A, int K, int N, int F, const int32_t* __restrict__ perm_token,
-    const int32_t* __restrict__ offsets, const int2* __restrict__ work,
-    const int32_t* __restrict__ work_count, const void* __restrict__ W,
-    const float* __restrict__ scales, void* __restrict__ out) {
+__global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(
+    const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
+    const int2* __restrict__ work, const int32_t* __restrict__ work_count,
+    const void* __restrict__ W, const float* __restrict__ scales, void* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) WideRing bsm;
     if ((int)blockIdx.y >= *work_count) return;
     const int2 item = work[blockIdx.y];
     const int e = item.x;
-    const int off = offsets[e];
+    const int off = offsets[e];                                      // a multiple of 16
     const int n_e = min(offsets[e + 1] - off, item.y + kMoeRows);   // rows end (expert-relative)
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * kTileN;
     const int KB = FP8 ? (K >> 6) : (K >> 5);     // packed k-steps
-
-    if (w >= kWideConsumers) {
-        const size_t gsize = (size_t)KB * 1024;
-        wide_produce((const uint8_t*)W + (size_t)e * (N >> 4) * gsize + (size_t)(n0 >> 4) * gsize +
-                         (size_t)lane * 16,
-                     gsize, 0, KB, bsm);
-        return;
-    }
-    // ---------------- consumer: rows r = item.y + 32 w + 16 mt + lane % 16 (expert-relative)
+    const size_t gsize = (size_t)KB * 1024;       // bytes per packed 16-column group
+    const __amdgpu_buffer_rsrc_t rsrc =
+        group_rsrc((const uint8_t*)W + ((size_t)e * (N >> 4) + (n0 >> 4) + w) * gsize, (uint32_t)gsize);
+    const uint32_t voff = (uint32_t)lane * 16;
+    // rows r = item.y + 32 w + 16 mt + lane % 16 (expert-relative); n_e is a
+    // multiple of 16, so a row tile is wholly inside or outside the expert
     const int wr0 = item.y + 32 * w;
-    const bool act0 = wr0 < n_e, act1 = wr0 + 16 < n_e;   // (row tile 1 runs regardless)
-    if (!act0) {
-        wide_idle(0, KB);
+    const bool act1 = wr0 + 16 < n_e;
+    if (wr0 >= n_e) {
+        wide_stream_only(rsrc, voff, 0, KB, bsm, w);
         return;
     }
-    const uint8_t* arow[2];
-    {
-        const size_t row_bytes = FP8 ? (size_t)K : (size_t)K * 2;
+    const uint8_t* afrag[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            int r = wr0 + 16 * mt + (lane & 15);
-            r = r < n_e ? r : n_e - 1;
-            const int64_t src_row = GEMM == 1 ? (int64_t)perm_token[off + r] : (int64_t)(off + r);
-            arow[mt] = (const uint8_t*)A + src_row * row_bytes;
-        }
+    for (int mt = 0; mt < 2; ++mt) {
+        const int64_t tile = (off + wr0 + (mt == 1 && act1 ? 16 : 0)) >> 4;   // tile 1 repeats tile 0 past the rows
+        afrag[mt] = Af + ((size_t)tile * KB * 64 + lane) * 16;
     }
     f32x4_t acc[kMT][kNT];
-    wide_consume<FP8>(acc, arow, 0, KB, bsm, lane);
+    wide_mainloop<FP8>(acc, afrag, rsrc, voff, 0, KB, bsm, w, lane);
 
     // ---------------- epilogue: lane holds column lane % 16 of each group, rows 4 (lane / 16) + i
     const int l16 = lane & 15, g4 = 4 * (lane >> 4);
@@ -461,12 +517,11 @@ __global__ __launch_bounds__(kWideThreads) void k_moe_wide(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wr0 + 16 * mt + g4 + i;
-                    if (r >= n_e) continue;
                     const float g = acc[mt][2 * p][i] * sg, uu = acc[mt][2 * p + 1][i] * su;
                     const float hv = g / (1.0f + expf(-g)) * uu;
-                    const size_t o = (size_t)(off + r) * F + hcol;
+                    const size_t o = frag_offset<FP8>(off + r, hcol, F);   // GEMM 2's A order
                     if (FP8) ((uint8_t*)out)[o] = (uint8_t)f32_to_e4m3(hv);
-                    else ((bf16_t*)out)[o] = f32_to_bf16(hv);
+                    else *(bf16_t*)((uint8_t*)out + o) = f32_to_bf16(hv);
                 }
             }
         } else {
@@ -477,12 +532,40 @@ __global__ __launch_bounds__(kWideThreads) void k_moe_wide(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wr0 + 16 * mt + g4 + i;
-                    if (r >= n_e) continue;
                     ((float*)out)[(size_t)(off + r) * N + c] = acc[mt][nt][i] * sc;
                 }
             }
         }
     }
+}
+
+// GEMM 1's activation fragments: the token rows of every 16-row tile of the
+// permuted entries in MFMA A-operand order (frag_offset), zero for padding rows.
+// Done once here, the expert GEMM's activation loads become contiguous 1 KiB
+// reads instead of 16-row gathers repeated for every weight slab.
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_moe_gather_frag(const uint8_t* __restrict__ X, int K,
+                                                         const int32_t* __restrict__ perm_token,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int E, uint8_t* __restrict__ Xf) {
+    const int KB = FP8 ? (K >> 6) : (K >> 5);
+    const int kb = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int tile = blockIdx.y;
+    if (kb >= KB || 16 * tile >= offsets[E]) return;
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const int tok = perm_token[16 * tile + (lane & 15)];
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (tok >= 0) {
+        const uint8_t* row = X + (size_t)tok * (FP8 ? K : 2 * K);
+        if (FP8) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(row + kb * 64 + 8 * g);
+            const uint2 hi = *reinterpret_cast<const uint2*>(row + kb * 64 + 32 + 8 * g);
+            v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            v = *reinterpret_cast<const uint4*>(row + (kb * 32 + 8 * g) * 2);
+        }
+    }
+    *reinterpret_cast<uint4*>(Xf + (((size_t)tile * KB + kb) * 64 + lane) * 16) = v;
 }
 
 // ------------------------------------------------------------------ expert GEMMs (f32, VALU)
@@ -559,7 +642,8 @@ hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const 
 
 hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             const int32_t* perm_token, const int32_t* offsets, int E, int d,
-                            int F, int max_rows, const MoeWork& work, void* H, hipStream_t s) {
+                            int F, int max_rows, const MoeWork& work, void* Xf, void* H,
+                            hipStream_t s) {
     if (max_rows <= 0) return hipSuccess;
     if (dtype == kF32) {
         int64_t total = (int64_t)max_rows * F;
@@ -567,14 +651,24 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
             (const float*)X, d, F, perm_token, offsets, E, max_rows, (const float*)w.w1,
             (const float*)w.wu, (float*)H);
     } else {
-        if ((2 * F) % kTileN || d % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
+        const int kq = dtype == kFP8 ? 64 : 32;
+        if ((2 * F) % kTileN || d % kq || F % kq || !Xf) return hipErrorInvalidValue;
+        const int KB = d / kq;
+        dim3 gg((KB + 3) / 4, (max_rows + kMoePad - 1) / kMoePad);   // tiles past offsets[E] exit
         dim3 grid((2 * F) / kTileN, work.max_items);
-        if (dtype == kFP8)
-            k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>(X, d, 2 * F, F, perm_token, offsets,
-                                                              work.items, work.count, w.w1, w.s1, H);
-        else
-            k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>(X, d, 2 * F, F, perm_token, offsets,
-                                                               work.items, work.count, w.w1, w.s1, H);
+        if (dtype == kFP8) {
+            k_moe_gather_frag<true><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
+                                                       (uint8_t*)Xf);
+            k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
+                                                              offsets, work.items, work.count,
+                                                              w.w1, w.s1, H);
+        } else {
+            k_moe_gather_frag<false><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets,
+                                                        E, (uint8_t*)Xf);
+            k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
+                                                               offsets, work.items, work.count,
+                                                               w.w1, w.s1, H);
+        }
     }
     return hipGetLastError();
 }
@@ -591,10 +685,10 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
         if (d % kTileN || F % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
         dim3 grid(d / kTileN, work.max_items);
         if (dtype == kFP8)
-            k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>(H, F, d, F, nullptr, offsets,
+            k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
                                                               work.items, work.count, w.w2, w.s2, Y);
         else
-            k_moe_wide<false, 2><<<grid, kWideThreads, 0, s>>>(H, F, d, F, nullptr, offsets,
+            k_moe_wide<false, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
                                                                work.items, work.count, w.w2, w.s2, Y);
     }
     return hipGetLastError();

@@ -11,8 +11,9 @@
 // pass with no serial reduction chain.  Router logits may arrive as several
 // split-K partial sums; they are added here in a fixed order.
 //
-// Permutation: per-expert counts with LDS integer atomics, one exclusive scan,
-// then each entry takes the next free row of its expert.  The order of rows
+// Permutation: per-expert counts with LDS integer atomics, one exclusive scan
+// (of the counts rounded up to the row padding), then each entry takes the next
+// free row of its expert.  The order of rows
 // inside an expert is not fixed, but every expert-GEMM output row depends only
 // on its own input row, so the results are bit-identical across runs.
 #include "kernels.h"
@@ -73,14 +74,14 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
 constexpr int kPermSmall = 8192;
 
 // Work items of the expert GEMMs: (expert, first row) for every kMoeRows-row
-// chunk of every expert that received entries, experts in order.  woff[e] is
-// the first item of expert e (exclusive scan of the chunk counts).
-DG_DEV void emit_work(const int32_t* cnt, int E, int32_t* woff, int2* items, int32_t* count) {
+// chunk of every expert that received entries, experts in order.  off holds the
+// (padded) row offsets; woff[e] is the first item of expert e.
+DG_DEV void emit_work(const int32_t* off, int E, int32_t* woff, int2* items, int32_t* count) {
     if (threadIdx.x == 0) {
         int run = 0;
         for (int e = 0; e < E; ++e) {
             woff[e] = run;
-            run += (cnt[e] + kMoeRows - 1) / kMoeRows;
+            run += (off[e + 1] - off[e] + kMoeRows - 1) / kMoeRows;
         }
         woff[E] = run;
         *count = run;
@@ -90,8 +91,13 @@ DG_DEV void emit_work(const int32_t* cnt, int E, int32_t* woff, int2* items, int
         for (int i = woff[e]; i < woff[e + 1]; ++i) items[i] = make_int2(e, (i - woff[e]) * kMoeRows);
 }
 
+// Every expert's rows start at a multiple of pad (16 for the MFMA expert GEMMs,
+// whose activation tiles are 16 rows of one expert; 1 otherwise); the rows past
+// an expert's entries up to the next multiple are padding, perm_token = -1.
+DG_DEV int round_up(int v, int pad) { return (v + pad - 1) / pad * pad; }
+
 __global__ __launch_bounds__(1024) void k_moe_permute_small(const int32_t* __restrict__ idx, int n,
-                                                            int E, int k,
+                                                            int E, int k, int pad,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm_token,
                                                             int32_t* __restrict__ inv,
@@ -108,15 +114,18 @@ __global__ __launch_bounds__(1024) void k_moe_permute_small(const int32_t* __res
         int run = 0;
         for (int e = 0; e < E; ++e) {
             off[e] = run;
-            run += cnt[e];
+            run += round_up(cnt[e], pad);
         }
         off[E] = run;
     }
     __syncthreads();
-    emit_work(cnt, E, woff, work, work_count);
+    emit_work(off, E, woff, work, work_count);
     __syncthreads();
     for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        for (int j = off[e] + cnt[e]; j < off[e + 1]; ++j) perm_token[j] = -1;
+        cnt[e] = 0;
+    }
     __syncthreads();
     for (int f = threadIdx.x; f < n; f += blockDim.x) {
         const int e = idx[f];
@@ -142,12 +151,14 @@ __global__ __launch_bounds__(256) void k_moe_count(const int32_t* __restrict__ i
 }
 
 __global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ counts,
-                                                  int n_chunks, int E,
+                                                  int n_chunks, int E, int pad,
                                                   int32_t* __restrict__ base,
                                                   int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm_token,
                                                   int2* __restrict__ work,
                                                   int32_t* __restrict__ work_count) {
     __shared__ int32_t tot[kMaxExperts];
+    __shared__ int32_t off[kMaxExperts + 1];
     __shared__ int32_t woff[kMaxExperts + 1];
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int run = 0;
@@ -158,21 +169,22 @@ __global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ co
         tot[e] = run;
     }
     __syncthreads();
-    emit_work(tot, E, woff, work, work_count);
-    __syncthreads();
     if (threadIdx.x == 0) {
         int run = 0;
         for (int e = 0; e < E; ++e) {
-            const int t = tot[e];
-            tot[e] = run;
-            offsets[e] = run;
-            run += t;
+            off[e] = run;
+            run += round_up(tot[e], pad);
         }
-        offsets[E] = run;
+        off[E] = run;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        for (int c = 0; c < n_chunks; ++c) base[(int64_t)c * E + e] += tot[e];
+    emit_work(off, E, woff, work, work_count);
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        for (int j = off[e] + tot[e]; j < off[e + 1]; ++j) perm_token[j] = -1;
+        for (int c = 0; c < n_chunks; ++c) base[(int64_t)c * E + e] += off[e];
+    }
 }
 
 __global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__ idx, int n,
@@ -197,19 +209,22 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__
 hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, int k,
                                  int32_t* idx, float* gates, int32_t* counts, int32_t* base,
                                  int32_t* offsets, int32_t* perm_token, int32_t* inv,
-                                 const MoeWork& work, hipStream_t s) {
+                                 const MoeWork& work, int pad, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    if (E > kMaxExperts || (E & 3) || k > 16 || nsplit > kMaxRouterSplit) return hipErrorInvalidValue;
+    if (E > kMaxExperts || (E & 3) || k > 16 || nsplit > kMaxRouterSplit || pad < 1 ||
+        kMoeRows % pad)
+        return hipErrorInvalidValue;
     const int n = M * k;
     if (work.max_items < (n + kMoeRows - 1) / kMoeRows + E) return hipErrorInvalidValue;
     k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
     if (n <= kPermSmall) {
-        k_moe_permute_small<<<1, 1024, 0, s>>>(idx, n, E, k, offsets, perm_token, inv,
+        k_moe_permute_small<<<1, 1024, 0, s>>>(idx, n, E, k, pad, offsets, perm_token, inv,
                                                 work.items, work.count);
     } else {
         const int n_chunks = (n + kPermChunk - 1) / kPermChunk;
         k_moe_count<<<n_chunks, 256, 0, s>>>(idx, n, E, counts);
-        k_moe_scan<<<1, 256, 0, s>>>(counts, n_chunks, E, base, offsets, work.items, work.count);
+        k_moe_scan<<<1, 256, 0, s>>>(counts, n_chunks, E, pad, base, offsets, perm_token,
+                                     work.items, work.count);
         k_moe_scatter<<<n_chunks, 256, 0, s>>>(idx, n, E, k, base, perm_token, inv);
     }
     return hipGetLastError();
