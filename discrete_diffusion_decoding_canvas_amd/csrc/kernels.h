@@ -13,7 +13,7 @@ constexpr int kPermChunk = 1024;   // entries per permutation workgroup
 constexpr int kMaxCanvas = 1024;   // sampler capacity (one workgroup)
 constexpr int kMaxTopK = 16;       // experts per token
 constexpr int kCombineCols = 16;   // combine: columns per thread, d <= 256 * 16
-constexpr int kMoeRows = 128;      // rows of one expert-GEMM work item
+constexpr int kMoeRows = 256;      // rows of one expert-GEMM work item (a whole canvas)
 constexpr int kMaxRouterSplit = 8; // K split of the router GEMM (partials summed in top-k)
 constexpr int kMoePad = 16;        // expert row padding of the MFMA expert GEMMs (one row tile)
 

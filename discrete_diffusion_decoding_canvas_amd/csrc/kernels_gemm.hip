@@ -239,81 +239,93 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 }
 
 // ------------------------------------------------------------------ expert GEMMs (MFMA)
-// One workgroup per (64-column weight slab, work item); a work item is up to
-// kMoeRows = 128 rows of one expert, so an expert's weights leave HBM once per
-// 128 of its rows (once per pass for all but the most loaded experts).
+// One workgroup per (kWideN-column weight slab, work item); a work item is up
+// to kMoeRows = 256 rows of one expert (a whole canvas), so an expert's weights
+// leave HBM once per pass.  Wide slabs keep the activation traffic, which every
+// slab re-reads, at K * 2 bytes per row per kWideN output columns.
 //
-// Four waves, each with two roles:
-//   * weight streaming: wave w owns column group w of the slab and copies its
-//     two packed k-steps of every stage (2 KiB) from HBM straight into an LDS
-//     ring of kRing stages with global_load_lds (no registers), kRing - 1
-//     stages ahead.  Before the barrier that ends stage st each wave waits,
-//     with a counted vmcnt, only for its own copy of stage st + 1; after the
-//     barrier all four groups of that stage are in LDS;
-//   * MFMA: wave w owns rows 32 w .. 32 w + 31 of the item (two MFMA row
-//     tiles), reads its activation rows (gathered token rows for GEMM 1, the
-//     expert's H rows for GEMM 2) straight into registers kWideLead stages
-//     ahead, and multiplies them with the four groups' fragments in LDS.
-//     Waves past the expert's rows only stream weights.
-// Four-wave workgroups of <= 128 VGPRs and a 40 KiB ring fit four to a CU (a
-// fifth, producer-only wave would limit a CU to two).  The barrier is the bare
-// s_barrier: a workgroup fence would wait for every load in flight.
+// kWideWaves waves, each with two roles:
+//   * weight streaming: a stage is two packed k-steps of the slab's kWideNT
+//     16-column groups (2 kWideNT KiB, one 1 KiB copy per (k-step, group));
+//     wave w issues kCopies of them, from HBM straight into an LDS ring of
+//     kRing stages with buffer loads to LDS (no registers), kRing - 1 stages
+//     ahead.  Before the barrier that ends stage st each wave waits, with a
+//     counted vmcnt, only for its own copies of stage st + 1; after the
+//     barrier the whole stage is in LDS;
+//   * MFMA: wave w owns rows 16 kWideMT w .. + 16 kWideMT - 1 of the item
+//     (kWideMT MFMA row tiles), reads its activation fragments (contiguous
+//     1 KiB per load, see frag_offset) into registers kWideLead stages ahead,
+//     and multiplies them with the stage's fragments in LDS.  Waves past the
+//     expert's rows only stream weights.
+// Sixteen waves of <= 128 VGPRs fill a CU; the ring takes most of its LDS.
+// The barrier is the bare s_barrier: a workgroup fence would wait for every
+// load in flight.
 //   GEMM 1: H[entry, :F] = silu(x Wg_e) * (x Wu_e).  The slab's columns are
-//           [g_j | u_j | g_j+1 | u_j+1] (16 each), so a lane holds the gate and
-//           up values of the same (row, column) and the SwiGLU runs in registers.
-//   GEMM 2: Y[entry, :d] = H[entry] Wd_e (fp32).
+//           [g_j | u_j | g_j+1 | u_j+1 | ...] (16 each), so a lane holds the
+//           gate and up values of the same (row, column) and the SwiGLU runs in
+//           registers.
+//   GEMM 2: Y[entry, :d] = H[entry] Wd_e (fp32).  Column groups past d (when
+//           d is not a multiple of kWideN) read as zero and are not stored.
 // fp8: e4m3 operands on both sides, per output column scales applied after the
 // accumulation.
 #ifndef DG_WIDE_RING
-#define DG_WIDE_RING 5
+#define DG_WIDE_RING 8
 #endif
-constexpr int kWideWaves = 4;
+constexpr int kWideNT = 8;                          // 16-column groups per slab
+constexpr int kWideN = 16 * kWideNT;                // slab width
+constexpr int kWideMT = 1;                          // 16-row MFMA tiles per wave
+constexpr int kWideWaves = kMoeRows / (16 * kWideMT);
 constexpr int kWideThreads = 64 * kWideWaves;
-constexpr int kRing = DG_WIDE_RING;          // LDS stages (8 KiB each)
-constexpr int kWideLead = 2;                 // activation stages loaded ahead per wave
+constexpr int kCopies = 2 * kWideNT / kWideWaves;   // 1 KiB weight copies per wave per stage
+constexpr int kRing = DG_WIDE_RING;                 // LDS stages (2 kWideNT KiB each)
+#ifndef DG_WIDE_LEAD
+#define DG_WIDE_LEAD 4
+#endif
+constexpr int kWideLead = DG_WIDE_LEAD;             // activation stages loaded ahead per wave
 constexpr int kWideSlots = kWideLead + 1;
-static_assert(kMoeRows == 32 * kWideWaves, "a work item is one row tile pair per wave");
-static_assert(kNT == kWideWaves, "one column group per wave");
-static_assert(kRing >= 3 && kRing * 8 * 1024 * 4 <= 160 * 1024, "ring size");
-static_assert(kRing <= kWideLead + 3, "the steady-state wait must also hold for the first stages");
+static_assert(kCopies >= 1 && kCopies * kWideWaves == 2 * kWideNT, "copies split evenly over the waves");
+static_assert(kCopies <= 2, "a wave's copies are of one column group");
+static_assert(kWideWaves <= 16, "at most 16 waves per workgroup");
+static_assert(kRing >= 3 && kRing * 2 * kWideNT * 1024 <= 160 * 1024, "ring size");
+static_assert(kRing - 1 >= kWideLead, "prologue order");
+static_assert(kWideNT % 4 == 0, "fragments are read from LDS four groups at a time");
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n, other counters free.
 constexpr int vmcnt_le(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Vector-memory operations a wave issues per stage: the activation loads (one
-// 16-byte fragment load per (k-step, row tile)) and its two weight copies.  The
-// counted waits below rely on these numbers.
-constexpr int kWideAOps = 4;
-constexpr int kWideWaitActive = (kRing - 2) * (kWideAOps + 2);
-constexpr int kWideWaitIdle = (kRing - 2) * 2;
+// 16-byte fragment load per (k-step, row tile)) and its weight copies.  The
+// counted waits below take these as lower bounds (the compiler may split a
+// load, never merge two): every operation issued after the copy waited for
+// only makes the wait stricter.
+constexpr int kWideAOps = 2 * kWideMT;
+constexpr int kWideWaitActive = (kRing - 2) * (kWideAOps + kCopies);
+constexpr int kWideWaitIdle = (kRing - 2) * kCopies;
 static_assert(kWideWaitActive < 64, "vmcnt holds at most 63 operations");
+
+using WideAcc = f32x4_t[kWideMT][kWideNT];
+using WideFrag = Frag16[2][kWideMT];              // [k-step][row tile]
 
 // Activation fragments of stage st of the k-step range [kb_lo, kb_hi) (clamped).
 // afrag[mt] points at the row tile's fragment of k-step 0 plus lane * 16 bytes;
 // k-steps are 1 KiB apart, so each load is one contiguous 1 KiB per wave.
-DG_DEV void wide_load_a(Frag16 (&a)[2][2], const uint8_t* const (&afrag)[2], int st, int kb_lo,
+DG_DEV void wide_load_a(WideFrag& a, const uint8_t* const (&afrag)[kWideMT], int st, int kb_lo,
                         int kb_hi) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int kb = min(kb_lo + 2 * st + ks, kb_hi - 1);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) a[ks][mt].u = ld16(afrag[mt] + (size_t)kb * 1024);
+        for (int mt = 0; mt < kWideMT; ++mt) a[ks][mt].u = ld16(afrag[mt] + (size_t)kb * 1024);
     }
 }
 
-// Both k-steps of a stage for both row tiles, straight-line.  When K has an odd
-// number of packed k-steps the last stage's second k-step is multiplied by a
-// zeroed activation fragment (keep1 = false).
-//
 // The weight fragments are read from LDS in inline asm: the waves also issue
-// LDS copies (global_load_lds), and the compiler cannot tell the ring slots
-// apart, so for a plain LDS read it would first wait for every copy in flight.
-// The barrier that ends the previous stage orders these reads after the copies
-// they need.
+// LDS copies, and the compiler cannot tell the ring slots apart, so for a plain
+// LDS read it would first wait for every copy in flight.  The barrier that ends
+// the previous stage orders these reads after the copies they need.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-DG_DEV void lds_read_groups(u32x4_t (&f)[kNT], uint32_t addr) {
-    static_assert(kNT == 4, "four 1 KiB column groups");
+DG_DEV void lds_read4(u32x4_t (&f)[4], uint32_t addr) {
     asm volatile(
         "ds_read_b128 %0, %4\n"
         "ds_read_b128 %1, %4 offset:1024\n"
@@ -325,37 +337,44 @@ DG_DEV void lds_read_groups(u32x4_t (&f)[kNT], uint32_t addr) {
         : "memory");
 }
 
+// Both k-steps of a stage, straight-line.  When K has an odd number of packed
+// k-steps the last stage's second k-step is multiplied by a zeroed activation
+// fragment (keep1 = false).
 template <bool FP8>
-DG_DEV void wide_mma(f32x4_t (&acc)[kMT][kNT], const Frag16 (&a)[2][2],
-                     const uint4 (*bs)[kNT][64], bool keep1, int lane) {
+DG_DEV void wide_mma(WideAcc& acc, const WideFrag& a, const uint4 (*bs)[kWideNT][64], bool keep1,
+                     int lane) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        Frag16 fb[kNT];
-        {
-            u32x4_t f[kNT];
-            lds_read_groups(f, (uint32_t)(uintptr_t)&bs[ks][0][lane]);
+        Frag16 am[kWideMT];
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) fb[nt].u = uint4{f[nt].x, f[nt].y, f[nt].z, f[nt].w};
-        }
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            Frag16 am = a[ks][mt];
+        for (int mt = 0; mt < kWideMT; ++mt) {
+            am[mt] = a[ks][mt];
             if (ks == 1) {
                 const uint32_t m = keep1 ? 0xffffffffu : 0u;
-                am.u = uint4{am.u.x & m, am.u.y & m, am.u.z & m, am.u.w & m};
+                am[mt].u = uint4{am[mt].u.x & m, am[mt].u.y & m, am[mt].u.z & m, am[mt].u.w & m};
+            }
+        }
+#pragma unroll
+        for (int n4 = 0; n4 < kWideNT; n4 += 4) {
+            Frag16 fb[4];
+            {
+                u32x4_t f[4];
+                lds_read4(f, (uint32_t)(uintptr_t)&bs[ks][n4][lane]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fb[i].u = uint4{f[i].x, f[i].y, f[i].z, f[i].w};
             }
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                if (FP8) {
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-                        am.l.lo, fb[nt].l.lo, acc[mt][nt], 0, 0, 0);
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-                        am.l.hi, fb[nt].l.hi, acc[mt][nt], 0, 0, 0);
-                } else {
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        am.b, fb[nt].b, acc[mt][nt], 0, 0, 0);
+            for (int mt = 0; mt < kWideMT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f32x4_t& c = acc[mt][n4 + i];
+                    if (FP8) {
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(am[mt].l.lo, fb[i].l.lo, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(am[mt].l.hi, fb[i].l.hi, c, 0, 0, 0);
+                    } else {
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[mt].b, fb[i].b, c, 0, 0, 0);
+                    }
                 }
-            }
         }
     }
 }
@@ -366,87 +385,121 @@ DG_DEV void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-using WideRing = uint4[kRing][2][kNT][64];       // [stage][k-step][group][lane]
+using WideRing = uint4[kRing][2][kWideNT][64];   // [stage][k-step][group][lane]
 
-// This wave's weight copy of stage st (clamped to the last stage) into ring slot
-// `slot`: k-steps 2 st and 2 st + 1 of column group g.  The copy is a buffer
-// load to LDS: the group's packed weights are the buffer (rsrc), the lane's
-// 16 bytes its constant VGPR offset (voff = lane * 16) and the k-step its scalar
-// offset, so no VGPR is rewritten per copy (a rewritten address register would
-// make the compiler wait for the copy before reusing it).
-DG_DEV void wide_copy_b(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int st, int slot, int NS,
-                        int kb_lo, int kb_hi, WideRing& bsm, int g) {
-    const int sc = min(st, NS - 1);
-    const int kb0 = min(kb_lo + 2 * sc, kb_hi - 1), kb1 = min(kb_lo + 2 * sc + 1, kb_hi - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)&bsm[slot][0][g][0], 16, voff, kb0 * 1024, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)&bsm[slot][1][g][0], 16, voff, kb1 * 1024, 0, 0);
+// The part of the weight stream a wave copies: copies q = w * kCopies + c,
+// c < kCopies, with k-step q % 2 of column group q / 2 (so a wave's copies are
+// of one group).  The copy is a buffer load to LDS: the group's packed weights
+// are the buffer (rsrc), the lane's 16 bytes its constant VGPR offset
+// (voff = lane * 16) and the k-step its scalar offset, so no VGPR is rewritten
+// per copy (a rewritten address register would make the compiler wait for the
+// copy before reusing it).
+struct WeightStream {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t voff;
+    int g, ks0;            // column group, first k-step parity
+    int kb_lo, kb_hi, NS;  // k-step range and its stage count
+};
+
+// Copies of stage st (clamped to the last stage) into ring slot `slot`.
+DG_DEV void wide_copy_b(const WeightStream& ws, int st, int slot, WideRing& bsm) {
+    const int sc = min(st, ws.NS - 1);
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) {
+        const int ks = ws.ks0 + c;
+        const int kb = min(ws.kb_lo + 2 * sc + ks, ws.kb_hi - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ws.rsrc, (__attribute__((address_space(3))) void*)&bsm[slot][ks][ws.g][0], 16, ws.voff,
+            kb * 1024, 0, 0);
+    }
 }
 
 // Buffer resource of one packed 16-column group (nbytes bytes at p): raw, no
-// stride; loads past nbytes return zero.
+// stride; loads past nbytes (all of them for nbytes = 0) return zero.
 DG_DEV __amdgpu_buffer_rsrc_t group_rsrc(const void* p, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
 }
 
-// A wave without rows streams its weight group and keeps the barrier count.
-DG_DEV void wide_stream_only(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int kb_lo, int kb_hi,
-                             WideRing& bsm, int g) {
-    const int NS = (kb_hi - kb_lo + 1) >> 1;
+// A wave without rows streams its share of the weights and keeps the barrier count.
+DG_DEV void wide_stream_only(const WeightStream& ws, WideRing& bsm) {
 #pragma unroll
-    for (int st = 0; st < kRing - 1; ++st) wide_copy_b(rsrc, voff, st, st, NS, kb_lo, kb_hi, bsm, g);
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitIdle));             // own copy of stage 0
+    for (int st = 0; st < kRing - 1; ++st) wide_copy_b(ws, st, st, bsm);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitIdle));             // own copies of stage 0
     bare_barrier();
-    for (int s0 = 0; s0 < NS; s0 += kRing) {
+    for (int s0 = 0; s0 < ws.NS; s0 += kRing) {
 #pragma unroll
         for (int u = 0; u < kRing; ++u) {
             const int st = s0 + u;
-            if (st >= NS) break;
-            wide_copy_b(rsrc, voff, st + kRing - 1, (u + kRing - 1) % kRing, NS, kb_lo, kb_hi, bsm, g);
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitIdle));     // own copy of st + 1
+            if (st >= ws.NS) break;
+            wide_copy_b(ws, st + kRing - 1, (u + kRing - 1) % kRing, bsm);   // into the slot of st - 1
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitIdle));     // own copies of st + 1
             bare_barrier();
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
-// acc[2 row tiles][4 column groups] over k-steps [kb_lo, kb_hi), streaming weight
-// group g.  Per stage st, in issue order: the activation loads of stage
-// st + kWideLead, the weight copy of stage st + kRing - 1, the MFMAs of stage st,
-// the wait for this wave's copy of stage st + 1 (every operation issued after it:
-// kRing - 2 stages' worth), the barrier.  The slot indices are compile-time: the
-// loop is unrolled over kRing * kWideSlots stages.
+// Operations a wave has issued after its copies of stage st + 1 when stage st
+// (st < kRing - 2) ends: the prologue's later copies and activation loads, and
+// stages 0..st.  From stage kRing - 2 on it is kWideWaitActive.
+constexpr int wide_wait_early(int st) {
+    return (kRing - 3 - st) * kCopies + kWideLead * kWideAOps + (st + 1) * (kWideAOps + kCopies);
+}
+constexpr int kWideEarly = kRing - 3 - kWideLead;   // stages whose exact count is below the steady one
+static_assert(kWideEarly <= 0 || wide_wait_early(kWideEarly - 1) < kWideWaitActive, "");
+static_assert(kWideEarly <= 0 || wide_wait_early(kWideEarly) >= kWideWaitActive, "");
+
+// The exact wait at the end of stage u < N of the first pass (u is a constant
+// once the stage loop is unrolled, and the chain folds to one s_waitcnt).
+template <int N>
+DG_DEV void wide_wait_first(int u) {
+    if constexpr (N > 0) {
+        if (u == N - 1) __builtin_amdgcn_s_waitcnt(vmcnt_le(wide_wait_early(N - 1)));
+        wide_wait_first<N - 1>(u);
+    }
+}
+
+// acc over the stream's k-steps.  The prologue issues the copies of stages
+// 0..kRing - 2, then the activation loads of stages 0..kWideLead - 1; stage st
+// then issues the activation loads of stage st + kWideLead and the copies of
+// stage st + kRing - 1, runs its MFMAs, waits for this wave's copies of stage
+// st + 1 and meets the barrier.  The slot indices are compile-time: the loop is
+// unrolled over kRing * kWideSlots stages.
 template <bool FP8>
-DG_DEV void wide_mainloop(f32x4_t (&acc)[kMT][kNT], const uint8_t* const (&afrag)[2],
-                          __amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int kb_lo, int kb_hi,
-                          WideRing& bsm, int g, int lane) {
-    const int NS = (kb_hi - kb_lo + 1) >> 1;
-    zero_acc(acc);
+DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
+                          const WeightStream& ws, WideRing& bsm, int lane) {
+    const int NS = ws.NS;
 #pragma unroll
-    for (int st = 0; st < kRing - 1; ++st) wide_copy_b(rsrc, voff, st, st, NS, kb_lo, kb_hi, bsm, g);
-    __builtin_amdgcn_sched_barrier(0);          // the copies stay ahead of the activation loads
-    Frag16 ra[kWideSlots][2][2];                  // [slot][k-step][row tile]
+    for (int mt = 0; mt < kWideMT; ++mt)
 #pragma unroll
-    for (int j = 0; j < kWideLead; ++j) wide_load_a(ra[j], afrag, min(j, NS - 1), kb_lo, kb_hi);
-    __builtin_amdgcn_sched_barrier(0);
-    // issued after the copy of stage 0: the other kRing - 2 copies and kWideLead
-    // stages of activations
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * (kRing - 2) + kWideLead * kWideAOps));
+        for (int nt = 0; nt < kWideNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < kRing - 1; ++st) wide_copy_b(ws, st, st, bsm);
+    asm volatile("" ::: "memory");   // the copies stay ahead of the activation loads
+    WideFrag ra[kWideSlots];
+#pragma unroll
+    for (int j = 0; j < kWideLead; ++j) wide_load_a(ra[j], afrag, min(j, NS - 1), ws.kb_lo, ws.kb_hi);
+    asm volatile("" ::: "memory");
+    // issued after the copies of stage 0: the other kRing - 2 stages' copies and
+    // kWideLead stages of activations
+    __builtin_amdgcn_s_waitcnt(vmcnt_le((kRing - 2) * kCopies + kWideLead * kWideAOps));
     bare_barrier();
     constexpr int kUnroll = kRing * kWideSlots;
+    static_assert(kUnroll >= kWideEarly, "");
     for (int s0 = 0; s0 < NS; s0 += kUnroll) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int st = s0 + u;
             if (st >= NS) break;
-            wide_load_a(ra[(u + kWideLead) % kWideSlots], afrag, min(st + kWideLead, NS - 1), kb_lo,
-                        kb_hi);
-            wide_copy_b(rsrc, voff, st + kRing - 1, (u + kRing - 1) % kRing, NS, kb_lo, kb_hi, bsm, g);
+            wide_load_a(ra[(u + kWideLead) % kWideSlots], afrag, min(st + kWideLead, NS - 1),
+                        ws.kb_lo, ws.kb_hi);
+            wide_copy_b(ws, st + kRing - 1, (u + kRing - 1) % kRing, bsm);
             __builtin_amdgcn_sched_barrier(0);      // issue the loads before the MFMAs
-            wide_mma<FP8>(acc, ra[u % kWideSlots], bsm[u % kRing], kb_lo + 2 * st + 1 < kb_hi, lane);
+            wide_mma<FP8>(acc, ra[u % kWideSlots], bsm[u % kRing], ws.kb_lo + 2 * st + 1 < ws.kb_hi,
+                          lane);
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitActive));   // own copy of st + 1
+            if (s0 == 0) wide_wait_first<kWideEarly>(u);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitActive));   // own copies of st + 1
             bare_barrier();
         }
     }
@@ -468,7 +521,7 @@ DG_DEV size_t frag_offset(int64_t row, int col, int K) {
 }
 
 template <bool FP8, int GEMM>
-__global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(
+__global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(   // <= 128 VGPRs
     const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
     const int2* __restrict__ work, const int32_t* __restrict__ work_count,
     const void* __restrict__ W, const float* __restrict__ scales, void* __restrict__ out) {
@@ -479,37 +532,43 @@ __global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(
     const int off = offsets[e];                                      // a multiple of 16
     const int n_e = min(offsets[e + 1] - off, item.y + kMoeRows);   // rows end (expert-relative)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * kTileN;
+    const int n0 = blockIdx.x * kWideN;
     const int KB = FP8 ? (K >> 6) : (K >> 5);     // packed k-steps
     const size_t gsize = (size_t)KB * 1024;       // bytes per packed 16-column group
-    const __amdgpu_buffer_rsrc_t rsrc =
-        group_rsrc((const uint8_t*)W + ((size_t)e * (N >> 4) + (n0 >> 4) + w) * gsize, (uint32_t)gsize);
-    const uint32_t voff = (uint32_t)lane * 16;
-    // rows r = item.y + 32 w + 16 mt + lane % 16 (expert-relative); n_e is a
-    // multiple of 16, so a row tile is wholly inside or outside the expert
-    const int wr0 = item.y + 32 * w;
-    const bool act1 = wr0 + 16 < n_e;
+    WeightStream ws;
+    ws.g = w * kCopies / 2;
+    ws.ks0 = (w * kCopies) & 1;
+    const int gcol = (n0 >> 4) + ws.g;            // the group's first column / 16
+    ws.rsrc = group_rsrc((const uint8_t*)W + ((size_t)e * (N >> 4) + gcol) * gsize,
+                         gcol < (N >> 4) ? (uint32_t)gsize : 0u);
+    ws.voff = (uint32_t)lane * 16;
+    ws.kb_lo = 0;
+    ws.kb_hi = KB;
+    ws.NS = (KB + 1) >> 1;
+    // rows r = item.y + 16 (kWideMT w + mt) + lane % 16 (expert-relative); n_e is
+    // a multiple of 16, so a row tile is wholly inside or outside the expert
+    const int wr0 = item.y + 16 * kWideMT * w;
     if (wr0 >= n_e) {
-        wide_stream_only(rsrc, voff, 0, KB, bsm, w);
+        wide_stream_only(ws, bsm);
         return;
     }
-    const uint8_t* afrag[2];
+    const uint8_t* afrag[kWideMT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int64_t tile = (off + wr0 + (mt == 1 && act1 ? 16 : 0)) >> 4;   // tile 1 repeats tile 0 past the rows
-        afrag[mt] = Af + ((size_t)tile * KB * 64 + lane) * 16;
+    for (int mt = 0; mt < kWideMT; ++mt) {
+        const int r = wr0 + 16 * mt < n_e ? wr0 + 16 * mt : wr0;   // tiles past the rows repeat tile 0
+        afrag[mt] = Af + ((size_t)((off + r) >> 4) * KB * 64 + lane) * 16;
     }
-    f32x4_t acc[kMT][kNT];
-    wide_mainloop<FP8>(acc, afrag, rsrc, voff, 0, KB, bsm, w, lane);
+    WideAcc acc;
+    wide_mainloop<FP8>(acc, afrag, ws, bsm, lane);
 
     // ---------------- epilogue: lane holds column lane % 16 of each group, rows 4 (lane / 16) + i
     const int l16 = lane & 15, g4 = 4 * (lane >> 4);
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-        if (mt == 1 && !act1) break;
+    for (int mt = 0; mt < kWideMT; ++mt) {
+        if (wr0 + 16 * mt >= n_e) break;
         if (GEMM == 1) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
+            for (int p = 0; p < kWideNT / 2; ++p) {
                 const int cg = n0 + 32 * p + l16, cu = cg + 16;   // interleaved weight columns
                 const float sg = FP8 ? scales[(size_t)e * N + cg] : 1.f;
                 const float su = FP8 ? scales[(size_t)e * N + cu] : 1.f;
@@ -526,8 +585,9 @@ __global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(
             }
         } else {
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
+            for (int nt = 0; nt < kWideNT; ++nt) {
                 const int c = n0 + 16 * nt + l16;
+                if (c >= N) break;
                 const float sc = FP8 ? scales[(size_t)e * N + c] : 1.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -652,10 +712,10 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
             (const float*)w.wu, (float*)H);
     } else {
         const int kq = dtype == kFP8 ? 64 : 32;
-        if ((2 * F) % kTileN || d % kq || F % kq || !Xf) return hipErrorInvalidValue;
+        if ((2 * F) % kWideN || d % kq || F % kq || !Xf) return hipErrorInvalidValue;
         const int KB = d / kq;
         dim3 gg((KB + 3) / 4, (max_rows + kMoePad - 1) / kMoePad);   // tiles past offsets[E] exit
-        dim3 grid((2 * F) / kTileN, work.max_items);
+        dim3 grid((2 * F) / kWideN, work.max_items);
         if (dtype == kFP8) {
             k_moe_gather_frag<true><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
                                                        (uint8_t*)Xf);
@@ -682,8 +742,8 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
         k_moe2_f32<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
             (const float*)H, d, F, offsets, E, max_rows, (const float*)w.w2, Y);
     } else {
-        if (d % kTileN || F % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
-        dim3 grid(d / kTileN, work.max_items);
+        if (d % 16 || F % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
+        dim3 grid((d + kWideN - 1) / kWideN, work.max_items);
         if (dtype == kFP8)
             k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
                                                               work.items, work.count, w.w2, w.s2, Y);
