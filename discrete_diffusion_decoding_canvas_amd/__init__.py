@@ -24,7 +24,7 @@ EXPORTED = (
     "dg_denoise_step", "dg_generate_block", "dg_commit_canvas", "dg_check_finite",
     "dg_reset_context", "dg_get_state", "dg_get_capture", "dg_get_kv", "dg_attention",
     "dg_moe_layer", "dg_init_canvas", "dg_profile_begin", "dg_profile_end", "dg_set_kv",
-    "dg_set_capture",
+    "dg_set_capture", "dg_set_graphs",
 )
 DG_PROF_MOE_GEMM1, DG_PROF_MOE_GEMM2, DG_PROF_ATTENTION, DG_PROF_LM_HEAD, DG_PROF_DENSE = range(5)
 DG_PROF_N = 5
@@ -72,6 +72,7 @@ def _load_library():
         "dg_get_kv": ([vp, i32, i32, i64, i64, vp, vp], i32),
         "dg_set_kv": ([vp, i32, i32, i64, i64, vp, vp], i32),
         "dg_set_capture": ([vp, u32], i32),
+        "dg_set_graphs": ([vp, i32], i32),
         "dg_attention": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float, i32, i32,
                           i32, vp], i32),
         "dg_moe_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
@@ -178,6 +179,10 @@ def dg_get_state(h):
 
 def dg_set_capture(h, capture_mask: int) -> None:
     _check(_lib.dg_set_capture(h, capture_mask))
+
+
+def dg_set_graphs(h, enable: bool) -> None:
+    _check(_lib.dg_set_graphs(h, 1 if enable else 0))
 
 
 def dg_get_capture(h, what: int, layer: int, d_dst, stream=None) -> None:

@@ -124,6 +124,13 @@ struct dg_handle {
     int k_blk = 0;
     bool prefilled = false;
 
+    // layer stack of a denoise pass as a HIP graph, captured for one context
+    // length (the attention and RoPE launches depend on it) and replayed
+    bool use_graphs = true;
+    hipStream_t gstream = nullptr;   // capture stream (default priority)
+    hipGraphExec_t gexec = nullptr;
+    int64_t g_nctx = -1;
+
     // per-kernel-class event timing
     bool prof = false;
     std::vector<hipEvent_t> ev;
@@ -223,6 +230,13 @@ static MoeWork moe_work(dg_handle* h, int n) {
     w.count = h->work_count;
     w.max_items = (n * h->k + kMoeRows - 1) / kMoeRows + h->E;
     return w;
+}
+
+// Drop the captured layer-stack graph (weights or context changed).
+static void drop_graph(dg_handle* h) {
+    if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
+    h->gexec = nullptr;
+    h->g_nctx = -1;
 }
 
 // Allocate the capture buffers a mask needs (once) and make it the active mask.
@@ -490,6 +504,8 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
 void dg_destroy(dg_handle* h) {
     if (!h) return;
     (void)hipDeviceSynchronize();
+    if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
+    if (h->gstream) (void)hipStreamDestroy(h->gstream);
     for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
     for (void* p : h->allocs) (void)hipFree(p);
     if (h->stage) (void)hipFree(h->stage);
@@ -519,6 +535,8 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
     if (kind < DG_T_EMBED || kind > DG_T_WD) return fail(DG_EINVAL, "bad tensor kind %d", kind);
     const bool is_exp = kind >= DG_T_WG;
     if (kind != DG_T_EMBED && (layer < 0 || layer >= h->L)) return fail(DG_EINVAL, "bad layer %d", layer);
+    HIP_TRY(hipDeviceSynchronize());
+    drop_graph(h);
     if (is_exp && (expert < -1 || expert >= h->E)) return fail(DG_EINVAL, "bad expert %d", expert);
     const int dt = is_exp ? h->edt : h->act;
     const size_t es = dsize(dt);
@@ -613,6 +631,15 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
     return DG_OK;
 }
 
+int dg_set_graphs(dg_handle* h, int32_t enable) {
+    g_err.clear();
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    HIP_TRY(hipDeviceSynchronize());
+    h->use_graphs = enable != 0;
+    if (!h->use_graphs) drop_graph(h);
+    return DG_OK;
+}
+
 int dg_set_capture(dg_handle* h, uint32_t capture_mask) {
     g_err.clear();
     if (!h) return fail(DG_EINVAL, "NULL handle");
@@ -659,6 +686,7 @@ int dg_profile_end(dg_handle* h, double* total_ms, int32_t* counts) {
 
 int dg_reset_context(dg_handle* h) {
     if (!h) return fail(DG_EINVAL, "NULL handle");
+    drop_graph(h);
     h->n_ctx = 0;
     h->k_blk = 0;
     h->prefilled = false;
@@ -705,6 +733,36 @@ int dg_commit_canvas(dg_handle* h, const int32_t* d_canvas, void* stream) {
     return DG_OK;
 }
 
+// The L decoder layers of a denoise pass over the canvas at n_ctx, as one HIP
+// graph replayed on stream s.  Captured on the handle's own stream the first
+// time for this context length.  The kernels record no memset nodes.
+static int run_layers_graph(dg_handle* h, hipStream_t s) {
+    if (!h->gexec || h->g_nctx != h->n_ctx) {
+        drop_graph(h);
+        if (!h->gstream) HIP_TRY(hipStreamCreateWithFlags(&h->gstream, hipStreamNonBlocking));
+        HIP_TRY(hipStreamBeginCapture(h->gstream, hipStreamCaptureModeThreadLocal));
+        int rc = DG_OK;
+        for (int l = 0; l < h->L && rc == DG_OK; ++l)
+            rc = run_layer(h, l, h->C, h->n_ctx, false, false, h->gstream, false);
+        hipGraph_t g = nullptr;
+        const hipError_t e = hipStreamEndCapture(h->gstream, &g);
+        if (rc != DG_OK || e != hipSuccess) {
+            if (g) (void)hipGraphDestroy(g);
+            (void)hipGetLastError();
+            return rc != DG_OK ? rc : fail(DG_EHIP, "graph capture failed: %s", hipGetErrorString(e));
+        }
+        const hipError_t ei = hipGraphInstantiate(&h->gexec, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (ei != hipSuccess) {
+            h->gexec = nullptr;
+            return fail(DG_EHIP, "graph instantiation failed: %s", hipGetErrorString(ei));
+        }
+        h->g_nctx = h->n_ctx;
+    }
+    HIP_TRY(hipGraphLaunch(h->gexec, s));
+    return DG_OK;
+}
+
 int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t step,
                     int32_t T, uint64_t seed, void* stream) {
     g_err.clear();
@@ -719,7 +777,10 @@ int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int
     const int C = h->C;
     K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, C, h->d,
                                h->cfg.rms_eps, h->x, h->a, s));
-    for (int l = 0; l < h->L; ++l) {
+    const uint32_t per_layer = DG_CAP_ROUTING | DG_CAP_HIDDEN | DG_CAP_ATTN | DG_CAP_ROUTER_LOGITS;
+    if (h->use_graphs && !h->prof && !(h->cap_mask & per_layer)) {
+        DG_TRY(run_layers_graph(h, s));
+    } else for (int l = 0; l < h->L; ++l) {
         DG_TRY(run_layer(h, l, C, h->n_ctx, false, false, s, true));
         if (h->cap(DG_CAP_ROUTING)) {
             HIP_TRY(hipMemcpyAsync(h->cap_idx + (size_t)l * C * h->k, h->idx,

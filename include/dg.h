@@ -196,6 +196,15 @@ int dg_reset_context(dg_handle* h);
 /* Current committed context length and canvas index. */
 int dg_get_state(dg_handle* h, int64_t* n_ctx, int32_t* k_blk);
 
+/* Replay the decoder-layer stack of dg_denoise_step as a HIP graph (enable = 1,
+ * the default) or launch its kernels one by one (0).  The graph is captured
+ * on first use for the current context length and replaced when n_ctx, the
+ * weights or the context change; passes with per-layer captures
+ * (DG_CAP_ROUTING, _HIDDEN, _ATTN, _ROUTER_LOGITS) or kernel timing enabled
+ * run eagerly.  Both paths launch the same kernels with the same arguments,
+ * so results are identical.  Waits for the device. */
+int dg_set_graphs(dg_handle* h, int32_t enable);
+
 /* Change which captures the following passes record (DG_CAP_* bits; 0 turns
  * them off).  Allocates the buffers a capture needs on first use; waits for
  * the device. */
