@@ -98,6 +98,7 @@ struct dg_handle {
     float* Y = nullptr;
     int2* work_items = nullptr;
     int32_t* work_count = nullptr;
+    uint32_t* route_ticket = nullptr;
 
     HeadPartials hp{};
     float* st_m = nullptr;
@@ -180,7 +181,9 @@ static int validate_cfg(const dg_model_cfg* c) {
         return fail(DG_EINVAL, "n_experts must be a multiple of 4, at most 256");
     if (c->canvas > kMaxCanvas) return fail(DG_EINVAL, "canvas must be <= %d", kMaxCanvas);
     if (c->head_dim & 1) return fail(DG_EINVAL, "head_dim must be even");
-    if (c->d_model > 256 * kCombineCols) return fail(DG_EINVAL, "d_model must be <= %d", 256 * kCombineCols);
+    if (c->d_model > 256 * kCombineCols || c->d_model % 4)
+        return fail(DG_EINVAL, "d_model must be a multiple of 4, at most %d", 256 * kCombineCols);
+    if (c->head_dim > 128) return fail(DG_EINVAL, "head_dim must be <= 128");
     if (c->max_ctx < c->canvas) return fail(DG_EINVAL, "max_ctx must hold at least one canvas");
     if (!(c->temperature > 0.f)) return fail(DG_EINVAL, "temperature must be > 0");
     if (!(c->rope_base > 0.0)) return fail(DG_EINVAL, "rope_base must be > 0");
@@ -229,6 +232,7 @@ static MoeWork moe_work(dg_handle* h, int n) {
     w.items = h->work_items;
     w.count = h->work_count;
     w.max_items = (n * h->k + kMoeRows - 1) / kMoeRows + h->E;
+    w.ticket = h->route_ticket;
     return w;
 }
 
@@ -477,6 +481,8 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->inv, T * k));
     A_TRY(h->allocT(&h->work_items, (T * k + kMoeRows - 1) / kMoeRows + E));
     A_TRY(h->allocT(&h->work_count, 1));
+    A_TRY(h->allocT(&h->route_ticket, 1));
+    if (hipMemset(h->route_ticket, 0, 4) != hipSuccess) return cleanup(fail(DG_EHIP, "ticket reset failed"));
     if (h->edt != kF32) A_TRY(h->alloc(&h->Xf, rows * d * esz));
     A_TRY(h->alloc(&h->H, rows * F * esz));
     A_TRY(h->allocT(&h->Y, rows * d));

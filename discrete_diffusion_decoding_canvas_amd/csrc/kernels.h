@@ -23,9 +23,10 @@ inline int64_t moe_rows_cap(int64_t n, int k, int E, int pad) { return n * k + (
 // Expert-GEMM work list built by the permutation: item i covers rows
 // [row0, row0 + kMoeRows) of expert e (clipped to the expert's count).
 struct MoeWork {
-    int2* items;      // {e, row0}
-    int32_t* count;   // number of valid items
-    int max_items;    // grid bound: ceil(entries / kMoeRows) + E
+    int2* items;       // {e, row0}
+    int32_t* count;    // number of valid items
+    int max_items;     // grid bound: ceil(entries / kMoeRows) + E
+    uint32_t* ticket;  // zero-initialised block counter of the fused top-k + permutation
 };
 
 // Transposed, key-permuted V cache: Vt[h][dim][slot], rows padded to a multiple

@@ -63,71 +63,118 @@ __global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict
 
 // ------------------------------------------------------------------ RMSNorm
 // a = rmsnorm(x) (unit gains); a8 (optional) = e4m3(a) for fp8 expert inputs.
+// One block per row, four columns per thread per pass (d % 4 == 0): every load
+// of the row is issued before the reduction.
+constexpr int kRowPasses = kCombineCols / 4;   // float4 passes per thread: d <= 1024 * kRowPasses
+
+template <typename T>
+DG_DEV void store4(T* dst, float4 v) {
+    if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<float4*>(dst) = v;
+    } else {
+        ushort4 u;
+        u.x = f32_to_bf16(v.x);
+        u.y = f32_to_bf16(v.y);
+        u.z = f32_to_bf16(v.z);
+        u.w = f32_to_bf16(v.w);
+        *reinterpret_cast<ushort4*>(dst) = u;
+    }
+}
+
+// Normalised row (xs scaled by r) to a (as T) and a8 (e4m3 of the rounded a).
+template <typename T>
+DG_DEV void store_norm(const float4 (&xs)[kRowPasses], float r, int d4, T* __restrict__ a,
+                       uint8_t* __restrict__ a8) {
+#pragma unroll
+    for (int p = 0; p < kRowPasses; ++p) {
+        const int c4 = threadIdx.x + 256 * p;
+        if (c4 >= d4) break;
+        const float4 v = make_float4(xs[p].x * r, xs[p].y * r, xs[p].z * r, xs[p].w * r);
+        store4<T>(a + 4 * (int64_t)c4, v);
+        if (a8) {
+            uchar4 q;
+            q.x = (uint8_t)f32_to_e4m3(to_f32<T>(from_f32<T>(v.x)));
+            q.y = (uint8_t)f32_to_e4m3(to_f32<T>(from_f32<T>(v.y)));
+            q.z = (uint8_t)f32_to_e4m3(to_f32<T>(from_f32<T>(v.z)));
+            q.w = (uint8_t)f32_to_e4m3(to_f32<T>(from_f32<T>(v.w)));
+            *reinterpret_cast<uchar4*>(a8 + 4 * (int64_t)c4) = q;
+        }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int d, float eps,
                                                  T* __restrict__ a, uint8_t* __restrict__ a8) {
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
-    const float* xr = x + row * d;
-    float xs[kCombineCols];   // d <= 256 * kCombineCols: the row stays in registers
+    const int d4 = d >> 2;
+    const float4* xr = reinterpret_cast<const float4*>(x + row * d);
+    float4 xs[kRowPasses];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < kCombineCols; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        xs[i] = c < d ? xr[c] : 0.f;
-        ss += xs[i] * xs[i];
+    for (int p = 0; p < kRowPasses; ++p) {
+        const int c4 = threadIdx.x + 256 * p;
+        xs[p] = c4 < d4 ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        ss += xs[p].x * xs[p].x + xs[p].y * xs[p].y + xs[p].z * xs[p].z + xs[p].w * xs[p].w;
     }
     const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-#pragma unroll
-    for (int i = 0; i < kCombineCols; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        if (c < d) {
-            const T av = from_f32<T>(xs[i] * r);
-            a[row * d + c] = av;
-            if (a8) a8[row * d + c] = (uint8_t)f32_to_e4m3(to_f32<T>(av));
-        }
-    }
+    store_norm<T>(xs, r, d4, a + row * d, a8 ? a8 + row * d : nullptr);
 }
 
 // ------------------------------------------------------------------ RoPE + scatter
 // qkv float [M, (Hq + 2 Hkv) D] -> Q [Hq][M][D] rotated, K cache rows pos0+m rotated,
 // V cache rows pos0+m.  Rotate-half pairs (j, j + D/2), angle table [pos][D/2].
 // bf16 V is stored transposed and key-permuted for the attention MFMA (vt_index).
+// One block per (32 tokens, head): Q and K rows are written along j; a V head
+// goes through LDS so that its transposed stores run along the positions
+// (32 consecutive positions of one dimension are one 64-byte run).
+constexpr int kRopeTokens = 32;
+
 template <typename T, bool VPACKED>
-__global__ void k_rope_scatter(const float* __restrict__ qkv, int M, int Hq, int Hkv, int D,
-                               int64_t pos0, const float* __restrict__ cos_t,
-                               const float* __restrict__ sin_t, T* __restrict__ q,
-                               T* __restrict__ kc, T* __restrict__ vc, int64_t kv_rows) {
-    const int m = blockIdx.x;
-    const int head = blockIdx.y;           // 0..Hq-1 queries, Hq..Hq+Hkv-1 keys, then values
+__global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ qkv, int M, int Hq,
+                                                      int Hkv, int D, int64_t pos0,
+                                                      const float* __restrict__ cos_t,
+                                                      const float* __restrict__ sin_t,
+                                                      T* __restrict__ q, T* __restrict__ kc,
+                                                      T* __restrict__ vc, int64_t kv_rows) {
+    __shared__ float vt[kRopeTokens][129];   // D <= 128
+    const int m0 = blockIdx.x * kRopeTokens;
+    const int head = blockIdx.y;             // 0..Hq-1 queries, Hq..Hq+Hkv-1 keys, then values
     const int half = D >> 1;
-    const int64_t pos = pos0 + m;
-    const float* src = qkv + (int64_t)m * (Hq + 2 * Hkv) * D + (int64_t)head * D;
-    for (int j = threadIdx.x; j < half; j += blockDim.x) {
-        float x1 = src[j], x2 = src[j + half];
-        if (head < Hq + Hkv) {
-            float c = cos_t[pos * half + j], s = sin_t[pos * half + j];
-            float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
-            if (head < Hq) {
-                T* dst = q + ((int64_t)head * M + m) * D;
+    const int64_t ld = (int64_t)(Hq + 2 * Hkv) * D;
+    const int nt = min(kRopeTokens, M - m0);
+    if (head < Hq + Hkv || !VPACKED) {
+        for (int e = threadIdx.x; e < nt * half; e += 256) {
+            const int mi = e / half, j = e - mi * half;
+            const int m = m0 + mi;
+            const int64_t pos = pos0 + m;
+            const float* src = qkv + (int64_t)m * ld + (int64_t)head * D;
+            const float x1 = src[j], x2 = src[j + half];
+            if (head < Hq + Hkv) {
+                const float c = cos_t[pos * half + j], sn = sin_t[pos * half + j];
+                const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+                T* dst = head < Hq ? q + ((int64_t)head * M + m) * D
+                                   : kc + ((int64_t)(head - Hq) * kv_rows + pos) * D;
                 dst[j] = from_f32<T>(y1);
                 dst[j + half] = from_f32<T>(y2);
             } else {
-                T* dst = kc + ((int64_t)(head - Hq) * kv_rows + pos) * D;
-                dst[j] = from_f32<T>(y1);
-                dst[j + half] = from_f32<T>(y2);
-            }
-        } else {
-            const int h = head - Hq - Hkv;
-            if (VPACKED) {
-                vc[vt_index(h, j, pos, D, kv_rows)] = from_f32<T>(x1);
-                vc[vt_index(h, j + half, pos, D, kv_rows)] = from_f32<T>(x2);
-            } else {
-                T* dst = vc + ((int64_t)h * kv_rows + pos) * D;
+                T* dst = vc + ((int64_t)(head - Hq - Hkv) * kv_rows + pos) * D;
                 dst[j] = from_f32<T>(x1);
                 dst[j + half] = from_f32<T>(x2);
             }
         }
+        return;
+    }
+    // packed V: rows in along the dimensions, out along the positions
+    for (int e = threadIdx.x; e < nt * D; e += 256) {
+        const int mi = e / D, t = e - mi * D;
+        vt[mi][t] = qkv[(int64_t)(m0 + mi) * ld + (int64_t)head * D + t];
+    }
+    __syncthreads();
+    const int h = head - Hq - Hkv;
+    for (int e = threadIdx.x; e < kRopeTokens * D; e += 256) {
+        const int t = e / kRopeTokens, mi = e - t * kRopeTokens;
+        if (mi < nt) vc[vt_index(h, t, pos0 + m0 + mi, D, kv_rows)] = from_f32<T>(vt[mi][t]);
     }
 }
 
@@ -172,7 +219,9 @@ __global__ void k_write_kv(T* __restrict__ cache, int Hkv, int D, int64_t rows, 
 // y = sum_j gates[t, j] * Y[inv[t*k + j], :] in slot order.
 // MODE 0: x += y, then a = rmsnorm(x) (and a8 = e4m3(a) if given) when a != null.
 // MODE 1: out = y (stored as T), no residual (the stand-alone MoE layer).
-template <typename T, int MODE>
+// One block per token, four columns per thread per pass (d % 4 == 0); all of
+// the token's expert rows are loaded before they are summed.
+template <typename T, int MODE, int KMAX>
 __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y, int d, int k,
                                                      const float* __restrict__ gates,
                                                      const int32_t* __restrict__ inv,
@@ -181,46 +230,46 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y
                                                      T* __restrict__ out) {
     __shared__ float red[4];
     const int64_t t = blockIdx.x;
-    float g[kMaxTopK];
-    const float* yr[kMaxTopK];
+    const int d4 = d >> 2;
+    float g[KMAX];
+    const float4* yr[KMAX];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
+    for (int j = 0; j < KMAX; ++j) {
         g[j] = j < k ? gates[t * k + j] : 0.f;
-        yr[j] = Y + (int64_t)(j < k ? inv[t * k + j] : inv[t * k]) * d;
+        yr[j] = reinterpret_cast<const float4*>(Y + (int64_t)(j < k ? inv[t * k + j] : inv[t * k]) * d);
     }
-    float xs[kCombineCols];
+    float4* xr = reinterpret_cast<float4*>(x + t * d);
+    float4 xs[kRowPasses];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < kCombineCols; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        if (c < d) {
-            float v[kMaxTopK];
+    for (int p = 0; p < kRowPasses; ++p) {
+        const int c4 = threadIdx.x + 256 * p;
+        if (c4 >= d4) break;
+        float4 v[KMAX];
 #pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j) v[j] = j < k ? yr[j][c] : 0.f;
-            float y = 0.f;
+        for (int j = 0; j < KMAX; ++j) v[j] = j < k ? yr[j][c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j) y += g[j] * v[j];   // slot order
-            if (MODE == 0) {
-                const float nx = x[t * d + c] + y;
-                x[t * d + c] = nx;
-                xs[i] = nx;
-                ss += nx * nx;
-            } else {
-                out[t * d + c] = from_f32<T>(y);
-            }
+        for (int j = 0; j < KMAX; ++j) {   // slot order
+            if (j >= k) break;
+            y.x += g[j] * v[j].x;
+            y.y += g[j] * v[j].y;
+            y.z += g[j] * v[j].z;
+            y.w += g[j] * v[j].w;
+        }
+        if (MODE == 0) {
+            const float4 xo = xr[c4];
+            const float4 nx = make_float4(xo.x + y.x, xo.y + y.y, xo.z + y.z, xo.w + y.w);
+            xr[c4] = nx;
+            xs[p] = nx;
+            ss += nx.x * nx.x + nx.y * nx.y + nx.z * nx.z + nx.w * nx.w;
+        } else {
+            store4<T>(out + t * d + 4 * c4, y);
         }
     }
     if (MODE == 0 && a != nullptr) {
         const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-#pragma unroll
-        for (int i = 0; i < kCombineCols; ++i) {
-            const int c = threadIdx.x + 256 * i;
-            if (c < d) {
-                const T av = from_f32<T>(xs[i] * r);
-                a[t * d + c] = av;
-                if (a8) a8[t * d + c] = (uint8_t)f32_to_e4m3(to_f32<T>(av));
-            }
-        }
+        store_norm<T>(xs, r, d4, a + t * d, a8 ? a8 + t * d : nullptr);
     }
 }
 
@@ -404,6 +453,7 @@ hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, c
 hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
                           uint8_t* a8, hipStream_t s) {
     if (M <= 0) return hipSuccess;
+    if ((d & 3) || d > 1024 * kRowPasses) return hipErrorInvalidValue;
     if (dtype == kF32)
         k_rmsnorm<float><<<M, 256, 0, s>>>(x, d, eps, (float*)a, a8);
     else
@@ -415,8 +465,9 @@ hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int H
                                int64_t pos0, const float* cos_t, const float* sin_t, void* q,
                                void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    dim3 grid(M, Hq + 2 * Hkv);
-    int threads = D / 2 < 64 ? 64 : D / 2;
+    if (D > 128) return hipErrorInvalidValue;
+    dim3 grid((M + kRopeTokens - 1) / kRopeTokens, Hq + 2 * Hkv);
+    const int threads = 256;
     if (dtype == kF32)
         k_rope_scatter<float, false><<<grid, threads, 0, s>>>(
             qkv, M, Hq, Hkv, D, pos0, cos_t, sin_t, (float*)q, (float*)kc, (float*)vc, kv_rows);
@@ -469,24 +520,32 @@ hipError_t launch_write_kv(int dtype, bool vpacked, void* cache, int Hkv, int D,
     LAUNCH_CHECK();
 }
 
+template <typename T, int MODE, int KMAX>
+static void combine_k(const float* Y, int M, int d, int k, const float* gates, const int32_t* inv,
+                      float* x, float eps, void* a, uint8_t* a8, void* out, hipStream_t s) {
+    k_moe_combine<T, MODE, KMAX><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, (T*)a, a8, (T*)out);
+}
+
+template <typename T, int MODE>
+static void combine_m(const float* Y, int M, int d, int k, const float* gates, const int32_t* inv,
+                      float* x, float eps, void* a, uint8_t* a8, void* out, hipStream_t s) {
+    if (k <= 2) combine_k<T, MODE, 2>(Y, M, d, k, gates, inv, x, eps, a, a8, out, s);
+    else if (k <= 4) combine_k<T, MODE, 4>(Y, M, d, k, gates, inv, x, eps, a, a8, out, s);
+    else if (k <= 8) combine_k<T, MODE, 8>(Y, M, d, k, gates, inv, x, eps, a, a8, out, s);
+    else combine_k<T, MODE, kMaxTopK>(Y, M, d, k, gates, inv, x, eps, a, a8, out, s);
+}
+
 hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
                               const float* gates, const int32_t* inv, float* x, float eps,
                               void* a, uint8_t* a8, void* out, hipStream_t s) {
     if (M <= 0) return hipSuccess;
+    if ((d & 3) || d > 1024 * kRowPasses || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
     if (dtype == kF32) {
-        if (mode == 0)
-            k_moe_combine<float, 0><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, (float*)a, a8,
-                                                      nullptr);
-        else
-            k_moe_combine<float, 1><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, nullptr,
-                                                      nullptr, (float*)out);
+        if (mode == 0) combine_m<float, 0>(Y, M, d, k, gates, inv, x, eps, a, a8, nullptr, s);
+        else combine_m<float, 1>(Y, M, d, k, gates, inv, x, eps, nullptr, nullptr, out, s);
     } else {
-        if (mode == 0)
-            k_moe_combine<bf16_t, 0><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, (bf16_t*)a,
-                                                       a8, nullptr);
-        else
-            k_moe_combine<bf16_t, 1><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, nullptr,
-                                                       nullptr, (bf16_t*)out);
+        if (mode == 0) combine_m<bf16_t, 0>(Y, M, d, k, gates, inv, x, eps, a, a8, nullptr, s);
+        else combine_m<bf16_t, 1>(Y, M, d, k, gates, inv, x, eps, nullptr, nullptr, out, s);
     }
     LAUNCH_CHECK();
 }

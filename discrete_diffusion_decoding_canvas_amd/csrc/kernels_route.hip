@@ -22,15 +22,12 @@ namespace dg {
 
 constexpr int kMaxExperts = 256;
 
-__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int nsplit,
-                                                     int M, int E, int k,
-                                                     int32_t* __restrict__ idx,
-                                                     float* __restrict__ gates) {
-    __shared__ __attribute__((aligned(16))) float lg[4][kMaxExperts];
-    __shared__ float sv[4][16];
+// Top-k of token t by wave w of the block (no block-level synchronisation:
+// only wave-level LDS use).
+DG_DEV void topk_token(const float* __restrict__ logits, int nsplit, int M, int E, int k, int t,
+                       int32_t* __restrict__ idx, float* __restrict__ gates,
+                       float (*lg)[kMaxExperts], float (*sv)[16]) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + w;
-    if (t >= M) return;   // no block-level synchronisation below: only wave-level LDS use
     for (int e = lane; e < E; e += 64) {
         float part[kMaxRouterSplit];
 #pragma unroll
@@ -70,25 +67,15 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
     }
 }
 
-// One workgroup for up to kPermSmall entries: counts, scan, row assignment.
-constexpr int kPermSmall = 8192;
-
-// Work items of the expert GEMMs: (expert, first row) for every kMoeRows-row
-// chunk of every expert that received entries, experts in order.  off holds the
-// (padded) row offsets; woff[e] is the first item of expert e.
-DG_DEV void emit_work(const int32_t* off, int E, int32_t* woff, int2* items, int32_t* count) {
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            woff[e] = run;
-            run += (off[e + 1] - off[e] + kMoeRows - 1) / kMoeRows;
-        }
-        woff[E] = run;
-        *count = run;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        for (int i = woff[e]; i < woff[e + 1]; ++i) items[i] = make_int2(e, (i - woff[e]) * kMoeRows);
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int nsplit,
+                                                     int M, int E, int k,
+                                                     int32_t* __restrict__ idx,
+                                                     float* __restrict__ gates) {
+    __shared__ __attribute__((aligned(16))) float lg[4][kMaxExperts];
+    __shared__ float sv[4][16];
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= M) return;
+    topk_token(logits, nsplit, M, E, k, t, idx, gates, lg, sv);
 }
 
 // Every expert's rows start at a multiple of pad (16 for the MFMA expert GEMMs,
@@ -96,13 +83,67 @@ DG_DEV void emit_work(const int32_t* off, int E, int32_t* woff, int2* items, int
 // an expert's entries up to the next multiple are padding, perm_token = -1.
 DG_DEV int round_up(int v, int pad) { return (v + pad - 1) / pad * pad; }
 
-__global__ __launch_bounds__(1024) void k_moe_permute_small(const int32_t* __restrict__ idx, int n,
-                                                            int E, int k, int pad,
-                                                            int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ perm_token,
-                                                            int32_t* __restrict__ inv,
-                                                            int2* __restrict__ work,
-                                                            int32_t* __restrict__ work_count) {
+// In-place exclusive prefix sum of v[0..n), n <= 256, by wave 0 (four values
+// per lane, then a shuffle scan across the lanes); v[n] = total.  The caller
+// synchronises the block before and after.
+DG_DEV void wave0_exclusive_scan(int32_t* v, int n) {
+    if (threadIdx.x >= 64) return;
+    const int l = threadIdx.x;
+    int a[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * l + i;
+        a[i] = e < n ? v[e] : 0;
+        s += a[i];
+    }
+    int inc = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(inc, o, 64);
+        if (l >= o) inc += u;
+    }
+    int run = inc - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * l + i;
+        if (e < n) v[e] = run;
+        run += a[i];
+    }
+    if (l == 63) v[n] = inc;
+}
+
+// From per-expert entry counts cnt[0..E): padded row offsets (to global
+// `offsets` and LDS off), the expert-GEMM work items ((expert, first row) for
+// every kMoeRows-row chunk, experts in order) and -1 in perm_token for the
+// padding rows.  woff is LDS scratch of E + 1 entries.
+DG_DEV void route_offsets(const int32_t* cnt, int E, int pad, int32_t* off, int32_t* woff,
+                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+                          int2* __restrict__ items, int32_t* __restrict__ count) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) off[e] = round_up(cnt[e], pad);
+    __syncthreads();
+    wave0_exclusive_scan(off, E);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        woff[e] = (off[e + 1] - off[e] + kMoeRows - 1) / kMoeRows;
+    __syncthreads();
+    wave0_exclusive_scan(woff, E);
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
+    if (threadIdx.x == 0) *count = woff[E];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        for (int i = woff[e]; i < woff[e + 1]; ++i) items[i] = make_int2(e, (i - woff[e]) * kMoeRows);
+        for (int j = off[e] + cnt[e]; j < off[e + 1]; ++j) perm_token[j] = -1;
+    }
+}
+
+// The permutation of n <= kPermSmall entries by one block: counts, offsets,
+// work items, and every entry's row (the next free row of its expert).
+constexpr int kPermSmall = 8192;
+
+DG_DEV void permute_block(const int32_t* __restrict__ idx, int n, int E, int k, int pad,
+                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+                          int32_t* __restrict__ inv, int2* __restrict__ work,
+                          int32_t* __restrict__ work_count) {
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
     __shared__ int32_t woff[kMaxExperts + 1];
@@ -110,22 +151,9 @@ __global__ __launch_bounds__(1024) void k_moe_permute_small(const int32_t* __res
     __syncthreads();
     for (int f = threadIdx.x; f < n; f += blockDim.x) atomicAdd(&cnt[idx[f]], 1);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = run;
-            run += round_up(cnt[e], pad);
-        }
-        off[E] = run;
-    }
+    route_offsets(cnt, E, pad, off, woff, offsets, perm_token, work, work_count);
     __syncthreads();
-    emit_work(off, E, woff, work, work_count);
-    __syncthreads();
-    for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        for (int j = off[e] + cnt[e]; j < off[e + 1]; ++j) perm_token[j] = -1;
-        cnt[e] = 0;
-    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
     for (int f = threadIdx.x; f < n; f += blockDim.x) {
         const int e = idx[f];
@@ -133,6 +161,36 @@ __global__ __launch_bounds__(1024) void k_moe_permute_small(const int32_t* __res
         perm_token[pos] = f / k;
         inv[f] = pos;
     }
+}
+
+// Top-k and permutation in one launch (M * k <= kPermSmall): each block ranks
+// its tokens; the last block to finish (a ticket counter, reset by that block
+// for the next launch) permutes all entries.
+__global__ __launch_bounds__(256) void k_router_route(const float* __restrict__ logits, int nsplit,
+                                                      int M, int E, int k, int pad,
+                                                      int32_t* __restrict__ idx,
+                                                      float* __restrict__ gates,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm_token,
+                                                      int32_t* __restrict__ inv,
+                                                      int2* __restrict__ work,
+                                                      int32_t* __restrict__ work_count,
+                                                      uint32_t* __restrict__ ticket) {
+    __shared__ __attribute__((aligned(16))) float lg[4][kMaxExperts];
+    __shared__ float sv[4][16];
+    __shared__ bool last;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t < M) topk_token(logits, nsplit, M, E, k, t, idx, gates, lg, sv);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();                                   // this block's idx before the ticket
+        last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();                                       // every block's idx visible here
+    permute_block(idx, M * k, E, k, pad, offsets, perm_token, inv, work, work_count);
+    if (threadIdx.x == 0) *ticket = 0u;
 }
 
 // Larger batches (prefill chunks): per-chunk counts, one scan, per-chunk assignment.
@@ -169,22 +227,10 @@ __global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ co
         tot[e] = run;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = run;
-            run += round_up(tot[e], pad);
-        }
-        off[E] = run;
-    }
+    route_offsets(tot, E, pad, off, woff, offsets, perm_token, work, work_count);
     __syncthreads();
-    emit_work(off, E, woff, work, work_count);
-    __syncthreads();
-    for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        for (int j = off[e] + tot[e]; j < off[e + 1]; ++j) perm_token[j] = -1;
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
         for (int c = 0; c < n_chunks; ++c) base[(int64_t)c * E + e] += off[e];
-    }
 }
 
 __global__ __launch_bounds__(256) void k_moe_scatter(const int32_t* __restrict__ idx, int n,
@@ -216,11 +262,12 @@ hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, 
         return hipErrorInvalidValue;
     const int n = M * k;
     if (work.max_items < (n + kMoeRows - 1) / kMoeRows + E) return hipErrorInvalidValue;
-    k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
     if (n <= kPermSmall) {
-        k_moe_permute_small<<<1, 1024, 0, s>>>(idx, n, E, k, pad, offsets, perm_token, inv,
-                                                work.items, work.count);
+        k_router_route<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, pad, idx, gates,
+                                                   offsets, perm_token, inv, work.items,
+                                                   work.count, work.ticket);
     } else {
+        k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
         const int n_chunks = (n + kPermChunk - 1) / kPermChunk;
         k_moe_count<<<n_chunks, 256, 0, s>>>(idx, n, E, counts);
         k_moe_scan<<<1, 256, 0, s>>>(counts, n_chunks, E, pad, base, offsets, perm_token,

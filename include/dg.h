@@ -104,13 +104,13 @@ extern "C" {
 
 typedef struct dg_model_cfg {
     int32_t n_layers;      /* L */
-    int32_t d_model;       /* d, multiple of 32 for bf16/fp8 */
+    int32_t d_model;       /* d, multiple of 4, at most 4096 (bf16/fp8: multiple of 64) */
     int32_t n_q_heads;     /* Hq, multiple of n_kv_heads */
     int32_t n_kv_heads;    /* Hkv */
     int32_t head_dim;      /* D: 64 or 128 (bf16 path: 128) */
     int32_t n_experts;     /* E */
     int32_t top_k;         /* k <= E, k <= 16 */
-    int32_t d_ff;          /* F, expert hidden width, multiple of 32 for bf16/fp8 */
+    int32_t d_ff;          /* F, expert hidden width, multiple of 64 for bf16/fp8 */
     int32_t vocab;         /* V, multiple of 16 */
     int32_t canvas;        /* C, canvas length (<= 1024) */
     int64_t max_ctx;       /* KV rows per layer: >= P + K*C */
