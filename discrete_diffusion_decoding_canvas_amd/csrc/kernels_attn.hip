@@ -21,6 +21,8 @@
 //   parts so the softmax weights keep ~16 significant bits.
 // Softmax runs in fp32 in the log2 domain: the running max is kept on raw
 // scores and each exponent scale*log2(e)*(s - m) is one fma ahead of exp2.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace dg {
@@ -66,6 +68,8 @@ DG_DEV void dma16(const bf16_t* src, uint4* dst) {
 // 2^x with the hardware exponential; results below the smallest normal flush to
 // zero (a softmax weight under 2^-126 of the row maximum is dropped).
 DG_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kAttnLazy = 8.f;   // log2 units a score may exceed the reference max by
 
 // S^T block of 32 keys x 32 query rows (two query blocks): four independent
 // accumulation chains over the four 32-dimension steps.
@@ -167,7 +171,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
 #pragma unroll
         for (int s = 0; s < 4; ++s) qf[qb][s].u = *reinterpret_cast<const uint4*>(src + 32 * s);
     }
-    float m_run[2] = {-INFINITY, -INFINITY};
+    // Running reference maximum per query row, kept in log2 units (score * scale_log2).
+    // It is raised only when a score exceeds it by more than kAttnLazy (a factor 2^8):
+    // the weights 2^(score - ref) then stay below 2^8, the sums are the same in exact
+    // arithmetic, and most blocks need neither a cross-lane maximum nor a rescale.
+    float m_ref[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
     f32x4_t o[2][8];
 #pragma unroll
@@ -176,88 +184,104 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         for (int dt = 0; dt < 8; ++dt) o[qb][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
 
-    // Software pipeline per wave: iteration b issues the score MFMAs of block b + 1
-    // (matrix cores) ahead of the softmax of block b (VALU) and then the PV MFMAs of
-    // block b, so the two units overlap.
     int qlim[2];                        // causal: last key position each query row sees
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) qlim[qb] = (int)(q_pos0 + qm[qb]);
+    int wave_qlim = min(qlim[0], qlim[1]);   // causal: keys up to here need no per-row test
+#pragma unroll
+    for (int o2 = 1; o2 < 64; o2 <<= 1) wave_qlim = min(wave_qlim, __shfl_xor(wave_qlim, o2, 64));
+
+    // One block of 32 keys: softmax weights of the scores st (block key0), then the PV
+    // MFMAs.  MASK: keys past kend (and, causal, past each row's position) are -inf.
+    auto softmax_pv = [&](const f32x4_t (&st)[2][2], int key0, const AttnSlot& sl, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        auto score = [&](int qb, int kh, int j) {
+            const float v = st[qb][kh][j];
+            if (!MASK) return v;
+            const int key = key0 + 16 * kh + 4 * g + j;
+            bool ok = key < kend;
+            if (CAUSAL) ok = ok && key <= qlim[qb];
+            return ok ? v : -INFINITY;
+        };
+        float lm[2];
+        bool need = false;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            lm[qb] = -INFINITY;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lm[qb] = fmaxf(lm[qb], score(qb, kh, j));
+            need |= fmaf(lm[qb], scale_log2, -m_ref[qb]) > kAttnLazy;
+        }
+        if (__any(need)) {
+            // raise the reference of every row of this wave to its maximum so far
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float mx = lm[qb];
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float m_new = fmaxf(m_ref[qb], mx * scale_log2);
+                if (m_new > m_ref[qb]) {
+                    const float alpha = m_ref[qb] == -INFINITY ? 0.f : fast_exp2(m_ref[qb] - m_new);
+                    l_run[qb] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) o[qb][dt] *= alpha;
+                    m_ref[qb] = m_new;
+                }
+            }
+        }
+        AFrag pf[2], pl[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float nb = m_ref[qb] == -INFINITY ? 0.f : -m_ref[qb];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = fast_exp2(fmaf(score(qb, i >> 2, i & 3), scale_log2, nb));
+                psum += p;
+                const __bf16 hi = (__bf16)p;                 // round to nearest even
+                pf[qb].b[i] = hi;
+                pl[qb].b[i] = (__bf16)(p - (float)hi);
+            }
+            l_run[qb] += psum;
+        }
+        // O^T += V^T P^T, hi parts then lo parts
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            AFrag vf;
+            vf.u = sl.v[dt][lane];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.b, pf[qb].b, o[qb][dt], 0, 0, 0);
+                o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.b, pl[qb].b, o[qb][dt], 0, 0, 0);
+            }
+        }
+    };
+
+    // Software pipeline per wave: block b's softmax and PV MFMAs run after the score
+    // MFMAs of block b + 1 are issued, so the matrix cores and the VALU overlap.  The
+    // blocks that need no key mask (all but the last, and for the causal encoder all
+    // before this wave's diagonal) come first and run a loop of their own.
     f32x4_t st[2][2];
-    if (wave_active && n_blocks > 0) attn_scores(st, ring[0], qf, lane);
-    for (int b = 0; b < n_blocks; ++b) {
-        const int key0 = kbeg + 32 * b;
+    auto block = [&](int b, auto mask_tag) {
         if (wave_active) {
             f32x4_t sn[2][2];
             if (b + 1 < n_blocks) attn_scores(sn, ring[(b + 1) % kAttnRing], qf, lane);
-            AFrag pf[2], pl[2];
-            float alpha[2];
-            // keys past the end (and, causal, past each row's position) are masked; a
-            // block wholly inside the range skips the per-element test
-            const bool full = !CAUSAL && key0 + 32 <= kend;
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                float sc[8];
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float v = st[qb][kh][j];
-                        if (!full) {
-                            const int key = key0 + 16 * kh + 4 * g + j;
-                            bool ok = key < kend;
-                            if (CAUSAL) ok = ok && key <= qlim[qb];
-                            v = ok ? v : -INFINITY;
-                        }
-                        sc[4 * kh + j] = v;
-                        mx = fmaxf(mx, v);
-                    }
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                // running max kept on raw scores; exponents scale_log2 * (s - m) in one fma
-                const float m_new = fmaxf(m_run[qb], mx);
-                const float nb = (m_new == -INFINITY) ? 0.f : -m_new * scale_log2;
-                alpha[qb] = fast_exp2(fmaf(m_run[qb], scale_log2, nb));
-                float psum = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p = fast_exp2(fmaf(sc[i], scale_log2, nb));
-                    psum += p;
-                    const __bf16 hi = (__bf16)p;                 // round to nearest even
-                    pf[qb].b[i] = hi;
-                    pl[qb].b[i] = (__bf16)(p - (float)hi);
-                }
-                l_run[qb] = l_run[qb] * alpha[qb] + psum;
-                m_run[qb] = m_new;
-            }
-            // O^T = alpha O^T + V^T P^T, hi parts then lo parts.  The rescale is skipped
-            // when no lane's running max moved (alpha == 1 exactly).
-            if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) o[qb][dt] *= alpha[qb];
-            }
-            const AttnSlot& sl = ring[b % kAttnRing];
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                AFrag vf;
-                vf.u = sl.v[dt][lane];
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.b, pf[qb].b, o[qb][dt],
-                                                                        0, 0, 0);
-                    o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.b, pl[qb].b, o[qb][dt],
-                                                                        0, 0, 0);
-                }
-            }
+            softmax_pv(st, kbeg + 32 * b, ring[b % kAttnRing], mask_tag);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) st[qb][kh] = sn[qb][kh];
         }
         __syncthreads();
-    }
+    };
+    int n_full = (kend - kbeg) / 32;
+    if (CAUSAL) n_full = min(n_full, max(0, (wave_qlim - kbeg + 1) / 32));
+    if (wave_active && n_blocks > 0) attn_scores(st, ring[0], qf, lane);
+    int b = 0;
+    for (; b < n_full; ++b) block(b, std::false_type{});
+    for (; b < n_blocks; ++b) block(b, std::true_type{});
     if (!wave_active) return;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -286,7 +310,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
             for (int dt = 0; dt < 8; ++dt)
                 *reinterpret_cast<f32x4_t*>(dst + 16 * dt + 4 * g) = o[qb][dt];
             if (g == 0) {
-                part_ml[pr * 2 + 0] = m_run[qb] * scale_log2;   // log2 units, as the weights
+                part_ml[pr * 2 + 0] = m_ref[qb];   // log2 units, as the weights
                 part_ml[pr * 2 + 1] = l;
             }
         }
