@@ -296,6 +296,7 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
     ExpertWeights w = expert_weights(h, l);
     const int rows = (int)moe_rows_cap(n, h->k, h->E, moe_pad(h));
     const void* X1 = (h->edt == kFP8) ? (const void*)xin8 : xin;
+    K_TRY(launch_moe_gather(h->edt, X1, h->d, h->perm_token, h->offsets, h->E, rows, h->Xf, s));
     {
         ProfScope p(h, DG_PROF_MOE_GEMM1, s);
         K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows,

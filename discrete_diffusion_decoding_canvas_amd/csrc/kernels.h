@@ -104,8 +104,8 @@ hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const 
 //   bf16: X bf16 [*, d], W1 packed with interleaved gate/up groups, H bf16.
 //   fp8 : X e4m3 [*, d], W1 packed e4m3 + column scales (2F), H e4m3.
 //   f32 : X f32, Wg/Wu row-major [E][d][F], H f32.
-//   bf16/fp8 first gather x into Xf, MFMA A-operand fragment order
-//   ([row / 16][k-step][lane][16 bytes], padding rows zero), and write H in the
+//   bf16/fp8 read x from Xf (launch_moe_gather: MFMA A-operand fragment order,
+//   [row / 16][k-step][lane][16 bytes], padding rows zero) and write H in the
 //   same order for GEMM 2; rows padded to kMoePad, max_rows = moe_rows_cap.
 // GEMM 2: Y[entry, :d] = H[entry] Wd_e (float).
 struct ExpertWeights {
@@ -115,6 +115,10 @@ struct ExpertWeights {
     const float* s1;       // fp8 column scales of w1 [E][2F] (interleaved)
     const float* s2;       // fp8 column scales of w2 [E][d]
 };
+// GEMM 1's activation fragments: Xf = X[perm_token] in MFMA A-operand order
+// (bf16/fp8; padding rows zero).  No-op for f32.
+hipError_t launch_moe_gather(int dtype, const void* X, int d, const int32_t* perm_token,
+                             const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s);
 hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             const int32_t* perm_token, const int32_t* offsets, int E, int d,
                             int F, int max_rows, const MoeWork& work, void* Xf, void* H,

@@ -713,23 +713,34 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
     } else {
         const int kq = dtype == kFP8 ? 64 : 32;
         if ((2 * F) % kWideN || d % kq || F % kq || !Xf) return hipErrorInvalidValue;
-        const int KB = d / kq;
-        dim3 gg((KB + 3) / 4, (max_rows + kMoePad - 1) / kMoePad);   // tiles past offsets[E] exit
+        (void)X;
+        (void)perm_token;
         dim3 grid((2 * F) / kWideN, work.max_items);
-        if (dtype == kFP8) {
-            k_moe_gather_frag<true><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
-                                                       (uint8_t*)Xf);
+        if (dtype == kFP8)
             k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
                                                               offsets, work.items, work.count,
                                                               w.w1, w.s1, H);
-        } else {
-            k_moe_gather_frag<false><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets,
-                                                        E, (uint8_t*)Xf);
+        else
             k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
                                                                offsets, work.items, work.count,
                                                                w.w1, w.s1, H);
-        }
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_gather(int dtype, const void* X, int d, const int32_t* perm_token,
+                             const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s) {
+    if (max_rows <= 0 || dtype == kF32) return hipSuccess;
+    const int kq = dtype == kFP8 ? 64 : 32;
+    if (d % kq || !Xf) return hipErrorInvalidValue;
+    const int KB = d / kq;
+    dim3 gg((KB + 3) / 4, (max_rows + kMoePad - 1) / kMoePad);   // tiles past offsets[E] exit
+    if (dtype == kFP8)
+        k_moe_gather_frag<true><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
+                                                   (uint8_t*)Xf);
+    else
+        k_moe_gather_frag<false><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
+                                                    (uint8_t*)Xf);
     return hipGetLastError();
 }
 
