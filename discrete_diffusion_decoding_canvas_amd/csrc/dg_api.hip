@@ -94,6 +94,7 @@ struct dg_handle {
     int32_t* perm_token = nullptr;
     int32_t* inv = nullptr;
     void* Xf = nullptr;      // expert GEMM 1 activations in fragment order (bf16/fp8)
+    void* Af = nullptr;      // dense-projection activations in fragment order (bf16)
     void* H = nullptr;
     float* Y = nullptr;
     int2* work_items = nullptr;
@@ -317,8 +318,13 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
                      hipStream_t s, bool capture = false) {
     {
         ProfScope p(h, DG_PROF_DENSE, s);
-        K_TRY(launch_gemm(h->act, kEpiStoreF32, h->a, h->d, n, h->wqkv[l], h->d, h->qkv_n, h->qkv,
-                          h->qkv_n, s));
+        if (h->act == kBF16) {   // Af: a in fragment order, from the norm that wrote a
+            K_TRY(launch_gemm_frag(kEpiStoreF32, h->Af, n, h->wqkv[l], h->d, h->qkv_n, h->qkv,
+                                   h->qkv_n, s));
+        } else {
+            K_TRY(launch_gemm(h->act, kEpiStoreF32, h->a, h->d, n, h->wqkv[l], h->d, h->qkv_n,
+                              h->qkv, h->qkv_n, s));
+        }
     }
     K_TRY(launch_rope_scatter(h->act, h->qkv, n, h->Hq, h->Hkv, h->D, pos0, h->cos_t, h->sin_t,
                               h->q, h->klayer(l), h->vlayer(l), h->kv_rows, s));
@@ -328,6 +334,7 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
     aa.k = h->klayer(l);
     aa.v = h->vlayer(l);
     aa.o = h->attn_o;
+    aa.of = h->act == kBF16 ? h->Af : nullptr;
     aa.Hq = h->Hq;
     aa.Hkv = h->Hkv;
     aa.M = n;
@@ -352,25 +359,30 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
     }
     {
         ProfScope p(h, DG_PROF_DENSE, s);
-        K_TRY(launch_gemm(h->act, kEpiAddF32, h->attn_o, h->Hq * h->D, n, h->wo[l], h->Hq * h->D,
-                          h->d, h->x, h->d, s));
+        if (h->act == kBF16) {   // Af: the attention output in fragment order
+            K_TRY(launch_gemm_frag(kEpiAddF32, h->Af, n, h->wo[l], h->Hq * h->D, h->d, h->x, h->d, s));
+        } else {
+            K_TRY(launch_gemm(h->act, kEpiAddF32, h->attn_o, h->Hq * h->D, n, h->wo[l],
+                              h->Hq * h->D, h->d, h->x, h->d, s));
+        }
     }
     K_TRY(launch_rmsnorm(h->act, h->x, n, h->d, h->cfg.rms_eps, h->a,
-                         h->edt == kFP8 ? h->a8 : nullptr, s));
+                         h->edt == kFP8 ? h->a8 : nullptr, nullptr, s));
     DG_TRY(run_moe(h, l, n, h->a, h->a8, s));
     if (capture && h->cap(DG_CAP_ROUTER_LOGITS))
         HIP_TRY(hipMemcpyAsync(h->cap_rlog + (size_t)l * n * h->E, h->rlog, (size_t)n * h->E * 4,
                                hipMemcpyDeviceToDevice, s));
     // residual add, then the next norm (next layer's input, or the final norm)
     K_TRY(launch_moe_combine(h->act, 0, h->Y, n, h->d, h->k, h->gates, h->inv, h->x,
-                             h->cfg.rms_eps, h->a, h->edt == kFP8 ? h->a8 : nullptr, nullptr, s));
+                             h->cfg.rms_eps, h->a, h->edt == kFP8 ? h->a8 : nullptr, h->Af,
+                             nullptr, s));
     return DG_OK;
 }
 
 // Causal encoder over n tokens at positions pos0.. (prefill chunk or commit).
 static int encode(dg_handle* h, const int32_t* tokens, int n, int64_t pos0, hipStream_t s) {
     K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, tokens, h->embed, n, h->d,
-                               h->cfg.rms_eps, h->x, h->a, s));
+                               h->cfg.rms_eps, h->x, h->a, h->Af, s));
     for (int l = 0; l < h->L; ++l)
         DG_TRY(run_layer(h, l, n, pos0, true, l == h->L - 1, s));
     return DG_OK;
@@ -485,6 +497,8 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->route_ticket, 1));
     if (hipMemset(h->route_ticket, 0, 4) != hipSuccess) return cleanup(fail(DG_EHIP, "ticket reset failed"));
     if (h->edt != kF32) A_TRY(h->alloc(&h->Xf, rows * d * esz));
+    if (h->act == kBF16)
+        A_TRY(h->alloc(&h->Af, (T + 15) / 16 * 16 * std::max<size_t>(d, (size_t)h->Hq * h->D) * 2));
     A_TRY(h->alloc(&h->H, rows * F * esz));
     A_TRY(h->allocT(&h->Y, rows * d));
     const int ns = lm_head_slices(h->act, h->V);
@@ -783,7 +797,7 @@ int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int
     hipStream_t s = (hipStream_t)stream;
     const int C = h->C;
     K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, C, h->d,
-                               h->cfg.rms_eps, h->x, h->a, s));
+                               h->cfg.rms_eps, h->x, h->a, h->Af, s));
     const uint32_t per_layer = DG_CAP_ROUTING | DG_CAP_HIDDEN | DG_CAP_ATTN | DG_CAP_ROUTER_LOGITS;
     if (h->use_graphs && !h->prof && !(h->cap_mask & per_layer)) {
         DG_TRY(run_layers_graph(h, s));
@@ -1036,7 +1050,7 @@ int dg_moe_layer(dg_handle* h, int32_t layer, const void* d_x, int32_t n_tokens,
     }
     DG_TRY(run_moe(h, layer, n_tokens, d_x, x8, s));
     K_TRY(launch_moe_combine(h->act, 1, h->Y, n_tokens, h->d, h->k, h->gates, h->inv, nullptr,
-                             0.f, nullptr, nullptr, d_y, s));
+                             0.f, nullptr, nullptr, nullptr, d_y, s));
     if (d_idx) HIP_TRY(hipMemcpyAsync(d_idx, h->idx, (size_t)n_tokens * h->k * 4, hipMemcpyDeviceToDevice, s));
     if (d_gates) HIP_TRY(hipMemcpyAsync(d_gates, h->gates, (size_t)n_tokens * h->k * 4, hipMemcpyDeviceToDevice, s));
     return DG_OK;

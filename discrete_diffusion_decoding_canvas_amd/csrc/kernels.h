@@ -29,6 +29,22 @@ struct MoeWork {
     uint32_t* ticket;  // zero-initialised block counter of the fused top-k + permutation
 };
 
+// Byte offset of element (row, col) of a [rows][K] matrix stored in MFMA
+// A-operand fragment order: [row / 16][k-step][lane = 16 g + row % 16][16 bytes].
+// bf16: k-step of 32 columns, lane group g = (col % 32) / 8, element col % 8.
+// e4m3: k-step of 64 columns, the lane's 16 bytes hold columns 8 g..8 g+7 (low
+// half) and 32 + 8 g..32 + 8 g + 7 (high half) of the k-step.  A 16-row x k-step
+// fragment set is one contiguous 1 KiB, so an MFMA operand load is one
+// coalesced 16-byte load per lane.
+template <bool FP8>
+DG_DEV size_t frag_offset(int64_t row, int col, int K) {
+    const int KB = FP8 ? (K >> 6) : (K >> 5);
+    const int kb = FP8 ? (col >> 6) : (col >> 5);
+    const int g = (col & 31) >> 3;
+    const int byte = FP8 ? (8 * ((col >> 5) & 1) + (col & 7)) : 2 * (col & 7);
+    return ((size_t)((row >> 4) * KB + kb) * 64 + 16 * g + (row & 15)) * 16 + byte;
+}
+
 // Transposed, key-permuted V cache: Vt[h][dim][slot], rows padded to a multiple
 // of 32.  Within each 32-key block, key 16*hi + 4*g + j sits at slot 8*g + 4*hi + j,
 // so one 16-byte load gives a lane exactly the 8 keys its MFMA operand needs.
@@ -49,10 +65,13 @@ struct HeadPartials {
 };
 
 // ---------------------------------------------------------------- misc
+// The row-normalising kernels also write the bf16 rows in fragment order to af
+// (frag_offset, K = d) when af is given (bf16 only).
 hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, const void* E,
-                                int C, int d, float eps, float* x, void* a, hipStream_t s);
+                                int C, int d, float eps, float* x, void* a, void* af,
+                                hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
-                          uint8_t* a8, hipStream_t s);
+                          uint8_t* a8, void* af, hipStream_t s);
 hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int Hkv, int D,
                                int64_t pos0, const float* cos_t, const float* sin_t, void* q,
                                void* kc, void* vc, int64_t kv_rows, hipStream_t s);
@@ -71,7 +90,7 @@ hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, 
                                  hipStream_t s);
 hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
                               const float* gates, const int32_t* inv, float* x, float eps,
-                              void* a, uint8_t* a8, void* out, hipStream_t s);
+                              void* a, uint8_t* a8, void* af, void* out, hipStream_t s);
 hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint64_t seed,
                               int k_blk, hipStream_t s);
 hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, float* st_m,
@@ -98,6 +117,11 @@ constexpr int kEpiAddF32 = 1;     // C[m, n] += acc (residual add, single writer
 // only): partial sums over ksplit K ranges at C + z * M * ldc, z < ksplit.
 hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const void* B, int K,
                        int N, float* C, int ldc, hipStream_t s, int ksplit = 1);
+// The same product (bf16) with A in MFMA A-fragment order ([row/16][K/32][64][16 B],
+// rows padded to 16), as written by launch_pack_afrag or by the producing kernel.
+hipError_t launch_gemm_frag(int epi, const void* Af, int M, const void* B, int K, int N, float* C,
+                            int ldc, hipStream_t s, int ksplit = 1);
+hipError_t launch_pack_afrag(const void* A, int M, int K, void* Af, hipStream_t s);
 
 // Expert GEMMs over the permuted entries (offsets[e]..offsets[e+1] belong to expert e).
 // GEMM 1: H[entry, :F] = silu(x Wg_e) * (x Wu_e), x = X[perm_token[entry]].
@@ -142,6 +166,7 @@ struct AttnArgs {
     const void* k;
     const void* v;
     void* o;
+    void* of = nullptr;    // optional bf16 copy of O in fragment order (frag_offset, K = Hq D)
     int Hq, Hkv, M, S, D;
     int64_t kv_rows;       // row capacity per head of K (and of f32 V)
     int64_t v_rows;        // row capacity per head of the bf16 transposed V (multiple of 32)

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt,
     int Hq, int Hkv, int M, int S, int64_t k_rows, int64_t v_rows, float scale_log2,
     int64_t q_pos0, int keys_per_split, int n_splits, bf16_t* __restrict__ O,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    uint8_t* __restrict__ Of, float* __restrict__ part_o, float* __restrict__ part_ml) {
     __shared__ AttnSlot ring[kAttnRing];
     const int G = Hq / Hkv;
     const int GM = G * M;
@@ -302,6 +302,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                 pk.y = (uint32_t)f32_to_bf16(o[qb][dt][2] * inv) |
                        ((uint32_t)f32_to_bf16(o[qb][dt][3] * inv) << 16);
                 *reinterpret_cast<uint2*>(dst + 16 * dt + 4 * g) = pk;
+                if (Of)
+                    *reinterpret_cast<uint2*>(Of + frag_offset<false>(q, h * kAttnD + 16 * dt + 4 * g,
+                                                                      Hq * kAttnD)) = pk;
             }
         } else {
             const int64_t pr = ((int64_t)split * Hq + h) * M + q;
@@ -323,7 +326,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int n_splits, int Hq, int M,
-                                                      T* __restrict__ O) {
+                                                      T* __restrict__ O, uint8_t* __restrict__ Of) {
     const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (wid >= M * Hq) return;
@@ -349,8 +352,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
         n1 += ws * v.y;
     }
     T* dst = O + (int64_t)q * Hq * kAttnD + (int64_t)h * kAttnD + 2 * lane;
-    dst[0] = from_f32<T>(n0 / den);
-    dst[1] = from_f32<T>(n1 / den);
+    const T o0 = from_f32<T>(n0 / den), o1 = from_f32<T>(n1 / den);
+    dst[0] = o0;
+    dst[1] = o1;
+    if (Of) {
+        T* f = reinterpret_cast<T*>(Of + frag_offset<false>(q, h * kAttnD + 2 * lane, Hq * kAttnD));
+        f[0] = o0;
+        f[1] = o1;
+    }
 }
 
 // f32 attention (VALU): one thread per (head, query), online softmax over keys.
@@ -446,15 +455,15 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
         k_attn_bf16<true><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                (const bf16_t*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                a.kv_rows, a.v_rows, sl2, a.q_pos0, kps, n,
-                                               (bf16_t*)a.o, a.part_o, pml);
+                                               (bf16_t*)a.o, (uint8_t*)a.of, a.part_o, pml);
     else
         k_attn_bf16<false><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                 (const bf16_t*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                 a.kv_rows, a.v_rows, sl2, a.q_pos0, kps, n,
-                                                (bf16_t*)a.o, a.part_o, pml);
+                                                (bf16_t*)a.o, (uint8_t*)a.of, a.part_o, pml);
     if (n > 1)
         k_attn_combine<bf16_t><<<(a.M * a.Hq + 3) / 4, 256, 0, s>>>(a.part_o, pml, n, a.Hq, a.M,
-                                                                    (bf16_t*)a.o);
+                                                                    (bf16_t*)a.o, (uint8_t*)a.of);
     return hipGetLastError();
 }
 

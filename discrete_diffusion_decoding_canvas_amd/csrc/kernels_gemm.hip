@@ -191,6 +191,120 @@ __global__ __launch_bounds__(kThreads) void k_gemm_bf16(const bf16_t* __restrict
     }
 }
 
+// ------------------------------------------------------------------ dense bf16 GEMM, A in fragment order
+// A given in MFMA A-fragment order (see frag_offset: [row/16][k-step][lane][16 B]),
+// so every activation load is a contiguous 1 KiB per wave.  Tile DMT row tiles of
+// 16 x 64 columns; the kDenseWaves waves split K, keep kDensePrefetch k-steps of operands
+// in flight in registers and add their partial tiles in LDS in wave order.
+// grid (N / 64, ceil(M / (16 DMT)), ksplit); ksplit > 1 stores partial sums at
+// C + z * M * ldc (store epilogue only).
+#ifndef DG_DENSE_WAVES
+#define DG_DENSE_WAVES 8
+#endif
+constexpr int kDenseMT = 4;
+constexpr int kDensePrefetch = 4;
+constexpr int kDenseWaves = DG_DENSE_WAVES;
+constexpr int kDenseThreads = 64 * kDenseWaves;
+
+struct DenseStage {
+    Frag16 a[kDenseMT];
+    Frag16 b[kNT];
+};
+
+template <int EPI>
+__global__ __launch_bounds__(kDenseThreads) void k_dense_frag(const uint8_t* __restrict__ Af, int M,
+                                                         const bf16_t* __restrict__ Bp, int K,
+                                                         int N, float* __restrict__ C, int ldc) {
+    __shared__ float red[kDenseWaves][16 * kDenseMT][kTileN];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n0 = blockIdx.x * kTileN;
+    const int m0 = blockIdx.y * 16 * kDenseMT;
+    const int KB = K >> 5;
+    const int tiles = (M + 15) >> 4;
+    const uint8_t* ap[kDenseMT];
+#pragma unroll
+    for (int mt = 0; mt < kDenseMT; ++mt) {
+        const int t = min((m0 >> 4) + mt, tiles - 1);   // tiles past M repeat the last one
+        ap[mt] = Af + ((size_t)t * KB * 64 + lane) * 16;
+    }
+    const size_t gstride = (size_t)KB * 1024;
+    const uint8_t* bg = (const uint8_t*)(Bp + (size_t)(n0 >> 4) * KB * 512) + (size_t)lane * 16;
+    int zb, ze, kb0, kb1;
+    split_range(KB, gridDim.z, blockIdx.z, zb, ze);
+    split_range(ze - zb, kDenseWaves, w, kb0, kb1);
+    kb0 += zb;
+    kb1 += zb;
+    f32x4_t acc[kDenseMT][kNT];
+#pragma unroll
+    for (int mt = 0; mt < kDenseMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto load = [&](DenseStage& st, int kb) {
+#pragma unroll
+        for (int mt = 0; mt < kDenseMT; ++mt) st.a[mt].u = ld16(ap[mt] + (size_t)kb * 1024);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) st.b[nt].u = ld16(bg + nt * gstride + (size_t)kb * 1024);
+    };
+    DenseStage buf[kDensePrefetch];
+#pragma unroll
+    for (int i = 0; i < kDensePrefetch - 1; ++i)
+        if (kb0 + i < kb1) load(buf[i], kb0 + i);
+    for (int kb = kb0; kb < kb1; kb += kDensePrefetch) {
+#pragma unroll
+        for (int u = 0; u < kDensePrefetch; ++u) {
+            const int k = kb + u;
+            if (k < kb1) {
+                const int kn = k + kDensePrefetch - 1;
+                if (kn < kb1) load(buf[(u + kDensePrefetch - 1) % kDensePrefetch], kn);
+                const DenseStage& st = buf[u];
+#pragma unroll
+                for (int mt = 0; mt < kDenseMT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.a[mt].b, st.b[nt].b,
+                                                                              acc[mt][nt], 0, 0, 0);
+            }
+        }
+    }
+    // partial tiles of the four waves, added in wave order
+#pragma unroll
+    for (int mt = 0; mt < kDenseMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                red[w][16 * mt + 4 * (lane >> 4) + j][16 * nt + (lane & 15)] = acc[mt][nt][j];
+    __syncthreads();
+    float* Cz = C + (size_t)blockIdx.z * M * ldc;
+    for (int e = threadIdx.x; e < 16 * kDenseMT * kTileN; e += kDenseThreads) {
+        const int r = e >> 6, c = e & 63;
+        const int m = m0 + r, n = n0 + c;
+        if (m >= M) continue;
+        float v = red[0][r][c];
+#pragma unroll
+        for (int i = 1; i < kDenseWaves; ++i) v += red[i][r][c];
+        if (EPI == kEpiStoreF32) Cz[(size_t)m * ldc + n] = v;
+        else Cz[(size_t)m * ldc + n] += v;
+    }
+}
+
+// Natural row-major bf16 A [M][K] -> fragment order (see frag_offset), rows padded
+// to a multiple of 16 with zeros.
+__global__ void k_pack_afrag(const bf16_t* __restrict__ A, int M, int K, uint8_t* __restrict__ Af) {
+    const int KB = K >> 5;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (tile, kb, lane)
+    const int64_t total = (int64_t)((M + 15) >> 4) * KB * 64;
+    if (idx >= total) return;
+    const int lane = (int)(idx & 63);
+    const int64_t tk = idx >> 6;
+    const int kb = (int)(tk % KB);
+    const int64_t t = tk / KB;
+    const int64_t row = t * 16 + (lane & 15);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < M) v = *reinterpret_cast<const uint4*>(A + row * K + kb * 32 + 8 * (lane >> 4));
+    *reinterpret_cast<uint4*>(Af + idx * 16) = v;
+}
+
 // ------------------------------------------------------------------ dense f32 GEMM (VALU)
 // 64x64 tile, 256 threads x (4x4) outputs, K steps of 16 through LDS.
 template <int EPI>
@@ -506,20 +620,6 @@ DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
-// Byte offset of element (row, col) of a [rows][K] matrix in MFMA A-fragment
-// order: [row / 16][k-step][lane = 16 g + row % 16][16 bytes].  bf16: k-step of
-// 32 columns, lane group g = (col % 32) / 8, element col % 8.  e4m3: k-step of
-// 64 columns, the lane's 16 bytes hold columns 8 g..8 g+7 (low half) and
-// 32 + 8 g..32 + 8 g + 7 (high half) of the k-step.
-template <bool FP8>
-DG_DEV size_t frag_offset(int64_t row, int col, int K) {
-    const int KB = FP8 ? (K >> 6) : (K >> 5);
-    const int kb = FP8 ? (col >> 6) : (col >> 5);
-    const int g = (col & 31) >> 3;
-    const int byte = FP8 ? (8 * ((col >> 5) & 1) + (col & 7)) : 2 * (col & 7);
-    return ((size_t)((row >> 4) * KB + kb) * 64 + 16 * g + (row & 15)) * 16 + byte;
-}
-
 template <bool FP8, int GEMM>
 __global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(   // <= 128 VGPRs
     const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
@@ -674,6 +774,29 @@ __global__ void k_moe2_f32(const float* __restrict__ H, int d, int F,
 }
 
 // ================================================================== launchers
+hipError_t launch_pack_afrag(const void* A, int M, int K, void* Af, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (K & 31) return hipErrorInvalidValue;
+    const int64_t total = (int64_t)((M + 15) >> 4) * (K >> 5) * 64;
+    k_pack_afrag<<<(unsigned)((total + 255) / 256), 256, 0, s>>>((const bf16_t*)A, M, K, (uint8_t*)Af);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_frag(int epi, const void* Af, int M, const void* B, int K, int N, float* C,
+                            int ldc, hipStream_t s, int ksplit) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if ((K & 31) || (N % kTileN) || ksplit < 1 || (ksplit > 1 && epi != kEpiStoreF32))
+        return hipErrorInvalidValue;
+    dim3 grid(N / kTileN, (M + 16 * kDenseMT - 1) / (16 * kDenseMT), ksplit);
+    if (epi == kEpiStoreF32)
+        k_dense_frag<kEpiStoreF32><<<grid, kDenseThreads, 0, s>>>((const uint8_t*)Af, M, (const bf16_t*)B,
+                                                              K, N, C, ldc);
+    else
+        k_dense_frag<kEpiAddF32><<<grid, kDenseThreads, 0, s>>>((const uint8_t*)Af, M, (const bf16_t*)B,
+                                                            K, N, C, ldc);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const void* B, int K,
                        int N, float* C, int ldc, hipStream_t s, int ksplit) {
     if (M <= 0 || N <= 0) return hipSuccess;

@@ -36,7 +36,7 @@ template <typename T, bool PACKED>
 __global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict__ tokens,
                                                        const T* __restrict__ E, int d,
                                                        float eps, float* __restrict__ x,
-                                                       T* __restrict__ a) {
+                                                       T* __restrict__ a, uint8_t* __restrict__ af) {
     __shared__ float red[4];
     const int i = blockIdx.x;
     const int64_t v = tokens[i];
@@ -56,7 +56,9 @@ __global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict
         const int c = threadIdx.x + 256 * j;
         if (c < d) {
             x[(int64_t)i * d + c] = xs[j];
-            a[(int64_t)i * d + c] = from_f32<T>(xs[j] * r);
+            const T av = from_f32<T>(xs[j] * r);
+            a[(int64_t)i * d + c] = av;
+            if (af) *reinterpret_cast<T*>(af + frag_offset<false>(i, c, d)) = av;
         }
     }
 }
@@ -81,16 +83,18 @@ DG_DEV void store4(T* dst, float4 v) {
     }
 }
 
-// Normalised row (xs scaled by r) to a (as T) and a8 (e4m3 of the rounded a).
+// Normalised row `row` (xs scaled by r) to a (as T), a8 (e4m3 of the rounded a) and
+// af (the bf16 row in fragment order, frag_offset with K = 4 d4).
 template <typename T>
 DG_DEV void store_norm(const float4 (&xs)[kRowPasses], float r, int d4, T* __restrict__ a,
-                       uint8_t* __restrict__ a8) {
+                       uint8_t* __restrict__ a8, uint8_t* __restrict__ af, int64_t row) {
 #pragma unroll
     for (int p = 0; p < kRowPasses; ++p) {
         const int c4 = threadIdx.x + 256 * p;
         if (c4 >= d4) break;
         const float4 v = make_float4(xs[p].x * r, xs[p].y * r, xs[p].z * r, xs[p].w * r);
         store4<T>(a + 4 * (int64_t)c4, v);
+        if (af) store4<T>(reinterpret_cast<T*>(af + frag_offset<false>(row, 4 * c4, 4 * d4)), v);
         if (a8) {
             uchar4 q;
             q.x = (uint8_t)f32_to_e4m3(to_f32<T>(from_f32<T>(v.x)));
@@ -104,7 +108,8 @@ DG_DEV void store_norm(const float4 (&xs)[kRowPasses], float r, int d4, T* __res
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int d, float eps,
-                                                 T* __restrict__ a, uint8_t* __restrict__ a8) {
+                                                 T* __restrict__ a, uint8_t* __restrict__ a8,
+                                                 uint8_t* __restrict__ af) {
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
     const int d4 = d >> 2;
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
         ss += xs[p].x * xs[p].x + xs[p].y * xs[p].y + xs[p].z * xs[p].z + xs[p].w * xs[p].w;
     }
     const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-    store_norm<T>(xs, r, d4, a + row * d, a8 ? a8 + row * d : nullptr);
+    store_norm<T>(xs, r, d4, a + row * d, a8 ? a8 + row * d : nullptr, af, row);
 }
 
 // ------------------------------------------------------------------ RoPE + scatter
@@ -227,6 +232,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y
                                                      const int32_t* __restrict__ inv,
                                                      float* __restrict__ x, float eps,
                                                      T* __restrict__ a, uint8_t* __restrict__ a8,
+                                                     uint8_t* __restrict__ af,
                                                      T* __restrict__ out) {
     __shared__ float red[4];
     const int64_t t = blockIdx.x;
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y
     }
     if (MODE == 0 && a != nullptr) {
         const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-        store_norm<T>(xs, r, d4, a + t * d, a8 ? a8 + t * d : nullptr);
+        store_norm<T>(xs, r, d4, a + t * d, a8 ? a8 + t * d : nullptr, af, t);
     }
 }
 
@@ -437,27 +443,28 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, int64_t n) {
 #define LAUNCH_CHECK() return hipGetLastError()
 
 hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, const void* E,
-                                int C, int d, float eps, float* x, void* a, hipStream_t s) {
+                                int C, int d, float eps, float* x, void* a, void* af,
+                                hipStream_t s) {
     if (dtype == kF32)
         k_embed_rmsnorm<float, false><<<C, 256, 0, s>>>(tokens, (const float*)E, d, eps, x,
-                                                        (float*)a);
+                                                        (float*)a, nullptr);
     else if (packed)
         k_embed_rmsnorm<bf16_t, true><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, d, eps, x,
-                                                        (bf16_t*)a);
+                                                        (bf16_t*)a, (uint8_t*)af);
     else
         k_embed_rmsnorm<bf16_t, false><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, d, eps, x,
-                                                         (bf16_t*)a);
+                                                         (bf16_t*)a, (uint8_t*)af);
     LAUNCH_CHECK();
 }
 
 hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
-                          uint8_t* a8, hipStream_t s) {
+                          uint8_t* a8, void* af, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if ((d & 3) || d > 1024 * kRowPasses) return hipErrorInvalidValue;
     if (dtype == kF32)
-        k_rmsnorm<float><<<M, 256, 0, s>>>(x, d, eps, (float*)a, a8);
+        k_rmsnorm<float><<<M, 256, 0, s>>>(x, d, eps, (float*)a, a8, nullptr);
     else
-        k_rmsnorm<bf16_t><<<M, 256, 0, s>>>(x, d, eps, (bf16_t*)a, a8);
+        k_rmsnorm<bf16_t><<<M, 256, 0, s>>>(x, d, eps, (bf16_t*)a, a8, (uint8_t*)af);
     LAUNCH_CHECK();
 }
 
@@ -522,30 +529,33 @@ hipError_t launch_write_kv(int dtype, bool vpacked, void* cache, int Hkv, int D,
 
 template <typename T, int MODE, int KMAX>
 static void combine_k(const float* Y, int M, int d, int k, const float* gates, const int32_t* inv,
-                      float* x, float eps, void* a, uint8_t* a8, void* out, hipStream_t s) {
-    k_moe_combine<T, MODE, KMAX><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, (T*)a, a8, (T*)out);
+                      float* x, float eps, void* a, uint8_t* a8, void* af, void* out,
+                      hipStream_t s) {
+    k_moe_combine<T, MODE, KMAX><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, (T*)a, a8,
+                                                   (uint8_t*)af, (T*)out);
 }
 
 template <typename T, int MODE>
 static void combine_m(const float* Y, int M, int d, int k, const float* gates, const int32_t* inv,
-                      float* x, float eps, void* a, uint8_t* a8, void* out, hipStream_t s) {
-    if (k <= 2) combine_k<T, MODE, 2>(Y, M, d, k, gates, inv, x, eps, a, a8, out, s);
-    else if (k <= 4) combine_k<T, MODE, 4>(Y, M, d, k, gates, inv, x, eps, a, a8, out, s);
-    else if (k <= 8) combine_k<T, MODE, 8>(Y, M, d, k, gates, inv, x, eps, a, a8, out, s);
-    else combine_k<T, MODE, kMaxTopK>(Y, M, d, k, gates, inv, x, eps, a, a8, out, s);
+                      float* x, float eps, void* a, uint8_t* a8, void* af, void* out,
+                      hipStream_t s) {
+    if (k <= 2) combine_k<T, MODE, 2>(Y, M, d, k, gates, inv, x, eps, a, a8, af, out, s);
+    else if (k <= 4) combine_k<T, MODE, 4>(Y, M, d, k, gates, inv, x, eps, a, a8, af, out, s);
+    else if (k <= 8) combine_k<T, MODE, 8>(Y, M, d, k, gates, inv, x, eps, a, a8, af, out, s);
+    else combine_k<T, MODE, kMaxTopK>(Y, M, d, k, gates, inv, x, eps, a, a8, af, out, s);
 }
 
 hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
                               const float* gates, const int32_t* inv, float* x, float eps,
-                              void* a, uint8_t* a8, void* out, hipStream_t s) {
+                              void* a, uint8_t* a8, void* af, void* out, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if ((d & 3) || d > 1024 * kRowPasses || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
     if (dtype == kF32) {
-        if (mode == 0) combine_m<float, 0>(Y, M, d, k, gates, inv, x, eps, a, a8, nullptr, s);
-        else combine_m<float, 1>(Y, M, d, k, gates, inv, x, eps, nullptr, nullptr, out, s);
+        if (mode == 0) combine_m<float, 0>(Y, M, d, k, gates, inv, x, eps, a, a8, nullptr, nullptr, s);
+        else combine_m<float, 1>(Y, M, d, k, gates, inv, x, eps, nullptr, nullptr, nullptr, out, s);
     } else {
-        if (mode == 0) combine_m<bf16_t, 0>(Y, M, d, k, gates, inv, x, eps, a, a8, nullptr, s);
-        else combine_m<bf16_t, 1>(Y, M, d, k, gates, inv, x, eps, nullptr, nullptr, out, s);
+        if (mode == 0) combine_m<bf16_t, 0>(Y, M, d, k, gates, inv, x, eps, a, a8, af, nullptr, s);
+        else combine_m<bf16_t, 1>(Y, M, d, k, gates, inv, x, eps, nullptr, nullptr, nullptr, out, s);
     }
     LAUNCH_CHECK();
 }
