@@ -135,17 +135,17 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
 // (32 consecutive positions of one dimension are one 64-byte run).
 constexpr int kRopeTokens = 32;
 
-template <typename T, bool VPACKED>
+template <typename T, bool VPACKED, int D>
 __global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ qkv, int M, int Hq,
-                                                      int Hkv, int D, int64_t pos0,
+                                                      int Hkv, int64_t pos0,
                                                       const float* __restrict__ cos_t,
                                                       const float* __restrict__ sin_t,
                                                       T* __restrict__ q, T* __restrict__ kc,
                                                       T* __restrict__ vc, int64_t kv_rows) {
-    __shared__ float vt[kRopeTokens][129];   // D <= 128
+    __shared__ float vt[kRopeTokens][D + 1];
     const int m0 = blockIdx.x * kRopeTokens;
     const int head = blockIdx.y;             // 0..Hq-1 queries, Hq..Hq+Hkv-1 keys, then values
-    const int half = D >> 1;
+    constexpr int half = D >> 1;
     const int64_t ld = (int64_t)(Hq + 2 * Hkv) * D;
     const int nt = min(kRopeTokens, M - m0);
     if (head < Hq + Hkv || !VPACKED) {
@@ -468,20 +468,26 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, vo
     LAUNCH_CHECK();
 }
 
+template <typename T, bool VPACKED, int D>
+static void rope_d(const float* qkv, int M, int Hq, int Hkv, int64_t pos0, const float* cos_t,
+                   const float* sin_t, void* q, void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
+    dim3 grid((M + kRopeTokens - 1) / kRopeTokens, Hq + 2 * Hkv);
+    k_rope_scatter<T, VPACKED, D><<<grid, 256, 0, s>>>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, (T*)q,
+                                                       (T*)kc, (T*)vc, kv_rows);
+}
+
 hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int Hkv, int D,
                                int64_t pos0, const float* cos_t, const float* sin_t, void* q,
                                void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    if (D > 128) return hipErrorInvalidValue;
-    dim3 grid((M + kRopeTokens - 1) / kRopeTokens, Hq + 2 * Hkv);
-    const int threads = 256;
-    if (dtype == kF32)
-        k_rope_scatter<float, false><<<grid, threads, 0, s>>>(
-            qkv, M, Hq, Hkv, D, pos0, cos_t, sin_t, (float*)q, (float*)kc, (float*)vc, kv_rows);
-    else
-        k_rope_scatter<bf16_t, true><<<grid, threads, 0, s>>>(
-            qkv, M, Hq, Hkv, D, pos0, cos_t, sin_t, (bf16_t*)q, (bf16_t*)kc, (bf16_t*)vc,
-            kv_rows);
+    if (dtype == kF32) {
+        if (D == 64) rope_d<float, false, 64>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
+        else if (D == 128) rope_d<float, false, 128>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
+        else return hipErrorInvalidValue;
+    } else {
+        if (D != 128) return hipErrorInvalidValue;
+        rope_d<bf16_t, true, 128>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
+    }
     LAUNCH_CHECK();
 }
 

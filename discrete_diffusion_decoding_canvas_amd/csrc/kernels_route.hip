@@ -5,11 +5,9 @@
 // softmax over the experts, top-k with gates renormalised over the k chosen,
 // then the (token, slot) entries grouped by expert for the grouped GEMMs.
 //
-// Top-k: one wave per token.  The logits go to LDS and every lane ranks its
-// own logits against all of them (rank = number of larger logits plus equal
-// ones with a lower expert id), so the k winners land at their rank in one
-// pass with no serial reduction chain.  Router logits may arrive as several
-// split-K partial sums; they are added here in a fixed order.
+// Top-k: one wave per token, k rounds of a DPP wave maximum (the ranking:
+// logit descending, ties to the lower expert id).  Router logits may arrive as
+// several split-K partial sums; they are added here in a fixed order.
 //
 // Permutation: per-expert counts with LDS integer atomics, one exclusive scan
 // (of the counts rounded up to the row padding), then each entry takes the next
@@ -22,48 +20,80 @@ namespace dg {
 
 constexpr int kMaxExperts = 256;
 
-// Top-k of token t by wave w of the block (no block-level synchronisation:
-// only wave-level LDS use).
+// One step of a DPP maximum: lane i takes max(x_i, x of the lane CTRL selects);
+// lanes without a source keep x_i (old = -inf).
+template <int CTRL, int ROW_MASK>
+DG_DEV float dpp_max_step(float x) {
+    const int y = __builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(x), CTRL,
+                                              ROW_MASK, 0xf, false);
+    return fmaxf(x, __int_as_float(y));
+}
+
+// Maximum over the 64 lanes, uniform: prefix maxima within each 16-lane row (row
+// shifts by 1, 2, 4, 8), then the rows' last lanes broadcast into the next rows
+// (row_bcast:15, row_bcast:31); lane 63 ends with the wave's maximum.
+DG_DEV float wave_max_dpp(float x) {
+    x = dpp_max_step<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_max_step<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_max_step<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_max_step<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_max_step<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x = dpp_max_step<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// Top-k of token t by one wave (no block-level synchronisation).  Lane l holds
+// the summed logits of experts l, 64 + l, ...; k rounds each take the wave
+// maximum and the lowest expert id holding it (ballot), which is the ranking
+// (logit descending, ties to the lower id).
 DG_DEV void topk_token(const float* __restrict__ logits, int nsplit, int M, int E, int k, int t,
-                       int32_t* __restrict__ idx, float* __restrict__ gates,
-                       float (*lg)[kMaxExperts], float (*sv)[16]) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int e = lane; e < E; e += 64) {
+                       int32_t* __restrict__ idx, float* __restrict__ gates) {
+    const int lane = threadIdx.x & 63;
+    constexpr int NQ = kMaxExperts / 64;
+    float v[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int e = 64 * q + lane;
         float part[kMaxRouterSplit];
 #pragma unroll
         for (int sp = 0; sp < kMaxRouterSplit; ++sp)   // all loads in flight together
-            part[sp] = sp < nsplit ? logits[((int64_t)sp * M + t) * E + e] : 0.f;
-        float v = 0.f;
+            part[sp] = (sp < nsplit && e < E) ? logits[((int64_t)sp * M + t) * E + e] : 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int sp = 0; sp < kMaxRouterSplit; ++sp) v += part[sp];   // fixed order
-        lg[w][e] = v;
+        for (int sp = 0; sp < kMaxRouterSplit; ++sp) sum += part[sp];   // fixed order
+        v[q] = e < E ? sum : -INFINITY;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    for (int e = lane; e < E; e += 64) {
-        const float v = lg[w][e];
-        int rank = 0;
-        const float4* row = reinterpret_cast<const float4*>(lg[w]);
-        for (int j4 = 0; j4 < (E >> 2); ++j4) {   // E is a multiple of 4 (checked by the launcher)
-            const float4 u = row[j4];
-            const int j = 4 * j4;
-            rank += (u.x > v) || (u.x == v && j < e);
-            rank += (u.y > v) || (u.y == v && j + 1 < e);
-            rank += (u.z > v) || (u.z == v && j + 2 < e);
-            rank += (u.w > v) || (u.w == v && j + 3 < e);
+    float sel[kMaxTopK];
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r) {
+        if (r >= k) break;
+        float lm = v[0];
+#pragma unroll
+        for (int q = 1; q < NQ; ++q) lm = fmaxf(lm, v[q]);
+        const float m = wave_max_dpp(lm);
+        int win = -1;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const uint64_t b = __ballot(v[q] == m);
+            if (win < 0 && b) win = 64 * q + __ffsll((long long)b) - 1;
         }
-        if (rank < k) {
-            idx[(int64_t)t * k + rank] = e;
-            sv[w][rank] = v;
-        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            if (win == 64 * q + lane) v[q] = -INFINITY;
+        sel[r] = m;
+        if (lane == 0) idx[(int64_t)t * k + r] = win;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     if (lane < k) {
-        const float mx = sv[w][0];
-        float s = 0.f;
-        for (int j = 0; j < k; ++j) s += expf(sv[w][j] - mx);
-        gates[(int64_t)t * k + lane] = expf(sv[w][lane] - mx) / s;
+        const float mx = sel[0];
+        float s = 0.f, mine = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j >= k) break;
+            const float ex = expf(sel[j] - mx);
+            s += ex;
+            if (j == lane) mine = ex;
+        }
+        gates[(int64_t)t * k + lane] = mine / s;
     }
 }
 
@@ -71,11 +101,9 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
                                                      int M, int E, int k,
                                                      int32_t* __restrict__ idx,
                                                      float* __restrict__ gates) {
-    __shared__ __attribute__((aligned(16))) float lg[4][kMaxExperts];
-    __shared__ float sv[4][16];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= M) return;
-    topk_token(logits, nsplit, M, E, k, t, idx, gates, lg, sv);
+    topk_token(logits, nsplit, M, E, k, t, idx, gates);
 }
 
 // Every expert's rows start at a multiple of pad (16 for the MFMA expert GEMMs,
@@ -147,17 +175,27 @@ DG_DEV void permute_block(const int32_t* __restrict__ idx, int n, int E, int k, 
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
     __shared__ int32_t woff[kMaxExperts + 1];
+    constexpr int kPer = kPermSmall / 256;     // entries per thread (blocks of 256 threads)
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    for (int f = threadIdx.x; f < n; f += blockDim.x) atomicAdd(&cnt[idx[f]], 1);
+    // each entry's expert and its place among the expert's entries (the counter's
+    // old value), kept in registers for the scatter below
+    int ex[kPer], lp[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int f = threadIdx.x + 256 * i;
+        ex[i] = f < n ? idx[f] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) lp[i] = ex[i] >= 0 ? atomicAdd(&cnt[ex[i]], 1) : 0;
     __syncthreads();
     route_offsets(cnt, E, pad, off, woff, offsets, perm_token, work, work_count);
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
-    __syncthreads();
-    for (int f = threadIdx.x; f < n; f += blockDim.x) {
-        const int e = idx[f];
-        const int pos = off[e] + atomicAdd(&cnt[e], 1);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int f = threadIdx.x + 256 * i;
+        if (ex[i] < 0) continue;
+        const int pos = off[ex[i]] + lp[i];
         perm_token[pos] = f / k;
         inv[f] = pos;
     }
@@ -176,11 +214,9 @@ __global__ __launch_bounds__(256) void k_router_route(const float* __restrict__ 
                                                       int2* __restrict__ work,
                                                       int32_t* __restrict__ work_count,
                                                       uint32_t* __restrict__ ticket) {
-    __shared__ __attribute__((aligned(16))) float lg[4][kMaxExperts];
-    __shared__ float sv[4][16];
     __shared__ bool last;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t < M) topk_token(logits, nsplit, M, E, k, t, idx, gates, lg, sv);
+    if (t < M) topk_token(logits, nsplit, M, E, k, t, idx, gates);
     __syncthreads();
     if (threadIdx.x == 0) {
         __threadfence();                                   // this block's idx before the ticket
