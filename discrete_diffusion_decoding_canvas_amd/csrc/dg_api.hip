@@ -815,7 +815,7 @@ int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int
     }
     {
         ProfScope p(h, DG_PROF_LM_HEAD, s);
-        K_TRY(launch_lm_head(h->act, h->a, C, h->d, h->embed, h->V, 1.0f / h->cfg.temperature,
+        K_TRY(launch_lm_head(h->act, h->a, h->Af, C, h->d, h->embed, h->V, 1.0f / h->cfg.temperature,
                              d_locked_mask, seed, step, h->k_blk, h->hp,
                              h->cap(DG_CAP_LOGITS) ? h->logits_cap : nullptr, s));
     }

@@ -1,0 +1,118 @@
+// Streaming vocabulary epilogue of the tied LM head (device code shared by the
+// head kernels).
+//
+// Logits L_t = Decoder(x_t, z_t, H) in R^{C x V} and p0 = Softmax(L_t / tau)
+// (DiffusionGemma technical-report summary, Method: decoder and update
+// equations).  The C x V logits are never stored: each wave reduces its
+// 128-id vocabulary slice to per-row partials (max, lowest argmax, sum of
+// exp(z - max)) and, for rows still unlocked, the Gumbel-max redraw (best
+// z + G and its id) with Philox4x32-10 uniforms drawn per (vocabulary id,
+// position).
+#pragma once
+
+#include "kernels.h"
+
+namespace dg {
+
+constexpr int kHeadRows = 256;    // rows per workgroup (4 row waves x 64)
+constexpr int kHeadTile = 256;    // vocabulary ids per workgroup (2 column waves)
+constexpr int kHeadCols = 128;    // vocabulary ids per wave = one partial slice
+
+union HFrag {
+    uint4 u;
+    bf16x8_t b;
+};
+
+struct Run {
+    float m;
+    int32_t a;
+    float s;
+    float g;
+    int32_t gi;
+};
+
+DG_DEV void run_merge(Run& x, float ym, int32_t ya, float ys, float yg, int32_t ygi) {
+    if (ym > x.m || (ym == x.m && ya < x.a)) {
+        x.s = ys + (x.m == -INFINITY ? 0.f : x.s * __expf(x.m - ym));
+        x.m = ym;
+        x.a = ya;
+    } else {
+        x.s += (ym == -INFINITY ? 0.f : ys * __expf(ym - x.m));
+    }
+    if (yg > x.g || (yg == x.g && ygi < x.gi)) { x.g = yg; x.gi = ygi; }
+}
+
+DG_DEV float gumbel_of(uint32_t w) { return -logf(-logf(philox_open_uniform(w))); }
+
+struct EpiArgs {
+    int C, V, v0, rbase, g, l16;
+    float inv_tau;
+    const uint8_t* mask;
+    uint32_t key0, key1, c2;
+    HeadPartials p;
+    float* logits_out;
+};
+
+// Epilogue of one 16-row fragment group MT of a wave's 64 x 128 tile: each lane
+// folds its 8 columns for its 4 rows, then the 16 lanes sharing the rows merge.
+// MT is a template argument so that every accumulator index is static.
+template <int MT>
+DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
+    const int r4 = e.rbase + 16 * MT + 4 * e.g;      // rows r4 .. r4+3 in this lane
+    bool unl[4];
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        unl[j] = (r4 + j < e.C) && e.mask[r4 + j] == 0;
+        any |= unl[j];
+    }
+    Run run[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) run[j] = Run{-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const int v = e.v0 + 16 * nt + e.l16;
+        u32x4 rw = {0u, 0u, 0u, 0u};
+        if (any) rw = philox4x32_10(u32x4{(uint32_t)v, (uint32_t)(r4 >> 2), e.c2, kGumbelTag},
+                                    e.key0, e.key1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t word = j == 0 ? rw.x : j == 1 ? rw.y : j == 2 ? rw.z : rw.w;
+            const float z = acc[nt][j] * e.inv_tau;
+            if (e.logits_out != nullptr && r4 + j < e.C) e.logits_out[(size_t)(r4 + j) * e.V + v] = z;
+            if (z > run[j].m) {
+                run[j].s = (run[j].m == -INFINITY ? 0.f : run[j].s * __expf(run[j].m - z)) + 1.f;
+                run[j].m = z;
+                run[j].a = v;
+            } else {
+                run[j].s += __expf(z - run[j].m);
+            }
+            if (unl[j]) {
+                const float gs = z + gumbel_of(word);
+                if (gs > run[j].g) { run[j].g = gs; run[j].gi = v; }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const float ym = __shfl_xor(run[j].m, o, 64);
+            const int32_t ya = __shfl_xor(run[j].a, o, 64);
+            const float ys = __shfl_xor(run[j].s, o, 64);
+            const float yg = __shfl_xor(run[j].g, o, 64);
+            const int32_t ygi = __shfl_xor(run[j].gi, o, 64);
+            run_merge(run[j], ym, ya, ys, yg, ygi);
+        }
+        if (e.l16 == 0 && r4 + j < e.C) {
+            const size_t o = (size_t)(r4 + j) * e.p.n_slices + e.v0 / kHeadCols;
+            e.p.m[o] = run[j].m;
+            e.p.a[o] = run[j].a;
+            e.p.s[o] = run[j].s;
+            e.p.g[o] = run[j].g;
+            e.p.gi[o] = run[j].gi;
+        }
+    }
+}
+
+}  // namespace dg

@@ -153,9 +153,14 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
 
 // LM head: per (row, slice) partial max / argmax / sum-exp / Gumbel best of
 // z = (h E^T) / tau over the vocabulary.  Gumbel noise for rows with mask == 0.
-hipError_t launch_lm_head(int dtype, const void* h, int C, int d, const void* E, int V,
-                          float inv_tau, const uint8_t* mask, uint64_t seed, int step, int k_blk,
-                          const HeadPartials& p, float* logits_out, hipStream_t s);
+// bf16: hf, when given, holds the same rows in MFMA fragment order (frag_offset,
+// K = d) and the head runs on the streamed-weight pipeline of the expert GEMMs.
+hipError_t launch_lm_head(int dtype, const void* h, const void* hf, int C, int d, const void* E,
+                          int V, float inv_tau, const uint8_t* mask, uint64_t seed, int step,
+                          int k_blk, const HeadPartials& p, float* logits_out, hipStream_t s);
+hipError_t launch_head_wide(const void* hf, int C, int d, const void* E, int V, float inv_tau,
+                            const uint8_t* mask, uint32_t key0, uint32_t key1, uint32_t c2,
+                            const HeadPartials& p, float* logits_out, hipStream_t s);
 int lm_head_slices(int dtype, int V);
 
 // ---------------------------------------------------------------- attention

@@ -24,7 +24,7 @@
 //     v_mfma_f32_16x16x32_fp8_fp8 for e4m3 experts);
 //   * the SwiGLU of the first expert GEMM runs in the epilogue (gate and up
 //     columns are interleaved per 16-column group at pack time).
-#include "kernels.h"
+#include "head_epilogue.h"
 
 namespace dg {
 
@@ -699,6 +699,47 @@ __global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(   // <= 128 VGPRs
     }
 }
 
+// LM head on the same pipeline: the "weights" are the packed embedding E (one
+// 128-id slab per workgroup, streamed once), the activations the final normed
+// hidden rows in fragment order, and the epilogue the streaming vocabulary
+// statistics of each (row, 128-id slice) (head_epilogue).  grid (V / 128, ceil(C / 256)).
+static_assert(kWideN == kHeadCols, "one workgroup slab is one partial slice");
+__global__ __launch_bounds__(kWideThreads, 4) void k_head_wide(   // <= 128 VGPRs
+    const uint8_t* Hf, int C, int d, const void* __restrict__ Ep, int V, float inv_tau,
+    const uint8_t* __restrict__ mask, uint32_t key0, uint32_t key1, uint32_t c2, HeadPartials p,
+    float* __restrict__ logits_out) {
+    __shared__ __attribute__((aligned(16))) WideRing bsm;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n0 = blockIdx.x * kWideN;            // first vocabulary id of the slab
+    const int KB = d >> 5;
+    const size_t gsize = (size_t)KB * 1024;
+    WeightStream ws;
+    ws.g = w * kCopies / 2;
+    ws.ks0 = (w * kCopies) & 1;
+    const int gcol = (n0 >> 4) + ws.g;
+    ws.rsrc = group_rsrc((const uint8_t*)Ep + (size_t)gcol * gsize, (uint32_t)gsize);
+    ws.voff = (uint32_t)lane * 16;
+    ws.kb_lo = 0;
+    ws.kb_hi = KB;
+    ws.NS = (KB + 1) >> 1;
+    const int wr0 = blockIdx.y * kMoeRows + 16 * kWideMT * w;   // this wave's first row
+    if (wr0 >= C) {
+        wide_stream_only(ws, bsm);
+        return;
+    }
+    const uint8_t* afrag[kWideMT];
+#pragma unroll
+    for (int mt = 0; mt < kWideMT; ++mt) {
+        const int r = wr0 + 16 * mt < C ? wr0 + 16 * mt : wr0;
+        afrag[mt] = Hf + ((size_t)(r >> 4) * KB * 64 + lane) * 16;
+    }
+    WideAcc acc;
+    wide_mainloop<false>(acc, afrag, ws, bsm, lane);
+    static_assert(kWideMT == 1, "head_epilogue takes one 16-row group of eight 16-id groups");
+    const EpiArgs ea{C, V, n0, wr0, lane >> 4, lane & 15, inv_tau, mask, key0, key1, c2, p, logits_out};
+    head_epilogue<0>(acc[0], ea);
+}
+
 // GEMM 1's activation fragments: the token rows of every 16-row tile of the
 // permuted entries in MFMA A-operand order (frag_offset), zero for padding rows.
 // Done once here, the expert GEMM's activation loads become contiguous 1 KiB
@@ -848,6 +889,17 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                                                                offsets, work.items, work.count,
                                                                w.w1, w.s1, H);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_head_wide(const void* hf, int C, int d, const void* E, int V, float inv_tau,
+                            const uint8_t* mask, uint32_t key0, uint32_t key1, uint32_t c2,
+                            const HeadPartials& p, float* logits_out, hipStream_t s) {
+    if (C <= 0) return hipSuccess;
+    if ((V % kWideN) || (d & 31)) return hipErrorInvalidValue;
+    dim3 grid(V / kWideN, (C + kMoeRows - 1) / kMoeRows);
+    k_head_wide<<<grid, kWideThreads, 0, s>>>((const uint8_t*)hf, C, d, E, V, inv_tau, mask, key0,
+                                              key1, c2, p, logits_out);
     return hipGetLastError();
 }
 
