@@ -381,8 +381,8 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
 
 // Causal encoder over n tokens at positions pos0.. (prefill chunk or commit).
 static int encode(dg_handle* h, const int32_t* tokens, int n, int64_t pos0, hipStream_t s) {
-    K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, tokens, h->embed, n, h->d,
-                               h->cfg.rms_eps, h->x, h->a, h->Af, s));
+    K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, tokens, h->embed, h->V, n, h->d,
+                               h->cfg.rms_eps, h->x, h->a, h->Af, h->bad, s));
     for (int l = 0; l < h->L; ++l)
         DG_TRY(run_layer(h, l, n, pos0, true, l == h->L - 1, s));
     return DG_OK;
@@ -796,8 +796,8 @@ int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int
     DG_TRY(ensure_ready(h));
     hipStream_t s = (hipStream_t)stream;
     const int C = h->C;
-    K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, C, h->d,
-                               h->cfg.rms_eps, h->x, h->a, h->Af, s));
+    K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, h->V, C, h->d,
+                               h->cfg.rms_eps, h->x, h->a, h->Af, h->bad, s));
     const uint32_t per_layer = DG_CAP_ROUTING | DG_CAP_HIDDEN | DG_CAP_ATTN | DG_CAP_ROUTER_LOGITS;
     if (h->use_graphs && !h->prof && !(h->cap_mask & per_layer)) {
         DG_TRY(run_layers_graph(h, s));
@@ -832,6 +832,7 @@ static int check_bad(dg_handle* h, hipStream_t s) {
     if (bad) {
         HIP_TRY(launch_fill_u32(h->bad, 0u, 1, s));
         HIP_TRY(hipStreamSynchronize(s));
+        if (bad & kBadToken) return fail(DG_ETOKEN, "a token id outside [0, %d) was embedded", h->V);
         return fail(DG_ENONFINITE, "non-finite logits statistics");
     }
     return DG_OK;

@@ -11,6 +11,9 @@ constexpr int kFP8 = 2;
 
 constexpr int kPermChunk = 1024;   // entries per permutation workgroup
 constexpr int kMaxCanvas = 1024;   // sampler capacity (one workgroup)
+// Bits of the handle's sticky error word.
+constexpr int32_t kBadNonFinite = 1;   // a row's logits statistics were not finite
+constexpr int32_t kBadToken = 2;       // a token id outside [0, V) was embedded
 constexpr int kMaxTopK = 16;       // experts per token
 constexpr int kCombineCols = 16;   // combine: columns per thread, d <= 256 * 16
 constexpr int kMoeRows = 256;      // rows of one expert-GEMM work item (a whole canvas)
@@ -68,8 +71,8 @@ struct HeadPartials {
 // The row-normalising kernels also write the bf16 rows in fragment order to af
 // (frag_offset, K = d) when af is given (bf16 only).
 hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, const void* E,
-                                int C, int d, float eps, float* x, void* a, void* af,
-                                hipStream_t s);
+                                int V, int C, int d, float eps, float* x, void* a, void* af,
+                                int32_t* bad, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
                           uint8_t* a8, void* af, hipStream_t s);
 hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int Hkv, int D,

@@ -32,21 +32,27 @@ DG_DEV float block_sum(float v, float* red) {
 
 // ------------------------------------------------------------------ embed + RMSNorm
 // x[i, :] = E[canvas[i], :] (float residual), a[i, :] = rmsnorm(x[i, :]).
+// An id outside [0, V) (caller data, or the argmax of a row whose logits were
+// all NaN) reads as a zero row and sets bit kBadToken of *bad; no load leaves
+// the table.
 template <typename T, bool PACKED>
 __global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict__ tokens,
-                                                       const T* __restrict__ E, int d,
+                                                       const T* __restrict__ E, int V, int d,
                                                        float eps, float* __restrict__ x,
-                                                       T* __restrict__ a, uint8_t* __restrict__ af) {
+                                                       T* __restrict__ a, uint8_t* __restrict__ af,
+                                                       int32_t* __restrict__ bad) {
     __shared__ float red[4];
     const int i = blockIdx.x;
     const int64_t v = tokens[i];
+    const bool valid = v >= 0 && v < V;
+    if (!valid && threadIdx.x == 0) atomicOr(bad, kBadToken);
     float xs[kCombineCols];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kCombineCols; ++j) {
         const int c = threadIdx.x + 256 * j;
         float e = 0.f;
-        if (c < d) e = PACKED ? to_f32<T>(E[packed_b_index(v, c, d)]) : to_f32<T>(E[v * d + c]);
+        if (valid && c < d) e = PACKED ? to_f32<T>(E[packed_b_index(v, c, d)]) : to_f32<T>(E[v * d + c]);
         xs[j] = e;
         ss += e * e;
     }
@@ -347,7 +353,7 @@ __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm
         st_lse[row] = r.m + ls;
         st_conf[row] = -ls;
         st_draw[row] = mask[row] ? -1 : r.gi;
-        if (!isfinite(r.m) || !isfinite(ls) || (!mask[row] && r.gi < 0)) atomicOr(bad, 1);
+        if (!isfinite(r.m) || !isfinite(ls) || (!mask[row] && r.gi < 0)) atomicOr(bad, kBadNonFinite);
     }
 }
 
@@ -443,17 +449,18 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, int64_t n) {
 #define LAUNCH_CHECK() return hipGetLastError()
 
 hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, const void* E,
-                                int C, int d, float eps, float* x, void* a, void* af,
-                                hipStream_t s) {
+                                int V, int C, int d, float eps, float* x, void* a, void* af,
+                                int32_t* bad, hipStream_t s) {
+    if (C == 0) return hipSuccess;
     if (dtype == kF32)
-        k_embed_rmsnorm<float, false><<<C, 256, 0, s>>>(tokens, (const float*)E, d, eps, x,
-                                                        (float*)a, nullptr);
+        k_embed_rmsnorm<float, false><<<C, 256, 0, s>>>(tokens, (const float*)E, V, d, eps, x,
+                                                        (float*)a, nullptr, bad);
     else if (packed)
-        k_embed_rmsnorm<bf16_t, true><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, d, eps, x,
-                                                        (bf16_t*)a, (uint8_t*)af);
+        k_embed_rmsnorm<bf16_t, true><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, V, d, eps, x,
+                                                        (bf16_t*)a, (uint8_t*)af, bad);
     else
-        k_embed_rmsnorm<bf16_t, false><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, d, eps, x,
-                                                         (bf16_t*)a, (uint8_t*)af);
+        k_embed_rmsnorm<bf16_t, false><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, V, d, eps, x,
+                                                         (bf16_t*)a, (uint8_t*)af, bad);
     LAUNCH_CHECK();
 }
 

@@ -77,6 +77,10 @@ DG_DEV void topk_token(const float* __restrict__ logits, int nsplit, int M, int 
             const uint64_t b = __ballot(v[q] == m);
             if (win < 0 && b) win = 64 * q + __ffsll((long long)b) - 1;
         }
+        // Only NaN logits leave no valid winner (fmaxf skips NaN, so m is then
+        // NaN or the -inf of a lane past E): take expert 0 so that every id
+        // stays in [0, E); the NaN gate reaches the logits statistics.
+        if (win < 0 || win >= E) win = 0;
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
             if (win == 64 * q + lane) v[q] = -INFINITY;

@@ -52,6 +52,7 @@ extern "C" {
 #define DG_ECAPACITY (-4)   /* the KV cache cannot hold n_ctx + canvas rows */
 #define DG_ESTATE (-5)      /* call out of order: no prompt prefilled, weights missing */
 #define DG_ENONFINITE (-6)  /* non-finite logits statistics were produced */
+#define DG_ETOKEN (-7)      /* a token id outside [0, V) was read (it embeds as a zero row) */
 
 /* ---------------------------------------------------------------- dtypes */
 #define DG_F32 0
@@ -146,7 +147,8 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
 /* Stage 1 (technical report, Method, generation pipeline): run the causal
  * encoder over P prompt ids (d_prompt_ids, device int32 [P]) and fill K/V
  * rows 0..P-1 of every layer.  Resets the context: afterwards n_ctx = P and
- * the canvas index k_blk = 0.  P >= 0 (P = 0 gives an empty context). */
+ * the canvas index k_blk = 0.  P >= 0 (P = 0 gives an empty context).
+ * Prompt ids outside [0, V) embed as zero rows; dg_check_finite reports them. */
 int dg_prefill_prompt_kv(dg_handle* h, const int32_t* d_prompt_ids, int32_t P, void* stream);
 
 /* Stage 2, one denoise pass over the canvas at positions n_ctx..n_ctx+C-1:
@@ -160,7 +162,9 @@ int dg_prefill_prompt_kv(dg_handle* h, const int32_t* d_prompt_ids, int32_t P, v
  * word i&3, u = (2*(word>>9)+1) * 2^-24).  Locked positions are not written.
  * d_canvas: device int32 [C], updated in place; d_locked_mask: device uint8
  * [C], updated in place.  0 <= step < T.  Needs a prefilled context
- * (DG_ESTATE otherwise) and room for C rows (DG_ECAPACITY). */
+ * (DG_ESTATE otherwise) and room for C rows (DG_ECAPACITY).  Asynchronous:
+ * canvas ids outside [0, V) and non-finite statistics are reported later by
+ * dg_check_finite or dg_generate_block. */
 int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t step,
                     int32_t T, uint64_t seed, void* stream);
 
@@ -186,8 +190,12 @@ int dg_generate_block(dg_handle* h, int32_t* d_out_tokens, int32_t T, uint64_t s
  * (device int32 [C]) at rows n_ctx..n_ctx+C-1; n_ctx += C, k_blk += 1. */
 int dg_commit_canvas(dg_handle* h, const int32_t* d_canvas, void* stream);
 
-/* Read and clear the handle's non-finite flag (set by any pass whose logits
- * statistics were not finite).  Synchronises the stream.  DG_ENONFINITE if set. */
+/* Read and clear the handle's sticky error flags.  A pass whose logits
+ * statistics were not finite sets one; an embedding of a token id outside
+ * [0, V) (prompt, canvas or committed canvas ids) sets the other and reads a
+ * zero row instead of the table.  Neither stops the passes queued after it.
+ * Synchronises the stream.  DG_ETOKEN if an id was out of range, else
+ * DG_ENONFINITE if statistics were not finite, else DG_OK. */
 int dg_check_finite(dg_handle* h, void* stream);
 
 /* Forget the context (n_ctx = 0, k_blk = 0).  Weights stay loaded. */
