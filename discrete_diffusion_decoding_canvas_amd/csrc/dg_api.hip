@@ -141,10 +141,11 @@ struct dg_handle {
 
     int alloc(void** p, size_t bytes) {
         if (bytes == 0) bytes = 256;
-        if (hipMalloc(p, bytes) != hipSuccess) {
+        const hipError_t e = hipMalloc(p, bytes);
+        if (e != hipSuccess) {
             (void)hipGetLastError();
             *p = nullptr;
-            return fail(DG_ENOMEM, "hipMalloc of %zu bytes failed", bytes);
+            return fail(DG_ENOMEM, "hipMalloc of %zu bytes failed: %s", bytes, hipGetErrorString(e));
         }
         allocs.push_back(*p);
         if (hipMemset(*p, 0, bytes) != hipSuccess) return fail(DG_EHIP, "hipMemset failed");
@@ -493,7 +494,7 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->perm_token, rows));
     A_TRY(h->allocT(&h->inv, T * k));
     A_TRY(h->allocT(&h->work_items, (T * k + kMoeRows - 1) / kMoeRows + E));
-    A_TRY(h->allocT(&h->work_count, 1));
+    A_TRY(h->allocT(&h->work_count, 3));   // item count, two GEMM unit counters
     A_TRY(h->allocT(&h->route_ticket, 1));
     if (hipMemset(h->route_ticket, 0, 4) != hipSuccess) return cleanup(fail(DG_EHIP, "ticket reset failed"));
     if (h->edt != kF32) A_TRY(h->alloc(&h->Xf, rows * d * esz));

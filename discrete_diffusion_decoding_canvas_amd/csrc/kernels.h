@@ -27,7 +27,8 @@ inline int64_t moe_rows_cap(int64_t n, int k, int E, int pad) { return n * k + (
 // [row0, row0 + kMoeRows) of expert e (clipped to the expert's count).
 struct MoeWork {
     int2* items;       // {e, row0}
-    int32_t* count;    // number of valid items
+    int32_t* count;    // [0] number of valid items; [1], [2] unit counters of the two
+                       // persistent expert GEMMs (zeroed by the kernel that writes [0])
     int max_items;     // grid bound: ceil(entries / kMoeRows) + E
     uint32_t* ticket;  // zero-initialised block counter of the fused top-k + permutation
 };

@@ -24,6 +24,8 @@
 //     v_mfma_f32_16x16x32_fp8_fp8 for e4m3 experts);
 //   * the SwiGLU of the first expert GEMM runs in the epilogue (gate and up
 //     columns are interleaved per 16-column group at pack time).
+#include <algorithm>
+
 #include "head_epilogue.h"
 
 namespace dg {
@@ -353,10 +355,11 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 }
 
 // ------------------------------------------------------------------ expert GEMMs (MFMA)
-// One workgroup per (kWideN-column weight slab, work item); a work item is up
-// to kMoeRows = 256 rows of one expert (a whole canvas), so an expert's weights
+// A unit is (kWideN-column weight slab, work item); a work item is up to
+// kMoeRows = 256 rows of one expert (a whole canvas), so an expert's weights
 // leave HBM once per pass.  Wide slabs keep the activation traffic, which every
-// slab re-reads, at K * 2 bytes per row per kWideN output columns.
+// slab re-reads, at K * 2 bytes per row per kWideN output columns.  The kernels
+// are persistent (about one workgroup per CU taking units in turn).
 //
 // kWideWaves waves, each with two roles:
 //   * weight streaming: a stage is two packed k-steps of the slab's kWideNT
@@ -390,10 +393,11 @@ constexpr int kWideN = 16 * kWideNT;                // slab width
 constexpr int kWideMT = 1;                          // 16-row MFMA tiles per wave
 constexpr int kWideWaves = kMoeRows / (16 * kWideMT);
 constexpr int kWideThreads = 64 * kWideWaves;
+constexpr int kWideWavesPerEU = kWideWaves / 4;     // one workgroup per CU: the VGPR budget
 constexpr int kCopies = 2 * kWideNT / kWideWaves;   // 1 KiB weight copies per wave per stage
 constexpr int kRing = DG_WIDE_RING;                 // LDS stages (2 kWideNT KiB each)
 #ifndef DG_WIDE_LEAD
-#define DG_WIDE_LEAD 4
+#define DG_WIDE_LEAD 3
 #endif
 constexpr int kWideLead = DG_WIDE_LEAD;             // activation stages loaded ahead per wave
 constexpr int kWideSlots = kWideLead + 1;
@@ -534,10 +538,19 @@ DG_DEV __amdgpu_buffer_rsrc_t group_rsrc(const void* p, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes, 0x00020000);
 }
 
-// A wave without rows streams its share of the weights and keeps the barrier count.
-DG_DEV void wide_stream_only(const WeightStream& ws, WideRing& bsm) {
+// The copies of stages 0..kRing - 2 of a stream into slots 0..kRing - 2.  A
+// persistent workgroup issues them for its next unit before the epilogue of the
+// current one (every slot is free once the current unit's last barrier passed).
+DG_DEV void wide_fill(const WeightStream& ws, WideRing& bsm) {
 #pragma unroll
     for (int st = 0; st < kRing - 1; ++st) wide_copy_b(ws, st, st, bsm);
+}
+
+// A wave without rows streams its share of the weights and keeps the barrier
+// count (that of wide_mainloop: kRing - 1 filled stages, then NS + 2 barriers).
+// The loads of a wave return in issue order, so a count that a wave's stores
+// (an epilogue between the fill and here) push up only makes a wait stricter.
+DG_DEV void wide_stream_only(const WeightStream& ws, WideRing& bsm) {
     __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitIdle));             // own copies of stage 0
     bare_barrier();
     for (int s0 = 0; s0 < ws.NS; s0 += kRing) {
@@ -551,6 +564,7 @@ DG_DEV void wide_stream_only(const WeightStream& ws, WideRing& bsm) {
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+    bare_barrier();   // every wave's copies landed: the ring may be refilled
 }
 
 // Operations a wave has issued after its copies of stage st + 1 when stage st
@@ -573,8 +587,8 @@ DG_DEV void wide_wait_first(int u) {
     }
 }
 
-// acc over the stream's k-steps.  The prologue issues the copies of stages
-// 0..kRing - 2, then the activation loads of stages 0..kWideLead - 1; stage st
+// acc over the stream's k-steps, after wide_fill of the same stream.  The
+// prologue issues the activation loads of stages 0..kWideLead - 1; stage st
 // then issues the activation loads of stage st + kWideLead and the copies of
 // stage st + kRing - 1, runs its MFMAs, waits for this wave's copies of stage
 // st + 1 and meets the barrier.  The slot indices are compile-time: the loop is
@@ -587,8 +601,6 @@ DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
     for (int mt = 0; mt < kWideMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kWideNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < kRing - 1; ++st) wide_copy_b(ws, st, st, bsm);
     asm volatile("" ::: "memory");   // the copies stay ahead of the activation loads
     WideFrag ra[kWideSlots];
 #pragma unroll
@@ -618,67 +630,64 @@ DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+    bare_barrier();   // every wave's copies landed and LDS reads done: the ring may be refilled
 }
 
-template <bool FP8, int GEMM>
-__global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(   // <= 128 VGPRs
-    const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
-    const int2* __restrict__ work, const int32_t* __restrict__ work_count,
-    const void* __restrict__ W, const float* __restrict__ scales, void* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) WideRing bsm;
-    if ((int)blockIdx.y >= *work_count) return;
-    const int2 item = work[blockIdx.y];
-    const int e = item.x;
-    const int off = offsets[e];                                      // a multiple of 16
-    const int n_e = min(offsets[e + 1] - off, item.y + kMoeRows);   // rows end (expert-relative)
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * kWideN;
-    const int KB = FP8 ? (K >> 6) : (K >> 5);     // packed k-steps
-    const size_t gsize = (size_t)KB * 1024;       // bytes per packed 16-column group
+// One unit of an expert GEMM: a work item (up to kMoeRows rows of one expert)
+// times one kWideN-column slab.  Units are numbered item-major, so the slabs of
+// an item (which share its activation rows) are taken up together.
+struct MoeUnit {
+    int e, off, n_e;   // expert, its first row, its rows end (expert-relative, item-clamped)
+    int wr0, n0;       // this wave's first row (expert-relative), the slab's first column
     WeightStream ws;
-    ws.g = w * kCopies / 2;
-    ws.ks0 = (w * kCopies) & 1;
-    const int gcol = (n0 >> 4) + ws.g;            // the group's first column / 16
-    ws.rsrc = group_rsrc((const uint8_t*)W + ((size_t)e * (N >> 4) + gcol) * gsize,
-                         gcol < (N >> 4) ? (uint32_t)gsize : 0u);
-    ws.voff = (uint32_t)lane * 16;
-    ws.kb_lo = 0;
-    ws.kb_hi = KB;
-    ws.NS = (KB + 1) >> 1;
+};
+
+DG_DEV MoeUnit moe_unit(int u, int n_slabs, const int2* __restrict__ work,
+                        const int32_t* __restrict__ offsets, int N, int KB, const void* W, int w,
+                        int lane) {
+    MoeUnit c;
+    const int2 item = work[u / n_slabs];
+    c.e = item.x;
+    c.off = offsets[c.e];                                          // a multiple of 16
+    c.n_e = min(offsets[c.e + 1] - c.off, item.y + kMoeRows);
+    c.n0 = (u % n_slabs) * kWideN;
     // rows r = item.y + 16 (kWideMT w + mt) + lane % 16 (expert-relative); n_e is
     // a multiple of 16, so a row tile is wholly inside or outside the expert
-    const int wr0 = item.y + 16 * kWideMT * w;
-    if (wr0 >= n_e) {
-        wide_stream_only(ws, bsm);
-        return;
-    }
-    const uint8_t* afrag[kWideMT];
-#pragma unroll
-    for (int mt = 0; mt < kWideMT; ++mt) {
-        const int r = wr0 + 16 * mt < n_e ? wr0 + 16 * mt : wr0;   // tiles past the rows repeat tile 0
-        afrag[mt] = Af + ((size_t)((off + r) >> 4) * KB * 64 + lane) * 16;
-    }
-    WideAcc acc;
-    wide_mainloop<FP8>(acc, afrag, ws, bsm, lane);
+    c.wr0 = item.y + 16 * kWideMT * w;
+    const size_t gsize = (size_t)KB * 1024;                         // bytes per packed 16-column group
+    c.ws.g = w * kCopies / 2;
+    c.ws.ks0 = (w * kCopies) & 1;
+    const int gcol = (c.n0 >> 4) + c.ws.g;                         // the group's first column / 16
+    c.ws.rsrc = group_rsrc((const uint8_t*)W + ((size_t)c.e * (N >> 4) + gcol) * gsize,
+                           gcol < (N >> 4) ? (uint32_t)gsize : 0u);
+    c.ws.voff = (uint32_t)lane * 16;
+    c.ws.kb_lo = 0;
+    c.ws.kb_hi = KB;
+    c.ws.NS = (KB + 1) >> 1;
+    return c;
+}
 
-    // ---------------- epilogue: lane holds column lane % 16 of each group, rows 4 (lane / 16) + i
+// Epilogue of a unit: lane holds column lane % 16 of each group, rows 4 (lane / 16) + i.
+template <bool FP8, int GEMM>
+DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
+                         const float* __restrict__ scales, void* __restrict__ out, int lane) {
     const int l16 = lane & 15, g4 = 4 * (lane >> 4);
 #pragma unroll
     for (int mt = 0; mt < kWideMT; ++mt) {
-        if (wr0 + 16 * mt >= n_e) break;
+        if (c.wr0 + 16 * mt >= c.n_e) break;
         if (GEMM == 1) {
 #pragma unroll
             for (int p = 0; p < kWideNT / 2; ++p) {
-                const int cg = n0 + 32 * p + l16, cu = cg + 16;   // interleaved weight columns
-                const float sg = FP8 ? scales[(size_t)e * N + cg] : 1.f;
-                const float su = FP8 ? scales[(size_t)e * N + cu] : 1.f;
-                const int hcol = (n0 >> 1) + 16 * p + l16;
+                const int cg = c.n0 + 32 * p + l16, cu = cg + 16;   // interleaved weight columns
+                const float sg = FP8 ? scales[(size_t)c.e * N + cg] : 1.f;
+                const float su = FP8 ? scales[(size_t)c.e * N + cu] : 1.f;
+                const int hcol = (c.n0 >> 1) + 16 * p + l16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = wr0 + 16 * mt + g4 + i;
+                    const int r = c.wr0 + 16 * mt + g4 + i;
                     const float g = acc[mt][2 * p][i] * sg, uu = acc[mt][2 * p + 1][i] * su;
                     const float hv = g / (1.0f + expf(-g)) * uu;
-                    const size_t o = frag_offset<FP8>(off + r, hcol, F);   // GEMM 2's A order
+                    const size_t o = frag_offset<FP8>(c.off + r, hcol, F);   // GEMM 2's A order
                     if (FP8) ((uint8_t*)out)[o] = (uint8_t)f32_to_e4m3(hv);
                     else *(bf16_t*)((uint8_t*)out + o) = f32_to_bf16(hv);
                 }
@@ -686,58 +695,136 @@ __global__ __launch_bounds__(kWideThreads, 4) void k_moe_wide(   // <= 128 VGPRs
         } else {
 #pragma unroll
             for (int nt = 0; nt < kWideNT; ++nt) {
-                const int c = n0 + 16 * nt + l16;
-                if (c >= N) break;
-                const float sc = FP8 ? scales[(size_t)e * N + c] : 1.f;
+                const int col = c.n0 + 16 * nt + l16;
+                if (col >= N) break;
+                const float sc = FP8 ? scales[(size_t)c.e * N + col] : 1.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = wr0 + 16 * mt + g4 + i;
-                    ((float*)out)[(size_t)(off + r) * N + c] = acc[mt][nt][i] * sc;
+                    const int r = c.wr0 + 16 * mt + g4 + i;
+                    ((float*)out)[(size_t)(c.off + r) * N + col] = acc[mt][nt][i] * sc;
                 }
             }
         }
     }
 }
 
+// Persistent: about one workgroup per CU, each taking units from the counter
+// unit_ctr (zeroed by the routing kernel that wrote the work items) until
+// work_count * n_slabs are taken.  After a unit's last stage the workgroup
+// takes its next unit and issues that unit's first kRing - 1 weight stages
+// before it runs the current unit's epilogue, so the weight stream does not
+// stop between units and no workgroup is launched for an absent item.
+template <bool FP8, int GEMM>
+__global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
+    const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
+    const int2* __restrict__ work, const int32_t* __restrict__ work_count,
+    int32_t* __restrict__ unit_ctr, const void* __restrict__ W, const float* __restrict__ scales,
+    void* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) WideRing bsm;
+    __shared__ int s_unit[2];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int KB = FP8 ? (K >> 6) : (K >> 5);     // packed k-steps
+    const int n_slabs = (N + kWideN - 1) / kWideN;
+    const int total = *work_count * n_slabs;
+    if (threadIdx.x == 0) s_unit[0] = atomicAdd(unit_ctr, 1);
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(s_unit[0]);
+    if (u >= total) return;
+    MoeUnit c = moe_unit(u, n_slabs, work, offsets, N, KB, W, w, lane);
+    wide_fill(c.ws, bsm);
+    for (int it = 1;; ++it) {
+        const bool rows = c.wr0 < c.n_e;          // uniform per wave
+        WideAcc acc;
+        if (rows) {
+            const uint8_t* afrag[kWideMT];
+#pragma unroll
+            for (int mt = 0; mt < kWideMT; ++mt) {
+                const int r = c.wr0 + 16 * mt < c.n_e ? c.wr0 + 16 * mt : c.wr0;   // past the rows: tile 0
+                afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 16;
+            }
+            wide_mainloop<FP8>(acc, afrag, c.ws, bsm, lane);
+        } else {
+            wide_stream_only(c.ws, bsm);
+        }
+        if (threadIdx.x == 0) s_unit[it & 1] = atomicAdd(unit_ctr, 1);
+        __syncthreads();
+        const int un = __builtin_amdgcn_readfirstlane(s_unit[it & 1]);
+        if (un < total) wide_fill(moe_unit(un, n_slabs, work, offsets, N, KB, W, w, lane).ws, bsm);
+        if (rows) moe_epilogue<FP8, GEMM>(acc, c, N, F, scales, out, lane);
+        if (un >= total) break;
+        c = moe_unit(un, n_slabs, work, offsets, N, KB, W, w, lane);   // recomputed: less live state
+    }
+}
+
 // LM head on the same pipeline: the "weights" are the packed embedding E (one
-// 128-id slab per workgroup, streamed once), the activations the final normed
-// hidden rows in fragment order, and the epilogue the streaming vocabulary
-// statistics of each (row, 128-id slice) (head_epilogue).  grid (V / 128, ceil(C / 256)).
-static_assert(kWideN == kHeadCols, "one workgroup slab is one partial slice");
-__global__ __launch_bounds__(kWideThreads, 4) void k_head_wide(   // <= 128 VGPRs
+// 128-id slab per unit, streamed once), the activations the final normed hidden
+// rows in fragment order, and the epilogue the streaming vocabulary statistics
+// of each (row, 128-id slice) (head_epilogue).  Units (slab, 256-row block) are
+// numbered slab-fastest and dealt round-robin to a persistent grid; the next
+// unit's first weight stages are issued before the current unit's epilogue.
+static_assert(kWideN == kHeadCols, "one unit's slab is one partial slice");
+
+struct HeadUnit {
+    int n0, wr0;
+    WeightStream ws;
+};
+
+DG_DEV HeadUnit head_unit(int u, int n_slabs, const void* Ep, int KB, int w, int lane) {
+    HeadUnit c;
+    c.n0 = (u % n_slabs) * kWideN;                                 // first vocabulary id of the slab
+    c.wr0 = (u / n_slabs) * kMoeRows + 16 * kWideMT * w;           // this wave's first row
+    const size_t gsize = (size_t)KB * 1024;
+    c.ws.g = w * kCopies / 2;
+    c.ws.ks0 = (w * kCopies) & 1;
+    const int gcol = (c.n0 >> 4) + c.ws.g;
+    c.ws.rsrc = group_rsrc((const uint8_t*)Ep + (size_t)gcol * gsize, (uint32_t)gsize);
+    c.ws.voff = (uint32_t)lane * 16;
+    c.ws.kb_lo = 0;
+    c.ws.kb_hi = KB;
+    c.ws.NS = (KB + 1) >> 1;
+    return c;
+}
+
+__global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_head_wide(
     const uint8_t* Hf, int C, int d, const void* __restrict__ Ep, int V, float inv_tau,
     const uint8_t* __restrict__ mask, uint32_t key0, uint32_t key1, uint32_t c2, HeadPartials p,
     float* __restrict__ logits_out) {
     __shared__ __attribute__((aligned(16))) WideRing bsm;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * kWideN;            // first vocabulary id of the slab
     const int KB = d >> 5;
-    const size_t gsize = (size_t)KB * 1024;
-    WeightStream ws;
-    ws.g = w * kCopies / 2;
-    ws.ks0 = (w * kCopies) & 1;
-    const int gcol = (n0 >> 4) + ws.g;
-    ws.rsrc = group_rsrc((const uint8_t*)Ep + (size_t)gcol * gsize, (uint32_t)gsize);
-    ws.voff = (uint32_t)lane * 16;
-    ws.kb_lo = 0;
-    ws.kb_hi = KB;
-    ws.NS = (KB + 1) >> 1;
-    const int wr0 = blockIdx.y * kMoeRows + 16 * kWideMT * w;   // this wave's first row
-    if (wr0 >= C) {
-        wide_stream_only(ws, bsm);
-        return;
-    }
-    const uint8_t* afrag[kWideMT];
+    const int n_slabs = V / kWideN;
+    const int total = n_slabs * ((C + kMoeRows - 1) / kMoeRows);
+    int u = blockIdx.x;
+    if (u >= total) return;
+    HeadUnit c = head_unit(u, n_slabs, Ep, KB, w, lane);
+    wide_fill(c.ws, bsm);
+    for (;;) {
+        const bool rows = c.wr0 < C;              // uniform per wave
+        WideAcc acc;
+        if (rows) {
+            const uint8_t* afrag[kWideMT];
 #pragma unroll
-    for (int mt = 0; mt < kWideMT; ++mt) {
-        const int r = wr0 + 16 * mt < C ? wr0 + 16 * mt : wr0;
-        afrag[mt] = Hf + ((size_t)(r >> 4) * KB * 64 + lane) * 16;
+            for (int mt = 0; mt < kWideMT; ++mt) {
+                const int r = c.wr0 + 16 * mt < C ? c.wr0 + 16 * mt : c.wr0;
+                afrag[mt] = Hf + ((size_t)(r >> 4) * KB * 64 + lane) * 16;
+            }
+            wide_mainloop<false>(acc, afrag, c.ws, bsm, lane);
+        } else {
+            wide_stream_only(c.ws, bsm);
+        }
+        const int un = u + gridDim.x;
+        if (un < total) wide_fill(head_unit(un, n_slabs, Ep, KB, w, lane).ws, bsm);
+        if (rows) {
+            static_assert(kWideMT <= 2, "head epilogue of one or two 16-row groups");
+            const EpiArgs ea{C, V, c.n0, c.wr0, lane >> 4, lane & 15, inv_tau, mask, key0, key1, c2, p,
+                             logits_out};
+            head_epilogue<0>(acc[0], ea);
+            if constexpr (kWideMT > 1) head_epilogue<1>(acc[1], ea);
+        }
+        if (un >= total) break;
+        u = un;
+        c = head_unit(u, n_slabs, Ep, KB, w, lane);
     }
-    WideAcc acc;
-    wide_mainloop<false>(acc, afrag, ws, bsm, lane);
-    static_assert(kWideMT == 1, "head_epilogue takes one 16-row group of eight 16-id groups");
-    const EpiArgs ea{C, V, n0, wr0, lane >> 4, lane & 15, inv_tau, mask, key0, key1, c2, p, logits_out};
-    head_epilogue<0>(acc[0], ea);
 }
 
 // GEMM 1's activation fragments: the token rows of every 16-row tile of the
@@ -864,6 +951,25 @@ hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const 
     return hipGetLastError();
 }
 
+// Workgroups of a persistent wide kernel: one per CU of the current device.
+static int persistent_wgs() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+static unsigned moe_grid(const MoeWork& work, int n_slabs) {
+    const int64_t units = (int64_t)work.max_items * n_slabs;
+    return (unsigned)std::min<int64_t>(units, persistent_wgs());
+}
+
 hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             const int32_t* perm_token, const int32_t* offsets, int E, int d,
                             int F, int max_rows, const MoeWork& work, void* Xf, void* H,
@@ -879,15 +985,15 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
         if ((2 * F) % kWideN || d % kq || F % kq || !Xf) return hipErrorInvalidValue;
         (void)X;
         (void)perm_token;
-        dim3 grid((2 * F) / kWideN, work.max_items);
+        const unsigned grid = moe_grid(work, (2 * F) / kWideN);
         if (dtype == kFP8)
             k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
                                                               offsets, work.items, work.count,
-                                                              w.w1, w.s1, H);
+                                                              work.count + 1, w.w1, w.s1, H);
         else
             k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
                                                                offsets, work.items, work.count,
-                                                               w.w1, w.s1, H);
+                                                               work.count + 1, w.w1, w.s1, H);
     }
     return hipGetLastError();
 }
@@ -897,7 +1003,8 @@ hipError_t launch_head_wide(const void* hf, int C, int d, const void* E, int V, 
                             const HeadPartials& p, float* logits_out, hipStream_t s) {
     if (C <= 0) return hipSuccess;
     if ((V % kWideN) || (d & 31)) return hipErrorInvalidValue;
-    dim3 grid(V / kWideN, (C + kMoeRows - 1) / kMoeRows);
+    const int64_t units = (int64_t)(V / kWideN) * ((C + kMoeRows - 1) / kMoeRows);
+    const unsigned grid = (unsigned)std::min<int64_t>(units, persistent_wgs());
     k_head_wide<<<grid, kWideThreads, 0, s>>>((const uint8_t*)hf, C, d, E, V, inv_tau, mask, key0,
                                               key1, c2, p, logits_out);
     return hipGetLastError();
@@ -929,13 +1036,15 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
             (const float*)H, d, F, offsets, E, max_rows, (const float*)w.w2, Y);
     } else {
         if (d % 16 || F % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
-        dim3 grid((d + kWideN - 1) / kWideN, work.max_items);
+        const unsigned grid = moe_grid(work, (d + kWideN - 1) / kWideN);
         if (dtype == kFP8)
             k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
-                                                              work.items, work.count, w.w2, w.s2, Y);
+                                                              work.items, work.count, work.count + 2,
+                                                              w.w2, w.s2, Y);
         else
             k_moe_wide<false, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
-                                                               work.items, work.count, w.w2, w.s2, Y);
+                                                               work.items, work.count, work.count + 2,
+                                                               w.w2, w.s2, Y);
     }
     return hipGetLastError();
 }

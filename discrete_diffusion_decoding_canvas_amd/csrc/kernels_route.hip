@@ -161,7 +161,11 @@ DG_DEV void route_offsets(const int32_t* cnt, int E, int pad, int32_t* off, int3
     wave0_exclusive_scan(woff, E);
     __syncthreads();
     for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
-    if (threadIdx.x == 0) *count = woff[E];
+    if (threadIdx.x == 0) {
+        count[0] = woff[E];
+        count[1] = 0;   // unit counters of the two expert GEMMs that read these items
+        count[2] = 0;
+    }
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         for (int i = woff[e]; i < woff[e + 1]; ++i) items[i] = make_int2(e, (i - woff[e]) * kMoeRows);
         for (int j = off[e] + cnt[e]; j < off[e + 1]; ++j) perm_token[j] = -1;
