@@ -142,38 +142,67 @@ def _grid_key(row):
            f"x{row.get('Grid_Size_Z', '')}"
 
 
+def _phase_of(rows):
+    """Phase of each dispatch: "load" (weight packing) before the first embedding
+    launch, "prefill" from it up to the embedding launch that opens the first denoise
+    pass (the last one before the first LM-head launch), "pass" from there on (the
+    passes, and the commits between blocks, which run the encoder on a canvas).  The
+    persistent kernels launch one grid for every batch size, so the grid alone does
+    not tell the prefill launches from the pass launches."""
+    def ids(word):
+        return sorted(int(r["Dispatch_Id"]) for r in rows if word in r["Kernel_Name"])
+    heads, embeds = ids("k_head"), ids("k_embed_rmsnorm")
+    first_embed = embeds[0] if embeds else None
+    pass_start = None
+    if heads and embeds:
+        before = [d for d in embeds if d < heads[0]]
+        pass_start = before[-1] if before else heads[0]
+    out = []
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        if pass_start is not None and d >= pass_start:
+            out.append("pass")
+        elif first_embed is not None and d >= first_embed:
+            out.append("prefill")
+        else:
+            out.append("load")
+    return out
+
+
 def summarize_trace(path):
-    """Per (kernel, grid) launch count and mean / min / max duration of a rocprofv3
-    --kernel-trace CSV: the denoise pass and the prefill launch the same kernels on
-    different grids, so they are listed apart."""
+    """Per (kernel, grid, phase) launch count and mean / min / max duration of a
+    rocprofv3 --kernel-trace CSV."""
     import csv
-    groups = {}
     with open(path) as f:
-        for row in csv.DictReader(f):
-            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
-            key = (row["Kernel_Name"].split("(")[0][:60], _grid_key(row))
-            groups.setdefault(key, []).append(dur)
+        rows = list(csv.DictReader(f))
+    groups = {}
+    for row, ph in zip(rows, _phase_of(rows)):
+        dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+        key = (row["Kernel_Name"].split("(")[0][:60], _grid_key(row), ph)
+        groups.setdefault(key, []).append(dur)
     total = sum(sum(v) for v in groups.values())
-    print(f"{'kernel':60s} {'grid':>18s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} "
+    print(f"{'kernel':60s} {'grid':>18s} {'phase':>8s} {'calls':>6s} {'mean_us':>9s} {'min_us':>9s} "
           f"{'max_us':>9s} {'pct':>6s}")
-    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        print(f"{name:60s} {grid:>18s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} "
+    for (name, grid, ph), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{name:60s} {grid:>18s} {ph:>8s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} "
               f"{max(v):9.2f} {100 * sum(v) / total:6.2f}")
 
 
 def summarize_pmc(path):
-    """Per (kernel, grid, counter) dispatch count and mean value of a rocprofv3 --pmc CSV."""
+    """Per (kernel, grid, phase, counter) dispatch count and mean value of a rocprofv3
+    --pmc CSV."""
     import csv
-    groups = {}
     with open(path) as f:
-        for row in csv.DictReader(f):
-            key = (row["Kernel_Name"].split("(")[0][:60], _grid_key(row), row["Counter_Name"])
-            groups.setdefault(key, {}).setdefault(row.get("Dispatch_Id", len(groups)), 0.0)
-            groups[key][row.get("Dispatch_Id")] += float(row["Counter_Value"])
-    print(f"{'kernel':60s} {'grid':>18s} {'counter':>12s} {'dispatches':>10s} {'mean':>14s}")
-    for (name, grid, ctr), d in sorted(groups.items()):
+        rows = list(csv.DictReader(f))
+    groups = {}
+    for row, ph in zip(rows, _phase_of(rows)):
+        key = (row["Kernel_Name"].split("(")[0][:60], _grid_key(row), ph, row["Counter_Name"])
+        groups.setdefault(key, {}).setdefault(row["Dispatch_Id"], 0.0)
+        groups[key][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    print(f"{'kernel':60s} {'grid':>18s} {'phase':>8s} {'counter':>12s} {'dispatches':>10s} {'mean':>14s}")
+    for (name, grid, ph, ctr), d in sorted(groups.items()):
         vals = list(d.values())
-        print(f"{name:60s} {grid:>18s} {ctr:>12s} {len(vals):10d} {sum(vals) / len(vals):14.1f}")
+        print(f"{name:60s} {grid:>18s} {ph:>8s} {ctr:>12s} {len(vals):10d} {sum(vals) / len(vals):14.1f}")
 
 
 def main():
