@@ -317,18 +317,32 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
 // writing K/V (the last encoder layer).
 static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool kv_only,
                      hipStream_t s, bool capture = false) {
-    {
+    if (h->act == kBF16) {
+        // Af: a in fragment order, from the norm that wrote it.  The QKV weights are
+        // pair-tiled (rope_hd 128), so the GEMM's epilogue applies RoPE and writes Q
+        // and the K/V cache rows itself.
         ProfScope p(h, DG_PROF_DENSE, s);
-        if (h->act == kBF16) {   // Af: a in fragment order, from the norm that wrote a
-            K_TRY(launch_gemm_frag(kEpiStoreF32, h->Af, n, h->wqkv[l], h->d, h->qkv_n, h->qkv,
-                                   h->qkv_n, s));
-        } else {
+        RopeArgs ra;
+        ra.Hq = h->Hq;
+        ra.Hkv = h->Hkv;
+        ra.pos0 = pos0;
+        ra.cos_t = h->cos_t;
+        ra.sin_t = h->sin_t;
+        ra.q = h->q;
+        ra.kc = h->klayer(l);
+        ra.vc = h->vlayer(l);
+        ra.kv_rows = h->kv_rows;
+        K_TRY(launch_gemm_frag(kEpiRope, h->Af, n, h->wqkv[l], h->d, h->qkv_n, nullptr, 0, s, 1,
+                               &ra));
+    } else {
+        {
+            ProfScope p(h, DG_PROF_DENSE, s);
             K_TRY(launch_gemm(h->act, kEpiStoreF32, h->a, h->d, n, h->wqkv[l], h->d, h->qkv_n,
                               h->qkv, h->qkv_n, s));
         }
+        K_TRY(launch_rope_scatter(h->act, h->qkv, n, h->Hq, h->Hkv, h->D, pos0, h->cos_t,
+                                  h->sin_t, h->q, h->klayer(l), h->vlayer(l), h->kv_rows, s));
     }
-    K_TRY(launch_rope_scatter(h->act, h->qkv, n, h->Hq, h->Hkv, h->D, pos0, h->cos_t, h->sin_t,
-                              h->q, h->klayer(l), h->vlayer(l), h->kv_rows, s));
     if (kv_only) return DG_OK;
     AttnArgs aa;
     aa.q = h->q;
@@ -475,7 +489,7 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->x, T * d));
     A_TRY(h->alloc(&h->a, T * d * as));
     if (h->edt == kFP8) A_TRY(h->allocT(&h->a8, T * d));
-    A_TRY(h->allocT(&h->qkv, T * h->qkv_n));
+    if (h->act == kF32) A_TRY(h->allocT(&h->qkv, T * h->qkv_n));   // bf16: RoPE in the QKV epilogue
     A_TRY(h->alloc(&h->q, T * h->Hq * h->D * as));
     A_TRY(h->alloc(&h->attn_o, T * h->Hq * h->D * as));
     // split-KV partials: the split count keeps (splits x query workgroups) near 512,
@@ -597,8 +611,8 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
         if (dt == kF32)
             HIP_TRY(hipMemcpy2D((float*)dst + col0, (size_t)ldn * 4, src, (size_t)N * 4,
                                 (size_t)N * 4, K, hipMemcpyDeviceToDevice));
-        else
-            HIP_TRY(launch_pack_b16(src, true, K, N, 1, col0 / 16, dst, s));
+        else   // Q, K and V columns pair-tiled for the QKV GEMM's RoPE epilogue
+            HIP_TRY(launch_pack_b16(src, true, K, N, 1, col0 / 16, dst, s, kind <= DG_T_WV ? 128 : 0));
         h->dense_flag(layer, kind - DG_T_WQ) = 1;
     } else {
         const int which = kind - DG_T_WG;   // 0 gate, 1 up, 2 down

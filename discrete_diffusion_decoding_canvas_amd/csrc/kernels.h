@@ -102,8 +102,11 @@ hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, 
                              int32_t* bad, hipStream_t s);
 hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t* draw,
                           int32_t* canvas, uint8_t* mask, int C, int step, int T, hipStream_t s);
+// rope_hd > 0 (128): the 16-column groups of every rope_hd-column head are
+// reordered so that each 64-column tile holds 32 rotary pairs (dims j and
+// j + 64 for j in one 32-dim quarter), see kEpiRope.
 hipError_t launch_pack_b16(const void* src, bool src_kn, int K, int N, int gstride, int goff,
-                           void* dst, hipStream_t s);
+                           void* dst, hipStream_t s, int rope_hd = 0);
 hipError_t launch_pack_b8(const void* src, int K, int N, int gstride, int goff, void* dst,
                           hipStream_t s);
 hipError_t launch_scatter_scales(const float* src, int N, int gstride, int goff, float* dst,
@@ -115,6 +118,21 @@ hipError_t launch_cast_e4m3(const void* x_bf16, int64_t n, uint8_t* out, hipStre
 // Epilogue modes of the dense GEMM.
 constexpr int kEpiStoreF32 = 0;   // C[m, n] = acc
 constexpr int kEpiAddF32 = 1;     // C[m, n] += acc (residual add, single writer)
+constexpr int kEpiRope = 2;       // QKV with pair-tiled columns: RoPE, bf16 Q, K and V cache writes
+
+// The QKV epilogue's destinations (head dim 128): Q bf16 [Hq][M][128], the K
+// cache bf16 [Hkv][kv_rows][128] and the V cache transposed (vt_index), rows at
+// positions pos0 + m; cos/sin tables [position][64].
+struct RopeArgs {
+    int Hq = 0, Hkv = 0;
+    int64_t pos0 = 0;
+    const float* cos_t = nullptr;
+    const float* sin_t = nullptr;
+    void* q = nullptr;
+    void* kc = nullptr;
+    void* vc = nullptr;
+    int64_t kv_rows = 0;
+};
 
 // C = A[M, K] B[K, N].  bf16: A row-major (lda), B packed (see packed_b_index).
 // f32: A row-major, B row-major [K, N].  bf16 with ksplit > 1 (store epilogue
@@ -123,8 +141,10 @@ hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const 
                        int N, float* C, int ldc, hipStream_t s, int ksplit = 1);
 // The same product (bf16) with A in MFMA A-fragment order ([row/16][K/32][64][16 B],
 // rows padded to 16), as written by launch_pack_afrag or by the producing kernel.
+// epi = kEpiRope: B packed with rope_hd = 128, N = (Hq + 2 Hkv) * 128, C unused.
 hipError_t launch_gemm_frag(int epi, const void* Af, int M, const void* B, int K, int N, float* C,
-                            int ldc, hipStream_t s, int ksplit = 1);
+                            int ldc, hipStream_t s, int ksplit = 1,
+                            const RopeArgs* rope = nullptr);
 hipError_t launch_pack_afrag(const void* A, int M, int K, void* Af, hipStream_t s);
 
 // Expert GEMMs over the permuted entries (offsets[e]..offsets[e+1] belong to expert e).

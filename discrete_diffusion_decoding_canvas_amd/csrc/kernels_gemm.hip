@@ -216,8 +216,10 @@ struct DenseStage {
 template <int EPI>
 __global__ __launch_bounds__(kDenseThreads) void k_dense_frag(const uint8_t* __restrict__ Af, int M,
                                                          const bf16_t* __restrict__ Bp, int K,
-                                                         int N, float* __restrict__ C, int ldc) {
-    __shared__ float red[kDenseWaves][16 * kDenseMT][kTileN];
+                                                         int N, float* __restrict__ C, int ldc,
+                                                         RopeArgs ra) {
+    // row pitch kTileN + 1: the transposed V stores of the QKV epilogue read columns
+    __shared__ float red[kDenseWaves][16 * kDenseMT][kTileN + 1];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * kTileN;
     const int m0 = blockIdx.y * 16 * kDenseMT;
@@ -277,6 +279,45 @@ __global__ __launch_bounds__(kDenseThreads) void k_dense_frag(const uint8_t* __r
             for (int j = 0; j < 4; ++j)
                 red[w][16 * mt + 4 * (lane >> 4) + j][16 * nt + (lane & 15)] = acc[mt][nt][j];
     __syncthreads();
+    if constexpr (EPI == kEpiRope) {
+        // The tile is 64 columns of one 128-dim head, pair-tiled: column c < 32 is dim
+        // 32 tp + c, column c + 32 its rotary partner 64 + 32 tp + c (rotate-half RoPE,
+        // y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin at the row's position).
+        constexpr int D = 128, half = 64;
+        const int head = n0 / D, tp = (n0 % D) / 64;
+        auto rsum = [&](int r, int c) {
+            float v = red[0][r][c];
+#pragma unroll
+            for (int i = 1; i < kDenseWaves; ++i) v += red[i][r][c];
+            return v;
+        };
+        if (head < ra.Hq + ra.Hkv) {
+            bf16_t* base = head < ra.Hq ? (bf16_t*)ra.q + (size_t)head * M * D
+                                        : (bf16_t*)ra.kc + (size_t)(head - ra.Hq) * ra.kv_rows * D;
+            for (int e = threadIdx.x; e < 16 * kDenseMT * 32; e += kDenseThreads) {
+                const int r = e >> 5, c = e & 31;          // consecutive lanes: consecutive dims
+                const int m = m0 + r;
+                if (m >= M) continue;
+                const int64_t pos = ra.pos0 + m;
+                const int j = 32 * tp + c;
+                const float x1 = rsum(r, c), x2 = rsum(r, c + 32);
+                const float cs = ra.cos_t[pos * half + j], sn = ra.sin_t[pos * half + j];
+                bf16_t* dst = base + (size_t)(head < ra.Hq ? m : pos) * D;
+                dst[j] = f32_to_bf16(x1 * cs - x2 * sn);
+                dst[j + half] = f32_to_bf16(x2 * cs + x1 * sn);
+            }
+        } else {
+            const int hv = head - ra.Hq - ra.Hkv;
+            for (int e = threadIdx.x; e < 16 * kDenseMT * kTileN; e += kDenseThreads) {
+                const int r = e & (16 * kDenseMT - 1), c = e / (16 * kDenseMT);   // lanes along positions
+                const int m = m0 + r;
+                if (m >= M) continue;
+                const int dim = c < 32 ? 32 * tp + c : half + 32 * tp + (c - 32);
+                ((bf16_t*)ra.vc)[vt_index(hv, dim, ra.pos0 + m, D, ra.kv_rows)] = f32_to_bf16(rsum(r, c));
+            }
+        }
+        return;
+    }
     float* Cz = C + (size_t)blockIdx.z * M * ldc;
     for (int e = threadIdx.x; e < 16 * kDenseMT * kTileN; e += kDenseThreads) {
         const int r = e >> 6, c = e & 63;
@@ -911,17 +952,24 @@ hipError_t launch_pack_afrag(const void* A, int M, int K, void* Af, hipStream_t 
 }
 
 hipError_t launch_gemm_frag(int epi, const void* Af, int M, const void* B, int K, int N, float* C,
-                            int ldc, hipStream_t s, int ksplit) {
+                            int ldc, hipStream_t s, int ksplit, const RopeArgs* rope) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if ((K & 31) || (N % kTileN) || ksplit < 1 || (ksplit > 1 && epi != kEpiStoreF32))
         return hipErrorInvalidValue;
     dim3 grid(N / kTileN, (M + 16 * kDenseMT - 1) / (16 * kDenseMT), ksplit);
-    if (epi == kEpiStoreF32)
+    const RopeArgs ra = rope ? *rope : RopeArgs{};
+    if (epi == kEpiRope) {
+        if (!rope || ksplit != 1 || N != (ra.Hq + 2 * ra.Hkv) * 128 || !ra.q || !ra.kc || !ra.vc)
+            return hipErrorInvalidValue;
+        k_dense_frag<kEpiRope><<<grid, kDenseThreads, 0, s>>>((const uint8_t*)Af, M, (const bf16_t*)B,
+                                                          K, N, C, ldc, ra);
+    } else if (epi == kEpiStoreF32) {
         k_dense_frag<kEpiStoreF32><<<grid, kDenseThreads, 0, s>>>((const uint8_t*)Af, M, (const bf16_t*)B,
-                                                              K, N, C, ldc);
-    else
+                                                              K, N, C, ldc, ra);
+    } else {
         k_dense_frag<kEpiAddF32><<<grid, kDenseThreads, 0, s>>>((const uint8_t*)Af, M, (const bf16_t*)B,
-                                                            K, N, C, ldc);
+                                                            K, N, C, ldc, ra);
+    }
     return hipGetLastError();
 }
 

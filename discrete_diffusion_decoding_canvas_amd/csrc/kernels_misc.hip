@@ -402,14 +402,23 @@ __global__ __launch_bounds__(1024) void k_sampler(const float* __restrict__ conf
 // src [K][N] (SRC_KN) or [N][K] (!SRC_KN), 16-bit elements -> packed B operand.
 // The destination column group of source group g is g * gstride + goff (the
 // gate / up interleave of the first expert GEMM uses gstride 2).
+// Pair-tiled group order of a 128-column head: group gi (dims 16 gi ..) goes to
+// group 4 ((gi % 4) / 2) + 2 (gi / 4) + gi % 2, so tile t (groups 4t..4t+3) holds
+// dims 32t..32t+31 and their rotary partners 64 + 32t..64 + 32t + 31.
+DG_DEV int64_t rope_pair_group(int64_t g) {
+    const int64_t gi = g & 7;
+    return (g & ~(int64_t)7) + 4 * ((gi & 3) >> 1) + 2 * (gi >> 2) + (gi & 1);
+}
+
 template <bool SRC_KN>
 __global__ void k_pack_b16(const uint16_t* __restrict__ src, int K, int N, int gstride, int goff,
-                           uint16_t* __restrict__ dst) {
+                           uint16_t* __restrict__ dst, int rope_hd) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)K * N) return;
     int64_t n, kk;
     if (SRC_KN) { kk = idx / N; n = idx % N; } else { n = idx / K; kk = idx % K; }
-    const int64_t dn = ((n >> 4) * gstride + goff) * 16 + (n & 15);
+    const int64_t g = rope_hd == 128 ? rope_pair_group(n >> 4) : (n >> 4);
+    const int64_t dn = (g * gstride + goff) * 16 + (n & 15);
     dst[packed_b_index(dn, kk, K)] = src[idx];
 }
 
@@ -595,15 +604,17 @@ hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t*
 }
 
 hipError_t launch_pack_b16(const void* src, bool src_kn, int K, int N, int gstride, int goff,
-                           void* dst, hipStream_t s) {
+                           void* dst, hipStream_t s, int rope_hd) {
+    if (rope_hd != 0 && (rope_hd != 128 || N % 128 != 0 || gstride != 1 || goff % 8 != 0))
+        return hipErrorInvalidValue;
     int64_t total = (int64_t)K * N;
     unsigned blocks = (unsigned)((total + 255) / 256);
     if (src_kn)
         k_pack_b16<true><<<blocks, 256, 0, s>>>((const uint16_t*)src, K, N, gstride, goff,
-                                                (uint16_t*)dst);
+                                                (uint16_t*)dst, rope_hd);
     else
         k_pack_b16<false><<<blocks, 256, 0, s>>>((const uint16_t*)src, K, N, gstride, goff,
-                                                 (uint16_t*)dst);
+                                                 (uint16_t*)dst, rope_hd);
     LAUNCH_CHECK();
 }
 
