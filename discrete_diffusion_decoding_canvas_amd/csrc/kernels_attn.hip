@@ -16,9 +16,11 @@
 //   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16, A = K rows, B = Q rows) puts the
 //   scores of one query in one lane column, so the online-softmax statistics
 //   and the rescale of the output stay lane-local;
-//   O^T = V^T P^T (A = V^T from the transposed, key-permuted V cache, B = P
-//   taken straight from the score registers), with P split into hi + lo bf16
-//   parts so the softmax weights keep ~16 significant bits.
+//   O^T = V^T P^T (v_mfma_f32_16x16x32_f16: A = V^T from the transposed,
+//   key-permuted bf16 V cache, converted to binary16 in LDS by the V producer
+//   wave, exact; B = P taken straight from the score registers, rounded to
+//   binary16: 11 significant bits, against 8 for bf16; the causal encoder, whose
+//   K/V persist in the cache, adds the remainder as a second binary16 part).
 // Softmax runs in fp32 in the log2 domain: the running max is kept on raw
 // scores and each exponent scale*log2(e)*(s - m) is one fma ahead of exp2.
 #include <type_traits>
@@ -37,6 +39,7 @@ static_assert(kAttnRing >= 3, "two blocks ahead of the one being consumed");
 union AFrag {
     uint4 u;
     bf16x8_t b;
+    f16x8_t f;
     uint16_t h[8];
 };
 
@@ -60,9 +63,61 @@ constexpr int attn_vmcnt_le(int n) {
     return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
-DG_DEV void dma16(const bf16_t* src, uint4* dst) {
+DG_DEV void dma16(const uint16_t* src, uint4* dst) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// The V^T fragments of one ring slot, bf16 as copied from the cache, rewritten
+// in place as binary16 (the PV MFMA's operand type) by the V producer wave once
+// its copies of the block have landed.  bf16 values in binary16's normal range
+// convert exactly (round toward zero only trims values below 2^-14 and clamps
+// magnitudes above 65504).  LDS is read and written in inline asm so that the
+// compiler does not wait for this wave's later copies in flight.
+typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
+
+DG_DEV uint32_t bf16x2_to_f16x2(uint32_t w) {
+    const half2_t h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+typedef unsigned int v4u32_t __attribute__((ext_vector_type(4)));
+
+DG_DEV void convert_v_slot(uint4 (*v)[64], int lane) {
+    const uint32_t addr = (uint32_t)(uintptr_t)&v[0][lane];
+    v4u32_t f[8];
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:1024\n"
+        "ds_read_b128 %2, %8 offset:2048\n"
+        "ds_read_b128 %3, %8 offset:3072\n"
+        "ds_read_b128 %4, %8 offset:4096\n"
+        "ds_read_b128 %5, %8 offset:5120\n"
+        "ds_read_b128 %6, %8 offset:6144\n"
+        "ds_read_b128 %7, %8 offset:7168\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
+          "=&v"(f[6]), "=&v"(f[7])
+        : "v"(addr)
+        : "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        f[i] = v4u32_t{bf16x2_to_f16x2(f[i].x), bf16x2_to_f16x2(f[i].y), bf16x2_to_f16x2(f[i].z),
+                       bf16x2_to_f16x2(f[i].w)};
+    asm volatile(
+        "ds_write_b128 %0, %1\n"
+        "ds_write_b128 %0, %2 offset:1024\n"
+        "ds_write_b128 %0, %3 offset:2048\n"
+        "ds_write_b128 %0, %4 offset:3072\n"
+        "ds_write_b128 %0, %5 offset:4096\n"
+        "ds_write_b128 %0, %6 offset:5120\n"
+        "ds_write_b128 %0, %7 offset:6144\n"
+        "ds_write_b128 %0, %8 offset:7168\n"
+        "s_waitcnt lgkmcnt(0)"
+        :
+        : "v"(addr), "v"(f[0]), "v"(f[1]), "v"(f[2]), "v"(f[3]), "v"(f[4]), "v"(f[5]), "v"(f[6]),
+          "v"(f[7])
+        : "memory");
 }
 
 // 2^x with the hardware exponential; results below the smallest normal flush to
@@ -142,13 +197,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
             }
         };
         // The consumers read K of block b + 1 and V of block b in iteration b, so before
-        // the barrier that opens iteration b the blocks up to b + 1 must have landed.
+        // the barrier that opens iteration b the blocks up to b + 1 must have landed and
+        // the V of block b must be in binary16.
         for (int b = 0; b < kAttnRing - 1; ++b) issue(b);
         __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(8 * (kAttnRing - 3)));   // blocks 0, 1 landed
+        if (is_v && n_blocks > 0) convert_v_slot(ring[0].v, lane);
         attn_bare_barrier();
         for (int b = 0; b < n_blocks; ++b) {
             issue(b + kAttnRing - 1);                                   // into the slot of block b - 1
             __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(8 * (kAttnRing - 3)));   // block b + 2 landed
+            if (is_v && b + 1 < n_blocks) convert_v_slot(ring[(b + 1) % kAttnRing].v, lane);
             attn_bare_barrier();
         }
         __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(0));
@@ -231,6 +289,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                 }
             }
         }
+        // P in binary16 (round to nearest even; p < 2^9).  The causal encoder, whose K/V
+        // stay in the cache for every later pass, adds the rounding remainder as a second
+        // binary16 part (about 22 significant bits); a decoder pass uses one part.
         AFrag pf[2], pl[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -240,21 +301,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
             for (int i = 0; i < 8; ++i) {
                 const float p = fast_exp2(fmaf(score(qb, i >> 2, i & 3), scale_log2, nb));
                 psum += p;
-                const __bf16 hi = (__bf16)p;                 // round to nearest even
-                pf[qb].b[i] = hi;
-                pl[qb].b[i] = (__bf16)(p - (float)hi);
+                const _Float16 hi = (_Float16)p;
+                pf[qb].f[i] = hi;
+                if (CAUSAL) pl[qb].f[i] = (_Float16)(p - (float)hi);
             }
             l_run[qb] += psum;
         }
-        // O^T += V^T P^T, hi parts then lo parts
+        // O^T += V^T P^T (the V cache is binary16)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             AFrag vf;
             vf.u = sl.v[dt][lane];
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.b, pf[qb].b, o[qb][dt], 0, 0, 0);
-                o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.b, pl[qb].b, o[qb][dt], 0, 0, 0);
+                o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f, pf[qb].f, o[qb][dt], 0, 0, 0);
+                if (CAUSAL)
+                    o[qb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf.f, pl[qb].f, o[qb][dt], 0, 0, 0);
             }
         }
     };

@@ -133,59 +133,42 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
 }
 
 // ------------------------------------------------------------------ RoPE + scatter
-// qkv float [M, (Hq + 2 Hkv) D] -> Q [Hq][M][D] rotated, K cache rows pos0+m rotated,
-// V cache rows pos0+m.  Rotate-half pairs (j, j + D/2), angle table [pos][D/2].
-// bf16 V is stored transposed and key-permuted for the attention MFMA (vt_index).
-// One block per (32 tokens, head): Q and K rows are written along j; a V head
-// goes through LDS so that its transposed stores run along the positions
-// (32 consecutive positions of one dimension are one 64-byte run).
+// f32 path: qkv [M, (Hq + 2 Hkv) D] -> Q [Hq][M][D] rotated, K cache rows pos0+m
+// rotated, V cache rows pos0+m.  Rotate-half pairs (j, j + D/2), angle table
+// [pos][D/2].  One block per (32 tokens, head).  (The bf16 path rotates in the
+// QKV GEMM's epilogue.)
 constexpr int kRopeTokens = 32;
 
-template <typename T, bool VPACKED, int D>
+template <int D>
 __global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ qkv, int M, int Hq,
                                                       int Hkv, int64_t pos0,
                                                       const float* __restrict__ cos_t,
                                                       const float* __restrict__ sin_t,
-                                                      T* __restrict__ q, T* __restrict__ kc,
-                                                      T* __restrict__ vc, int64_t kv_rows) {
-    __shared__ float vt[kRopeTokens][D + 1];
+                                                      float* __restrict__ q, float* __restrict__ kc,
+                                                      float* __restrict__ vc, int64_t kv_rows) {
     const int m0 = blockIdx.x * kRopeTokens;
     const int head = blockIdx.y;             // 0..Hq-1 queries, Hq..Hq+Hkv-1 keys, then values
     constexpr int half = D >> 1;
     const int64_t ld = (int64_t)(Hq + 2 * Hkv) * D;
     const int nt = min(kRopeTokens, M - m0);
-    if (head < Hq + Hkv || !VPACKED) {
-        for (int e = threadIdx.x; e < nt * half; e += 256) {
-            const int mi = e / half, j = e - mi * half;
-            const int m = m0 + mi;
-            const int64_t pos = pos0 + m;
-            const float* src = qkv + (int64_t)m * ld + (int64_t)head * D;
-            const float x1 = src[j], x2 = src[j + half];
-            if (head < Hq + Hkv) {
-                const float c = cos_t[pos * half + j], sn = sin_t[pos * half + j];
-                const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
-                T* dst = head < Hq ? q + ((int64_t)head * M + m) * D
+    for (int e = threadIdx.x; e < nt * half; e += 256) {
+        const int mi = e / half, j = e - mi * half;
+        const int m = m0 + mi;
+        const int64_t pos = pos0 + m;
+        const float* src = qkv + (int64_t)m * ld + (int64_t)head * D;
+        const float x1 = src[j], x2 = src[j + half];
+        if (head < Hq + Hkv) {
+            const float c = cos_t[pos * half + j], sn = sin_t[pos * half + j];
+            const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+            float* dst = head < Hq ? q + ((int64_t)head * M + m) * D
                                    : kc + ((int64_t)(head - Hq) * kv_rows + pos) * D;
-                dst[j] = from_f32<T>(y1);
-                dst[j + half] = from_f32<T>(y2);
-            } else {
-                T* dst = vc + ((int64_t)(head - Hq - Hkv) * kv_rows + pos) * D;
-                dst[j] = from_f32<T>(x1);
-                dst[j + half] = from_f32<T>(x2);
-            }
+            dst[j] = y1;
+            dst[j + half] = y2;
+        } else {
+            float* dst = vc + ((int64_t)(head - Hq - Hkv) * kv_rows + pos) * D;
+            dst[j] = x1;
+            dst[j + half] = x2;
         }
-        return;
-    }
-    // packed V: rows in along the dimensions, out along the positions
-    for (int e = threadIdx.x; e < nt * D; e += 256) {
-        const int mi = e / D, t = e - mi * D;
-        vt[mi][t] = qkv[(int64_t)(m0 + mi) * ld + (int64_t)head * D + t];
-    }
-    __syncthreads();
-    const int h = head - Hq - Hkv;
-    for (int e = threadIdx.x; e < kRopeTokens * D; e += 256) {
-        const int t = e / kRopeTokens, mi = e - t * kRopeTokens;
-        if (mi < nt) vc[vt_index(h, t, pos0 + m0 + mi, D, kv_rows)] = from_f32<T>(vt[mi][t]);
     }
 }
 
@@ -484,12 +467,12 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, vo
     LAUNCH_CHECK();
 }
 
-template <typename T, bool VPACKED, int D>
+template <int D>
 static void rope_d(const float* qkv, int M, int Hq, int Hkv, int64_t pos0, const float* cos_t,
                    const float* sin_t, void* q, void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
     dim3 grid((M + kRopeTokens - 1) / kRopeTokens, Hq + 2 * Hkv);
-    k_rope_scatter<T, VPACKED, D><<<grid, 256, 0, s>>>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, (T*)q,
-                                                       (T*)kc, (T*)vc, kv_rows);
+    k_rope_scatter<D><<<grid, 256, 0, s>>>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, (float*)q,
+                                           (float*)kc, (float*)vc, kv_rows);
 }
 
 hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int Hkv, int D,
@@ -497,12 +480,11 @@ hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int H
                                void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if (dtype == kF32) {
-        if (D == 64) rope_d<float, false, 64>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
-        else if (D == 128) rope_d<float, false, 128>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
+        if (D == 64) rope_d<64>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
+        else if (D == 128) rope_d<128>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
         else return hipErrorInvalidValue;
     } else {
-        if (D != 128) return hipErrorInvalidValue;
-        rope_d<bf16_t, true, 128>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
+        return hipErrorInvalidValue;   // bf16: RoPE runs in the QKV GEMM's epilogue (kEpiRope)
     }
     LAUNCH_CHECK();
 }
