@@ -438,7 +438,7 @@ constexpr int kWideWavesPerEU = kWideWaves / 4;     // one workgroup per CU: the
 constexpr int kCopies = 2 * kWideNT / kWideWaves;   // 1 KiB weight copies per wave per stage
 constexpr int kRing = DG_WIDE_RING;                 // LDS stages (2 kWideNT KiB each)
 #ifndef DG_WIDE_LEAD
-#define DG_WIDE_LEAD 3
+#define DG_WIDE_LEAD 1
 #endif
 constexpr int kWideLead = DG_WIDE_LEAD;             // activation stages loaded ahead per wave
 constexpr int kWideSlots = kWideLead + 1;
@@ -484,6 +484,26 @@ DG_DEV void wide_load_a(WideFrag& a, const uint8_t* const (&afrag)[kWideMT], int
 // the previous stage orders these reads after the copies they need.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kWideReadGroups = 8;   // column groups read per LDS round trip (a whole k-step)
+static_assert(kWideReadGroups == 4 || kWideReadGroups == 8, "");
+
+DG_DEV void lds_read8(u32x4_t (&f)[8], uint32_t addr) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:1024\n"
+        "ds_read_b128 %2, %8 offset:2048\n"
+        "ds_read_b128 %3, %8 offset:3072\n"
+        "ds_read_b128 %4, %8 offset:4096\n"
+        "ds_read_b128 %5, %8 offset:5120\n"
+        "ds_read_b128 %6, %8 offset:6144\n"
+        "ds_read_b128 %7, %8 offset:7168\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
+          "=&v"(f[6]), "=&v"(f[7])
+        : "v"(addr)
+        : "memory");
+}
+
 DG_DEV void lds_read4(u32x4_t (&f)[4], uint32_t addr) {
     asm volatile(
         "ds_read_b128 %0, %4\n"
@@ -495,6 +515,9 @@ DG_DEV void lds_read4(u32x4_t (&f)[4], uint32_t addr) {
         : "v"(addr)
         : "memory");
 }
+
+DG_DEV void lds_read_groups(u32x4_t (&f)[4], uint32_t addr) { lds_read4(f, addr); }
+DG_DEV void lds_read_groups(u32x4_t (&f)[8], uint32_t addr) { lds_read8(f, addr); }
 
 // Both k-steps of a stage, straight-line.  When K has an odd number of packed
 // k-steps the last stage's second k-step is multiplied by a zeroed activation
@@ -514,18 +537,18 @@ DG_DEV void wide_mma(WideAcc& acc, const WideFrag& a, const uint4 (*bs)[kWideNT]
             }
         }
 #pragma unroll
-        for (int n4 = 0; n4 < kWideNT; n4 += 4) {
-            Frag16 fb[4];
+        for (int n4 = 0; n4 < kWideNT; n4 += kWideReadGroups) {
+            Frag16 fb[kWideReadGroups];
             {
-                u32x4_t f[4];
-                lds_read4(f, (uint32_t)(uintptr_t)&bs[ks][n4][lane]);
+                u32x4_t f[kWideReadGroups];
+                lds_read_groups(f, (uint32_t)(uintptr_t)&bs[ks][n4][lane]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) fb[i].u = uint4{f[i].x, f[i].y, f[i].z, f[i].w};
+                for (int i = 0; i < kWideReadGroups; ++i) fb[i].u = uint4{f[i].x, f[i].y, f[i].z, f[i].w};
             }
 #pragma unroll
             for (int mt = 0; mt < kWideMT; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < kWideReadGroups; ++i) {
                     f32x4_t& c = acc[mt][n4 + i];
                     if (FP8) {
                         c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(am[mt].l.lo, fb[i].l.lo, c, 0, 0, 0);
