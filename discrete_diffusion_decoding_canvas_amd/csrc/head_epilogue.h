@@ -42,7 +42,13 @@ DG_DEV void run_merge(Run& x, float ym, int32_t ya, float ys, float yg, int32_t 
     if (yg > x.g || (yg == x.g && ygi < x.gi)) { x.g = yg; x.gi = ygi; }
 }
 
-DG_DEV float gumbel_of(uint32_t w) { return -logf(-logf(philox_open_uniform(w))); }
+// Gumbel noise G = -ln(-ln u) from the hardware base-2 logarithm: u >= 2^-24 and
+// -ln u >= 2^-24 are normal floats, so no denormal scaling is needed.
+DG_DEV float gumbel_of(uint32_t w) {
+    constexpr float kLn2 = 0.69314718055994531f;
+    const float t = -__builtin_amdgcn_logf(philox_open_uniform(w)) * kLn2;   // -ln u > 0
+    return -__builtin_amdgcn_logf(t) * kLn2;
+}
 
 struct EpiArgs {
     int C, V, v0, rbase, g, l16;
@@ -53,11 +59,15 @@ struct EpiArgs {
     float* logits_out;
 };
 
-// Epilogue of one 16-row fragment group MT of a wave's 64 x 128 tile: each lane
-// folds its 8 columns for its 4 rows, then the 16 lanes sharing the rows merge.
-// MT is a template argument so that every accumulator index is static.
+// Epilogue of one 16-row fragment group MT of a wave's 16 x 128 tile: each lane
+// holds 8 columns (ids v0 + 16 nt + l16, increasing with nt) of 4 rows.  Per row it
+// takes the maximum and its first id and the Gumbel best in one pass over the 8
+// columns, then the sum of exp(z - max) in a second (one exponential per element);
+// the 16 lanes sharing the rows then merge.  MT is a template argument so that
+// every accumulator index is static.
 template <int MT>
 DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
+    constexpr float kLog2e = 1.4426950408889634f;
     const int r4 = e.rbase + 16 * MT + 4 * e.g;      // rows r4 .. r4+3 in this lane
     bool unl[4];
     bool any = false;
@@ -66,9 +76,15 @@ DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
         unl[j] = (r4 + j < e.C) && e.mask[r4 + j] == 0;
         any |= unl[j];
     }
-    Run run[4];
+    float m[4], g[4];
+    int am[4], ag[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) run[j] = Run{-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff};
+    for (int j = 0; j < 4; ++j) {
+        m[j] = -INFINITY;
+        g[j] = -INFINITY;
+        am[j] = 0;
+        ag[j] = -1;
+    }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         const int v = e.v0 + 16 * nt + e.l16;
@@ -77,21 +93,28 @@ DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
                                     e.key0, e.key1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t word = j == 0 ? rw.x : j == 1 ? rw.y : j == 2 ? rw.z : rw.w;
             const float z = acc[nt][j] * e.inv_tau;
             if (e.logits_out != nullptr && r4 + j < e.C) e.logits_out[(size_t)(r4 + j) * e.V + v] = z;
-            if (z > run[j].m) {
-                run[j].s = (run[j].m == -INFINITY ? 0.f : run[j].s * __expf(run[j].m - z)) + 1.f;
-                run[j].m = z;
-                run[j].a = v;
-            } else {
-                run[j].s += __expf(z - run[j].m);
-            }
+            if (z > m[j]) { m[j] = z; am[j] = nt; }
             if (unl[j]) {
+                const uint32_t word = j == 0 ? rw.x : j == 1 ? rw.y : j == 2 ? rw.z : rw.w;
                 const float gs = z + gumbel_of(word);
-                if (gs > run[j].g) { run[j].g = gs; run[j].gi = v; }
+                if (gs > g[j]) { g[j] = gs; ag[j] = nt; }
             }
         }
+    }
+    Run run[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float s = 0.f;
+        if (m[j] != -INFINITY) {
+            const float mb = m[j] * kLog2e;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                s += __builtin_amdgcn_exp2f(fmaf(acc[nt][j] * e.inv_tau, kLog2e, -mb));
+        }
+        run[j] = Run{m[j], m[j] == -INFINITY ? 0x7fffffff : e.v0 + 16 * am[j] + e.l16, s, g[j],
+                     ag[j] < 0 ? 0x7fffffff : e.v0 + 16 * ag[j] + e.l16};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
