@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm
                                                     float* __restrict__ st_conf,
                                                     int32_t* __restrict__ st_draw,
                                                     int32_t* __restrict__ bad) {
-    __shared__ HeadPart sh[256];
+    __shared__ HeadPart sh[4];
     const int row = blockIdx.x;
     HeadPart acc = {-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff};
     for (int i = threadIdx.x; i < n_slices; i += 256) {
@@ -318,18 +318,19 @@ __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm
         HeadPart p = {pm[o], pa[o], ps[o], pg[o], pgi[o]};
         head_merge(acc, p);
     }
-    sh[threadIdx.x] = acc;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (threadIdx.x < w) {
-            HeadPart a = sh[threadIdx.x];
-            head_merge(a, sh[threadIdx.x + w]);
-            sh[threadIdx.x] = a;
-        }
-        __syncthreads();
+    // within each wave by shuffles, then the four waves in order
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const HeadPart y = {__shfl_xor(acc.m, o, 64), __shfl_xor(acc.a, o, 64), __shfl_xor(acc.s, o, 64),
+                            __shfl_xor(acc.g, o, 64), __shfl_xor(acc.gi, o, 64)};
+        head_merge(acc, y);
     }
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
+    __syncthreads();
     if (threadIdx.x == 0) {
         HeadPart r = sh[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) head_merge(r, sh[w]);
         const float ls = logf(r.s);
         st_m[row] = r.m;
         st_a[row] = r.a;
@@ -350,16 +351,17 @@ __global__ __launch_bounds__(1024) void k_sampler(const float* __restrict__ conf
                                                   int32_t* __restrict__ canvas,
                                                   uint8_t* __restrict__ mask, int C, int step,
                                                   int T) {
-    __shared__ float cf[kMaxCanvas];
-    __shared__ uint8_t un[kMaxCanvas];
+    __shared__ __attribute__((aligned(16))) float cf[kMaxCanvas];
+    __shared__ __attribute__((aligned(16))) uint8_t un[kMaxCanvas];
     __shared__ int n_unl;
     if (threadIdx.x == 0) n_unl = 0;
     __syncthreads();
     int mine = 0;
-    for (int i = threadIdx.x; i < C; i += blockDim.x) {
-        cf[i] = conf[i];
-        un[i] = mask[i] == 0;
-        mine += un[i];
+    for (int i = threadIdx.x; i < (C + 3) / 4 * 4; i += blockDim.x) {   // tail padded locked
+        const bool u = i < C && mask[i] == 0;
+        cf[i] = i < C ? conf[i] : 0.f;
+        un[i] = u;
+        mine += u;
     }
     atomicAdd(&n_unl, mine);
     __syncthreads();
@@ -370,8 +372,17 @@ __global__ __launch_bounds__(1024) void k_sampler(const float* __restrict__ conf
         if (!un[i]) continue;
         const float ci = cf[i];
         int rank = 0;
-        for (int j = 0; j < C; ++j)
-            rank += un[j] && (cf[j] > ci || (cf[j] == ci && j < i));
+        // four positions per LDS read, 16 per unrolled step
+#pragma unroll 4
+        for (int j4 = 0; j4 < (C + 3) / 4; ++j4) {
+            const float4 c = reinterpret_cast<const float4*>(cf)[j4];
+            const uchar4 u = reinterpret_cast<const uchar4*>(un)[j4];
+            const int j = 4 * j4;
+            rank += u.x && (c.x > ci || (c.x == ci && j < i));
+            rank += u.y && (c.y > ci || (c.y == ci && j + 1 < i));
+            rank += u.z && (c.z > ci || (c.z == ci && j + 2 < i));
+            rank += u.w && (c.w > ci || (c.w == ci && j + 3 < i));
+        }
         if (rank < n_s) {
             canvas[i] = amax[i];
             mask[i] = 1;
