@@ -30,7 +30,8 @@ the oracle is "parity unpinned" against the pages; it is pinned piece by piece.
 """
 from .numerics import (round_bf16, e4m3_round, e4m3_value_of_code, rmsnorm, rope,
                        softmax, silu)
-from .philox import philox4x32_10, init_canvas, gumbel_uniforms
+from .philox import philox4x32_10, init_canvas, gumbel_uniforms, renoise_tokens
+from . import eb_sampler
 from .model import (OracleModel, attention, route_topk, moe_ffn, lm_head_stats,
                     sampler_update, lock_count, gumbel_noise)
 
@@ -38,4 +39,5 @@ __all__ = [
     "round_bf16", "e4m3_round", "e4m3_value_of_code", "rmsnorm", "rope", "softmax", "silu",
     "philox4x32_10", "init_canvas", "gumbel_uniforms", "OracleModel", "attention",
     "route_topk", "moe_ffn", "lm_head_stats", "sampler_update", "lock_count", "gumbel_noise",
+    "renoise_tokens", "eb_sampler",
 ]

@@ -61,6 +61,7 @@ import numpy as np
 
 from .numerics import rmsnorm, rope, round_bf16, e4m3_round, softmax, silu
 from .philox import init_canvas, gumbel_uniforms
+from . import eb_sampler as eb
 
 
 # =========================================================================== pieces
@@ -375,6 +376,57 @@ class OracleModel:
                           route_idx=[r[0] for r in routes], route_gates=[r[1] for r in routes],
                           route_margin=[r[2] for r in routes],
                           logits=z if keep_logits else None, hidden=hidden)
+
+    def _draws(self, z, mask, s: int, seed: int):
+        C = z.shape[0]
+        redraw = np.full(C, -1, np.int32)
+        gap = np.full(C, np.nan)
+        unlocked = np.flatnonzero(np.asarray(mask) == 0)
+        chunk = max(1, (1 << 24) // self.w.vocab)
+        for c0 in range(0, unlocked.size, chunk):
+            pos = unlocked[c0:c0 + chunk]
+            u = gumbel_uniforms(seed, self.k_blk, s, pos, self.w.vocab)
+            redraw[pos], gap[pos] = gumbel_draw(z[pos], u)
+        return redraw, gap
+
+    def denoise_step_eb(self, canvas, mask, prev_argmax, s: int, p, seed: int,
+                        keep_logits=False):
+        """One pass of the entropy-bounded sampler (``eb_sampler``): logits tempered at
+        tau_s, per-position entropy, Gumbel draws for unlocked positions, then the update.
+        Returns (StepResult, EbResult, entropies)."""
+        logits, routes, _ = self.decoder_logits(canvas)
+        z = logits / eb.tau_at(s, p)
+        st = lm_head_stats(z)
+        H = eb.entropy(z)
+        redraw, gap = self._draws(z, mask, s, seed)
+        er = eb.eb_update(canvas, mask, H, st.argmax, redraw, prev_argmax, s, p, seed,
+                          self.k_blk, self.w.vocab)
+        res = StepResult(canvas=er.canvas, mask=er.mask, stats=st, redraw=redraw,
+                         redraw_gap=gap, sampler=None,
+                         route_idx=[r[0] for r in routes], route_gates=[r[1] for r in routes],
+                         route_margin=[r[2] for r in routes],
+                         logits=z if keep_logits else None)
+        return res, er, H
+
+    def generate_block_eb(self, p, seed: int, commit: bool = True, on_step=None):
+        """Passes of the entropy-bounded sampler until it ends the block; returns
+        (canvas, number of passes)."""
+        w = self.w
+        canvas = init_canvas(seed, self.k_blk, w.canvas, w.vocab)
+        mask = np.zeros(w.canvas, np.uint8)
+        prev = None
+        n = 0
+        for s in range(p.max_steps):
+            res, er, H = self.denoise_step_eb(canvas, mask, prev, s, p, seed)
+            if on_step is not None:
+                on_step(s, canvas, mask, res, er, H)
+            canvas, mask, prev = er.canvas, er.mask, res.stats.argmax
+            n = s + 1
+            if er.done:
+                break
+        if commit:
+            self.commit(canvas)
+        return canvas, n
 
     def generate_block(self, T: int, seed: int, commit: bool = True, on_step=None):
         w = self.w

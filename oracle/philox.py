@@ -1,4 +1,4 @@
-"""Philox4x32-10 and the two random streams the sampler draws.
+"""Philox4x32-10 and the random streams the samplers draw.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -8,6 +8,10 @@ Philox4x32-10 follows its published definition (Salmon, Moraes, Dror & Shaw,
 round constants, keeps high and low halves, XORs the high halves with the
 other counter words and the round key, and bumps the key by the two Weyl
 constants between rounds.
+
+The entropy-bounded sampler renoises the positions it does not accept
+"uniformly at random" ([TR] Method, the paragraph after the update equations),
+which is the third stream.
 
 The pages ask for canvas tokens "initialised with random placeholder tokens"
 ([AS] "How text diffusion actually works", step 1; [TR] Method, forward
@@ -19,6 +23,8 @@ is this implementation's reading (the pages fix none):
                 token = (word * V) >> 32           (multiply-high)
   redraw      : counter (v, i >> 2, s | k_blk << 16, 0x47554D42), word i & 3;
                 u = (2 * (word >> 9) + 1) * 2^-24    (exact float in (0, 1))
+  renoise     : counter (i >> 2, k_blk, s, 0x524E5345), output word i & 3;
+                token = (word * V) >> 32           (multiply-high)
 key = (seed & 0xffffffff, seed >> 32).  i = canvas position, v = vocabulary
 id, s = pass index, k_blk = index of the canvas within the generation.
 """
@@ -34,6 +40,7 @@ MASK32 = np.uint64(0xFFFFFFFF)
 
 INIT_TAG = 0x494E4954
 GUMBEL_TAG = 0x47554D42
+RENOISE_TAG = 0x524E5345
 
 
 def philox4x32_10(c0, c1, c2, c3, k0, k1):
@@ -80,3 +87,11 @@ def gumbel_uniforms(seed: int, k_blk: int, s: int, positions, V: int, v0: int = 
     lane = np.broadcast_to((pos & np.uint64(3)).astype(np.int64), w[0].shape)
     word = _word(w, lane)
     return ((word >> np.uint32(9)).astype(np.float64) * 2.0 + 1.0) * 2.0 ** -24
+
+
+def renoise_tokens(seed: int, k_blk: int, s: int, C: int, V: int) -> np.ndarray:
+    """Uniform token over [0, V) for every canvas position at pass s (entropy-bounded sampler)."""
+    i = np.arange(C, dtype=np.uint64)
+    w = philox4x32_10(i >> np.uint64(2), k_blk, s, RENOISE_TAG, seed & 0xFFFFFFFF, seed >> 32)
+    word = _word(w, (i & np.uint64(3)).astype(np.int64))
+    return ((word.astype(np.uint64) * np.uint64(V)) >> np.uint64(32)).astype(np.int32)

@@ -114,3 +114,34 @@ def test_block_schedule_invariants_tiny_fp32_workload():
     # mean tokens fixed per pass 256/12 ~ 21.3, close to the reported ~20 per forward
     assert abs(np.mean(seen) - 256 / 12) < 1e-9
     assert out.shape == (w.canvas,)
+
+
+def test_entropy_bounded_block_invariants_tiny_fp32_workload():
+    from oracle import eb_sampler as eb
+    from oracle.philox import renoise_tokens
+    w = fx.TINY_FP32
+    m = om.OracleModel(w, FixtureWeights(w))
+    m.prefill(fx.prompt_ids(w))
+    p = eb.EbParams(gamma=30.0, theta=0.0, max_steps=12)
+    seen = []
+
+    def cb(s, canvas, mask, res, er, H):
+        locked = mask == 1
+        assert np.array_equal(er.canvas[locked], canvas[locked])
+        assert np.all((H >= 0) & (H <= np.log(w.vocab) + 1e-9))
+        new = er.mask.astype(bool) & ~locked
+        if not er.done:
+            assert er.n_accept >= 1 and set(np.flatnonzero(new)) == set(er.accepted.tolist())
+            assert np.array_equal(er.canvas[new], res.redraw[new])
+            rest = ~er.mask.astype(bool)
+            assert np.array_equal(er.canvas[rest], renoise_tokens(w.seed, 0, s, w.canvas,
+                                                                  w.vocab)[rest])
+            # the accepted set is a prefix of the entropy order whose bound stays below gamma
+            assert eb.mi_bound(H[er.accepted]) < p.gamma
+            if er.n_accept < er.order.size:
+                assert eb.mi_bound(H[er.order[:er.n_accept + 1]]) >= p.gamma
+        seen.append(int(new.sum()))
+
+    out, n = m.generate_block_eb(p, w.seed, commit=False, on_step=cb)
+    assert n == len(seen) <= p.max_steps and sum(seen) == w.canvas
+    assert np.all((out >= 0) & (out < w.vocab))
