@@ -19,13 +19,15 @@ DG_ETOKEN = -7
 DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
 DG_T_EMBED, DG_T_WQ, DG_T_WK, DG_T_WV, DG_T_WO, DG_T_WR, DG_T_WG, DG_T_WU, DG_T_WD = range(9)
 DG_CAP_LOGITS, DG_CAP_STATS, DG_CAP_ROUTING, DG_CAP_HIDDEN, DG_CAP_ATTN, DG_CAP_ROUTER_LOGITS = 1, 2, 4, 8, 16, 32
+DG_CAP_ENTROPY = 64
 
 EXPORTED = (
     "dg_create", "dg_destroy", "dg_last_error", "dg_load_tensor", "dg_prefill_prompt_kv",
     "dg_denoise_step", "dg_generate_block", "dg_commit_canvas", "dg_check_finite",
     "dg_reset_context", "dg_get_state", "dg_get_capture", "dg_get_kv", "dg_attention",
     "dg_moe_layer", "dg_init_canvas", "dg_profile_begin", "dg_profile_end", "dg_set_kv",
-    "dg_set_capture", "dg_set_graphs",
+    "dg_set_capture", "dg_set_graphs", "dg_eb_sample", "dg_denoise_step_eb",
+    "dg_generate_block_eb",
 )
 DG_PROF_MOE_GEMM1, DG_PROF_MOE_GEMM2, DG_PROF_ATTENTION, DG_PROF_LM_HEAD, DG_PROF_DENSE = range(5)
 DG_PROF_N = 5
@@ -48,6 +50,17 @@ class dg_model_cfg(ctypes.Structure):
         ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
         ("capture_mask", ctypes.c_uint32),
     ]
+
+
+class dg_eb_params(ctypes.Structure):
+    _fields_ = [
+        ("tau_max", ctypes.c_float), ("tau_min", ctypes.c_float), ("gamma", ctypes.c_float),
+        ("theta", ctypes.c_float), ("max_steps", ctypes.c_int32),
+    ]
+
+
+def eb_params(tau_max=0.8, tau_min=0.4, gamma=0.5, theta=0.1, max_steps=48) -> dg_eb_params:
+    return dg_eb_params(tau_max, tau_min, gamma, theta, max_steps)
 
 
 def _load_library():
@@ -80,6 +93,11 @@ def _load_library():
         "dg_init_canvas": ([vp, vp, vp, u64, vp], i32),
         "dg_profile_begin": ([vp, i32], i32),
         "dg_profile_end": ([vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], i32),
+        "dg_eb_sample": ([vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                          ctypes.POINTER(dg_eb_params), u64, i32, vp], i32),
+        "dg_denoise_step_eb": ([vp, vp, vp, i32, ctypes.POINTER(dg_eb_params), u64, vp, vp], i32),
+        "dg_generate_block_eb": ([vp, vp, ctypes.POINTER(dg_eb_params), u64, i32,
+                                  ctypes.POINTER(i32), vp], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -157,6 +175,29 @@ def dg_generate_block(h, d_out_tokens, T: int, seed: int, commit: bool = True,
                       stream=None) -> None:
     _check(_lib.dg_generate_block(h, _ptr(d_out_tokens), T, seed, int(bool(commit)),
                                   _stream(stream)))
+
+
+def dg_eb_sample(d_entropy, d_argmax, d_draw, d_prev_argmax, d_canvas, d_locked_mask, d_info,
+                 C: int, V: int, step: int, params: dg_eb_params, seed: int, k_blk: int,
+                 stream=None) -> None:
+    _check(_lib.dg_eb_sample(_ptr(d_entropy), _ptr(d_argmax), _ptr(d_draw), _ptr(d_prev_argmax),
+                             _ptr(d_canvas), _ptr(d_locked_mask), _ptr(d_info), C, V, step,
+                             ctypes.byref(params), seed, k_blk, _stream(stream)))
+
+
+def dg_denoise_step_eb(h, d_canvas, d_locked_mask, step: int, params: dg_eb_params, seed: int,
+                       d_info=None, stream=None) -> None:
+    _check(_lib.dg_denoise_step_eb(h, _ptr(d_canvas), _ptr(d_locked_mask), step,
+                                   ctypes.byref(params), seed, _ptr(d_info), _stream(stream)))
+
+
+def dg_generate_block_eb(h, d_out_tokens, params: dg_eb_params, seed: int, commit: bool = True,
+                         stream=None) -> int:
+    """Returns the number of passes run."""
+    n = ctypes.c_int32()
+    _check(_lib.dg_generate_block_eb(h, _ptr(d_out_tokens), ctypes.byref(params), seed,
+                                     int(bool(commit)), ctypes.byref(n), _stream(stream)))
+    return n.value
 
 
 def dg_commit_canvas(h, d_canvas, stream=None) -> None:

@@ -87,6 +87,7 @@ DG_DEV u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
 
 constexpr uint32_t kInitTag = 0x494E4954u;
 constexpr uint32_t kGumbelTag = 0x47554D42u;
+constexpr uint32_t kRenoiseTag = 0x524E5345u;
 
 // u in (0,1), exact float: (2*(word>>9)+1) * 2^-24
 DG_DEV float philox_open_uniform(uint32_t w) {

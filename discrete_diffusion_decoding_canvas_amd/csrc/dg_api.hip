@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <map>
 #include <string>
 #include <vector>
@@ -107,6 +108,10 @@ struct dg_handle {
     float* st_lse = nullptr;
     float* st_conf = nullptr;
     int32_t* st_draw = nullptr;
+    float* st_ent = nullptr;      // predictive entropy per position (entropy-bounded passes)
+    float* hp_q = nullptr;        // entropy partials [C][n_slices]
+    int32_t* eb_prev = nullptr;   // argmax of the previous entropy-bounded pass
+    int32_t* eb_info = nullptr;   // [4] outcome of the last entropy-bounded pass
     int32_t* bad = nullptr;
     float* logits_cap = nullptr;
     int32_t* cap_idx = nullptr;
@@ -528,6 +533,10 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->st_lse, h->C));
     A_TRY(h->allocT(&h->st_conf, h->C));
     A_TRY(h->allocT(&h->st_draw, h->C));
+    A_TRY(h->allocT(&h->st_ent, h->C));
+    A_TRY(h->allocT(&h->hp_q, (size_t)h->C * ns));
+    A_TRY(h->allocT(&h->eb_prev, h->C));
+    A_TRY(h->allocT(&h->eb_info, 4));
     A_TRY(h->allocT(&h->bad, 1));
     A_TRY(h->allocT(&h->blk_canvas, h->C));
     A_TRY(h->allocT(&h->blk_mask, h->C));
@@ -799,17 +808,16 @@ static int run_layers_graph(dg_handle* h, hipStream_t s) {
     return DG_OK;
 }
 
-int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t step,
-                    int32_t T, uint64_t seed, void* stream) {
-    g_err.clear();
-    if (!h || !d_canvas || !d_locked_mask) return fail(DG_EINVAL, "NULL handle, canvas or mask");
-    if (T <= 0 || step < 0 || step >= T) return fail(DG_EINVAL, "need 0 <= step < T (step %d, T %d)", step, T);
+// Decoder over the canvas, LM head at temperature 1 / inv_tau and the per-position
+// statistics (with the predictive entropy when ent is set): everything of a pass
+// but the sampler.
+static int decode_and_head(dg_handle* h, const int32_t* d_canvas, const uint8_t* d_locked_mask,
+                           int32_t step, float inv_tau, uint64_t seed, bool ent, hipStream_t s) {
     if (!h->prefilled) return fail(DG_ESTATE, "denoise step before prefill");
     if (h->n_ctx + h->C > h->max_ctx)
         return fail(DG_ECAPACITY, "canvas at %lld exceeds max_ctx %lld", (long long)h->n_ctx,
                     (long long)h->max_ctx);
     DG_TRY(ensure_ready(h));
-    hipStream_t s = (hipStream_t)stream;
     const int C = h->C;
     K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, h->V, C, h->d,
                                h->cfg.rms_eps, h->x, h->a, h->Af, h->bad, s));
@@ -828,15 +836,79 @@ int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int
             HIP_TRY(hipMemcpyAsync(h->cap_hidden + (size_t)l * C * h->d, h->x,
                                    (size_t)C * h->d * 4, hipMemcpyDeviceToDevice, s));
     }
+    HeadPartials hp = h->hp;
+    hp.q = ent ? h->hp_q : nullptr;
     {
         ProfScope p(h, DG_PROF_LM_HEAD, s);
-        K_TRY(launch_lm_head(h->act, h->a, h->Af, C, h->d, h->embed, h->V, 1.0f / h->cfg.temperature,
-                             d_locked_mask, seed, step, h->k_blk, h->hp,
+        K_TRY(launch_lm_head(h->act, h->a, h->Af, C, h->d, h->embed, h->V, inv_tau, d_locked_mask,
+                             seed, step, h->k_blk, hp,
                              h->cap(DG_CAP_LOGITS) ? h->logits_cap : nullptr, s));
     }
-    K_TRY(launch_head_stats(h->hp, C, d_locked_mask, h->st_m, h->st_a, h->st_lse, h->st_conf,
-                            h->st_draw, h->bad, s));
-    K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, C, step, T, s));
+    K_TRY(launch_head_stats(hp, C, d_locked_mask, h->st_m, h->st_a, h->st_lse, h->st_conf,
+                            h->st_draw, ent ? h->st_ent : nullptr, h->bad, s));
+    return DG_OK;
+}
+
+int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t step,
+                    int32_t T, uint64_t seed, void* stream) {
+    g_err.clear();
+    if (!h || !d_canvas || !d_locked_mask) return fail(DG_EINVAL, "NULL handle, canvas or mask");
+    if (T <= 0 || step < 0 || step >= T) return fail(DG_EINVAL, "need 0 <= step < T (step %d, T %d)", step, T);
+    hipStream_t s = (hipStream_t)stream;
+    DG_TRY(decode_and_head(h, d_canvas, d_locked_mask, step, 1.0f / h->cfg.temperature, seed,
+                           false, s));
+    K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, h->C, step, T, s));
+    return DG_OK;
+}
+
+static int check_eb_params(const dg_eb_params* p, int32_t step) {
+    if (!p) return fail(DG_EINVAL, "NULL sampler parameters");
+    if (!(p->tau_max > 0.f) || !(p->tau_min > 0.f) || !std::isfinite(p->tau_max) ||
+        !std::isfinite(p->tau_min))
+        return fail(DG_EINVAL, "temperatures must be finite and > 0");
+    if (std::isnan(p->gamma) || std::isnan(p->theta)) return fail(DG_EINVAL, "NaN threshold");
+    if (p->max_steps <= 0) return fail(DG_EINVAL, "max_steps must be > 0");
+    if (step < 0 || step >= p->max_steps)
+        return fail(DG_EINVAL, "need 0 <= step < max_steps (step %d, max_steps %d)", step,
+                    p->max_steps);
+    return DG_OK;
+}
+
+// tau_s falls linearly from tau_max at pass 0 to tau_min at pass max_steps - 1.
+static double eb_tau(const dg_eb_params* p, int32_t step) {
+    if (p->max_steps <= 1) return (double)p->tau_min;
+    const double t = (double)(p->max_steps - 1 - step) / (double)(p->max_steps - 1);
+    return (double)p->tau_min + ((double)p->tau_max - (double)p->tau_min) * t;
+}
+
+int dg_eb_sample(const float* d_entropy, const int32_t* d_argmax, const int32_t* d_draw,
+                 int32_t* d_prev_argmax, int32_t* d_canvas, uint8_t* d_locked_mask,
+                 int32_t* d_info, int32_t C, int32_t V, int32_t step, const dg_eb_params* p,
+                 uint64_t seed, int32_t k_blk, void* stream) {
+    g_err.clear();
+    if (!d_entropy || !d_argmax || !d_draw || !d_prev_argmax || !d_canvas || !d_locked_mask ||
+        !d_info)
+        return fail(DG_EINVAL, "NULL buffer");
+    if (C <= 0 || C > kMaxCanvas) return fail(DG_EINVAL, "need 0 < C <= %d", kMaxCanvas);
+    if (V <= 0 || k_blk < 0) return fail(DG_EINVAL, "need V > 0 and k_blk >= 0");
+    DG_TRY(check_eb_params(p, step));
+    K_TRY(launch_sampler_eb(d_entropy, d_argmax, d_draw, d_prev_argmax, d_canvas, d_locked_mask,
+                            d_info, C, V, step, p->max_steps, p->gamma, p->theta, seed, k_blk,
+                            (hipStream_t)stream));
+    return DG_OK;
+}
+
+int dg_denoise_step_eb(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t step,
+                       const dg_eb_params* p, uint64_t seed, int32_t* d_info, void* stream) {
+    g_err.clear();
+    if (!h || !d_canvas || !d_locked_mask) return fail(DG_EINVAL, "NULL handle, canvas or mask");
+    DG_TRY(check_eb_params(p, step));
+    hipStream_t s = (hipStream_t)stream;
+    DG_TRY(decode_and_head(h, d_canvas, d_locked_mask, step, (float)(1.0 / eb_tau(p, step)), seed,
+                           true, s));
+    K_TRY(launch_sampler_eb(h->st_ent, h->st_a, h->st_draw, h->eb_prev, d_canvas, d_locked_mask,
+                            d_info ? d_info : h->eb_info, h->C, h->V, step, p->max_steps, p->gamma,
+                            p->theta, seed, h->k_blk, s));
     return DG_OK;
 }
 
@@ -889,6 +961,34 @@ int dg_generate_block(dg_handle* h, int32_t* d_out_tokens, int32_t T, uint64_t s
     return check_bad(h, s);
 }
 
+int dg_generate_block_eb(dg_handle* h, int32_t* d_out_tokens, const dg_eb_params* p,
+                         uint64_t seed, int32_t commit, int32_t* n_steps, void* stream) {
+    g_err.clear();
+    if (!h || !d_out_tokens) return fail(DG_EINVAL, "NULL handle or output");
+    DG_TRY(check_eb_params(p, 0));
+    if (!h->prefilled) return fail(DG_ESTATE, "generate before prefill");
+    if (h->n_ctx + h->C > h->max_ctx)
+        return fail(DG_ECAPACITY, "canvas at %lld exceeds max_ctx %lld", (long long)h->n_ctx,
+                    (long long)h->max_ctx);
+    DG_TRY(ensure_ready(h));
+    hipStream_t s = (hipStream_t)stream;
+    K_TRY(launch_canvas_init(h->blk_canvas, h->blk_mask, h->C, h->V, seed, h->k_blk, s));
+    int32_t info[4] = {0, 0, 0, 0};
+    int st = 0;
+    while (st < p->max_steps) {
+        DG_TRY(dg_denoise_step_eb(h, h->blk_canvas, h->blk_mask, st, p, seed, h->eb_info, stream));
+        ++st;
+        HIP_TRY(hipMemcpyAsync(info, h->eb_info, sizeof(info), hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        if (info[0]) break;
+    }
+    if (n_steps) *n_steps = st;
+    HIP_TRY(hipMemcpyAsync(d_out_tokens, h->blk_canvas, (size_t)h->C * 4,
+                           hipMemcpyDeviceToDevice, s));
+    if (commit) DG_TRY(dg_commit_canvas(h, h->blk_canvas, stream));
+    return check_bad(h, s);
+}
+
 int dg_get_capture(dg_handle* h, uint32_t what, int32_t layer, void* d_dst, size_t bytes,
                    void* stream) {
     g_err.clear();
@@ -903,6 +1003,11 @@ int dg_get_capture(dg_handle* h, uint32_t what, int32_t layer, void* d_dst, size
         HIP_TRY(hipMemcpyAsync(d + C * 8, h->st_lse, C * 4, hipMemcpyDeviceToDevice, s));
         HIP_TRY(hipMemcpyAsync(d + C * 12, h->st_conf, C * 4, hipMemcpyDeviceToDevice, s));
         HIP_TRY(hipMemcpyAsync(d + C * 16, h->st_draw, C * 4, hipMemcpyDeviceToDevice, s));
+        return DG_OK;
+    }
+    if (what == DG_CAP_ENTROPY) {
+        if (bytes != C * 4) return fail(DG_EINVAL, "entropy capture is %zu bytes", C * 4);
+        HIP_TRY(hipMemcpyAsync(d_dst, h->st_ent, C * 4, hipMemcpyDeviceToDevice, s));
         return DG_OK;
     }
     if (what == DG_CAP_LOGITS) {

@@ -7,7 +7,10 @@
 // 128-id vocabulary slice to per-row partials (max, lowest argmax, sum of
 // exp(z - max)) and, for rows still unlocked, the Gumbel-max redraw (best
 // z + G and its id) with Philox4x32-10 uniforms drawn per (vocabulary id,
-// position).
+// position).  With ENT it also keeps q = sum exp(z - max) (z - max), from which
+// the predictive entropy of the row is log s - q / s (the entropy-bounded
+// sampler ranks positions by it: technical-report summary, Method, sampler
+// paragraph).
 #pragma once
 
 #include "kernels.h"
@@ -29,15 +32,32 @@ struct Run {
     float s;
     float g;
     int32_t gi;
+    float q;
 };
 
-DG_DEV void run_merge(Run& x, float ym, int32_t ya, float ys, float yg, int32_t ygi) {
+// Absorb y into x.  Rescaling a slice's sums from its max m_i to m multiplies s
+// by f = exp(m_i - m) and turns q into f (q + (m_i - m) s).
+template <bool ENT = false>
+DG_DEV void run_merge(Run& x, float ym, int32_t ya, float ys, float yg, int32_t ygi,
+                      float yq = 0.f) {
     if (ym > x.m || (ym == x.m && ya < x.a)) {
-        x.s = ys + (x.m == -INFINITY ? 0.f : x.s * __expf(x.m - ym));
+        if constexpr (ENT) {
+            const float f = x.m == -INFINITY ? 0.f : __expf(x.m - ym);
+            x.q = yq + (f == 0.f ? 0.f : f * fmaf(x.m - ym, x.s, x.q));
+            x.s = ys + f * x.s;
+        } else {
+            x.s = ys + (x.m == -INFINITY ? 0.f : x.s * __expf(x.m - ym));
+        }
         x.m = ym;
         x.a = ya;
     } else {
-        x.s += (ym == -INFINITY ? 0.f : ys * __expf(ym - x.m));
+        if constexpr (ENT) {
+            const float f = ym == -INFINITY ? 0.f : __expf(ym - x.m);
+            x.q += f == 0.f ? 0.f : f * fmaf(ym - x.m, ys, yq);
+            x.s += f * ys;
+        } else {
+            x.s += (ym == -INFINITY ? 0.f : ys * __expf(ym - x.m));
+        }
     }
     if (yg > x.g || (yg == x.g && ygi < x.gi)) { x.g = yg; x.gi = ygi; }
 }
@@ -65,7 +85,7 @@ struct EpiArgs {
 // columns, then the sum of exp(z - max) in a second (one exponential per element);
 // the 16 lanes sharing the rows then merge.  MT is a template argument so that
 // every accumulator index is static.
-template <int MT>
+template <int MT, bool ENT = false>
 DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
     constexpr float kLog2e = 1.4426950408889634f;
     const int r4 = e.rbase + 16 * MT + 4 * e.g;      // rows r4 .. r4+3 in this lane
@@ -106,15 +126,25 @@ DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
     Run run[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        float s = 0.f;
+        float s = 0.f, q = 0.f;
         if (m[j] != -INFINITY) {
-            const float mb = m[j] * kLog2e;
+            if constexpr (ENT) {
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                s += __builtin_amdgcn_exp2f(fmaf(acc[nt][j] * e.inv_tau, kLog2e, -mb));
+                for (int nt = 0; nt < 8; ++nt) {
+                    const float dz = acc[nt][j] * e.inv_tau - m[j];      // z - max, 0 at the max
+                    const float ex = __builtin_amdgcn_exp2f(dz * kLog2e);
+                    s += ex;
+                    q = fmaf(ex, dz, q);
+                }
+            } else {
+                const float mb = m[j] * kLog2e;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+                    s += __builtin_amdgcn_exp2f(fmaf(acc[nt][j] * e.inv_tau, kLog2e, -mb));
+            }
         }
         run[j] = Run{m[j], m[j] == -INFINITY ? 0x7fffffff : e.v0 + 16 * am[j] + e.l16, s, g[j],
-                     ag[j] < 0 ? 0x7fffffff : e.v0 + 16 * ag[j] + e.l16};
+                     ag[j] < 0 ? 0x7fffffff : e.v0 + 16 * ag[j] + e.l16, q};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -125,7 +155,10 @@ DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
             const float ys = __shfl_xor(run[j].s, o, 64);
             const float yg = __shfl_xor(run[j].g, o, 64);
             const int32_t ygi = __shfl_xor(run[j].gi, o, 64);
-            run_merge(run[j], ym, ya, ys, yg, ygi);
+            if constexpr (ENT)
+                run_merge<true>(run[j], ym, ya, ys, yg, ygi, __shfl_xor(run[j].q, o, 64));
+            else
+                run_merge(run[j], ym, ya, ys, yg, ygi);
         }
         if (e.l16 == 0 && r4 + j < e.C) {
             const size_t o = (size_t)(r4 + j) * e.p.n_slices + e.v0 / kHeadCols;
@@ -134,6 +167,7 @@ DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
             e.p.s[o] = run[j].s;
             e.p.g[o] = run[j].g;
             e.p.gi[o] = run[j].gi;
+            if constexpr (ENT) e.p.q[o] = run[j].q;
         }
     }
 }

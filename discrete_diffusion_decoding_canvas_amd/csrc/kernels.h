@@ -65,6 +65,7 @@ struct HeadPartials {
     float* s;       // sum exp(z - m)
     float* g;       // best Gumbel-perturbed score (-inf for locked rows)
     int32_t* gi;    // its id
+    float* q;       // sum exp(z - m) (z - m), for the predictive entropy; nullptr: not kept
     int n_slices;
 };
 
@@ -97,11 +98,17 @@ hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d,
                               void* a, uint8_t* a8, void* af, void* out, hipStream_t s);
 hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint64_t seed,
                               int k_blk, hipStream_t s);
+// st_ent (entropy per row) is written when p.q is kept, and must be given exactly then.
 hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, float* st_m,
                              int32_t* st_a, float* st_lse, float* st_conf, int32_t* st_draw,
-                             int32_t* bad, hipStream_t s);
+                             float* st_ent, int32_t* bad, hipStream_t s);
 hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t* draw,
                           int32_t* canvas, uint8_t* mask, int C, int step, int T, hipStream_t s);
+// One pass of the entropy-bounded sampler (k_sampler_eb); C <= kMaxCanvas.
+hipError_t launch_sampler_eb(const float* ent, const int32_t* amax, const int32_t* draw,
+                             int32_t* prev, int32_t* canvas, uint8_t* mask, int32_t* info, int C,
+                             int V, int step, int max_steps, float gamma, float theta,
+                             uint64_t seed, int k_blk, hipStream_t s);
 // rope_hd > 0 (128): the 16-column groups of every rope_hd-column head are
 // reordered so that each 64-column tile holds 32 rotary pairs (dims j and
 // j + 64 for j in one 32-dim quarter), see kEpiRope.

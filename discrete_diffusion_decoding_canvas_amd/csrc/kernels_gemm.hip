@@ -849,6 +849,7 @@ DG_DEV HeadUnit head_unit(int u, int n_slabs, const void* Ep, int KB, int w, int
     return c;
 }
 
+template <bool ENT>
 __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_head_wide(
     const uint8_t* Hf, int C, int d, const void* __restrict__ Ep, int V, float inv_tau,
     const uint8_t* __restrict__ mask, uint32_t key0, uint32_t key1, uint32_t c2, HeadPartials p,
@@ -882,8 +883,8 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_head_wide(
             static_assert(kWideMT <= 2, "head epilogue of one or two 16-row groups");
             const EpiArgs ea{C, V, c.n0, c.wr0, lane >> 4, lane & 15, inv_tau, mask, key0, key1, c2, p,
                              logits_out};
-            head_epilogue<0>(acc[0], ea);
-            if constexpr (kWideMT > 1) head_epilogue<1>(acc[1], ea);
+            head_epilogue<0, ENT>(acc[0], ea);
+            if constexpr (kWideMT > 1) head_epilogue<1, ENT>(acc[1], ea);
         }
         if (un >= total) break;
         u = un;
@@ -1076,8 +1077,12 @@ hipError_t launch_head_wide(const void* hf, int C, int d, const void* E, int V, 
     if ((V % kWideN) || (d & 31)) return hipErrorInvalidValue;
     const int64_t units = (int64_t)(V / kWideN) * ((C + kMoeRows - 1) / kMoeRows);
     const unsigned grid = (unsigned)std::min<int64_t>(units, persistent_wgs());
-    k_head_wide<<<grid, kWideThreads, 0, s>>>((const uint8_t*)hf, C, d, E, V, inv_tau, mask, key0,
-                                              key1, c2, p, logits_out);
+    if (p.q)
+        k_head_wide<true><<<grid, kWideThreads, 0, s>>>((const uint8_t*)hf, C, d, E, V, inv_tau, mask,
+                                                        key0, key1, c2, p, logits_out);
+    else
+        k_head_wide<false><<<grid, kWideThreads, 0, s>>>((const uint8_t*)hf, C, d, E, V, inv_tau, mask,
+                                                         key0, key1, c2, p, logits_out);
     return hipGetLastError();
 }
 

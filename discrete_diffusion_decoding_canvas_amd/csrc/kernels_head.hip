@@ -6,7 +6,8 @@
 // The C x V logits are never stored: each workgroup reduces its vocabulary
 // slice to per-row partials (max, lowest argmax, sum of exp(z - max)) and, for
 // rows still unlocked, the Gumbel-max redraw (best z + G and its id) with
-// Philox4x32-10 uniforms drawn per (vocabulary id, position).
+// Philox4x32-10 uniforms drawn per (vocabulary id, position).  ENT adds the
+// weighted sum q = sum exp(z - max) (z - max) of the predictive entropy.
 #include "head_epilogue.h"
 
 namespace dg {
@@ -16,6 +17,7 @@ namespace dg {
 // double-buffered LDS in MFMA fragment order (the embedding is packed that way
 // at load time, so its copy is contiguous), and each wave (64 rows x 128 ids)
 // reads its fragments from LDS.
+template <bool ENT>
 __global__ __launch_bounds__(512) void k_lm_head_bf16(
     const bf16_t* __restrict__ Hn, int C, int d, const bf16_t* __restrict__ Ep, int V,
     float inv_tau, const uint8_t* __restrict__ mask, uint32_t key0, uint32_t key1, uint32_t c2,
@@ -85,13 +87,14 @@ __global__ __launch_bounds__(512) void k_lm_head_bf16(
     }
     if (rbase >= C) return;
     const EpiArgs ea{C, V, v0, rbase, g, l16, inv_tau, mask, key0, key1, c2, p, logits_out};
-    head_epilogue<0>(acc[0], ea);
-    head_epilogue<1>(acc[1], ea);
-    head_epilogue<2>(acc[2], ea);
-    head_epilogue<3>(acc[3], ea);
+    head_epilogue<0, ENT>(acc[0], ea);
+    head_epilogue<1, ENT>(acc[1], ea);
+    head_epilogue<2, ENT>(acc[2], ea);
+    head_epilogue<3, ENT>(acc[3], ea);
 }
 
 // f32 head (VALU): one thread per (row, vocabulary id), workgroup = 256 ids of one row.
+template <bool ENT>
 __global__ __launch_bounds__(256) void k_lm_head_f32(
     const float* __restrict__ Hn, int C, int d, const float* __restrict__ E, int V,
     float inv_tau, const uint8_t* __restrict__ mask, uint32_t key0, uint32_t key1, uint32_t c2,
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(256) void k_lm_head_f32(
     __shared__ Run sh[256];
     const int row = blockIdx.y;
     const int v = blockIdx.x * 256 + threadIdx.x;
-    Run r = {-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff};
+    Run r = {-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff, 0.f};
     if (v < V) {
         const float* h = Hn + (size_t)row * d;
         const float* e = E + (size_t)v * d;
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(256) void k_lm_head_f32(
         if (threadIdx.x < wdt) {
             Run x = sh[threadIdx.x];
             const Run y = sh[threadIdx.x + wdt];
-            run_merge(x, y.m, y.a, y.s, y.g, y.gi);
+            run_merge<ENT>(x, y.m, y.a, y.s, y.g, y.gi, y.q);
             sh[threadIdx.x] = x;
         }
         __syncthreads();
@@ -136,6 +139,7 @@ __global__ __launch_bounds__(256) void k_lm_head_f32(
         p.s[o] = sh[0].s;
         p.g[o] = sh[0].g;
         p.gi[o] = sh[0].gi;
+        if constexpr (ENT) p.q[o] = sh[0].q;
     }
 }
 
@@ -152,13 +156,15 @@ hipError_t launch_lm_head(int dtype, const void* h, const void* hf, int C, int d
         return launch_head_wide(hf, C, d, E, V, inv_tau, mask, key0, key1, c2, p, logits_out, s);
     if (dtype == kF32) {
         dim3 grid((V + 255) / 256, C);
-        k_lm_head_f32<<<grid, 256, 0, s>>>((const float*)h, C, d, (const float*)E, V, inv_tau,
-                                           mask, key0, key1, c2, p, logits_out);
+        auto k = p.q ? k_lm_head_f32<true> : k_lm_head_f32<false>;
+        k<<<grid, 256, 0, s>>>((const float*)h, C, d, (const float*)E, V, inv_tau, mask, key0, key1,
+                               c2, p, logits_out);
     } else {
         if ((V % kHeadTile) || (d & 31)) return hipErrorInvalidValue;
         dim3 grid(V / kHeadTile, (C + kHeadRows - 1) / kHeadRows);
-        k_lm_head_bf16<<<grid, 512, 0, s>>>((const bf16_t*)h, C, d, (const bf16_t*)E, V,
-                                            inv_tau, mask, key0, key1, c2, p, logits_out);
+        auto k = p.q ? k_lm_head_bf16<true> : k_lm_head_bf16<false>;
+        k<<<grid, 512, 0, s>>>((const bf16_t*)h, C, d, (const bf16_t*)E, V, inv_tau, mask, key0,
+                               key1, c2, p, logits_out);
     }
     return hipGetLastError();
 }

@@ -282,56 +282,70 @@ __global__ void k_canvas_init(int32_t* __restrict__ canvas, uint8_t* __restrict_
 
 // ------------------------------------------------------------------ LM-head statistics
 // Reduce the per-slice partials of one row in a fixed tree: max with the
-// lowest id on ties, sum of exp(z - max), Gumbel best with the lowest id on ties.
-struct HeadPart { float m; int32_t a; float s; float g; int32_t gi; };
+// lowest id on ties, sum of exp(z - max), Gumbel best with the lowest id on ties,
+// and with ENT the weighted sum q = sum exp(z - max) (z - max), rescaled to a
+// new max m as f (q + (m_i - m) s) with f = exp(m_i - m).
+struct HeadPart { float m; int32_t a; float s; float g; int32_t gi; float q; };
 
+template <bool ENT>
 DG_DEV void head_merge(HeadPart& x, const HeadPart& y) {
     if (y.m > x.m || (y.m == x.m && y.a < x.a)) {
-        float sx = (x.m == -INFINITY) ? 0.f : x.s * exp2f((x.m - y.m) * 1.4426950408889634f);
-        x.s = y.s + sx;
+        const float f = (x.m == -INFINITY) ? 0.f : exp2f((x.m - y.m) * 1.4426950408889634f);
+        if constexpr (ENT) x.q = y.q + (f == 0.f ? 0.f : f * fmaf(x.m - y.m, x.s, x.q));
+        x.s = y.s + x.s * f;
         x.m = y.m;
         x.a = y.a;
     } else {
-        float sy = (y.m == -INFINITY) ? 0.f : y.s * exp2f((y.m - x.m) * 1.4426950408889634f);
-        x.s += sy;
+        const float f = (y.m == -INFINITY) ? 0.f : exp2f((y.m - x.m) * 1.4426950408889634f);
+        if constexpr (ENT) x.q += f == 0.f ? 0.f : f * fmaf(y.m - x.m, y.s, y.q);
+        x.s += y.s * f;
     }
     if (y.g > x.g || (y.g == x.g && y.gi < x.gi)) { x.g = y.g; x.gi = y.gi; }
 }
 
+template <bool ENT>
 __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm,
                                                     const int32_t* __restrict__ pa,
                                                     const float* __restrict__ ps,
                                                     const float* __restrict__ pg,
                                                     const int32_t* __restrict__ pgi,
+                                                    const float* __restrict__ pq,
                                                     int n_slices, const uint8_t* __restrict__ mask,
                                                     float* __restrict__ st_m,
                                                     int32_t* __restrict__ st_a,
                                                     float* __restrict__ st_lse,
                                                     float* __restrict__ st_conf,
                                                     int32_t* __restrict__ st_draw,
+                                                    float* __restrict__ st_ent,
                                                     int32_t* __restrict__ bad) {
     __shared__ HeadPart sh[4];
     const int row = blockIdx.x;
-    HeadPart acc = {-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff};
+    HeadPart acc = {-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff, 0.f};
     for (int i = threadIdx.x; i < n_slices; i += 256) {
         const int64_t o = (int64_t)row * n_slices + i;
-        HeadPart p = {pm[o], pa[o], ps[o], pg[o], pgi[o]};
-        head_merge(acc, p);
+        HeadPart p = {pm[o], pa[o], ps[o], pg[o], pgi[o], ENT ? pq[o] : 0.f};
+        head_merge<ENT>(acc, p);
     }
     // within each wave by shuffles, then the four waves in order
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const HeadPart y = {__shfl_xor(acc.m, o, 64), __shfl_xor(acc.a, o, 64), __shfl_xor(acc.s, o, 64),
-                            __shfl_xor(acc.g, o, 64), __shfl_xor(acc.gi, o, 64)};
-        head_merge(acc, y);
+                            __shfl_xor(acc.g, o, 64), __shfl_xor(acc.gi, o, 64),
+                            ENT ? __shfl_xor(acc.q, o, 64) : 0.f};
+        head_merge<ENT>(acc, y);
     }
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
         HeadPart r = sh[0];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) head_merge(r, sh[w]);
+        for (int w = 1; w < 4; ++w) head_merge<ENT>(r, sh[w]);
         const float ls = logf(r.s);
+        if constexpr (ENT) {
+            const float h = ls - r.q / r.s;                    // entropy of Softmax(z), nats
+            st_ent[row] = h;
+            if (!isfinite(h)) atomicOr(bad, kBadNonFinite);
+        }
         st_m[row] = r.m;
         st_a[row] = r.a;
         st_lse[row] = r.m + ls;
@@ -389,6 +403,124 @@ __global__ __launch_bounds__(1024) void k_sampler(const float* __restrict__ conf
         } else {
             canvas[i] = draw[i];
         }
+    }
+}
+
+// ------------------------------------------------------------------ entropy-bounded sampler
+// One pass of the sampler of the technical-report summary (Method, the sampler
+// and adaptive-stopping paragraphs), one workgroup:
+//  * stop test (pass >= 1): the canvas-mean entropy, summed in float64 in
+//    position order, is below theta and every position's argmax equals the
+//    previous pass's; the last pass always ends the block.  Ending, every
+//    unlocked position takes its argmax and locks;
+//  * otherwise unlocked positions are ranked by entropy (ties to the lower
+//    position) and accepted in rank order while B = (running float64 sum of
+//    their entropies) - (the entropy just added, the prefix's largest) stays
+//    below gamma.  Accepted positions take their Gumbel draw and lock; the
+//    rest take a uniform token (Philox stream kRenoiseTag); locked ones are
+//    untouched.
+// prev holds the previous pass's argmax and is overwritten with this pass's.
+// info: [0] 1 if the block is finished, [1] positions locked by this pass,
+// [2] positions left unlocked, [3] 1 if the stop test held.  NaN entropies
+// rank last (the head statistics flag them).
+__global__ __launch_bounds__(1024) void k_sampler_eb(const float* __restrict__ ent,
+                                                     const int32_t* __restrict__ amax,
+                                                     const int32_t* __restrict__ draw,
+                                                     int32_t* __restrict__ prev,
+                                                     int32_t* __restrict__ canvas,
+                                                     uint8_t* __restrict__ mask,
+                                                     int32_t* __restrict__ info, int C, int V,
+                                                     int step, int max_steps, float gamma,
+                                                     float theta, uint32_t key0, uint32_t key1,
+                                                     int k_blk) {
+    __shared__ __attribute__((aligned(16))) float hs[kMaxCanvas];
+    __shared__ __attribute__((aligned(16))) uint8_t un[kMaxCanvas];
+    __shared__ float h_sorted[kMaxCanvas];
+    __shared__ int16_t rank_of[kMaxCanvas];
+    __shared__ int n_unl, n_diff, n_acc, stop;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        n_unl = 0;
+        n_diff = 0;
+    }
+    __syncthreads();
+    int mine = 0, diff = 0;
+    for (int i = tid; i < (C + 3) / 4 * 4; i += blockDim.x) {   // tail padded locked
+        const bool u = i < C && mask[i] == 0;
+        float h = i < C ? ent[i] : 0.f;
+        if (h != h) h = INFINITY;
+        hs[i] = h;
+        un[i] = u;
+        mine += u;
+        if (i < C && step > 0) diff += prev[i] != amax[i];
+    }
+    if (mine) atomicAdd(&n_unl, mine);
+    if (diff) atomicAdd(&n_diff, diff);
+    __syncthreads();
+    for (int i = tid; i < C; i += blockDim.x) {
+        if (!un[i]) continue;
+        const float hi = hs[i];
+        int rank = 0;
+#pragma unroll 4
+        for (int j4 = 0; j4 < (C + 3) / 4; ++j4) {
+            const float4 c = reinterpret_cast<const float4*>(hs)[j4];
+            const uchar4 u = reinterpret_cast<const uchar4*>(un)[j4];
+            const int j = 4 * j4;
+            rank += u.x && (c.x < hi || (c.x == hi && j < i));
+            rank += u.y && (c.y < hi || (c.y == hi && j + 1 < i));
+            rank += u.z && (c.z < hi || (c.z == hi && j + 2 < i));
+            rank += u.w && (c.w < hi || (c.w == hi && j + 3 < i));
+        }
+        rank_of[i] = (int16_t)rank;
+        h_sorted[rank] = hi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double acc = 0.0;
+        for (int i = 0; i < C; ++i) acc += (double)hs[i];
+        const bool rule = step >= 1 && n_diff == 0 && acc / (double)C < (double)theta;
+        stop = rule ? 2 : (step == max_steps - 1 ? 1 : 0);
+    } else if (tid == 64) {
+        const int nu = n_unl;
+        int n = 0;
+        if (nu > 0) {
+            n = 1;
+            double run = (double)h_sorted[0];
+            for (int k = 1; k < nu; ++k) {
+                const double hk = (double)h_sorted[k];
+                run += hk;
+                if (run - hk < (double)gamma) n = k + 1;
+                else break;
+            }
+        }
+        n_acc = n;
+    }
+    __syncthreads();
+    const bool fin = stop != 0;
+    const int na = n_acc, nu = n_unl;
+    for (int i = tid; i < C; i += blockDim.x) {
+        const int32_t a = amax[i];
+        prev[i] = a;
+        if (!un[i]) continue;
+        if (fin) {
+            canvas[i] = a;
+            mask[i] = 1;
+        } else if (rank_of[i] < na) {
+            canvas[i] = draw[i];
+            mask[i] = 1;
+        } else {
+            const u32x4 r = philox4x32_10(u32x4{(uint32_t)(i >> 2), (uint32_t)k_blk, (uint32_t)step,
+                                                kRenoiseTag}, key0, key1);
+            const uint32_t w = (i & 3) == 0 ? r.x : (i & 3) == 1 ? r.y : (i & 3) == 2 ? r.z : r.w;
+            canvas[i] = (int32_t)(((uint64_t)w * (uint64_t)V) >> 32);
+        }
+    }
+    if (tid == 0) {
+        const int locked_now = fin ? nu : na;
+        info[0] = fin || nu - locked_now == 0;
+        info[1] = locked_now;
+        info[2] = nu - locked_now;
+        info[3] = stop == 2;
     }
 }
 
@@ -583,9 +715,12 @@ hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint
 
 hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, float* st_m,
                              int32_t* st_a, float* st_lse, float* st_conf, int32_t* st_draw,
-                             int32_t* bad, hipStream_t s) {
-    k_head_stats<<<C, 256, 0, s>>>(p.m, p.a, p.s, p.g, p.gi, p.n_slices, mask, st_m, st_a,
-                                   st_lse, st_conf, st_draw, bad);
+                             float* st_ent, int32_t* bad, hipStream_t s) {
+    if (C <= 0) return hipSuccess;
+    if ((p.q == nullptr) != (st_ent == nullptr)) return hipErrorInvalidValue;
+    auto k = p.q ? k_head_stats<true> : k_head_stats<false>;
+    k<<<C, 256, 0, s>>>(p.m, p.a, p.s, p.g, p.gi, p.q, p.n_slices, mask, st_m, st_a, st_lse,
+                        st_conf, st_draw, st_ent, bad);
     LAUNCH_CHECK();
 }
 
@@ -593,6 +728,18 @@ hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t*
                           int32_t* canvas, uint8_t* mask, int C, int step, int T,
                           hipStream_t s) {
     k_sampler<<<1, 1024, 0, s>>>(conf, amax, draw, canvas, mask, C, step, T);
+    LAUNCH_CHECK();
+}
+
+hipError_t launch_sampler_eb(const float* ent, const int32_t* amax, const int32_t* draw,
+                             int32_t* prev, int32_t* canvas, uint8_t* mask, int32_t* info, int C,
+                             int V, int step, int max_steps, float gamma, float theta,
+                             uint64_t seed, int k_blk, hipStream_t s) {
+    if (C <= 0 || C > kMaxCanvas || V <= 0 || step < 0 || step >= max_steps)
+        return hipErrorInvalidValue;
+    k_sampler_eb<<<1, 1024, 0, s>>>(ent, amax, draw, prev, canvas, mask, info, C, V, step,
+                                    max_steps, gamma, theta, (uint32_t)seed,
+                                    (uint32_t)(seed >> 32), k_blk);
     LAUNCH_CHECK();
 }
 

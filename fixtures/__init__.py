@@ -282,3 +282,33 @@ def moe_inputs(m: MoeWorkload = MOE_LAYER):
     wu = normal(m.seed, layer_tid("wu", 0), (m.n_experts, m.d_model, m.d_ff), m.sigma, "bf16")
     wd = normal(m.seed, layer_tid("wd", 0), (m.n_experts, m.d_ff, m.d_model), m.sigma, "bf16")
     return x, wr, wg, wu, wd
+
+
+def eb_sampler_inputs(seed: int, C: int, V: int, locked_frac: float = 0.3,
+                      prev_diff: int = 0, nan_at: int | None = None):
+    """Per-position statistics for one pass of the entropy-bounded sampler, seeded.
+
+    Entropies: a mix of near-certain positions (multiples of 2^-12 in [0, 2^-6],
+    many tied) and uncertain ones (exponential, mean 2, capped at log V), as
+    float32.  argmax, draw and canvas uniform over [0, V); prev = argmax with
+    prev_diff positions changed; mask: locked_frac of positions locked.
+    Returns dict of numpy arrays."""
+    rng = np.random.default_rng([seed, C, V])
+    sure = rng.random(C) < 0.4
+    h = np.where(sure, rng.integers(0, 65, C) / 4096.0,
+                 np.minimum(rng.exponential(2.0, C), np.log(V))).astype(np.float32)
+    if nan_at is not None:
+        h[nan_at] = np.nan
+    argmax = rng.integers(0, V, C).astype(np.int32)
+    prev = argmax.copy()
+    if prev_diff:
+        at = rng.choice(C, size=prev_diff, replace=False)
+        prev[at] = (prev[at] + 1) % V
+    return {
+        "entropy": h,
+        "argmax": argmax,
+        "draw": rng.integers(0, V, C).astype(np.int32),
+        "prev": prev,
+        "canvas": rng.integers(0, V, C).astype(np.int32),
+        "mask": (rng.random(C) < locked_frac).astype(np.uint8),
+    }

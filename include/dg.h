@@ -95,6 +95,9 @@ extern "C" {
  *   DG_CAP_HIDDEN   per layer: float residual stream [C, d] after the layer
  *   DG_CAP_ATTN     per layer: attention output [C, Hq*D] in act_dtype
  *   DG_CAP_ROUTER_LOGITS per layer: float router logits [C, E]
+ *   DG_CAP_ENTROPY  float [C] predictive entropy (nats) per position of the
+ *                   last dg_denoise_step_eb pass; always available (no
+ *                   capture_mask bit needed)
  */
 #define DG_CAP_LOGITS 1u
 #define DG_CAP_STATS 2u
@@ -102,6 +105,7 @@ extern "C" {
 #define DG_CAP_HIDDEN 8u
 #define DG_CAP_ATTN 16u
 #define DG_CAP_ROUTER_LOGITS 32u
+#define DG_CAP_ENTROPY 64u
 
 typedef struct dg_model_cfg {
     int32_t n_layers;      /* L */
@@ -185,6 +189,63 @@ int dg_init_canvas(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, uint
  * handle checks the non-finite flag (always: it reads one int at the end). */
 int dg_generate_block(dg_handle* h, int32_t* d_out_tokens, int32_t T, uint64_t seed,
                       int32_t commit, void* stream);
+
+/* ---------------------------------------------------------------- entropy-bounded sampler
+ * The sampler of the technical-report summary (Method, the paragraphs on the
+ * sampler and on adaptive stopping; Experiment, the recommended sampler:
+ * tau 0.8 -> 0.4, at most 48 passes, separate thresholds for selection and
+ * stopping, whose values the pages do not give). */
+typedef struct dg_eb_params {
+    float tau_max;       /* temperature at pass 0 (0.8) */
+    float tau_min;       /* temperature at pass max_steps - 1 (0.4) */
+    float gamma;         /* selection tolerance on the bound B, nats */
+    float theta;         /* stop threshold on the canvas-mean entropy, nats */
+    int32_t max_steps;   /* passes at most (48) */
+} dg_eb_params;
+
+/* One sampler pass given its statistics (all device buffers of C elements):
+ * d_entropy float H_i, d_argmax int32, d_draw int32 (Gumbel-max draw at
+ * tau_s), d_prev_argmax int32 in/out (the previous pass's argmax; ignored at
+ * step 0, overwritten with d_argmax), d_canvas int32 and d_locked_mask uint8
+ * in/out, d_info int32 [4] out: finished (0/1), positions locked by this
+ * pass, positions left unlocked, 1 if the stop test held.
+ *   Stop test (step >= 1): sum_i H_i (float64, in position order) / C < theta
+ *   and d_argmax equals d_prev_argmax everywhere.  It, or step = max_steps-1,
+ *   locks every unlocked position to its argmax and finishes the block.
+ *   Otherwise unlocked positions are ranked by H ascending (ties to the lower
+ *   position; NaN last) and accepted in rank order while B stays below
+ *   gamma, B = (float64 running sum of the accepted entropies in rank order)
+ *   minus the entropy just added (the largest so far); the first candidate
+ *   always is.  Accepted positions take d_draw and lock; the other unlocked
+ *   ones take a uniform token: Philox4x32-10, key = seed, counter (i>>2,
+ *   k_blk, step, 0x524E5345), word i&3, token = word*V >> 32.  A pass that
+ *   leaves nothing unlocked also finishes the block.
+ * 0 < C <= 1024, V > 0, 0 <= step < max_steps; tau_max, tau_min unused here.
+ * The caller owns every buffer; nothing is allocated.  Asynchronous. */
+int dg_eb_sample(const float* d_entropy, const int32_t* d_argmax, const int32_t* d_draw,
+                 int32_t* d_prev_argmax, int32_t* d_canvas, uint8_t* d_locked_mask,
+                 int32_t* d_info, int32_t C, int32_t V, int32_t step, const dg_eb_params* p,
+                 uint64_t seed, int32_t k_blk, void* stream);
+
+/* One pass of stage 2 with the entropy-bounded sampler: the decoder as in
+ * dg_denoise_step, the LM head at tau_s = tau_min + (tau_max - tau_min) *
+ * (max_steps-1-step) / (max_steps-1) (tau_min if max_steps = 1), the
+ * per-position entropy H_i of softmax(logits / tau_s) kept by the head's
+ * streaming epilogue, the Gumbel-max draw of unlocked positions at tau_s
+ * (the dg_denoise_step stream), then dg_eb_sample with the handle's own
+ * previous-argmax buffer.  d_info: device int32 [4] as in dg_eb_sample, or
+ * NULL to keep it in the handle.  Passes of one block must run in order from
+ * step 0.  Errors and asynchrony as dg_denoise_step. */
+int dg_denoise_step_eb(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t step,
+                       const dg_eb_params* p, uint64_t seed, int32_t* d_info, void* stream);
+
+/* One block with the entropy-bounded sampler: the initial canvas of
+ * dg_generate_block, then dg_denoise_step_eb passes until one finishes the
+ * block (reads 16 bytes back after each pass), then the output copy and the
+ * optional commit as in dg_generate_block.  *n_steps (if not NULL) receives
+ * the number of passes run.  Synchronous. */
+int dg_generate_block_eb(dg_handle* h, int32_t* d_out_tokens, const dg_eb_params* p,
+                         uint64_t seed, int32_t commit, int32_t* n_steps, void* stream);
 
 /* Stage 3 alone: append the causal-encoder K/V of a finished canvas
  * (device int32 [C]) at rows n_ctx..n_ctx+C-1; n_ctx += C, k_blk += 1. */

@@ -64,3 +64,20 @@ def test_null_arguments_are_rejected(dg):
                             None) == dg.DG_EINVAL
     assert lib.dg_create(None, None) == dg.DG_EINVAL
     lib.dg_destroy(None)
+
+
+def test_entropy_bounded_entry_points_validate_before_any_device_call(dg):
+    lib = dg._lib
+    p = dg.eb_params()
+    fake = [16 * (i + 1) for i in range(7)]      # never dereferenced: every case fails validation
+    assert lib.dg_eb_sample(None, *fake[1:], 256, 1024, 0, ctypes.byref(p), 0, 0, None) == dg.DG_EINVAL
+    for C, V, step, k_blk in ((0, 1024, 0, 0), (1025, 1024, 0, 0), (256, 0, 0, 0),
+                              (256, 1024, 48, 0), (256, 1024, -1, 0), (256, 1024, 0, -1)):
+        assert lib.dg_eb_sample(*fake, C, V, step, ctypes.byref(p), 0, k_blk, None) == dg.DG_EINVAL
+    for bad in (dict(max_steps=0), dict(tau_min=0.0), dict(tau_max=float("inf")),
+                dict(gamma=float("nan"))):
+        q = dg.eb_params(**bad)
+        assert lib.dg_eb_sample(*fake, 256, 1024, 0, ctypes.byref(q), 0, 0, None) == dg.DG_EINVAL
+    assert lib.dg_eb_sample(*fake, 256, 1024, 0, None, 0, 0, None) == dg.DG_EINVAL
+    assert lib.dg_denoise_step_eb(None, None, None, 0, ctypes.byref(p), 0, None, None) == dg.DG_EINVAL
+    assert lib.dg_generate_block_eb(None, None, ctypes.byref(p), 0, 1, None, None) == dg.DG_EINVAL
