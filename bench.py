@@ -339,6 +339,51 @@ def main():
         commit_ms = (time.perf_counter() - t0) * 1e3
         log(f"block {block_ms:.2f} ms, commit {commit_ms:.2f} ms")
 
+    # the entropy-bounded sampler on the same model: same decoder, the LM head with its
+    # entropy term, the one-workgroup sampler.  Per-pass time (no stop: theta = 0), the
+    # head's time with the entropy term, and one block with the pages' schedule
+    # (tau 0.8 -> 0.4, at most 48 passes).
+    ebr = None
+    if not args.no_blocks:
+        p_run = dg.eb_params(theta=0.0)
+        info = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+        def eb_step(i):
+            s = i % T
+            if s == 0:
+                dg.dg_init_canvas(h, canvas, mask, seed + 100 + i // T)
+            dg.dg_denoise_step_eb(h, canvas, mask, s, p_run, seed, info)
+
+        for i in range(args.warmup):
+            eb_step(i)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            eb_step(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        eb_ms = start.elapsed_time(end) / args.steps
+        dg.dg_profile_begin(h, args.steps * (w.n_layers * 7 + 4))
+        for i in range(args.steps):
+            eb_step(i)
+        torch.cuda.synchronize()
+        eb_prof_ms, eb_prof_n = dg.dg_profile_end(h)
+        head_i = dg.DG_PROF_LM_HEAD
+        eb_head_us = eb_prof_ms[head_i] / eb_prof_n[head_i] * 1e3 if eb_prof_n[head_i] else None
+        p_block = dg.eb_params()
+        out = torch.empty(C, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n_eb = dg.dg_generate_block_eb(h, out, p_block, seed + 7, False)
+        eb_block_ms = (time.perf_counter() - t0) * 1e3
+        ebr = {"ms_per_pass": round(eb_ms, 4), "lm_head_us_with_entropy": round(eb_head_us, 2),
+               "block_passes": n_eb, "block_ms": round(eb_block_ms, 2),
+               "params": {"tau_max": p_block.tau_max, "tau_min": round(p_block.tau_min, 6),
+                          "gamma": p_block.gamma, "theta": round(p_block.theta, 6),
+                          "max_steps": p_block.max_steps}}
+        log(f"entropy-bounded: {eb_ms:.3f} ms per pass (head {eb_head_us:.1f} us); "
+            f"block of {n_eb} passes {eb_block_ms:.1f} ms")
+
     # roofline of the dominant kernel (expert gate/up GEMM + SwiGLU)
     names = ["moe_gemm1", "moe_gemm2", "attention", "lm_head", "dense_gemm"]
     per_class_us = {n: (prof_ms[i] / prof_n[i] * 1e3 if prof_n[i] else None)
@@ -383,6 +428,7 @@ def main():
         "block_ms": round(block_ms, 3) if block_ms else None,
         "commit_ms": round(commit_ms, 3) if block_ms else None,
         "prefill_ms": round(prefill_ms, 2),
+        "entropy_bounded_sampler": ebr,
         "pass_tflops": round(flops / (ms_per_pass * 1e-3) / 1e12, 2),
         "mfma_util_pct": {
             "moe_grouped_gemm": round(100 * moe_tflops / BF16_PEAK_TFLOPS, 2),

@@ -356,6 +356,39 @@ __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm
 }
 
 // ------------------------------------------------------------------ sampler
+// Partial rank of position i among the flagged positions (keys ascending if ASC,
+// else descending; ties to the lower position) over the groups of four j4 = part,
+// part + 4, ...: four lanes share a position and their parts are summed by the
+// caller (rank_sum4).  Tail entries past C must be unflagged.
+template <bool ASC>
+DG_DEV int rank_part(const float* keys, const uint8_t* flag, int C4, int i, float ki, int part) {
+    int rank = 0;
+#pragma unroll 4
+    for (int j4 = part; j4 < C4; j4 += 4) {
+        const float4 c = reinterpret_cast<const float4*>(keys)[j4];
+        const uchar4 u = reinterpret_cast<const uchar4*>(flag)[j4];
+        const int j = 4 * j4;
+        if constexpr (ASC) {
+            rank += u.x && (c.x < ki || (c.x == ki && j < i));
+            rank += u.y && (c.y < ki || (c.y == ki && j + 1 < i));
+            rank += u.z && (c.z < ki || (c.z == ki && j + 2 < i));
+            rank += u.w && (c.w < ki || (c.w == ki && j + 3 < i));
+        } else {
+            rank += u.x && (c.x > ki || (c.x == ki && j < i));
+            rank += u.y && (c.y > ki || (c.y == ki && j + 1 < i));
+            rank += u.z && (c.z > ki || (c.z == ki && j + 2 < i));
+            rank += u.w && (c.w > ki || (c.w == ki && j + 3 < i));
+        }
+    }
+    return rank;
+}
+
+// Sum over the four adjacent lanes of a position (all four take part together).
+DG_DEV int rank_sum4(int r) {
+    r += __shfl_xor(r, 1, 64);
+    return r + __shfl_xor(r, 2, 64);
+}
+
 // One workgroup.  Among unlocked positions, the n_s with the highest
 // confidence (ties to the lower position) are locked to their argmax; the
 // other unlocked positions take their Gumbel draw.  Locked ones are untouched.
@@ -382,21 +415,11 @@ __global__ __launch_bounds__(1024) void k_sampler(const float* __restrict__ conf
     const int nu = n_unl;
     const int quota = (C + T - 1) / T;
     const int n_s = (step == T - 1) ? nu : (quota < nu ? quota : nu);
-    for (int i = threadIdx.x; i < C; i += blockDim.x) {
-        if (!un[i]) continue;
-        const float ci = cf[i];
-        int rank = 0;
-        // four positions per LDS read, 16 per unrolled step
-#pragma unroll 4
-        for (int j4 = 0; j4 < (C + 3) / 4; ++j4) {
-            const float4 c = reinterpret_cast<const float4*>(cf)[j4];
-            const uchar4 u = reinterpret_cast<const uchar4*>(un)[j4];
-            const int j = 4 * j4;
-            rank += u.x && (c.x > ci || (c.x == ci && j < i));
-            rank += u.y && (c.y > ci || (c.y == ci && j + 1 < i));
-            rank += u.z && (c.z > ci || (c.z == ci && j + 2 < i));
-            rank += u.w && (c.w > ci || (c.w == ci && j + 3 < i));
-        }
+    const int C4 = (C + 3) / 4, part = threadIdx.x & 3;
+    for (int i = threadIdx.x >> 2; i < C; i += blockDim.x >> 2) {   // four lanes per position
+        const bool u = un[i] != 0;
+        const int rank = rank_sum4(u ? rank_part<false>(cf, un, C4, i, cf[i], part) : 0);
+        if (!u || part != 0) continue;
         if (rank < n_s) {
             canvas[i] = amax[i];
             mask[i] = 1;
@@ -435,7 +458,7 @@ __global__ __launch_bounds__(1024) void k_sampler_eb(const float* __restrict__ e
                                                      int k_blk) {
     __shared__ __attribute__((aligned(16))) float hs[kMaxCanvas];
     __shared__ __attribute__((aligned(16))) uint8_t un[kMaxCanvas];
-    __shared__ float h_sorted[kMaxCanvas];
+    __shared__ __attribute__((aligned(16))) float h_sorted[kMaxCanvas];
     __shared__ int16_t rank_of[kMaxCanvas];
     __shared__ int n_unl, n_diff, n_acc, stop;
     const int tid = threadIdx.x;
@@ -457,41 +480,58 @@ __global__ __launch_bounds__(1024) void k_sampler_eb(const float* __restrict__ e
     if (mine) atomicAdd(&n_unl, mine);
     if (diff) atomicAdd(&n_diff, diff);
     __syncthreads();
-    for (int i = tid; i < C; i += blockDim.x) {
-        if (!un[i]) continue;
+    const int C4 = (C + 3) / 4, part = tid & 3;
+    for (int i = tid >> 2; i < C; i += blockDim.x >> 2) {   // four lanes per position
+        const bool u = un[i] != 0;
         const float hi = hs[i];
-        int rank = 0;
-#pragma unroll 4
-        for (int j4 = 0; j4 < (C + 3) / 4; ++j4) {
-            const float4 c = reinterpret_cast<const float4*>(hs)[j4];
-            const uchar4 u = reinterpret_cast<const uchar4*>(un)[j4];
-            const int j = 4 * j4;
-            rank += u.x && (c.x < hi || (c.x == hi && j < i));
-            rank += u.y && (c.y < hi || (c.y == hi && j + 1 < i));
-            rank += u.z && (c.z < hi || (c.z == hi && j + 2 < i));
-            rank += u.w && (c.w < hi || (c.w == hi && j + 3 < i));
+        const int rank = rank_sum4(u ? rank_part<true>(hs, un, C4, i, hi, part) : 0);
+        if (u && part == 0) {
+            rank_of[i] = (int16_t)rank;
+            h_sorted[rank] = hi;
         }
-        rank_of[i] = (int16_t)rank;
-        h_sorted[rank] = hi;
     }
     __syncthreads();
+    const float4* hs4 = reinterpret_cast<const float4*>(hs);
+    const float4* hq4 = reinterpret_cast<const float4*>(h_sorted);
     if (tid == 0) {
+        // position order; the padded tail adds zeros
         double acc = 0.0;
-        for (int i = 0; i < C; ++i) acc += (double)hs[i];
+#pragma unroll 8
+        for (int g = 0; g < C4; ++g) {
+            const float4 v = hs4[g];
+            acc += (double)v.x;
+            acc += (double)v.y;
+            acc += (double)v.z;
+            acc += (double)v.w;
+        }
         const bool rule = step >= 1 && n_diff == 0 && acc / (double)C < (double)theta;
         stop = rule ? 2 : (step == max_steps - 1 ? 1 : 0);
     } else if (tid == 64) {
+        // rank order, four sorted entropies per LDS read with the next four in flight
         const int nu = n_unl;
-        int n = 0;
-        if (nu > 0) {
-            n = 1;
-            double run = (double)h_sorted[0];
-            for (int k = 1; k < nu; ++k) {
-                const double hk = (double)h_sorted[k];
+        int n = nu > 0 ? 1 : 0;
+        double run = 0.0;
+        float4 v = hq4[0];
+        for (int g = 0; 4 * g < nu; ++g) {
+            const float4 nxt = hq4[(g + 1) < kMaxCanvas / 4 ? g + 1 : g];
+            const float w4[4] = {v.x, v.y, v.z, v.w};
+            bool go = true;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = 4 * g + q;
+                if (k >= nu) break;
+                const double hk = (double)w4[q];
                 run += hk;
-                if (run - hk < (double)gamma) n = k + 1;
-                else break;
+                if (k == 0) continue;
+                if (run - hk < (double)gamma) {
+                    n = k + 1;
+                } else {
+                    go = false;
+                    break;
+                }
             }
+            if (!go) break;
+            v = nxt;
         }
         n_acc = n;
     }
