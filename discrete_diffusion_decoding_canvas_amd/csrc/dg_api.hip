@@ -98,7 +98,8 @@ struct dg_handle {
     void* Af = nullptr;      // dense-projection activations in fragment order (bf16)
     void* H = nullptr;
     float* Y = nullptr;
-    int2* work_items = nullptr;
+    int2* work_items = nullptr;      // the first GEMM's items, then the second's
+    int work_cap1 = 0;               // capacity of the first list
     int32_t* work_count = nullptr;
     uint32_t* route_ticket = nullptr;
 
@@ -237,8 +238,10 @@ static int moe_pad(const dg_handle* h) { return h->edt == kF32 ? 1 : kMoePad; }
 static MoeWork moe_work(dg_handle* h, int n) {
     MoeWork w;
     w.items = h->work_items;
+    w.items2 = h->work_items + h->work_cap1;
     w.count = h->work_count;
-    w.max_items = (n * h->k + kMoeRows - 1) / kMoeRows + h->E;
+    w.max_items = (n * h->k + kMoeItemRows - 1) / kMoeItemRows + h->E;
+    w.max_items2 = (n * h->k + kMoeRows - 1) / kMoeRows + h->E;
     w.ticket = h->route_ticket;
     return w;
 }
@@ -512,8 +515,9 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->offsets, E + 1));
     A_TRY(h->allocT(&h->perm_token, rows));
     A_TRY(h->allocT(&h->inv, T * k));
-    A_TRY(h->allocT(&h->work_items, (T * k + kMoeRows - 1) / kMoeRows + E));
-    A_TRY(h->allocT(&h->work_count, 3));   // item count, two GEMM unit counters
+    h->work_cap1 = (T * k + kMoeItemRows - 1) / kMoeItemRows + E;
+    A_TRY(h->allocT(&h->work_items, (size_t)h->work_cap1 + (T * k + kMoeRows - 1) / kMoeRows + E));
+    A_TRY(h->allocT(&h->work_count, 4));   // item counts and the two GEMMs' unit counters
     A_TRY(h->allocT(&h->route_ticket, 1));
     if (hipMemset(h->route_ticket, 0, 4) != hipSuccess) return cleanup(fail(DG_EHIP, "ticket reset failed"));
     if (h->edt != kF32) A_TRY(h->alloc(&h->Xf, rows * d * esz));

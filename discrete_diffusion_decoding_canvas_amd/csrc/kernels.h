@@ -16,20 +16,33 @@ constexpr int32_t kBadNonFinite = 1;   // a row's logits statistics were not fin
 constexpr int32_t kBadToken = 2;       // a token id outside [0, V) was embedded
 constexpr int kMaxTopK = 16;       // experts per token
 constexpr int kCombineCols = 16;   // combine: columns per thread, d <= 256 * 16
-constexpr int kMoeRows = 256;      // rows of one expert-GEMM work item (a whole canvas)
+constexpr int kMoeRows = 256;      // rows one expert-GEMM workgroup covers (a whole canvas)
+#ifndef DG_MOE_ITEM_ROWS
+#define DG_MOE_ITEM_ROWS 128
+#endif
+// Rows of one work item of the first expert GEMM.  Below kMoeRows an expert with
+// many rows is split over several workgroups (its weights are read once per
+// item), which shortens the longest unit; the second GEMM (K = d_ff, short
+// units) keeps whole-canvas items.
+constexpr int kMoeItemRows = DG_MOE_ITEM_ROWS;
+static_assert(kMoeItemRows % 16 == 0 && kMoeItemRows <= kMoeRows, "work item rows");
 constexpr int kMaxRouterSplit = 8; // K split of the router GEMM (partials summed in top-k)
 constexpr int kMoePad = 16;        // expert row padding of the MFMA expert GEMMs (one row tile)
 
 // Permuted-row capacity for n tokens, k experts each, E experts, rows padded to pad.
 inline int64_t moe_rows_cap(int64_t n, int k, int E, int pad) { return n * k + (int64_t)E * (pad - 1); }
 
-// Expert-GEMM work list built by the permutation: item i covers rows
-// [row0, row0 + kMoeRows) of expert e (clipped to the expert's count).
+// Expert-GEMM work lists built by the permutation: item i of `items` covers rows
+// [row0, row0 + kMoeItemRows) of expert e (clipped to the expert's count), item i
+// of `items2` rows [row0, row0 + kMoeRows).
 struct MoeWork {
-    int2* items;       // {e, row0}
+    int2* items;       // {e, row0}, first GEMM
+    int2* items2;      // {e, row0}, second GEMM
     int32_t* count;    // [0] number of valid items; [1], [2] unit counters of the two
-                       // persistent expert GEMMs (zeroed by the kernel that writes [0])
-    int max_items;     // grid bound: ceil(entries / kMoeRows) + E
+                       // persistent expert GEMMs (zeroed by the kernel that writes [0]);
+                       // [3] number of valid items2
+    int max_items;     // grid bound: ceil(entries / kMoeItemRows) + E
+    int max_items2;    // grid bound: ceil(entries / kMoeRows) + E
     uint32_t* ticket;  // zero-initialised block counter of the fused top-k + permutation
 };
 

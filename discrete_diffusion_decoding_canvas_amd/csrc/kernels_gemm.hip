@@ -697,7 +697,7 @@ DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
     bare_barrier();   // every wave's copies landed and LDS reads done: the ring may be refilled
 }
 
-// One unit of an expert GEMM: a work item (up to kMoeRows rows of one expert)
+// One unit of an expert GEMM: a work item (up to kMoeItemRows rows of one expert)
 // times one kWideN-column slab.  Units are numbered item-major, so the slabs of
 // an item (which share its activation rows) are taken up together.
 struct MoeUnit {
@@ -706,6 +706,7 @@ struct MoeUnit {
     WeightStream ws;
 };
 
+template <int ITEM_ROWS>
 DG_DEV MoeUnit moe_unit(int u, int n_slabs, const int2* __restrict__ work,
                         const int32_t* __restrict__ offsets, int N, int KB, const void* W, int w,
                         int lane) {
@@ -713,7 +714,7 @@ DG_DEV MoeUnit moe_unit(int u, int n_slabs, const int2* __restrict__ work,
     const int2 item = work[u / n_slabs];
     c.e = item.x;
     c.off = offsets[c.e];                                          // a multiple of 16
-    c.n_e = min(offsets[c.e + 1] - c.off, item.y + kMoeRows);
+    c.n_e = min(offsets[c.e + 1] - c.off, item.y + ITEM_ROWS);
     c.n0 = (u % n_slabs) * kWideN;
     // rows r = item.y + 16 (kWideMT w + mt) + lane % 16 (expert-relative); n_e is
     // a multiple of 16, so a row tile is wholly inside or outside the expert
@@ -794,7 +795,8 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
     __syncthreads();
     const int u = __builtin_amdgcn_readfirstlane(s_unit[0]);
     if (u >= total) return;
-    MoeUnit c = moe_unit(u, n_slabs, work, offsets, N, KB, W, w, lane);
+    constexpr int kItem = GEMM == 1 ? kMoeItemRows : kMoeRows;   // rows of one work item
+    MoeUnit c = moe_unit<kItem>(u, n_slabs, work, offsets, N, KB, W, w, lane);
     wide_fill(c.ws, bsm);
     for (int it = 1;; ++it) {
         const bool rows = c.wr0 < c.n_e;          // uniform per wave
@@ -813,10 +815,10 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
         if (threadIdx.x == 0) s_unit[it & 1] = atomicAdd(unit_ctr, 1);
         __syncthreads();
         const int un = __builtin_amdgcn_readfirstlane(s_unit[it & 1]);
-        if (un < total) wide_fill(moe_unit(un, n_slabs, work, offsets, N, KB, W, w, lane).ws, bsm);
+        if (un < total) wide_fill(moe_unit<kItem>(un, n_slabs, work, offsets, N, KB, W, w, lane).ws, bsm);
         if (rows) moe_epilogue<FP8, GEMM>(acc, c, N, F, scales, out, lane);
         if (un >= total) break;
-        c = moe_unit(un, n_slabs, work, offsets, N, KB, W, w, lane);   // recomputed: less live state
+        c = moe_unit<kItem>(un, n_slabs, work, offsets, N, KB, W, w, lane);   // recomputed: less live state
     }
 }
 
@@ -1037,8 +1039,8 @@ static int persistent_wgs() {
     return cached[dev];
 }
 
-static unsigned moe_grid(const MoeWork& work, int n_slabs) {
-    const int64_t units = (int64_t)work.max_items * n_slabs;
+static unsigned moe_grid(int max_items, int n_slabs) {
+    const int64_t units = (int64_t)max_items * n_slabs;
     return (unsigned)std::min<int64_t>(units, persistent_wgs());
 }
 
@@ -1057,7 +1059,7 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
         if ((2 * F) % kWideN || d % kq || F % kq || !Xf) return hipErrorInvalidValue;
         (void)X;
         (void)perm_token;
-        const unsigned grid = moe_grid(work, (2 * F) / kWideN);
+        const unsigned grid = moe_grid(work.max_items, (2 * F) / kWideN);
         if (dtype == kFP8)
             k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
                                                               offsets, work.items, work.count,
@@ -1112,15 +1114,15 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
             (const float*)H, d, F, offsets, E, max_rows, (const float*)w.w2, Y);
     } else {
         if (d % 16 || F % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
-        const unsigned grid = moe_grid(work, (d + kWideN - 1) / kWideN);
+        const unsigned grid = moe_grid(work.max_items2, (d + kWideN - 1) / kWideN);
         if (dtype == kFP8)
             k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
-                                                              work.items, work.count, work.count + 2,
-                                                              w.w2, w.s2, Y);
+                                                              work.items2, work.count + 3,
+                                                              work.count + 2, w.w2, w.s2, Y);
         else
             k_moe_wide<false, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
-                                                               work.items, work.count, work.count + 2,
-                                                               w.w2, w.s2, Y);
+                                                               work.items2, work.count + 3,
+                                                               work.count + 2, w.w2, w.s2, Y);
     }
     return hipGetLastError();
 }

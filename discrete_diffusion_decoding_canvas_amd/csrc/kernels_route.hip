@@ -144,32 +144,42 @@ DG_DEV void wave0_exclusive_scan(int32_t* v, int n) {
     if (l == 63) v[n] = inc;
 }
 
+// Work items (expert, first row) of `rows`-row chunks of every expert, experts
+// in order; their number to *count.  woff is LDS scratch of E + 1 entries.
+DG_DEV void route_items(const int32_t* off, int E, int rows, int32_t* woff,
+                        int2* __restrict__ items, int32_t* __restrict__ count) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        woff[e] = (off[e + 1] - off[e] + rows - 1) / rows;
+    __syncthreads();
+    wave0_exclusive_scan(woff, E);
+    __syncthreads();
+    if (threadIdx.x == 0) *count = woff[E];
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        for (int i = woff[e]; i < woff[e + 1]; ++i) items[i] = make_int2(e, (i - woff[e]) * rows);
+    __syncthreads();   // woff is reused
+}
+
 // From per-expert entry counts cnt[0..E): padded row offsets (to global
-// `offsets` and LDS off), the expert-GEMM work items ((expert, first row) for
-// every kMoeRows-row chunk, experts in order) and -1 in perm_token for the
-// padding rows.  woff is LDS scratch of E + 1 entries.
+// `offsets` and LDS off), the work items of the two expert GEMMs
+// (kMoeItemRows- and kMoeRows-row chunks) and -1 in perm_token for the padding
+// rows.  woff is LDS scratch of E + 1 entries.
 DG_DEV void route_offsets(const int32_t* cnt, int E, int pad, int32_t* off, int32_t* woff,
                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
-                          int2* __restrict__ items, int32_t* __restrict__ count) {
+                          int2* __restrict__ items, int2* __restrict__ items2,
+                          int32_t* __restrict__ count) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) off[e] = round_up(cnt[e], pad);
     __syncthreads();
     wave0_exclusive_scan(off, E);
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        woff[e] = (off[e + 1] - off[e] + kMoeRows - 1) / kMoeRows;
-    __syncthreads();
-    wave0_exclusive_scan(woff, E);
-    __syncthreads();
+    route_items(off, E, kMoeItemRows, woff, items, count);
+    route_items(off, E, kMoeRows, woff, items2, count + 3);
     for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = off[e];
     if (threadIdx.x == 0) {
-        count[0] = woff[E];
         count[1] = 0;   // unit counters of the two expert GEMMs that read these items
         count[2] = 0;
     }
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        for (int i = woff[e]; i < woff[e + 1]; ++i) items[i] = make_int2(e, (i - woff[e]) * kMoeRows);
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
         for (int j = off[e] + cnt[e]; j < off[e + 1]; ++j) perm_token[j] = -1;
-    }
 }
 
 // The permutation of n <= kPermSmall entries by one block: counts, offsets,
@@ -179,7 +189,7 @@ constexpr int kPermSmall = 8192;
 DG_DEV void permute_block(const int32_t* __restrict__ idx, int n, int E, int k, int pad,
                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
                           int32_t* __restrict__ inv, int2* __restrict__ work,
-                          int32_t* __restrict__ work_count) {
+                          int2* __restrict__ work2, int32_t* __restrict__ work_count) {
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
     __shared__ int32_t woff[kMaxExperts + 1];
@@ -197,7 +207,7 @@ DG_DEV void permute_block(const int32_t* __restrict__ idx, int n, int E, int k, 
 #pragma unroll
     for (int i = 0; i < kPer; ++i) lp[i] = ex[i] >= 0 ? atomicAdd(&cnt[ex[i]], 1) : 0;
     __syncthreads();
-    route_offsets(cnt, E, pad, off, woff, offsets, perm_token, work, work_count);
+    route_offsets(cnt, E, pad, off, woff, offsets, perm_token, work, work2, work_count);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -220,6 +230,7 @@ __global__ __launch_bounds__(256) void k_router_route(const float* __restrict__ 
                                                       int32_t* __restrict__ perm_token,
                                                       int32_t* __restrict__ inv,
                                                       int2* __restrict__ work,
+                                                      int2* __restrict__ work2,
                                                       int32_t* __restrict__ work_count,
                                                       uint32_t* __restrict__ ticket) {
     __shared__ bool last;
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(256) void k_router_route(const float* __restrict__ 
     __syncthreads();
     if (!last) return;
     __threadfence();                                       // every block's idx visible here
-    permute_block(idx, M * k, E, k, pad, offsets, perm_token, inv, work, work_count);
+    permute_block(idx, M * k, E, k, pad, offsets, perm_token, inv, work, work2, work_count);
     if (threadIdx.x == 0) *ticket = 0u;
 }
 
@@ -258,6 +269,7 @@ __global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ co
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ perm_token,
                                                   int2* __restrict__ work,
+                                                  int2* __restrict__ work2,
                                                   int32_t* __restrict__ work_count) {
     __shared__ int32_t tot[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
@@ -271,7 +283,7 @@ __global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ co
         tot[e] = run;
     }
     __syncthreads();
-    route_offsets(tot, E, pad, off, woff, offsets, perm_token, work, work_count);
+    route_offsets(tot, E, pad, off, woff, offsets, perm_token, work, work2, work_count);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x)
         for (int c = 0; c < n_chunks; ++c) base[(int64_t)c * E + e] += off[e];
@@ -302,20 +314,22 @@ hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, 
                                  const MoeWork& work, int pad, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if (E > kMaxExperts || (E & 3) || k > 16 || nsplit > kMaxRouterSplit || pad < 1 ||
-        kMoeRows % pad)
+        kMoeItemRows % pad)
         return hipErrorInvalidValue;
     const int n = M * k;
-    if (work.max_items < (n + kMoeRows - 1) / kMoeRows + E) return hipErrorInvalidValue;
+    if (work.max_items < (n + kMoeItemRows - 1) / kMoeItemRows + E ||
+        work.max_items2 < (n + kMoeRows - 1) / kMoeRows + E)
+        return hipErrorInvalidValue;
     if (n <= kPermSmall) {
         k_router_route<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, pad, idx, gates,
                                                    offsets, perm_token, inv, work.items,
-                                                   work.count, work.ticket);
+                                                   work.items2, work.count, work.ticket);
     } else {
         k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
         const int n_chunks = (n + kPermChunk - 1) / kPermChunk;
         k_moe_count<<<n_chunks, 256, 0, s>>>(idx, n, E, counts);
         k_moe_scan<<<1, 256, 0, s>>>(counts, n_chunks, E, pad, base, offsets, perm_token,
-                                     work.items, work.count);
+                                     work.items, work.items2, work.count);
         k_moe_scatter<<<n_chunks, 256, 0, s>>>(idx, n, E, k, base, perm_token, inv);
     }
     return hipGetLastError();
