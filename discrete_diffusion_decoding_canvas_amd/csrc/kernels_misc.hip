@@ -71,9 +71,14 @@ __global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict
 
 // ------------------------------------------------------------------ RMSNorm
 // a = rmsnorm(x) (unit gains); a8 (optional) = e4m3(a) for fp8 expert inputs.
-// One block per row, four columns per thread per pass (d % 4 == 0): every load
-// of the row is issued before the reduction.
-constexpr int kRowPasses = kCombineCols / 4;   // float4 passes per thread: d <= 1024 * kRowPasses
+// One block of NT threads per row, four columns per thread per pass (d % 4 == 0):
+// every load of the row is issued before the reduction.  d <= 4096.
+#ifndef DG_ROW_THREADS
+#define DG_ROW_THREADS 1024
+#endif
+constexpr int kRowThreads = DG_ROW_THREADS;    // block of the row kernels (norm, combine)
+template <int NT>
+constexpr int row_passes() { return 1024 / NT; }   // float4 passes per thread for d = 4096
 
 template <typename T>
 DG_DEV void store4(T* dst, float4 v) {
@@ -91,12 +96,12 @@ DG_DEV void store4(T* dst, float4 v) {
 
 // Normalised row `row` (xs scaled by r) to a (as T), a8 (e4m3 of the rounded a) and
 // af (the bf16 row in fragment order, frag_offset with K = 4 d4).
-template <typename T>
-DG_DEV void store_norm(const float4 (&xs)[kRowPasses], float r, int d4, T* __restrict__ a,
+template <typename T, int NT>
+DG_DEV void store_norm(const float4 (&xs)[row_passes<NT>()], float r, int d4, T* __restrict__ a,
                        uint8_t* __restrict__ a8, uint8_t* __restrict__ af, int64_t row) {
 #pragma unroll
-    for (int p = 0; p < kRowPasses; ++p) {
-        const int c4 = threadIdx.x + 256 * p;
+    for (int p = 0; p < row_passes<NT>(); ++p) {
+        const int c4 = threadIdx.x + NT * p;
         if (c4 >= d4) break;
         const float4 v = make_float4(xs[p].x * r, xs[p].y * r, xs[p].z * r, xs[p].w * r);
         store4<T>(a + 4 * (int64_t)c4, v);
@@ -112,24 +117,24 @@ DG_DEV void store_norm(const float4 (&xs)[kRowPasses], float r, int d4, T* __res
     }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int d, float eps,
-                                                 T* __restrict__ a, uint8_t* __restrict__ a8,
-                                                 uint8_t* __restrict__ af) {
-    __shared__ float red[4];
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void k_rmsnorm(const float* __restrict__ x, int d, float eps,
+                                                T* __restrict__ a, uint8_t* __restrict__ a8,
+                                                uint8_t* __restrict__ af) {
+    __shared__ float red[NT / 64];
     const int64_t row = blockIdx.x;
     const int d4 = d >> 2;
     const float4* xr = reinterpret_cast<const float4*>(x + row * d);
-    float4 xs[kRowPasses];
+    float4 xs[row_passes<NT>()];
     float ss = 0.f;
 #pragma unroll
-    for (int p = 0; p < kRowPasses; ++p) {
-        const int c4 = threadIdx.x + 256 * p;
+    for (int p = 0; p < row_passes<NT>(); ++p) {
+        const int c4 = threadIdx.x + NT * p;
         xs[p] = c4 < d4 ? xr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
         ss += xs[p].x * xs[p].x + xs[p].y * xs[p].y + xs[p].z * xs[p].z + xs[p].w * xs[p].w;
     }
-    const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-    store_norm<T>(xs, r, d4, a + row * d, a8 ? a8 + row * d : nullptr, af, row);
+    const float r = rsqrtf(block_sum<NT>(ss, red) / (float)d + eps);
+    store_norm<T, NT>(xs, r, d4, a + row * d, a8 ? a8 + row * d : nullptr, af, row);
 }
 
 // ------------------------------------------------------------------ RoPE + scatter
@@ -213,17 +218,17 @@ __global__ void k_write_kv(T* __restrict__ cache, int Hkv, int D, int64_t rows, 
 // y = sum_j gates[t, j] * Y[inv[t*k + j], :] in slot order.
 // MODE 0: x += y, then a = rmsnorm(x) (and a8 = e4m3(a) if given) when a != null.
 // MODE 1: out = y (stored as T), no residual (the stand-alone MoE layer).
-// One block per token, four columns per thread per pass (d % 4 == 0); all of
+// One block of NT threads per token, four columns per thread per pass (d % 4 == 0); all of
 // the token's expert rows are loaded before they are summed.
-template <typename T, int MODE, int KMAX>
-__global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y, int d, int k,
+template <typename T, int MODE, int KMAX, int NT>
+__global__ __launch_bounds__(NT) void k_moe_combine(const float* __restrict__ Y, int d, int k,
                                                      const float* __restrict__ gates,
                                                      const int32_t* __restrict__ inv,
                                                      float* __restrict__ x, float eps,
                                                      T* __restrict__ a, uint8_t* __restrict__ a8,
                                                      uint8_t* __restrict__ af,
                                                      T* __restrict__ out) {
-    __shared__ float red[4];
+    __shared__ float red[NT / 64];
     const int64_t t = blockIdx.x;
     const int d4 = d >> 2;
     float g[KMAX];
@@ -234,11 +239,11 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y
         yr[j] = reinterpret_cast<const float4*>(Y + (int64_t)(j < k ? inv[t * k + j] : inv[t * k]) * d);
     }
     float4* xr = reinterpret_cast<float4*>(x + t * d);
-    float4 xs[kRowPasses];
+    float4 xs[row_passes<NT>()];
     float ss = 0.f;
 #pragma unroll
-    for (int p = 0; p < kRowPasses; ++p) {
-        const int c4 = threadIdx.x + 256 * p;
+    for (int p = 0; p < row_passes<NT>(); ++p) {
+        const int c4 = threadIdx.x + NT * p;
         if (c4 >= d4) break;
         float4 v[KMAX];
 #pragma unroll
@@ -263,8 +268,8 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ Y
         }
     }
     if (MODE == 0 && a != nullptr) {
-        const float r = rsqrtf(block_sum<256>(ss, red) / (float)d + eps);
-        store_norm<T>(xs, r, d4, a + t * d, a8 ? a8 + t * d : nullptr, af, t);
+        const float r = rsqrtf(block_sum<NT>(ss, red) / (float)d + eps);
+        store_norm<T, NT>(xs, r, d4, a + t * d, a8 ? a8 + t * d : nullptr, af, t);
     }
 }
 
@@ -642,11 +647,11 @@ hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, c
 hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
                           uint8_t* a8, void* af, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    if ((d & 3) || d > 1024 * kRowPasses) return hipErrorInvalidValue;
+    if ((d & 3) || d > 4096) return hipErrorInvalidValue;
     if (dtype == kF32)
-        k_rmsnorm<float><<<M, 256, 0, s>>>(x, d, eps, (float*)a, a8, nullptr);
+        k_rmsnorm<float, kRowThreads><<<M, kRowThreads, 0, s>>>(x, d, eps, (float*)a, a8, nullptr);
     else
-        k_rmsnorm<bf16_t><<<M, 256, 0, s>>>(x, d, eps, (bf16_t*)a, a8, (uint8_t*)af);
+        k_rmsnorm<bf16_t, kRowThreads><<<M, kRowThreads, 0, s>>>(x, d, eps, (bf16_t*)a, a8, (uint8_t*)af);
     LAUNCH_CHECK();
 }
 
@@ -718,8 +723,9 @@ template <typename T, int MODE, int KMAX>
 static void combine_k(const float* Y, int M, int d, int k, const float* gates, const int32_t* inv,
                       float* x, float eps, void* a, uint8_t* a8, void* af, void* out,
                       hipStream_t s) {
-    k_moe_combine<T, MODE, KMAX><<<M, 256, 0, s>>>(Y, d, k, gates, inv, x, eps, (T*)a, a8,
-                                                   (uint8_t*)af, (T*)out);
+    k_moe_combine<T, MODE, KMAX, kRowThreads><<<M, kRowThreads, 0, s>>>(Y, d, k, gates, inv, x, eps,
+                                                                        (T*)a, a8, (uint8_t*)af,
+                                                                        (T*)out);
 }
 
 template <typename T, int MODE>
@@ -736,7 +742,7 @@ hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d,
                               const float* gates, const int32_t* inv, float* x, float eps,
                               void* a, uint8_t* a8, void* af, void* out, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    if ((d & 3) || d > 1024 * kRowPasses || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
+    if ((d & 3) || d > 4096 || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
     if (dtype == kF32) {
         if (mode == 0) combine_m<float, 0>(Y, M, d, k, gates, inv, x, eps, a, a8, nullptr, nullptr, s);
         else combine_m<float, 1>(Y, M, d, k, gates, inv, x, eps, nullptr, nullptr, nullptr, out, s);
