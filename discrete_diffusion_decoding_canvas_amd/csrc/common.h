@@ -13,6 +13,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));  // MFMA bf16 opera
 typedef float f32x4_t __attribute__((ext_vector_type(4)));    // MFMA 16x16 accumulator
 typedef long fp8x8_t;                            // 8 packed e4m3 codes (MFMA fp8 operand)
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));  // MFMA f16 operand
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- conversions
 DG_DEV float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }

@@ -222,7 +222,8 @@ struct AttnArgs {
     float scale;
     int causal;
     int64_t q_pos0;
-    float* part_o;         // split partials workspace
+    float* part_o;         // split partials workspace: binary16 averages (first half of the
+                           // n Hq M D floats), then float (max, sum) pairs
     float* part_ml;
     int64_t part_capacity; // floats available in part_o
 };

@@ -369,11 +369,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                                                                       Hq * kAttnD)) = pk;
             }
         } else {
+            // the split's own softmax average (bounded by max |V|) as binary16,
+            // rounded to nearest and saturated at its largest finite value
             const int64_t pr = ((int64_t)split * Hq + h) * M + q;
-            float* dst = part_o + pr * kAttnD;
+            const float inv = l > 0.f ? 1.0f / l : 0.f;
+            _Float16* dst = reinterpret_cast<_Float16*>(part_o) + pr * kAttnD;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                *reinterpret_cast<f32x4_t*>(dst + 16 * dt + 4 * g) = o[qb][dt];
+            for (int dt = 0; dt < 8; ++dt) {
+                f16x4_t pk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pk[i] = (_Float16)fminf(fmaxf(o[qb][dt][i] * inv, -65504.f), 65504.f);
+                *reinterpret_cast<f16x4_t*>(dst + 16 * dt + 4 * g) = pk;
+            }
             if (g == 0) {
                 part_ml[pr * 2 + 0] = m_ref[qb];   // log2 units, as the weights
                 part_ml[pr * 2 + 1] = l;
@@ -382,7 +390,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
 }
 
-// Fixed-order combine of the key splits: O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s.
+// Fixed-order combine of the key splits: with each split's average A_s = O_s / l_s
+// (stored as binary16), O = sum_s 2^(m_s - m*) l_s A_s / sum_s 2^(m_s - m*) l_s.
 // One wave per (query, head); each lane owns two of the 128 dimensions.
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
@@ -402,16 +411,17 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
         ls = ml.y;
     }
     const float mstar = wave_max(ms);
-    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - mstar);
-    const float den = wave_sum(wgt * ls);
+    const float wl = (ms == -INFINITY) ? 0.f : exp2f(ms - mstar) * ls;
+    const float den = wave_sum(wl);
+    const _Float16* pa = reinterpret_cast<const _Float16*>(part_o);
     float n0 = 0.f, n1 = 0.f;
 #pragma unroll 8
     for (int s = 0; s < n_splits; ++s) {
-        const float ws = __shfl(wgt, s, 64);
+        const float ws = __shfl(wl, s, 64);
         const int64_t pr = ((int64_t)s * Hq + h) * M + q;
-        const float2 v = *reinterpret_cast<const float2*>(part_o + pr * kAttnD + 2 * lane);
-        n0 += ws * v.x;
-        n1 += ws * v.y;
+        const f16x2_t v = *reinterpret_cast<const f16x2_t*>(pa + pr * kAttnD + 2 * lane);
+        n0 += ws * (float)v[0];
+        n1 += ws * (float)v[1];
     }
     T* dst = O + (int64_t)q * Hq * kAttnD + (int64_t)h * kAttnD + 2 * lane;
     const T o0 = from_f32<T>(n0 / den), o1 = from_f32<T>(n1 / den);
