@@ -94,7 +94,7 @@ struct dg_handle {
     int32_t* offsets = nullptr;
     int32_t* perm_token = nullptr;
     int32_t* inv = nullptr;
-    void* Xf = nullptr;      // expert GEMM 1 activations in fragment order (bf16/fp8)
+    void* Xf = nullptr;      // fp8 expert GEMM 1 activations in fragment order
     void* Af = nullptr;      // dense-projection activations in fragment order (bf16)
     void* H = nullptr;
     float* Y = nullptr;
@@ -306,7 +306,10 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
     ExpertWeights w = expert_weights(h, l);
     const int rows = (int)moe_rows_cap(n, h->k, h->E, moe_pad(h));
     const void* X1 = (h->edt == kFP8) ? (const void*)xin8 : xin;
-    K_TRY(launch_moe_gather(h->edt, X1, h->d, h->perm_token, h->offsets, h->E, rows, h->Xf, s));
+    // fp8 experts take their inputs gathered into fragment order; the bf16 GEMM reads
+    // the token rows in place
+    if (h->edt == kFP8)
+        K_TRY(launch_moe_gather(h->edt, X1, h->d, h->perm_token, h->offsets, h->E, rows, h->Xf, s));
     {
         ProfScope p(h, DG_PROF_MOE_GEMM1, s);
         K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows,
@@ -520,7 +523,7 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->work_count, 4));   // item counts and the two GEMMs' unit counters
     A_TRY(h->allocT(&h->route_ticket, 1));
     if (hipMemset(h->route_ticket, 0, 4) != hipSuccess) return cleanup(fail(DG_EHIP, "ticket reset failed"));
-    if (h->edt != kF32) A_TRY(h->alloc(&h->Xf, rows * d * esz));
+    if (h->edt == kFP8) A_TRY(h->alloc(&h->Xf, rows * d * esz));
     if (h->act == kBF16)
         A_TRY(h->alloc(&h->Af, (T + 15) / 16 * 16 * std::max<size_t>(d, (size_t)h->Hq * h->D) * 2));
     A_TRY(h->alloc(&h->H, rows * F * esz));

@@ -468,13 +468,15 @@ using WideFrag = Frag16[2][kWideMT];              // [k-step][row tile]
 // Activation fragments of stage st of the k-step range [kb_lo, kb_hi) (clamped).
 // afrag[mt] points at the row tile's fragment of k-step 0 plus lane * 16 bytes;
 // k-steps are 1 KiB apart, so each load is one contiguous 1 KiB per wave.
+// astride: bytes from one k-step to the next (1 KiB in fragment order, 64 B along a
+// natural bf16 row).
 DG_DEV void wide_load_a(WideFrag& a, const uint8_t* const (&afrag)[kWideMT], int st, int kb_lo,
-                        int kb_hi) {
+                        int kb_hi, uint32_t astride) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int kb = min(kb_lo + 2 * st + ks, kb_hi - 1);
 #pragma unroll
-        for (int mt = 0; mt < kWideMT; ++mt) a[ks][mt].u = ld16(afrag[mt] + (size_t)kb * 1024);
+        for (int mt = 0; mt < kWideMT; ++mt) a[ks][mt].u = ld16(afrag[mt] + (size_t)kb * astride);
     }
 }
 
@@ -659,7 +661,8 @@ DG_DEV void wide_wait_first(int u) {
 // unrolled over kRing * kWideSlots stages.
 template <bool FP8>
 DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
-                          const WeightStream& ws, WideRing& bsm, int lane) {
+                          const WeightStream& ws, WideRing& bsm, int lane,
+                          uint32_t astride = 1024) {
     const int NS = ws.NS;
 #pragma unroll
     for (int mt = 0; mt < kWideMT; ++mt)
@@ -668,7 +671,8 @@ DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
     asm volatile("" ::: "memory");   // the copies stay ahead of the activation loads
     WideFrag ra[kWideSlots];
 #pragma unroll
-    for (int j = 0; j < kWideLead; ++j) wide_load_a(ra[j], afrag, min(j, NS - 1), ws.kb_lo, ws.kb_hi);
+    for (int j = 0; j < kWideLead; ++j)
+        wide_load_a(ra[j], afrag, min(j, NS - 1), ws.kb_lo, ws.kb_hi, astride);
     asm volatile("" ::: "memory");
     // issued after the copies of stage 0: the other kRing - 2 stages' copies and
     // kWideLead stages of activations
@@ -682,7 +686,7 @@ DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
             const int st = s0 + u;
             if (st >= NS) break;
             wide_load_a(ra[(u + kWideLead) % kWideSlots], afrag, min(st + kWideLead, NS - 1),
-                        ws.kb_lo, ws.kb_hi);
+                        ws.kb_lo, ws.kb_hi, astride);
             wide_copy_b(ws, st + kRing - 1, (u + kRing - 1) % kRing, bsm);
             __builtin_amdgcn_sched_barrier(0);      // issue the loads before the MFMAs
             wide_mma<FP8>(acc, ra[u % kWideSlots], bsm[u % kRing], ws.kb_lo + 2 * st + 1 < ws.kb_hi,
@@ -773,6 +777,11 @@ DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
     }
 }
 
+// Activations: Af in fragment order (frag_offset) by permuted row, or, with perm
+// (bf16 GEMM 1), the natural bf16 token rows X [tokens][K]: lane l of a row tile
+// reads 16 bytes of token perm[row0 + l % 16] (token 0 for padding rows, whose
+// results are never combined) at k-chunk l / 16 of each k-step, the same
+// fragment the permutation would have copied.
 // Persistent: about one workgroup per CU, each taking units from the counter
 // unit_ctr (zeroed by the routing kernel that wrote the work items) until
 // work_count * n_slabs are taken.  After a unit's last stage the workgroup
@@ -784,7 +793,7 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
     const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
     const int2* __restrict__ work, const int32_t* __restrict__ work_count,
     int32_t* __restrict__ unit_ctr, const void* __restrict__ W, const float* __restrict__ scales,
-    void* __restrict__ out) {
+    void* __restrict__ out, const int32_t* __restrict__ perm) {
     __shared__ __attribute__((aligned(16))) WideRing bsm;
     __shared__ int s_unit[2];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -806,9 +815,14 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
 #pragma unroll
             for (int mt = 0; mt < kWideMT; ++mt) {
                 const int r = c.wr0 + 16 * mt < c.n_e ? c.wr0 + 16 * mt : c.wr0;   // past the rows: tile 0
-                afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 16;
+                if (!FP8 && perm != nullptr) {
+                    const int tok = max(perm[c.off + r + (lane & 15)], 0);
+                    afrag[mt] = Af + ((size_t)tok * K + 8 * (lane >> 4)) * 2;
+                } else {
+                    afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 16;
+                }
             }
-            wide_mainloop<FP8>(acc, afrag, c.ws, bsm, lane);
+            wide_mainloop<FP8>(acc, afrag, c.ws, bsm, lane, !FP8 && perm != nullptr ? 64u : 1024u);
         } else {
             wide_stream_only(c.ws, bsm);
         }
@@ -1056,18 +1070,21 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
             (const float*)w.wu, (float*)H);
     } else {
         const int kq = dtype == kFP8 ? 64 : 32;
-        if ((2 * F) % kWideN || d % kq || F % kq || !Xf) return hipErrorInvalidValue;
-        (void)X;
-        (void)perm_token;
+        if ((2 * F) % kWideN || d % kq || F % kq) return hipErrorInvalidValue;
         const unsigned grid = moe_grid(work.max_items, (2 * F) / kWideN);
-        if (dtype == kFP8)
+        if (dtype == kFP8) {
+            if (!Xf) return hipErrorInvalidValue;
             k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
                                                               offsets, work.items, work.count,
-                                                              work.count + 1, w.w1, w.s1, H);
-        else
-            k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
+                                                              work.count + 1, w.w1, w.s1, H,
+                                                              nullptr);
+        } else {
+            // token rows read in place through the permutation
+            k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)X, d, 2 * F, F,
                                                                offsets, work.items, work.count,
-                                                               work.count + 1, w.w1, w.s1, H);
+                                                               work.count + 1, w.w1, w.s1, H,
+                                                               perm_token);
+        }
     }
     return hipGetLastError();
 }
@@ -1118,11 +1135,13 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
         if (dtype == kFP8)
             k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
                                                               work.items2, work.count + 3,
-                                                              work.count + 2, w.w2, w.s2, Y);
+                                                              work.count + 2, w.w2, w.s2, Y,
+                                                              nullptr);
         else
             k_moe_wide<false, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
                                                                work.items2, work.count + 3,
-                                                               work.count + 2, w.w2, w.s2, Y);
+                                                               work.count + 2, w.w2, w.s2, Y,
+                                                               nullptr);
     }
     return hipGetLastError();
 }
