@@ -203,8 +203,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_bf16(const bf16_t* __restrict
 #ifndef DG_DENSE_WAVES
 #define DG_DENSE_WAVES 8
 #endif
-constexpr int kDenseMT = 4;
-constexpr int kDensePrefetch = 4;
+#ifndef DG_DENSE_MT
+#define DG_DENSE_MT 4
+#endif
+#ifndef DG_DENSE_PREFETCH
+#define DG_DENSE_PREFETCH 4
+#endif
+constexpr int kDenseMT = DG_DENSE_MT;
+constexpr int kDensePrefetch = DG_DENSE_PREFETCH;
 constexpr int kDenseWaves = DG_DENSE_WAVES;
 constexpr int kDenseThreads = 64 * kDenseWaves;
 
