@@ -16,10 +16,10 @@
 //     partial tiles are summed once through LDS in a fixed order; narrow GEMMs
 //     (the router, N = E) split K across workgroups as well and leave the
 //     partial sums to their consumer, which adds them in order;
-//   * expert GEMMs: a workgroup owns all rows of an expert (up to a whole
-//     canvas) for a 64-column slab, the weight fragments go through LDS once
-//     and feed every wave, so an expert's weights leave HBM once per pass
-//     however many tokens it received;
+//   * expert GEMMs: a workgroup owns up to 256 rows of an expert (the second
+//     GEMM: all of them; the first: 128, so that an expert with many rows is
+//     spread over more CUs) for a 128-column slab, and the weight fragments go
+//     through LDS once and feed every wave;
 //   * tokens sit on the 16-row MFMA side (v_mfma_f32_16x16x32_bf16, or
 //     v_mfma_f32_16x16x32_fp8_fp8 for e4m3 experts);
 //   * the SwiGLU of the first expert GEMM runs in the epilogue (gate and up
@@ -403,10 +403,11 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 
 // ------------------------------------------------------------------ expert GEMMs (MFMA)
 // A unit is (kWideN-column weight slab, work item); a work item is up to
-// kMoeRows = 256 rows of one expert (a whole canvas), so an expert's weights
-// leave HBM once per pass.  Wide slabs keep the activation traffic, which every
-// slab re-reads, at K * 2 bytes per row per kWideN output columns.  The kernels
-// are persistent (about one workgroup per CU taking units in turn).
+// kMoeItemRows (GEMM 1) or kMoeRows = 256 (GEMM 2, a whole canvas) rows of one
+// expert, so an expert's weights leave HBM once per item.  Wide slabs keep the
+// activation traffic, which every slab re-reads, at K * 2 bytes per row per
+// kWideN output columns.  The kernels are persistent (about one workgroup per
+// CU taking units in turn).
 //
 // kWideWaves waves, each with two roles:
 //   * weight streaming: a stage is two packed k-steps of the slab's kWideNT
