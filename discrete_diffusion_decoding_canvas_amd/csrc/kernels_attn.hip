@@ -478,10 +478,13 @@ __global__ __launch_bounds__(64) void k_attn_f32(const float* __restrict__ Q,
 
 // ================================================================== launchers
 // Splits of the key range: about 256 workgroups in total, at least 256 keys each.
+#ifndef DG_ATTN_TARGET_WGS
+#define DG_ATTN_TARGET_WGS 256
+#endif
 static int attn_splits(int Hq, int Hkv, int M, int S) {
     const int G = Hq / Hkv;
     const int qwgs = Hkv * ((G * M + kAttnRows - 1) / kAttnRows);
-    int n = (256 + qwgs - 1) / qwgs;
+    int n = (DG_ATTN_TARGET_WGS + qwgs - 1) / qwgs;
     const int max_by_keys = (S + 255) / 256;
     if (n > max_by_keys) n = max_by_keys;
     if (n > 64) n = 64;
