@@ -229,7 +229,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the denoise pass is "
-              "measured on a single MI355X; multi-GPU sharding is not part of this build.",
+              "measured on a single MI355X; sharding across GPUs is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 
