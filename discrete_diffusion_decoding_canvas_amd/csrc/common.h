@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #define DG_DEV __device__ __forceinline__
 
 namespace dg {
@@ -18,6 +20,11 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- conversions
 DG_DEV float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+// Nearest binary16 of a float; finite values beyond +-65504 saturate there, NaN and
+// infinities pass through (so that the non-finite checks downstream still see them).
+DG_DEV _Float16 f32_to_f16_sat(float v) {
+    return (_Float16)(fabsf(v) <= 65504.f || !isfinite(v) ? v : copysignf(65504.f, v));
+}
 
 DG_DEV bf16_t f32_to_bf16(float f) {            // round to nearest even
     uint32_t u = __float_as_uint(f);

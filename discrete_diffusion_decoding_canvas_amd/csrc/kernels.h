@@ -106,7 +106,7 @@ hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, 
                                  float* gates, int32_t* counts, int32_t* base, int32_t* offsets,
                                  int32_t* perm_token, int32_t* inv, const MoeWork& work, int pad,
                                  hipStream_t s);
-hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
+hipError_t launch_moe_combine(int dtype, int mode, const void* Y, int M, int d, int k,
                               const float* gates, const int32_t* inv, float* x, float eps,
                               void* a, uint8_t* a8, void* af, void* out, hipStream_t s);
 hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint64_t seed,
@@ -193,7 +193,7 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             hipStream_t s);
 hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
                             const int32_t* offsets, int E, int d, int F, int max_rows,
-                            const MoeWork& work, float* Y, hipStream_t s);
+                            const MoeWork& work, float* Y, hipStream_t s);   // Y: binary16 rows unless f32
 
 // LM head: per (row, slice) partial max / argmax / sum-exp / Gumbel best of
 // z = (h E^T) / tau over the vocabulary.  Gumbel noise for rows with mask == 0.

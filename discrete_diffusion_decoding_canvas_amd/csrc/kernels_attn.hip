@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
             }
         } else {
             // the split's own softmax average (bounded by max |V|) as binary16,
-            // rounded to nearest and saturated at its largest finite value
+            // rounded to nearest, finite values saturated at its largest one
             const int64_t pr = ((int64_t)split * Hq + h) * M + q;
             const float inv = l > 0.f ? 1.0f / l : 0.f;
             _Float16* dst = reinterpret_cast<_Float16*>(part_o) + pr * kAttnD;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                 f16x4_t pk;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    pk[i] = (_Float16)fminf(fmaxf(o[qb][dt][i] * inv, -65504.f), 65504.f);
+                    pk[i] = f32_to_f16_sat(o[qb][dt][i] * inv);
                 *reinterpret_cast<f16x4_t*>(dst + 16 * dt + 4 * g) = pk;
             }
             if (g == 0) {

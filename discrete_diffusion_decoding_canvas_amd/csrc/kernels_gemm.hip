@@ -429,8 +429,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 //           [g_j | u_j | g_j+1 | u_j+1 | ...] (16 each), so a lane holds the
 //           gate and up values of the same (row, column) and the SwiGLU runs in
 //           registers.
-//   GEMM 2: Y[entry, :d] = H[entry] Wd_e (fp32).  Column groups past d (when
-//           d is not a multiple of kWideN) read as zero and are not stored.
+//   GEMM 2: Y[entry, :d] = H[entry] Wd_e, stored as binary16 (f32_to_f16_sat)
+//           for the combine.  Column groups past d (when d is not a multiple of
+//           kWideN) read as zero and are not stored.
 // fp8: e4m3 operands on both sides, per output column scales applied after the
 // accumulation.
 #ifndef DG_WIDE_RING
@@ -777,7 +778,7 @@ DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = c.wr0 + 16 * mt + g4 + i;
-                    ((float*)out)[(size_t)(c.off + r) * N + col] = acc[mt][nt][i] * sc;
+                    ((_Float16*)out)[(size_t)(c.off + r) * N + col] = f32_to_f16_sat(acc[mt][nt][i] * sc);
                 }
             }
         }

@@ -221,7 +221,7 @@ __global__ void k_write_kv(T* __restrict__ cache, int Hkv, int D, int64_t rows, 
 // One block of NT threads per token, four columns per thread per pass (d % 4 == 0); all of
 // the token's expert rows are loaded before they are summed.
 template <typename T, int MODE, int KMAX, int NT>
-__global__ __launch_bounds__(NT) void k_moe_combine(const float* __restrict__ Y, int d, int k,
+__global__ __launch_bounds__(NT) void k_moe_combine(const void* __restrict__ Yv, int d, int k,
                                                      const float* __restrict__ gates,
                                                      const int32_t* __restrict__ inv,
                                                      float* __restrict__ x, float eps,
@@ -231,12 +231,16 @@ __global__ __launch_bounds__(NT) void k_moe_combine(const float* __restrict__ Y,
     __shared__ float red[NT / 64];
     const int64_t t = blockIdx.x;
     const int d4 = d >> 2;
+    // expert outputs: float rows for f32 experts, binary16 rows otherwise (bf16 activations)
+    using YT = std::conditional_t<sizeof(T) == 4, float, _Float16>;
+    using Y4 = std::conditional_t<sizeof(T) == 4, float4, f16x4_t>;
+    const YT* Y = static_cast<const YT*>(Yv);
     float g[KMAX];
-    const float4* yr[KMAX];
+    const Y4* yr[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         g[j] = j < k ? gates[t * k + j] : 0.f;
-        yr[j] = reinterpret_cast<const float4*>(Y + (int64_t)(j < k ? inv[t * k + j] : inv[t * k]) * d);
+        yr[j] = reinterpret_cast<const Y4*>(Y + (int64_t)(j < k ? inv[t * k + j] : inv[t * k]) * d);
     }
     float4* xr = reinterpret_cast<float4*>(x + t * d);
     float4 xs[row_passes<NT>()];
@@ -247,7 +251,14 @@ __global__ __launch_bounds__(NT) void k_moe_combine(const float* __restrict__ Y,
         if (c4 >= d4) break;
         float4 v[KMAX];
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) v[j] = j < k ? yr[j][c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < KMAX; ++j) {
+            if (j < k) {
+                const Y4 yv = yr[j][c4];
+                v[j] = make_float4((float)yv[0], (float)yv[1], (float)yv[2], (float)yv[3]);
+            } else {
+                v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
         float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {   // slot order
@@ -720,7 +731,7 @@ hipError_t launch_write_kv(int dtype, bool vpacked, void* cache, int Hkv, int D,
 }
 
 template <typename T, int MODE, int KMAX>
-static void combine_k(const float* Y, int M, int d, int k, const float* gates, const int32_t* inv,
+static void combine_k(const void* Y, int M, int d, int k, const float* gates, const int32_t* inv,
                       float* x, float eps, void* a, uint8_t* a8, void* af, void* out,
                       hipStream_t s) {
     k_moe_combine<T, MODE, KMAX, kRowThreads><<<M, kRowThreads, 0, s>>>(Y, d, k, gates, inv, x, eps,
@@ -729,7 +740,7 @@ static void combine_k(const float* Y, int M, int d, int k, const float* gates, c
 }
 
 template <typename T, int MODE>
-static void combine_m(const float* Y, int M, int d, int k, const float* gates, const int32_t* inv,
+static void combine_m(const void* Y, int M, int d, int k, const float* gates, const int32_t* inv,
                       float* x, float eps, void* a, uint8_t* a8, void* af, void* out,
                       hipStream_t s) {
     if (k <= 2) combine_k<T, MODE, 2>(Y, M, d, k, gates, inv, x, eps, a, a8, af, out, s);
@@ -738,7 +749,7 @@ static void combine_m(const float* Y, int M, int d, int k, const float* gates, c
     else combine_k<T, MODE, kMaxTopK>(Y, M, d, k, gates, inv, x, eps, a, a8, af, out, s);
 }
 
-hipError_t launch_moe_combine(int dtype, int mode, const float* Y, int M, int d, int k,
+hipError_t launch_moe_combine(int dtype, int mode, const void* Y, int M, int d, int k,
                               const float* gates, const int32_t* inv, float* x, float eps,
                               void* a, uint8_t* a8, void* af, void* out, hipStream_t s) {
     if (M <= 0) return hipSuccess;
