@@ -392,7 +392,7 @@ def main():
     moe1_us = per_class_us["moe_gemm1"]
     moe1_bytes = int(moe1_algorithmic_bytes(w, mean_active))
     moe1_gbs = moe1_bytes / (moe1_us * 1e-6) / 1e9
-    moe2_bytes = int(mean_active * w.d_ff * w.d_model * 2 + C * w.top_k * (w.d_ff * 2 + w.d_model * 4))
+    moe2_bytes = int(mean_active * w.d_ff * w.d_model * 2 + C * w.top_k * (w.d_ff * 2 + w.d_model * 2))
     moe2_gbs = moe2_bytes / (per_class_us["moe_gemm2"] * 1e-6) / 1e9
     S = w.prompt_len + C
     attn_flops = 4 * C * S * w.head_dim * w.n_q_heads

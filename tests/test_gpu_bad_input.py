@@ -90,3 +90,22 @@ def test_nan_router_weights(dg):
         log("NaN router weights: expert ids in range, DG_ENONFINITE, then DG_ETOKEN")
     finally:
         dg.dg_destroy(h)
+
+
+def test_nan_expert_weights_reach_the_flag(dg):
+    """NaN in the second expert GEMM's weights: the binary16 expert outputs keep the NaN
+    (saturation applies to finite values only), so the pass's statistics flag it."""
+    h = build_handle(dg, W)
+    try:
+        nan = np.full(fx.tensor_shape(W, "wd"), 0x7FC0, dtype=np.uint16)   # bf16 quiet NaN
+        dg.dg_load_tensor(h, dg.DG_T_WD, 0, -1, nan)
+        dg.dg_prefill_prompt_kv(h, i32_dev(fx.prompt_ids(W)), W.prompt_len)
+        canvas = torch.empty(W.canvas, dtype=torch.int32, device="cuda")
+        mask = torch.empty(W.canvas, dtype=torch.uint8, device="cuda")
+        dg.dg_init_canvas(h, canvas, mask, 9)
+        dg.dg_denoise_step(h, canvas, mask, 0, 4, 9)
+        torch.cuda.synchronize()
+        assert _flag(dg, h) in (dg.DG_ENONFINITE, dg.DG_ETOKEN)
+        log("NaN expert weights: flagged")
+    finally:
+        dg.dg_destroy(h)
