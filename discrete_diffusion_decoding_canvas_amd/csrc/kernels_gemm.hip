@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 // fp8: e4m3 operands on both sides, per output column scales applied after the
 // accumulation.
 #ifndef DG_WIDE_RING
-#define DG_WIDE_RING 8
+#define DG_WIDE_RING 6
 #endif
 constexpr int kWideNT = 8;                          // 16-column groups per slab
 constexpr int kWideN = 16 * kWideNT;                // slab width
