@@ -27,7 +27,7 @@ EXPORTED = (
     "dg_reset_context", "dg_get_state", "dg_get_capture", "dg_get_kv", "dg_attention",
     "dg_moe_layer", "dg_init_canvas", "dg_profile_begin", "dg_profile_end", "dg_set_kv",
     "dg_set_capture", "dg_set_graphs", "dg_eb_sample", "dg_denoise_step_eb",
-    "dg_generate_block_eb",
+    "dg_generate_block_eb", "dg_attention_workspace_size",
 )
 DG_PROF_MOE_GEMM1, DG_PROF_MOE_GEMM2, DG_PROF_ATTENTION, DG_PROF_LM_HEAD, DG_PROF_DENSE = range(5)
 DG_PROF_N = 5
@@ -88,7 +88,9 @@ def _load_library():
         "dg_set_capture": ([vp, u32], i32),
         "dg_set_graphs": ([vp, i32], i32),
         "dg_attention": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float, i32, i32,
-                          i32, vp], i32),
+                          i32, vp, sz, vp], i32),
+        "dg_attention_workspace_size": ([i32, i32, i32, i32, i32, i32, i32, i32,
+                                         ctypes.POINTER(sz)], i32),
         "dg_moe_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
         "dg_init_canvas": ([vp, vp, vp, u64, vp], i32),
         "dg_profile_begin": ([vp, i32], i32),
@@ -240,10 +242,25 @@ def dg_set_kv(h, layer: int, which: int, row0: int, n: int, d_src, stream=None) 
     _check(_lib.dg_set_kv(h, layer, which, row0, n, _ptr(d_src), _stream(stream)))
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def dg_attention_workspace_size(Hq: int, Hkv: int, M: int, S: int, D: int, causal: bool,
+                                q_pos0: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.dg_attention_workspace_size(Hq, Hkv, M, S, D, int(bool(causal)), q_pos0, dtype,
+                                            ctypes.byref(n)))
+    return n.value
+
+
 def dg_attention(d_q, d_k, d_v, d_o, Hq: int, Hkv: int, M: int, S: int, D: int, scale: float,
-                 causal: bool, q_pos0: int, dtype: int, stream=None) -> None:
+                 causal: bool, q_pos0: int, dtype: int, d_workspace=None, stream=None) -> None:
+    """d_workspace: device tensor of at least dg_attention_workspace_size bytes (or None
+    when that is 0)."""
     _check(_lib.dg_attention(_ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_o), Hq, Hkv, M, S, D,
-                             scale, int(bool(causal)), q_pos0, dtype, _stream(stream)))
+                             scale, int(bool(causal)), q_pos0, dtype, _ptr(d_workspace),
+                             _nbytes(d_workspace), _stream(stream)))
 
 
 def dg_moe_layer(h, layer: int, d_x, n_tokens: int, d_y, d_idx=None, d_gates=None,

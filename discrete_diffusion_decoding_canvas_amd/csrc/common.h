@@ -20,10 +20,14 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- conversions
 DG_DEV float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-// Nearest binary16 of a float; finite values beyond +-65504 saturate there, NaN and
-// infinities pass through (so that the non-finite checks downstream still see them).
-DG_DEV _Float16 f32_to_f16_sat(float v) {
-    return (_Float16)(fabsf(v) <= 65504.f || !isfinite(v) ? v : copysignf(65504.f, v));
+// Nearest binary16 of a float.  Finite values that would round beyond the
+// largest finite binary16 (|v| >= 65520) saturate at +-65504 and set `range`;
+// NaN and infinities pass through (the non-finite checks downstream see them).
+DG_DEV _Float16 f32_to_f16_sat(float v, bool& range) {
+    const float a = fabsf(v);
+    const bool big = a >= 65520.f && a != __builtin_inff();
+    range |= big;
+    return (_Float16)(big ? copysignf(65504.f, v) : v);
 }
 
 DG_DEV bf16_t f32_to_bf16(float f) {            // round to nearest even

@@ -14,7 +14,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <map>
 #include <string>
 #include <vector>
 
@@ -84,8 +83,8 @@ struct dg_handle {
     float* qkv = nullptr;
     void* q = nullptr;
     void* attn_o = nullptr;
-    float* part = nullptr;
-    int64_t part_floats = 0;
+    void* part = nullptr;     // attention split partials
+    size_t part_bytes = 0;
     float* rlog = nullptr;
     int32_t* idx = nullptr;
     float* gates = nullptr;
@@ -309,7 +308,7 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
     // fp8 experts take their inputs gathered into fragment order; the bf16 GEMM reads
     // the token rows in place
     if (h->edt == kFP8)
-        K_TRY(launch_moe_gather(h->edt, X1, h->d, h->perm_token, h->offsets, h->E, rows, h->Xf, s));
+        K_TRY(launch_moe_gather8(X1, h->d, h->perm_token, h->offsets, h->E, rows, h->Xf, s));
     {
         ProfScope p(h, DG_PROF_MOE_GEMM1, s);
         K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows,
@@ -318,7 +317,7 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
     {
         ProfScope p(h, DG_PROF_MOE_GEMM2, s);
         K_TRY(launch_moe_gemm2(h->edt, w, h->H, h->offsets, h->E, h->d, h->F, rows,
-                               moe_work(h, n), h->Y, s));
+                               moe_work(h, n), h->Y, h->bad, s));
     }
     return DG_OK;
 }
@@ -371,9 +370,9 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
     aa.scale = 1.0f / sqrtf((float)h->D);
     aa.causal = causal ? 1 : 0;
     aa.q_pos0 = pos0;
-    aa.part_o = h->part;
-    aa.part_ml = nullptr;
-    aa.part_capacity = h->part_floats;
+    aa.part = h->part;
+    aa.part_bytes = h->part_bytes;
+    aa.bad = h->bad;
     {
         ProfScope p(h, DG_PROF_ATTENTION, s);
         K_TRY(launch_attention(h->act, aa, s));
@@ -503,10 +502,9 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     if (h->act == kF32) A_TRY(h->allocT(&h->qkv, T * h->qkv_n));   // bf16: RoPE in the QKV epilogue
     A_TRY(h->alloc(&h->q, T * h->Hq * h->D * as));
     A_TRY(h->alloc(&h->attn_o, T * h->Hq * h->D * as));
-    // split-KV partials: the split count keeps (splits x query workgroups) near 512,
-    // so (D + 2) floats for at most 1024 x 128 query rows bound every call
-    h->part_floats = h->act == kF32 ? 64 : (int64_t)1024 * 128 * (h->D + 2);
-    A_TRY(h->allocT(&h->part, (size_t)h->part_floats));
+    // split-KV partials, sized for the largest split call of any batch size
+    h->part_bytes = h->act == kF32 ? 256 : attention_part_bytes_bound(h->D);
+    A_TRY(h->alloc(&h->part, h->part_bytes));
     A_TRY(h->allocT(&h->rlog, T * E * kRouterSplit));
     A_TRY(h->allocT(&h->idx, T * k));
     A_TRY(h->allocT(&h->gates, T * k));
@@ -927,7 +925,9 @@ static int check_bad(dg_handle* h, hipStream_t s) {
         HIP_TRY(launch_fill_u32(h->bad, 0u, 1, s));
         HIP_TRY(hipStreamSynchronize(s));
         if (bad & kBadToken) return fail(DG_ETOKEN, "a token id outside [0, %d) was embedded", h->V);
-        return fail(DG_ENONFINITE, "non-finite logits statistics");
+        if (bad & kBadNonFinite) return fail(DG_ENONFINITE, "non-finite logits statistics");
+        return fail(DG_ENONFINITE, "an expert output or attention split average exceeded the "
+                                   "binary16 range (|value| >= 65520) and was saturated");
     }
     return DG_OK;
 }
@@ -1087,30 +1087,34 @@ int dg_set_kv(dg_handle* h, int32_t layer, int32_t which, int64_t row0, int64_t 
 
 // ---------------------------------------------------------------- kernel-level entry points
 namespace {
-struct AttnWorkspace {
-    void* vt = nullptr;
-    size_t vt_bytes = 0;
-    float* part = nullptr;
-    size_t part_floats = 0;
-};
-std::map<int, AttnWorkspace> g_attn_ws;   // per device; calls on one device must not overlap
-}  // namespace
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, int32_t Hq,
-                 int32_t Hkv, int32_t M, int32_t S, int32_t D, float scale, int32_t causal,
-                 int32_t q_pos0, int32_t dtype, void* stream) {
-    g_err.clear();
-    if (!d_q || !d_k || !d_v || !d_o) return fail(DG_EINVAL, "NULL tensor");
+// Rows of the transposed V copy a bf16 attention call packs (a multiple of 32).
+int64_t attn_vt_rows(int32_t S) { return ((int64_t)S + 31) & ~(int64_t)31; }
+
+int check_attention_args(int32_t Hq, int32_t Hkv, int32_t M, int32_t S, int32_t D,
+                         int32_t causal, int32_t q_pos0, int32_t dtype) {
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || M <= 0 || S <= 0 || D <= 0 || q_pos0 < 0)
         return fail(DG_EINVAL, "bad attention sizes");
     if (dtype != DG_F32 && dtype != DG_BF16) return fail(DG_EINVAL, "dtype must be DG_F32 or DG_BF16");
     if (dtype == DG_F32 && D != 64 && D != 128) return fail(DG_EINVAL, "f32 needs D 64 or 128");
     if (dtype == DG_BF16 && D != 128) return fail(DG_EINVAL, "bf16 needs D 128");
     if (causal && (int64_t)q_pos0 + M > S) return fail(DG_EINVAL, "causal queries beyond the keys");
-    hipStream_t s = (hipStream_t)stream;
-    int dev = 0;
-    HIP_TRY(hipGetDevice(&dev));
-    AttnWorkspace& ws = g_attn_ws[dev];
+    return DG_OK;
+}
+
+// Workspace of a bf16 call: the transposed, key-permuted copy of V, then the split
+// partials.  f32 calls need none.
+size_t attention_ws_bytes(int32_t Hq, int32_t Hkv, int32_t M, int32_t S, int32_t D, int32_t dtype) {
+    if (dtype != DG_BF16) return 0;
+    return align256((size_t)Hkv * D * attn_vt_rows(S) * 2) +
+           attention_part_bytes(kBF16, Hq, Hkv, M, S, D);
+}
+
+// The attention call on a workspace of ws_bytes at d_ws (sizes already checked).
+int run_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, int32_t Hq,
+                  int32_t Hkv, int32_t M, int32_t S, int32_t D, float scale, int32_t causal,
+                  int32_t q_pos0, int32_t dtype, void* d_ws, size_t ws_bytes, hipStream_t s) {
     AttnArgs aa;
     aa.q = d_q;
     aa.k = d_k;
@@ -1126,37 +1130,43 @@ int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, i
     aa.scale = scale;
     aa.causal = causal;
     aa.q_pos0 = q_pos0;
-    aa.part_ml = nullptr;
     const int dt = dtype == DG_F32 ? kF32 : kBF16;
-    const size_t pf = (size_t)attention_part_floats(dt, Hq, Hkv, M, S, D);
     if (dt == kBF16) {
-        const int64_t rows = ((int64_t)S + 31) & ~(int64_t)31;
-        const size_t vb = (size_t)Hkv * D * rows * 2;
-        if (vb > ws.vt_bytes || pf > ws.part_floats) {
-            HIP_TRY(hipStreamSynchronize(s));
-            if (vb > ws.vt_bytes) {
-                if (ws.vt) (void)hipFree(ws.vt);
-                ws.vt = nullptr;
-                ws.vt_bytes = 0;
-                if (hipMalloc(&ws.vt, vb) != hipSuccess) return fail(DG_ENOMEM, "attention workspace");
-                ws.vt_bytes = vb;
-            }
-            if (pf > ws.part_floats) {
-                if (ws.part) (void)hipFree(ws.part);
-                ws.part = nullptr;
-                ws.part_floats = 0;
-                if (hipMalloc(&ws.part, pf * 4) != hipSuccess) return fail(DG_ENOMEM, "attention workspace");
-                ws.part_floats = pf;
-            }
-        }
-        HIP_TRY(launch_pack_vt(d_v, Hkv, S, D, ws.vt, rows, s));
-        aa.v = ws.vt;
+        const int64_t rows = attn_vt_rows(S);
+        const size_t vb = align256((size_t)Hkv * D * rows * 2);
+        HIP_TRY(launch_pack_vt(d_v, Hkv, S, D, d_ws, rows, s));
+        aa.v = d_ws;
         aa.v_rows = rows;
+        aa.part = (char*)d_ws + vb;
+        aa.part_bytes = ws_bytes - vb;
     }
-    aa.part_o = ws.part;
-    aa.part_capacity = (int64_t)ws.part_floats;
     HIP_TRY(launch_attention(dt, aa, s));
     return DG_OK;
+}
+}  // namespace
+
+int dg_attention_workspace_size(int32_t Hq, int32_t Hkv, int32_t M, int32_t S, int32_t D,
+                                int32_t causal, int32_t q_pos0, int32_t dtype, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(DG_EINVAL, "NULL bytes");
+    DG_TRY(check_attention_args(Hq, Hkv, M, S, D, causal, q_pos0, dtype));
+    *bytes = attention_ws_bytes(Hq, Hkv, M, S, D, dtype);
+    return DG_OK;
+}
+
+int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, int32_t Hq,
+                 int32_t Hkv, int32_t M, int32_t S, int32_t D, float scale, int32_t causal,
+                 int32_t q_pos0, int32_t dtype, void* d_workspace, size_t workspace_bytes,
+                 void* stream) {
+    g_err.clear();
+    if (!d_q || !d_k || !d_v || !d_o) return fail(DG_EINVAL, "NULL tensor");
+    DG_TRY(check_attention_args(Hq, Hkv, M, S, D, causal, q_pos0, dtype));
+    const size_t need = attention_ws_bytes(Hq, Hkv, M, S, D, dtype);
+    if (need > 0 && (!d_workspace || workspace_bytes < need))
+        return fail(DG_EINVAL, "attention workspace of %zu bytes needed, %zu given", need,
+                    d_workspace ? workspace_bytes : (size_t)0);
+    return run_attention(d_q, d_k, d_v, d_o, Hq, Hkv, M, S, D, scale, causal, q_pos0, dtype,
+                         d_workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int dg_moe_layer(dg_handle* h, int32_t layer, const void* d_x, int32_t n_tokens, void* d_y,

@@ -17,14 +17,7 @@
 
 namespace dg {
 
-constexpr int kHeadRows = 256;    // rows per workgroup (4 row waves x 64)
-constexpr int kHeadTile = 256;    // vocabulary ids per workgroup (2 column waves)
-constexpr int kHeadCols = 128;    // vocabulary ids per wave = one partial slice
-
-union HFrag {
-    uint4 u;
-    bf16x8_t b;
-};
+constexpr int kHeadCols = 128;    // vocabulary ids of one partial slice (one weight slab)
 
 struct Run {
     float m;

@@ -14,6 +14,8 @@ constexpr int kMaxCanvas = 1024;   // sampler capacity (one workgroup)
 // Bits of the handle's sticky error word.
 constexpr int32_t kBadNonFinite = 1;   // a row's logits statistics were not finite
 constexpr int32_t kBadToken = 2;       // a token id outside [0, V) was embedded
+constexpr int32_t kBadRange = 4;       // an expert output or attention split average saturated
+                                       // at the binary16 range (|value| >= 65520)
 constexpr int kMaxTopK = 16;       // experts per token
 constexpr int kCombineCols = 16;   // combine: columns per thread, d <= 256 * 16
 constexpr int kMoeRows = 256;      // rows one expert-GEMM workgroup covers (a whole canvas)
@@ -160,22 +162,23 @@ struct RopeArgs {
 hipError_t launch_gemm(int dtype, int epi, const void* A, int lda, int M, const void* B, int K,
                        int N, float* C, int ldc, hipStream_t s, int ksplit = 1);
 // The same product (bf16) with A in MFMA A-fragment order ([row/16][K/32][64][16 B],
-// rows padded to 16), as written by launch_pack_afrag or by the producing kernel.
+// rows padded to 16), as written by the kernel that produces A.
 // epi = kEpiRope: B packed with rope_hd = 128, N = (Hq + 2 Hkv) * 128, C unused.
 hipError_t launch_gemm_frag(int epi, const void* Af, int M, const void* B, int K, int N, float* C,
                             int ldc, hipStream_t s, int ksplit = 1,
                             const RopeArgs* rope = nullptr);
-hipError_t launch_pack_afrag(const void* A, int M, int K, void* Af, hipStream_t s);
 
 // Expert GEMMs over the permuted entries (offsets[e]..offsets[e+1] belong to expert e).
 // GEMM 1: H[entry, :F] = silu(x Wg_e) * (x Wu_e), x = X[perm_token[entry]].
-//   bf16: X bf16 [*, d], W1 packed with interleaved gate/up groups, H bf16.
-//   fp8 : X e4m3 [*, d], W1 packed e4m3 + column scales (2F), H e4m3.
+//   bf16: X bf16 [*, d] natural token rows, read in place through perm_token;
+//         W1 packed with interleaved gate/up groups; H bf16.
+//   fp8 : Xf e4m3 in MFMA A-operand fragment order (launch_moe_gather8:
+//         [row / 16][k-step][lane][16 bytes], padding rows zero); W1 packed
+//         e4m3 + column scales (2F); H e4m3.
 //   f32 : X f32, Wg/Wu row-major [E][d][F], H f32.
-//   bf16/fp8 read x from Xf (launch_moe_gather: MFMA A-operand fragment order,
-//   [row / 16][k-step][lane][16 bytes], padding rows zero) and write H in the
-//   same order for GEMM 2; rows padded to kMoePad, max_rows = moe_rows_cap.
-// GEMM 2: Y[entry, :d] = H[entry] Wd_e (float).
+//   bf16/fp8 write H in fragment order for GEMM 2; rows padded to kMoePad,
+//   max_rows = moe_rows_cap.
+// GEMM 2: Y[entry, :d] = H[entry] Wd_e (binary16 rows, f32 for f32 experts).
 struct ExpertWeights {
     const void* w1;        // bf16/fp8 packed gate|up, or f32 Wg
     const void* wu;        // f32 Wu (f32 path only)
@@ -183,17 +186,18 @@ struct ExpertWeights {
     const float* s1;       // fp8 column scales of w1 [E][2F] (interleaved)
     const float* s2;       // fp8 column scales of w2 [E][d]
 };
-// GEMM 1's activation fragments: Xf = X[perm_token] in MFMA A-operand order
-// (bf16/fp8; padding rows zero).  No-op for f32.
-hipError_t launch_moe_gather(int dtype, const void* X, int d, const int32_t* perm_token,
-                             const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s);
+// fp8 GEMM 1's activation fragments: Xf = X[perm_token] (e4m3) in MFMA A-operand
+// order, padding rows zero.
+hipError_t launch_moe_gather8(const void* X, int d, const int32_t* perm_token,
+                              const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s);
 hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             const int32_t* perm_token, const int32_t* offsets, int E, int d,
                             int F, int max_rows, const MoeWork& work, void* Xf, void* H,
                             hipStream_t s);
+// bad (optional): kBadRange is set when a binary16 output saturates.
 hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
                             const int32_t* offsets, int E, int d, int F, int max_rows,
-                            const MoeWork& work, float* Y, hipStream_t s);   // Y: binary16 rows unless f32
+                            const MoeWork& work, float* Y, int32_t* bad, hipStream_t s);
 
 // LM head: per (row, slice) partial max / argmax / sum-exp / Gumbel best of
 // z = (h E^T) / tau over the vocabulary.  Gumbel noise for rows with mask == 0.
@@ -222,12 +226,19 @@ struct AttnArgs {
     float scale;
     int causal;
     int64_t q_pos0;
-    float* part_o;         // split partials workspace: binary16 averages (first half of the
-                           // n Hq M D floats), then float (max, sum) pairs
-    float* part_ml;
-    int64_t part_capacity; // floats available in part_o
+    void* part = nullptr;  // split partials workspace (attention_part_bytes): binary16
+                           // averages [split][Hq][M][D], then float (max, sum) pairs
+    size_t part_bytes = 0; // bytes available at part
+    int32_t* bad = nullptr; // optional: kBadRange when a binary16 split average saturates
 };
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
-int64_t attention_part_floats(int dtype, int Hq, int Hkv, int M, int S, int D);
+// Bytes of split partials a call with these sizes needs (0 when it runs unsplit).
+size_t attention_part_bytes(int dtype, int Hq, int Hkv, int M, int S, int D);
+// Query rows x splits of any split call stay below this bound, whatever M and S:
+// a handle sized for it never runs short.
+constexpr int64_t kAttnMaxPartRows = 131072;
+inline size_t attention_part_bytes_bound(int D) {
+    return (size_t)kAttnMaxPartRows * D * 2 + 256 + (size_t)kAttnMaxPartRows * 8;
+}
 
 }  // namespace dg

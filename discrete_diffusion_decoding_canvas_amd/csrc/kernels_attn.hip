@@ -6,13 +6,15 @@
 // alphasignal, paragraph on bidirectional attention: every canvas position
 // attends to every other).  GQA: query head h reads KV head h / (Hq / Hkv).
 //
-// bf16 kernel (D = 128).  A workgroup of 8 waves owns 256 query rows of one KV
-// head's group (the G query heads of the group packed row after row) and a
-// range of keys; the key range is split over workgroups for occupancy and the
-// splits are merged by a fixed-order combine.  Per block of 32 keys the eight
-// waves load K and V once into double-buffered LDS (row pitches padded so the
-// 16-byte fragment reads are bank-conflict free) and every wave reads its
-// MFMA fragments from there:
+// bf16 kernel (D = 128).  A workgroup owns 256 query rows of one KV head's
+// group (the G query heads of the group packed row after row) and a range of
+// keys; the key range is split over workgroups for occupancy and the splits
+// are merged by a fixed-order combine.  Two producer waves copy every 32-key
+// block of K (16-byte pieces of the key rows) and of V^T (the transposed,
+// key-permuted cache) into a 6-block LDS ring with global_load_lds, landing in
+// MFMA fragment order and keeping the consumers two blocks ahead; eight
+// consumer waves own 32 query rows each and read their operand fragments from
+// the ring:
 //   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16, A = K rows, B = Q rows) puts the
 //   scores of one query in one lane column, so the online-softmax statistics
 //   and the rescale of the output stay lane-local;
@@ -153,7 +155,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ Vt,
     int Hq, int Hkv, int M, int S, int64_t k_rows, int64_t v_rows, float scale_log2,
     int64_t q_pos0, int keys_per_split, int n_splits, bf16_t* __restrict__ O,
-    uint8_t* __restrict__ Of, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    uint8_t* __restrict__ Of, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int32_t* __restrict__ bad) {
     __shared__ AttnSlot ring[kAttnRing];
     const int G = Hq / Hkv;
     const int GM = G * M;
@@ -374,14 +377,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
             const int64_t pr = ((int64_t)split * Hq + h) * M + q;
             const float inv = l > 0.f ? 1.0f / l : 0.f;
             _Float16* dst = reinterpret_cast<_Float16*>(part_o) + pr * kAttnD;
+            bool range = false;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 f16x4_t pk;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    pk[i] = f32_to_f16_sat(o[qb][dt][i] * inv);
+                    pk[i] = f32_to_f16_sat(o[qb][dt][i] * inv, range);
                 *reinterpret_cast<f16x4_t*>(dst + 16 * dt + 4 * g) = pk;
             }
+            if (range && bad) atomicOr(bad, kBadRange);
             if (g == 0) {
                 part_ml[pr * 2 + 0] = m_ref[qb];   // log2 units, as the weights
                 part_ml[pr * 2 + 1] = l;
@@ -481,6 +486,10 @@ __global__ __launch_bounds__(64) void k_attn_f32(const float* __restrict__ Q,
 #ifndef DG_ATTN_TARGET_WGS
 #define DG_ATTN_TARGET_WGS 256
 #endif
+// With T target workgroups and 256-row query workgroups, a split call (n >= 2
+// splits) has fewer than T query workgroups, so Hq M < 256 T, and n Hq M <
+// (T / qwgs + 1) Hq M <= 256 T + Hq M < 512 T query rows of partials.
+static_assert(2 * 256 * DG_ATTN_TARGET_WGS <= kAttnMaxPartRows, "partials bound");
 static int attn_splits(int Hq, int Hkv, int M, int S) {
     const int G = Hq / Hkv;
     const int qwgs = Hkv * ((G * M + kAttnRows - 1) / kAttnRows);
@@ -491,10 +500,23 @@ static int attn_splits(int Hq, int Hkv, int M, int S) {
     return n < 1 ? 1 : n;
 }
 
-int64_t attention_part_floats(int dtype, int Hq, int Hkv, int M, int S, int D) {
-    if (dtype == kF32) return 0;
-    const int n = attn_splits(Hq, Hkv, M, S);
-    return n > 1 ? (int64_t)n * Hq * M * (D + 2) : 0;
+// Split count and keys per split (a multiple of the 32-key block).
+static void attn_split_plan(int Hq, int Hkv, int M, int S, int& n, int& kps) {
+    n = attn_splits(Hq, Hkv, M, S);
+    kps = (S + n - 1) / n;
+    kps = (kps + 31) & ~31;
+    n = (S + kps - 1) / kps;
+}
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t attention_part_bytes(int dtype, int Hq, int Hkv, int M, int S, int D) {
+    if (dtype == kF32 || M <= 0 || S <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
+    int n, kps;
+    attn_split_plan(Hq, Hkv, M, S, n, kps);
+    if (n <= 1) return 0;
+    const size_t rows = (size_t)n * Hq * M;
+    return align256(rows * D * 2) + rows * 8;
 }
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
@@ -517,27 +539,28 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
     }
     if (a.D != kAttnD || (a.v_rows & 31) || a.v_rows < a.S || a.kv_rows < a.S)
         return hipErrorInvalidValue;
-    int n = attn_splits(a.Hq, a.Hkv, a.M, a.S);
-    int kps = (a.S + n - 1) / n;
-    kps = (kps + 31) & ~31;
-    n = (a.S + kps - 1) / kps;
-    if (n > 1 && (int64_t)n * a.Hq * a.M * (a.D + 2) > a.part_capacity) return hipErrorInvalidValue;
+    int n, kps;
+    attn_split_plan(a.Hq, a.Hkv, a.M, a.S, n, kps);
+    const size_t prow = (size_t)n * a.Hq * a.M;
+    if (n > 1 && (!a.part || align256(prow * a.D * 2) + prow * 8 > a.part_bytes))
+        return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
     dim3 grid((G * a.M + kAttnRows - 1) / kAttnRows, a.Hkv, n);
     const float sl2 = a.scale * 1.4426950408889634f;
-    float* pml = a.part_o + (int64_t)n * a.Hq * a.M * a.D;
+    float* po = (float*)a.part;
+    float* pml = n > 1 ? (float*)((char*)a.part + align256(prow * a.D * 2)) : nullptr;
     if (a.causal)
         k_attn_bf16<true><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                (const bf16_t*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                a.kv_rows, a.v_rows, sl2, a.q_pos0, kps, n,
-                                               (bf16_t*)a.o, (uint8_t*)a.of, a.part_o, pml);
+                                               (bf16_t*)a.o, (uint8_t*)a.of, po, pml, a.bad);
     else
         k_attn_bf16<false><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                 (const bf16_t*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                 a.kv_rows, a.v_rows, sl2, a.q_pos0, kps, n,
-                                                (bf16_t*)a.o, (uint8_t*)a.of, a.part_o, pml);
+                                                (bf16_t*)a.o, (uint8_t*)a.of, po, pml, a.bad);
     if (n > 1)
-        k_attn_combine<bf16_t><<<(a.M * a.Hq + 3) / 4, 256, 0, s>>>(a.part_o, pml, n, a.Hq, a.M,
+        k_attn_combine<bf16_t><<<(a.M * a.Hq + 3) / 4, 256, 0, s>>>(po, pml, n, a.Hq, a.M,
                                                                     (bf16_t*)a.o, (uint8_t*)a.of);
     return hipGetLastError();
 }

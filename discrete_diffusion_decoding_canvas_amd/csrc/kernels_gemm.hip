@@ -337,23 +337,6 @@ __global__ __launch_bounds__(kDenseThreads) void k_dense_frag(const uint8_t* __r
     }
 }
 
-// Natural row-major bf16 A [M][K] -> fragment order (see frag_offset), rows padded
-// to a multiple of 16 with zeros.
-__global__ void k_pack_afrag(const bf16_t* __restrict__ A, int M, int K, uint8_t* __restrict__ Af) {
-    const int KB = K >> 5;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (tile, kb, lane)
-    const int64_t total = (int64_t)((M + 15) >> 4) * KB * 64;
-    if (idx >= total) return;
-    const int lane = (int)(idx & 63);
-    const int64_t tk = idx >> 6;
-    const int kb = (int)(tk % KB);
-    const int64_t t = tk / KB;
-    const int64_t row = t * 16 + (lane & 15);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < M) v = *reinterpret_cast<const uint4*>(A + row * K + kb * 32 + 8 * (lane >> 4));
-    *reinterpret_cast<uint4*>(Af + idx * 16) = v;
-}
-
 // ------------------------------------------------------------------ dense f32 GEMM (VALU)
 // 64x64 tile, 256 threads x (4x4) outputs, K steps of 16 through LDS.
 template <int EPI>
@@ -429,8 +412,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 //           [g_j | u_j | g_j+1 | u_j+1 | ...] (16 each), so a lane holds the
 //           gate and up values of the same (row, column) and the SwiGLU runs in
 //           registers.
-//   GEMM 2: Y[entry, :d] = H[entry] Wd_e, stored as binary16 (f32_to_f16_sat)
-//           for the combine.  Column groups past d (when d is not a multiple of
+//   GEMM 2: Y[entry, :d] = H[entry] Wd_e, stored as binary16 (f32_to_f16_sat;
+//           a saturated value sets kBadRange in *bad) for the combine.  Column groups past d (when d is not a multiple of
 //           kWideN) read as zero and are not stored.
 // fp8: e4m3 operands on both sides, per output column scales applied after the
 // accumulation.
@@ -747,8 +730,10 @@ DG_DEV MoeUnit moe_unit(int u, int n_slabs, const int2* __restrict__ work,
 // Epilogue of a unit: lane holds column lane % 16 of each group, rows 4 (lane / 16) + i.
 template <bool FP8, int GEMM>
 DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
-                         const float* __restrict__ scales, void* __restrict__ out, int lane) {
+                         const float* __restrict__ scales, void* __restrict__ out, int lane,
+                         int32_t* __restrict__ bad) {
     const int l16 = lane & 15, g4 = 4 * (lane >> 4);
+    bool range = false;
 #pragma unroll
     for (int mt = 0; mt < kWideMT; ++mt) {
         if (c.wr0 + 16 * mt >= c.n_e) break;
@@ -778,11 +763,13 @@ DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = c.wr0 + 16 * mt + g4 + i;
-                    ((_Float16*)out)[(size_t)(c.off + r) * N + col] = f32_to_f16_sat(acc[mt][nt][i] * sc);
+                    ((_Float16*)out)[(size_t)(c.off + r) * N + col] =
+                        f32_to_f16_sat(acc[mt][nt][i] * sc, range);
                 }
             }
         }
     }
+    if (range && bad) atomicOr(bad, kBadRange);
 }
 
 // Activations: Af in fragment order (frag_offset) by permuted row, or, with perm
@@ -801,7 +788,7 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
     const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
     const int2* __restrict__ work, const int32_t* __restrict__ work_count,
     int32_t* __restrict__ unit_ctr, const void* __restrict__ W, const float* __restrict__ scales,
-    void* __restrict__ out, const int32_t* __restrict__ perm) {
+    void* __restrict__ out, const int32_t* __restrict__ perm, int32_t* __restrict__ bad) {
     __shared__ __attribute__((aligned(16))) WideRing bsm;
     __shared__ int s_unit[2];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -838,7 +825,7 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
         __syncthreads();
         const int un = __builtin_amdgcn_readfirstlane(s_unit[it & 1]);
         if (un < total) wide_fill(moe_unit<kItem>(un, n_slabs, work, offsets, N, KB, W, w, lane).ws, bsm);
-        if (rows) moe_epilogue<FP8, GEMM>(acc, c, N, F, scales, out, lane);
+        if (rows) moe_epilogue<FP8, GEMM>(acc, c, N, F, scales, out, lane, bad);
         if (un >= total) break;
         c = moe_unit<kItem>(un, n_slabs, work, offsets, N, KB, W, w, lane);   // recomputed: less live state
     }
@@ -916,16 +903,16 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_head_wide(
     }
 }
 
-// GEMM 1's activation fragments: the token rows of every 16-row tile of the
-// permuted entries in MFMA A-operand order (frag_offset), zero for padding rows.
-// Done once here, the expert GEMM's activation loads become contiguous 1 KiB
-// reads instead of 16-row gathers repeated for every weight slab.
-template <bool FP8>
-__global__ __launch_bounds__(256) void k_moe_gather_frag(const uint8_t* __restrict__ X, int K,
-                                                         const int32_t* __restrict__ perm_token,
-                                                         const int32_t* __restrict__ offsets,
-                                                         int E, uint8_t* __restrict__ Xf) {
-    const int KB = FP8 ? (K >> 6) : (K >> 5);
+// fp8 GEMM 1's activation fragments: the e4m3 token rows of every 16-row tile
+// of the permuted entries in MFMA A-operand order (frag_offset), zero for
+// padding rows.  Done once here, the expert GEMM's activation loads become
+// contiguous 1 KiB reads instead of 16-row gathers repeated for every weight
+// slab.  (bf16 GEMM 1 reads the token rows in place instead.)
+__global__ __launch_bounds__(256) void k_moe_gather_frag8(const uint8_t* __restrict__ X, int K,
+                                                          const int32_t* __restrict__ perm_token,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int E, uint8_t* __restrict__ Xf) {
+    const int KB = K >> 6;
     const int kb = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int tile = blockIdx.y;
     if (kb >= KB || 16 * tile >= offsets[E]) return;
@@ -933,14 +920,10 @@ __global__ __launch_bounds__(256) void k_moe_gather_frag(const uint8_t* __restri
     const int tok = perm_token[16 * tile + (lane & 15)];
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (tok >= 0) {
-        const uint8_t* row = X + (size_t)tok * (FP8 ? K : 2 * K);
-        if (FP8) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(row + kb * 64 + 8 * g);
-            const uint2 hi = *reinterpret_cast<const uint2*>(row + kb * 64 + 32 + 8 * g);
-            v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-            v = *reinterpret_cast<const uint4*>(row + (kb * 32 + 8 * g) * 2);
-        }
+        const uint8_t* row = X + (size_t)tok * K;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + kb * 64 + 8 * g);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + kb * 64 + 32 + 8 * g);
+        v = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
     *reinterpret_cast<uint4*>(Xf + (((size_t)tile * KB + kb) * 64 + lane) * 16) = v;
 }
@@ -991,14 +974,6 @@ __global__ void k_moe2_f32(const float* __restrict__ H, int d, int F,
 }
 
 // ================================================================== launchers
-hipError_t launch_pack_afrag(const void* A, int M, int K, void* Af, hipStream_t s) {
-    if (M <= 0) return hipSuccess;
-    if (K & 31) return hipErrorInvalidValue;
-    const int64_t total = (int64_t)((M + 15) >> 4) * (K >> 5) * 64;
-    k_pack_afrag<<<(unsigned)((total + 255) / 256), 256, 0, s>>>((const bf16_t*)A, M, K, (uint8_t*)Af);
-    return hipGetLastError();
-}
-
 hipError_t launch_gemm_frag(int epi, const void* Af, int M, const void* B, int K, int N, float* C,
                             int ldc, hipStream_t s, int ksplit, const RopeArgs* rope) {
     if (M <= 0 || N <= 0) return hipSuccess;
@@ -1085,13 +1060,13 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
             k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
                                                               offsets, work.items, work.count,
                                                               work.count + 1, w.w1, w.s1, H,
-                                                              nullptr);
+                                                              nullptr, nullptr);
         } else {
             // token rows read in place through the permutation
             k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)X, d, 2 * F, F,
                                                                offsets, work.items, work.count,
                                                                work.count + 1, w.w1, w.s1, H,
-                                                               perm_token);
+                                                               perm_token, nullptr);
         }
     }
     return hipGetLastError();
@@ -1113,25 +1088,20 @@ hipError_t launch_head_wide(const void* hf, int C, int d, const void* E, int V, 
     return hipGetLastError();
 }
 
-hipError_t launch_moe_gather(int dtype, const void* X, int d, const int32_t* perm_token,
-                             const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s) {
-    if (max_rows <= 0 || dtype == kF32) return hipSuccess;
-    const int kq = dtype == kFP8 ? 64 : 32;
-    if (d % kq || !Xf) return hipErrorInvalidValue;
-    const int KB = d / kq;
+hipError_t launch_moe_gather8(const void* X, int d, const int32_t* perm_token,
+                              const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s) {
+    if (max_rows <= 0) return hipSuccess;
+    if (d % 64 || !Xf) return hipErrorInvalidValue;
+    const int KB = d / 64;
     dim3 gg((KB + 3) / 4, (max_rows + kMoePad - 1) / kMoePad);   // tiles past offsets[E] exit
-    if (dtype == kFP8)
-        k_moe_gather_frag<true><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
-                                                   (uint8_t*)Xf);
-    else
-        k_moe_gather_frag<false><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
-                                                    (uint8_t*)Xf);
+    k_moe_gather_frag8<<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
+                                          (uint8_t*)Xf);
     return hipGetLastError();
 }
 
 hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
                             const int32_t* offsets, int E, int d, int F, int max_rows,
-                            const MoeWork& work, float* Y, hipStream_t s) {
+                            const MoeWork& work, float* Y, int32_t* bad, hipStream_t s) {
     if (max_rows <= 0) return hipSuccess;
     if (dtype == kF32) {
         int64_t total = (int64_t)max_rows * d;
@@ -1144,12 +1114,12 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
             k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
                                                               work.items2, work.count + 3,
                                                               work.count + 2, w.w2, w.s2, Y,
-                                                              nullptr);
+                                                              nullptr, bad);
         else
             k_moe_wide<false, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
                                                                work.items2, work.count + 3,
                                                                work.count + 2, w.w2, w.s2, Y,
-                                                               nullptr);
+                                                               nullptr, bad);
     }
     return hipGetLastError();
 }

@@ -236,11 +236,13 @@ __global__ __launch_bounds__(256) void k_router_route(const float* __restrict__ 
     __shared__ bool last;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t < M) topk_token(logits, nsplit, M, E, k, t, idx, gates);
+    // Every wave releases its own idx / gates stores at device scope before the
+    // barrier: the block-scope release of the barrier alone does not wait for
+    // another wave's stores to reach the device-coherent level, and the last block
+    // (on another CU) reads them all.
+    __threadfence();
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();                                   // this block's idx before the ticket
-        last = atomicAdd(ticket, 1u) == gridDim.x - 1;
-    }
+    if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == gridDim.x - 1;
     __syncthreads();
     if (!last) return;
     __threadfence();                                       // every block's idx visible here

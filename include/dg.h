@@ -116,7 +116,7 @@ typedef struct dg_model_cfg {
     int32_t n_experts;     /* E */
     int32_t top_k;         /* k <= E, k <= 16 */
     int32_t d_ff;          /* F, expert hidden width, multiple of 64 for bf16/fp8 */
-    int32_t vocab;         /* V, multiple of 16 */
+    int32_t vocab;         /* V (bf16 path: multiple of 128) */
     int32_t canvas;        /* C, canvas length (<= 1024) */
     int64_t max_ctx;       /* KV rows per layer: >= P + K*C */
     double rope_base;      /* RoPE base (rotate-half pairs, absolute positions) */
@@ -315,25 +315,44 @@ int dg_profile_end(dg_handle* h, double* total_ms, int32_t* counts);
 
 /* ---------------------------------------------------------------- kernel-level entry points */
 
-/* Attention for one batch of queries (the decoder's attention step):
+/* Attention for one batch of queries, the decoder's attention step
+ * (technical-report summary, Method, generation pipeline: bidirectional
+ * attention across the canvas and attention to the KV cache; alphasignal,
+ * paragraph on bidirectional attention):
  *   O[m, h*D + t] = sum_j softmax_j(scale * q_h,m . k_g,j [+ mask]) v_g,j,t
  * with GQA group g = h / (Hq / Hkv).  d_q: [Hq, M, D]; d_k, d_v: [Hkv, S, D];
  * d_o: [M, Hq*D]; all dtype (DG_F32 or DG_BF16, bf16 requires D = 128).
  * causal != 0 masks key j for query m when j > q_pos0 + m (keys are at
  * positions 0..S-1); causal = 0 is the canvas' bidirectional attention.
- * Uses a library-owned device workspace (allocated on first use). */
+ * d_workspace: caller-owned device scratch of at least the bytes
+ * dg_attention_workspace_size reports for the same arguments (NULL allowed
+ * when that is 0): the bf16 path packs a transposed, key-permuted copy of V
+ * there and keeps the per-split partials of a key range split over
+ * workgroups (binary16 split averages: |v| entries of 65520 and above
+ * saturate at 65504).  Nothing is allocated.  A workspace must not be shared
+ * by calls that may overlap.  DG_EINVAL for bad sizes or a short workspace,
+ * before any work is enqueued.  Asynchronous. */
 int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, int32_t Hq,
                  int32_t Hkv, int32_t M, int32_t S, int32_t D, float scale, int32_t causal,
-                 int32_t q_pos0, int32_t dtype, void* stream);
+                 int32_t q_pos0, int32_t dtype, void* d_workspace, size_t workspace_bytes,
+                 void* stream);
 
-/* One MoE FFN layer on hidden states (the decoder's MoE step, applied to its
- * input directly: no norm, no residual): router logits r = x Wr; top-k of
+/* Workspace bytes dg_attention needs for these arguments (*bytes = 0: none).
+ * Validates them as dg_attention does; touches no device. */
+int dg_attention_workspace_size(int32_t Hq, int32_t Hkv, int32_t M, int32_t S, int32_t D,
+                                int32_t causal, int32_t q_pos0, int32_t dtype, size_t* bytes);
+
+/* One MoE FFN layer on hidden states, the decoder's MoE step
+ * (technical-report summary, Experiment: a mixture-of-experts transformer
+ * with a small number of active experts among many), applied to its input
+ * directly (no norm, no residual): router logits r = x Wr; top-k of
  * softmax(r) (ties to the lower expert id) with gates renormalised over the
  * k chosen; y = sum_j gate_j * (silu(x Wg_e) * (x Wu_e)) Wd_e, e = idx_j.
  * Uses layer `layer` of the handle's weights.  d_x: [n_tokens, d] act_dtype;
  * d_y: [n_tokens, d] act_dtype.  Optional d_idx (int32 [n_tokens, k]) and
  * d_gates (float [n_tokens, k]) receive the routing; pass NULL to skip.
- * n_tokens <= handle capacity max(C, max_ctx). */
+ * n_tokens <= max(C, 4096), the handle's batch capacity.  Uses the
+ * handle's workspace: calls on one handle must not overlap. */
 int dg_moe_layer(dg_handle* h, int32_t layer, const void* d_x, int32_t n_tokens, void* d_y,
                  int32_t* d_idx, float* d_gates, void* stream);
 

@@ -61,7 +61,7 @@ def test_null_arguments_are_rejected(dg):
     assert lib.dg_generate_block(None, None, 12, 0, 1, None) == dg.DG_EINVAL
     assert lib.dg_prefill_prompt_kv(None, None, 0, None) == dg.DG_EINVAL
     assert lib.dg_attention(None, None, None, None, 16, 8, 256, 4352, 128, 0.1, 0, 0, 1,
-                            None) == dg.DG_EINVAL
+                            None, 0, None) == dg.DG_EINVAL
     assert lib.dg_create(None, None) == dg.DG_EINVAL
     lib.dg_destroy(None)
 
@@ -81,3 +81,23 @@ def test_entropy_bounded_entry_points_validate_before_any_device_call(dg):
     assert lib.dg_eb_sample(*fake, 256, 1024, 0, None, 0, 0, None) == dg.DG_EINVAL
     assert lib.dg_denoise_step_eb(None, None, None, 0, ctypes.byref(p), 0, None, None) == dg.DG_EINVAL
     assert lib.dg_generate_block_eb(None, None, ctypes.byref(p), 0, 1, None, None) == dg.DG_EINVAL
+
+
+def test_attention_workspace_size_and_checks(dg):
+    """The workspace query needs no device; an undersized workspace is rejected before
+    any device work (the tensor pointers are never dereferenced)."""
+    n = dg.dg_attention_workspace_size(16, 8, 256, 4352, 128, False, 0, dg.DG_BF16)
+    # transposed V copy (8 heads x 128 dims x 4352 keys, bf16) + 16 splits of binary16
+    # averages and (max, sum) pairs for 16 heads x 256 queries
+    assert n == 8 * 128 * 4352 * 2 + 16 * 16 * 256 * (128 * 2 + 8)
+    assert dg.dg_attention_workspace_size(4, 2, 40, 100, 64, False, 0, dg.DG_F32) == 0
+    with pytest.raises(dg.DGError) as ei:
+        dg.dg_attention_workspace_size(16, 8, 256, 4352, 64, False, 0, dg.DG_BF16)
+    assert ei.value.code == dg.DG_EINVAL
+    lib = dg._lib
+    fake = [4096 * (i + 1) for i in range(5)]
+    assert lib.dg_attention(*fake[:4], 16, 8, 256, 4352, 128, 0.1, 0, 0, 1, fake[4], n - 1,
+                            None) == dg.DG_EINVAL
+    assert "workspace" in dg.dg_last_error()
+    assert lib.dg_attention(*fake[:4], 16, 8, 256, 4352, 128, 0.1, 1, 4200, 1, fake[4], n,
+                            None) == dg.DG_EINVAL     # causal queries beyond the keys

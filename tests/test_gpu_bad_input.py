@@ -109,3 +109,28 @@ def test_nan_expert_weights_reach_the_flag(dg):
         log("NaN expert weights: flagged")
     finally:
         dg.dg_destroy(h)
+
+
+def test_binary16_saturation_is_flagged(dg):
+    """Expert outputs are stored as binary16 for the combine.  Down-projection weights of
+    2^20 push finite expert outputs far beyond its range (|y| >= 65520): they saturate at
+    65504 and the range bit makes dg_check_finite report DG_ENONFINITE with its own message,
+    in the prefill and again in a denoise pass."""
+    h = build_handle(dg, W)
+    try:
+        big = np.full(fx.tensor_shape(W, "wd"), 0x4980, dtype=np.uint16)   # bf16 2^20
+        dg.dg_load_tensor(h, dg.DG_T_WD, 0, -1, big)
+        dg.dg_prefill_prompt_kv(h, i32_dev(fx.prompt_ids(W)), W.prompt_len)
+        assert _flag(dg, h) == dg.DG_ENONFINITE
+        assert "binary16" in dg.dg_last_error()
+        assert _flag(dg, h) == dg.DG_OK                      # cleared by the read
+        canvas = torch.empty(W.canvas, dtype=torch.int32, device="cuda")
+        mask = torch.empty(W.canvas, dtype=torch.uint8, device="cuda")
+        dg.dg_init_canvas(h, canvas, mask, 11)
+        dg.dg_denoise_step(h, canvas, mask, 0, 4, 11)
+        torch.cuda.synchronize()
+        assert _flag(dg, h) == dg.DG_ENONFINITE
+        assert "binary16" in dg.dg_last_error()
+        log("expert outputs beyond the binary16 range: flagged in prefill and pass")
+    finally:
+        dg.dg_destroy(h)

@@ -20,6 +20,12 @@ def dg():
 
 
 # ------------------------------------------------------------------ attention
+def _workspace(dg, Hq, Hkv, M, S, D, causal, q_pos0, code):
+    """Caller-owned workspace of the attention call (None when it needs none)."""
+    n = dg.dg_attention_workspace_size(Hq, Hkv, M, S, D, causal, q_pos0, code)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+
+
 def _attn_case(dg, Hq, Hkv, M, S, causal, q_pos0, seed, dtype="bf16", D=128):
     rng = np.random.default_rng(seed)
     if dtype == "bf16":
@@ -39,7 +45,8 @@ def _attn_case(dg, Hq, Hkv, M, S, causal, q_pos0, seed, dtype="bf16", D=128):
         o = torch.empty(M, Hq * D, dtype=torch.float32, device="cuda")
         code = dg.DG_F32
     log(f"attention Hq={Hq} Hkv={Hkv} M={M} S={S} causal={causal} q_pos0={q_pos0} {dtype}")
-    dg.dg_attention(qd, kd, vd, o, Hq, Hkv, M, S, D, 1.0 / math.sqrt(D), causal, q_pos0, code)
+    ws = _workspace(dg, Hq, Hkv, M, S, D, causal, q_pos0, code)
+    dg.dg_attention(qd, kd, vd, o, Hq, Hkv, M, S, D, 1.0 / math.sqrt(D), causal, q_pos0, code, ws)
     torch.cuda.synchronize()
     ref = om.attention(qf, kf, vf, causal=causal, q_pos=np.arange(q_pos0, q_pos0 + M),
                        k_pos=np.arange(S))
@@ -57,8 +64,10 @@ def test_attention_gqa_prompt4096_canvas256_bf16(dg):
     a = fx.ATTN
     o = torch.empty(a.canvas, a.n_q_heads * a.head_dim, dtype=torch.bfloat16, device="cuda")
     log("attention workload 16x8 heads, S=4352")
+    ws = _workspace(dg, a.n_q_heads, a.n_kv_heads, a.canvas, a.seq, a.head_dim, False, 0,
+                    dg.DG_BF16)
     dg.dg_attention(bf16_dev(q), bf16_dev(k), bf16_dev(v), o, a.n_q_heads, a.n_kv_heads,
-                    a.canvas, a.seq, a.head_dim, 1.0 / math.sqrt(128), False, 0, dg.DG_BF16)
+                    a.canvas, a.seq, a.head_dim, 1.0 / math.sqrt(128), False, 0, dg.DG_BF16, ws)
     torch.cuda.synchronize()
     ref = om.attention(bits_f64(q), bits_f64(k), bits_f64(v))
     ref = ref.transpose(1, 0, 2).reshape(a.canvas, -1)
