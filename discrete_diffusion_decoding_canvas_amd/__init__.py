@@ -27,7 +27,7 @@ EXPORTED = (
     "dg_reset_context", "dg_get_state", "dg_get_capture", "dg_get_kv", "dg_attention",
     "dg_moe_layer", "dg_init_canvas", "dg_profile_begin", "dg_profile_end", "dg_set_kv",
     "dg_set_capture", "dg_set_graphs", "dg_eb_sample", "dg_denoise_step_eb",
-    "dg_generate_block_eb", "dg_attention_workspace_size",
+    "dg_generate_block_eb", "dg_attention_workspace_size", "dg_attention_noalloc",
 )
 DG_PROF_MOE_GEMM1, DG_PROF_MOE_GEMM2, DG_PROF_ATTENTION, DG_PROF_LM_HEAD, DG_PROF_DENSE = range(5)
 DG_PROF_N = 5
@@ -91,6 +91,8 @@ def _load_library():
                           i32, vp, sz, vp], i32),
         "dg_attention_workspace_size": ([i32, i32, i32, i32, i32, i32, i32, i32,
                                          ctypes.POINTER(sz)], i32),
+        "dg_attention_noalloc": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
+                                  i32, i32, i32, vp], i32),
         "dg_moe_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
         "dg_init_canvas": ([vp, vp, vp, u64, vp], i32),
         "dg_profile_begin": ([vp, i32], i32),
@@ -261,6 +263,14 @@ def dg_attention(d_q, d_k, d_v, d_o, Hq: int, Hkv: int, M: int, S: int, D: int, 
     _check(_lib.dg_attention(_ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_o), Hq, Hkv, M, S, D,
                              scale, int(bool(causal)), q_pos0, dtype, _ptr(d_workspace),
                              _nbytes(d_workspace), _stream(stream)))
+
+
+def dg_attention_noalloc(d_q, d_k, d_v, d_o, Hq: int, Hkv: int, M: int, S: int, D: int,
+                         scale: float, causal: bool, q_pos0: int, dtype: int,
+                         stream=None) -> None:
+    _check(_lib.dg_attention_noalloc(_ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_o), Hq, Hkv, M, S,
+                                     D, scale, int(bool(causal)), q_pos0, dtype,
+                                     _stream(stream)))
 
 
 def dg_moe_layer(h, layer: int, d_x, n_tokens: int, d_y, d_idx=None, d_gates=None,

@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1167,6 +1168,52 @@ int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, i
                     d_workspace ? workspace_bytes : (size_t)0);
     return run_attention(d_q, d_k, d_v, d_o, Hq, Hkv, M, S, D, scale, causal, q_pos0, dtype,
                          d_workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+// Scratch of dg_attention_noalloc: a file-scope device array, one copy per GPU the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (resolved on the first call there).
+int scratch_address(void** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DG_EINVAL, "device %d beyond the scratch table", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(DG_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DG_OK;
+}
+}  // namespace
+
+int dg_attention_noalloc(const void* d_q, const void* d_k, const void* d_v, void* d_o, int32_t Hq,
+                         int32_t Hkv, int32_t M, int32_t S, int32_t D, float scale,
+                         int32_t causal, int32_t q_pos0, int32_t dtype, void* stream) {
+    g_err.clear();
+    if (!d_q || !d_k || !d_v || !d_o) return fail(DG_EINVAL, "NULL tensor");
+    DG_TRY(check_attention_args(Hq, Hkv, M, S, D, causal, q_pos0, dtype));
+    const size_t need = attention_ws_bytes(Hq, Hkv, M, S, D, dtype);
+    if (need > kNoAllocScratchBytes)
+        return fail(DG_EINVAL, "attention needs %zu bytes of scratch, the static scratch holds %zu",
+                    need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) DG_TRY(scratch_address(&ws));
+    return run_attention(d_q, d_k, d_v, d_o, Hq, Hkv, M, S, D, scale, causal, q_pos0, dtype, ws,
+                         kNoAllocScratchBytes, (hipStream_t)stream);
 }
 
 int dg_moe_layer(dg_handle* h, int32_t layer, const void* d_x, int32_t n_tokens, void* d_y,

@@ -342,6 +342,19 @@ int dg_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o, i
 int dg_attention_workspace_size(int32_t Hq, int32_t Hkv, int32_t M, int32_t S, int32_t D,
                                 int32_t causal, int32_t q_pos0, int32_t dtype, size_t* bytes);
 
+/* dg_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array of
+ * 64 MiB (one per GPU, held until the process ends); calls whose workspace
+ * (dg_attention_workspace_size) exceeds it fail with DG_EINVAL before any work
+ * is enqueued.  The first call on a device resolves the array's address
+ * (hipGetSymbolAddress).  Every call on one GPU shares the array, so calls
+ * that may overlap on one GPU (other streams, other threads) race: the caller
+ * orders them.  Nothing is allocated; results equal dg_attention's. */
+int dg_attention_noalloc(const void* d_q, const void* d_k, const void* d_v, void* d_o,
+                         int32_t Hq, int32_t Hkv, int32_t M, int32_t S, int32_t D, float scale,
+                         int32_t causal, int32_t q_pos0, int32_t dtype, void* stream);
+
 /* One MoE FFN layer on hidden states, the decoder's MoE step
  * (technical-report summary, Experiment: a mixture-of-experts transformer
  * with a small number of active experts among many), applied to its input
