@@ -255,12 +255,18 @@ class OracleModel:
         w = self.w
         M = a.shape[0]
         q = (a @ self.W.dense("wq", l)).reshape(M, w.n_q_heads, w.head_dim).transpose(1, 0, 2)
+        q = self._act(rope(q, positions, w.rope_base))
+        k, v = self.kv_rows(l, a, positions)
+        return q, k, v
+
+    def kv_rows(self, l, a, positions):
+        """Cache rows of layer l for the normed rows a [M, d] at `positions`: the rotated
+        keys and the values, [Hkv, M, D] each."""
+        w = self.w
+        M = a.shape[0]
         k = (a @ self.W.dense("wk", l)).reshape(M, w.n_kv_heads, w.head_dim).transpose(1, 0, 2)
         v = (a @ self.W.dense("wv", l)).reshape(M, w.n_kv_heads, w.head_dim).transpose(1, 0, 2)
-        q = self._act(rope(q, positions, w.rope_base))
-        k = self._act(rope(k, positions, w.rope_base))
-        v = self._act(v)
-        return q, k, v
+        return self._act(rope(k, positions, w.rope_base)), self._act(v)
 
     def _moe(self, l, b):
         w = self.w
@@ -295,6 +301,26 @@ class OracleModel:
         b = self._act(rmsnorm(h, w.rms_eps))
         y, idx, gates, margin = self._moe(l, b)
         return h + y, k, v, (idx, gates, margin)
+
+    def encoder_layer_rows(self, l, h, positions):
+        """Causal encoder layer l applied to some rows only: h [n, d] are the layer's input
+        rows at `positions`, and the cache of layer l (self.K[l], self.V[l], rows at
+        positions 0, 1, ...) already holds every position up to max(positions), these rows'
+        own keys included.  Each row attends to the cached keys at positions <= its own.
+        Returns (output rows [n, d], routing margin of each row)."""
+        w = self.w
+        positions = np.asarray(positions)
+        a = self._act(rmsnorm(h, w.rms_eps))
+        q = (a @ self.W.dense("wq", l)).reshape(len(positions), w.n_q_heads,
+                                                w.head_dim).transpose(1, 0, 2)
+        q = self._act(rope(q, positions, w.rope_base))
+        S = self.K[l].shape[1]
+        o = attention(q, self.K[l], self.V[l], causal=True, q_pos=positions, k_pos=np.arange(S))
+        o = self._act(o.transpose(1, 0, 2).reshape(len(positions), w.n_q_heads * w.head_dim))
+        h = h + o @ self.W.dense("wo", l)
+        b = self._act(rmsnorm(h, w.rms_eps))
+        y, _, _, margin = self._moe(l, b)
+        return h + y, margin
 
     # ------------------------------------------------------------ stage 1 / stage 3
     def _encode(self, ids, start):

@@ -56,6 +56,11 @@ class FixtureWeights:
     def embed(self) -> np.ndarray:
         return self.dense("embed", 0)
 
+    def forget_layer(self, layer: int) -> None:
+        """Drop the cached tensors of one layer (memory only; they are regenerated on use)."""
+        for key in [k for k in self._cache if k[0] != "embed" and k[1] == layer]:
+            del self._cache[key]
+
 
 class ArrayWeights:
     """Weights given directly as float64 arrays (tiny hand-built test models).

@@ -6,7 +6,7 @@ Calls only the CPU oracle (``oracle/``) on inputs from the seeded generator
 their margins, routing with margins, sampled logits and sampled K/V rows.
 
     python tests/golden/make_golden.py moe26b_2layer
-    python tests/golden/make_golden.py moe26b_fp8_long_1layer
+    python tests/golden/make_golden.py moe26b_fp8_long_2layer
 """
 from __future__ import annotations
 
@@ -88,28 +88,59 @@ def moe26b_2layer():
     np.savez_compressed(os.path.join(HERE, "moe26b_2layer.npz"), **out)
 
 
-def moe26b_fp8_long_1layer():
-    """The long-context fp8-expert variant truncated to layer 0, P = 131072: canvas 0
-    pass 0, then canvas 1 pass 0 after committing the oracle's canvas-0 pass-0 output."""
-    w = fx.MOE26B_FP8_LONG.with_(name="moe26b_fp8_long_1layer", n_layers=1)
+def moe26b_fp8_long_2layer():
+    """The long-context fp8-expert variant truncated to layers 0-1, P = 131072.
+
+    A whole prefill of two layers over 131072 tokens is out of the oracle's reach (its
+    causal attention alone is ~70 TFLOP), so this stores what the oracle can compute
+    exactly: the layer-0 cache (the projection of the embedded prompt), sampled at 64
+    positions; the layer-1 cache at the same positions, from layer 0 run at those rows
+    against the whole layer-0 cache; the canvas inits of blocks 0 and 1; and the cache rows
+    a commit of block 0's initial canvas appends at both layers (sampled at 64 rows), with
+    the layer-0 routing margins that gate the layer-1 rows."""
+    from oracle.numerics import rmsnorm
+
+    w = fx.MOE26B_FP8_LONG.with_(name="moe26b_fp8_long_2layer", n_layers=2)
     t0 = time.time()
-    m = OracleModel(w, FixtureWeights(w))
-    m.prefill(fx.prompt_ids(w))
-    print(f"prefill {time.time() - t0:.1f}s", flush=True)
-    rng = np.random.default_rng(20261)
+    m = OracleModel(w, FixtureWeights(w, cache_experts=False))
+    E = m.W.embed()
+    ids = fx.prompt_ids(w)
+    P, C = w.prompt_len, w.canvas
+    n_tot = P + C
+    K0 = np.empty((w.n_kv_heads, n_tot, w.head_dim))
+    V0 = np.empty_like(K0)
+    step = 8192
+    for c0 in range(0, P, step):
+        pos = np.arange(c0, min(P, c0 + step))
+        K0[:, pos], V0[:, pos] = m.kv_rows(0, m._act(rmsnorm(E[ids[pos]], w.rms_eps)), pos)
+    print(f"layer-0 prompt cache {time.time() - t0:.1f}s", flush=True)
+    rng = np.random.default_rng(20263)
     out = {"seed": np.array(w.seed), "T": np.array(w.T)}
-    out.update(_kv_samples(m, rng, m.n_ctx))
+    kv_pos = np.sort(rng.choice(P, size=N_KV_SAMPLES, replace=False))
+    out["kv_pos"] = kv_pos.astype(np.int64)
+    out["k_0"], out["v_0"] = K0[:, kv_pos], V0[:, kv_pos]
+    m.K[0], m.V[0] = K0[:, :P], V0[:, :P]
+    h1, margin0 = m.encoder_layer_rows(0, E[ids[kv_pos]], kv_pos)
+    out["k_1"], out["v_1"] = m.kv_rows(1, m._act(rmsnorm(h1, w.rms_eps)), kv_pos)
+    out["kv_margin0"] = margin0
+    print(f"layer-1 prompt cache samples {time.time() - t0:.1f}s", flush=True)
     for blk in range(2):
-        canvas = init_canvas(w.seed, blk, w.canvas, w.vocab)
-        mask = np.zeros(w.canvas, np.uint8)
-        out[f"b{blk}_canvas_in"] = canvas
-        res = m.denoise_step(canvas, mask, 0, w.T, w.seed, keep_logits=True)
-        out.update(_step_record(f"b{blk}", res, rng, w.vocab))
-        print(f"canvas {blk} {time.time() - t0:.1f}s", flush=True)
-        if blk == 0:
-            m.commit(res.canvas)
-            out["commit_tokens"] = res.canvas
-    np.savez_compressed(os.path.join(HERE, "moe26b_fp8_long_1layer.npz"), **out)
+        out[f"b{blk}_canvas_in"] = init_canvas(w.seed, blk, C, w.vocab)
+    # commit of block 0's initial canvas at positions P..P+C-1
+    tokens = out["b0_canvas_in"]
+    cpos = np.arange(P, P + C)
+    K0[:, cpos], V0[:, cpos] = m.kv_rows(0, m._act(rmsnorm(E[tokens], w.rms_eps)), cpos)
+    m.K[0], m.V[0] = K0, V0
+    h1, cmargin0 = m.encoder_layer_rows(0, E[tokens], cpos)
+    k1, v1 = m.kv_rows(1, m._act(rmsnorm(h1, w.rms_eps)), cpos)
+    rows = np.sort(rng.choice(C, size=N_KV_SAMPLES, replace=False))
+    out["commit_tokens"] = tokens
+    out["commit_rows"] = rows.astype(np.int64)
+    out["commit_k_0"], out["commit_v_0"] = K0[:, P + rows], V0[:, P + rows]
+    out["commit_k_1"], out["commit_v_1"] = k1[:, rows], v1[:, rows]
+    out["commit_margin0"] = cmargin0[rows]
+    print(f"commit rows {time.time() - t0:.1f}s", flush=True)
+    np.savez_compressed(os.path.join(HERE, "moe26b_fp8_long_2layer.npz"), **out)
 
 
 if __name__ == "__main__":

@@ -1,6 +1,8 @@
 """Device-side helpers shared by the GPU tests (test infrastructure)."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 import time
 
@@ -72,3 +74,15 @@ def kv_read(dg, h, layer, which, row0, n, Hkv, D, dtype):
     dg.dg_get_kv(h, layer, which, row0, n, t)
     torch.cuda.synchronize()
     return t.float().cpu().numpy().astype(np.float64)
+
+
+def record(name: str, data: dict) -> None:
+    """Write a parity record (counts of in-band decisions, per-layer statistics) as JSON to
+    the directory named by DG_PARITY_RECORD_DIR, when it is set."""
+    out = os.environ.get("DG_PARITY_RECORD_DIR")
+    if not out:
+        return
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, f"{name}.json"), "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True, default=float)
+    log(f"parity record {name} written")

@@ -7,19 +7,26 @@ Tolerances:
   * discrete decisions (routing, argmax, lock set, redraw) must agree exactly
     wherever the oracle's own margin for that decision exceeds the gate, in
     natural-log probability units (= logit units at temperature 1); inside the
-    band a disagreement is counted, not failed.  The gate is 1e-2 for the fp32
-    configuration.  For bf16 storage it is 3e-2: a relative difference of ~1e-5
-    anywhere upstream of a bf16 store (fp32 vs fp64 accumulation) flips about
-    one in eight roundings of the unit-scale normed activations that feed the
-    router and the LM head, which moves each logit by up to ~6e-3 (measured on
-    the 26B-class model), so a difference of two logits can move by ~1.2e-2.
+    band a disagreement is counted, not failed.  The gate is 1e-2 (GATE) for
+    every comparison made on the GPU's own input of the stage that decides
+    (kernel-level calls, stage-by-stage passes, the fp32 configuration).
+  * decisions compared end to end through bf16 layers (E2E_GATE) use 3e-2: a
+    relative difference of ~1e-5 anywhere upstream of a bf16 store (fp32 vs
+    fp64 accumulation) flips about one in eight roundings of the unit-scale
+    normed activations that feed the router and the LM head, which moves each
+    logit by up to ~6e-3 (measured on the 26B-class model), so a difference of
+    two logits can move by ~1.2e-2 for reasons that are not a kernel error.
+    Through fp8 (e4m3) expert inputs the same differences flip about 1 in 15
+    codes by a whole 12.5 % step; end-to-end logits then move by up to ~0.2
+    (measured, 131072-token workload) and the gate is 0.25.
 """
 from __future__ import annotations
 
 import numpy as np
 
 DELTA = 1e-2                     # fp32 configuration
-GATE = {"f32": 1e-2, "bf16": 3e-2, "fp8": 3e-2}
+GATE = {"f32": 1e-2, "bf16": 1e-2, "fp8": 1e-2}          # decisions on the stage's own input
+E2E_GATE = {"f32": 1e-2, "bf16": 3e-2, "fp8": 2.5e-1}    # decisions end to end through bf16 layers
 TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4), "fp8": (2e-2, 5e-2)}
 
 

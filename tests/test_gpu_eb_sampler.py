@@ -24,7 +24,7 @@ from oracle import eb_sampler as eb
 from oracle.model import OracleModel
 from oracle.philox import init_canvas, renoise_tokens
 from oracle.weights import FixtureWeights
-from parity import GATE, gated_mismatches, routing_sets
+from parity import E2E_GATE, gated_mismatches, routing_sets
 from gpu_util import i32_dev, log, need_gpu, routing_capture, stats_capture, u8_dev
 
 pytestmark = pytest.mark.gpu
@@ -143,10 +143,10 @@ def _check_pass(dg, h, W, s, res, er, H, canvas_in, mask_in, cd, md, info, p, se
     err = np.abs(Hg - H)[ok]
     assert err.max(initial=0.0) <= tol, f"{tag}: entropy off by {err.max():.3g}"
     bad, n, _ = gated_mismatches(st["argmax"][ok], res.stats.argmax[ok], res.stats.top2_gap[ok],
-                                 GATE[kind])
+                                 E2E_GATE[kind])
     assert bad == 0, f"{tag}: {bad}/{n} gated argmax differ"
     unl = (mask_in == 0) & ok
-    bad, n, _ = gated_mismatches(st["redraw"][unl], res.redraw[unl], res.redraw_gap[unl], GATE[kind])
+    bad, n, _ = gated_mismatches(st["redraw"][unl], res.redraw[unl], res.redraw_gap[unl], E2E_GATE[kind])
     assert bad == 0, f"{tag}: {bad}/{n} gated draws differ"
 
     cg, mg, ig = cd.cpu().numpy(), md.cpu().numpy().astype(bool), info.cpu().tolist()

@@ -11,11 +11,11 @@ from fixtures.dg_glue import build_handle
 from oracle.model import OracleModel
 from oracle.philox import init_canvas
 from oracle.weights import FixtureWeights
-from parity import GATE, TOL, assert_close, routing_sets, worst_mismatch_margin
+from parity import E2E_GATE, TOL, assert_close, routing_sets, worst_mismatch_margin
 from parity import gated_mismatches as _gated
 from parity import lock_set_check as _lock_check
 
-DELTA = GATE["bf16"]
+DELTA = E2E_GATE["bf16"]   # passes end to end through two bf16 layers
 
 
 def gated_mismatches(gpu, ref, margin):
@@ -130,9 +130,11 @@ def test_commit_rows(env):
     torch.cuda.synchronize()
     trusted = np.ones(W.canvas, bool)
     for l in range(W.n_layers):
-        got = kv_read(dg, h, l, 0, W.prompt_len, W.canvas, W.n_kv_heads, W.head_dim, torch.bfloat16)
-        assert_close(f"commit layer {l} K", got[:, trusted], oracle.K[l][:, W.prompt_len:][:, trusted],
-                     *TOL["bf16"])
+        for which, ref_kv, name in ((0, oracle.K[l], "K"), (1, oracle.V[l], "V")):
+            got = kv_read(dg, h, l, which, W.prompt_len, W.canvas, W.n_kv_heads, W.head_dim,
+                          torch.bfloat16)
+            assert_close(f"commit layer {l} {name}", got[:, trusted],
+                         ref_kv[:, W.prompt_len:][:, trusted], *TOL["bf16"])
         if l < W.n_layers - 1:
             trusted &= oracle.enc_route_margin[l][W.prompt_len:] > DELTA
     n_ctx, k_blk = dg.dg_get_state(h)

@@ -94,6 +94,10 @@ def test_all_passes_teacher_forced(env):
 
 
 def test_free_running_block_and_commit(env):
+    """One whole block on each side from the same seed.  The trajectories are equal unless a
+    decision of the oracle sits within 1e-3 of a tie (then the free run may legitimately
+    diverge, and the GPU's block is checked by its invariants).  The commit is checked on the
+    GPU's own tokens either way: K and V rows of every layer against the oracle's encoder."""
     dg, h, oracle = env
     seed = 777
     out = torch.empty(W.canvas, dtype=torch.int32, device="cuda")
@@ -107,16 +111,20 @@ def test_free_running_block_and_commit(env):
                            np.nanmin(np.where(unl, res.redraw_gap, np.inf)),
                            abs(res.sampler.cut_low - res.sampler.cut_high)))
 
-    ref = oracle.generate_block(W.T, seed, commit=True, on_step=cb)
+    ref = oracle.generate_block(W.T, seed, commit=False, on_step=cb)
     got = out.cpu().numpy()
     if not np.array_equal(got, ref):
         assert min(margins) < 1e-3, "free-running block diverged without a near-tie decision"
-        pytest.skip(f"near-tie decision (margin {min(margins):.2e}) made trajectories diverge")
+        log(f"near-tie decision (margin {min(margins):.2e}): trajectories diverged")
+    assert got.min() >= 0 and got.max() < W.vocab
+    oracle.commit(got)
     n_ctx, k_blk = dg.dg_get_state(h)
-    assert (n_ctx, k_blk) == (W.prompt_len + W.canvas, 1)
+    assert (n_ctx, k_blk) == (W.prompt_len + W.canvas, 1) == (oracle.n_ctx, oracle.k_blk)
     for l in range(W.n_layers):
-        got_k = kv_read(dg, h, l, 0, W.prompt_len, W.canvas, W.n_kv_heads, W.head_dim, torch.float32)
-        assert_close(f"commit layer {l} K", got_k, oracle.K[l][:, W.prompt_len:], *TOL["f32"])
+        for which, ref_kv, name in ((0, oracle.K[l], "K"), (1, oracle.V[l], "V")):
+            got_kv = kv_read(dg, h, l, which, W.prompt_len, W.canvas, W.n_kv_heads, W.head_dim,
+                             torch.float32)
+            assert_close(f"commit layer {l} {name}", got_kv, ref_kv[:, W.prompt_len:], *TOL["f32"])
 
 
 def test_determinism_repeat_pass(env):

@@ -145,3 +145,24 @@ def test_entropy_bounded_block_invariants_tiny_fp32_workload():
     out, n = m.generate_block_eb(p, w.seed, commit=False, on_step=cb)
     assert n == len(seen) <= p.max_steps and sum(seen) == w.canvas
     assert np.all((out >= 0) & (out < w.vocab))
+
+
+def test_encoder_rows_give_the_prefill_cache_of_the_next_layer():
+    """Layer 0 of the causal encoder evaluated at a few prompt rows only (against the full
+    layer-0 cache) gives exactly the layer-1 cache rows a whole prefill writes there."""
+    from oracle.numerics import rmsnorm
+    rng = np.random.default_rng(7)
+    w, W = _tiny(rng)
+    ids = rng.integers(0, w.vocab, 10)
+    full = om.OracleModel(w, W)
+    full.prefill(ids)
+    m = om.OracleModel(w, W)
+    positions = np.arange(10)
+    m.K[0], m.V[0] = m.kv_rows(0, m._act(rmsnorm(W.embed()[ids], w.rms_eps)), positions)
+    assert np.allclose(m.K[0], full.K[0], atol=1e-12) and np.allclose(m.V[0], full.V[0], atol=1e-12)
+    pos = np.array([0, 3, 9])
+    h1, margin = m.encoder_layer_rows(0, W.embed()[ids[pos]], pos)
+    k1, v1 = m.kv_rows(1, m._act(rmsnorm(h1, w.rms_eps)), pos)
+    assert np.allclose(k1, full.K[1][:, pos], atol=1e-12)
+    assert np.allclose(v1, full.V[1][:, pos], atol=1e-12)
+    assert np.allclose(margin, full.enc_route_margin[0][pos], atol=1e-12)
