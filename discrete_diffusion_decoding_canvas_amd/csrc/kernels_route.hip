@@ -42,10 +42,11 @@ DG_DEV float wave_max_dpp(float x) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
-// Top-k of token t by one wave (no block-level synchronisation).  Lane l holds
-// the summed logits of experts l, 64 + l, ...; k rounds each take the wave
-// maximum and the lowest expert id holding it (ballot), which is the ranking
-// (logit descending, ties to the lower id).
+// Top-k of token t by one wave (no block-level synchronisation), written to the
+// token's k slots idx[0..k) and gates[0..k).  Lane l holds the summed logits of
+// experts l, 64 + l, ...; k rounds each take the wave maximum and the lowest
+// expert id holding it (ballot), which is the ranking (logit descending, ties to
+// the lower id).
 DG_DEV void topk_token(const float* __restrict__ logits, int nsplit, int M, int E, int k, int t,
                        int32_t* __restrict__ idx, float* __restrict__ gates) {
     const int lane = threadIdx.x & 63;
@@ -85,7 +86,7 @@ DG_DEV void topk_token(const float* __restrict__ logits, int nsplit, int M, int 
         for (int q = 0; q < NQ; ++q)
             if (win == 64 * q + lane) v[q] = -INFINITY;
         sel[r] = m;
-        if (lane == 0) idx[(int64_t)t * k + r] = win;
+        if (lane == 0) idx[r] = win;
     }
     if (lane < k) {
         const float mx = sel[0];
@@ -97,7 +98,7 @@ DG_DEV void topk_token(const float* __restrict__ logits, int nsplit, int M, int 
             s += ex;
             if (j == lane) mine = ex;
         }
-        gates[(int64_t)t * k + lane] = mine / s;
+        gates[lane] = mine / s;
     }
 }
 
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
                                                      float* __restrict__ gates) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= M) return;
-    topk_token(logits, nsplit, M, E, k, t, idx, gates);
+    topk_token(logits, nsplit, M, E, k, t, idx + (int64_t)t * k, gates + (int64_t)t * k);
 }
 
 // Every expert's rows start at a multiple of pad (16 for the MFMA expert GEMMs,
@@ -234,15 +235,24 @@ __global__ __launch_bounds__(256) void k_router_route(const float* __restrict__ 
                                                       int32_t* __restrict__ work_count,
                                                       uint32_t* __restrict__ ticket) {
     __shared__ bool last;
+    __shared__ int32_t s_idx[4 * kMaxTopK];
+    __shared__ float s_gates[4 * kMaxTopK];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t < M) topk_token(logits, nsplit, M, E, k, t, idx, gates);
-    // Every wave releases its own idx / gates stores at device scope before the
-    // barrier: the block-scope release of the barrier alone does not wait for
-    // another wave's stores to reach the device-coherent level, and the last block
-    // (on another CU) reads them all.
-    __threadfence();
+    const int wt = threadIdx.x >> 6;
+    // each wave ranks its token into LDS; wave 0 then stores the block's results, so
+    // that one device-scope release (wave 0's, after its own stores) covers them all
+    // before the ticket: the last block, on another CU, reads every block's idx
+    if (t < M) topk_token(logits, nsplit, M, E, k, t, s_idx + wt * k, s_gates + wt * k);
     __syncthreads();
-    if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+    if (threadIdx.x < 64) {
+        const int n_tok = min(4, M - (int)blockIdx.x * 4);
+        for (int i = threadIdx.x; i < n_tok * k; i += 64) {
+            idx[(int64_t)blockIdx.x * 4 * k + i] = s_idx[i];
+            gates[(int64_t)blockIdx.x * 4 * k + i] = s_gates[i];
+        }
+        __threadfence();
+        if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+    }
     __syncthreads();
     if (!last) return;
     __threadfence();                                       // every block's idx visible here
