@@ -205,6 +205,10 @@ def summarize_pmc(path):
         print(f"{name:60s} {grid:>18s} {ph:>8s} {ctr:>12s} {len(vals):10d} {sum(vals) / len(vals):14.1f}")
 
 
+# canvases per batched pass measured beside the single-canvas pass
+BATCHES = (1, 2, 4, 8, 16)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,7 +253,9 @@ def main():
         return
     log(f"building {w.name} (weights from the seeded generator)")
     t0 = time.time()
-    h = build_handle(dg, w, max_ctx=w.prompt_len + 2 * w.canvas)
+    # room for a committed canvas (the block timing) and the largest batch after it
+    h = build_handle(dg, w, max_ctx=w.prompt_len + (BATCHES[-1] + 1) * w.canvas,
+                     max_batch=BATCHES[-1])
     log(f"weights loaded in {time.time() - t0:.1f} s; prefilling {w.prompt_len} tokens")
     ids = torch.from_numpy(fx.prompt_ids(w)).cuda()
     stream = torch.cuda.current_stream()
@@ -384,6 +390,33 @@ def main():
         log(f"entropy-bounded: {eb_ms:.3f} ms per pass (head {eb_head_us:.1f} us); "
             f"block of {n_eb} passes {eb_block_ms:.1f} ms")
 
+    # batched canvases: B canvases over the same context in one pass (one graph per B)
+    batched = {}
+    for B in BATCHES:
+        bc = torch.empty(B * C, dtype=torch.int32, device="cuda")
+        bm = torch.empty(B * C, dtype=torch.uint8, device="cuda")
+
+        def bstep(i, B=B, bc=bc, bm=bm):
+            s = i % T
+            if s == 0:
+                dg.dg_init_canvas_batch(h, bc, bm, B, seed + 200 + i // T)
+            dg.dg_denoise_step_batch(h, bc, bm, B, s, T, seed + 200 + i // T)
+
+        for i in range(2):
+            bstep(i)
+        n_b = max(4, args.steps // 4)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(n_b):
+            bstep(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        b_ms = start.elapsed_time(end) / n_b
+        batched[str(B)] = {"ms_per_pass": round(b_ms, 4),
+                           "canvas_tok_s": round(B * C / (b_ms / 1e3), 1)}
+        log(f"batch of {B} canvases: {b_ms:.3f} ms per pass, {B * C / (b_ms / 1e3):.0f} canvas tok/s")
+    dg.dg_check_finite(h)
+
     # roofline of the dominant kernel (expert gate/up GEMM + SwiGLU)
     names = ["moe_gemm1", "moe_gemm2", "attention", "lm_head", "dense_gemm"]
     per_class_us = {n: (prof_ms[i] / prof_n[i] * 1e3 if prof_n[i] else None)
@@ -429,6 +462,7 @@ def main():
         "commit_ms": round(commit_ms, 3) if block_ms else None,
         "prefill_ms": round(prefill_ms, 2),
         "entropy_bounded_sampler": ebr,
+        "batched_canvases": batched,
         "pass_tflops": round(flops / (ms_per_pass * 1e-3) / 1e12, 2),
         "mfma_util_pct": {
             "moe_grouped_gemm": round(100 * moe_tflops / BF16_PEAK_TFLOPS, 2),

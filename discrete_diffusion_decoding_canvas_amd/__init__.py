@@ -28,6 +28,7 @@ EXPORTED = (
     "dg_moe_layer", "dg_init_canvas", "dg_profile_begin", "dg_profile_end", "dg_set_kv",
     "dg_set_capture", "dg_set_graphs", "dg_eb_sample", "dg_denoise_step_eb",
     "dg_generate_block_eb", "dg_attention_workspace_size", "dg_attention_noalloc",
+    "dg_denoise_step_batch", "dg_init_canvas_batch", "dg_generate_block_batch",
 )
 DG_PROF_MOE_GEMM1, DG_PROF_MOE_GEMM2, DG_PROF_ATTENTION, DG_PROF_LM_HEAD, DG_PROF_DENSE = range(5)
 DG_PROF_N = 5
@@ -48,7 +49,7 @@ class dg_model_cfg(ctypes.Structure):
         ("canvas", ctypes.c_int32), ("max_ctx", ctypes.c_int64), ("rope_base", ctypes.c_double),
         ("rms_eps", ctypes.c_float), ("temperature", ctypes.c_float),
         ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
-        ("capture_mask", ctypes.c_uint32),
+        ("capture_mask", ctypes.c_uint32), ("max_batch", ctypes.c_int32),
     ]
 
 
@@ -93,6 +94,9 @@ def _load_library():
                                          ctypes.POINTER(sz)], i32),
         "dg_attention_noalloc": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
                                   i32, i32, i32, vp], i32),
+        "dg_denoise_step_batch": ([vp, vp, vp, i32, i32, i32, u64, vp], i32),
+        "dg_init_canvas_batch": ([vp, vp, vp, i32, u64, vp], i32),
+        "dg_generate_block_batch": ([vp, vp, i32, i32, u64, vp], i32),
         "dg_moe_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
         "dg_init_canvas": ([vp, vp, vp, u64, vp], i32),
         "dg_profile_begin": ([vp, i32], i32),
@@ -169,6 +173,21 @@ def dg_denoise_step(h, d_canvas, d_locked_mask, step: int, T: int, seed: int,
                     stream=None) -> None:
     _check(_lib.dg_denoise_step(h, _ptr(d_canvas), _ptr(d_locked_mask), step, T, seed,
                                 _stream(stream)))
+
+
+def dg_denoise_step_batch(h, d_canvas, d_locked_mask, B: int, step: int, T: int, seed: int,
+                          stream=None) -> None:
+    _check(_lib.dg_denoise_step_batch(h, _ptr(d_canvas), _ptr(d_locked_mask), B, step, T, seed,
+                                      _stream(stream)))
+
+
+def dg_init_canvas_batch(h, d_canvas, d_locked_mask, B: int, seed: int, stream=None) -> None:
+    _check(_lib.dg_init_canvas_batch(h, _ptr(d_canvas), _ptr(d_locked_mask), B, seed,
+                                     _stream(stream)))
+
+
+def dg_generate_block_batch(h, d_out_tokens, B: int, T: int, seed: int, stream=None) -> None:
+    _check(_lib.dg_generate_block_batch(h, _ptr(d_out_tokens), B, T, seed, _stream(stream)))
 
 
 def dg_init_canvas(h, d_canvas, d_locked_mask, seed: int, stream=None) -> None:
@@ -294,10 +313,11 @@ def dg_profile_end(h):
 # ------------------------------------------------------------------ convenience
 def make_cfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, n_experts, top_k, d_ff, vocab,
              canvas, max_ctx, rope_base=10000.0, rms_eps=1e-6, temperature=1.0,
-             act_dtype=DG_BF16, expert_dtype=DG_BF16, capture_mask=0) -> dg_model_cfg:
+             act_dtype=DG_BF16, expert_dtype=DG_BF16, capture_mask=0,
+             max_batch=1) -> dg_model_cfg:
     return dg_model_cfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, n_experts, top_k,
                         d_ff, vocab, canvas, max_ctx, rope_base, rms_eps, temperature,
-                        act_dtype, expert_dtype, capture_mask)
+                        act_dtype, expert_dtype, capture_mask, max_batch)
 
 
 def load_weights(h, n_layers: int, n_experts: int, tensor_fn, experts_at_once: bool = True):

@@ -60,6 +60,9 @@ size_t dsize(int dt) { return dt == kF32 ? 4 : dt == kBF16 ? 2 : 1; }
 struct dg_handle {
     dg_model_cfg cfg;
     int L, d, Hq, Hkv, D, E, k, F, V, C;
+    int B_max = 1;          // canvases one batched pass can hold
+    int rows_max = 0;       // C * B_max: rows of the per-pass buffers
+    int last_rows = 0;      // rows of the last pass (what the captures hold)
     int act, edt;
     int64_t max_ctx, kv_rows;
     int max_tokens;
@@ -138,6 +141,7 @@ struct dg_handle {
     hipStream_t gstream = nullptr;   // capture stream (default priority)
     hipGraphExec_t gexec = nullptr;
     int64_t g_nctx = -1;
+    int g_rows = -1;
 
     // per-kernel-class event timing
     bool prof = false;
@@ -188,6 +192,8 @@ static int validate_cfg(const dg_model_cfg* c) {
     if (c->n_experts > 256 || c->n_experts % 4)
         return fail(DG_EINVAL, "n_experts must be a multiple of 4, at most 256");
     if (c->canvas > kMaxCanvas) return fail(DG_EINVAL, "canvas must be <= %d", kMaxCanvas);
+    if (c->max_batch < 0 || (int64_t)c->canvas * (c->max_batch > 1 ? c->max_batch : 1) > 65536)
+        return fail(DG_EINVAL, "max_batch must be >= 0 and max_batch * canvas <= 65536");
     if (c->head_dim & 1) return fail(DG_EINVAL, "head_dim must be even");
     if (c->d_model > 256 * kCombineCols || c->d_model % 4)
         return fail(DG_EINVAL, "d_model must be a multiple of 4, at most %d", 256 * kCombineCols);
@@ -251,11 +257,12 @@ static void drop_graph(dg_handle* h) {
     if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
     h->gexec = nullptr;
     h->g_nctx = -1;
+    h->g_rows = -1;
 }
 
 // Allocate the capture buffers a mask needs (once) and make it the active mask.
 static int alloc_captures(dg_handle* h, uint32_t mask) {
-    const size_t L = h->L, C = h->C, k = h->k;
+    const size_t L = h->L, C = h->rows_max, k = h->k;
     if ((mask & DG_CAP_LOGITS) && !h->logits_cap) DG_TRY(h->allocT(&h->logits_cap, C * h->V));
     if ((mask & DG_CAP_ROUTING) && !h->cap_idx) {
         DG_TRY(h->allocT(&h->cap_idx, L * C * k));
@@ -326,8 +333,11 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
 // One transformer layer for n tokens at positions pos0..pos0+n-1 (x, a hold the
 // residual and its norm).  Keys: cache rows [0, pos0 + n).  kv_only: stop after
 // writing K/V (the last encoder layer).
+// period > 0: the n rows are n / period canvases at the same positions pos0..pos0 +
+// period - 1 (a batched decoder pass); canvas b's cache rows are pos0 + b period +
+// i, and its queries see the context rows [0, pos0) and its own rows.
 static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool kv_only,
-                     hipStream_t s, bool capture = false) {
+                     hipStream_t s, bool capture = false, int period = 0) {
     if (h->act == kBF16) {
         // Af: a in fragment order, from the norm that wrote it.  The QKV weights are
         // pair-tiled (rope_hd 128), so the GEMM's epilogue applies RoPE and writes Q
@@ -337,6 +347,7 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
         ra.Hq = h->Hq;
         ra.Hkv = h->Hkv;
         ra.pos0 = pos0;
+        ra.period = period;
         ra.cos_t = h->cos_t;
         ra.sin_t = h->sin_t;
         ra.q = h->q;
@@ -351,7 +362,7 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
             K_TRY(launch_gemm(h->act, kEpiStoreF32, h->a, h->d, n, h->wqkv[l], h->d, h->qkv_n,
                               h->qkv, h->qkv_n, s));
         }
-        K_TRY(launch_rope_scatter(h->act, h->qkv, n, h->Hq, h->Hkv, h->D, pos0, h->cos_t,
+        K_TRY(launch_rope_scatter(h->act, h->qkv, n, h->Hq, h->Hkv, h->D, pos0, period, h->cos_t,
                                   h->sin_t, h->q, h->klayer(l), h->vlayer(l), h->kv_rows, s));
     }
     if (kv_only) return DG_OK;
@@ -364,7 +375,9 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
     aa.Hq = h->Hq;
     aa.Hkv = h->Hkv;
     aa.M = n;
-    aa.S = (int)(pos0 + n);
+    aa.S = (int)(pos0 + (period > 0 ? period : n));
+    aa.ctx = period > 0 ? pos0 : 0;
+    aa.canvas = period;
     aa.D = h->D;
     aa.kv_rows = h->kv_rows;
     aa.v_rows = h->kv_rows;
@@ -436,11 +449,13 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     h->F = cfg->d_ff;
     h->V = cfg->vocab;
     h->C = cfg->canvas;
+    h->B_max = cfg->max_batch > 1 ? cfg->max_batch : 1;
+    h->rows_max = h->C * h->B_max;
     h->act = cfg->act_dtype == DG_F32 ? kF32 : kBF16;
     h->edt = cfg->expert_dtype == DG_F32 ? kF32 : cfg->expert_dtype == DG_BF16 ? kBF16 : kFP8;
     h->max_ctx = cfg->max_ctx;
     h->kv_rows = (cfg->max_ctx + 31) & ~(int64_t)31;
-    h->max_tokens = std::max(h->C, kPrefillChunk);
+    h->max_tokens = std::max(h->rows_max, kPrefillChunk);
     h->qkv_n = (h->Hq + 2 * h->Hkv) * h->D;
     h->loaded.assign(1 + (size_t)h->L * 5 + (size_t)h->L * 3 * h->E, 0);
 
@@ -529,23 +544,23 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->Y, rows * d));
     const int ns = lm_head_slices(h->act, h->V);
     h->hp.n_slices = ns;
-    A_TRY(h->allocT(&h->hp.m, (size_t)h->C * ns));
-    A_TRY(h->allocT(&h->hp.a, (size_t)h->C * ns));
-    A_TRY(h->allocT(&h->hp.s, (size_t)h->C * ns));
-    A_TRY(h->allocT(&h->hp.g, (size_t)h->C * ns));
-    A_TRY(h->allocT(&h->hp.gi, (size_t)h->C * ns));
-    A_TRY(h->allocT(&h->st_m, h->C));
-    A_TRY(h->allocT(&h->st_a, h->C));
-    A_TRY(h->allocT(&h->st_lse, h->C));
-    A_TRY(h->allocT(&h->st_conf, h->C));
-    A_TRY(h->allocT(&h->st_draw, h->C));
-    A_TRY(h->allocT(&h->st_ent, h->C));
-    A_TRY(h->allocT(&h->hp_q, (size_t)h->C * ns));
+    A_TRY(h->allocT(&h->hp.m, (size_t)h->rows_max * ns));
+    A_TRY(h->allocT(&h->hp.a, (size_t)h->rows_max * ns));
+    A_TRY(h->allocT(&h->hp.s, (size_t)h->rows_max * ns));
+    A_TRY(h->allocT(&h->hp.g, (size_t)h->rows_max * ns));
+    A_TRY(h->allocT(&h->hp.gi, (size_t)h->rows_max * ns));
+    A_TRY(h->allocT(&h->st_m, h->rows_max));
+    A_TRY(h->allocT(&h->st_a, h->rows_max));
+    A_TRY(h->allocT(&h->st_lse, h->rows_max));
+    A_TRY(h->allocT(&h->st_conf, h->rows_max));
+    A_TRY(h->allocT(&h->st_draw, h->rows_max));
+    A_TRY(h->allocT(&h->st_ent, h->rows_max));
+    A_TRY(h->allocT(&h->hp_q, (size_t)h->rows_max * ns));
     A_TRY(h->allocT(&h->eb_prev, h->C));
     A_TRY(h->allocT(&h->eb_info, 4));
     A_TRY(h->allocT(&h->bad, 1));
-    A_TRY(h->allocT(&h->blk_canvas, h->C));
-    A_TRY(h->allocT(&h->blk_mask, h->C));
+    A_TRY(h->allocT(&h->blk_canvas, h->rows_max));
+    A_TRY(h->allocT(&h->blk_mask, h->rows_max));
     A_TRY(alloc_captures(h, cfg->capture_mask));
 #undef A_TRY
     *out = h;
@@ -787,14 +802,16 @@ int dg_commit_canvas(dg_handle* h, const int32_t* d_canvas, void* stream) {
 // The L decoder layers of a denoise pass over the canvas at n_ctx, as one HIP
 // graph replayed on stream s.  Captured on the handle's own stream the first
 // time for this context length.  The kernels record no memset nodes.
-static int run_layers_graph(dg_handle* h, hipStream_t s) {
-    if (!h->gexec || h->g_nctx != h->n_ctx) {
+static int run_layers_graph(dg_handle* h, int B, hipStream_t s) {
+    const int rows = B * h->C;
+    if (!h->gexec || h->g_nctx != h->n_ctx || h->g_rows != rows) {
         drop_graph(h);
         if (!h->gstream) HIP_TRY(hipStreamCreateWithFlags(&h->gstream, hipStreamNonBlocking));
         HIP_TRY(hipStreamBeginCapture(h->gstream, hipStreamCaptureModeThreadLocal));
         int rc = DG_OK;
         for (int l = 0; l < h->L && rc == DG_OK; ++l)
-            rc = run_layer(h, l, h->C, h->n_ctx, false, false, h->gstream, false);
+            rc = run_layer(h, l, rows, h->n_ctx, false, false, h->gstream, false,
+                           B > 1 ? h->C : 0);
         hipGraph_t g = nullptr;
         const hipError_t e = hipStreamEndCapture(h->gstream, &g);
         if (rc != DG_OK || e != hipSuccess) {
@@ -809,6 +826,7 @@ static int run_layers_graph(dg_handle* h, hipStream_t s) {
             return fail(DG_EHIP, "graph instantiation failed: %s", hipGetErrorString(ei));
         }
         h->g_nctx = h->n_ctx;
+        h->g_rows = rows;
     }
     HIP_TRY(hipGraphLaunch(h->gexec, s));
     return DG_OK;
@@ -817,21 +835,25 @@ static int run_layers_graph(dg_handle* h, hipStream_t s) {
 // Decoder over the canvas, LM head at temperature 1 / inv_tau and the per-position
 // statistics (with the predictive entropy when ent is set): everything of a pass
 // but the sampler.
+// B canvases of C rows each (B > 1: a batch at the same positions, see run_layer).
 static int decode_and_head(dg_handle* h, const int32_t* d_canvas, const uint8_t* d_locked_mask,
-                           int32_t step, float inv_tau, uint64_t seed, bool ent, hipStream_t s) {
+                           int32_t step, float inv_tau, uint64_t seed, bool ent, hipStream_t s,
+                           int B = 1) {
     if (!h->prefilled) return fail(DG_ESTATE, "denoise step before prefill");
-    if (h->n_ctx + h->C > h->max_ctx)
-        return fail(DG_ECAPACITY, "canvas at %lld exceeds max_ctx %lld", (long long)h->n_ctx,
-                    (long long)h->max_ctx);
+    if (h->n_ctx + (int64_t)B * h->C > h->max_ctx)
+        return fail(DG_ECAPACITY, "%d canvas(es) at %lld exceed max_ctx %lld", B,
+                    (long long)h->n_ctx, (long long)h->max_ctx);
     DG_TRY(ensure_ready(h));
-    const int C = h->C;
+    const int C = B * h->C;        // rows of this pass
+    const int period = B > 1 ? h->C : 0;
+    h->last_rows = C;
     K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, h->V, C, h->d,
                                h->cfg.rms_eps, h->x, h->a, h->Af, h->bad, s));
     const uint32_t per_layer = DG_CAP_ROUTING | DG_CAP_HIDDEN | DG_CAP_ATTN | DG_CAP_ROUTER_LOGITS;
     if (h->use_graphs && !h->prof && !(h->cap_mask & per_layer)) {
-        DG_TRY(run_layers_graph(h, s));
+        DG_TRY(run_layers_graph(h, B, s));
     } else for (int l = 0; l < h->L; ++l) {
-        DG_TRY(run_layer(h, l, C, h->n_ctx, false, false, s, true));
+        DG_TRY(run_layer(h, l, C, h->n_ctx, false, false, s, true, period));
         if (h->cap(DG_CAP_ROUTING)) {
             HIP_TRY(hipMemcpyAsync(h->cap_idx + (size_t)l * C * h->k, h->idx,
                                    (size_t)C * h->k * 4, hipMemcpyDeviceToDevice, s));
@@ -863,7 +885,34 @@ int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int
     hipStream_t s = (hipStream_t)stream;
     DG_TRY(decode_and_head(h, d_canvas, d_locked_mask, step, 1.0f / h->cfg.temperature, seed,
                            false, s));
-    K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, h->C, step, T, s));
+    K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, h->C, 1, step,
+                         T, s));
+    return DG_OK;
+}
+
+// A batch of canvases is B canvases continuing the same context at the same
+// positions: each attends to the context and to itself (not to the others), and
+// canvas b draws its Philox uniforms as positions b C .. b C + C - 1 of one long
+// canvas, so a batch of one is dg_denoise_step.
+static int check_batch(dg_handle* h, int32_t B) {
+    if (B < 1 || B > h->B_max) return fail(DG_EINVAL, "batch %d outside [1, %d] (max_batch)", B, h->B_max);
+    if (B > 1 && h->act == kBF16 && (h->C % 256 || (h->n_ctx & 31)))
+        return fail(DG_EINVAL, "batched bf16 passes need canvas %% 256 == 0 and a context length "
+                               "that is a multiple of 32 (n_ctx %lld)", (long long)h->n_ctx);
+    return DG_OK;
+}
+
+int dg_denoise_step_batch(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t B,
+                          int32_t step, int32_t T, uint64_t seed, void* stream) {
+    g_err.clear();
+    if (!h || !d_canvas || !d_locked_mask) return fail(DG_EINVAL, "NULL handle, canvas or mask");
+    if (T <= 0 || step < 0 || step >= T) return fail(DG_EINVAL, "need 0 <= step < T (step %d, T %d)", step, T);
+    DG_TRY(check_batch(h, B));
+    hipStream_t s = (hipStream_t)stream;
+    DG_TRY(decode_and_head(h, d_canvas, d_locked_mask, step, 1.0f / h->cfg.temperature, seed,
+                           false, s, B));
+    K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, h->C, B, step,
+                         T, s));
     return DG_OK;
 }
 
@@ -949,6 +998,37 @@ int dg_init_canvas(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, uint
     return DG_OK;
 }
 
+int dg_init_canvas_batch(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t B,
+                         uint64_t seed, void* stream) {
+    g_err.clear();
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    if (B < 1 || B > h->B_max) return fail(DG_EINVAL, "batch %d outside [1, %d]", B, h->B_max);
+    if (!d_canvas && !d_locked_mask) return DG_OK;
+    K_TRY(launch_canvas_init(d_canvas, d_locked_mask, B * h->C, h->V, seed, h->k_blk,
+                             (hipStream_t)stream));
+    return DG_OK;
+}
+
+int dg_generate_block_batch(dg_handle* h, int32_t* d_out_tokens, int32_t B, int32_t T,
+                            uint64_t seed, void* stream) {
+    g_err.clear();
+    if (!h || !d_out_tokens) return fail(DG_EINVAL, "NULL handle or output");
+    if (T <= 0) return fail(DG_EINVAL, "T must be > 0");
+    if (!h->prefilled) return fail(DG_ESTATE, "generate before prefill");
+    DG_TRY(check_batch(h, B));
+    if (h->n_ctx + (int64_t)B * h->C > h->max_ctx)
+        return fail(DG_ECAPACITY, "%d canvases at %lld exceed max_ctx %lld", B,
+                    (long long)h->n_ctx, (long long)h->max_ctx);
+    DG_TRY(ensure_ready(h));
+    hipStream_t s = (hipStream_t)stream;
+    K_TRY(launch_canvas_init(h->blk_canvas, h->blk_mask, B * h->C, h->V, seed, h->k_blk, s));
+    for (int st = 0; st < T; ++st)
+        DG_TRY(dg_denoise_step_batch(h, h->blk_canvas, h->blk_mask, B, st, T, seed, stream));
+    HIP_TRY(hipMemcpyAsync(d_out_tokens, h->blk_canvas, (size_t)B * h->C * 4,
+                           hipMemcpyDeviceToDevice, s));
+    return check_bad(h, s);
+}
+
 int dg_generate_block(dg_handle* h, int32_t* d_out_tokens, int32_t T, uint64_t seed,
                       int32_t commit, void* stream) {
     g_err.clear();
@@ -1002,7 +1082,7 @@ int dg_get_capture(dg_handle* h, uint32_t what, int32_t layer, void* d_dst, size
     g_err.clear();
     if (!h || !d_dst) return fail(DG_EINVAL, "NULL handle or destination");
     hipStream_t s = (hipStream_t)stream;
-    const size_t C = h->C;
+    const size_t C = h->last_rows > 0 ? h->last_rows : h->C;   // rows of the last pass
     if (what == DG_CAP_STATS) {
         if (bytes != C * 4 * 5) return fail(DG_EINVAL, "stats capture is %zu bytes", C * 20);
         char* d = (char*)d_dst;

@@ -92,9 +92,11 @@ hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, c
                                 int32_t* bad, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
                           uint8_t* a8, void* af, hipStream_t s);
+// Token m sits at RoPE position pos0 + m (period 0) or pos0 + m % period, and in
+// cache row pos0 + m.
 hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int Hkv, int D,
-                               int64_t pos0, const float* cos_t, const float* sin_t, void* q,
-                               void* kc, void* vc, int64_t kv_rows, hipStream_t s);
+                               int64_t pos0, int period, const float* cos_t, const float* sin_t,
+                               void* q, void* kc, void* vc, int64_t kv_rows, hipStream_t s);
 hipError_t launch_pack_vt(const void* v, int Hkv, int S, int D, void* vt, int64_t rows,
                           hipStream_t s);
 hipError_t launch_read_kv(int dtype, bool vpacked, const void* cache, int Hkv, int D,
@@ -117,8 +119,10 @@ hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint
 hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, float* st_m,
                              int32_t* st_a, float* st_lse, float* st_conf, int32_t* st_draw,
                              float* st_ent, int32_t* bad, hipStream_t s);
+// B canvases of C positions each, one workgroup per canvas.
 hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t* draw,
-                          int32_t* canvas, uint8_t* mask, int C, int step, int T, hipStream_t s);
+                          int32_t* canvas, uint8_t* mask, int C, int B, int step, int T,
+                          hipStream_t s);
 // One pass of the entropy-bounded sampler (k_sampler_eb); C <= kMaxCanvas.
 hipError_t launch_sampler_eb(const float* ent, const int32_t* amax, const int32_t* draw,
                              int32_t* prev, int32_t* canvas, uint8_t* mask, int32_t* info, int C,
@@ -143,11 +147,12 @@ constexpr int kEpiAddF32 = 1;     // C[m, n] += acc (residual add, single writer
 constexpr int kEpiRope = 2;       // QKV with pair-tiled columns: RoPE, bf16 Q, K and V cache writes
 
 // The QKV epilogue's destinations (head dim 128): Q bf16 [Hq][M][128], the K
-// cache bf16 [Hkv][kv_rows][128] and the V cache transposed (vt_index), rows at
-// positions pos0 + m; cos/sin tables [position][64].
+// cache bf16 [Hkv][kv_rows][128] and the V cache transposed (vt_index), rows
+// pos0 + m; cos/sin tables [position][64].
 struct RopeArgs {
     int Hq = 0, Hkv = 0;
     int64_t pos0 = 0;
+    int period = 0;        // > 0: token m at RoPE position pos0 + m % period (cache row pos0 + m)
     const float* cos_t = nullptr;
     const float* sin_t = nullptr;
     void* q = nullptr;
@@ -230,6 +235,12 @@ struct AttnArgs {
                            // averages [split][Hq][M][D], then float (max, sum) pairs
     size_t part_bytes = 0; // bytes available at part
     int32_t* bad = nullptr; // optional: kBadRange when a binary16 split average saturates
+    // A batch of canvases at the same positions (canvas > 0, decoder only): queries
+    // m of canvas b = m / canvas see keys 0..S-1 where key j < ctx is cache row j
+    // (the shared context) and key j >= ctx is row j + b * canvas (the canvas's own
+    // rows); S = ctx + canvas.  bf16 needs canvas % 256 == 0 and ctx % 32 == 0.
+    int64_t ctx = 0;
+    int canvas = 0;
 };
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 // Bytes of split partials a call with these sizes needs (0 when it runs unsplit).

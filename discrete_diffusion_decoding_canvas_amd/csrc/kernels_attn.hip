@@ -156,13 +156,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     int Hq, int Hkv, int M, int S, int64_t k_rows, int64_t v_rows, float scale_log2,
     int64_t q_pos0, int keys_per_split, int n_splits, bf16_t* __restrict__ O,
     uint8_t* __restrict__ Of, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int32_t* __restrict__ bad) {
+    int32_t* __restrict__ bad, int ctx, int canvas) {
     __shared__ AttnSlot ring[kAttnRing];
     const int G = Hq / Hkv;
     const int GM = G * M;
     const int kvh = blockIdx.y;
     const int split = blockIdx.z;
     const int row_base = blockIdx.x * kAttnRows;
+    // batch of canvases: this workgroup's rows are queries of one canvas (canvas is a
+    // multiple of kAttnRows), whose own keys sit boff rows past the shared context
+    const int boff = canvas > 0 ? (row_base % M) / canvas * canvas : 0;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, g = lane >> 4;
 
@@ -188,15 +191,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
             if (!is_v) {
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) {
-                    const int key = min(key0 + 16 * kh + l16, S - 1);
+                    int key = min(key0 + 16 * kh + l16, S - 1);
+                    if (key >= ctx) key += boff;
                     const bf16_t* src = Kh + (int64_t)key * kAttnD + 8 * g;
 #pragma unroll
                     for (int st = 0; st < 4; ++st) dma16(src + 32 * st, &slot->k[kh][st][0]);
                 }
             } else {
+                const int vkey0 = key0 >= ctx ? key0 + boff : key0;   // ctx % 32 == 0 when batched
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt)
-                    dma16(Vh + (int64_t)(16 * dt + l16) * v_rows + key0 + 8 * g, &slot->v[dt][0]);
+                    dma16(Vh + (int64_t)(16 * dt + l16) * v_rows + vkey0 + 8 * g, &slot->v[dt][0]);
             }
         };
         // The consumers read K of block b + 1 and V of block b in iteration b, so before
@@ -446,10 +451,11 @@ __global__ __launch_bounds__(64) void k_attn_f32(const float* __restrict__ Q,
                                                  const float* __restrict__ V, int Hq, int Hkv,
                                                  int M, int S, int64_t rows, float scale,
                                                  int causal, int64_t q_pos0,
-                                                 float* __restrict__ O) {
+                                                 float* __restrict__ O, int ctx, int canvas) {
     const int q = blockIdx.x * 64 + threadIdx.x;
     const int h = blockIdx.y;
     if (q >= M) return;
+    const int boff = canvas > 0 ? q / canvas * canvas : 0;   // batch: the canvas's own rows
     const int kvh = h / (Hq / Hkv);
     float qv[D], ov[D];
 #pragma unroll
@@ -466,14 +472,15 @@ __global__ __launch_bounds__(64) void k_attn_f32(const float* __restrict__ Q,
     const float* Kh = K + (int64_t)kvh * rows * D;
     const float* Vh = V + (int64_t)kvh * rows * D;
     for (int j = 0; j < kend; ++j) {
+        const int64_t jr = j >= ctx ? j + boff : j;
         float s = 0.f;
 #pragma unroll
-        for (int t = 0; t < D; ++t) s = fmaf(qv[t], Kh[(int64_t)j * D + t], s);
+        for (int t = 0; t < D; ++t) s = fmaf(qv[t], Kh[jr * D + t], s);
         const float mn = fmaxf(m, s);
         const float a = expf(m - mn), p = expf(s - mn);
         l = l * a + p;
 #pragma unroll
-        for (int t = 0; t < D; ++t) ov[t] = ov[t] * a + p * Vh[(int64_t)j * D + t];
+        for (int t = 0; t < D; ++t) ov[t] = ov[t] * a + p * Vh[jr * D + t];
         m = mn;
     }
     const float inv = 1.0f / l;
@@ -521,18 +528,26 @@ size_t attention_part_bytes(int dtype, int Hq, int Hkv, int M, int S, int D) {
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
+    const int ctx = a.canvas > 0 ? (int)a.ctx : a.S;   // no remap: every key below ctx
+    if (a.canvas > 0) {
+        // every query's keys: the shared context, then its canvas's own rows
+        if (a.causal || a.M % a.canvas || a.ctx < 0 || a.S != a.ctx + a.canvas ||
+            a.kv_rows < a.ctx + a.M || (dtype != kF32 && (a.canvas % kAttnRows || (a.ctx & 31) ||
+                                                        a.v_rows < a.ctx + a.M)))
+            return hipErrorInvalidValue;
+    }
     if (dtype == kF32) {
         dim3 grid((a.M + 63) / 64, a.Hq);
         if (a.D == 64)
             k_attn_f32<64><<<grid, 64, 0, s>>>((const float*)a.q, (const float*)a.k,
                                                (const float*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                a.kv_rows, a.scale, a.causal, a.q_pos0,
-                                               (float*)a.o);
+                                               (float*)a.o, ctx, a.canvas);
         else if (a.D == 128)
             k_attn_f32<128><<<grid, 64, 0, s>>>((const float*)a.q, (const float*)a.k,
                                                 (const float*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                 a.kv_rows, a.scale, a.causal, a.q_pos0,
-                                                (float*)a.o);
+                                                (float*)a.o, ctx, a.canvas);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
@@ -553,12 +568,14 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
         k_attn_bf16<true><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                (const bf16_t*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                a.kv_rows, a.v_rows, sl2, a.q_pos0, kps, n,
-                                               (bf16_t*)a.o, (uint8_t*)a.of, po, pml, a.bad);
+                                               (bf16_t*)a.o, (uint8_t*)a.of, po, pml, a.bad, ctx,
+                                               a.canvas);
     else
         k_attn_bf16<false><<<grid, kAttnThreads, 0, s>>>((const bf16_t*)a.q, (const bf16_t*)a.k,
                                                 (const bf16_t*)a.v, a.Hq, a.Hkv, a.M, a.S,
                                                 a.kv_rows, a.v_rows, sl2, a.q_pos0, kps, n,
-                                                (bf16_t*)a.o, (uint8_t*)a.of, po, pml, a.bad);
+                                                (bf16_t*)a.o, (uint8_t*)a.of, po, pml, a.bad, ctx,
+                                               a.canvas);
     if (n > 1)
         k_attn_combine<bf16_t><<<(a.M * a.Hq + 3) / 4, 256, 0, s>>>(po, pml, n, a.Hq, a.M,
                                                                     (bf16_t*)a.o, (uint8_t*)a.of);

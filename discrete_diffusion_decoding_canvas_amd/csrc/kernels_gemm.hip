@@ -304,11 +304,11 @@ __global__ __launch_bounds__(kDenseThreads) void k_dense_frag(const uint8_t* __r
                 const int r = e >> 5, c = e & 31;          // consecutive lanes: consecutive dims
                 const int m = m0 + r;
                 if (m >= M) continue;
-                const int64_t pos = ra.pos0 + m;
+                const int64_t pos = ra.pos0 + (ra.period > 0 ? m % ra.period : m);
                 const int j = 32 * tp + c;
                 const float x1 = rsum(r, c), x2 = rsum(r, c + 32);
                 const float cs = ra.cos_t[pos * half + j], sn = ra.sin_t[pos * half + j];
-                bf16_t* dst = base + (size_t)(head < ra.Hq ? m : pos) * D;
+                bf16_t* dst = base + (size_t)(head < ra.Hq ? m : ra.pos0 + m) * D;
                 dst[j] = f32_to_bf16(x1 * cs - x2 * sn);
                 dst[j + half] = f32_to_bf16(x2 * cs + x1 * sn);
             }

@@ -140,13 +140,14 @@ __global__ __launch_bounds__(NT) void k_rmsnorm(const float* __restrict__ x, int
 // ------------------------------------------------------------------ RoPE + scatter
 // f32 path: qkv [M, (Hq + 2 Hkv) D] -> Q [Hq][M][D] rotated, K cache rows pos0+m
 // rotated, V cache rows pos0+m.  Rotate-half pairs (j, j + D/2), angle table
-// [pos][D/2].  One block per (32 tokens, head).  (The bf16 path rotates in the
-// QKV GEMM's epilogue.)
+// [pos][D/2]; the position of token m is pos0 + m, or pos0 + m % period for a
+// batch of canvases at the same positions (period = C > 0).  One block per (32
+// tokens, head).  (The bf16 path rotates in the QKV GEMM's epilogue.)
 constexpr int kRopeTokens = 32;
 
 template <int D>
 __global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ qkv, int M, int Hq,
-                                                      int Hkv, int64_t pos0,
+                                                      int Hkv, int64_t pos0, int period,
                                                       const float* __restrict__ cos_t,
                                                       const float* __restrict__ sin_t,
                                                       float* __restrict__ q, float* __restrict__ kc,
@@ -159,18 +160,19 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ 
     for (int e = threadIdx.x; e < nt * half; e += 256) {
         const int mi = e / half, j = e - mi * half;
         const int m = m0 + mi;
-        const int64_t pos = pos0 + m;
+        const int64_t row = pos0 + m;                              // cache row
+        const int64_t pos = pos0 + (period > 0 ? m % period : m);  // RoPE position
         const float* src = qkv + (int64_t)m * ld + (int64_t)head * D;
         const float x1 = src[j], x2 = src[j + half];
         if (head < Hq + Hkv) {
             const float c = cos_t[pos * half + j], sn = sin_t[pos * half + j];
             const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
             float* dst = head < Hq ? q + ((int64_t)head * M + m) * D
-                                   : kc + ((int64_t)(head - Hq) * kv_rows + pos) * D;
+                                   : kc + ((int64_t)(head - Hq) * kv_rows + row) * D;
             dst[j] = y1;
             dst[j + half] = y2;
         } else {
-            float* dst = vc + ((int64_t)(head - Hq - Hkv) * kv_rows + pos) * D;
+            float* dst = vc + ((int64_t)(head - Hq - Hkv) * kv_rows + row) * D;
             dst[j] = x1;
             dst[j + half] = x2;
         }
@@ -414,6 +416,15 @@ __global__ __launch_bounds__(1024) void k_sampler(const float* __restrict__ conf
                                                   int32_t* __restrict__ canvas,
                                                   uint8_t* __restrict__ mask, int C, int step,
                                                   int T) {
+    // workgroup b samples canvas b of a batch (positions b C .. b C + C - 1)
+    {
+        const int64_t o = (int64_t)blockIdx.x * C;
+        conf += o;
+        amax += o;
+        draw += o;
+        canvas += o;
+        mask += o;
+    }
     __shared__ __attribute__((aligned(16))) float cf[kMaxCanvas];
     __shared__ __attribute__((aligned(16))) uint8_t un[kMaxCanvas];
     __shared__ int n_unl;
@@ -667,20 +678,22 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, vo
 }
 
 template <int D>
-static void rope_d(const float* qkv, int M, int Hq, int Hkv, int64_t pos0, const float* cos_t,
-                   const float* sin_t, void* q, void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
+static void rope_d(const float* qkv, int M, int Hq, int Hkv, int64_t pos0, int period,
+                   const float* cos_t, const float* sin_t, void* q, void* kc, void* vc,
+                   int64_t kv_rows, hipStream_t s) {
     dim3 grid((M + kRopeTokens - 1) / kRopeTokens, Hq + 2 * Hkv);
-    k_rope_scatter<D><<<grid, 256, 0, s>>>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, (float*)q,
+    k_rope_scatter<D><<<grid, 256, 0, s>>>(qkv, M, Hq, Hkv, pos0, period, cos_t, sin_t, (float*)q,
                                            (float*)kc, (float*)vc, kv_rows);
 }
 
 hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int Hkv, int D,
-                               int64_t pos0, const float* cos_t, const float* sin_t, void* q,
-                               void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
+                               int64_t pos0, int period, const float* cos_t, const float* sin_t,
+                               void* q, void* kc, void* vc, int64_t kv_rows, hipStream_t s) {
     if (M <= 0) return hipSuccess;
+    if (period < 0) return hipErrorInvalidValue;
     if (dtype == kF32) {
-        if (D == 64) rope_d<64>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
-        else if (D == 128) rope_d<128>(qkv, M, Hq, Hkv, pos0, cos_t, sin_t, q, kc, vc, kv_rows, s);
+        if (D == 64) rope_d<64>(qkv, M, Hq, Hkv, pos0, period, cos_t, sin_t, q, kc, vc, kv_rows, s);
+        else if (D == 128) rope_d<128>(qkv, M, Hq, Hkv, pos0, period, cos_t, sin_t, q, kc, vc, kv_rows, s);
         else return hipErrorInvalidValue;
     } else {
         return hipErrorInvalidValue;   // bf16: RoPE runs in the QKV GEMM's epilogue (kEpiRope)
@@ -782,9 +795,10 @@ hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, 
 }
 
 hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t* draw,
-                          int32_t* canvas, uint8_t* mask, int C, int step, int T,
+                          int32_t* canvas, uint8_t* mask, int C, int B, int step, int T,
                           hipStream_t s) {
-    k_sampler<<<1, 1024, 0, s>>>(conf, amax, draw, canvas, mask, C, step, T);
+    if (C <= 0 || C > kMaxCanvas || B <= 0) return hipErrorInvalidValue;
+    k_sampler<<<B, 1024, 0, s>>>(conf, amax, draw, canvas, mask, C, step, T);
     LAUNCH_CHECK();
 }
 

@@ -12,13 +12,14 @@ from . import Workload, model_tensor, prompt_ids, tensor_shape
 KIND_NAMES = ("embed", "wq", "wk", "wv", "wo", "wr", "wg", "wu", "wd")
 
 
-def make_cfg(dg, w: Workload, capture_mask: int = 0, max_ctx: int | None = None):
+def make_cfg(dg, w: Workload, capture_mask: int = 0, max_ctx: int | None = None,
+             max_batch: int = 1):
     act = dg.DG_F32 if w.act == "f32" else dg.DG_BF16
     exp = {"f32": dg.DG_F32, "bf16": dg.DG_BF16, "fp8": dg.DG_FP8_E4M3}[w.experts]
     return dg.make_cfg(w.n_layers, w.d_model, w.n_q_heads, w.n_kv_heads, w.head_dim,
                        w.n_experts, w.top_k, w.d_ff, w.vocab, w.canvas,
                        max_ctx if max_ctx is not None else w.max_ctx, w.rope_base, w.rms_eps,
-                       w.temperature, act, exp, capture_mask)
+                       w.temperature, act, exp, capture_mask, max_batch)
 
 
 def tensor_fn(w: Workload):
@@ -37,8 +38,9 @@ def tensor_fn(w: Workload):
     return fn
 
 
-def build_handle(dg, w: Workload, capture_mask: int = 0, max_ctx: int | None = None):
-    h = dg.dg_create(make_cfg(dg, w, capture_mask, max_ctx))
+def build_handle(dg, w: Workload, capture_mask: int = 0, max_ctx: int | None = None,
+                 max_batch: int = 1):
+    h = dg.dg_create(make_cfg(dg, w, capture_mask, max_ctx, max_batch))
     try:
         dg.load_weights(h, w.n_layers, w.n_experts, tensor_fn(w))
     except Exception:

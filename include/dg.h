@@ -85,7 +85,8 @@ extern "C" {
 
 /* ---------------------------------------------------------------- captures
  * Debug captures of the last dg_denoise_step, enabled per handle by
- * capture_mask.  Layouts:
+ * capture_mask.  Layouts, with C the rows of that pass (the canvas, or
+ * B * canvas after a batched pass):
  *   DG_CAP_LOGITS   float [C, V] tempered logits of the last pass
  *   DG_CAP_STATS    per position, 5 arrays of C elements in this order:
  *                   float m (max tempered logit), int32 argmax,
@@ -125,6 +126,8 @@ typedef struct dg_model_cfg {
     int32_t act_dtype;     /* DG_F32 or DG_BF16: activations, KV cache, dense weights */
     int32_t expert_dtype;  /* DG_F32, DG_BF16 or DG_FP8_E4M3 (needs act_dtype DG_BF16) */
     uint32_t capture_mask; /* DG_CAP_* bits */
+    int32_t max_batch;     /* canvases one batched pass holds (dg_denoise_step_batch); 0 or 1:
+                              single canvases only.  max_batch * canvas <= 65536 */
 } dg_model_cfg;
 
 typedef struct dg_handle dg_handle;
@@ -189,6 +192,34 @@ int dg_init_canvas(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, uint
  * handle checks the non-finite flag (always: it reads one int at the end). */
 int dg_generate_block(dg_handle* h, int32_t* d_out_tokens, int32_t T, uint64_t seed,
                       int32_t commit, void* stream);
+
+/* ---------------------------------------------------------------- batched canvases
+ * B canvases (1 <= B <= cfg.max_batch) denoised in one pass (the technical-report
+ * summary's Experiment, inference analysis: the method's advantage is largest at
+ * low batch, its throughput at large batch lower; the alphasignal page, "The
+ * numbers", low-to-medium batch).  The B canvases continue the same context at
+ * the same positions n_ctx..n_ctx+C-1, as independent samples of the next
+ * block: every canvas attends bidirectionally to the context and to itself,
+ * never to another canvas of the batch; its K/V rows go to cache rows n_ctx + b*C
+ * + i, so n_ctx + B*C <= max_ctx.  Canvas b draws its Philox uniforms as
+ * positions b*C .. b*C+C-1 of one long canvas (same counters as dg_denoise_step
+ * and dg_init_canvas otherwise), so a batch of one equals the single-canvas
+ * calls.  The lock schedule runs per canvas.  Buffers are [B][C] (canvas b at
+ * offset b*C).  bf16 activations need canvas % 256 == 0 and n_ctx % 32 == 0
+ * when B > 1.  Errors and asynchrony as dg_denoise_step. */
+int dg_denoise_step_batch(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t B,
+                          int32_t step, int32_t T, uint64_t seed, void* stream);
+
+/* The initial canvases of a batch (dg_init_canvas over B*C positions); either
+ * pointer may be NULL. */
+int dg_init_canvas_batch(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int32_t B,
+                         uint64_t seed, void* stream);
+
+/* B blocks at once: the initial canvases of the batch, T batched passes, the B
+ * canvases written to d_out_tokens (device int32 [B][C]).  No commit (commit one
+ * of them with dg_commit_canvas).  Synchronous as dg_generate_block. */
+int dg_generate_block_batch(dg_handle* h, int32_t* d_out_tokens, int32_t B, int32_t T,
+                            uint64_t seed, void* stream);
 
 /* ---------------------------------------------------------------- entropy-bounded sampler
  * The sampler of the technical-report summary (Method, the paragraphs on the

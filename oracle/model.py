@@ -381,7 +381,10 @@ class OracleModel:
                 hidden.append(h.copy())
         return self.head_logits(h), routes, hidden
 
-    def denoise_step(self, canvas, mask, s: int, T: int, seed: int, keep_logits=False):
+    def denoise_step(self, canvas, mask, s: int, T: int, seed: int, keep_logits=False,
+                     row0: int = 0):
+        """One pass over the canvas at positions n_ctx..n_ctx+C-1.  row0 offsets the rows
+        its Gumbel uniforms are drawn for (canvas b of a batch draws as rows b C ..)."""
         w = self.w
         logits, routes, hidden = self.decoder_logits(canvas)
         z = logits / w.temperature
@@ -394,7 +397,7 @@ class OracleModel:
             chunk = max(1, (1 << 24) // w.vocab)
             for c0 in range(0, unlocked.size, chunk):
                 pos = unlocked[c0:c0 + chunk]
-                u = gumbel_uniforms(seed, self.k_blk, s, pos, w.vocab)
+                u = gumbel_uniforms(seed, self.k_blk, s, pos + row0, w.vocab)
                 redraw[pos], gap[pos] = gumbel_draw(z[pos], u)
         sr = sampler_update(canvas, mask, st.conf, st.argmax, redraw, s, T)
         return StepResult(canvas=sr.canvas, mask=sr.mask, stats=st, redraw=redraw,
@@ -402,6 +405,21 @@ class OracleModel:
                           route_idx=[r[0] for r in routes], route_gates=[r[1] for r in routes],
                           route_margin=[r[2] for r in routes],
                           logits=z if keep_logits else None, hidden=hidden)
+
+    def denoise_step_batch(self, canvases, masks, s: int, T: int, seed: int,
+                           keep_logits=False):
+        """A batch of canvases continuing the same context at the same positions: each
+        canvas is a pass of its own (it attends to the context and to itself only), the
+        lock schedule runs per canvas, and canvas b draws its Gumbel uniforms as rows
+        b C .. b C + C - 1 of one long canvas.  Returns one StepResult per canvas."""
+        C = self.w.canvas
+        return [self.denoise_step(c, m, s, T, seed, keep_logits=keep_logits, row0=b * C)
+                for b, (c, m) in enumerate(zip(canvases, masks))]
+
+    def init_canvas_batch(self, seed: int, B: int):
+        """The initial canvases of a batch: B C positions of one long canvas, [B, C]."""
+        C = self.w.canvas
+        return init_canvas(seed, self.k_blk, B * C, self.w.vocab).reshape(B, C)
 
     def _draws(self, z, mask, s: int, seed: int):
         C = z.shape[0]

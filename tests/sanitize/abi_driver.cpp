@@ -23,7 +23,7 @@ int main() {
     dg_handle* h = nullptr;
     CHECK(dg_create(nullptr, &h) == DG_EINVAL && h == nullptr);
     CHECK(dg_create(nullptr, nullptr) == DG_EINVAL);
-    const int n_bad = 9;
+    const int n_bad = 11;
     for (int i = 0; i < n_bad; ++i) {
         dg_model_cfg c = base_cfg();
         switch (i) {
@@ -36,6 +36,8 @@ int main() {
             case 6: c.act_dtype = 7; break;
             case 7: c.act_dtype = DG_BF16; c.expert_dtype = DG_BF16; c.head_dim = 64; break;
             case 8: c.n_experts = 300; break;
+            case 9: c.max_batch = -1; break;
+            case 10: c.max_batch = 257; break;
         }
         CHECK(dg_create(&c, &h) == DG_EINVAL);
         CHECK(strlen(dg_last_error()) > 0);
@@ -66,6 +68,9 @@ int main() {
                        0, &p, 0, 0, nullptr) == DG_EINVAL);
     CHECK(dg_denoise_step_eb(nullptr, nullptr, nullptr, 0, &p, 0, nullptr, nullptr) == DG_EINVAL);
     CHECK(dg_generate_block_eb(nullptr, nullptr, &p, 0, 1, nullptr, nullptr) == DG_EINVAL);
+    CHECK(dg_denoise_step_batch(nullptr, nullptr, nullptr, 2, 0, 12, 0, nullptr) == DG_EINVAL);
+    CHECK(dg_init_canvas_batch(nullptr, nullptr, nullptr, 2, 0, nullptr) == DG_EINVAL);
+    CHECK(dg_generate_block_batch(nullptr, nullptr, 2, 12, 0, nullptr) == DG_EINVAL);
     if (fails) return 1;
     printf("abi driver ok\n");
     return 0;

@@ -47,6 +47,7 @@ def _cfg(dg, **kw):
     dict(n_layers=0), dict(n_q_heads=3), dict(top_k=9), dict(canvas=2048), dict(max_ctx=100),
     dict(temperature=0.0), dict(act_dtype=7), dict(act_dtype=1, expert_dtype=0),
     dict(act_dtype=1, expert_dtype=1, head_dim=64), dict(n_experts=300, top_k=2),
+    dict(max_batch=-1), dict(max_batch=257),
 ])
 def test_create_rejects_bad_configs(dg, bad):
     with pytest.raises(dg.DGError) as ei:
@@ -101,3 +102,10 @@ def test_attention_workspace_size_and_checks(dg):
     assert "workspace" in dg.dg_last_error()
     assert lib.dg_attention(*fake[:4], 16, 8, 256, 4352, 128, 0.1, 1, 4200, 1, fake[4], n,
                             None) == dg.DG_EINVAL     # causal queries beyond the keys
+
+
+def test_batched_entry_points_validate_before_any_device_call(dg):
+    lib = dg._lib
+    assert lib.dg_denoise_step_batch(None, None, None, 2, 0, 12, 0, None) == dg.DG_EINVAL
+    assert lib.dg_init_canvas_batch(None, None, None, 2, 0, None) == dg.DG_EINVAL
+    assert lib.dg_generate_block_batch(None, None, 2, 12, 0, None) == dg.DG_EINVAL

@@ -166,3 +166,36 @@ def test_encoder_rows_give_the_prefill_cache_of_the_next_layer():
     assert np.allclose(k1, full.K[1][:, pos], atol=1e-12)
     assert np.allclose(v1, full.V[1][:, pos], atol=1e-12)
     assert np.allclose(margin, full.enc_route_margin[0][pos], atol=1e-12)
+
+
+def test_batched_canvases_are_independent_passes_on_long_canvas_streams():
+    """A batch of canvases: a batch of one is the single pass; canvas b's pass equals a
+    single pass whose Gumbel uniforms are drawn at rows b C + i; identical canvases in a
+    batch get identical logits and statistics but independent redraws; the initial
+    canvases are the first B C positions of one long canvas."""
+    from oracle.philox import init_canvas, gumbel_uniforms
+    rng = np.random.default_rng(11)
+    w, W = _tiny(rng)
+    m = om.OracleModel(w, W)
+    m.prefill(rng.integers(0, w.vocab, 10))
+    C, seed = w.canvas, 5
+    inits = m.init_canvas_batch(seed, 3)
+    assert np.array_equal(inits.ravel(), init_canvas(seed, 0, 3 * C, w.vocab))
+    assert np.array_equal(inits[0], init_canvas(seed, 0, C, w.vocab))
+    masks = np.zeros((3, C), np.uint8)
+    canv = np.stack([inits[0], inits[1], inits[0]])
+    out = m.denoise_step_batch(canv, masks, 0, w.T, seed)
+    single = m.denoise_step(inits[0], masks[0], 0, w.T, seed)
+    assert np.array_equal(out[0].canvas, single.canvas) and np.array_equal(out[0].mask, single.mask)
+    # canvas 2 equals canvas 0 in everything but its redraw stream
+    assert np.allclose(out[2].stats.conf, out[0].stats.conf, atol=0, rtol=0)
+    assert np.array_equal(out[2].stats.argmax, out[0].stats.argmax)
+    assert np.array_equal(out[2].mask, out[0].mask)          # the lock set follows conf
+    unl = out[0].mask == 0
+    assert not np.array_equal(out[2].redraw[unl], out[0].redraw[unl])
+    # its redraws are the Gumbel-max draws at rows 2 C + i
+    logits, _, _ = m.decoder_logits(inits[0])
+    pos = np.flatnonzero(unl)[:5]
+    u = gumbel_uniforms(seed, 0, 0, pos + 2 * C, w.vocab)
+    draws, _ = om.gumbel_draw(logits[pos] / w.temperature, u)
+    assert np.array_equal(out[2].redraw[pos], draws)
