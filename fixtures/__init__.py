@@ -10,7 +10,9 @@ storage) is in ``gen.c``; every value is a pure function of
 Weights follow the "random-init N(0, 0.02)" recipe of the synthetic
 configurations; logical layouts are ``[in, out]`` row-major:
 E [V, d], Wq [d, Hq*D], Wk/Wv [d, Hkv*D], Wo [Hq*D, d], Wr [d, E],
-Wg/Wu [E, d, F], Wd [E, F, d].  RMSNorm gains are 1 and are not stored.
+Wg/Wu [E, d, F], Wd [E, F, d], and for self-conditioning workloads the one
+feed-forward block of the signal, sc_wg/sc_wu [d, Fsc], sc_wd [Fsc, d], drawn
+N(0, sc_sigma).  RMSNorm gains are 1 and are not stored.
 """
 from __future__ import annotations
 
@@ -133,6 +135,7 @@ TID_EMBED = 1
 TID_PROMPT = 2
 TID_ATTN_Q, TID_ATTN_K, TID_ATTN_V = 3, 4, 5
 TID_MOE_X = 6
+TID_SC = {"sc_wg": 7, "sc_wu": 8, "sc_wd": 9}   # self-conditioning block (one per model)
 KINDS = ("wq", "wk", "wv", "wo", "wr", "wg", "wu", "wd")
 
 
@@ -165,6 +168,13 @@ class Workload:
     temperature: float = 1.0
     sigma: float = 0.02
     seed: int = 0
+    self_cond: bool = False    # z = FFW(p0 E) fed into the next pass
+    sc_ff: int = 0             # width of that feed-forward block (0: d_model)
+    sc_sigma: float = 0.02
+
+    @property
+    def sc_width(self) -> int:
+        return self.sc_ff if self.sc_ff > 0 else self.d_model
 
     @property
     def max_ctx(self) -> int:
@@ -226,7 +236,8 @@ def tensor_shape(w: Workload, kind: str) -> tuple:
                               w.n_experts, w.d_ff, w.vocab)
     return {"embed": (V, d), "wq": (d, hq * D), "wk": (d, hkv * D), "wv": (d, hkv * D),
             "wo": (hq * D, d), "wr": (d, E), "wg": (E, d, F), "wu": (E, d, F),
-            "wd": (E, F, d)}[kind]
+            "wd": (E, F, d), "sc_wg": (d, w.sc_width), "sc_wu": (d, w.sc_width),
+            "sc_wd": (w.sc_width, d)}[kind]
 
 
 def is_expert(kind: str) -> bool:
@@ -248,6 +259,8 @@ def model_tensor(w: Workload, kind: str, layer: int = 0, expert: int | None = No
             one expert at a time (``expert`` required)
     """
     shape = tensor_shape(w, kind)
+    if kind in TID_SC:
+        return normal(w.seed, TID_SC[kind], shape, w.sc_sigma, storage_dtype(w, kind))
     tid = TID_EMBED if kind == "embed" else layer_tid(kind, layer)
     dt = storage_dtype(w, kind)
     start = 0

@@ -36,8 +36,10 @@ softmax-renormalised gates, and the lock / redraw schedule):
     1/sqrt(D); decoder attention unmasked, encoder attention causal;
   * router: softmax over all experts, top-k (ties to the lower expert id),
     gates renormalised over the k chosen;
-  * self-conditioning input z_t is zero (the training recipe feeds a zero
-    state half of the time, [TR] Dataset, "How the data is used");
+  * self-conditioning input z_t: zero unless the workload enables the
+    self-conditioning block; then z = FFW(p0 E) of the previous pass is added
+    to the canvas embedding and the first pass of a block takes z = 0 (see
+    ``self_cond`` for the readings);
   * confidence = log of the largest tempered probability, m - lse;
   * schedule: pass s locks n_s = min(ceil(C/T), #unlocked) unlocked positions
     with the highest confidence (ties to the lower position), all remaining
@@ -62,6 +64,7 @@ import numpy as np
 from .numerics import rmsnorm, rope, round_bf16, e4m3_round, softmax, silu
 from .philox import init_canvas, gumbel_uniforms
 from . import eb_sampler as eb
+from .self_cond import SelfCond, next_signal
 
 
 # =========================================================================== pieces
@@ -225,6 +228,7 @@ class StepResult:
     route_margin: list            # per layer [C]
     logits: np.ndarray | None = None
     hidden: list = field(default_factory=list)   # per layer residual after the layer
+    sc: SelfCond | None = None    # the next pass's self-conditioning signal
 
 
 class OracleModel:
@@ -370,8 +374,12 @@ class OracleModel:
         hn = self._act(rmsnorm(h, self.w.rms_eps))
         return hn @ self.W.embed().T
 
-    def decoder_logits(self, canvas, capture: StepResult | None = None):
+    def decoder_logits(self, canvas, z_in=None):
+        """Logits of the canvas; z_in [C, d] is the self-conditioning signal added to the
+        token embedding (None: zero)."""
         h = self.W.embed()[np.asarray(canvas)]
+        if z_in is not None:
+            h = h + np.asarray(z_in, np.float64)
         routes = []
         hidden = []
         for l in range(self.L):
@@ -381,12 +389,21 @@ class OracleModel:
                 hidden.append(h.copy())
         return self.head_logits(h), routes, hidden
 
+    def next_signal(self, z) -> SelfCond:
+        """Self-conditioning signal for the next pass from the tempered logits z."""
+        W = self.W
+        return next_signal(z, W.embed(), W.dense("sc_wg"), W.dense("sc_wu"), W.dense("sc_wd"),
+                           self.bf16)
+
     def denoise_step(self, canvas, mask, s: int, T: int, seed: int, keep_logits=False,
-                     row0: int = 0):
+                     row0: int = 0, z_in=None, want_signal: bool | None = None):
         """One pass over the canvas at positions n_ctx..n_ctx+C-1.  row0 offsets the rows
-        its Gumbel uniforms are drawn for (canvas b of a batch draws as rows b C ..)."""
+        its Gumbel uniforms are drawn for (canvas b of a batch draws as rows b C ..).
+        z_in: the self-conditioning signal of this pass (None: zero); with the
+        self-conditioning block the result carries the next pass's signal (.sc) unless
+        want_signal is False."""
         w = self.w
-        logits, routes, hidden = self.decoder_logits(canvas)
+        logits, routes, hidden = self.decoder_logits(canvas, z_in)
         z = logits / w.temperature
         st = lm_head_stats(z)
         C = len(canvas)
@@ -400,20 +417,26 @@ class OracleModel:
                 u = gumbel_uniforms(seed, self.k_blk, s, pos + row0, w.vocab)
                 redraw[pos], gap[pos] = gumbel_draw(z[pos], u)
         sr = sampler_update(canvas, mask, st.conf, st.argmax, redraw, s, T)
+        sc = None
+        if w.self_cond and (want_signal if want_signal is not None else True):
+            sc = self.next_signal(z)
         return StepResult(canvas=sr.canvas, mask=sr.mask, stats=st, redraw=redraw,
                           redraw_gap=gap, sampler=sr,
                           route_idx=[r[0] for r in routes], route_gates=[r[1] for r in routes],
                           route_margin=[r[2] for r in routes],
-                          logits=z if keep_logits else None, hidden=hidden)
+                          logits=z if keep_logits else None, hidden=hidden, sc=sc)
 
     def denoise_step_batch(self, canvases, masks, s: int, T: int, seed: int,
-                           keep_logits=False):
+                           keep_logits=False, z_ins=None):
         """A batch of canvases continuing the same context at the same positions: each
         canvas is a pass of its own (it attends to the context and to itself only), the
         lock schedule runs per canvas, and canvas b draws its Gumbel uniforms as rows
-        b C .. b C + C - 1 of one long canvas.  Returns one StepResult per canvas."""
+        b C .. b C + C - 1 of one long canvas.  z_ins: per canvas self-conditioning
+        signal (None: zero).  Returns one StepResult per canvas."""
         C = self.w.canvas
-        return [self.denoise_step(c, m, s, T, seed, keep_logits=keep_logits, row0=b * C)
+        zs = z_ins if z_ins is not None else [None] * len(canvases)
+        return [self.denoise_step(c, m, s, T, seed, keep_logits=keep_logits, row0=b * C,
+                                  z_in=zs[b])
                 for b, (c, m) in enumerate(zip(canvases, masks))]
 
     def init_canvas_batch(self, seed: int, B: int):
@@ -434,11 +457,12 @@ class OracleModel:
         return redraw, gap
 
     def denoise_step_eb(self, canvas, mask, prev_argmax, s: int, p, seed: int,
-                        keep_logits=False):
+                        keep_logits=False, z_in=None):
         """One pass of the entropy-bounded sampler (``eb_sampler``): logits tempered at
         tau_s, per-position entropy, Gumbel draws for unlocked positions, then the update.
+        With the self-conditioning block, p0 of the next signal is tempered at tau_s too.
         Returns (StepResult, EbResult, entropies)."""
-        logits, routes, _ = self.decoder_logits(canvas)
+        logits, routes, _ = self.decoder_logits(canvas, z_in)
         z = logits / eb.tau_at(s, p)
         st = lm_head_stats(z)
         H = eb.entropy(z)
@@ -449,7 +473,8 @@ class OracleModel:
                          redraw_gap=gap, sampler=None,
                          route_idx=[r[0] for r in routes], route_gates=[r[1] for r in routes],
                          route_margin=[r[2] for r in routes],
-                         logits=z if keep_logits else None)
+                         logits=z if keep_logits else None,
+                         sc=self.next_signal(z) if self.w.self_cond else None)
         return res, er, H
 
     def generate_block_eb(self, p, seed: int, commit: bool = True, on_step=None):
@@ -460,11 +485,13 @@ class OracleModel:
         mask = np.zeros(w.canvas, np.uint8)
         prev = None
         n = 0
+        zs = None
         for s in range(p.max_steps):
-            res, er, H = self.denoise_step_eb(canvas, mask, prev, s, p, seed)
+            res, er, H = self.denoise_step_eb(canvas, mask, prev, s, p, seed, z_in=zs)
             if on_step is not None:
                 on_step(s, canvas, mask, res, er, H)
             canvas, mask, prev = er.canvas, er.mask, res.stats.argmax
+            zs = res.sc.z if res.sc is not None else None
             n = s + 1
             if er.done:
                 break
@@ -476,11 +503,14 @@ class OracleModel:
         w = self.w
         canvas = init_canvas(seed, self.k_blk, w.canvas, w.vocab)
         mask = np.zeros(w.canvas, np.uint8)
+        zs = None
         for s in range(T):
-            res = self.denoise_step(canvas, mask, s, T, seed)
+            # the last pass's signal would feed no pass: it is not formed
+            res = self.denoise_step(canvas, mask, s, T, seed, z_in=zs, want_signal=s < T - 1)
             if on_step is not None:
                 on_step(s, canvas, mask, res)
             canvas, mask = res.canvas, res.mask
+            zs = res.sc.z if res.sc is not None else None
         if commit:
             self.commit(canvas)
         return canvas
