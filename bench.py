@@ -209,6 +209,73 @@ def summarize_pmc(path):
 BATCHES = (1, 2, 4, 8, 16)
 
 
+def self_cond_bench(dg, torch, fx, build_handle, args, plain_ms):
+    """The same model with the self-conditioning block (Fsc = d): every pass but the last of a
+    block forms z = FFW(p0 E) for the next one.  Timed like the headline passes (steps cycle
+    through blocks of T), then once more with kernel timing for the vocabulary contraction."""
+    w = fx.MOE26B_SC
+    if args.layers:
+        w = w.with_(n_layers=args.layers)
+    log(f"building {w.name}")
+    h = build_handle(dg, w, max_ctx=w.prompt_len + w.canvas)
+    try:
+        dg.dg_prefill_prompt_kv(h, torch.from_numpy(fx.prompt_ids(w)).cuda(), w.prompt_len)
+        C, T, seed = w.canvas, w.T, w.seed
+        canvas = torch.empty(C, dtype=torch.int32, device="cuda")
+        mask = torch.empty(C, dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            s = i % T
+            if s == 0:
+                dg.dg_init_canvas(h, canvas, mask, seed + i // T)
+            dg.dg_denoise_step(h, canvas, mask, s, T, seed + i // T)
+
+        for i in range(args.warmup):
+            step(i)
+        stream = torch.cuda.current_stream()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            step(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        dg.dg_profile_begin(h, args.steps * (w.n_layers * 7 + 6))
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        prof_ms, prof_n = dg.dg_profile_end(h)
+        i_sc = dg.DG_PROF_SELF_COND
+        sc_us = prof_ms[i_sc] / prof_n[i_sc] * 1e3 if prof_n[i_sc] else None
+        # algorithmic bytes of one contraction: E once, the bf16 posterior rows once
+        sc_bytes = w.vocab * w.d_model * 2 + C * w.vocab * 2
+        sc_gbs = sc_bytes / (sc_us * 1e-6) / 1e9 if sc_us else None
+        out = torch.empty(C, dtype=torch.int32, device="cuda")
+        dg.dg_generate_block(h, out, T, seed, False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dg.dg_generate_block(h, out, T, seed + 1, False)
+        torch.cuda.synchronize()
+        block_ms = (time.perf_counter() - t0) * 1e3
+        dg.dg_check_finite(h)
+        n_sig = sum(1 for i in range(args.steps) if i % T < T - 1)
+        res = {"workload": w.name, "sc_ff": w.sc_width, "ms_per_pass": round(ms, 4),
+               "canvas_tok_s": round(C / (ms / 1e3), 1),
+               "signal_us_per_forming_pass": round((ms - plain_ms) * 1e3 * args.steps / n_sig, 1),
+               "contraction_us_per_launch": round(sc_us, 2) if sc_us else None,
+               "contraction_algorithmic_bytes": sc_bytes,
+               "contraction_gbs": round(sc_gbs, 1) if sc_gbs else None,
+               "contraction_hbm_frac": round(sc_gbs / HBM_PEAK_GBS, 4) if sc_gbs else None,
+               "block_ms": round(block_ms, 2)}
+        log(f"self-conditioned: {ms:.3f} ms per pass (plain {plain_ms:.3f}); contraction "
+            f"{sc_us:.1f} us ({sc_gbs:.0f} GB/s algorithmic); block {block_ms:.1f} ms")
+        return res
+    finally:
+        dg.dg_destroy(h)
+        torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +290,8 @@ def main():
                     help="print per-kernel, per-grid durations of a rocprofv3 kernel trace")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
                     help="print per-kernel, per-grid counter means of a rocprofv3 --pmc run")
+    ap.add_argument("--no-self-cond", action="store_true",
+                    help="skip the self-conditioned model (a second handle of the same size)")
     ap.add_argument("--layers", type=int, default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.summarize_trace:
@@ -487,6 +556,9 @@ def main():
     }
     dg.dg_destroy(h)
     torch.cuda.synchronize()
+    if not args.no_self_cond:
+        result["self_conditioning"] = self_cond_bench(dg, torch, fx, build_handle, args,
+                                                      ms_per_pass)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -18,8 +18,10 @@ DG_OK, DG_EINVAL, DG_ENOMEM, DG_EHIP, DG_ECAPACITY, DG_ESTATE, DG_ENONFINITE = 0
 DG_ETOKEN = -7
 DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
 DG_T_EMBED, DG_T_WQ, DG_T_WK, DG_T_WV, DG_T_WO, DG_T_WR, DG_T_WG, DG_T_WU, DG_T_WD = range(9)
+DG_T_SC_WG, DG_T_SC_WU, DG_T_SC_WD = 9, 10, 11
 DG_CAP_LOGITS, DG_CAP_STATS, DG_CAP_ROUTING, DG_CAP_HIDDEN, DG_CAP_ATTN, DG_CAP_ROUTER_LOGITS = 1, 2, 4, 8, 16, 32
 DG_CAP_ENTROPY = 64
+DG_CAP_SELFCOND = 128
 
 EXPORTED = (
     "dg_create", "dg_destroy", "dg_last_error", "dg_load_tensor", "dg_prefill_prompt_kv",
@@ -29,9 +31,11 @@ EXPORTED = (
     "dg_set_capture", "dg_set_graphs", "dg_eb_sample", "dg_denoise_step_eb",
     "dg_generate_block_eb", "dg_attention_workspace_size", "dg_attention_noalloc",
     "dg_denoise_step_batch", "dg_init_canvas_batch", "dg_generate_block_batch",
+    "dg_set_self_cond",
 )
 DG_PROF_MOE_GEMM1, DG_PROF_MOE_GEMM2, DG_PROF_ATTENTION, DG_PROF_LM_HEAD, DG_PROF_DENSE = range(5)
-DG_PROF_N = 5
+DG_PROF_SELF_COND = 5
+DG_PROF_N = 6
 
 
 class DGError(RuntimeError):
@@ -50,6 +54,7 @@ class dg_model_cfg(ctypes.Structure):
         ("rms_eps", ctypes.c_float), ("temperature", ctypes.c_float),
         ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
         ("capture_mask", ctypes.c_uint32), ("max_batch", ctypes.c_int32),
+        ("self_cond", ctypes.c_int32), ("sc_ff", ctypes.c_int32),
     ]
 
 
@@ -97,6 +102,7 @@ def _load_library():
         "dg_denoise_step_batch": ([vp, vp, vp, i32, i32, i32, u64, vp], i32),
         "dg_init_canvas_batch": ([vp, vp, vp, i32, u64, vp], i32),
         "dg_generate_block_batch": ([vp, vp, i32, i32, u64, vp], i32),
+        "dg_set_self_cond": ([vp, vp, i32, vp], i32),
         "dg_moe_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
         "dg_init_canvas": ([vp, vp, vp, u64, vp], i32),
         "dg_profile_begin": ([vp, i32], i32),
@@ -188,6 +194,10 @@ def dg_init_canvas_batch(h, d_canvas, d_locked_mask, B: int, seed: int, stream=N
 
 def dg_generate_block_batch(h, d_out_tokens, B: int, T: int, seed: int, stream=None) -> None:
     _check(_lib.dg_generate_block_batch(h, _ptr(d_out_tokens), B, T, seed, _stream(stream)))
+
+
+def dg_set_self_cond(h, d_z, rows: int, stream=None) -> None:
+    _check(_lib.dg_set_self_cond(h, _ptr(d_z), rows, _stream(stream)))
 
 
 def dg_init_canvas(h, d_canvas, d_locked_mask, seed: int, stream=None) -> None:
@@ -314,18 +324,21 @@ def dg_profile_end(h):
 def make_cfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, n_experts, top_k, d_ff, vocab,
              canvas, max_ctx, rope_base=10000.0, rms_eps=1e-6, temperature=1.0,
              act_dtype=DG_BF16, expert_dtype=DG_BF16, capture_mask=0,
-             max_batch=1) -> dg_model_cfg:
+             max_batch=1, self_cond=0, sc_ff=0) -> dg_model_cfg:
     return dg_model_cfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, n_experts, top_k,
                         d_ff, vocab, canvas, max_ctx, rope_base, rms_eps, temperature,
-                        act_dtype, expert_dtype, capture_mask, max_batch)
+                        act_dtype, expert_dtype, capture_mask, max_batch, int(self_cond),
+                        sc_ff)
 
 
-def load_weights(h, n_layers: int, n_experts: int, tensor_fn, experts_at_once: bool = True):
+def load_weights(h, n_layers: int, n_experts: int, tensor_fn, experts_at_once: bool = True,
+                 self_cond: bool = False):
     """Load every tensor of a model.
 
     tensor_fn(kind, layer, expert) returns a numpy array in storage type, or
     (codes, scales) for e4m3 expert tensors; expert is None for dense tensors
-    and -1 for "all experts at once" ([E, in, out]).
+    and -1 for "all experts at once" ([E, in, out]).  With self_cond the three
+    DG_T_SC_* tensors are loaded too (layer 0).
     """
     def put(kind, layer, expert, val):
         if isinstance(val, tuple):
@@ -343,3 +356,6 @@ def load_weights(h, n_layers: int, n_experts: int, tensor_fn, experts_at_once: b
             else:
                 for e in range(n_experts):
                     put(kind, l, e, tensor_fn(kind, l, e))
+    if self_cond:
+        for kind in (DG_T_SC_WG, DG_T_SC_WU, DG_T_SC_WD):
+            put(kind, 0, 0, tensor_fn(kind, 0, None))

@@ -128,6 +128,22 @@ struct dg_handle {
     int32_t* blk_canvas = nullptr;
     uint8_t* blk_mask = nullptr;
 
+    // self-conditioning (cfg.self_cond): weights, the vocabulary-packed copy of E,
+    // the posterior rows of the last pass and the signal chain u -> h1 -> H -> z
+    bool sc = false;
+    int Fsc = 0;
+    void* sc_w1 = nullptr;      // bf16: packed [d][2 Fsc] gate | up columns; f32: Wg [d][Fsc]
+    void* sc_wu = nullptr;      // f32: Wu [d][Fsc]
+    void* sc_w2 = nullptr;      // bf16: packed [Fsc][d]; f32: Wd [Fsc][d]
+    void* embed_kn = nullptr;   // bf16: E packed as the B operand of a [V] x [d] product
+    void* sc_post = nullptr;    // posterior rows [rows_max][V] (bf16 or float)
+    float* sc_part = nullptr;   // stream-K partial tiles of the contraction
+    float* sc_u = nullptr;      // p0 E, float [rows_max][d]
+    void* sc_uf = nullptr;      // bf16 fragment order of u
+    float* sc_h1 = nullptr;     // [rows_max][2 Fsc] gate | up pre-activations
+    void* sc_hf = nullptr;      // gated hidden layer (bf16 fragment order, or float rows)
+    float* sc_z = nullptr;      // the signal the next pass reads, float [rows_max][d]
+
     void* stage = nullptr;
     size_t stage_bytes = 0;
 
@@ -173,11 +189,12 @@ struct dg_handle {
     void* klayer(int l) const { return (char*)kcache + (size_t)l * kv_layer_elems() * dsize(act); }
     void* vlayer(int l) const { return (char*)vcache + (size_t)l * kv_layer_elems() * dsize(act); }
 
-    // loaded flags: [L][5 dense] then [L][3][E]
+    // loaded flags: [L][5 dense] then [L][3][E], then the three self-conditioning tensors
     uint8_t& dense_flag(int l, int kind) { return loaded[1 + l * 5 + kind]; }
     uint8_t& expert_flag(int l, int which, int e) {
         return loaded[1 + L * 5 + ((size_t)l * 3 + which) * E + e];
     }
+    uint8_t& sc_flag(int which) { return loaded[1 + (size_t)L * 5 + (size_t)L * 3 * E + which]; }
 };
 
 // =========================================================================== helpers
@@ -200,6 +217,15 @@ static int validate_cfg(const dg_model_cfg* c) {
     if (c->head_dim > 128) return fail(DG_EINVAL, "head_dim must be <= 128");
     if (c->max_ctx < c->canvas) return fail(DG_EINVAL, "max_ctx must hold at least one canvas");
     if (!(c->temperature > 0.f)) return fail(DG_EINVAL, "temperature must be > 0");
+    if (c->self_cond != 0 && c->self_cond != 1) return fail(DG_EINVAL, "self_cond must be 0 or 1");
+    if (c->sc_ff < 0) return fail(DG_EINVAL, "sc_ff must be >= 0");
+    if (c->self_cond) {
+        const int fsc = c->sc_ff > 0 ? c->sc_ff : c->d_model;
+        if (c->act_dtype == DG_BF16 && fsc % 64)
+            return fail(DG_EINVAL, "bf16 self-conditioning needs sc_ff a multiple of 64");
+        if (c->act_dtype != DG_BF16 && fsc % 4)
+            return fail(DG_EINVAL, "self-conditioning needs sc_ff a multiple of 4");
+    }
     if (!(c->rope_base > 0.0)) return fail(DG_EINVAL, "rope_base must be > 0");
     if (c->act_dtype == DG_F32) {
         if (c->expert_dtype != DG_F32) return fail(DG_EINVAL, "f32 activations need f32 experts");
@@ -457,7 +483,10 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     h->kv_rows = (cfg->max_ctx + 31) & ~(int64_t)31;
     h->max_tokens = std::max(h->rows_max, kPrefillChunk);
     h->qkv_n = (h->Hq + 2 * h->Hkv) * h->D;
+    h->sc = cfg->self_cond != 0;
+    h->Fsc = h->sc ? (cfg->sc_ff > 0 ? cfg->sc_ff : cfg->d_model) : 0;
     h->loaded.assign(1 + (size_t)h->L * 5 + (size_t)h->L * 3 * h->E, 0);
+    if (h->sc) h->loaded.resize(h->loaded.size() + 3, 0);
 
     auto cleanup = [&](int r) {
         dg_destroy(h);
@@ -561,6 +590,27 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->bad, 1));
     A_TRY(h->allocT(&h->blk_canvas, h->rows_max));
     A_TRY(h->allocT(&h->blk_mask, h->rows_max));
+    if (h->sc) {
+        const size_t Fs = h->Fsc, R = h->rows_max, Rp = (R + 15) / 16 * 16;
+        if (h->act == kBF16) {
+            A_TRY(h->alloc(&h->sc_w1, d * 2 * Fs * 2));
+            A_TRY(h->alloc(&h->sc_w2, Fs * d * 2));
+            A_TRY(h->alloc(&h->embed_kn, V * d * 2));
+            A_TRY(h->alloc(&h->sc_post, R * V * 2));
+            A_TRY(h->allocT(&h->sc_part, sc_part_floats(h->rows_max, h->d, h->V)));
+            A_TRY(h->alloc(&h->sc_uf, Rp * d * 2));
+            A_TRY(h->alloc(&h->sc_hf, Rp * Fs * 2));
+        } else {
+            A_TRY(h->alloc(&h->sc_w1, d * Fs * 4));
+            A_TRY(h->alloc(&h->sc_wu, d * Fs * 4));
+            A_TRY(h->alloc(&h->sc_w2, Fs * d * 4));
+            A_TRY(h->alloc(&h->sc_post, R * V * 4));
+            A_TRY(h->alloc(&h->sc_hf, R * Fs * 4));
+        }
+        A_TRY(h->allocT(&h->sc_u, R * d));
+        A_TRY(h->allocT(&h->sc_h1, R * 2 * Fs));
+        A_TRY(h->allocT(&h->sc_z, R * d));
+    }
     A_TRY(alloc_captures(h, cfg->capture_mask));
 #undef A_TRY
     *out = h;
@@ -598,9 +648,12 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
                    const void* host_src, size_t bytes, const float* host_scales) {
     g_err.clear();
     if (!h || !host_src) return fail(DG_EINVAL, "NULL handle or source");
-    if (kind < DG_T_EMBED || kind > DG_T_WD) return fail(DG_EINVAL, "bad tensor kind %d", kind);
-    const bool is_exp = kind >= DG_T_WG;
-    if (kind != DG_T_EMBED && (layer < 0 || layer >= h->L)) return fail(DG_EINVAL, "bad layer %d", layer);
+    if (kind < DG_T_EMBED || kind > DG_T_SC_WD) return fail(DG_EINVAL, "bad tensor kind %d", kind);
+    const bool is_sc = kind >= DG_T_SC_WG;
+    if (is_sc && !h->sc) return fail(DG_EINVAL, "self-conditioning tensors need cfg.self_cond");
+    const bool is_exp = kind >= DG_T_WG && !is_sc;
+    if (kind != DG_T_EMBED && !is_sc && (layer < 0 || layer >= h->L))
+        return fail(DG_EINVAL, "bad layer %d", layer);
     HIP_TRY(hipDeviceSynchronize());
     drop_graph(h);
     if (is_exp && (expert < -1 || expert >= h->E)) return fail(DG_EINVAL, "bad expert %d", expert);
@@ -617,6 +670,8 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
         case DG_T_WR: K = h->d; N = h->E; break;
         case DG_T_WG: case DG_T_WU: K = h->d; N = h->F; break;
         case DG_T_WD: K = h->F; N = h->d; break;
+        case DG_T_SC_WG: case DG_T_SC_WU: K = h->d; N = h->Fsc; break;
+        case DG_T_SC_WD: K = h->Fsc; N = h->d; break;
     }
     const size_t per = (size_t)K * N * es;
     if (bytes != per * nexp)
@@ -628,7 +683,20 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
     if (kind == DG_T_EMBED) {
         if (dt == kF32) HIP_TRY(hipMemcpy(h->embed, src, bytes, hipMemcpyDeviceToDevice));
         else HIP_TRY(launch_pack_b16(src, false, K, N, 1, 0, h->embed, s));
+        // the self-conditioning contraction runs over the vocabulary: [V] x [d]
+        if (dt != kF32 && h->sc) HIP_TRY(launch_pack_b16(src, true, N, K, 1, 0, h->embed_kn, s));
         h->loaded[0] = 1;
+    } else if (is_sc) {
+        const int which = kind - DG_T_SC_WG;   // 0 gate, 1 up, 2 down
+        if (dt == kF32) {
+            void* dst = which == 0 ? h->sc_w1 : which == 1 ? h->sc_wu : h->sc_w2;
+            HIP_TRY(hipMemcpy(dst, src, bytes, hipMemcpyDeviceToDevice));
+        } else if (which < 2) {   // gate columns 0..Fsc-1, up columns Fsc..2Fsc-1
+            HIP_TRY(launch_pack_b16(src, true, K, N, 1, which * (h->Fsc / 16), h->sc_w1, s));
+        } else {
+            HIP_TRY(launch_pack_b16(src, true, K, N, 1, 0, h->sc_w2, s));
+        }
+        h->sc_flag(which) = 1;
     } else if (!is_exp) {
         void* dst = nullptr;
         int col0 = 0, ldn = N;
@@ -750,6 +818,17 @@ int dg_profile_end(dg_handle* h, double* total_ms, int32_t* counts) {
     return DG_OK;
 }
 
+int dg_set_self_cond(dg_handle* h, const float* d_z, int32_t rows, void* stream) {
+    g_err.clear();
+    if (!h || !d_z) return fail(DG_EINVAL, "NULL handle or signal");
+    if (!h->sc) return fail(DG_ESTATE, "self-conditioning is off");
+    if (rows < 0 || rows > h->rows_max)
+        return fail(DG_EINVAL, "rows %d outside [0, %d]", rows, h->rows_max);
+    HIP_TRY(hipMemcpyAsync(h->sc_z, d_z, (size_t)rows * h->d * 4, hipMemcpyDeviceToDevice,
+                           (hipStream_t)stream));
+    return DG_OK;
+}
+
 int dg_reset_context(dg_handle* h) {
     if (!h) return fail(DG_EINVAL, "NULL handle");
     drop_graph(h);
@@ -836,9 +915,41 @@ static int run_layers_graph(dg_handle* h, int B, hipStream_t s) {
 // statistics (with the predictive entropy when ent is set): everything of a pass
 // but the sampler.
 // B canvases of C rows each (B > 1: a batch at the same positions, see run_layer).
+// The next pass's self-conditioning signal from the posterior rows the head and its
+// statistics left in sc_post: u = p0 E (the contraction over the vocabulary), then
+// z = (silu(u Wg) * (u Wu)) Wd.
+static int run_self_cond(dg_handle* h, int rows, hipStream_t s) {
+    const int d = h->d, F = h->Fsc;
+    if (h->act == kBF16) {
+        {
+            ProfScope p(h, DG_PROF_SELF_COND, s);
+            K_TRY(launch_sc_expect((const uint16_t*)h->sc_post, rows, h->V, h->embed_kn, d,
+                                   h->sc_part, s));
+        }
+        K_TRY(launch_sc_reduce(h->sc_part, rows, d, h->V, h->sc_u, h->sc_uf, s));
+        K_TRY(launch_gemm_frag(kEpiStoreF32, h->sc_uf, rows, h->sc_w1, d, 2 * F, h->sc_h1, 2 * F, s));
+        K_TRY(launch_swiglu_rows(kBF16, h->sc_h1, rows, F, h->sc_hf, s));
+        K_TRY(launch_gemm_frag(kEpiStoreF32, h->sc_hf, rows, h->sc_w2, F, d, h->sc_z, d, s));
+    } else {
+        {
+            ProfScope p(h, DG_PROF_SELF_COND, s);
+            K_TRY(launch_gemm(kF32, kEpiStoreF32, h->sc_post, h->V, rows, h->embed, h->V, d,
+                              h->sc_u, d, s));
+        }
+        K_TRY(launch_gemm(kF32, kEpiStoreF32, h->sc_u, d, rows, h->sc_w1, d, F, h->sc_h1, 2 * F, s));
+        K_TRY(launch_gemm(kF32, kEpiStoreF32, h->sc_u, d, rows, h->sc_wu, d, F, h->sc_h1 + F,
+                          2 * F, s));
+        K_TRY(launch_swiglu_rows(kF32, h->sc_h1, rows, F, h->sc_hf, s));
+        K_TRY(launch_gemm(kF32, kEpiStoreF32, (const float*)h->sc_hf, F, rows, h->sc_w2, F, d,
+                          h->sc_z, d, s));
+    }
+    return DG_OK;
+}
+
+// sc_out: also form the self-conditioning signal of the next pass (cfg.self_cond).
 static int decode_and_head(dg_handle* h, const int32_t* d_canvas, const uint8_t* d_locked_mask,
                            int32_t step, float inv_tau, uint64_t seed, bool ent, hipStream_t s,
-                           int B = 1) {
+                           int B = 1, bool sc_out = false) {
     if (!h->prefilled) return fail(DG_ESTATE, "denoise step before prefill");
     if (h->n_ctx + (int64_t)B * h->C > h->max_ctx)
         return fail(DG_ECAPACITY, "%d canvas(es) at %lld exceed max_ctx %lld", B,
@@ -847,8 +958,11 @@ static int decode_and_head(dg_handle* h, const int32_t* d_canvas, const uint8_t*
     const int C = B * h->C;        // rows of this pass
     const int period = B > 1 ? h->C : 0;
     h->last_rows = C;
+    sc_out = sc_out && h->sc;
+    // the first pass of a block takes z = 0, later ones the previous pass's signal
     K_TRY(launch_embed_rmsnorm(h->act, h->act == kBF16, d_canvas, h->embed, h->V, C, h->d,
-                               h->cfg.rms_eps, h->x, h->a, h->Af, h->bad, s));
+                               h->cfg.rms_eps, h->x, h->a, h->Af, h->bad, s,
+                               h->sc && step > 0 ? h->sc_z : nullptr));
     const uint32_t per_layer = DG_CAP_ROUTING | DG_CAP_HIDDEN | DG_CAP_ATTN | DG_CAP_ROUTER_LOGITS;
     if (h->use_graphs && !h->prof && !(h->cap_mask & per_layer)) {
         DG_TRY(run_layers_graph(h, B, s));
@@ -866,14 +980,28 @@ static int decode_and_head(dg_handle* h, const int32_t* d_canvas, const uint8_t*
     }
     HeadPartials hp = h->hp;
     hp.q = ent ? h->hp_q : nullptr;
+    // self-conditioning: bf16 heads store exp(z - slice max) per logit, the f32 head
+    // the tempered logits; the statistics kernel turns them into p0 in place
+    const bool f32_post = sc_out && h->act == kF32;
+    float* logits_out = f32_post ? (float*)h->sc_post : h->cap(DG_CAP_LOGITS) ? h->logits_cap : nullptr;
     {
         ProfScope p(h, DG_PROF_LM_HEAD, s);
         K_TRY(launch_lm_head(h->act, h->a, h->Af, C, h->d, h->embed, h->V, inv_tau, d_locked_mask,
-                             seed, step, h->k_blk, hp,
-                             h->cap(DG_CAP_LOGITS) ? h->logits_cap : nullptr, s));
+                             seed, step, h->k_blk, hp, logits_out, s,
+                             sc_out && h->act == kBF16 ? (uint16_t*)h->sc_post : nullptr));
+    }
+    if (f32_post && h->cap(DG_CAP_LOGITS))
+        HIP_TRY(hipMemcpyAsync(h->logits_cap, h->sc_post, (size_t)C * h->V * 4,
+                               hipMemcpyDeviceToDevice, s));
+    PosteriorRows post;
+    if (sc_out) {
+        post.rows = h->sc_post;
+        post.dtype = h->act;
+        post.V = h->V;
     }
     K_TRY(launch_head_stats(hp, C, d_locked_mask, h->st_m, h->st_a, h->st_lse, h->st_conf,
-                            h->st_draw, ent ? h->st_ent : nullptr, h->bad, s));
+                            h->st_draw, ent ? h->st_ent : nullptr, h->bad, s, post));
+    if (sc_out) DG_TRY(run_self_cond(h, C, s));
     return DG_OK;
 }
 
@@ -884,7 +1012,7 @@ int dg_denoise_step(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, int
     if (T <= 0 || step < 0 || step >= T) return fail(DG_EINVAL, "need 0 <= step < T (step %d, T %d)", step, T);
     hipStream_t s = (hipStream_t)stream;
     DG_TRY(decode_and_head(h, d_canvas, d_locked_mask, step, 1.0f / h->cfg.temperature, seed,
-                           false, s));
+                           false, s, 1, step < T - 1));
     K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, h->C, 1, step,
                          T, s));
     return DG_OK;
@@ -910,7 +1038,7 @@ int dg_denoise_step_batch(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mas
     DG_TRY(check_batch(h, B));
     hipStream_t s = (hipStream_t)stream;
     DG_TRY(decode_and_head(h, d_canvas, d_locked_mask, step, 1.0f / h->cfg.temperature, seed,
-                           false, s, B));
+                           false, s, B, step < T - 1));
     K_TRY(launch_sampler(h->st_conf, h->st_a, h->st_draw, d_canvas, d_locked_mask, h->C, B, step,
                          T, s));
     return DG_OK;
@@ -960,7 +1088,7 @@ int dg_denoise_step_eb(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, 
     DG_TRY(check_eb_params(p, step));
     hipStream_t s = (hipStream_t)stream;
     DG_TRY(decode_and_head(h, d_canvas, d_locked_mask, step, (float)(1.0 / eb_tau(p, step)), seed,
-                           true, s));
+                           true, s, 1, step < p->max_steps - 1));
     K_TRY(launch_sampler_eb(h->st_ent, h->st_a, h->st_draw, h->eb_prev, d_canvas, d_locked_mask,
                             d_info ? d_info : h->eb_info, h->C, h->V, step, p->max_steps, p->gamma,
                             p->theta, seed, h->k_blk, s));
@@ -1096,6 +1224,13 @@ int dg_get_capture(dg_handle* h, uint32_t what, int32_t layer, void* d_dst, size
     if (what == DG_CAP_ENTROPY) {
         if (bytes != C * 4) return fail(DG_EINVAL, "entropy capture is %zu bytes", C * 4);
         HIP_TRY(hipMemcpyAsync(d_dst, h->st_ent, C * 4, hipMemcpyDeviceToDevice, s));
+        return DG_OK;
+    }
+    if (what == DG_CAP_SELFCOND) {
+        if (!h->sc) return fail(DG_ESTATE, "self-conditioning is off");
+        if (layer != 0 && layer != 1) return fail(DG_EINVAL, "layer 0 (u) or 1 (z)");
+        if (bytes != C * h->d * 4) return fail(DG_EINVAL, "self-conditioning capture is %zu bytes", C * h->d * 4);
+        HIP_TRY(hipMemcpyAsync(d_dst, layer == 0 ? h->sc_u : h->sc_z, bytes, hipMemcpyDeviceToDevice, s));
         return DG_OK;
     }
     if (what == DG_CAP_LOGITS) {

@@ -10,14 +10,16 @@
 // position).  With ENT it also keeps q = sum exp(z - max) (z - max), from which
 // the predictive entropy of the row is log s - q / s (the entropy-bounded
 // sampler ranks positions by it: technical-report summary, Method, sampler
-// paragraph).
+// paragraph).  When the pass forms the self-conditioning signal z = FFW(p0 E)
+// (same page, update equations) it also stores exp(z - max) of every logit in
+// bf16: the posterior rows up to one factor per (row, slice).
 #pragma once
 
 #include "kernels.h"
 
 namespace dg {
 
-constexpr int kHeadCols = 128;    // vocabulary ids of one partial slice (one weight slab)
+constexpr int kHeadCols = kHeadSlice;    // vocabulary ids of one partial slice (one weight slab)
 
 struct Run {
     float m;
@@ -70,6 +72,7 @@ struct EpiArgs {
     uint32_t key0, key1, c2;
     HeadPartials p;
     float* logits_out;
+    uint16_t* sc_w;    // bf16 [C][V] exp(z - slice max), or nullptr
 };
 
 // Epilogue of one 16-row fragment group MT of a wave's 16 x 128 tile: each lane
@@ -161,6 +164,20 @@ DG_DEV void head_epilogue(const f32x4_t (&acc)[8], const EpiArgs& e) {
             e.p.g[o] = run[j].g;
             e.p.gi[o] = run[j].gi;
             if constexpr (ENT) e.p.q[o] = run[j].q;
+        }
+    }
+    // Unnormalised posterior of every row for the self-conditioning signal: exp(z - m)
+    // with m the slice maximum the partials keep (every lane of the 16 holds it after
+    // the merge), so that p0 = exp(z - m) exp(m - lse) once lse is known.
+    if (e.sc_w != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (r4 + j >= e.C) continue;
+            const float mb = run[j].m * kLog2e;
+            uint16_t* row = e.sc_w + (size_t)(r4 + j) * e.V + e.v0 + e.l16;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                row[16 * nt] = f32_to_bf16(__builtin_amdgcn_exp2f(fmaf(acc[nt][j] * e.inv_tau, kLog2e, -mb)));
         }
     }
 }

@@ -73,6 +73,9 @@ DG_DEV size_t vt_index(int64_t h, int64_t dim, int64_t pos, int64_t D, int64_t r
     return (size_t)((h * D + dim) * rows + slot);
 }
 
+// Vocabulary ids of one partial slice of the bf16 LM head (one 128-column weight slab).
+constexpr int kHeadSlice = 128;
+
 // Per (row, vocabulary slice) partial statistics of the LM head, [C][n_slices] each.
 struct HeadPartials {
     float* m;       // max tempered logit
@@ -87,9 +90,10 @@ struct HeadPartials {
 // ---------------------------------------------------------------- misc
 // The row-normalising kernels also write the bf16 rows in fragment order to af
 // (frag_offset, K = d) when af is given (bf16 only).
+// zadd (optional, float [C][d]): the self-conditioning signal added to the embedding.
 hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, const void* E,
                                 int V, int C, int d, float eps, float* x, void* a, void* af,
-                                int32_t* bad, hipStream_t s);
+                                int32_t* bad, hipStream_t s, const float* zadd = nullptr);
 hipError_t launch_rmsnorm(int dtype, const float* x, int M, int d, float eps, void* a,
                           uint8_t* a8, void* af, hipStream_t s);
 // Token m sits at RoPE position pos0 + m (period 0) or pos0 + m % period, and in
@@ -116,9 +120,21 @@ hipError_t launch_moe_combine(int dtype, int mode, const void* Y, int M, int d, 
 hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint64_t seed,
                               int k_blk, hipStream_t s);
 // st_ent (entropy per row) is written when p.q is kept, and must be given exactly then.
+// post (optional, rows [C][V]): turned in place into the posterior p0 of each row once
+// its log-sum-exp is known: bf16 rows hold exp(z - m) of their 128-id slice (the head
+// epilogue's sc output), f32 rows the tempered logits z.
+struct PosteriorRows {
+    void* rows = nullptr;
+    int dtype = 0;     // kBF16: exp(z - slice max), kF32: z
+    int V = 0;
+};
 hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, float* st_m,
                              int32_t* st_a, float* st_lse, float* st_conf, int32_t* st_draw,
-                             float* st_ent, int32_t* bad, hipStream_t s);
+                             float* st_ent, int32_t* bad, hipStream_t s,
+                             const PosteriorRows& post = PosteriorRows{});
+// H[r][f] = silu(h1[r][f]) * h1[r][F + f] (h1 float [M][2F]); bf16: H in MFMA fragment
+// order (frag_offset, K = F, rows padded to 16); f32: H natural float [M][F].
+hipError_t launch_swiglu_rows(int dtype, const float* h1, int M, int F, void* H, hipStream_t s);
 // B canvases of C positions each, one workgroup per canvas.
 hipError_t launch_sampler(const float* conf, const int32_t* amax, const int32_t* draw,
                           int32_t* canvas, uint8_t* mask, int C, int B, int step, int T,
@@ -208,13 +224,32 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
 // z = (h E^T) / tau over the vocabulary.  Gumbel noise for rows with mask == 0.
 // bf16: hf, when given, holds the same rows in MFMA fragment order (frag_offset,
 // K = d) and the head runs on the streamed-weight pipeline of the expert GEMMs.
+// sc_w (optional, bf16 [C][V]): exp(z - m) of every logit, m the max of its 128-id
+// slice (the unnormalised posterior rows that launch_head_stats rescales).
 hipError_t launch_lm_head(int dtype, const void* h, const void* hf, int C, int d, const void* E,
                           int V, float inv_tau, const uint8_t* mask, uint64_t seed, int step,
-                          int k_blk, const HeadPartials& p, float* logits_out, hipStream_t s);
+                          int k_blk, const HeadPartials& p, float* logits_out, hipStream_t s,
+                          uint16_t* sc_w = nullptr);
 hipError_t launch_head_wide(const void* hf, int C, int d, const void* E, int V, float inv_tau,
                             const uint8_t* mask, uint32_t key0, uint32_t key1, uint32_t c2,
-                            const HeadPartials& p, float* logits_out, hipStream_t s);
+                            const HeadPartials& p, float* logits_out, hipStream_t s,
+                            uint16_t* sc_w = nullptr);
 int lm_head_slices(int dtype, int V);
+
+// ---------------------------------------------------------------- self-conditioning
+// u = P E over the vocabulary: P bf16 [M][V] (natural rows), E packed as the B
+// operand of a [K = V] x [N = d] product (launch_pack_b16 with src_kn, K = V, N = d).
+// Stream-K: the (256-row block, 128-column slab, k-step) space is cut into `grid`
+// equal ranges, one per workgroup, each spanning at most two (block, slab) units;
+// every range stores its partial tiles, and launch_sc_reduce adds them in range
+// order (deterministic).  part holds sc_part_floats(M, d, V) floats.
+int sc_grid(int M, int d, int V);
+size_t sc_part_floats(int M, int d, int V);
+hipError_t launch_sc_expect(const uint16_t* P, int M, int V, const void* Ep, int d, float* part,
+                            hipStream_t s);
+// u (float [M][d]) and uf (bf16 fragment order, K = d, rows padded to 16) from the partials.
+hipError_t launch_sc_reduce(const float* part, int M, int d, int V, float* u, void* uf,
+                            hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 // q [Hq][M][D]; K [Hkv][rows][D]; V natural [Hkv][rows][D] (f32) or

@@ -25,6 +25,7 @@
 //   * the SwiGLU of the first expert GEMM runs in the epilogue (gate and up
 //     columns are interleaved per 16-column group at pack time).
 #include <algorithm>
+#include <climits>
 
 #include "head_epilogue.h"
 
@@ -864,7 +865,7 @@ template <bool ENT>
 __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_head_wide(
     const uint8_t* Hf, int C, int d, const void* __restrict__ Ep, int V, float inv_tau,
     const uint8_t* __restrict__ mask, uint32_t key0, uint32_t key1, uint32_t c2, HeadPartials p,
-    float* __restrict__ logits_out) {
+    float* __restrict__ logits_out, uint16_t* __restrict__ sc_w) {
     __shared__ __attribute__((aligned(16))) WideRing bsm;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int KB = d >> 5;
@@ -893,7 +894,7 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_head_wide(
         if (rows) {
             static_assert(kWideMT <= 2, "head epilogue of one or two 16-row groups");
             const EpiArgs ea{C, V, c.n0, c.wr0, lane >> 4, lane & 15, inv_tau, mask, key0, key1, c2, p,
-                             logits_out};
+                             logits_out, sc_w};
             head_epilogue<0, ENT>(acc[0], ea);
             if constexpr (kWideMT > 1) head_epilogue<1, ENT>(acc[1], ea);
         }
@@ -901,6 +902,117 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_head_wide(
         u = un;
         c = head_unit(u, n_slabs, Ep, KB, w, lane);
     }
+}
+
+// Self-conditioning signal, its vocabulary-sized contraction u = P E (P the
+// posterior rows p0 = Softmax(L_t / tau) in bf16, E the token embedding; the
+// technical-report summary's update equations, the argument of FFW).  Same
+// pipeline once more: the "weights" are E packed as the B operand of a
+// [K = V] x [N = d] product (one 128-column slab of d per unit, the vocabulary
+// as the streamed k-steps), the activations the natural posterior rows read in
+// place (lane l of a row tile: 16 bytes of row l % 16 at k-chunk l / 16).
+// M is small and K huge, so the work is cut stream-K style: the k-steps of all
+// (256-row block, slab) units, unit after unit, are split into gridDim.x equal
+// ranges, one per workgroup.  A range of at most KB k-steps touches at most two
+// units; the workgroup stores one partial 256 x 128 tile per unit touched (slot
+// 2 b + segment) and k_sc_reduce adds the tiles of each unit in range order.
+DG_DEV WeightStream sc_stream(const void* Ep, int KB, int n_groups, int slab, int lo, int hi,
+                              int w, int lane) {
+    WeightStream ws;
+    const size_t gsize = (size_t)KB * 1024;                         // bytes per packed 16-column group
+    ws.g = w * kCopies / 2;
+    ws.ks0 = (w * kCopies) & 1;
+    const int gcol = slab * kWideNT + ws.g;
+    ws.rsrc = group_rsrc((const uint8_t*)Ep + (size_t)gcol * gsize,
+                         gcol < n_groups ? (uint32_t)gsize : 0u);    // groups past d read as zero
+    ws.voff = (uint32_t)lane * 16;
+    ws.kb_lo = lo;
+    ws.kb_hi = hi;
+    ws.NS = (hi - lo + 1) >> 1;
+    return ws;
+}
+
+__global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_sc_expect(
+    const uint8_t* __restrict__ P, int M, int V, const void* __restrict__ Ep, int d,
+    float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) WideRing bsm;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int KB = V >> 5;
+    const int n_slabs = (d + kWideN - 1) / kWideN;
+    const int total = ((M + kMoeRows - 1) / kMoeRows) * n_slabs * KB;
+    int x0, x1;
+    split_range(total, gridDim.x, blockIdx.x, x0, x1);
+    if (x0 >= x1) return;
+    int unit = x0 / KB;
+    WeightStream ws = sc_stream(Ep, KB, d >> 4, unit % n_slabs, x0 - unit * KB,
+                                min(KB, x1 - unit * KB), w, lane);
+    wide_fill(ws, bsm);
+    for (int seg = 0; seg < 2; ++seg) {
+        const int wr0 = (unit / n_slabs) * kMoeRows + 16 * w;      // this wave's first row
+        const bool rows = wr0 < M;                                  // uniform per wave
+        WideAcc acc;
+        if (rows) {
+            const int r = min(wr0 + (lane & 15), M - 1);
+            const uint8_t* afrag[kWideMT] = {P + ((size_t)r * V + 8 * (lane >> 4)) * 2};
+            wide_mainloop<false>(acc, afrag, ws, bsm, lane, 64u);
+        } else {
+            wide_stream_only(ws, bsm);
+        }
+        const int nx = (unit + 1) * KB;                             // the range goes on in unit + 1
+        const bool more = seg == 0 && nx < x1;
+        if (more) {
+            ws = sc_stream(Ep, KB, d >> 4, (unit + 1) % n_slabs, 0, min(KB, x1 - nx), w, lane);
+            wide_fill(ws, bsm);
+        }
+        if (rows) {
+            float* dst = part + ((size_t)(2 * blockIdx.x + seg) * kMoeRows + 16 * w +
+                                 4 * (lane >> 4)) * kWideN + (lane & 15);
+#pragma unroll
+            for (int nt = 0; nt < kWideNT; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * kWideN + 16 * nt] = acc[0][nt][i];
+        }
+        if (!more) break;
+        ++unit;
+    }
+}
+
+// u[r, c] = sum of the partial tiles of unit (r / 256, c / 128) over the ranges
+// that touch it, in range order; also u in bf16 MFMA fragment order for the
+// feed-forward block's first GEMM.  One thread per four columns.
+__global__ __launch_bounds__(256) void k_sc_reduce(const float* __restrict__ part, int M, int d,
+                                                   int V, int grid, float* __restrict__ u,
+                                                   uint8_t* __restrict__ uf) {
+    const int d4 = d >> 2;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * d4) return;
+    const int r = (int)(i / d4), c = (int)(i % d4) * 4;
+    const int KB = V >> 5;
+    const int n_slabs = (d + kWideN - 1) / kWideN;
+    const int total = ((M + kMoeRows - 1) / kMoeRows) * n_slabs * KB;
+    const int per = total / grid, rem = total % grid;
+    const int edge = rem * (per + 1);
+    auto range_of = [&](int x) { return x < edge ? x / (per + 1) : rem + (x - edge) / per; };
+    const int unit = (r / kMoeRows) * n_slabs + c / kWideN;
+    const int b0 = range_of(unit * KB), b1 = range_of(unit * KB + KB - 1);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int b = b0; b <= b1; ++b) {
+        const int start = b * per + min(b, rem);
+        const int seg = start / KB == unit ? 0 : 1;
+        const float4 v = *reinterpret_cast<const float4*>(
+            part + ((size_t)(2 * b + seg) * kMoeRows + r % kMoeRows) * kWideN + c % kWideN);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(u + (size_t)r * d + c) = acc;
+    ushort4 h;
+    h.x = f32_to_bf16(acc.x);
+    h.y = f32_to_bf16(acc.y);
+    h.z = f32_to_bf16(acc.z);
+    h.w = f32_to_bf16(acc.w);
+    *reinterpret_cast<ushort4*>(uf + frag_offset<false>(r, c, d)) = h;   // c % 8 in {0, 4}
 }
 
 // fp8 GEMM 1's activation fragments: the e4m3 token rows of every 16-row tile
@@ -1074,17 +1186,51 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
 
 hipError_t launch_head_wide(const void* hf, int C, int d, const void* E, int V, float inv_tau,
                             const uint8_t* mask, uint32_t key0, uint32_t key1, uint32_t c2,
-                            const HeadPartials& p, float* logits_out, hipStream_t s) {
+                            const HeadPartials& p, float* logits_out, hipStream_t s,
+                            uint16_t* sc_w) {
     if (C <= 0) return hipSuccess;
     if ((V % kWideN) || (d & 31)) return hipErrorInvalidValue;
     const int64_t units = (int64_t)(V / kWideN) * ((C + kMoeRows - 1) / kMoeRows);
     const unsigned grid = (unsigned)std::min<int64_t>(units, persistent_wgs());
     if (p.q)
         k_head_wide<true><<<grid, kWideThreads, 0, s>>>((const uint8_t*)hf, C, d, E, V, inv_tau, mask,
-                                                        key0, key1, c2, p, logits_out);
+                                                        key0, key1, c2, p, logits_out, sc_w);
     else
         k_head_wide<false><<<grid, kWideThreads, 0, s>>>((const uint8_t*)hf, C, d, E, V, inv_tau, mask,
-                                                         key0, key1, c2, p, logits_out);
+                                                         key0, key1, c2, p, logits_out, sc_w);
+    return hipGetLastError();
+}
+
+int sc_grid(int M, int d, int V) {
+    const int64_t n_units = (int64_t)((M + kMoeRows - 1) / kMoeRows) * ((d + kWideN - 1) / kWideN);
+    const int64_t total = n_units * (V >> 5);
+    // about one range per CU of at least 16 k-steps, and no fewer ranges than units
+    // (a range then spans at most two units)
+    const int64_t g = std::max<int64_t>(std::min<int64_t>(persistent_wgs(), total / 16), n_units);
+    return (int)g;
+}
+
+size_t sc_part_floats(int M, int d, int V) {
+    return (size_t)sc_grid(M, d, V) * 2 * kMoeRows * kWideN;
+}
+
+hipError_t launch_sc_expect(const uint16_t* P, int M, int V, const void* Ep, int d, float* part,
+                            hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if ((V & 31) || (d & 15) || (int64_t)V * 64 > 0xffffffffLL) return hipErrorInvalidValue;
+    if ((int64_t)((M + kMoeRows - 1) / kMoeRows) * ((d + kWideN - 1) / kWideN) * (V >> 5) > INT32_MAX)
+        return hipErrorInvalidValue;
+    k_sc_expect<<<sc_grid(M, d, V), kWideThreads, 0, s>>>((const uint8_t*)P, M, V, Ep, d, part);
+    return hipGetLastError();
+}
+
+hipError_t launch_sc_reduce(const float* part, int M, int d, int V, float* u, void* uf,
+                            hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if ((d & 15) || (V & 31)) return hipErrorInvalidValue;
+    const int64_t n = (int64_t)M * (d / 4);
+    k_sc_reduce<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, M, d, V, sc_grid(M, d, V), u,
+                                                           (uint8_t*)uf);
     return hipGetLastError();
 }
 

@@ -68,12 +68,14 @@ int lm_head_slices(int dtype, int V) {
 
 hipError_t launch_lm_head(int dtype, const void* h, const void* hf, int C, int d, const void* E,
                           int V, float inv_tau, const uint8_t* mask, uint64_t seed, int step,
-                          int k_blk, const HeadPartials& p, float* logits_out, hipStream_t s) {
+                          int k_blk, const HeadPartials& p, float* logits_out, hipStream_t s,
+                          uint16_t* sc_w) {
     const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
     const uint32_t c2 = (uint32_t)step | ((uint32_t)k_blk << 16);
     if (dtype != kF32 && hf != nullptr)
-        return launch_head_wide(hf, C, d, E, V, inv_tau, mask, key0, key1, c2, p, logits_out, s);
-    if (dtype != kF32) return hipErrorInvalidValue;   // bf16 rows come in fragment order
+        return launch_head_wide(hf, C, d, E, V, inv_tau, mask, key0, key1, c2, p, logits_out, s,
+                                sc_w);
+    if (dtype != kF32 || sc_w != nullptr) return hipErrorInvalidValue;   // bf16 rows come in fragment order
     dim3 grid((V + 255) / 256, C);
     auto k = p.q ? k_lm_head_f32<true> : k_lm_head_f32<false>;
     k<<<grid, 256, 0, s>>>((const float*)h, C, d, (const float*)E, V, inv_tau, mask, key0, key1,

@@ -31,7 +31,8 @@ DG_DEV float block_sum(float v, float* red) {
 }
 
 // ------------------------------------------------------------------ embed + RMSNorm
-// x[i, :] = E[canvas[i], :] (float residual), a[i, :] = rmsnorm(x[i, :]).
+// x[i, :] = E[canvas[i], :] (+ zadd[i, :], the self-conditioning signal, when given;
+// float residual), a[i, :] = rmsnorm(x[i, :]).
 // An id outside [0, V) (caller data, or the argmax of a row whose logits were
 // all NaN) reads as a zero row and sets bit kBadToken of *bad; no load leaves
 // the table.
@@ -40,7 +41,8 @@ __global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict
                                                        const T* __restrict__ E, int V, int d,
                                                        float eps, float* __restrict__ x,
                                                        T* __restrict__ a, uint8_t* __restrict__ af,
-                                                       int32_t* __restrict__ bad) {
+                                                       int32_t* __restrict__ bad,
+                                                       const float* __restrict__ zadd) {
     __shared__ float red[4];
     const int i = blockIdx.x;
     const int64_t v = tokens[i];
@@ -53,6 +55,7 @@ __global__ __launch_bounds__(256) void k_embed_rmsnorm(const int32_t* __restrict
         const int c = threadIdx.x + 256 * j;
         float e = 0.f;
         if (valid && c < d) e = PACKED ? to_f32<T>(E[packed_b_index(v, c, d)]) : to_f32<T>(E[v * d + c]);
+        if (zadd != nullptr && c < d) e += zadd[(int64_t)i * d + c];
         xs[j] = e;
         ss += e * e;
     }
@@ -321,7 +324,11 @@ DG_DEV void head_merge(HeadPart& x, const HeadPart& y) {
     if (y.g > x.g || (y.g == x.g && y.gi < x.gi)) { x.g = y.g; x.gi = y.gi; }
 }
 
-template <bool ENT>
+// PT: the posterior rows kept for the self-conditioning signal (0 none; 1 bf16
+// exp(z - m_slice) with 128-id slices, rescaled by exp(m_slice - lse); 2 float
+// tempered logits z, replaced by exp(z - lse)).  Every thread waits for the row's
+// lse and then rewrites its share of the row in place.
+template <bool ENT, int PT>
 __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm,
                                                     const int32_t* __restrict__ pa,
                                                     const float* __restrict__ ps,
@@ -335,8 +342,10 @@ __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm
                                                     float* __restrict__ st_conf,
                                                     int32_t* __restrict__ st_draw,
                                                     float* __restrict__ st_ent,
-                                                    int32_t* __restrict__ bad) {
+                                                    int32_t* __restrict__ bad,
+                                                    void* __restrict__ post, int V) {
     __shared__ HeadPart sh[4];
+    __shared__ float s_lse;
     const int row = blockIdx.x;
     HeadPart acc = {-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff, 0.f};
     for (int i = threadIdx.x; i < n_slices; i += 256) {
@@ -370,6 +379,31 @@ __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm
         st_conf[row] = -ls;
         st_draw[row] = mask[row] ? -1 : r.gi;
         if (!isfinite(r.m) || !isfinite(ls) || (!mask[row] && r.gi < 0)) atomicOr(bad, kBadNonFinite);
+        s_lse = r.m + ls;
+    }
+    if constexpr (PT != 0) {
+        __syncthreads();
+        const float lse = s_lse;
+        if constexpr (PT == 1) {
+            // 16-byte chunks of 8 ids, each inside one 128-id slice
+            uint4* rowp = reinterpret_cast<uint4*>((uint16_t*)post + (size_t)row * V);
+            const float* pmr = pm + (size_t)row * n_slices;
+            for (int c = threadIdx.x; c < (V >> 3); c += 256) {
+                const float f = __builtin_amdgcn_exp2f((pmr[c >> 4] - lse) * 1.4426950408889634f);
+                uint4 v = rowp[c];
+                uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float lo = bf16_to_f32((bf16_t)(w[k] & 0xffffu)) * f;
+                    const float hi = bf16_to_f32((bf16_t)(w[k] >> 16)) * f;
+                    w[k] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+                }
+                rowp[c] = v;
+            }
+        } else {
+            float* rowp = (float*)post + (size_t)row * V;
+            for (int v = threadIdx.x; v < V; v += 256) rowp[v] = expf(rowp[v] - lse);
+        }
     }
 }
 
@@ -652,17 +686,58 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, int64_t n) {
 
 hipError_t launch_embed_rmsnorm(int dtype, bool packed, const int32_t* tokens, const void* E,
                                 int V, int C, int d, float eps, float* x, void* a, void* af,
-                                int32_t* bad, hipStream_t s) {
+                                int32_t* bad, hipStream_t s, const float* zadd) {
     if (C == 0) return hipSuccess;
     if (dtype == kF32)
         k_embed_rmsnorm<float, false><<<C, 256, 0, s>>>(tokens, (const float*)E, V, d, eps, x,
-                                                        (float*)a, nullptr, bad);
+                                                        (float*)a, nullptr, bad, zadd);
     else if (packed)
         k_embed_rmsnorm<bf16_t, true><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, V, d, eps, x,
-                                                        (bf16_t*)a, (uint8_t*)af, bad);
+                                                        (bf16_t*)a, (uint8_t*)af, bad, zadd);
     else
         k_embed_rmsnorm<bf16_t, false><<<C, 256, 0, s>>>(tokens, (const bf16_t*)E, V, d, eps, x,
-                                                         (bf16_t*)a, (uint8_t*)af, bad);
+                                                         (bf16_t*)a, (uint8_t*)af, bad, zadd);
+    LAUNCH_CHECK();
+}
+
+// ------------------------------------------------------------------ self-conditioning FFW
+// H[r, f] = silu(h1[r, f]) * h1[r, F + f]: the gated hidden layer of the feed-forward
+// block of the self-conditioning signal (gate columns first, then up).  bf16: H in
+// MFMA fragment order (K = F) for the down projection; f32: natural rows.  One thread
+// per four columns (F % 4 == 0).
+template <bool FRAG>
+__global__ __launch_bounds__(256) void k_swiglu_rows(const float* __restrict__ h1, int M, int F,
+                                                     void* __restrict__ H) {
+    const int f4 = F >> 2;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * f4) return;
+    const int r = (int)(i / f4), c = (int)(i % f4) * 4;
+    const float4 g = *reinterpret_cast<const float4*>(h1 + (size_t)r * 2 * F + c);
+    const float4 u = *reinterpret_cast<const float4*>(h1 + (size_t)r * 2 * F + F + c);
+    float4 h;
+    h.x = g.x / (1.0f + expf(-g.x)) * u.x;
+    h.y = g.y / (1.0f + expf(-g.y)) * u.y;
+    h.z = g.z / (1.0f + expf(-g.z)) * u.z;
+    h.w = g.w / (1.0f + expf(-g.w)) * u.w;
+    if constexpr (FRAG) {
+        ushort4 b;
+        b.x = f32_to_bf16(h.x);
+        b.y = f32_to_bf16(h.y);
+        b.z = f32_to_bf16(h.z);
+        b.w = f32_to_bf16(h.w);
+        *reinterpret_cast<ushort4*>((uint8_t*)H + frag_offset<false>(r, c, F)) = b;
+    } else {
+        *reinterpret_cast<float4*>((float*)H + (size_t)r * F + c) = h;
+    }
+}
+
+hipError_t launch_swiglu_rows(int dtype, const float* h1, int M, int F, void* H, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (F & (dtype == kF32 ? 3 : 31)) return hipErrorInvalidValue;
+    const int64_t n = (int64_t)M * (F / 4);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (dtype == kF32) k_swiglu_rows<false><<<blocks, 256, 0, s>>>(h1, M, F, H);
+    else k_swiglu_rows<true><<<blocks, 256, 0, s>>>(h1, M, F, H);
     LAUNCH_CHECK();
 }
 
@@ -785,12 +860,26 @@ hipError_t launch_canvas_init(int32_t* canvas, uint8_t* mask, int C, int V, uint
 
 hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, float* st_m,
                              int32_t* st_a, float* st_lse, float* st_conf, int32_t* st_draw,
-                             float* st_ent, int32_t* bad, hipStream_t s) {
+                             float* st_ent, int32_t* bad, hipStream_t s,
+                             const PosteriorRows& post) {
     if (C <= 0) return hipSuccess;
     if ((p.q == nullptr) != (st_ent == nullptr)) return hipErrorInvalidValue;
-    auto k = p.q ? k_head_stats<true> : k_head_stats<false>;
+    int pt = 0;
+    if (post.rows != nullptr) {
+        if (post.dtype == kBF16) {
+            if (post.V % kHeadSlice || p.n_slices != post.V / kHeadSlice) return hipErrorInvalidValue;
+            pt = 1;
+        } else if (post.dtype == kF32) {
+            pt = 2;
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
+    decltype(&k_head_stats<false, 0>) k;
+    if (p.q) k = pt == 0 ? k_head_stats<true, 0> : pt == 1 ? k_head_stats<true, 1> : k_head_stats<true, 2>;
+    else k = pt == 0 ? k_head_stats<false, 0> : pt == 1 ? k_head_stats<false, 1> : k_head_stats<false, 2>;
     k<<<C, 256, 0, s>>>(p.m, p.a, p.s, p.g, p.gi, p.q, p.n_slices, mask, st_m, st_a, st_lse,
-                        st_conf, st_draw, st_ent, bad);
+                        st_conf, st_draw, st_ent, bad, post.rows, post.V);
     LAUNCH_CHECK();
 }
 

@@ -197,6 +197,18 @@ MOE26B = Workload("moe26b_30L_d2816_E128k8_V262144_P8192", n_layers=30, d_model=
                   vocab=262144, prompt_len=8192)
 MOE26B_FP8_LONG = MOE26B.with_(name="moe26b_fp8experts_P131072_K4", experts="fp8",
                                prompt_len=131072, n_canvases=4)
+# Self-conditioning.  The small configurations run at tau = 0.5 with N(0, 1) weights in the
+# signal's feed-forward block, so that the posterior is spread (largest p0 ~0.1 on average)
+# and z has the size of an embedding row: the signal then moves later logits by O(1).
+# The large one is the benched model with the block added (Fsc = d, N(0, 0.02)), one layer
+# and a short prompt, for checks of the signal's kernels at their full size.
+TINY_FP32_SC = TINY_FP32.with_(name="tiny_fp32_2L_d256_V1024_selfcond", self_cond=True,
+                               temperature=0.5, sc_sigma=1.0)
+SMALL_BF16_SC = SMALL_BF16.with_(name="small_bf16_2L_d256_E64k4_V1024_P300_selfcond",
+                                 prompt_len=300, self_cond=True, temperature=0.5, sc_sigma=1.0)
+MOE26B_SC = MOE26B.with_(name="moe26b_30L_d2816_E128k8_V262144_P8192_selfcond", self_cond=True)
+MOE26B_SC_1L = MOE26B_SC.with_(name="moe26b_1L_d2816_E128k8_V262144_P64_selfcond", n_layers=1,
+                               prompt_len=64, n_canvases=2)
 
 
 @dataclass(frozen=True)

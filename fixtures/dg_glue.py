@@ -9,7 +9,7 @@ import numpy as np
 
 from . import Workload, model_tensor, prompt_ids, tensor_shape
 
-KIND_NAMES = ("embed", "wq", "wk", "wv", "wo", "wr", "wg", "wu", "wd")
+KIND_NAMES = ("embed", "wq", "wk", "wv", "wo", "wr", "wg", "wu", "wd", "sc_wg", "sc_wu", "sc_wd")
 
 
 def make_cfg(dg, w: Workload, capture_mask: int = 0, max_ctx: int | None = None,
@@ -19,7 +19,8 @@ def make_cfg(dg, w: Workload, capture_mask: int = 0, max_ctx: int | None = None,
     return dg.make_cfg(w.n_layers, w.d_model, w.n_q_heads, w.n_kv_heads, w.head_dim,
                        w.n_experts, w.top_k, w.d_ff, w.vocab, w.canvas,
                        max_ctx if max_ctx is not None else w.max_ctx, w.rope_base, w.rms_eps,
-                       w.temperature, act, exp, capture_mask, max_batch)
+                       w.temperature, act, exp, capture_mask, max_batch, int(w.self_cond),
+                       w.sc_ff)
 
 
 def tensor_fn(w: Workload):
@@ -42,7 +43,7 @@ def build_handle(dg, w: Workload, capture_mask: int = 0, max_ctx: int | None = N
                  max_batch: int = 1):
     h = dg.dg_create(make_cfg(dg, w, capture_mask, max_ctx, max_batch))
     try:
-        dg.load_weights(h, w.n_layers, w.n_experts, tensor_fn(w))
+        dg.load_weights(h, w.n_layers, w.n_experts, tensor_fn(w), self_cond=w.self_cond)
     except Exception:
         dg.dg_destroy(h)
         raise

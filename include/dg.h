@@ -70,6 +70,9 @@ extern "C" {
  *   DG_T_WG    [d, F]        expert gate projection (one expert)
  *   DG_T_WU    [d, F]        expert up projection   (one expert)
  *   DG_T_WD    [F, d]        expert down projection (one expert)
+ *   DG_T_SC_WG [d, Fsc]      self-conditioning block, gate projection (cfg.self_cond)
+ *   DG_T_SC_WU [d, Fsc]      self-conditioning block, up projection
+ *   DG_T_SC_WD [Fsc, d]      self-conditioning block, down projection
  * Element type: act_dtype for the non-expert tensors, expert_dtype for
  * DG_T_WG / DG_T_WU / DG_T_WD.  bf16 is passed as its 16-bit pattern,
  * e4m3 as its 8-bit code plus one float scale per output column. */
@@ -82,6 +85,9 @@ extern "C" {
 #define DG_T_WG 6
 #define DG_T_WU 7
 #define DG_T_WD 8
+#define DG_T_SC_WG 9
+#define DG_T_SC_WU 10
+#define DG_T_SC_WD 11
 
 /* ---------------------------------------------------------------- captures
  * Debug captures of the last dg_denoise_step, enabled per handle by
@@ -107,6 +113,10 @@ extern "C" {
 #define DG_CAP_ATTN 16u
 #define DG_CAP_ROUTER_LOGITS 32u
 #define DG_CAP_ENTROPY 64u
+/* DG_CAP_SELFCOND (cfg.self_cond; always kept, no capture bit needed): float
+ * [C, d] of the last pass that formed the self-conditioning signal, layer 0
+ * selecting u = p0 E and layer 1 the signal z = FFW(u) the next pass reads. */
+#define DG_CAP_SELFCOND 128u
 
 typedef struct dg_model_cfg {
     int32_t n_layers;      /* L */
@@ -128,6 +138,9 @@ typedef struct dg_model_cfg {
     uint32_t capture_mask; /* DG_CAP_* bits */
     int32_t max_batch;     /* canvases one batched pass holds (dg_denoise_step_batch); 0 or 1:
                               single canvases only.  max_batch * canvas <= 65536 */
+    int32_t self_cond;     /* 1: self-conditioning (see "self-conditioning" below), 0: off */
+    int32_t sc_ff;         /* Fsc, hidden width of its feed-forward block (0: d_model);
+                              multiple of 64 (bf16) or of 4 (f32) */
 } dg_model_cfg;
 
 typedef struct dg_handle dg_handle;
@@ -278,6 +291,29 @@ int dg_denoise_step_eb(dg_handle* h, int32_t* d_canvas, uint8_t* d_locked_mask, 
 int dg_generate_block_eb(dg_handle* h, int32_t* d_out_tokens, const dg_eb_params* p,
                          uint64_t seed, int32_t commit, int32_t* n_steps, void* stream);
 
+/* ---------------------------------------------------------------- self-conditioning
+ * The decoder's continuous input z_t that feeds its previous predictions back
+ * (technical-report summary, Method: decoder equation L_t = Decoder(x_t, z_t, H)
+ * and the update equations p0 = Softmax(L_t / tau_t), z = FFW(p0 E); Dataset,
+ * "How the data is used": a zero state in half of the training examples).
+ * With cfg.self_cond = 1 (and the DG_T_SC_* tensors loaded):
+ *   - z is added to the canvas token embedding before the first layer;
+ *   - a pass with step 0 takes z = 0; a pass with step > 0 reads the z the
+ *     handle holds (that of the previous pass, or dg_set_self_cond);
+ *   - every pass but the last of its block (step < T-1, entropy-bounded:
+ *     step < max_steps-1) forms the next signal from its own logits:
+ *     p0 = Softmax(L / tau) at the pass's temperature, u = p0 E over the whole
+ *     vocabulary, z = (silu(u Wg) * (u Wu)) Wd with the DG_T_SC_* weights.
+ * So the passes of one block (or batch) run in order on one handle.  bf16:
+ * p0, u and the hidden layer are stored in bf16, z in float; the contraction
+ * reads a second copy of E packed over the vocabulary (V d bf16 more device
+ * memory).  The signal rows of a batch are [B][C][d]. */
+
+/* Overwrite the signal the next pass with step > 0 reads: d_z device float
+ * [rows, d], rows <= max_batch * canvas (rows of canvas b at b*C).
+ * DG_ESTATE without cfg.self_cond.  Asynchronous. */
+int dg_set_self_cond(dg_handle* h, const float* d_z, int32_t rows, void* stream);
+
 /* Stage 3 alone: append the causal-encoder K/V of a finished canvas
  * (device int32 [C]) at rows n_ctx..n_ctx+C-1; n_ctx += C, k_blk += 1. */
 int dg_commit_canvas(dg_handle* h, const int32_t* d_canvas, void* stream);
@@ -340,7 +376,8 @@ int dg_set_kv(dg_handle* h, int32_t layer, int32_t which, int64_t row0, int64_t 
 #define DG_PROF_ATTENTION 2   /* attention incl. split combine */
 #define DG_PROF_LM_HEAD 3     /* LM head with the streaming epilogue */
 #define DG_PROF_DENSE 4       /* QKV, output and router projections */
-#define DG_PROF_N 5
+#define DG_PROF_SELF_COND 5   /* self-conditioning: the p0 E contraction over the vocabulary */
+#define DG_PROF_N 6
 int dg_profile_begin(dg_handle* h, int32_t max_launches);
 int dg_profile_end(dg_handle* h, double* total_ms, int32_t* counts);
 

@@ -48,6 +48,9 @@ def _cfg(dg, **kw):
     dict(temperature=0.0), dict(act_dtype=7), dict(act_dtype=1, expert_dtype=0),
     dict(act_dtype=1, expert_dtype=1, head_dim=64), dict(n_experts=300, top_k=2),
     dict(max_batch=-1), dict(max_batch=257),
+    dict(self_cond=2), dict(self_cond=1, sc_ff=-4), dict(self_cond=1, sc_ff=6),
+    dict(act_dtype=1, expert_dtype=1, head_dim=128, d_model=256, d_ff=512, self_cond=1,
+         sc_ff=96),
 ])
 def test_create_rejects_bad_configs(dg, bad):
     with pytest.raises(dg.DGError) as ei:
@@ -58,6 +61,7 @@ def test_create_rejects_bad_configs(dg, bad):
 
 def test_null_arguments_are_rejected(dg):
     lib = dg._lib
+    assert lib.dg_set_self_cond(None, None, 0, None) == dg.DG_EINVAL
     assert lib.dg_denoise_step(None, None, None, 0, 12, 0, None) == dg.DG_EINVAL
     assert lib.dg_generate_block(None, None, 12, 0, 1, None) == dg.DG_EINVAL
     assert lib.dg_prefill_prompt_kv(None, None, 0, None) == dg.DG_EINVAL
