@@ -15,7 +15,11 @@ pass).  Also reported: output tokens per second of whole 256-token blocks
 (12 passes, with and without the commit), per-kernel-class times from HIP
 events recorded on the stream inside the timed region, the roofline of the
 dominant kernel (the expert gate/up GEMM), and the CPU oracle timed on a
-bounded sample of the same pass.
+bounded sample of the same pass.  Further lines in the same JSON object: the
+entropy-bounded sampler, batches of 1-16 canvases, the same model with the
+self-conditioning block, the attention entry point alone (4096 + 256 keys),
+one MoE layer alone (256 tokens, all 128 experts), and the long-context fp8
+model (prompt 131072, four canvases with commits), each with its roofline.
 """
 from __future__ import annotations
 
@@ -117,7 +121,7 @@ def cpu_baseline(w, seconds_budget=30.0):
     t_pass = w.n_layers * t_layer + t_head
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(w.canvas / t_pass, 3), "unit": "canvas tok/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "extrapolated": True,
             "sample": (f"decoder layer 0 of one pass ({t_layer:.2f} s, 256 canvas queries over "
                        f"{m.n_ctx + w.canvas} keys + MoE) and the LM head + sampler "
                        f"({t_head:.2f} s); pass = {w.n_layers} x layer + head = {t_pass:.1f} s")}
@@ -188,25 +192,219 @@ def summarize_trace(path):
               f"{max(v):9.2f} {100 * sum(v) / total:6.2f}")
 
 
+SIMDS = 1024        # 256 CUs x 4 SIMDs
+XCDS = 8            # accelerator complex dies, one GRBM each
+
+
 def summarize_pmc(path):
     """Per (kernel, grid, phase, counter) dispatch count and mean value of a rocprofv3
-    --pmc CSV."""
+    --pmc CSV (each dispatch's value summed over the counter's instances).  When both
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE were collected it also prints the MFMA
+    utilisation of every kernel, rocprofv3's MfmaUtil: busy cycles summed over all SIMDs
+    over (active cycles x SIMDs), the active cycles being the largest GRBM_GUI_ACTIVE
+    instance (one per XCD).  rocprofv3 writes GRBM_GUI_ACTIVE as one value summed over
+    the 8 XCDs, which is then divided by 8 (each XCD counts the same active time; the
+    quotient matches the traced durations at the shader clock within a few per cent)."""
     import csv
     with open(path) as f:
         rows = list(csv.DictReader(f))
-    groups = {}
+    groups, peak = {}, {}
     for row, ph in zip(rows, _phase_of(rows)):
         key = (row["Kernel_Name"].split("(")[0][:60], _grid_key(row), ph, row["Counter_Name"])
+        v = float(row["Counter_Value"])
         groups.setdefault(key, {}).setdefault(row["Dispatch_Id"], 0.0)
-        groups[key][row["Dispatch_Id"]] += float(row["Counter_Value"])
+        groups[key][row["Dispatch_Id"]] += v
+        peak.setdefault(key, {}).setdefault(row["Dispatch_Id"], []).append(v)
     print(f"{'kernel':60s} {'grid':>18s} {'phase':>8s} {'counter':>12s} {'dispatches':>10s} {'mean':>14s}")
     for (name, grid, ph, ctr), d in sorted(groups.items()):
         vals = list(d.values())
         print(f"{name:60s} {grid:>18s} {ph:>8s} {ctr:>12s} {len(vals):10d} {sum(vals) / len(vals):14.1f}")
+    util = []
+    for (name, grid, ph, ctr), d in groups.items():
+        if ctr != "SQ_VALU_MFMA_BUSY_CYCLES":
+            continue
+        gk = (name, grid, ph, "GRBM_GUI_ACTIVE")
+        if gk not in groups:
+            continue
+        busy = sum(d.values())
+        active = sum(max(vs) if len(vs) > 1 else vs[0] / XCDS for vs in peak[gk].values())
+        if busy > 0 and active > 0:
+            util.append((name, grid, ph, len(d), busy / (active * SIMDS)))
+    if util:
+        print(f"\n{'kernel':60s} {'grid':>18s} {'phase':>8s} {'dispatches':>10s} {'mfma_util_pct':>14s}")
+        for name, grid, ph, n, u in sorted(util, key=lambda t: -t[4]):
+            print(f"{name:60s} {grid:>18s} {ph:>8s} {n:10d} {100 * u:14.2f}")
 
 
 # canvases per batched pass measured beside the single-canvas pass
 BATCHES = (1, 2, 4, 8, 16)
+
+
+def ATTN_LONG(fx):
+    """The attention shape of the long-context model: 131072 prompt + 256 canvas keys."""
+    return fx.ATTN.__class__(name="attn_gqa16x8_D128_S131072p256_bf16", prompt_len=131072)
+
+
+def _timed(torch, fn, n):
+    """Mean milliseconds of n calls of fn on the current stream (HIP events)."""
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def attention_bench(dg, torch, fx, a=None):
+    """The attention entry point alone: 16 query / 8 KV heads of dim 128, 256 canvas queries
+    over the prompt's + 256 canvas keys (4096 + 256 by default), bidirectional, bf16, N(0, 1)
+    inputs."""
+    import numpy as np
+    a = a or fx.ATTN
+    q, k, v = fx.attn_inputs(a)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o = torch.empty(a.canvas, a.n_q_heads * a.head_dim, dtype=torch.bfloat16, device="cuda")
+    S = a.seq
+    ws = dg.dg_attention_workspace_size(a.n_q_heads, a.n_kv_heads, a.canvas, S, a.head_dim, False,
+                                        0, dg.DG_BF16)
+    wsd = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / np.sqrt(a.head_dim)
+    n = 50 if S <= 16384 else 10
+    ms = _timed(torch, lambda: dg.dg_attention(qd, kd, vd, o, a.n_q_heads, a.n_kv_heads, a.canvas, S,
+                                               a.head_dim, scale, False, 0, dg.DG_BF16, wsd), n)
+    flops = 4 * a.canvas * S * a.head_dim * a.n_q_heads
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"attention {a.name}: {ms * 1e3:.1f} us per call, {tf:.0f} TFLOP/s")
+    return {"workload": a.name, "us_per_call": round(ms * 1e3, 2), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)},
+            "note": "includes the per-call transposed pack of V into the caller's workspace"}
+
+
+def moe_layer_bench(dg, torch, fx):
+    """One MoE layer alone: 256 tokens of N(0, 1) hidden states, d = 2816, 128 experts top-8,
+    SwiGLU width 704, bf16, router and experts N(0, 0.02)."""
+    import numpy as np
+    m = fx.MOE_LAYER
+    x, wr, wg, wu, wd = fx.moe_inputs(m)
+    cfg = dg.make_cfg(1, m.d_model, 16, 8, 128, m.n_experts, m.top_k, m.d_ff, 128, 256, 256,
+                      act_dtype=dg.DG_BF16, expert_dtype=dg.DG_BF16)
+    h = dg.dg_create(cfg)
+    try:
+        dg.dg_load_tensor(h, dg.DG_T_WR, 0, 0, wr)
+        for kind, t in ((dg.DG_T_WG, wg), (dg.DG_T_WU, wu), (dg.DG_T_WD, wd)):
+            dg.dg_load_tensor(h, kind, 0, -1, np.ascontiguousarray(t))
+        xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        y = torch.empty_like(xd)
+        idx = torch.empty(m.tokens, m.top_k, dtype=torch.int32, device="cuda")
+        dg.dg_moe_layer(h, 0, xd, m.tokens, y, idx)
+        torch.cuda.synchronize()
+        cnt = np.bincount(idx.cpu().numpy().ravel(), minlength=m.n_experts)
+        hit = int((cnt > 0).sum())
+        ms = _timed(torch, lambda: dg.dg_moe_layer(h, 0, xd, m.tokens, y), 50)
+    finally:
+        dg.dg_destroy(h)
+    nbytes = hit * 3 * m.d_model * m.d_ff * 2 + m.d_model * m.n_experts * 2 + 2 * m.tokens * m.d_model * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    flops = 2 * m.tokens * m.top_k * 3 * m.d_model * m.d_ff
+    log(f"MoE layer {m.name}: {ms * 1e3:.1f} us per call, {hit} experts hit (largest load "
+        f"{int(cnt.max())}), {gbs:.0f} GB/s algorithmic")
+    return {"workload": m.name, "us_per_call": round(ms * 1e3, 2), "experts_hit": hit,
+            "largest_expert_load": int(cnt.max()), "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+
+
+def long_context_bench(dg, torch, fx, build_handle, args):
+    """The long-context variant: fp8 (e4m3) experts with per-column scales, a prompt of 131072
+    uniform-random ids prefilled by the causal encoder, and four canvases of 256 generated one
+    after another, each committed before the next (later canvases attend to the prompt and to
+    every committed canvas).  Timed: the prefill, every pass (HIP events per pass) and every
+    commit."""
+    import numpy as np
+    w = fx.MOE26B_FP8_LONG
+    if args.layers:
+        w = w.with_(n_layers=args.layers)
+    log(f"building {w.name}")
+    t0 = time.time()
+    h = build_handle(dg, w)
+    log(f"weights loaded in {time.time() - t0:.1f} s; prefilling {w.prompt_len} tokens")
+    try:
+        ids = torch.from_numpy(fx.prompt_ids(w)).cuda()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dg.dg_prefill_prompt_kv(h, ids, w.prompt_len)
+        torch.cuda.synchronize()
+        prefill_ms = (time.perf_counter() - t0) * 1e3
+        log(f"prefill {prefill_ms:.0f} ms")
+        C, T, K = w.canvas, w.T, w.n_canvases
+        canvas = torch.empty(C, dtype=torch.int32, device="cuda")
+        mask = torch.empty(C, dtype=torch.uint8, device="cuda")
+        # one untimed block with kernel timing (warm-up, graph capture at this context)
+        dg.dg_profile_begin(h, T * (w.n_layers * 7 + 4))
+        dg.dg_init_canvas(h, canvas, mask, w.seed + 99)
+        for s in range(T):
+            dg.dg_denoise_step(h, canvas, mask, s, T, w.seed + 99)
+        torch.cuda.synchronize()
+        prof_ms, prof_n = dg.dg_profile_end(h)
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K * (T + 2) + 1)]
+        i = 0
+        ev[i].record(stream)
+        for kk in range(K):
+            dg.dg_init_canvas(h, canvas, mask, w.seed + kk)
+            for s in range(T):
+                dg.dg_denoise_step(h, canvas, mask, s, T, w.seed + kk)
+                i += 1
+                ev[i].record(stream)
+            dg.dg_commit_canvas(h, canvas)
+            i += 1
+            ev[i].record(stream)
+            i += 1
+            ev[i].record(stream)
+        torch.cuda.synchronize()
+        dg.dg_check_finite(h)
+    finally:
+        dg.dg_destroy(h)
+        torch.cuda.synchronize()
+    per_pass, commits, first = [], [], []
+    i = 0
+    for kk in range(K):
+        for s in range(T):
+            d = ev[i].elapsed_time(ev[i + 1])
+            (first if s == 0 else per_pass).append(d)
+            i += 1
+        commits.append(ev[i].elapsed_time(ev[i + 1]))
+        i += 2
+    total_ms = ev[0].elapsed_time(ev[i - 1])
+    ms_pass = float(np.mean(per_pass))
+    names = ["moe_gemm1", "moe_gemm2", "attention", "lm_head", "dense_gemm"]
+    cls_us = {n: round(prof_ms[j] / T * 1e3, 1) for j, n in enumerate(names)}
+    attn_us = prof_ms[2] / prof_n[2] * 1e3 if prof_n[2] else None
+    S = w.prompt_len + C
+    attn_tf = 4 * C * S * w.head_dim * w.n_q_heads / (attn_us * 1e-6) / 1e12 if attn_us else None
+    res = {"workload": w.name, "canvases": K, "passes_per_canvas": T,
+           "prefill_ms": round(prefill_ms, 1),
+           "ms_per_pass": round(ms_pass, 3), "canvas_tok_s": round(C / (ms_pass / 1e3), 1),
+           "first_pass_of_canvas_ms": [round(x, 2) for x in first],
+           "commit_ms": [round(x, 2) for x in commits],
+           "output_tok_s_with_commits": round(K * C / (total_ms / 1e3), 1),
+           "kernel_us_per_pass": cls_us,
+           "roofline": {"bound": "mfma", "kernel": "attention over the prompt's 131328 keys",
+                        "achieved": round(attn_tf, 1) if attn_tf else None,
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(attn_tf / BF16_PEAK_TFLOPS, 4) if attn_tf else None,
+                        "avg_launch_us": round(attn_us, 2) if attn_us else None},
+           }
+    log(f"long context: {ms_pass:.3f} ms per pass, {res['output_tok_s_with_commits']:.0f} output "
+        f"tok/s over {K} canvases with commits; attention {attn_us:.0f} us per layer")
+    return res
 
 
 def self_cond_bench(dg, torch, fx, build_handle, args, plain_ms):
@@ -262,13 +460,15 @@ def self_cond_bench(dg, torch, fx, build_handle, args, plain_ms):
         n_sig = sum(1 for i in range(args.steps) if i % T < T - 1)
         res = {"workload": w.name, "sc_ff": w.sc_width, "ms_per_pass": round(ms, 4),
                "canvas_tok_s": round(C / (ms / 1e3), 1),
-               "signal_us_per_forming_pass": round((ms - plain_ms) * 1e3 * args.steps / n_sig, 1),
+               "signal_us_per_forming_pass":
+                   round((ms - plain_ms) * 1e3 * args.steps / n_sig, 1) if plain_ms else None,
                "contraction_us_per_launch": round(sc_us, 2) if sc_us else None,
                "contraction_algorithmic_bytes": sc_bytes,
                "contraction_gbs": round(sc_gbs, 1) if sc_gbs else None,
                "contraction_hbm_frac": round(sc_gbs / HBM_PEAK_GBS, 4) if sc_gbs else None,
+               "contraction_traffic": measured_traffic("sc_contraction"),
                "block_ms": round(block_ms, 2)}
-        log(f"self-conditioned: {ms:.3f} ms per pass (plain {plain_ms:.3f}); contraction "
+        log(f"self-conditioned: {ms:.3f} ms per pass (plain {plain_ms or float('nan'):.3f}); contraction "
             f"{sc_us:.1f} us ({sc_gbs:.0f} GB/s algorithmic); block {block_ms:.1f} ms")
         return res
     finally:
@@ -290,8 +490,16 @@ def main():
                     help="print per-kernel, per-grid durations of a rocprofv3 kernel trace")
     ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
                     help="print per-kernel, per-grid counter means of a rocprofv3 --pmc run")
+    ap.add_argument("--no-batches", action="store_true",
+                    help="skip the batched-canvas passes (profiler runs of the single pass)")
+    ap.add_argument("--no-kernels", action="store_true",
+                    help="skip the attention and MoE-layer kernel lines")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context fp8 model (P = 131072, four canvases)")
     ap.add_argument("--no-self-cond", action="store_true",
                     help="skip the self-conditioned model (a second handle of the same size)")
+    ap.add_argument("--only", choices=("self_cond", "kernels", "attn_long", "long"),
+                    help="run one further line alone and print its JSON (for profiler runs)")
     ap.add_argument("--layers", type=int, default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.summarize_trace:
@@ -319,6 +527,18 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.only:
+        if args.only == "self_cond":
+            out = self_cond_bench(dg, torch, fx, build_handle, args, None)
+        elif args.only == "kernels":
+            out = {"attention_kernel": attention_bench(dg, torch, fx),
+                   "moe_layer": moe_layer_bench(dg, torch, fx)}
+        elif args.only == "attn_long":
+            out = attention_bench(dg, torch, fx, ATTN_LONG(fx))
+        else:
+            out = long_context_bench(dg, torch, fx, build_handle, args)
+        print(json.dumps(out), flush=True)
         return
     log(f"building {w.name} (weights from the seeded generator)")
     t0 = time.time()
@@ -461,7 +681,7 @@ def main():
 
     # batched canvases: B canvases over the same context in one pass (one graph per B)
     batched = {}
-    for B in BATCHES:
+    for B in (() if args.no_batches else BATCHES):
         bc = torch.empty(B * C, dtype=torch.int32, device="cuda")
         bm = torch.empty(B * C, dtype=torch.uint8, device="cuda")
 
@@ -559,6 +779,12 @@ def main():
     if not args.no_self_cond:
         result["self_conditioning"] = self_cond_bench(dg, torch, fx, build_handle, args,
                                                       ms_per_pass)
+    if not args.no_kernels:
+        result["attention_kernel"] = attention_bench(dg, torch, fx)
+        result["attention_kernel_long"] = attention_bench(dg, torch, fx, ATTN_LONG(fx))
+        result["moe_layer"] = moe_layer_bench(dg, torch, fx)
+    if not args.no_long:
+        result["long_context_fp8"] = long_context_bench(dg, torch, fx, build_handle, args)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)

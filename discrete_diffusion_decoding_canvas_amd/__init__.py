@@ -31,7 +31,7 @@ EXPORTED = (
     "dg_set_capture", "dg_set_graphs", "dg_eb_sample", "dg_denoise_step_eb",
     "dg_generate_block_eb", "dg_attention_workspace_size", "dg_attention_noalloc",
     "dg_denoise_step_batch", "dg_init_canvas_batch", "dg_generate_block_batch",
-    "dg_set_self_cond",
+    "dg_set_self_cond", "dg_set_state",
 )
 DG_PROF_MOE_GEMM1, DG_PROF_MOE_GEMM2, DG_PROF_ATTENTION, DG_PROF_LM_HEAD, DG_PROF_DENSE = range(5)
 DG_PROF_SELF_COND = 5
@@ -103,6 +103,7 @@ def _load_library():
         "dg_init_canvas_batch": ([vp, vp, vp, i32, u64, vp], i32),
         "dg_generate_block_batch": ([vp, vp, i32, i32, u64, vp], i32),
         "dg_set_self_cond": ([vp, vp, i32, vp], i32),
+        "dg_set_state": ([vp, i64, i32], i32),
         "dg_moe_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
         "dg_init_canvas": ([vp, vp, vp, u64, vp], i32),
         "dg_profile_begin": ([vp, i32], i32),
@@ -243,6 +244,10 @@ def dg_check_finite(h, stream=None) -> None:
 
 def dg_reset_context(h) -> None:
     _check(_lib.dg_reset_context(h))
+
+
+def dg_set_state(h, n_ctx: int, k_blk: int) -> None:
+    _check(_lib.dg_set_state(h, n_ctx, k_blk))
 
 
 def dg_get_state(h):

@@ -223,8 +223,8 @@ static int validate_cfg(const dg_model_cfg* c) {
         const int fsc = c->sc_ff > 0 ? c->sc_ff : c->d_model;
         if (c->act_dtype == DG_BF16 && fsc % 64)
             return fail(DG_EINVAL, "bf16 self-conditioning needs sc_ff a multiple of 64");
-        if (c->act_dtype != DG_BF16 && fsc % 4)
-            return fail(DG_EINVAL, "self-conditioning needs sc_ff a multiple of 4");
+        if (c->act_dtype != DG_BF16 && (fsc % 4 || c->vocab % 8))
+            return fail(DG_EINVAL, "f32 self-conditioning needs sc_ff %% 4 == 0 and vocab %% 8 == 0");
     }
     if (!(c->rope_base > 0.0)) return fail(DG_EINVAL, "rope_base must be > 0");
     if (c->act_dtype == DG_F32) {
@@ -835,6 +835,19 @@ int dg_reset_context(dg_handle* h) {
     h->n_ctx = 0;
     h->k_blk = 0;
     h->prefilled = false;
+    return DG_OK;
+}
+
+int dg_set_state(dg_handle* h, int64_t n_ctx, int32_t k_blk) {
+    g_err.clear();
+    if (!h) return fail(DG_EINVAL, "NULL handle");
+    if (n_ctx < 0 || n_ctx + h->C > h->max_ctx || k_blk < 0)
+        return fail(DG_EINVAL, "need 0 <= n_ctx, n_ctx + C <= max_ctx %lld and k_blk >= 0",
+                    (long long)h->max_ctx);
+    DG_TRY(ensure_ready(h));
+    h->n_ctx = n_ctx;
+    h->k_blk = k_blk;
+    h->prefilled = true;
     return DG_OK;
 }
 

@@ -423,7 +423,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 #endif
 constexpr int kWideNT = 8;                          // 16-column groups per slab
 constexpr int kWideN = 16 * kWideNT;                // slab width
-constexpr int kWideMT = 1;                          // 16-row MFMA tiles per wave
+#ifndef DG_WIDE_MT
+#define DG_WIDE_MT 1
+#endif
+constexpr int kWideMT = DG_WIDE_MT;                 // 16-row MFMA tiles per wave
 constexpr int kWideWaves = kMoeRows / (16 * kWideMT);
 constexpr int kWideThreads = 64 * kWideWaves;
 constexpr int kWideWavesPerEU = kWideWaves / 4;     // one workgroup per CU: the VGPR budget
@@ -948,12 +951,16 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_sc_expect(
                                 min(KB, x1 - unit * KB), w, lane);
     wide_fill(ws, bsm);
     for (int seg = 0; seg < 2; ++seg) {
-        const int wr0 = (unit / n_slabs) * kMoeRows + 16 * w;      // this wave's first row
+        const int wr0 = (unit / n_slabs) * kMoeRows + 16 * kWideMT * w;   // this wave's first row
         const bool rows = wr0 < M;                                  // uniform per wave
         WideAcc acc;
         if (rows) {
-            const int r = min(wr0 + (lane & 15), M - 1);
-            const uint8_t* afrag[kWideMT] = {P + ((size_t)r * V + 8 * (lane >> 4)) * 2};
+            const uint8_t* afrag[kWideMT];
+#pragma unroll
+            for (int mt = 0; mt < kWideMT; ++mt) {
+                const int r = min(wr0 + 16 * mt + (lane & 15), M - 1);
+                afrag[mt] = P + ((size_t)r * V + 8 * (lane >> 4)) * 2;
+            }
             wide_mainloop<false>(acc, afrag, ws, bsm, lane, 64u);
         } else {
             wide_stream_only(ws, bsm);
@@ -965,12 +972,15 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_sc_expect(
             wide_fill(ws, bsm);
         }
         if (rows) {
-            float* dst = part + ((size_t)(2 * blockIdx.x + seg) * kMoeRows + 16 * w +
-                                 4 * (lane >> 4)) * kWideN + (lane & 15);
 #pragma unroll
-            for (int nt = 0; nt < kWideNT; ++nt)
+            for (int mt = 0; mt < kWideMT; ++mt) {
+                float* dst = part + ((size_t)(2 * blockIdx.x + seg) * kMoeRows + 16 * (kWideMT * w + mt) +
+                                     4 * (lane >> 4)) * kWideN + (lane & 15);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i * kWideN + 16 * nt] = acc[0][nt][i];
+                for (int nt = 0; nt < kWideNT; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[i * kWideN + 16 * nt] = acc[mt][nt][i];
+            }
         }
         if (!more) break;
         ++unit;

@@ -324,11 +324,7 @@ DG_DEV void head_merge(HeadPart& x, const HeadPart& y) {
     if (y.g > x.g || (y.g == x.g && y.gi < x.gi)) { x.g = y.g; x.gi = y.gi; }
 }
 
-// PT: the posterior rows kept for the self-conditioning signal (0 none; 1 bf16
-// exp(z - m_slice) with 128-id slices, rescaled by exp(m_slice - lse); 2 float
-// tempered logits z, replaced by exp(z - lse)).  Every thread waits for the row's
-// lse and then rewrites its share of the row in place.
-template <bool ENT, int PT>
+template <bool ENT>
 __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm,
                                                     const int32_t* __restrict__ pa,
                                                     const float* __restrict__ ps,
@@ -342,10 +338,8 @@ __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm
                                                     float* __restrict__ st_conf,
                                                     int32_t* __restrict__ st_draw,
                                                     float* __restrict__ st_ent,
-                                                    int32_t* __restrict__ bad,
-                                                    void* __restrict__ post, int V) {
+                                                    int32_t* __restrict__ bad) {
     __shared__ HeadPart sh[4];
-    __shared__ float s_lse;
     const int row = blockIdx.x;
     HeadPart acc = {-INFINITY, 0x7fffffff, 0.f, -INFINITY, 0x7fffffff, 0.f};
     for (int i = threadIdx.x; i < n_slices; i += 256) {
@@ -379,30 +373,46 @@ __global__ __launch_bounds__(256) void k_head_stats(const float* __restrict__ pm
         st_conf[row] = -ls;
         st_draw[row] = mask[row] ? -1 : r.gi;
         if (!isfinite(r.m) || !isfinite(ls) || (!mask[row] && r.gi < 0)) atomicOr(bad, kBadNonFinite);
-        s_lse = r.m + ls;
     }
-    if constexpr (PT != 0) {
-        __syncthreads();
-        const float lse = s_lse;
-        if constexpr (PT == 1) {
-            // 16-byte chunks of 8 ids, each inside one 128-id slice
-            uint4* rowp = reinterpret_cast<uint4*>((uint16_t*)post + (size_t)row * V);
-            const float* pmr = pm + (size_t)row * n_slices;
-            for (int c = threadIdx.x; c < (V >> 3); c += 256) {
-                const float f = __builtin_amdgcn_exp2f((pmr[c >> 4] - lse) * 1.4426950408889634f);
-                uint4 v = rowp[c];
-                uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+}
+
+// Posterior rows of the self-conditioning signal, in place, once every row's lse is known:
+// bf16 rows hold exp(z - m_slice) (128-id slices, m_slice the partial max pm) and become
+// p0 = that * exp(m_slice - lse); float rows hold the tempered logits z and become
+// exp(z - lse).  One thread per 8 ids (16 bytes of bf16, two float4 of float).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_posterior_rows(void* __restrict__ post,
+                                                        const float* __restrict__ pm, int n_slices,
+                                                        const float* __restrict__ lse, int M,
+                                                        int V) {
+    const int v8 = V >> 3;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * v8) return;
+    const int row = (int)(i / v8), c = (int)(i % v8);
+    const float l = lse[row];
+    if constexpr (BF16) {
+        const float f = __builtin_amdgcn_exp2f((pm[(size_t)row * n_slices + (c >> 4)] - l) *
+                                               1.4426950408889634f);
+        uint4* p = reinterpret_cast<uint4*>(post) + i;
+        uint4 v = *p;
+        uint32_t* w = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float lo = bf16_to_f32((bf16_t)(w[k] & 0xffffu)) * f;
-                    const float hi = bf16_to_f32((bf16_t)(w[k] >> 16)) * f;
-                    w[k] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-                }
-                rowp[c] = v;
-            }
-        } else {
-            float* rowp = (float*)post + (size_t)row * V;
-            for (int v = threadIdx.x; v < V; v += 256) rowp[v] = expf(rowp[v] - lse);
+        for (int k = 0; k < 4; ++k) {
+            const float lo = bf16_to_f32((bf16_t)(w[k] & 0xffffu)) * f;
+            const float hi = bf16_to_f32((bf16_t)(w[k] >> 16)) * f;
+            w[k] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+        }
+        *p = v;
+    } else {
+        float4* p = reinterpret_cast<float4*>((float*)post + (size_t)row * V) + 2 * c;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            float4 v = p[k];
+            v.x = expf(v.x - l);
+            v.y = expf(v.y - l);
+            v.z = expf(v.z - l);
+            v.w = expf(v.w - l);
+            p[k] = v;
         }
     }
 }
@@ -864,22 +874,23 @@ hipError_t launch_head_stats(const HeadPartials& p, int C, const uint8_t* mask, 
                              const PosteriorRows& post) {
     if (C <= 0) return hipSuccess;
     if ((p.q == nullptr) != (st_ent == nullptr)) return hipErrorInvalidValue;
-    int pt = 0;
     if (post.rows != nullptr) {
-        if (post.dtype == kBF16) {
-            if (post.V % kHeadSlice || p.n_slices != post.V / kHeadSlice) return hipErrorInvalidValue;
-            pt = 1;
-        } else if (post.dtype == kF32) {
-            pt = 2;
-        } else {
+        if (post.dtype == kBF16 ? (post.V % kHeadSlice || p.n_slices != post.V / kHeadSlice)
+                                : (post.dtype != kF32 || post.V % 8))
             return hipErrorInvalidValue;
-        }
     }
-    decltype(&k_head_stats<false, 0>) k;
-    if (p.q) k = pt == 0 ? k_head_stats<true, 0> : pt == 1 ? k_head_stats<true, 1> : k_head_stats<true, 2>;
-    else k = pt == 0 ? k_head_stats<false, 0> : pt == 1 ? k_head_stats<false, 1> : k_head_stats<false, 2>;
+    auto k = p.q ? k_head_stats<true> : k_head_stats<false>;
     k<<<C, 256, 0, s>>>(p.m, p.a, p.s, p.g, p.gi, p.q, p.n_slices, mask, st_m, st_a, st_lse,
-                        st_conf, st_draw, st_ent, bad, post.rows, post.V);
+                        st_conf, st_draw, st_ent, bad);
+    if (post.rows == nullptr) LAUNCH_CHECK();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)C * (post.V / 8);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (post.dtype == kBF16)
+        k_posterior_rows<true><<<blocks, 256, 0, s>>>(post.rows, p.m, p.n_slices, st_lse, C, post.V);
+    else
+        k_posterior_rows<false><<<blocks, 256, 0, s>>>(post.rows, p.m, p.n_slices, st_lse, C, post.V);
     LAUNCH_CHECK();
 }
 

@@ -140,7 +140,7 @@ typedef struct dg_model_cfg {
                               single canvases only.  max_batch * canvas <= 65536 */
     int32_t self_cond;     /* 1: self-conditioning (see "self-conditioning" below), 0: off */
     int32_t sc_ff;         /* Fsc, hidden width of its feed-forward block (0: d_model);
-                              multiple of 64 (bf16) or of 4 (f32) */
+                              multiple of 64 (bf16) or of 4 (f32; then vocab % 8 == 0) */
 } dg_model_cfg;
 
 typedef struct dg_handle dg_handle;
@@ -331,6 +331,14 @@ int dg_reset_context(dg_handle* h);
 
 /* Current committed context length and canvas index. */
 int dg_get_state(dg_handle* h, int64_t* n_ctx, int32_t* k_blk);
+
+/* Declare the committed context: n_ctx rows of every layer's cache hold valid
+ * K/V (restored with dg_set_kv from a saved cache, or injected) and the next
+ * canvas has index k_blk.  With dg_get_state and dg_get_kv this saves and
+ * resumes a context without re-running the encoder.  0 <= n_ctx, n_ctx + C <=
+ * max_ctx, k_blk >= 0 (DG_EINVAL otherwise); afterwards the handle counts as
+ * prefilled.  Synchronous only in that it waits for nothing. */
+int dg_set_state(dg_handle* h, int64_t n_ctx, int32_t k_blk);
 
 /* Replay the decoder-layer stack of dg_denoise_step as a HIP graph (enable = 1,
  * the default) or launch its kernels one by one (0).  The graph is captured

@@ -62,6 +62,7 @@ def test_create_rejects_bad_configs(dg, bad):
 def test_null_arguments_are_rejected(dg):
     lib = dg._lib
     assert lib.dg_set_self_cond(None, None, 0, None) == dg.DG_EINVAL
+    assert lib.dg_set_state(None, 0, 0) == dg.DG_EINVAL
     assert lib.dg_denoise_step(None, None, None, 0, 12, 0, None) == dg.DG_EINVAL
     assert lib.dg_generate_block(None, None, 12, 0, 1, None) == dg.DG_EINVAL
     assert lib.dg_prefill_prompt_kv(None, None, 0, None) == dg.DG_EINVAL
