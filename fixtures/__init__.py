@@ -54,6 +54,9 @@ def _load():
         lib.fx_e4m3_encode.restype = ctypes.c_uint8
         lib.fx_bf16_encode.argtypes = [ctypes.c_float]
         lib.fx_bf16_encode.restype = ctypes.c_uint16
+        lib.fx_quant_mxfp4.argtypes = [vp, i64, i64, vp, vp]
+        lib.fx_e2m1_encode.argtypes = [ctypes.c_float]
+        lib.fx_e2m1_encode.restype = ctypes.c_uint8
         _lib = lib
     return _lib
 
@@ -99,6 +102,25 @@ def quant_e4m3_cols(w: np.ndarray):
     s = np.empty(cols, np.float32)
     _load().fx_quant_e4m3_cols(_ptr(w), rows, cols, _ptr(q), _ptr(s))
     return q, s
+
+
+def quant_mxfp4(w: np.ndarray):
+    """OCP MX FP4 storage of a [rows, cols] float32 matrix whose rows are the contraction
+    dimension (rows % 32 == 0, cols even): E2M1 codes two per byte along the columns (even
+    column in the low nibble), [rows, cols / 2] uint8, and one E8M0 scale per 32 rows of a
+    column, [rows / 32, cols] uint8 (value 2^(s - 127))."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, cols = w.shape
+    if rows % 32 or cols % 2:
+        raise ValueError("MX FP4 needs rows % 32 == 0 and an even column count")
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows // 32, cols), np.uint8)
+    _load().fx_quant_mxfp4(_ptr(w), rows, cols, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def e2m1_encode_scalar(x: float) -> int:
+    return int(_load().fx_e2m1_encode(float(x)))
 
 
 def e4m3_encode_scalar(x: float) -> int:
@@ -162,7 +184,7 @@ class Workload:
     T: int = 12
     n_canvases: int = 1
     act: str = "bf16"          # "f32" | "bf16"
-    experts: str = "bf16"      # "f32" | "bf16" | "fp8"
+    experts: str = "bf16"      # "f32" | "bf16" | "fp8" | "mxfp4"
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
     temperature: float = 1.0
@@ -207,6 +229,12 @@ TINY_FP32_SC = TINY_FP32.with_(name="tiny_fp32_2L_d256_V1024_selfcond", self_con
 SMALL_BF16_SC = SMALL_BF16.with_(name="small_bf16_2L_d256_E64k4_V1024_P300_selfcond",
                                  prompt_len=300, self_cond=True, temperature=0.5, sc_sigma=1.0)
 MOE26B_SC = MOE26B.with_(name="moe26b_30L_d2816_E128k8_V262144_P8192_selfcond", self_cond=True)
+# MX FP4 experts (OCP microscaling: E2M1 elements, an E8M0 scale per 32 along the contraction),
+# activations into the experts in e4m3.
+SMALL_BF16_MX = SMALL_BF16.with_(name="small_bf16_2L_d256_E64k4_V1024_P4296_mxfp4experts",
+                                 experts="mxfp4")
+MOE26B_MX = MOE26B.with_(name="moe26b_mxfp4experts_30L_d2816_E128k8_V262144_P8192",
+                         experts="mxfp4")
 MOE26B_SC_1L = MOE26B_SC.with_(name="moe26b_1L_d2816_E128k8_V262144_P64_selfcond", n_layers=1,
                                prompt_len=64, n_canvases=2)
 
@@ -284,6 +312,11 @@ def model_tensor(w: Workload, kind: str, layer: int = 0, expert: int | None = No
             raise ValueError("fp8 experts are produced one expert at a time")
         vals = normal(w.seed, tid, shape, w.sigma, "f32", start=start)
         return quant_e4m3_cols(vals)
+    if dt == "mxfp4":
+        if expert is None:
+            raise ValueError("MX FP4 experts are produced one expert at a time")
+        vals = normal(w.seed, tid, shape, w.sigma, "f32", start=start)
+        return quant_mxfp4(vals)
     return normal(w.seed, tid, shape, w.sigma, dt, start=start)
 
 

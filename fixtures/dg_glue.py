@@ -15,7 +15,8 @@ KIND_NAMES = ("embed", "wq", "wk", "wv", "wo", "wr", "wg", "wu", "wd", "sc_wg", 
 def make_cfg(dg, w: Workload, capture_mask: int = 0, max_ctx: int | None = None,
              max_batch: int = 1):
     act = dg.DG_F32 if w.act == "f32" else dg.DG_BF16
-    exp = {"f32": dg.DG_F32, "bf16": dg.DG_BF16, "fp8": dg.DG_FP8_E4M3}[w.experts]
+    exp = {"f32": dg.DG_F32, "bf16": dg.DG_BF16, "fp8": dg.DG_FP8_E4M3,
+           "mxfp4": getattr(dg, "DG_MXFP4", None)}[w.experts]
     return dg.make_cfg(w.n_layers, w.d_model, w.n_q_heads, w.n_kv_heads, w.head_dim,
                        w.n_experts, w.top_k, w.d_ff, w.vocab, w.canvas,
                        max_ctx if max_ctx is not None else w.max_ctx, w.rope_base, w.rms_eps,
@@ -28,7 +29,7 @@ def tensor_fn(w: Workload):
         name = KIND_NAMES[kind]
         if expert is None:
             return model_tensor(w, name, layer)
-        if expert == -1 and w.experts == "fp8":
+        if expert == -1 and w.experts in ("fp8", "mxfp4") and name in ("wg", "wu", "wd"):
             parts = [model_tensor(w, name, layer, expert=e) for e in range(w.n_experts)]
             codes = np.ascontiguousarray(np.stack([p[0] for p in parts]))
             scales = np.ascontiguousarray(np.stack([p[1] for p in parts]))

@@ -126,6 +126,63 @@ void fx_quant_e4m3_cols(const float* w, int64_t rows, int64_t cols, uint8_t* q,
         for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = fx_f32_to_e4m3(w[r * cols + c] / scales[c]);
 }
 
+/* OCP Microscaling (MX) FP4 storage of a [rows][cols] matrix whose rows are the
+ * contraction dimension: elements E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa
+ * bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one E8M0 scale 2^(s - 127) per 32
+ * consecutive rows of a column.  Per block: X = 2^(floor(log2 amax) - 2) (2 is the largest
+ * E2M1 exponent), elements rounded to the nearest E2M1 value of v / X, ties to the even
+ * mantissa, saturating at 6; an all-zero block gets s = 0.  codes: [rows][cols / 2], the
+ * even column in the low nibble; scales: [rows / 32][cols]. */
+static inline uint8_t fx_f32_to_e2m1(float x) {
+    static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    const uint8_t sign = signbit(x) ? 8 : 0;
+    const float a = fabsf(x);
+    if (!(a < 6.0f)) return (uint8_t)(7 | sign);          /* saturate (and NaN) */
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        const float dc = fabsf(a - mag[c]), db = fabsf(a - mag[best]);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;  /* ties: even mantissa */
+    }
+    return (uint8_t)(best | sign);
+}
+
+/* One block of 32 rows of column c: its scale byte, and the exponent e of X = 2^e. */
+static inline int fx_mx_block_scale(const float* w, int64_t cols, int64_t b, int64_t c, int* e_out) {
+    float amax = 0.0f;
+    for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(w[(b * 32 + r) * cols + c]));
+    if (!(amax > 0.0f)) { *e_out = 0; return 0; }
+    int ex;
+    frexpf(amax, &ex);                                  /* amax = m 2^ex, m in [0.5, 1) */
+    int e = ex - 1 - 2;
+    if (e < -126) e = -126;
+    if (e > 127) e = 127;
+    *e_out = e;
+    return e + 127;
+}
+
+void fx_quant_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* codes,
+                    uint8_t* scales) {
+    const int64_t nb = rows / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t c2 = 0; c2 < cols / 2; ++c2) {
+        for (int64_t b = 0; b < nb; ++b) {
+            int e[2], sb[2];
+            for (int h = 0; h < 2; ++h) {
+                sb[h] = fx_mx_block_scale(w, cols, b, 2 * c2 + h, &e[h]);
+                scales[b * cols + 2 * c2 + h] = (uint8_t)sb[h];
+            }
+            for (int r = 0; r < 32; ++r) {
+                const int64_t k = b * 32 + r;
+                uint8_t q[2];
+                for (int h = 0; h < 2; ++h)
+                    q[h] = sb[h] ? fx_f32_to_e2m1(ldexpf(w[k * cols + 2 * c2 + h], -e[h])) : 0;
+                codes[k * (cols / 2) + c2] = (uint8_t)(q[0] | (q[1] << 4));
+            }
+        }
+    }
+}
+
 /* Exposed for the generator's own unit tests. */
 uint8_t fx_e4m3_encode(float x) { return fx_f32_to_e4m3(x); }
 uint16_t fx_bf16_encode(float x) { return fx_f32_to_bf16(x); }
+uint8_t fx_e2m1_encode(float x) { return fx_f32_to_e2m1(x); }

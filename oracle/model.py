@@ -52,7 +52,9 @@ softmax-renormalised gates, and the lock / redraw schedule):
     output, SwiGLU output, KV cache); the residual stream, router logits,
     expert outputs and all statistics stay in full precision.  For fp8
     experts, the expert inputs (normed activation, SwiGLU output) are rounded
-    to e4m3 (saturating, no scale) and the weights are code * column scale.
+    to e4m3 (saturating, no scale) and the weights are code * column scale;
+    MX FP4 experts take the same e4m3 inputs and weights E2M1 value * E8M0
+    block scale.
 """
 from __future__ import annotations
 
@@ -245,7 +247,7 @@ class OracleModel:
         self.enc_route_margin = [np.zeros(0) for _ in range(self.L)]   # per layer, per row
         self.capture_hidden = capture_hidden
         self.bf16 = w.act == "bf16"
-        self.fp8 = w.experts == "fp8"
+        self.fp8 = w.experts in ("fp8", "mxfp4")     # e4m3 expert inputs either way
 
     # ------------------------------------------------------------ precision plan
     def _act(self, x):

@@ -66,6 +66,29 @@ def e4m3_value_of_code(codes) -> np.ndarray:
     return sign * val
 
 
+def e2m1_value_of_code(codes) -> np.ndarray:
+    """Decode OCP E2M1 (FP4) codes 0..15 to float64: bit 3 the sign, bits 2-1 the exponent
+    (bias 1), bit 0 the mantissa; exponent 0 is subnormal (0 or 0.5)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    val = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.ldexp(1.0, e - 1))
+    return sign * val
+
+
+def mxfp4_dequant(codes, scales) -> np.ndarray:
+    """Values of an OCP MX FP4 matrix [rows, cols]: codes [rows, cols / 2] (the even column
+    in the low nibble), E8M0 scales [rows / 32, cols] (2^(s - 127), one per 32 rows)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    rows, half = c.shape
+    q = np.empty((rows, 2 * half), np.int64)
+    q[:, 0::2] = c & 0xF
+    q[:, 1::2] = c >> 4
+    s = np.ldexp(1.0, np.asarray(scales, np.int64) - 127)            # [rows / 32, cols]
+    return e2m1_value_of_code(q) * np.repeat(s, 32, axis=0)
+
+
 def rmsnorm(x, eps: float = 1e-6) -> np.ndarray:
     """RMSNorm over the last axis with unit gains."""
     x = np.asarray(x, dtype=np.float64)

@@ -6,7 +6,7 @@ The weights themselves come from the seeded input generator (``fixtures``);
 this adapter only turns their storage form into exact float64 values:
 bf16 bit patterns are widened exactly, e4m3 codes decode to their value times
 the per-output-column scale (the fp8 expert storage of the long-context
-configuration).
+configuration), MX FP4 codes to their E2M1 value times their block's E8M0 scale.
 """
 from __future__ import annotations
 
@@ -14,7 +14,7 @@ import numpy as np
 
 import fixtures as fx
 
-from .numerics import e4m3_value_of_code
+from .numerics import e4m3_value_of_code, mxfp4_dequant
 
 
 def _bits_to_f64(a: np.ndarray) -> np.ndarray:
@@ -36,6 +36,8 @@ class FixtureWeights:
         if dt == "bf16":
             return _bits_to_f64(raw)
         codes, scales = raw
+        if dt == "mxfp4":
+            return mxfp4_dequant(codes, scales)
         return e4m3_value_of_code(codes) * scales.astype(np.float64)[None, :]
 
     def dense(self, kind: str, layer: int = 0) -> np.ndarray:
