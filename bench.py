@@ -18,8 +18,9 @@ dominant kernel (the expert gate/up GEMM), and the CPU oracle timed on a
 bounded sample of the same pass.  Further lines in the same JSON object: the
 entropy-bounded sampler, batches of 1-16 canvases, the same model with the
 self-conditioning block, the attention entry point alone (4096 + 256 keys),
-one MoE layer alone (256 tokens, all 128 experts), and the long-context fp8
-model (prompt 131072, four canvases with commits), each with its roofline.
+one MoE layer alone (256 tokens, all 128 experts; bf16 and MX FP4 experts), the
+same model with MX FP4 experts, and the long-context fp8 model (prompt 131072,
+four canvases with commits), each with its roofline.
 """
 from __future__ import annotations
 
@@ -286,19 +287,28 @@ def attention_bench(dg, torch, fx, a=None):
             "note": "includes the per-call transposed pack of V into the caller's workspace"}
 
 
-def moe_layer_bench(dg, torch, fx):
+def moe_layer_bench(dg, torch, fx, experts="bf16"):
     """One MoE layer alone: 256 tokens of N(0, 1) hidden states, d = 2816, 128 experts top-8,
-    SwiGLU width 704, bf16, router and experts N(0, 0.02)."""
+    SwiGLU width 704, router and experts N(0, 0.02); experts in bf16, or in MX FP4 (E2M1 codes
+    with an E8M0 scale per 32 along the contraction, quantized from the same bf16 weights)
+    with e4m3 inputs to the expert GEMMs."""
     import numpy as np
     m = fx.MOE_LAYER
     x, wr, wg, wu, wd = fx.moe_inputs(m)
+    mx = experts == "mxfp4"
     cfg = dg.make_cfg(1, m.d_model, 16, 8, 128, m.n_experts, m.top_k, m.d_ff, 128, 256, 256,
-                      act_dtype=dg.DG_BF16, expert_dtype=dg.DG_BF16)
+                      act_dtype=dg.DG_BF16, expert_dtype=dg.DG_MXFP4 if mx else dg.DG_BF16)
     h = dg.dg_create(cfg)
     try:
         dg.dg_load_tensor(h, dg.DG_T_WR, 0, 0, wr)
         for kind, t in ((dg.DG_T_WG, wg), (dg.DG_T_WU, wu), (dg.DG_T_WD, wd)):
-            dg.dg_load_tensor(h, kind, 0, -1, np.ascontiguousarray(t))
+            if mx:
+                f32 = (t.astype(np.uint32) << 16).view(np.float32)
+                parts = [fx.quant_mxfp4(f32[e]) for e in range(m.n_experts)]
+                dg.dg_load_tensor(h, kind, 0, -1, np.ascontiguousarray(np.stack([p[0] for p in parts])),
+                                  np.ascontiguousarray(np.stack([p[1] for p in parts])))
+            else:
+                dg.dg_load_tensor(h, kind, 0, -1, np.ascontiguousarray(t))
         xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
         y = torch.empty_like(xd)
         idx = torch.empty(m.tokens, m.top_k, dtype=torch.int32, device="cuda")
@@ -309,16 +319,99 @@ def moe_layer_bench(dg, torch, fx):
         ms = _timed(torch, lambda: dg.dg_moe_layer(h, 0, xd, m.tokens, y), 50)
     finally:
         dg.dg_destroy(h)
-    nbytes = hit * 3 * m.d_model * m.d_ff * 2 + m.d_model * m.n_experts * 2 + 2 * m.tokens * m.d_model * 2
+    # expert weights of every expert hit (MX: half a byte per element plus one scale byte per
+    # 32), the router once, the hidden states in and out (bf16)
+    per_weight = (0.5 + 1.0 / 32) if mx else 2
+    nbytes = int(hit * 3 * m.d_model * m.d_ff * per_weight + m.d_model * m.n_experts * 2
+                 + 2 * m.tokens * m.d_model * 2)
     gbs = nbytes / (ms * 1e-3) / 1e9
     flops = 2 * m.tokens * m.top_k * 3 * m.d_model * m.d_ff
-    log(f"MoE layer {m.name}: {ms * 1e3:.1f} us per call, {hit} experts hit (largest load "
-        f"{int(cnt.max())}), {gbs:.0f} GB/s algorithmic")
-    return {"workload": m.name, "us_per_call": round(ms * 1e3, 2), "experts_hit": hit,
+    log(f"MoE layer {m.name} ({experts} experts): {ms * 1e3:.1f} us per call, {hit} experts hit "
+        f"(largest load {int(cnt.max())}), {gbs:.0f} GB/s algorithmic")
+    return {"workload": m.name if not mx else m.name.replace("_bf16", "_mxfp4experts"),
+            "experts": experts, "us_per_call": round(ms * 1e3, 2), "experts_hit": hit,
             "largest_expert_load": int(cnt.max()), "algorithmic_bytes": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
             "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+
+
+def mxfp4_model_bench(dg, torch, fx, build_handle, args, plain_ms):
+    """The benched model with MX FP4 experts (E2M1 codes, an E8M0 scale per 32 along the
+    contraction, e4m3 inputs to the expert GEMMs on the block-scaled MFMA); everything else as
+    in the headline passes.  Timed like them, then once more with kernel timing; the roofline
+    is that of the expert gate/up GEMM at MX bytes."""
+    import numpy as np
+    w = fx.MOE26B_MX
+    if args.layers:
+        w = w.with_(n_layers=args.layers)
+    log(f"building {w.name}")
+    h = build_handle(dg, w, max_ctx=w.prompt_len + w.canvas)
+    try:
+        dg.dg_prefill_prompt_kv(h, torch.from_numpy(fx.prompt_ids(w)).cuda(), w.prompt_len)
+        C, T, seed = w.canvas, w.T, w.seed
+        canvas = torch.empty(C, dtype=torch.int32, device="cuda")
+        mask = torch.empty(C, dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            s = i % T
+            if s == 0:
+                dg.dg_init_canvas(h, canvas, mask, seed + i // T)
+            dg.dg_denoise_step(h, canvas, mask, s, T, seed + i // T)
+
+        for i in range(args.warmup):
+            step(i)
+        stream = torch.cuda.current_stream()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            step(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        dg.dg_profile_begin(h, args.steps * (w.n_layers * 7 + 4))
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        prof_ms, prof_n = dg.dg_profile_end(h)
+        dg.dg_set_capture(h, dg.DG_CAP_ROUTING)
+        dg.dg_init_canvas(h, canvas, mask, seed)
+        dg.dg_denoise_step(h, canvas, mask, 0, T, seed)
+        rbuf = torch.empty(2 * C * w.top_k, dtype=torch.int32, device="cuda")
+        active = []
+        for l in range(w.n_layers):
+            dg.dg_get_capture(h, dg.DG_CAP_ROUTING, l, rbuf)
+            torch.cuda.synchronize()
+            active.append(int((np.bincount(rbuf[:C * w.top_k].cpu().numpy(),
+                                           minlength=w.n_experts) > 0).sum()))
+        dg.dg_set_capture(h, 0)
+        dg.dg_check_finite(h)
+    finally:
+        dg.dg_destroy(h)
+        torch.cuda.synchronize()
+    names = ["moe_gemm1", "moe_gemm2", "attention", "lm_head", "dense_gemm"]
+    us = {n: prof_ms[i] / prof_n[i] * 1e3 if prof_n[i] else None for i, n in enumerate(names)}
+    hit = float(np.mean(active))
+    Fp = (w.d_ff + 127) // 128 * 128
+    # gate/up codes and scales of every expert hit, the e4m3 inputs once, H written (e4m3)
+    moe1_bytes = int(hit * w.d_model * 2 * w.d_ff * (0.5 + 1.0 / 32) + C * w.d_model
+                     + C * w.top_k * Fp)
+    moe1_gbs = moe1_bytes / (us["moe_gemm1"] * 1e-6) / 1e9
+    res = {"workload": w.name, "ms_per_pass": round(ms, 4), "canvas_tok_s": round(C / (ms / 1e3), 1),
+           "vs_bf16_experts": round(plain_ms / ms, 3) if plain_ms else None,
+           "kernel_us_per_pass": {n: round(prof_ms[i] / args.steps * 1e3, 1)
+                                  for i, n in enumerate(names)},
+           "experts_hit_per_layer": round(hit, 2),
+           "roofline": {"bound": "hbm", "kernel": "moe_gemm1 (MX FP4 expert gate/up GEMM + SwiGLU)",
+                        "achieved": round(moe1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(moe1_gbs / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes_per_launch": moe1_bytes,
+                        "avg_launch_us": round(us["moe_gemm1"], 2)}}
+    log(f"MX FP4 experts: {ms:.3f} ms per pass (bf16 experts {plain_ms or float('nan'):.3f}); "
+        f"gate/up GEMM {us['moe_gemm1']:.1f} us ({moe1_gbs:.0f} GB/s algorithmic), down GEMM "
+        f"{us['moe_gemm2']:.1f} us")
+    return res
 
 
 def long_context_bench(dg, torch, fx, build_handle, args):
@@ -498,7 +591,9 @@ def main():
                     help="skip the long-context fp8 model (P = 131072, four canvases)")
     ap.add_argument("--no-self-cond", action="store_true",
                     help="skip the self-conditioned model (a second handle of the same size)")
-    ap.add_argument("--only", choices=("self_cond", "kernels", "attn_long", "long"),
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the MX FP4 expert lines (model and MoE layer)")
+    ap.add_argument("--only", choices=("self_cond", "kernels", "attn_long", "long", "mx", "mx_layer"),
                     help="run one further line alone and print its JSON (for profiler runs)")
     ap.add_argument("--layers", type=int, default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -536,6 +631,10 @@ def main():
                    "moe_layer": moe_layer_bench(dg, torch, fx)}
         elif args.only == "attn_long":
             out = attention_bench(dg, torch, fx, ATTN_LONG(fx))
+        elif args.only == "mx":
+            out = mxfp4_model_bench(dg, torch, fx, build_handle, args, None)
+        elif args.only == "mx_layer":
+            out = moe_layer_bench(dg, torch, fx, "mxfp4")
         else:
             out = long_context_bench(dg, torch, fx, build_handle, args)
         print(json.dumps(out), flush=True)
@@ -783,6 +882,10 @@ def main():
         result["attention_kernel"] = attention_bench(dg, torch, fx)
         result["attention_kernel_long"] = attention_bench(dg, torch, fx, ATTN_LONG(fx))
         result["moe_layer"] = moe_layer_bench(dg, torch, fx)
+        if not args.no_mx:
+            result["moe_layer_mxfp4"] = moe_layer_bench(dg, torch, fx, "mxfp4")
+    if not args.no_mx:
+        result["mxfp4_experts"] = mxfp4_model_bench(dg, torch, fx, build_handle, args, ms_per_pass)
     if not args.no_long:
         result["long_context_fp8"] = long_context_bench(dg, torch, fx, build_handle, args)
     if not args.no_cpu_baseline:

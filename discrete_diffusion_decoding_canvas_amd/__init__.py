@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libdg.so")
 
 DG_OK, DG_EINVAL, DG_ENOMEM, DG_EHIP, DG_ECAPACITY, DG_ESTATE, DG_ENONFINITE = 0, -1, -2, -3, -4, -5, -6
 DG_ETOKEN = -7
-DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
+DG_F32, DG_BF16, DG_FP8_E4M3, DG_MXFP4 = 0, 1, 2, 3
 DG_T_EMBED, DG_T_WQ, DG_T_WK, DG_T_WV, DG_T_WO, DG_T_WR, DG_T_WG, DG_T_WU, DG_T_WD = range(9)
 DG_T_SC_WG, DG_T_SC_WU, DG_T_SC_WD = 9, 10, 11
 DG_CAP_LOGITS, DG_CAP_STATS, DG_CAP_ROUTING, DG_CAP_HIDDEN, DG_CAP_ATTN, DG_CAP_ROUTER_LOGITS = 1, 2, 4, 8, 16, 32
@@ -166,8 +166,8 @@ def dg_load_tensor(h, kind: int, layer: int, expert: int, host_array, scales=Non
     """host_array: C-contiguous numpy array in the tensor's storage type."""
     if not host_array.flags["C_CONTIGUOUS"]:
         raise ValueError("host_array must be C-contiguous")
-    if scales is not None and (scales.dtype.itemsize != 4 or not scales.flags["C_CONTIGUOUS"]):
-        raise ValueError("scales must be contiguous float32")
+    if scales is not None and (scales.dtype.itemsize not in (1, 4) or not scales.flags["C_CONTIGUOUS"]):
+        raise ValueError("scales must be contiguous float32 (e4m3) or uint8 (MX FP4 E8M0)")
     _check(_lib.dg_load_tensor(h, kind, layer, expert, host_array.ctypes.data,
                                host_array.nbytes, _ptr(scales)))
 

@@ -73,6 +73,7 @@ struct dg_handle {
     void* embed = nullptr;
     std::vector<void*> wqkv, wo, wr, w1, wu, w2;
     std::vector<float*> s1, s2;
+    std::vector<uint8_t*> x1, x2;  // MX FP4 experts: E8M0 block scales in stage order
     std::vector<uint8_t> loaded;   // per (layer, kind) dense flags and per expert flags
     bool ready = false;
 
@@ -231,8 +232,11 @@ static int validate_cfg(const dg_model_cfg* c) {
         if (c->expert_dtype != DG_F32) return fail(DG_EINVAL, "f32 activations need f32 experts");
         if (c->head_dim != 64 && c->head_dim != 128) return fail(DG_EINVAL, "f32 head_dim must be 64 or 128");
     } else if (c->act_dtype == DG_BF16) {
-        if (c->expert_dtype != DG_BF16 && c->expert_dtype != DG_FP8_E4M3)
-            return fail(DG_EINVAL, "bf16 activations need bf16 or e4m3 experts");
+        if (c->expert_dtype != DG_BF16 && c->expert_dtype != DG_FP8_E4M3 &&
+            c->expert_dtype != DG_MXFP4)
+            return fail(DG_EINVAL, "bf16 activations need bf16, e4m3 or MX FP4 experts");
+        if (c->expert_dtype == DG_MXFP4 && c->d_model % 128)
+            return fail(DG_EINVAL, "MX FP4 experts need d_model a multiple of 128");
         if (c->head_dim != 128) return fail(DG_EINVAL, "bf16 path needs head_dim 128");
         if (c->d_model % 64 || c->d_ff % 64) return fail(DG_EINVAL, "bf16 path needs d_model and d_ff multiples of 64");
         if (c->vocab % 128) return fail(DG_EINVAL, "bf16 path needs vocab multiple of 128");
@@ -252,6 +256,9 @@ static int ensure_ready(dg_handle* h) {
     return DG_OK;
 }
 
+// fp8 and MX FP4 experts read e4m3 copies of the normed activations.
+static bool e4m3_inputs(const dg_handle* h) { return h->edt == kFP8 || h->edt == kMX; }
+
 static ExpertWeights expert_weights(dg_handle* h, int l) {
     ExpertWeights w;
     w.w1 = h->w1[l];
@@ -259,6 +266,8 @@ static ExpertWeights expert_weights(dg_handle* h, int l) {
     w.w2 = h->w2[l];
     w.s1 = h->s1.empty() ? nullptr : h->s1[l];
     w.s2 = h->s2.empty() ? nullptr : h->s2[l];
+    w.x1 = h->x1.empty() ? nullptr : h->x1[l];
+    w.x2 = h->x2.empty() ? nullptr : h->x2[l];
     return w;
 }
 
@@ -338,11 +347,13 @@ static int run_moe(dg_handle* h, int l, int n, const void* xin, const uint8_t* x
                                 moe_pad(h), s));
     ExpertWeights w = expert_weights(h, l);
     const int rows = (int)moe_rows_cap(n, h->k, h->E, moe_pad(h));
-    const void* X1 = (h->edt == kFP8) ? (const void*)xin8 : xin;
-    // fp8 experts take their inputs gathered into fragment order; the bf16 GEMM reads
-    // the token rows in place
-    if (h->edt == kFP8)
-        K_TRY(launch_moe_gather8(X1, h->d, h->perm_token, h->offsets, h->E, rows, h->Xf, s));
+    const bool e4 = h->edt == kFP8 || h->edt == kMX;
+    const void* X1 = e4 ? (const void*)xin8 : xin;
+    // fp8 and MX FP4 experts take their e4m3 inputs gathered into fragment order; the
+    // bf16 GEMM reads the token rows in place
+    if (e4)
+        K_TRY(launch_moe_gather8(X1, h->d, h->perm_token, h->offsets, h->E, rows, h->Xf, s,
+                                 h->edt == kMX));
     {
         ProfScope p(h, DG_PROF_MOE_GEMM1, s);
         K_TRY(launch_moe_gemm1(h->edt, w, X1, h->perm_token, h->offsets, h->E, h->d, h->F, rows,
@@ -432,14 +443,14 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
         }
     }
     K_TRY(launch_rmsnorm(h->act, h->x, n, h->d, h->cfg.rms_eps, h->a,
-                         h->edt == kFP8 ? h->a8 : nullptr, nullptr, s));
+                         e4m3_inputs(h) ? h->a8 : nullptr, nullptr, s));
     DG_TRY(run_moe(h, l, n, h->a, h->a8, s));
     if (capture && h->cap(DG_CAP_ROUTER_LOGITS))
         HIP_TRY(hipMemcpyAsync(h->cap_rlog + (size_t)l * n * h->E, h->rlog, (size_t)n * h->E * 4,
                                hipMemcpyDeviceToDevice, s));
     // residual add, then the next norm (next layer's input, or the final norm)
     K_TRY(launch_moe_combine(h->act, 0, h->Y, n, h->d, h->k, h->gates, h->inv, h->x,
-                             h->cfg.rms_eps, h->a, h->edt == kFP8 ? h->a8 : nullptr, h->Af,
+                             h->cfg.rms_eps, h->a, e4m3_inputs(h) ? h->a8 : nullptr, h->Af,
                              nullptr, s));
     return DG_OK;
 }
@@ -478,7 +489,8 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     h->B_max = cfg->max_batch > 1 ? cfg->max_batch : 1;
     h->rows_max = h->C * h->B_max;
     h->act = cfg->act_dtype == DG_F32 ? kF32 : kBF16;
-    h->edt = cfg->expert_dtype == DG_F32 ? kF32 : cfg->expert_dtype == DG_BF16 ? kBF16 : kFP8;
+    h->edt = cfg->expert_dtype == DG_F32 ? kF32 : cfg->expert_dtype == DG_BF16 ? kBF16
+           : cfg->expert_dtype == DG_MXFP4 ? kMX : kFP8;
     h->max_ctx = cfg->max_ctx;
     h->kv_rows = (cfg->max_ctx + 31) & ~(int64_t)31;
     h->max_tokens = std::max(h->rows_max, kPrefillChunk);
@@ -508,10 +520,21 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
         h->s1.resize(L);
         h->s2.resize(L);
     }
+    if (h->edt == kMX) {
+        h->x1.resize(L);
+        h->x2.resize(L);
+    }
     for (size_t l = 0; l < L; ++l) {
         A_TRY(h->alloc(&h->wqkv[l], d * h->qkv_n * as));
         A_TRY(h->alloc(&h->wo[l], (size_t)h->Hq * h->D * d * as));
         A_TRY(h->alloc(&h->wr[l], d * E * as));
+        if (h->edt == kMX) {
+            A_TRY(h->alloc(&h->w1[l], E * mx_code_bytes(h->d, 2 * h->F)));
+            A_TRY(h->alloc(&h->w2[l], E * mx_code_bytes(h->F, h->d)));
+            A_TRY(h->allocT(&h->x1[l], E * mx_scale_bytes(h->d, 2 * h->F)));
+            A_TRY(h->allocT(&h->x2[l], E * mx_scale_bytes(h->F, h->d)));
+            continue;
+        }
         A_TRY(h->alloc(&h->w1[l], E * d * F * es * (h->edt == kF32 ? 1 : 2)));
         if (h->edt == kF32) A_TRY(h->alloc(&h->wu[l], E * d * F * es));
         A_TRY(h->alloc(&h->w2[l], E * F * d * es));
@@ -543,7 +566,7 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     }
     A_TRY(h->allocT(&h->x, T * d));
     A_TRY(h->alloc(&h->a, T * d * as));
-    if (h->edt == kFP8) A_TRY(h->allocT(&h->a8, T * d));
+    if (h->edt == kFP8 || h->edt == kMX) A_TRY(h->allocT(&h->a8, T * d));
     if (h->act == kF32) A_TRY(h->allocT(&h->qkv, T * h->qkv_n));   // bf16: RoPE in the QKV epilogue
     A_TRY(h->alloc(&h->q, T * h->Hq * h->D * as));
     A_TRY(h->alloc(&h->attn_o, T * h->Hq * h->D * as));
@@ -566,10 +589,11 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     A_TRY(h->allocT(&h->work_count, 4));   // item counts and the two GEMMs' unit counters
     A_TRY(h->allocT(&h->route_ticket, 1));
     if (hipMemset(h->route_ticket, 0, 4) != hipSuccess) return cleanup(fail(DG_EHIP, "ticket reset failed"));
-    if (h->edt == kFP8) A_TRY(h->alloc(&h->Xf, rows * d * esz));
+    if (h->edt == kFP8 || h->edt == kMX) A_TRY(h->alloc(&h->Xf, rows * d * esz));
     if (h->act == kBF16)
         A_TRY(h->alloc(&h->Af, (T + 15) / 16 * 16 * std::max<size_t>(d, (size_t)h->Hq * h->D) * 2));
-    A_TRY(h->alloc(&h->H, rows * F * esz));
+    // MX: H in the 128-column k-steps of the block-scaled MFMA; columns past F stay zero
+    A_TRY(h->alloc(&h->H, rows * (h->edt == kMX ? (F + 127) / 128 * 128 : F) * esz));
     A_TRY(h->allocT(&h->Y, rows * d));
     const int ns = lm_head_slices(h->act, h->V);
     h->hp.n_slices = ns;
@@ -645,7 +669,7 @@ static int stage_upload(dg_handle* h, const void* src, size_t bytes, void** dev)
 }
 
 int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
-                   const void* host_src, size_t bytes, const float* host_scales) {
+                   const void* host_src, size_t bytes, const void* host_scales) {
     g_err.clear();
     if (!h || !host_src) return fail(DG_EINVAL, "NULL handle or source");
     if (kind < DG_T_EMBED || kind > DG_T_SC_WD) return fail(DG_EINVAL, "bad tensor kind %d", kind);
@@ -673,10 +697,12 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
         case DG_T_SC_WG: case DG_T_SC_WU: K = h->d; N = h->Fsc; break;
         case DG_T_SC_WD: K = h->Fsc; N = h->d; break;
     }
-    const size_t per = (size_t)K * N * es;
+    // MX FP4: two E2M1 codes per byte
+    const size_t per = dt == kMX ? (size_t)K * N / 2 : (size_t)K * N * es;
     if (bytes != per * nexp)
         return fail(DG_EINVAL, "tensor kind %d: expected %zu bytes, got %zu", kind, per * nexp, bytes);
-    if (dt == kFP8 && !host_scales) return fail(DG_EINVAL, "e4m3 tensors need column scales");
+    if ((dt == kFP8 || dt == kMX) && !host_scales)
+        return fail(DG_EINVAL, "e4m3 and MX FP4 tensors need their scales");
     void* src = nullptr;
     DG_TRY(stage_upload(h, host_src, bytes, &src));
     hipStream_t s = 0;
@@ -716,9 +742,10 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
         const int which = kind - DG_T_WG;   // 0 gate, 1 up, 2 down
         std::vector<float> dummy;
         float* sdev = nullptr;
-        if (dt == kFP8) {
-            // scales are small: upload them through a temporary allocation
-            const size_t sb = (size_t)N * nexp * 4;
+        if (dt == kFP8 || dt == kMX) {
+            // scales are small: upload them through a temporary allocation (MX: one E8M0
+            // byte per 32 rows of a column)
+            const size_t sb = dt == kMX ? (size_t)(K / 32) * N * nexp : (size_t)N * nexp * 4;
             if (hipMalloc(&sdev, sb) != hipSuccess) return fail(DG_ENOMEM, "scale staging failed");
             if (hipMemcpy(sdev, host_scales, sb, hipMemcpyHostToDevice) != hipSuccess) {
                 (void)hipFree(sdev);
@@ -733,6 +760,16 @@ int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
             if (dt == kF32) {
                 void* dst = which == 0 ? h->w1[layer] : which == 1 ? h->wu[layer] : h->w2[layer];
                 he = hipMemcpy((char*)dst + per * e, se, per, hipMemcpyDeviceToDevice);
+            } else if (dt == kMX) {
+                const uint8_t* sx = (const uint8_t*)sdev + (size_t)(K / 32) * N * i;
+                if (which < 2)   // gate and up interleaved per 16 columns, as for bf16
+                    he = launch_pack_mx((const uint8_t*)se, sx, K, N, 2, which, 2 * N / 16,
+                                        (char*)h->w1[layer] + (size_t)e * mx_code_bytes(K, 2 * N),
+                                        h->x1[layer] + (size_t)e * mx_scale_bytes(K, 2 * N), s);
+                else
+                    he = launch_pack_mx((const uint8_t*)se, sx, K, N, 1, 0, N / 16,
+                                        (char*)h->w2[layer] + (size_t)e * mx_code_bytes(K, N),
+                                        h->x2[layer] + (size_t)e * mx_scale_bytes(K, N), s);
             } else if (dt == kBF16) {
                 if (which < 2) {
                     char* dst = (char*)h->w1[layer] + (size_t)e * 2 * per;
@@ -1457,7 +1494,7 @@ int dg_moe_layer(dg_handle* h, int32_t layer, const void* d_x, int32_t n_tokens,
     if (!h->dense_flag(layer, DG_T_WR - DG_T_WQ)) return fail(DG_ESTATE, "router of layer %d not loaded", layer);
     hipStream_t s = (hipStream_t)stream;
     const uint8_t* x8 = nullptr;
-    if (h->edt == kFP8) {
+    if (e4m3_inputs(h)) {
         K_TRY(launch_cast_e4m3(d_x, (int64_t)n_tokens * h->d, h->a8, s));
         x8 = h->a8;
     }

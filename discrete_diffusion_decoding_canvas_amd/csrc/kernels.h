@@ -8,6 +8,7 @@ namespace dg {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kFP8 = 2;
+constexpr int kMX = 3;    // MX FP4 expert weights (E2M1 + E8M0 per 32 along K), e4m3 inputs
 
 constexpr int kPermChunk = 1024;   // entries per permutation workgroup
 constexpr int kMaxCanvas = 1024;   // sampler capacity (one workgroup)
@@ -62,6 +63,16 @@ DG_DEV size_t frag_offset(int64_t row, int col, int K) {
     const int g = (col & 31) >> 3;
     const int byte = FP8 ? (8 * ((col >> 5) & 1) + (col & 7)) : 2 * (col & 7);
     return ((size_t)((row >> 4) * KB + kb) * 64 + 16 * g + (row & 15)) * 16 + byte;
+}
+
+// Byte offset of element (row, col) of an e4m3 [rows][K] matrix (K a multiple of 128)
+// in the A-operand order of the block-scaled 16x16x128 MFMA: [row / 16][k-step of
+// 128][lane = 16 g + row % 16][32 bytes]; the lane's byte j holds column
+// 16 g + 64 (j / 16) + j % 16 of the k-step (two runs of 16 consecutive columns).
+DG_DEV size_t frag_offset_mx(int64_t row, int col, int K) {
+    const int KS = K >> 7, ks = col >> 7, kk = col & 127;
+    const int g = (kk & 63) >> 4, j = 16 * (kk >> 6) + (kk & 15);
+    return ((size_t)((row >> 4) * KS + ks) * 64 + 16 * g + (row & 15)) * 32 + j;
 }
 
 // Transposed, key-permuted V cache: Vt[h][dim][slot], rows padded to a multiple
@@ -201,16 +212,38 @@ hipError_t launch_gemm_frag(int epi, const void* Af, int M, const void* B, int K
 //   max_rows = moe_rows_cap.
 // GEMM 2: Y[entry, :d] = H[entry] Wd_e (binary16 rows, f32 for f32 experts).
 struct ExpertWeights {
-    const void* w1;        // bf16/fp8 packed gate|up, or f32 Wg
+    const void* w1;        // bf16/fp8/MX packed gate|up, or f32 Wg
     const void* wu;        // f32 Wu (f32 path only)
     const void* w2;        // down projection (packed or row-major)
     const float* s1;       // fp8 column scales of w1 [E][2F] (interleaved)
     const float* s2;       // fp8 column scales of w2 [E][d]
+    const uint8_t* x1 = nullptr;   // MX: E8M0 block scales of w1 in stage order (mx_scale_bytes)
+    const uint8_t* x2 = nullptr;   // MX: the same for w2
 };
+
+// MX FP4 expert weights.  Codes of a [K][N] matrix (K padded to Kp, a multiple of 128)
+// as B-operand fragments of the block-scaled 16x16x128 MFMA: [N/16 groups][Kp/128
+// k-steps][64 lanes][16 bytes], lane l of group G holding column 16 G + l % 16 at rows
+// 128 ks + 32 (l / 16) + 0..31, two per byte (even row in the low nibble): the same
+// 1 KiB chunk per (group, k-step) as the bf16 and e4m3 weights.  The E8M0 scales in the
+// order the expert GEMM reads them, one 16-byte load per lane per stage of two
+// k-steps: [N/128 slabs][ceil(Kp/256) stages][64 lanes][2 k-steps][8 groups], the byte
+// of (k-step ks, group i) being the scale of rows 32 (4 ks + l / 16) .. + 31 of column
+// 16 (8 slab + i) + l % 16 (127 past K).  gstride / goff place source group g at
+// destination group g * gstride + goff (gate and up interleaved per 16 columns).
+inline size_t mx_code_bytes(int K, int N) { return (size_t)N / 16 * ((K + 127) / 128) * 1024; }
+inline size_t mx_scale_bytes(int K, int N) {
+    return (size_t)((N + 127) / 128) * (((K + 127) / 128 + 1) / 2) * 1024;
+}
+hipError_t launch_pack_mx(const uint8_t* codes, const uint8_t* scales, int K, int N, int gstride,
+                          int goff, int n_dst_groups, void* dst_codes, uint8_t* dst_scales,
+                          hipStream_t s);
 // fp8 GEMM 1's activation fragments: Xf = X[perm_token] (e4m3) in MFMA A-operand
 // order, padding rows zero.
+// mx: the MX FP4 experts' activation order (frag_offset_mx) instead.
 hipError_t launch_moe_gather8(const void* X, int d, const int32_t* perm_token,
-                              const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s);
+                              const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s,
+                              bool mx = false);
 hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
                             const int32_t* perm_token, const int32_t* offsets, int E, int d,
                             int F, int max_rows, const MoeWork& work, void* Xf, void* H,

@@ -418,6 +418,12 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
 //           kWideN) read as zero and are not stored.
 // fp8: e4m3 operands on both sides, per output column scales applied after the
 // accumulation.
+// MX: MX FP4 weights (E2M1 codes, an E8M0 scale per 32 along K) against e4m3
+// activations on the block-scaled 16x16x128 MFMA: a k-step is 128 of K, the
+// weight chunk of a (group, k-step) is still 1 KiB, the activation fragment of a
+// 16-row tile 2 KiB (frag_offset_mx), and the scales of a stage come as one 16-byte
+// load per lane (mx_scale_bytes).
+constexpr int kFmtBF16 = 0, kFmtFP8 = 1, kFmtMX = 2;
 #ifndef DG_WIDE_RING
 #define DG_WIDE_RING 6
 #endif
@@ -448,31 +454,56 @@ static_assert(kWideNT % 4 == 0, "fragments are read from LDS four groups at a ti
 constexpr int vmcnt_le(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Vector-memory operations a wave issues per stage: the activation loads (one
-// 16-byte fragment load per (k-step, row tile)) and its weight copies.  The
-// counted waits below take these as lower bounds (the compiler may split a
-// load, never merge two): every operation issued after the copy waited for
-// only makes the wait stricter.
-constexpr int kWideAOps = 2 * kWideMT;
-constexpr int kWideWaitActive = (kRing - 2) * (kWideAOps + kCopies);
+// 16-byte fragment load per (k-step, row tile), two for MX; MX adds one 16-byte
+// scale load) and its weight copies.  The counted waits below take these as lower
+// bounds (the compiler may split a load, never merge two): every operation issued
+// after the copy waited for only makes the wait stricter.
+template <int FMT>
+constexpr int wide_a_ops() { return FMT == kFmtMX ? 2 * 2 * kWideMT + 1 : 2 * kWideMT; }
+template <int FMT>
+constexpr int wide_wait_active() { return (kRing - 2) * (wide_a_ops<FMT>() + kCopies); }
 constexpr int kWideWaitIdle = (kRing - 2) * kCopies;
-static_assert(kWideWaitActive < 64, "vmcnt holds at most 63 operations");
+static_assert(wide_wait_active<kFmtMX>() < 64 && wide_wait_active<kFmtBF16>() < 64,
+              "vmcnt holds at most 63 operations");
 
 using WideAcc = f32x4_t[kWideMT][kWideNT];
-using WideFrag = Frag16[2][kWideMT];              // [k-step][row tile]
+// Activation fragments of one stage: [k-step][row tile] (MX: two 16-byte halves of
+// the 32-byte fragment, and the stage's weight scales).
+template <int FMT>
+struct WideFrag {
+    Frag16 a[2][kWideMT];
+};
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+template <>
+struct WideFrag<kFmtMX> {
+    i32x8_t a[2][kWideMT];   // the 32-byte operand, loaded as two 16-byte halves
+    uint4 sc;
+};
 
 // Activation fragments of stage st of the k-step range [kb_lo, kb_hi) (clamped).
-// afrag[mt] points at the row tile's fragment of k-step 0 plus lane * 16 bytes;
-// k-steps are 1 KiB apart, so each load is one contiguous 1 KiB per wave.
-// astride: bytes from one k-step to the next (1 KiB in fragment order, 64 B along a
-// natural bf16 row).
-DG_DEV void wide_load_a(WideFrag& a, const uint8_t* const (&afrag)[kWideMT], int st, int kb_lo,
-                        int kb_hi, uint32_t astride) {
+// afrag[mt] points at the row tile's fragment of k-step 0 plus the lane's bytes
+// (lane * 16, MX lane * 32); k-steps are astride apart (1 KiB in fragment order, 64 B
+// along a natural bf16 row, MX 2 KiB).  MX: sc points at the unit's scales of stage 0
+// plus lane * 16 (stages 1 KiB apart).
+template <int FMT>
+DG_DEV void wide_load_a(WideFrag<FMT>& a, const uint8_t* const (&afrag)[kWideMT], int st,
+                        int kb_lo, int kb_hi, uint32_t astride, const uint8_t* sc) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int kb = min(kb_lo + 2 * st + ks, kb_hi - 1);
 #pragma unroll
-        for (int mt = 0; mt < kWideMT; ++mt) a[ks][mt].u = ld16(afrag[mt] + (size_t)kb * astride);
+        for (int mt = 0; mt < kWideMT; ++mt) {
+            if constexpr (FMT == kFmtMX) {
+                const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(afrag[mt] + (size_t)kb * astride);
+                const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(afrag[mt] + (size_t)kb * astride + 16);
+                a.a[ks][mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                a.a[ks][mt].u = ld16(afrag[mt] + (size_t)kb * astride);
+            }
+        }
     }
+    if constexpr (FMT == kFmtMX) a.sc = ld16(sc + (size_t)st * 1024);
 }
 
 // The weight fragments are read from LDS in inline asm: the waves also issue
@@ -519,35 +550,58 @@ DG_DEV void lds_read_groups(u32x4_t (&f)[8], uint32_t addr) { lds_read8(f, addr)
 // Both k-steps of a stage, straight-line.  When K has an odd number of packed
 // k-steps the last stage's second k-step is multiplied by a zeroed activation
 // fragment (keep1 = false).
-template <bool FP8>
-DG_DEV void wide_mma(WideAcc& acc, const WideFrag& a, const uint4 (*bs)[kWideNT][64], bool keep1,
-                     int lane) {
+// MX: the block-scaled MFMA on one 32-byte e4m3 activation fragment and one 16-byte
+// E2M1 weight fragment.  The instruction reads only the low half of an E2M1 operand,
+// so its upper half is left undefined (no register copies); the scale of the lane's K
+// block is byte 0 of each scale operand (activations: 127, i.e. 1).
+DG_DEV f32x4_t mfma_mx(const i32x8_t& a, const i32x4_t& b, uint32_t bscale, f32x4_t c) {
+    const i32x8_t bv = __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bv, c, 0, 4, 0, 127, 0, (int)bscale);
+}
+
+template <int FMT>
+DG_DEV void wide_mma(WideAcc& acc, const WideFrag<FMT>& a, const uint4 (*bs)[kWideNT][64],
+                     bool keep1, int lane) {
+    constexpr bool FP8 = FMT == kFmtFP8;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+        // MX skips a second k-step past K (a wave-uniform branch); the others multiply
+        // it by a zeroed activation fragment
+        if (FMT == kFmtMX && ks == 1 && !keep1) break;
+        const uint32_t m = (ks == 0 || keep1) ? 0xffffffffu : 0u;
         Frag16 am[kWideMT];
+        if constexpr (FMT != kFmtMX) {
 #pragma unroll
-        for (int mt = 0; mt < kWideMT; ++mt) {
-            am[mt] = a[ks][mt];
-            if (ks == 1) {
-                const uint32_t m = keep1 ? 0xffffffffu : 0u;
-                am[mt].u = uint4{am[mt].u.x & m, am[mt].u.y & m, am[mt].u.z & m, am[mt].u.w & m};
+            for (int mt = 0; mt < kWideMT; ++mt) {
+                const uint4 v = a.a[ks][mt].u;
+                am[mt].u = uint4{v.x & m, v.y & m, v.z & m, v.w & m};
             }
         }
+        // MX reads four weight groups per LDS round trip (its 32-byte activation
+        // fragments leave fewer registers for the weight fragments)
+        constexpr int RG = FMT == kFmtMX ? 4 : kWideReadGroups;
 #pragma unroll
-        for (int n4 = 0; n4 < kWideNT; n4 += kWideReadGroups) {
-            Frag16 fb[kWideReadGroups];
+        for (int n4 = 0; n4 < kWideNT; n4 += RG) {
+            Frag16 fb[RG];
             {
-                u32x4_t f[kWideReadGroups];
+                u32x4_t f[RG];
                 lds_read_groups(f, (uint32_t)(uintptr_t)&bs[ks][n4][lane]);
 #pragma unroll
-                for (int i = 0; i < kWideReadGroups; ++i) fb[i].u = uint4{f[i].x, f[i].y, f[i].z, f[i].w};
+                for (int i = 0; i < RG; ++i) fb[i].u = uint4{f[i].x, f[i].y, f[i].z, f[i].w};
             }
 #pragma unroll
             for (int mt = 0; mt < kWideMT; ++mt)
 #pragma unroll
-                for (int i = 0; i < kWideReadGroups; ++i) {
+                for (int i = 0; i < RG; ++i) {
                     f32x4_t& c = acc[mt][n4 + i];
-                    if (FP8) {
+                    if constexpr (FMT == kFmtMX) {
+                        // scale byte (k-step ks, group n4 + i) of the stage's 16 bytes
+                        const int gi = n4 + i;
+                        const uint32_t w = ((2 * ks + gi / 4) == 0) ? a.sc.x : ((2 * ks + gi / 4) == 1) ? a.sc.y
+                                         : ((2 * ks + gi / 4) == 2) ? a.sc.z : a.sc.w;
+                        const i32x4_t b = {(int)fb[i].u.x, (int)fb[i].u.y, (int)fb[i].u.z, (int)fb[i].u.w};
+                        c = mfma_mx(a.a[ks][mt], b, w >> (8 * (gi & 3)), c);
+                    } else if constexpr (FP8) {
                         c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(am[mt].l.lo, fb[i].l.lo, c, 0, 0, 0);
                         c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(am[mt].l.hi, fb[i].l.hi, c, 0, 0, 0);
                     } else {
@@ -630,21 +684,25 @@ DG_DEV void wide_stream_only(const WeightStream& ws, WideRing& bsm) {
 
 // Operations a wave has issued after its copies of stage st + 1 when stage st
 // (st < kRing - 2) ends: the prologue's later copies and activation loads, and
-// stages 0..st.  From stage kRing - 2 on it is kWideWaitActive.
+// stages 0..st.  From stage kRing - 2 on it is wide_wait_active.
+template <int FMT>
 constexpr int wide_wait_early(int st) {
-    return (kRing - 3 - st) * kCopies + kWideLead * kWideAOps + (st + 1) * (kWideAOps + kCopies);
+    return (kRing - 3 - st) * kCopies + kWideLead * wide_a_ops<FMT>() +
+           (st + 1) * (wide_a_ops<FMT>() + kCopies);
 }
 constexpr int kWideEarly = kRing - 3 - kWideLead;   // stages whose exact count is below the steady one
-static_assert(kWideEarly <= 0 || wide_wait_early(kWideEarly - 1) < kWideWaitActive, "");
-static_assert(kWideEarly <= 0 || wide_wait_early(kWideEarly) >= kWideWaitActive, "");
+static_assert(kWideEarly <= 0 || wide_wait_early<kFmtBF16>(kWideEarly - 1) < wide_wait_active<kFmtBF16>(), "");
+static_assert(kWideEarly <= 0 || wide_wait_early<kFmtBF16>(kWideEarly) >= wide_wait_active<kFmtBF16>(), "");
+static_assert(kWideEarly <= 0 || wide_wait_early<kFmtMX>(kWideEarly - 1) < wide_wait_active<kFmtMX>(), "");
+static_assert(kWideEarly <= 0 || wide_wait_early<kFmtMX>(kWideEarly) >= wide_wait_active<kFmtMX>(), "");
 
 // The exact wait at the end of stage u < N of the first pass (u is a constant
 // once the stage loop is unrolled, and the chain folds to one s_waitcnt).
-template <int N>
+template <int FMT, int N>
 DG_DEV void wide_wait_first(int u) {
     if constexpr (N > 0) {
-        if (u == N - 1) __builtin_amdgcn_s_waitcnt(vmcnt_le(wide_wait_early(N - 1)));
-        wide_wait_first<N - 1>(u);
+        if (u == N - 1) __builtin_amdgcn_s_waitcnt(vmcnt_le(wide_wait_early<FMT>(N - 1)));
+        wide_wait_first<FMT, N - 1>(u);
     }
 }
 
@@ -654,24 +712,24 @@ DG_DEV void wide_wait_first(int u) {
 // stage st + kRing - 1, runs its MFMAs, waits for this wave's copies of stage
 // st + 1 and meets the barrier.  The slot indices are compile-time: the loop is
 // unrolled over kRing * kWideSlots stages.
-template <bool FP8>
+template <int FMT>
 DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
                           const WeightStream& ws, WideRing& bsm, int lane,
-                          uint32_t astride = 1024) {
+                          uint32_t astride = 1024, const uint8_t* sc = nullptr) {
     const int NS = ws.NS;
 #pragma unroll
     for (int mt = 0; mt < kWideMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kWideNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     asm volatile("" ::: "memory");   // the copies stay ahead of the activation loads
-    WideFrag ra[kWideSlots];
+    WideFrag<FMT> ra[kWideSlots];
 #pragma unroll
     for (int j = 0; j < kWideLead; ++j)
-        wide_load_a(ra[j], afrag, min(j, NS - 1), ws.kb_lo, ws.kb_hi, astride);
+        wide_load_a<FMT>(ra[j], afrag, min(j, NS - 1), ws.kb_lo, ws.kb_hi, astride, sc);
     asm volatile("" ::: "memory");
     // issued after the copies of stage 0: the other kRing - 2 stages' copies and
     // kWideLead stages of activations
-    __builtin_amdgcn_s_waitcnt(vmcnt_le((kRing - 2) * kCopies + kWideLead * kWideAOps));
+    __builtin_amdgcn_s_waitcnt(vmcnt_le((kRing - 2) * kCopies + kWideLead * wide_a_ops<FMT>()));
     bare_barrier();
     constexpr int kUnroll = kRing * kWideSlots;
     static_assert(kUnroll >= kWideEarly, "");
@@ -680,15 +738,15 @@ DG_DEV void wide_mainloop(WideAcc& acc, const uint8_t* const (&afrag)[kWideMT],
         for (int u = 0; u < kUnroll; ++u) {
             const int st = s0 + u;
             if (st >= NS) break;
-            wide_load_a(ra[(u + kWideLead) % kWideSlots], afrag, min(st + kWideLead, NS - 1),
-                        ws.kb_lo, ws.kb_hi, astride);
+            wide_load_a<FMT>(ra[(u + kWideLead) % kWideSlots], afrag, min(st + kWideLead, NS - 1),
+                             ws.kb_lo, ws.kb_hi, astride, sc);
             wide_copy_b(ws, st + kRing - 1, (u + kRing - 1) % kRing, bsm);
             __builtin_amdgcn_sched_barrier(0);      // issue the loads before the MFMAs
-            wide_mma<FP8>(acc, ra[u % kWideSlots], bsm[u % kRing], ws.kb_lo + 2 * st + 1 < ws.kb_hi,
+            wide_mma<FMT>(acc, ra[u % kWideSlots], bsm[u % kRing], ws.kb_lo + 2 * st + 1 < ws.kb_hi,
                           lane);
             __builtin_amdgcn_sched_barrier(0);
-            if (s0 == 0) wide_wait_first<kWideEarly>(u);
-            __builtin_amdgcn_s_waitcnt(vmcnt_le(kWideWaitActive));   // own copies of st + 1
+            if (s0 == 0) wide_wait_first<FMT, kWideEarly>(u);
+            __builtin_amdgcn_s_waitcnt(vmcnt_le(wide_wait_active<FMT>()));   // own copies of st + 1
             bare_barrier();
         }
     }
@@ -732,10 +790,14 @@ DG_DEV MoeUnit moe_unit(int u, int n_slabs, const int2* __restrict__ work,
 }
 
 // Epilogue of a unit: lane holds column lane % 16 of each group, rows 4 (lane / 16) + i.
-template <bool FP8, int GEMM>
+// fp8 applies the per-column scales; MX needs none (the block scales act in the MFMA)
+// and writes H in the MX activation order (K = F padded to 128).
+template <int FMT, int GEMM>
 DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
                          const float* __restrict__ scales, void* __restrict__ out, int lane,
                          int32_t* __restrict__ bad) {
+    constexpr bool FP8 = FMT == kFmtFP8;            // per-column scales
+    constexpr bool E4 = FMT != kFmtBF16;            // e4m3 H
     const int l16 = lane & 15, g4 = 4 * (lane >> 4);
     bool range = false;
 #pragma unroll
@@ -753,8 +815,10 @@ DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
                     const int r = c.wr0 + 16 * mt + g4 + i;
                     const float g = acc[mt][2 * p][i] * sg, uu = acc[mt][2 * p + 1][i] * su;
                     const float hv = g / (1.0f + expf(-g)) * uu;
-                    const size_t o = frag_offset<FP8>(c.off + r, hcol, F);   // GEMM 2's A order
-                    if (FP8) ((uint8_t*)out)[o] = (uint8_t)f32_to_e4m3(hv);
+                    // GEMM 2's A order
+                    const size_t o = FMT == kFmtMX ? frag_offset_mx(c.off + r, hcol, (F + 127) & ~127)
+                                                   : frag_offset<E4>(c.off + r, hcol, F);
+                    if (E4) ((uint8_t*)out)[o] = (uint8_t)f32_to_e4m3(hv);
                     else *(bf16_t*)((uint8_t*)out + o) = f32_to_bf16(hv);
                 }
             }
@@ -787,16 +851,19 @@ DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
 // takes its next unit and issues that unit's first kRing - 1 weight stages
 // before it runs the current unit's epilogue, so the weight stream does not
 // stop between units and no workgroup is launched for an absent item.
-template <bool FP8, int GEMM>
+template <int FMT, int GEMM>
 __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
     const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
     const int2* __restrict__ work, const int32_t* __restrict__ work_count,
     int32_t* __restrict__ unit_ctr, const void* __restrict__ W, const float* __restrict__ scales,
-    void* __restrict__ out, const int32_t* __restrict__ perm, int32_t* __restrict__ bad) {
+    void* __restrict__ out, const int32_t* __restrict__ perm, int32_t* __restrict__ bad,
+    const uint8_t* __restrict__ wscales = nullptr) {
+    constexpr bool FP8 = FMT == kFmtFP8;
     __shared__ __attribute__((aligned(16))) WideRing bsm;
     __shared__ int s_unit[2];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int KB = FP8 ? (K >> 6) : (K >> 5);     // packed k-steps
+    // packed k-steps (MX: K is padded to a multiple of 128 by the caller)
+    const int KB = FMT == kFmtMX ? (K >> 7) : FP8 ? (K >> 6) : (K >> 5);
     const int n_slabs = (N + kWideN - 1) / kWideN;
     const int total = *work_count * n_slabs;
     if (threadIdx.x == 0) s_unit[0] = atomicAdd(unit_ctr, 1);
@@ -814,14 +881,24 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
 #pragma unroll
             for (int mt = 0; mt < kWideMT; ++mt) {
                 const int r = c.wr0 + 16 * mt < c.n_e ? c.wr0 + 16 * mt : c.wr0;   // past the rows: tile 0
-                if (!FP8 && perm != nullptr) {
+                if (FMT == kFmtBF16 && perm != nullptr) {
                     const int tok = max(perm[c.off + r + (lane & 15)], 0);
                     afrag[mt] = Af + ((size_t)tok * K + 8 * (lane >> 4)) * 2;
+                } else if (FMT == kFmtMX) {
+                    afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 32;
                 } else {
                     afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 16;
                 }
             }
-            wide_mainloop<FP8>(acc, afrag, c.ws, bsm, lane, !FP8 && perm != nullptr ? 64u : 1024u);
+            // MX: this unit's (expert, slab) block scales, stage 0, this lane
+            const uint8_t* sc = nullptr;
+            if constexpr (FMT == kFmtMX) {
+                const int n_slabs = (N + kWideN - 1) / kWideN;
+                sc = wscales + (((size_t)c.e * n_slabs + c.n0 / kWideN) * ((KB + 1) >> 1) * 64 + lane) * 16;
+            }
+            wide_mainloop<FMT>(acc, afrag, c.ws, bsm, lane,
+                               FMT == kFmtMX ? 2048u : (FMT == kFmtBF16 && perm != nullptr) ? 64u : 1024u,
+                               sc);
         } else {
             wide_stream_only(c.ws, bsm);
         }
@@ -829,7 +906,7 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
         __syncthreads();
         const int un = __builtin_amdgcn_readfirstlane(s_unit[it & 1]);
         if (un < total) wide_fill(moe_unit<kItem>(un, n_slabs, work, offsets, N, KB, W, w, lane).ws, bsm);
-        if (rows) moe_epilogue<FP8, GEMM>(acc, c, N, F, scales, out, lane, bad);
+        if (rows) moe_epilogue<FMT, GEMM>(acc, c, N, F, scales, out, lane, bad);
         if (un >= total) break;
         c = moe_unit<kItem>(un, n_slabs, work, offsets, N, KB, W, w, lane);   // recomputed: less live state
     }
@@ -888,7 +965,7 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_head_wide(
                 const int r = c.wr0 + 16 * mt < C ? c.wr0 + 16 * mt : c.wr0;
                 afrag[mt] = Hf + ((size_t)(r >> 4) * KB * 64 + lane) * 16;
             }
-            wide_mainloop<false>(acc, afrag, c.ws, bsm, lane);
+            wide_mainloop<kFmtBF16>(acc, afrag, c.ws, bsm, lane);
         } else {
             wide_stream_only(c.ws, bsm);
         }
@@ -961,7 +1038,7 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_sc_expect(
                 const int r = min(wr0 + 16 * mt + (lane & 15), M - 1);
                 afrag[mt] = P + ((size_t)r * V + 8 * (lane >> 4)) * 2;
             }
-            wide_mainloop<false>(acc, afrag, ws, bsm, lane, 64u);
+            wide_mainloop<kFmtBF16>(acc, afrag, ws, bsm, lane, 64u);
         } else {
             wide_stream_only(ws, bsm);
         }
@@ -1030,24 +1107,39 @@ __global__ __launch_bounds__(256) void k_sc_reduce(const float* __restrict__ par
 // padding rows.  Done once here, the expert GEMM's activation loads become
 // contiguous 1 KiB reads instead of 16-row gathers repeated for every weight
 // slab.  (bf16 GEMM 1 reads the token rows in place instead.)
+// MX: the fragments of the block-scaled 16x16x128 MFMA instead (frag_offset_mx): a
+// lane's 32 bytes are columns 16 g .. + 15 and 64 + 16 g .. + 15 of a 128-column k-step.
+template <bool MX>
 __global__ __launch_bounds__(256) void k_moe_gather_frag8(const uint8_t* __restrict__ X, int K,
                                                           const int32_t* __restrict__ perm_token,
                                                           const int32_t* __restrict__ offsets,
                                                           int E, uint8_t* __restrict__ Xf) {
-    const int KB = K >> 6;
+    const int KB = MX ? (K >> 7) : (K >> 6);
     const int kb = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int tile = blockIdx.y;
     if (kb >= KB || 16 * tile >= offsets[E]) return;
     const int lane = threadIdx.x & 63, g = lane >> 4;
     const int tok = perm_token[16 * tile + (lane & 15)];
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (tok >= 0) {
-        const uint8_t* row = X + (size_t)tok * K;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + kb * 64 + 8 * g);
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + kb * 64 + 32 + 8 * g);
-        v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    if constexpr (MX) {
+        uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
+        if (tok >= 0) {
+            const uint8_t* row = X + (size_t)tok * K + kb * 128 + 16 * g;
+            lo = *reinterpret_cast<const uint4*>(row);
+            hi = *reinterpret_cast<const uint4*>(row + 64);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(Xf + (((size_t)tile * KB + kb) * 64 + lane) * 32);
+        dst[0] = lo;
+        dst[1] = hi;
+    } else {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tok >= 0) {
+            const uint8_t* row = X + (size_t)tok * K;
+            const uint2 lo = *reinterpret_cast<const uint2*>(row + kb * 64 + 8 * g);
+            const uint2 hi = *reinterpret_cast<const uint2*>(row + kb * 64 + 32 + 8 * g);
+            v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+        *reinterpret_cast<uint4*>(Xf + (((size_t)tile * KB + kb) * 64 + lane) * 16) = v;
     }
-    *reinterpret_cast<uint4*>(Xf + (((size_t)tile * KB + kb) * 64 + lane) * 16) = v;
 }
 
 // ------------------------------------------------------------------ expert GEMMs (f32, VALU)
@@ -1174,21 +1266,27 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
             (const float*)X, d, F, perm_token, offsets, E, max_rows, (const float*)w.w1,
             (const float*)w.wu, (float*)H);
     } else {
-        const int kq = dtype == kFP8 ? 64 : 32;
-        if ((2 * F) % kWideN || d % kq || F % kq) return hipErrorInvalidValue;
+        const int kq = dtype == kMX ? 128 : dtype == kFP8 ? 64 : 32;
+        if ((2 * F) % kWideN || d % kq || F % (dtype == kMX ? 32 : kq)) return hipErrorInvalidValue;
         const unsigned grid = moe_grid(work.max_items, (2 * F) / kWideN);
-        if (dtype == kFP8) {
+        if (dtype == kMX) {
+            if (!Xf || !w.x1) return hipErrorInvalidValue;
+            k_moe_wide<kFmtMX, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
+                                                                offsets, work.items, work.count,
+                                                                work.count + 1, w.w1, nullptr, H,
+                                                                nullptr, nullptr, w.x1);
+        } else if (dtype == kFP8) {
             if (!Xf) return hipErrorInvalidValue;
-            k_moe_wide<true, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
-                                                              offsets, work.items, work.count,
-                                                              work.count + 1, w.w1, w.s1, H,
-                                                              nullptr, nullptr);
+            k_moe_wide<kFmtFP8, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
+                                                                 offsets, work.items, work.count,
+                                                                 work.count + 1, w.w1, w.s1, H,
+                                                                 nullptr, nullptr);
         } else {
             // token rows read in place through the permutation
-            k_moe_wide<false, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)X, d, 2 * F, F,
-                                                               offsets, work.items, work.count,
-                                                               work.count + 1, w.w1, w.s1, H,
-                                                               perm_token, nullptr);
+            k_moe_wide<kFmtBF16, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)X, d, 2 * F, F,
+                                                                  offsets, work.items, work.count,
+                                                                  work.count + 1, w.w1, w.s1, H,
+                                                                  perm_token, nullptr);
         }
     }
     return hipGetLastError();
@@ -1245,13 +1343,18 @@ hipError_t launch_sc_reduce(const float* part, int M, int d, int V, float* u, vo
 }
 
 hipError_t launch_moe_gather8(const void* X, int d, const int32_t* perm_token,
-                              const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s) {
+                              const int32_t* offsets, int E, int max_rows, void* Xf, hipStream_t s,
+                              bool mx) {
     if (max_rows <= 0) return hipSuccess;
-    if (d % 64 || !Xf) return hipErrorInvalidValue;
-    const int KB = d / 64;
+    if (d % (mx ? 128 : 64) || !Xf) return hipErrorInvalidValue;
+    const int KB = mx ? d / 128 : d / 64;
     dim3 gg((KB + 3) / 4, (max_rows + kMoePad - 1) / kMoePad);   // tiles past offsets[E] exit
-    k_moe_gather_frag8<<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
-                                          (uint8_t*)Xf);
+    if (mx)
+        k_moe_gather_frag8<true><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
+                                                    (uint8_t*)Xf);
+    else
+        k_moe_gather_frag8<false><<<gg, 256, 0, s>>>((const uint8_t*)X, d, perm_token, offsets, E,
+                                                     (uint8_t*)Xf);
     return hipGetLastError();
 }
 
@@ -1266,16 +1369,24 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
     } else {
         if (d % 16 || F % (dtype == kFP8 ? 64 : 32)) return hipErrorInvalidValue;
         const unsigned grid = moe_grid(work.max_items2, (d + kWideN - 1) / kWideN);
-        if (dtype == kFP8)
-            k_moe_wide<true, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
-                                                              work.items2, work.count + 3,
-                                                              work.count + 2, w.w2, w.s2, Y,
-                                                              nullptr, bad);
-        else
-            k_moe_wide<false, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
-                                                               work.items2, work.count + 3,
-                                                               work.count + 2, w.w2, w.s2, Y,
-                                                               nullptr, bad);
+        if (dtype == kMX) {
+            if (!w.x2) return hipErrorInvalidValue;
+            // K of H and W2 padded to a multiple of 128 (zero columns / rows)
+            k_moe_wide<kFmtMX, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, (F + 127) & ~127,
+                                                                d, F, offsets, work.items2,
+                                                                work.count + 3, work.count + 2, w.w2,
+                                                                nullptr, Y, nullptr, bad, w.x2);
+        } else if (dtype == kFP8) {
+            k_moe_wide<kFmtFP8, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
+                                                                 work.items2, work.count + 3,
+                                                                 work.count + 2, w.w2, w.s2, Y,
+                                                                 nullptr, bad);
+        } else {
+            k_moe_wide<kFmtBF16, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
+                                                                  work.items2, work.count + 3,
+                                                                  work.count + 2, w.w2, w.s2, Y,
+                                                                  nullptr, bad);
+        }
     }
     return hipGetLastError();
 }

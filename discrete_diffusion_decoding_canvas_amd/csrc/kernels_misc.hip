@@ -929,6 +929,60 @@ hipError_t launch_pack_b16(const void* src, bool src_kn, int K, int N, int gstri
     LAUNCH_CHECK();
 }
 
+// MX FP4 weights into the fragment and stage orders of mx_code_bytes / mx_scale_bytes.
+// Codes: one thread per destination byte (source group gs, k-step, lane, byte t): rows
+// 128 ks + 32 (l / 16) + 2 t and + 1 of column 16 gs + l % 16, zero past K.  Scales: one
+// thread per (source group, k-step, lane).
+__global__ void k_pack_mx_codes(const uint8_t* __restrict__ src, int K, int N, int KS, int gstride,
+                                int goff, uint8_t* __restrict__ dst) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)(N / 16) * KS * 1024;
+    if (idx >= total) return;
+    const int t = (int)(idx & 15), lane = (int)((idx >> 4) & 63);
+    const int64_t rest = idx >> 10;
+    const int ks = (int)(rest % KS), gs = (int)(rest / KS);
+    const int n = 16 * gs + (lane & 15);
+    const int k0 = 128 * ks + 32 * (lane >> 4) + 2 * t;
+    auto nib = [&](int k) -> uint32_t {
+        if (k >= K) return 0u;
+        return (src[(size_t)k * (N / 2) + n / 2] >> (4 * (n & 1))) & 0xFu;
+    };
+    const int64_t G = (int64_t)gs * gstride + goff;
+    dst[((G * KS + ks) * 64 + lane) * 16 + t] = (uint8_t)(nib(k0) | (nib(k0 + 1) << 4));
+}
+
+__global__ void k_pack_mx_scales(const uint8_t* __restrict__ src, int K, int N, int KS, int gstride,
+                                 int goff, uint8_t* __restrict__ dst) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)(N / 16) * KS * 64;
+    if (idx >= total) return;
+    const int lane = (int)(idx & 63);
+    const int64_t rest = idx >> 6;
+    const int ks = (int)(rest % KS), gs = (int)(rest / KS);
+    const int n = 16 * gs + (lane & 15);
+    const int kb = 4 * ks + (lane >> 4);
+    const int64_t G = (int64_t)gs * gstride + goff;
+    const int64_t slab = G >> 3, i = G & 7;
+    const int NSt = (KS + 1) / 2;
+    dst[((slab * NSt + ks / 2) * 64 + lane) * 16 + 8 * (ks & 1) + i] =
+        kb < K / 32 ? src[(size_t)kb * N + n] : (uint8_t)127;
+}
+
+hipError_t launch_pack_mx(const uint8_t* codes, const uint8_t* scales, int K, int N, int gstride,
+                          int goff, int n_dst_groups, void* dst_codes, uint8_t* dst_scales,
+                          hipStream_t s) {
+    if (K <= 0 || K % 32 || N % 16 || gstride < 1 || goff < 0 || goff >= gstride ||
+        (int64_t)(N / 16 - 1) * gstride + goff >= n_dst_groups)
+        return hipErrorInvalidValue;
+    const int KS = (K + 127) / 128;
+    const int64_t nc = (int64_t)(N / 16) * KS * 1024, ns = (int64_t)(N / 16) * KS * 64;
+    k_pack_mx_codes<<<(unsigned)((nc + 255) / 256), 256, 0, s>>>(codes, K, N, KS, gstride, goff,
+                                                                 (uint8_t*)dst_codes);
+    k_pack_mx_scales<<<(unsigned)((ns + 255) / 256), 256, 0, s>>>(scales, K, N, KS, gstride, goff,
+                                                                  dst_scales);
+    LAUNCH_CHECK();
+}
+
 hipError_t launch_pack_b8(const void* src, int K, int N, int gstride, int goff, void* dst,
                           hipStream_t s) {
     int64_t total = (int64_t)K * N;

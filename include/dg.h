@@ -58,6 +58,9 @@ extern "C" {
 #define DG_F32 0
 #define DG_BF16 1
 #define DG_FP8_E4M3 2       /* OCP FP8 E4M3 (bias 7, max 448); expert weights only */
+#define DG_MXFP4 3          /* OCP MX FP4: E2M1 elements, one E8M0 scale per 32 along the
+                               contraction; expert weights only (the pages' 4-bit deployment,
+                               alphasignal, the FP8 / 4-bit quantisation paragraph) */
 
 /* ---------------------------------------------------------------- tensors
  * Logical layouts are [in, out] row-major (y = x W):
@@ -134,7 +137,8 @@ typedef struct dg_model_cfg {
     float rms_eps;         /* RMSNorm epsilon (unit gains) */
     float temperature;     /* tau > 0: p0 = softmax(logits / tau) */
     int32_t act_dtype;     /* DG_F32 or DG_BF16: activations, KV cache, dense weights */
-    int32_t expert_dtype;  /* DG_F32, DG_BF16 or DG_FP8_E4M3 (needs act_dtype DG_BF16) */
+    int32_t expert_dtype;  /* DG_F32, DG_BF16, DG_FP8_E4M3 or DG_MXFP4 (the last two need
+                              act_dtype DG_BF16; DG_MXFP4 needs d_model % 128 == 0) */
     uint32_t capture_mask; /* DG_CAP_* bits */
     int32_t max_batch;     /* canvases one batched pass holds (dg_denoise_step_batch); 0 or 1:
                               single canvases only.  max_batch * canvas <= 65536 */
@@ -158,11 +162,15 @@ const char* dg_last_error(void);
 
 /* Copy one logical tensor from host memory into the handle, re-laid out for
  * the kernels.  kind = DG_T_*; layer in [0, L) (ignored for DG_T_EMBED);
- * expert in [0, E) for expert tensors, else ignored.  bytes must equal the
- * tensor size in its storage type.  host_scales: e4m3 experts only, float
- * per output column (F for WG/WU, d for WD); NULL otherwise.  Synchronous. */
+ * expert in [0, E) for expert tensors (-1: all E at once, [E, in, out]),
+ * else ignored.  bytes must equal the tensor size in its storage type.
+ * host_scales: e4m3 experts: float per output column (F for WG/WU, d for WD);
+ * MX FP4 experts: the codes are [in][out / 2] bytes (two E2M1 per byte, the
+ * even output column in the low nibble) and host_scales holds uint8 E8M0
+ * exponents [in / 32][out] (one per 32 rows of a column, value 2^(s - 127));
+ * NULL otherwise.  Synchronous. */
 int dg_load_tensor(dg_handle* h, int32_t kind, int32_t layer, int32_t expert,
-                   const void* host_src, size_t bytes, const float* host_scales);
+                   const void* host_src, size_t bytes, const void* host_scales);
 
 /* Stage 1 (technical report, Method, generation pipeline): run the causal
  * encoder over P prompt ids (d_prompt_ids, device int32 [P]) and fill K/V
