@@ -105,7 +105,6 @@ struct dg_handle {
     int2* work_items = nullptr;      // the first GEMM's items, then the second's
     int work_cap1 = 0;               // capacity of the first list
     int32_t* work_count = nullptr;
-    uint32_t* route_ticket = nullptr;
 
     HeadPartials hp{};
     float* st_m = nullptr;
@@ -283,7 +282,6 @@ static MoeWork moe_work(dg_handle* h, int n) {
     w.count = h->work_count;
     w.max_items = (n * h->k + kMoeItemRows - 1) / kMoeItemRows + h->E;
     w.max_items2 = (n * h->k + kMoeRows - 1) / kMoeRows + h->E;
-    w.ticket = h->route_ticket;
     return w;
 }
 
@@ -587,8 +585,6 @@ int dg_create(const dg_model_cfg* cfg, dg_handle** out) {
     h->work_cap1 = (T * k + kMoeItemRows - 1) / kMoeItemRows + E;
     A_TRY(h->allocT(&h->work_items, (size_t)h->work_cap1 + (T * k + kMoeRows - 1) / kMoeRows + E));
     A_TRY(h->allocT(&h->work_count, 4));   // item counts and the two GEMMs' unit counters
-    A_TRY(h->allocT(&h->route_ticket, 1));
-    if (hipMemset(h->route_ticket, 0, 4) != hipSuccess) return cleanup(fail(DG_EHIP, "ticket reset failed"));
     if (h->edt == kFP8 || h->edt == kMX) A_TRY(h->alloc(&h->Xf, rows * d * esz));
     if (h->act == kBF16)
         A_TRY(h->alloc(&h->Af, (T + 15) / 16 * 16 * std::max<size_t>(d, (size_t)h->Hq * h->D) * 2));

@@ -46,7 +46,6 @@ struct MoeWork {
                        // [3] number of valid items2
     int max_items;     // grid bound: ceil(entries / kMoeItemRows) + E
     int max_items2;    // grid bound: ceil(entries / kMoeRows) + E
-    uint32_t* ticket;  // zero-initialised block counter of the fused top-k + permutation
 };
 
 // Byte offset of element (row, col) of a [rows][K] matrix stored in MFMA

@@ -183,18 +183,20 @@ DG_DEV void route_offsets(const int32_t* cnt, int E, int pad, int32_t* off, int3
         for (int j = off[e] + cnt[e]; j < off[e + 1]; ++j) perm_token[j] = -1;
 }
 
-// The permutation of n <= kPermSmall entries by one block: counts, offsets,
-// work items, and every entry's row (the next free row of its expert).
+// The permutation of n <= kPermSmall entries by one block of kPermThreads threads:
+// counts, offsets, work items, and every entry's row (the next free row of its
+// expert).
 constexpr int kPermSmall = 8192;
+constexpr int kPermThreads = 1024;
 
-DG_DEV void permute_block(const int32_t* __restrict__ idx, int n, int E, int k, int pad,
-                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
-                          int32_t* __restrict__ inv, int2* __restrict__ work,
-                          int2* __restrict__ work2, int32_t* __restrict__ work_count) {
+__global__ __launch_bounds__(kPermThreads) void k_moe_permute(
+    const int32_t* __restrict__ idx, int n, int E, int k, int pad, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv, int2* __restrict__ work,
+    int2* __restrict__ work2, int32_t* __restrict__ work_count) {
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
     __shared__ int32_t woff[kMaxExperts + 1];
-    constexpr int kPer = kPermSmall / 256;     // entries per thread (blocks of 256 threads)
+    constexpr int kPer = kPermSmall / kPermThreads;   // entries per thread
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
     // each entry's expert and its place among the expert's entries (the counter's
@@ -202,7 +204,7 @@ DG_DEV void permute_block(const int32_t* __restrict__ idx, int n, int E, int k, 
     int ex[kPer], lp[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const int f = threadIdx.x + 256 * i;
+        const int f = threadIdx.x + kPermThreads * i;
         ex[i] = f < n ? idx[f] : -1;
     }
 #pragma unroll
@@ -212,52 +214,12 @@ DG_DEV void permute_block(const int32_t* __restrict__ idx, int n, int E, int k, 
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const int f = threadIdx.x + 256 * i;
+        const int f = threadIdx.x + kPermThreads * i;
         if (ex[i] < 0) continue;
         const int pos = off[ex[i]] + lp[i];
         perm_token[pos] = f / k;
         inv[f] = pos;
     }
-}
-
-// Top-k and permutation in one launch (M * k <= kPermSmall): each block ranks
-// its tokens; the last block to finish (a ticket counter, reset by that block
-// for the next launch) permutes all entries.
-__global__ __launch_bounds__(256) void k_router_route(const float* __restrict__ logits, int nsplit,
-                                                      int M, int E, int k, int pad,
-                                                      int32_t* __restrict__ idx,
-                                                      float* __restrict__ gates,
-                                                      int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ perm_token,
-                                                      int32_t* __restrict__ inv,
-                                                      int2* __restrict__ work,
-                                                      int2* __restrict__ work2,
-                                                      int32_t* __restrict__ work_count,
-                                                      uint32_t* __restrict__ ticket) {
-    __shared__ bool last;
-    __shared__ int32_t s_idx[4 * kMaxTopK];
-    __shared__ float s_gates[4 * kMaxTopK];
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int wt = threadIdx.x >> 6;
-    // each wave ranks its token into LDS; wave 0 then stores the block's results, so
-    // that one device-scope release (wave 0's, after its own stores) covers them all
-    // before the ticket: the last block, on another CU, reads every block's idx
-    if (t < M) topk_token(logits, nsplit, M, E, k, t, s_idx + wt * k, s_gates + wt * k);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int n_tok = min(4, M - (int)blockIdx.x * 4);
-        for (int i = threadIdx.x; i < n_tok * k; i += 64) {
-            idx[(int64_t)blockIdx.x * 4 * k + i] = s_idx[i];
-            gates[(int64_t)blockIdx.x * 4 * k + i] = s_gates[i];
-        }
-        __threadfence();
-        if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();                                       // every block's idx visible here
-    permute_block(idx, M * k, E, k, pad, offsets, perm_token, inv, work, work2, work_count);
-    if (threadIdx.x == 0) *ticket = 0u;
 }
 
 // Larger batches (prefill chunks): per-chunk counts, one scan, per-chunk assignment.
@@ -332,12 +294,11 @@ hipError_t launch_router_permute(const float* logits, int nsplit, int M, int E, 
     if (work.max_items < (n + kMoeItemRows - 1) / kMoeItemRows + E ||
         work.max_items2 < (n + kMoeRows - 1) / kMoeRows + E)
         return hipErrorInvalidValue;
+    k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
     if (n <= kPermSmall) {
-        k_router_route<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, pad, idx, gates,
-                                                   offsets, perm_token, inv, work.items,
-                                                   work.items2, work.count, work.ticket);
+        k_moe_permute<<<1, kPermThreads, 0, s>>>(idx, n, E, k, pad, offsets, perm_token, inv,
+                                                 work.items, work.items2, work.count);
     } else {
-        k_router_topk<<<(M + 3) / 4, 256, 0, s>>>(logits, nsplit, M, E, k, idx, gates);
         const int n_chunks = (n + kPermChunk - 1) / kPermChunk;
         k_moe_count<<<n_chunks, 256, 0, s>>>(idx, n, E, counts);
         k_moe_scan<<<1, 256, 0, s>>>(counts, n_chunks, E, pad, base, offsets, perm_token,
