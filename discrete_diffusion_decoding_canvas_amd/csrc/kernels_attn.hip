@@ -402,7 +402,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
 
 // Fixed-order combine of the key splits: with each split's average A_s = O_s / l_s
 // (stored as binary16), O = sum_s 2^(m_s - m*) l_s A_s / sum_s 2^(m_s - m*) l_s.
-// One wave per (query, head); each lane owns two of the 128 dimensions.
+// One wave per (query, head): lane s first holds split s's statistics (n_splits <=
+// 64); then lane 16 i + c takes the 8 dimensions 8c.. of splits i, i + 4, i + 8, ..
+// (one 16-byte load each, four in flight together) and the four partial sums of a
+// chunk are added by two lane exchanges, in the same order for every call.
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
@@ -412,7 +415,6 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     const int lane = threadIdx.x & 63;
     if (wid >= M * Hq) return;
     const int q = wid / Hq, h = wid % Hq;
-    // lane s holds split s's statistics (n_splits <= 64); every split wrote its partials
     float ms = -INFINITY, ls = 0.f;
     if (lane < n_splits) {
         const float2 ml = *reinterpret_cast<const float2*>(
@@ -423,24 +425,41 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     const float mstar = wave_max(ms);
     const float wl = (ms == -INFINITY) ? 0.f : exp2f(ms - mstar) * ls;
     const float den = wave_sum(wl);
-    const _Float16* pa = reinterpret_cast<const _Float16*>(part_o);
-    float n0 = 0.f, n1 = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < n_splits; ++s) {
-        const float ws = __shfl(wl, s, 64);
-        const int64_t pr = ((int64_t)s * Hq + h) * M + q;
-        const f16x2_t v = *reinterpret_cast<const f16x2_t*>(pa + pr * kAttnD + 2 * lane);
-        n0 += ws * (float)v[0];
-        n1 += ws * (float)v[1];
+    const int gi = lane >> 4, c = lane & 15;
+    const _Float16* pa = reinterpret_cast<const _Float16*>(part_o) + 8 * c;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // splits past n_splits re-read the last one with weight 0
+    for (int t0 = 0; t0 < n_splits; t0 += 16) {
+        f16x8_t v[4];
+        float ws[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int sp = t0 + 4 * t + gi;
+            ws[t] = __shfl(wl, sp < 64 ? sp : 63, 64);
+            const int sl = sp < n_splits ? sp : n_splits - 1;
+            v[t] = *reinterpret_cast<const f16x8_t*>(pa + (((int64_t)sl * Hq + h) * M + q) * kAttnD);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += ws[t] * (float)v[t][i];
     }
-    T* dst = O + (int64_t)q * Hq * kAttnD + (int64_t)h * kAttnD + 2 * lane;
-    const T o0 = from_f32<T>(n0 / den), o1 = from_f32<T>(n1 / den);
-    dst[0] = o0;
-    dst[1] = o1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        acc[i] += __shfl_xor(acc[i], 16, 64);
+        acc[i] += __shfl_xor(acc[i], 32, 64);
+    }
+    if (gi != 0) return;
+    T r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = from_f32<T>(acc[i] / den);
+    T* dst = O + (int64_t)q * Hq * kAttnD + (int64_t)h * kAttnD + 8 * c;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = r[i];
     if (Of) {
-        T* f = reinterpret_cast<T*>(Of + frag_offset<false>(q, h * kAttnD + 2 * lane, Hq * kAttnD));
-        f[0] = o0;
-        f[1] = o1;
+        T* f = reinterpret_cast<T*>(Of + frag_offset<false>(q, h * kAttnD + 8 * c, Hq * kAttnD));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = r[i];
     }
 }
 
