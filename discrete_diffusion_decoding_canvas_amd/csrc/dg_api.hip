@@ -102,7 +102,7 @@ struct dg_handle {
     void* Af = nullptr;      // dense-projection activations in fragment order (bf16)
     void* H = nullptr;
     float* Y = nullptr;      // expert outputs: float rows (f32 experts) or binary16 rows
-    int2* work_items = nullptr;      // the first GEMM's items, then the second's
+    int4* work_items = nullptr;      // the first GEMM's items, then the second's
     int work_cap1 = 0;               // capacity of the first list
     int32_t* work_count = nullptr;
 

@@ -39,8 +39,8 @@ inline int64_t moe_rows_cap(int64_t n, int k, int E, int pad) { return n * k + (
 // [row0, row0 + kMoeItemRows) of expert e (clipped to the expert's count), item i
 // of `items2` rows [row0, row0 + kMoeRows).
 struct MoeWork {
-    int2* items;       // {e, row0}, first GEMM
-    int2* items2;      // {e, row0}, second GEMM
+    int4* items;       // {e, row0, first row of e, end of e's padded rows}, first GEMM
+    int4* items2;      // the same for the second GEMM
     int32_t* count;    // [0] number of valid items; [1], [2] unit counters of the two
                        // persistent expert GEMMs (zeroed by the kernel that writes [0]);
                        // [3] number of valid items2

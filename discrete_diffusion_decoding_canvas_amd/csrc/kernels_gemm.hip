@@ -764,14 +764,12 @@ struct MoeUnit {
 };
 
 template <int ITEM_ROWS>
-DG_DEV MoeUnit moe_unit(int u, int n_slabs, const int2* __restrict__ work,
-                        const int32_t* __restrict__ offsets, int N, int KB, const void* W, int w,
+DG_DEV MoeUnit moe_unit(int u, int n_slabs, const int4& item, int N, int KB, const void* W, int w,
                         int lane) {
     MoeUnit c;
-    const int2 item = work[u / n_slabs];
     c.e = item.x;
-    c.off = offsets[c.e];                                          // a multiple of 16
-    c.n_e = min(offsets[c.e + 1] - c.off, item.y + ITEM_ROWS);
+    c.off = item.z;                                                // a multiple of 16
+    c.n_e = min(item.w - item.z, item.y + ITEM_ROWS);
     c.n0 = (u % n_slabs) * kWideN;
     // rows r = item.y + 16 (kWideMT w + mt) + lane % 16 (expert-relative); n_e is
     // a multiple of 16, so a row tile is wholly inside or outside the expert
@@ -848,54 +846,59 @@ DG_DEV void moe_epilogue(const WideAcc& acc, const MoeUnit& c, int N, int F,
 // Persistent: about one workgroup per CU, each taking units from the counter
 // unit_ctr (zeroed by the routing kernel that wrote the work items) until
 // work_count * n_slabs are taken.  After a unit's last stage the workgroup
-// takes its next unit and issues that unit's first kRing - 1 weight stages
-// before it runs the current unit's epilogue, so the weight stream does not
-// stop between units and no workgroup is launched for an absent item.
+// takes its next unit and issues that unit's first kRing - 1 weight stages (and,
+// bf16 GEMM 1, its token indices) before it runs the current unit's epilogue, so
+// the weight stream does not stop between units and no workgroup is launched for
+// an absent item.  A work item carries its expert's row range, so a unit needs
+// one load after the counter.
+template <int FMT>
+DG_DEV void moe_afrag(const uint8_t* (&afrag)[kWideMT], const MoeUnit& c, const uint8_t* Af,
+                      int K, int KB, const int32_t* __restrict__ perm, int lane) {
+#pragma unroll
+    for (int mt = 0; mt < kWideMT; ++mt) {
+        const int r = c.wr0 + 16 * mt < c.n_e ? c.wr0 + 16 * mt : c.wr0;   // past the rows: tile 0
+        if (FMT == kFmtBF16 && perm != nullptr) {
+            const int tok = max(perm[c.off + r + (lane & 15)], 0);
+            afrag[mt] = Af + ((size_t)tok * K + 8 * (lane >> 4)) * 2;
+        } else if (FMT == kFmtMX) {
+            afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 32;
+        } else {
+            afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 16;
+        }
+    }
+}
+
 template <int FMT, int GEMM>
 __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
-    const uint8_t* Af, int K, int N, int F, const int32_t* __restrict__ offsets,
-    const int2* __restrict__ work, const int32_t* __restrict__ work_count,
-    int32_t* __restrict__ unit_ctr, const void* __restrict__ W, const float* __restrict__ scales,
-    void* __restrict__ out, const int32_t* __restrict__ perm, int32_t* __restrict__ bad,
+    const uint8_t* Af, int K, int N, int F, const int4* __restrict__ work,
+    const int32_t* __restrict__ work_count, int32_t* __restrict__ unit_ctr,
+    const void* __restrict__ W, const float* __restrict__ scales, void* __restrict__ out,
+    const int32_t* __restrict__ perm, int32_t* __restrict__ bad,
     const uint8_t* __restrict__ wscales = nullptr) {
-    constexpr bool FP8 = FMT == kFmtFP8;
     __shared__ __attribute__((aligned(16))) WideRing bsm;
     __shared__ int s_unit[2];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     // packed k-steps (MX: K is padded to a multiple of 128 by the caller)
-    const int KB = FMT == kFmtMX ? (K >> 7) : FP8 ? (K >> 6) : (K >> 5);
+    const int KB = FMT == kFmtMX ? (K >> 7) : FMT == kFmtFP8 ? (K >> 6) : (K >> 5);
     const int n_slabs = (N + kWideN - 1) / kWideN;
     const int total = *work_count * n_slabs;
     if (threadIdx.x == 0) s_unit[0] = atomicAdd(unit_ctr, 1);
     __syncthreads();
-    const int u = __builtin_amdgcn_readfirstlane(s_unit[0]);
+    int u = __builtin_amdgcn_readfirstlane(s_unit[0]);
     if (u >= total) return;
     constexpr int kItem = GEMM == 1 ? kMoeItemRows : kMoeRows;   // rows of one work item
-    MoeUnit c = moe_unit<kItem>(u, n_slabs, work, offsets, N, KB, W, w, lane);
+    MoeUnit c = moe_unit<kItem>(u, n_slabs, work[u / n_slabs], N, KB, W, w, lane);
     wide_fill(c.ws, bsm);
+    const uint8_t* afrag[kWideMT];
+    if (c.wr0 < c.n_e) moe_afrag<FMT>(afrag, c, Af, K, KB, perm, lane);
     for (int it = 1;; ++it) {
         const bool rows = c.wr0 < c.n_e;          // uniform per wave
         WideAcc acc;
         if (rows) {
-            const uint8_t* afrag[kWideMT];
-#pragma unroll
-            for (int mt = 0; mt < kWideMT; ++mt) {
-                const int r = c.wr0 + 16 * mt < c.n_e ? c.wr0 + 16 * mt : c.wr0;   // past the rows: tile 0
-                if (FMT == kFmtBF16 && perm != nullptr) {
-                    const int tok = max(perm[c.off + r + (lane & 15)], 0);
-                    afrag[mt] = Af + ((size_t)tok * K + 8 * (lane >> 4)) * 2;
-                } else if (FMT == kFmtMX) {
-                    afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 32;
-                } else {
-                    afrag[mt] = Af + ((size_t)((c.off + r) >> 4) * KB * 64 + lane) * 16;
-                }
-            }
             // MX: this unit's (expert, slab) block scales, stage 0, this lane
             const uint8_t* sc = nullptr;
-            if constexpr (FMT == kFmtMX) {
-                const int n_slabs = (N + kWideN - 1) / kWideN;
+            if constexpr (FMT == kFmtMX)
                 sc = wscales + (((size_t)c.e * n_slabs + c.n0 / kWideN) * ((KB + 1) >> 1) * 64 + lane) * 16;
-            }
             wide_mainloop<FMT>(acc, afrag, c.ws, bsm, lane,
                                FMT == kFmtMX ? 2048u : (FMT == kFmtBF16 && perm != nullptr) ? 64u : 1024u,
                                sc);
@@ -905,10 +908,16 @@ __global__ __launch_bounds__(kWideThreads, kWideWavesPerEU) void k_moe_wide(
         if (threadIdx.x == 0) s_unit[it & 1] = atomicAdd(unit_ctr, 1);
         __syncthreads();
         const int un = __builtin_amdgcn_readfirstlane(s_unit[it & 1]);
-        if (un < total) wide_fill(moe_unit<kItem>(un, n_slabs, work, offsets, N, KB, W, w, lane).ws, bsm);
+        int4 item;
+        if (un < total) {
+            item = work[un / n_slabs];
+            wide_fill(moe_unit<kItem>(un, n_slabs, item, N, KB, W, w, lane).ws, bsm);
+        }
         if (rows) moe_epilogue<FMT, GEMM>(acc, c, N, F, scales, out, lane, bad);
         if (un >= total) break;
-        c = moe_unit<kItem>(un, n_slabs, work, offsets, N, KB, W, w, lane);   // recomputed: less live state
+        u = un;
+        c = moe_unit<kItem>(un, n_slabs, item, N, KB, W, w, lane);   // recomputed: less live state
+        if (c.wr0 < c.n_e) moe_afrag<FMT>(afrag, c, Af, K, KB, perm, lane);
     }
 }
 
@@ -1272,21 +1281,18 @@ hipError_t launch_moe_gemm1(int dtype, const ExpertWeights& w, const void* X,
         if (dtype == kMX) {
             if (!Xf || !w.x1) return hipErrorInvalidValue;
             k_moe_wide<kFmtMX, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
-                                                                offsets, work.items, work.count,
-                                                                work.count + 1, w.w1, nullptr, H,
-                                                                nullptr, nullptr, w.x1);
+                                                                work.items, work.count, work.count + 1,
+                                                                w.w1, nullptr, H, nullptr, nullptr, w.x1);
         } else if (dtype == kFP8) {
             if (!Xf) return hipErrorInvalidValue;
             k_moe_wide<kFmtFP8, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)Xf, d, 2 * F, F,
-                                                                 offsets, work.items, work.count,
-                                                                 work.count + 1, w.w1, w.s1, H,
-                                                                 nullptr, nullptr);
+                                                                 work.items, work.count, work.count + 1,
+                                                                 w.w1, w.s1, H, nullptr, nullptr);
         } else {
             // token rows read in place through the permutation
             k_moe_wide<kFmtBF16, 1><<<grid, kWideThreads, 0, s>>>((const uint8_t*)X, d, 2 * F, F,
-                                                                  offsets, work.items, work.count,
-                                                                  work.count + 1, w.w1, w.s1, H,
-                                                                  perm_token, nullptr);
+                                                                  work.items, work.count, work.count + 1,
+                                                                  w.w1, w.s1, H, perm_token, nullptr);
         }
     }
     return hipGetLastError();
@@ -1373,16 +1379,16 @@ hipError_t launch_moe_gemm2(int dtype, const ExpertWeights& w, const void* H,
             if (!w.x2) return hipErrorInvalidValue;
             // K of H and W2 padded to a multiple of 128 (zero columns / rows)
             k_moe_wide<kFmtMX, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, (F + 127) & ~127,
-                                                                d, F, offsets, work.items2,
-                                                                work.count + 3, work.count + 2, w.w2,
-                                                                nullptr, Y, nullptr, bad, w.x2);
+                                                                d, F, work.items2, work.count + 3,
+                                                                work.count + 2, w.w2, nullptr, Y,
+                                                                nullptr, bad, w.x2);
         } else if (dtype == kFP8) {
-            k_moe_wide<kFmtFP8, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
+            k_moe_wide<kFmtFP8, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F,
                                                                  work.items2, work.count + 3,
                                                                  work.count + 2, w.w2, w.s2, Y,
                                                                  nullptr, bad);
         } else {
-            k_moe_wide<kFmtBF16, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F, offsets,
+            k_moe_wide<kFmtBF16, 2><<<grid, kWideThreads, 0, s>>>((const uint8_t*)H, F, d, F,
                                                                   work.items2, work.count + 3,
                                                                   work.count + 2, w.w2, w.s2, Y,
                                                                   nullptr, bad);

@@ -145,10 +145,11 @@ DG_DEV void wave0_exclusive_scan(int32_t* v, int n) {
     if (l == 63) v[n] = inc;
 }
 
-// Work items (expert, first row) of `rows`-row chunks of every expert, experts
-// in order; their number to *count.  woff is LDS scratch of E + 1 entries.
+// Work items of `rows`-row chunks of every expert, experts in order: (expert,
+// first row of the chunk within the expert, the expert's first row, the end of its
+// padded rows); their number to *count.  woff is LDS scratch of E + 1 entries.
 DG_DEV void route_items(const int32_t* off, int E, int rows, int32_t* woff,
-                        int2* __restrict__ items, int32_t* __restrict__ count) {
+                        int4* __restrict__ items, int32_t* __restrict__ count) {
     for (int e = threadIdx.x; e < E; e += blockDim.x)
         woff[e] = (off[e + 1] - off[e] + rows - 1) / rows;
     __syncthreads();
@@ -156,7 +157,8 @@ DG_DEV void route_items(const int32_t* off, int E, int rows, int32_t* woff,
     __syncthreads();
     if (threadIdx.x == 0) *count = woff[E];
     for (int e = threadIdx.x; e < E; e += blockDim.x)
-        for (int i = woff[e]; i < woff[e + 1]; ++i) items[i] = make_int2(e, (i - woff[e]) * rows);
+        for (int i = woff[e]; i < woff[e + 1]; ++i)
+            items[i] = make_int4(e, (i - woff[e]) * rows, off[e], off[e + 1]);
     __syncthreads();   // woff is reused
 }
 
@@ -166,7 +168,7 @@ DG_DEV void route_items(const int32_t* off, int E, int rows, int32_t* woff,
 // rows.  woff is LDS scratch of E + 1 entries.
 DG_DEV void route_offsets(const int32_t* cnt, int E, int pad, int32_t* off, int32_t* woff,
                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
-                          int2* __restrict__ items, int2* __restrict__ items2,
+                          int4* __restrict__ items, int4* __restrict__ items2,
                           int32_t* __restrict__ count) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) off[e] = round_up(cnt[e], pad);
     __syncthreads();
@@ -191,8 +193,8 @@ constexpr int kPermThreads = 1024;
 
 __global__ __launch_bounds__(kPermThreads) void k_moe_permute(
     const int32_t* __restrict__ idx, int n, int E, int k, int pad, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv, int2* __restrict__ work,
-    int2* __restrict__ work2, int32_t* __restrict__ work_count) {
+    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv, int4* __restrict__ work,
+    int4* __restrict__ work2, int32_t* __restrict__ work_count) {
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
     __shared__ int32_t woff[kMaxExperts + 1];
@@ -242,8 +244,8 @@ __global__ __launch_bounds__(256) void k_moe_scan(const int32_t* __restrict__ co
                                                   int32_t* __restrict__ base,
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ perm_token,
-                                                  int2* __restrict__ work,
-                                                  int2* __restrict__ work2,
+                                                  int4* __restrict__ work,
+                                                  int4* __restrict__ work2,
                                                   int32_t* __restrict__ work_count) {
     __shared__ int32_t tot[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
