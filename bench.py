@@ -83,10 +83,15 @@ def pass_flops(w, S):
     return w.n_layers * per_layer + 2 * C * d * V
 
 
-def cpu_baseline(w, seconds_budget=30.0):
+def cpu_baseline(w, deep=None, seconds_budget=30.0):
     """Time the CPU oracle on a bounded sample of one denoise pass: decoder layer 0 of the
-    canvas over the 8192-token prompt context, plus the LM head and sampler; the pass time is
-    estimated as n_layers x (layer time) + (head time)."""
+    canvas over the 8192-token prompt context, a deep decoder layer, and the LM head and
+    sampler.  The deep layer (deep = (layer, its input [C, d], its prompt K and V, the GPU
+    pass's expert ids there), taken from the GPU's pass since the oracle cannot run the
+    30-layer prefill within the budget) stands for layers 1..n-1: past the first layers
+    most tokens route to 10-20 experts, and the oracle's MoE cost follows the experts hit.  The pass time is estimated
+    as layer 0 + (n_layers - 1) x (deep layer) + head; without a deep sample, n_layers x
+    (layer 0) + head."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -119,13 +124,35 @@ def cpu_baseline(w, seconds_budget=30.0):
         red[rows], _ = gumbel_draw(z[rows], gumbel_uniforms(w.seed, 0, 0, rows, w.vocab))
     sampler_update(canvas, np.zeros(w.canvas, np.uint8), st.conf, st.argmax, red, 0, w.T)
     t_head = time.perf_counter() - t0
-    t_pass = w.n_layers * t_layer + t_head
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    if deep is None:
+        t_pass = w.n_layers * t_layer + t_head
+        sample = (f"decoder layer 0 of one pass ({t_layer:.2f} s, 256 canvas queries over "
+                  f"{m.n_ctx + w.canvas} keys + MoE) and the LM head + sampler "
+                  f"({t_head:.2f} s); pass = {w.n_layers} x layer + head = {t_pass:.1f} s")
+    else:
+        L, x_in, k_ctx, v_ctx, route = deep
+        del m, W, E, h, hl, hn, z                     # layer 0's weights and the head's logits
+        Wd = FixtureWeights(w)
+        md = OracleModel(w, Wd)
+        md.n_ctx = w.prompt_len
+        md.K[L], md.V[L] = k_ctx, v_ctx
+        for kind in ("wq", "wk", "wv", "wo", "wr"):   # weights outside the timed region
+            Wd.dense(kind, L)
+        hit = np.unique(route)                        # the experts the GPU pass hit there
+        for e in hit:
+            for kind in ("wg", "wu", "wd"):
+                Wd.expert(kind, L, int(e))
+        t0 = time.perf_counter()
+        md.decoder_layer(L, x_in)
+        t_deep = time.perf_counter() - t0
+        t_pass = t_layer + (w.n_layers - 1) * t_deep + t_head
+        sample = (f"decoder layer 0 ({t_layer:.2f} s), decoder layer {L} on the GPU pass's input "
+                  f"to it ({t_deep:.2f} s, {len(hit)} experts hit), each with 256 canvas queries over "
+                  f"{w.prompt_len + w.canvas} keys, and the LM head + sampler ({t_head:.2f} s); "
+                  f"pass = layer 0 + {w.n_layers - 1} x layer {L} + head = {t_pass:.1f} s")
     return {"value": round(w.canvas / t_pass, 3), "unit": "canvas tok/s", "cores": threads,
-            "kind": "oracle", "extrapolated": True,
-            "sample": (f"decoder layer 0 of one pass ({t_layer:.2f} s, 256 canvas queries over "
-                       f"{m.n_ctx + w.canvas} keys + MoE) and the LM head + sampler "
-                       f"({t_head:.2f} s); pass = {w.n_layers} x layer + head = {t_pass:.1f} s")}
+            "kind": "oracle", "extrapolated": True, "sample": sample}
 
 
 COPY_BYTES = 1 << 30
@@ -698,10 +725,13 @@ def main():
 
     # routing of one more (untimed) pass: experts actually hit per layer set the
     # algorithmic weight bytes of the expert GEMMs
-    dg.dg_set_capture(h, dg.DG_CAP_ROUTING)
+    # (the residual stream entering a deep layer and that layer's prompt K/V feed the CPU
+    # oracle's timed sample of a deep layer)
+    deep_layer = w.n_layers // 2
+    dg.dg_set_capture(h, dg.DG_CAP_ROUTING | (0 if args.no_cpu_baseline else dg.DG_CAP_HIDDEN))
     dg.dg_init_canvas(h, canvas, mask, seed)
     dg.dg_denoise_step(h, canvas, mask, 0, T, seed)
-    active, max_load = [], []
+    active, max_load, deep = [], [], None
     rbuf = torch.empty(2 * C * w.top_k, dtype=torch.int32, device="cuda")
     for l in range(w.n_layers):
         dg.dg_get_capture(h, dg.DG_CAP_ROUTING, l, rbuf)
@@ -710,6 +740,18 @@ def main():
         cnt = np.bincount(ids, minlength=w.n_experts)
         active.append(int((cnt > 0).sum()))
         max_load.append(int(cnt.max()))
+        if l == deep_layer:
+            deep_route = ids
+    if not args.no_cpu_baseline:
+        hid = torch.empty(C, w.d_model, dtype=torch.float32, device="cuda")
+        dg.dg_get_capture(h, dg.DG_CAP_HIDDEN, deep_layer - 1, hid)   # after layer L - 1
+        kv = []
+        for which in (0, 1):
+            t = torch.empty(w.n_kv_heads, w.prompt_len, w.head_dim, dtype=torch.bfloat16, device="cuda")
+            dg.dg_get_kv(h, deep_layer, which, 0, w.prompt_len, t)
+            kv.append(t.float().cpu().numpy().astype(np.float64))
+        torch.cuda.synchronize()
+        deep = (deep_layer, hid.cpu().numpy().astype(np.float64), kv[0], kv[1], deep_route)
     dg.dg_set_capture(h, 0)
     mean_active = float(np.mean(active))
     log(f"experts hit per layer: mean {mean_active:.1f}, min {min(active)}, max {max(active)}; "
@@ -890,7 +932,7 @@ def main():
         result["long_context_fp8"] = long_context_bench(dg, torch, fx, build_handle, args)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(w, deep)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
