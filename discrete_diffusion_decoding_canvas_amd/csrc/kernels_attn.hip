@@ -43,6 +43,7 @@ union AFrag {
     bf16x8_t b;
     f16x8_t f;
     uint16_t h[8];
+    uint32_t u32[4];
 };
 
 // One 32-key block of the LDS ring, in MFMA fragment order: K fragments
@@ -299,7 +300,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         }
         // P in binary16 (round to nearest even; p < 2^9).  The causal encoder, whose K/V
         // stay in the cache for every later pass, adds the rounding remainder as a second
-        // binary16 part (about 22 significant bits); a decoder pass uses one part.
+        // binary16 part (about 22 significant bits) and sums p in fp32; a decoder pass uses
+        // one part and sums the binary16 weights the PV product uses, two per fp32 dot
+        // product with (1, 1).
         AFrag pf[2], pl[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -308,10 +311,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float p = fast_exp2(fmaf(score(qb, i >> 2, i & 3), scale_log2, nb));
-                psum += p;
                 const _Float16 hi = (_Float16)p;
                 pf[qb].f[i] = hi;
-                if (CAUSAL) pl[qb].f[i] = (_Float16)(p - (float)hi);
+                if (CAUSAL) {
+                    psum += p;
+                    pl[qb].f[i] = (_Float16)(p - (float)hi);
+                }
+            }
+            if (!CAUSAL) {
+                const half2_t one2 = {(__fp16)1.0f, (__fp16)1.0f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pf[qb].u32[j]), one2, psum, false);
             }
             l_run[qb] += psum;
         }
@@ -333,25 +344,37 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     // MFMAs of block b + 1 are issued, so the matrix cores and the VALU overlap.  The
     // blocks that need no key mask (all but the last, and for the causal encoder all
     // before this wave's diagonal) come first and run a loop of their own.
-    f32x4_t st[2][2];
-    auto block = [&](int b, auto mask_tag) {
+    // The unmasked blocks go two at a time, the score registers swapping roles.
+    f32x4_t sa[2][2], sb[2][2];
+    auto block = [&](int b, const f32x4_t (&st)[2][2], f32x4_t (&sn)[2][2], auto mask_tag) {
         if (wave_active) {
-            f32x4_t sn[2][2];
             if (b + 1 < n_blocks) attn_scores(sn, ring[(b + 1) % kAttnRing], qf, lane);
             softmax_pv(st, kbeg + 32 * b, ring[b % kAttnRing], mask_tag);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) st[qb][kh] = sn[qb][kh];
         }
         __syncthreads();
     };
     int n_full = (kend - kbeg) / 32;
     if (CAUSAL) n_full = min(n_full, max(0, (wave_qlim - kbeg + 1) / 32));
-    if (wave_active && n_blocks > 0) attn_scores(st, ring[0], qf, lane);
+    if (wave_active && n_blocks > 0) attn_scores(sa, ring[0], qf, lane);
     int b = 0;
-    for (; b < n_full; ++b) block(b, std::false_type{});
-    for (; b < n_blocks; ++b) block(b, std::true_type{});
+    for (; b + 1 < n_full; b += 2) {
+        block(b, sa, sb, std::false_type{});
+        block(b + 1, sb, sa, std::false_type{});
+    }
+    auto swap_in = [&]() {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) sa[qb][kh] = sb[qb][kh];
+    };
+    if (b < n_full) {
+        block(b++, sa, sb, std::false_type{});
+        swap_in();
+    }
+    for (; b < n_blocks; ++b) {
+        block(b, sa, sb, std::true_type{});
+        swap_in();
+    }
     if (!wave_active) return;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
