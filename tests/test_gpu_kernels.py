@@ -175,6 +175,23 @@ def test_moe_layer_skewed_all_tokens_one_expert(dg):
     assert load[5] == T and (load == 0).sum() > 10
 
 
+@pytest.mark.parametrize("T", [512, 520])
+def test_moe_layer_routing_capacity(dg, T):
+    """256 experts top-16 (the largest expert count and k the routing takes).  512 tokens give
+    8192 entries, the most the one-block permutation takes (each of its 1024 threads holds 8);
+    520 tokens take the chunked path (per-chunk counts, one scan, per-chunk scatter)."""
+    d, E, k, F = 128, 256, 16, 128
+    x = fx.normal(3, 930, (T, d), 1.0, "bf16")
+    wr = fx.normal(3, 931, (d, E), 0.05, "bf16")
+    wg = fx.normal(3, 932, (E, d, F), 0.05, "bf16")
+    wu = fx.normal(3, 933, (E, d, F), 0.05, "bf16")
+    wd = fx.normal(3, 934, (E, F, d), 0.05, "bf16")
+    err, in_band, load = _run_moe(dg, x, wr, wg, wu, wd, k)
+    assert load.sum() == T * k
+    log(f"T={T} E={E} k={k}: max abs err {err:.3g}; in-band routing differences {in_band}; "
+        f"experts hit {(load > 0).sum()}")
+
+
 def test_moe_layer_fp8_experts(dg):
     T, d, E, k, F = 256, 256, 64, 4, 128
     x = fx.normal(2, 920, (T, d), 1.0, "bf16")
