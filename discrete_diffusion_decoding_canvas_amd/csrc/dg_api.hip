@@ -405,8 +405,10 @@ static int run_layer(dg_handle* h, int l, int n, int64_t pos0, bool causal, bool
     aa.q = h->q;
     aa.k = h->klayer(l);
     aa.v = h->vlayer(l);
-    aa.o = h->attn_o;
+    // bf16: the output projection reads the fragment-order copy; the row-order one is
+    // written only for the attention capture
     aa.of = h->act == kBF16 ? h->Af : nullptr;
+    aa.o = h->act == kBF16 && !(capture && h->cap(DG_CAP_ATTN)) ? nullptr : h->attn_o;
     aa.Hq = h->Hq;
     aa.Hkv = h->Hkv;
     aa.M = n;

@@ -290,7 +290,7 @@ struct AttnArgs {
     const void* q;
     const void* k;
     const void* v;
-    void* o;
+    void* o;               // O in row order; bf16 may pass null when of is given
     void* of = nullptr;    // optional bf16 copy of O in fragment order (frag_offset, K = Hq D)
     int Hq, Hkv, M, S, D;
     int64_t kv_rows;       // row capacity per head of K (and of f32 V)

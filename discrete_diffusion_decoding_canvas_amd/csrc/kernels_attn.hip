@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                        ((uint32_t)f32_to_bf16(o[qb][dt][1] * inv) << 16);
                 pk.y = (uint32_t)f32_to_bf16(o[qb][dt][2] * inv) |
                        ((uint32_t)f32_to_bf16(o[qb][dt][3] * inv) << 16);
-                *reinterpret_cast<uint2*>(dst + 16 * dt + 4 * g) = pk;
+                if (O) *reinterpret_cast<uint2*>(dst + 16 * dt + 4 * g) = pk;
                 if (Of)
                     *reinterpret_cast<uint2*>(Of + frag_offset<false>(q, h * kAttnD + 16 * dt + 4 * g,
                                                                       Hq * kAttnD)) = pk;
@@ -476,9 +476,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     T r[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = from_f32<T>(acc[i] / den);
-    T* dst = O + (int64_t)q * Hq * kAttnD + (int64_t)h * kAttnD + 8 * c;
+    if (O) {
+        T* dst = O + (int64_t)q * Hq * kAttnD + (int64_t)h * kAttnD + 8 * c;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = r[i];
+        for (int i = 0; i < 8; ++i) dst[i] = r[i];
+    }
     if (Of) {
         T* f = reinterpret_cast<T*>(Of + frag_offset<false>(q, h * kAttnD + 8 * c, Hq * kAttnD));
 #pragma unroll
@@ -594,7 +596,7 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
             return hipErrorInvalidValue;
         return hipGetLastError();
     }
-    if (a.D != kAttnD || (a.v_rows & 31) || a.v_rows < a.S || a.kv_rows < a.S)
+    if (a.D != kAttnD || (a.v_rows & 31) || a.v_rows < a.S || a.kv_rows < a.S || (!a.o && !a.of))
         return hipErrorInvalidValue;
     int n, kps;
     attn_split_plan(a.Hq, a.Hkv, a.M, a.S, n, kps);
