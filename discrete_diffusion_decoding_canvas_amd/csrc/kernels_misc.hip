@@ -183,15 +183,43 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ 
 }
 
 // Natural [Hkv][S][D] V -> transposed key-permuted layout (for the attention entry point).
-__global__ void k_pack_vt(const bf16_t* __restrict__ v, int Hkv, int S, int D,
-                          bf16_t* __restrict__ vt, int64_t rows) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)Hkv * rows * D;
-    if (idx >= total) return;
-    const int t = (int)(idx % D);
-    const int64_t p = (idx / D) % rows;
-    const int h = (int)(idx / ((int64_t)D * rows));
-    vt[vt_index(h, t, p, D, rows)] = p < S ? v[((int64_t)h * S + p) * D + t] : (bf16_t)0;
+// One workgroup per (32-key block, KV head): the block's key rows are read with 16-byte
+// loads into LDS (rows padded by 16 bytes), then every dimension row of the block (32 keys,
+// 64 bytes, in the slot order of vt_index) is written as four 16-byte stores.  Keys past S
+// are zero.  D is a multiple of 8 and at most kPackVtMaxD.
+constexpr int kPackVtMaxD = 128;
+
+__global__ __launch_bounds__(256) void k_pack_vt(const bf16_t* __restrict__ v, int S, int D,
+                                                 bf16_t* __restrict__ vt, int64_t rows) {
+    __shared__ __attribute__((aligned(16))) bf16_t tile[32][kPackVtMaxD + 8];
+    const int64_t p0 = (int64_t)blockIdx.x * 32;
+    const int h = blockIdx.y;
+    const int c8n = D >> 3;
+    for (int e = threadIdx.x; e < 32 * c8n; e += blockDim.x) {
+        const int r = e / c8n, c8 = e % c8n;
+        const int64_t p = p0 + r;
+        uint4 val = uint4{0u, 0u, 0u, 0u};
+        if (p < S) val = *reinterpret_cast<const uint4*>(v + ((int64_t)h * S + p) * D + 8 * c8);
+        *reinterpret_cast<uint4*>(&tile[r][8 * c8]) = val;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
+        const int dim = e >> 2, q0 = 8 * (e & 3);
+        uint16_t o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // output slot q holds key 16 b + 4 a + c, where q = 8 a + 4 b + c (vt_index)
+            const int q = q0 + j;
+            const int r = 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3);
+            o[j] = tile[r][dim];
+        }
+        uint4 w;
+        w.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        w.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        w.z = (uint32_t)o[4] | ((uint32_t)o[5] << 16);
+        w.w = (uint32_t)o[6] | ((uint32_t)o[7] << 16);
+        *reinterpret_cast<uint4*>(vt + ((int64_t)h * D + dim) * rows + p0 + q0) = w;
+    }
 }
 
 // K/V read-back in natural [Hkv][n][D] layout (debug / tests).
@@ -788,9 +816,9 @@ hipError_t launch_rope_scatter(int dtype, const float* qkv, int M, int Hq, int H
 
 hipError_t launch_pack_vt(const void* v, int Hkv, int S, int D, void* vt, int64_t rows,
                           hipStream_t s) {
-    int64_t total = (int64_t)Hkv * rows * D;
-    k_pack_vt<<<(unsigned)((total + 255) / 256), 256, 0, s>>>((const bf16_t*)v, Hkv, S, D,
-                                                              (bf16_t*)vt, rows);
+    if (Hkv <= 0 || rows <= 0) return hipSuccess;
+    if ((D & 7) || D > kPackVtMaxD || (rows & 31) || rows < S) return hipErrorInvalidValue;
+    k_pack_vt<<<dim3((unsigned)(rows / 32), Hkv), 256, 0, s>>>((const bf16_t*)v, S, D, (bf16_t*)vt, rows);
     LAUNCH_CHECK();
 }
 
