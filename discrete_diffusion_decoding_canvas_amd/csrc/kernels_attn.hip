@@ -37,6 +37,11 @@ constexpr int kAttnRows = 32 * kAttnWaves;   // query rows per workgroup
 constexpr int kAttnThreads = 64 * (kAttnWaves + 2);   // + a K and a V^T producer wave
 constexpr int kAttnRing = 6;                 // 32-key blocks in the LDS ring (16 KiB each)
 static_assert(kAttnRing >= 3, "two blocks ahead of the one being consumed");
+#ifndef DG_ATTN_PRE
+#define DG_ATTN_PRE 3
+#endif
+constexpr int kAttnPre = DG_ATTN_PRE;         // blocks copied before the first barrier
+static_assert(kAttnPre >= 3 && kAttnPre <= kAttnRing - 1, "blocks 0..2 before the first iteration ends");
 
 union AFrag {
     uint4 u;
@@ -208,12 +213,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         // The consumers read K of block b + 1 and V of block b in iteration b, so before
         // the barrier that opens iteration b the blocks up to b + 1 must have landed and
         // the V of block b must be in binary16.
-        for (int b = 0; b < kAttnRing - 1; ++b) issue(b);
-        __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(8 * (kAttnRing - 3)));   // blocks 0, 1 landed
+        // Before the first barrier only kAttnPre blocks are asked for (every CU starts at
+        // once, and the first two are the ones waited for); the first iteration asks for
+        // the rest of the ring.
+        for (int b = 0; b < kAttnPre; ++b) issue(b);
+        __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(8 * (kAttnPre - 2)));   // blocks 0, 1 landed
         if (is_v && n_blocks > 0) convert_v_slot(ring[0].v, lane);
         attn_bare_barrier();
         for (int b = 0; b < n_blocks; ++b) {
-            issue(b + kAttnRing - 1);                                   // into the slot of block b - 1
+            if (b == 0) {
+                for (int i = kAttnPre; i < kAttnRing; ++i) issue(i);   // unused slots
+            } else {
+                issue(b + kAttnRing - 1);                               // into the slot of block b - 1
+            }
             __builtin_amdgcn_s_waitcnt(attn_vmcnt_le(8 * (kAttnRing - 3)));   // block b + 2 landed
             if (is_v && b + 1 < n_blocks) convert_v_slot(ring[(b + 1) % kAttnRing].v, lane);
             attn_bare_barrier();
