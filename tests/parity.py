@@ -92,3 +92,29 @@ def lock_set_check(gpu_mask_out, ref_mask_out, mask_in, conf_ref, cut_low, cut_h
     bad = (g_new != r_new) & far & ~mask_in
     assert not bad.any(), f"lock decisions differ away from the cut at {np.flatnonzero(bad)}"
     return int(np.sum((g_new != r_new) & ~far))
+
+
+def entropy_tolerance(z, tolz):
+    """Largest change of the entropy H = -sum_j p_j ln p_j, p = softmax(z), per row of
+    the tempered logits z [..., V], over every perturbation d with |d_j| <= tolz_j.
+
+    The gradient of H is dH/dz_j = -p_j (z_j - E_p z).  Along the segment z + t d
+    (0 <= t <= 1) each weight p_j(t) stays within e^(2D) p_j (D = max tolz), and each
+    centred logit z_j(t) - E_p(t) z(t) within |z_j - E_p z| + (e^(2D) - 1) M + 2D
+    (M = E_p |z - E_p z|).  Integrating the gradient along the segment then gives
+
+        |H(z + d) - H(z)| <= e^(2D) (A + T ((e^(2D) - 1) M + 2D)),
+
+    A = sum_j p_j |z_j - E_p z| tolz_j, T = sum_j p_j tolz_j.  For small D it is the
+    first-order term A.  Used to turn the stated logit tolerance into one on entropies.
+    """
+    z = np.asarray(z, np.float64)
+    tolz = np.broadcast_to(np.asarray(tolz, np.float64), z.shape)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    p = e / e.sum(axis=-1, keepdims=True)
+    dev = np.abs(z - np.sum(p * z, axis=-1, keepdims=True))
+    A = np.sum(p * dev * tolz, axis=-1)
+    M = np.sum(p * dev, axis=-1)
+    T = np.sum(p * tolz, axis=-1)
+    D = tolz.max(axis=-1)
+    return np.exp(2 * D) * (A + T * (np.expm1(2 * D) * M + 2 * D))

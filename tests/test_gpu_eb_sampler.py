@@ -8,7 +8,10 @@ argmax / mean above theta, last pass, ragged C = 1000, C = 1, C = 1024 fully
 locked, acceptance of exactly one and of all, a NaN entropy, max_steps = 1.
 
 Whole passes (dg_denoise_step_eb) on the fp32 tiny model and the small bf16
-model, teacher-forced on the oracle's canvas: entropies within a tolerance,
+model, teacher-forced on the oracle's canvas: tempered logits within the stated
+logit tolerance, each entropy within 1e-4 nats of the entropy of the GPU's own
+logits (the streaming fp32 arithmetic) and within the tolerance that the logit
+tolerance implies of the oracle's (parity.entropy_tolerance, pinned on the CPU),
 argmax and Gumbel draws gated by their margins, the accepted set equal to the
 oracle's where its margins clear the entropy error (and a valid entropy-bounded
 prefix of the pass's own entropies everywhere), renoised tokens bit-exact; a
@@ -24,8 +27,8 @@ from oracle import eb_sampler as eb
 from oracle.model import OracleModel
 from oracle.philox import init_canvas, renoise_tokens
 from oracle.weights import FixtureWeights
-from parity import E2E_GATE, gated_mismatches, routing_sets
-from gpu_util import i32_dev, log, need_gpu, routing_capture, stats_capture, u8_dev
+from parity import E2E_GATE, TOL, assert_close, entropy_tolerance, gated_mismatches, routing_sets
+from gpu_util import i32_dev, log, logits_capture, need_gpu, routing_capture, stats_capture, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -113,11 +116,13 @@ def test_eb_sample_chained_passes(dg):
 
 
 # --------------------------------------------------------------------------- whole passes
-H_TOL = {"f32": 1e-3, "bf16": 5e-2}
+# Entropy of the GPU's own tempered logits against its streaming entropy: fp32 sums of
+# e^(z - m) and e^(z - m)(z - m) over at most 1024 ids, merged per slice (~1e-6 nats).
+H_SELF_TOL = 1e-4
 
 
 def _model_env(dg, W):
-    h = build_handle(dg, W, capture_mask=dg.DG_CAP_STATS | dg.DG_CAP_ROUTING)
+    h = build_handle(dg, W, capture_mask=dg.DG_CAP_STATS | dg.DG_CAP_ROUTING | dg.DG_CAP_LOGITS)
     oracle = OracleModel(W, FixtureWeights(W))
     ids = fx.prompt_ids(W)
     oracle.prefill(ids)
@@ -137,11 +142,21 @@ def _check_pass(dg, h, W, s, res, er, H, canvas_in, mask_in, cd, md, info, p, se
     Hd = torch.empty(C, dtype=torch.float32, device="cuda")
     dg.dg_get_capture(h, dg.DG_CAP_ENTROPY, 0, Hd)
     st = stats_capture(dg, h, C)
-    torch.cuda.synchronize()
+    zg = logits_capture(dg, h, C, W.vocab).cpu().numpy().astype(np.float64)
     Hg = Hd.cpu().numpy().astype(np.float64)
-    tol = H_TOL[kind]
+    # the streaming entropy against the entropy of the same (GPU) logits, every row
+    self_err = np.abs(Hg - eb.entropy(zg))
+    assert self_err.max() <= H_SELF_TOL, f"{tag}: streaming entropy off by {self_err.max():.3g}"
+    # logits L = tau z within the stated tolerance; it bounds the entropy's distance
+    # from the oracle's through entropy_tolerance
+    tau = eb.tau_at(s, p)
+    atol, rtol = TOL[kind]
+    zo = res.logits
+    assert_close(f"{tag} logits", zg[ok] * tau, zo[ok] * tau, atol, rtol)
+    h_tol = H_SELF_TOL + entropy_tolerance(zo[ok], atol / tau + rtol * np.abs(zo[ok]))
     err = np.abs(Hg - H)[ok]
-    assert err.max(initial=0.0) <= tol, f"{tag}: entropy off by {err.max():.3g}"
+    assert np.all(err <= h_tol), f"{tag}: entropy off by {np.max(err - h_tol):.3g} past its bound"
+    tol = float(h_tol.max(initial=H_SELF_TOL))
     bad, n, _ = gated_mismatches(st["argmax"][ok], res.stats.argmax[ok], res.stats.top2_gap[ok],
                                  E2E_GATE[kind])
     assert bad == 0, f"{tag}: {bad}/{n} gated argmax differ"
@@ -195,7 +210,7 @@ def _teacher_forced(dg, W, kind, gamma, n_passes):
             if last:                      # the previous pass's input again: the argmax repeats
                 canvas, mask = c_prev, m_prev
             p = p_stop if last else p_run
-            res, er, H = oracle.denoise_step_eb(canvas, mask, prev, s, p, seed)
+            res, er, H = oracle.denoise_step_eb(canvas, mask, prev, s, p, seed, keep_logits=True)
             cd, md = i32_dev(canvas), u8_dev(mask)
             info = torch.zeros(4, dtype=torch.int32, device="cuda")
             log(f"{kind} entropy-bounded pass {s}{' (repeat)' if last else ''}")
