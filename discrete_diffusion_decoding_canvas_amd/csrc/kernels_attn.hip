@@ -32,10 +32,16 @@
 namespace dg {
 
 constexpr int kAttnD = 128;
-constexpr int kAttnWaves = 8;                // consumer waves (32 query rows each)
+#ifndef DG_ATTN_WAVES
+#define DG_ATTN_WAVES 8
+#endif
+#ifndef DG_ATTN_RING
+#define DG_ATTN_RING 6
+#endif
+constexpr int kAttnWaves = DG_ATTN_WAVES;    // consumer waves (32 query rows each)
 constexpr int kAttnRows = 32 * kAttnWaves;   // query rows per workgroup
 constexpr int kAttnThreads = 64 * (kAttnWaves + 2);   // + a K and a V^T producer wave
-constexpr int kAttnRing = 6;                 // 32-key blocks in the LDS ring (16 KiB each)
+constexpr int kAttnRing = DG_ATTN_RING;      // 32-key blocks in the LDS ring (16 KiB each)
 static_assert(kAttnRing >= 3, "two blocks ahead of the one being consumed");
 #ifndef DG_ATTN_PRE
 #define DG_ATTN_PRE 3
@@ -549,10 +555,10 @@ __global__ __launch_bounds__(64) void k_attn_f32(const float* __restrict__ Q,
 #ifndef DG_ATTN_TARGET_WGS
 #define DG_ATTN_TARGET_WGS 256
 #endif
-// With T target workgroups and 256-row query workgroups, a split call (n >= 2
-// splits) has fewer than T query workgroups, so Hq M < 256 T, and n Hq M <
-// (T / qwgs + 1) Hq M <= 256 T + Hq M < 512 T query rows of partials.
-static_assert(2 * 256 * DG_ATTN_TARGET_WGS <= kAttnMaxPartRows, "partials bound");
+// With T target workgroups of R = kAttnRows query rows, a split call (n >= 2
+// splits) has qwgs < T query workgroups and Hq M <= R qwgs, so n Hq M <=
+// (T / qwgs + 1) R qwgs = R (T + qwgs) < 2 R T query rows of partials.
+static_assert(2 * kAttnRows * DG_ATTN_TARGET_WGS <= kAttnMaxPartRows, "partials bound");
 static int attn_splits(int Hq, int Hkv, int M, int S) {
     const int G = Hq / Hkv;
     const int qwgs = Hkv * ((G * M + kAttnRows - 1) / kAttnRows);
