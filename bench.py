@@ -845,6 +845,29 @@ def main():
         batched[str(B)] = {"ms_per_pass": round(b_ms, 4),
                            "canvas_tok_s": round(B * C / (b_ms / 1e3), 1)}
         log(f"batch of {B} canvases: {b_ms:.3f} ms per pass, {B * C / (b_ms / 1e3):.0f} canvas tok/s")
+        if B == BATCHES[-1]:
+            # the largest batch once more with per-kernel events: every token reaches k
+            # experts, so the expert GEMMs' FLOPs are exact whatever the routing
+            dg.dg_profile_begin(h, n_b * (w.n_layers * 7 + 4))
+            for i in range(n_b):
+                bstep(i)
+            torch.cuda.synchronize()
+            b_prof_ms, b_prof_n = dg.dg_profile_end(h)
+            rows = B * C * w.top_k
+            flops = {"moe_gemm1": rows * w.d_model * 2 * w.d_ff * 2,
+                     "moe_gemm2": rows * w.d_ff * w.d_model * 2,
+                     "attention": B * 4 * C * (w.prompt_len + C) * w.head_dim * w.n_q_heads}
+            mfma = {}
+            for i, n in enumerate(["moe_gemm1", "moe_gemm2", "attention"]):
+                if b_prof_n[i]:
+                    us = b_prof_ms[i] / b_prof_n[i] * 1e3
+                    tf = flops[n] / (us * 1e-6) / 1e12
+                    mfma[n] = {"us_per_launch": round(us, 2), "tflops": round(tf, 1),
+                               "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+            batched[str(B)]["mfma"] = mfma
+            log(f"batch of {B}: " + ", ".join(f"{n} {v['us_per_launch']:.1f} us = {v['tflops']:.0f} "
+                                              f"TFLOP/s ({100 * v['frac_bf16_peak']:.1f} % of bf16 peak)"
+                                              for n, v in mfma.items()))
     dg.dg_check_finite(h)
 
     # roofline of the dominant kernel (expert gate/up GEMM + SwiGLU)
