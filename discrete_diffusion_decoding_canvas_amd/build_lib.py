@@ -18,6 +18,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+# extra hipcc options, e.g. DG_HIPCC_FLAGS="-DDG_WIDE_RING=5" to build with another tuning value
+FLAGS += os.environ.get("DG_HIPCC_FLAGS", "").split()
 
 
 def _compile(src: str) -> str:
